@@ -1,0 +1,160 @@
+"""fp64 CPU oracle for the minGRU scan engine -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never calls it, and
+it shares no code with the GPU path: the arithmetic lives in ``oracle.c``
+(plain sequential loops over t in double precision), compiled with gcc into
+``liboracle.so`` next to this file.  This module only widens the fp32 inputs to
+float64 (exactly), calls the C loops and returns float64 results.
+
+What each function follows is stated in ``oracle.c``:
+  * ``log_fwd`` / ``log_bwd`` -- the minGRU linear recurrence
+    h_t = a_t h_{t-1} + b_t with inputs log a_t, log b_t, log h_0
+    (minGRU home page, introduction: the log-space baseline MinGRU and its
+    Heinsen scan); gradients by the chain rule.
+  * ``block_affine_fwd`` / ``block_affine_bwd`` -- h_t = A_t h_{t-1} + b_t
+    with block-diagonal k x k transitions (matrix_affine_scan in the
+    "Run the benchmarks" how-to, Step 2; RotationMinGRU / GivensMinGRU on the
+    home page).
+  * ``block_matrix_fwd`` / ``block_matrix_bwd`` -- P_t = A_t P_{t-1},
+    P_0 = I (matrix_scan in the same table).
+
+Parity pins: every function here is pinned against closed forms, special
+cases reducing to numpy routines, brute-force products, finite differences and
+exact invariants in ``tests/test_oracle_pins.py`` and the hand-derived
+fixtures under ``tests/golden/``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.c_int64
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (no fast-math; IEEE double arithmetic)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c99",
+               "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            sig = {
+                "oracle_log_fwd": [_D, _D, _D, _D, _I, _I, _I],
+                "oracle_log_bwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I],
+                "oracle_block_affine_fwd": [_D, _D, _D, _D, _I, _I, _I, _I],
+                "oracle_block_affine_bwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I],
+                "oracle_block_matrix_fwd": [_D, _D, _I, _I, _I, _I],
+                "oracle_block_matrix_bwd": [_D, _D, _D, _I, _I, _I, _I],
+            }
+            for name, args in sig.items():
+                fn = getattr(lib, name)
+                fn.argtypes = args
+                fn.restype = None
+            _lib = lib
+    return _lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _p(x):
+    return None if x is None else x.ctypes.data_as(_D)
+
+
+def log_fwd(log_a, log_b, log_h0):
+    """h (B,T,d) of the log-space scan; inputs (B,T,d), (B,T,d), (B,d)."""
+    la, lb, lh0 = _f64(log_a), _f64(log_b), _f64(log_h0)
+    B, T, d = la.shape
+    assert lb.shape == la.shape and lh0.shape == (B, d)
+    h = np.empty((B, T, d), np.float64)
+    _load().oracle_log_fwd(_p(la), _p(lb), _p(lh0), _p(h), B, T, d)
+    return h
+
+
+def log_bwd(log_a, log_b, log_h0, dh):
+    """(dlog_a, dlog_b, dlog_h0) for L = sum(dh * h)."""
+    la, lb, lh0, g = _f64(log_a), _f64(log_b), _f64(log_h0), _f64(dh)
+    B, T, d = la.shape
+    assert lb.shape == la.shape and g.shape == la.shape and lh0.shape == (B, d)
+    dla = np.empty_like(la)
+    dlb = np.empty_like(la)
+    dlh0 = np.empty_like(lh0)
+    _load().oracle_log_bwd(_p(la), _p(lb), _p(lh0), _p(g), _p(dla), _p(dlb), _p(dlh0), B, T, d)
+    return dla, dlb, dlh0
+
+
+def _block_shapes(A, d, k):
+    B, T, nb, k1, k2 = A.shape
+    assert k1 == k and k2 == k and nb * k == d
+    return B, T
+
+
+def block_affine_fwd(A, b, h0, k):
+    """h (B,T,d) of h_t = A_t h_{t-1} + b_t; A (B,T,d/k,k,k); h0 may be None (zeros)."""
+    A64, b64 = _f64(A), _f64(b)
+    B, T, d = b64.shape
+    _block_shapes(A64, d, k)
+    h064 = None if h0 is None else _f64(h0)
+    h = np.empty((B, T, d), np.float64)
+    _load().oracle_block_affine_fwd(_p(A64), _p(b64), _p(h064), _p(h), B, T, d, k)
+    return h
+
+
+def block_affine_bwd(A, b, h0, dh, k):
+    """(dA, db, dh0) for L = sum(dh * h) of the block-affine scan."""
+    A64, b64, g = _f64(A), _f64(b), _f64(dh)
+    B, T, d = b64.shape
+    _block_shapes(A64, d, k)
+    h064 = None if h0 is None else _f64(h0)
+    dA = np.empty_like(A64)
+    db = np.empty_like(b64)
+    dh0 = np.empty((B, d), np.float64)
+    _load().oracle_block_affine_bwd(_p(A64), _p(b64), _p(h064), _p(g), _p(dA), _p(db), _p(dh0),
+                                    B, T, d, k)
+    return dA, db, dh0
+
+
+def block_matrix_fwd(A, k):
+    """P (B,T,d/k,k,k) with P_t = A_t P_{t-1}, P_0 = I."""
+    A64 = _f64(A)
+    B, T, nb = A64.shape[:3]
+    d = nb * k
+    _block_shapes(A64, d, k)
+    P = np.empty_like(A64)
+    _load().oracle_block_matrix_fwd(_p(A64), _p(P), B, T, d, k)
+    return P
+
+
+def block_matrix_bwd(A, dP, k):
+    """dA for L = sum(dP * P) of the block cumulative product."""
+    A64, g = _f64(A), _f64(dP)
+    B, T, nb = A64.shape[:3]
+    d = nb * k
+    _block_shapes(A64, d, k)
+    assert g.shape == A64.shape
+    dA = np.empty_like(A64)
+    _load().oracle_block_matrix_bwd(_p(A64), _p(g), _p(dA), B, T, d, k)
+    return dA

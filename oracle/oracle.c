@@ -1,0 +1,255 @@
+/*
+ * oracle.c -- plain, sequential, fp64 CPU reference for the minGRU scan engine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or
+ * loads this file; only the tests, the package smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header or constant with the GPU
+ * path.
+ *
+ * What it computes (the pages never write the recurrences out; they name the
+ * operations and cite their sources):
+ *   - minGRU home page (mingru-scans), introduction: minGRU (Feng et al.,
+ *     arXiv:2410.01201) is a GRU reduced to the linear recurrence
+ *     h_t = a_t * h_{t-1} + b_t, solved by an associative scan; the log-space
+ *     baseline uses Heinsen's parallel scan (arXiv:2311.06281).  Heinsen's
+ *     log-space evaluation is a re-association of this same recurrence, so the
+ *     oracle evaluates the recurrence itself, one step at a time, in fp64.
+ *   - The block forms (RotationMinGRU / GivensMinGRU, same page; the scan ops
+ *     matrix_affine_scan and matrix_scan in the "Run the benchmarks" how-to,
+ *     Step 2 table) replace the scalar a_t by a block-diagonal k x k matrix:
+ *     h_t = A_t h_{t-1} + b_t, and the b = 0 product P_t = A_t P_{t-1}, P_0 = I.
+ *   - Gradients are the chain rule applied to these loops for the loss
+ *     L = sum_t <dh_t, h_t> (resp. sum_t <dP_t, P_t>).
+ *
+ * Layouts (row-major, last index fastest):
+ *   log scan:   la, lb, h, dh, dla, dlb : (B, T, d);  lh0, dlh0 : (B, d)
+ *   block ops:  A, dA, P, dP : (B, T, nb, k, k) with nb = d / k and
+ *               (A h)_r = sum_c A[r][c] h[c];  b, h, dh, db : (B, T, d);
+ *               h0, dh0 : (B, d);  block j owns channels [j*k, (j+1)*k).
+ * Inputs are the same fp32 arrays the GPU sees, widened exactly to double.
+ * Loops over t are sequential; there is no blocking, fusion or reordering.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- log scan */
+
+/* Forward: h_0 = exp(lh0); h_t = exp(la_t) h_{t-1} + exp(lb_t); writes h_1..T. */
+void oracle_log_fwd(const double *la, const double *lb, const double *lh0,
+                    double *h, int64_t B, int64_t T, int64_t d)
+{
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < d; ++c) {
+            double hp = exp(lh0[b * d + c]);
+            for (int64_t t = 0; t < T; ++t) {
+                int64_t i = (b * T + t) * d + c;
+                hp = exp(la[i]) * hp + exp(lb[i]);
+                h[i] = hp;
+            }
+        }
+}
+
+/* Backward of oracle_log_fwd under upstream dh = dL/dh_t:
+ *   g_T = dh_T,  g_t = dh_t + a_{t+1} g_{t+1}          (g_t = dL/dh_t total)
+ *   dla_t = g_t a_t h_{t-1},  dlb_t = g_t b_t,  dlh0 = g_1 a_1 h_0
+ * (d h_t / d log a_t = a_t h_{t-1}, d h_t / d log b_t = b_t,
+ *  d h_1 / d log h_0 = a_1 h_0). */
+void oracle_log_bwd(const double *la, const double *lb, const double *lh0,
+                    const double *dh, double *dla, double *dlb, double *dlh0,
+                    int64_t B, int64_t T, int64_t d)
+{
+    double *hs = (double *)malloc(sizeof(double) * (size_t)(T + 1));
+    if (!hs) return;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < d; ++c) {
+            /* hs[t] = h_t for t = 0..T (hs[0] = h_0) */
+            hs[0] = exp(lh0[b * d + c]);
+            for (int64_t t = 0; t < T; ++t) {
+                int64_t i = (b * T + t) * d + c;
+                hs[t + 1] = exp(la[i]) * hs[t] + exp(lb[i]);
+            }
+            double g = 0.0; /* g_{t+1}, zero past the end */
+            double a_next = 0.0;
+            for (int64_t t = T - 1; t >= 0; --t) {
+                int64_t i = (b * T + t) * d + c;
+                g = dh[i] + a_next * g;
+                double a = exp(la[i]);
+                dla[i] = g * a * hs[t];
+                dlb[i] = g * exp(lb[i]);
+                a_next = a;
+            }
+            /* here g = g_1 and a_next = a_1 */
+            dlh0[b * d + c] = (T > 0) ? g * a_next * hs[0] : 0.0;
+        }
+    free(hs);
+}
+
+/* ------------------------------------------------------- block-affine scan */
+
+static const double *blk(const double *M, int64_t b, int64_t t, int64_t j,
+                         int64_t T, int64_t nb, int64_t k)
+{
+    return M + (((b * T + t) * nb + j) * k * k);
+}
+
+/* Forward: h_0 = h0 (zero if h0 == NULL); h_t = A_t h_{t-1} + b_t, per block. */
+void oracle_block_affine_fwd(const double *A, const double *bv, const double *h0,
+                             double *h, int64_t B, int64_t T, int64_t d, int64_t k)
+{
+    int64_t nb = d / k;
+    double *cur = (double *)malloc(sizeof(double) * (size_t)k);
+    double *nxt = (double *)malloc(sizeof(double) * (size_t)k);
+    if (!cur || !nxt) { free(cur); free(nxt); return; }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t j = 0; j < nb; ++j) {
+            for (int64_t r = 0; r < k; ++r)
+                cur[r] = h0 ? h0[b * d + j * k + r] : 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                const double *At = blk(A, b, t, j, T, nb, k);
+                for (int64_t r = 0; r < k; ++r) {
+                    double s = bv[(b * T + t) * d + j * k + r];
+                    for (int64_t c = 0; c < k; ++c) s += At[r * k + c] * cur[c];
+                    nxt[r] = s;
+                }
+                for (int64_t r = 0; r < k; ++r) {
+                    cur[r] = nxt[r];
+                    h[(b * T + t) * d + j * k + r] = nxt[r];
+                }
+            }
+        }
+    free(cur);
+    free(nxt);
+}
+
+/* Backward of oracle_block_affine_fwd under upstream dh:
+ *   g_T = dh_T,  g_t = dh_t + A_{t+1}^T g_{t+1}
+ *   dA_t = g_t h_{t-1}^T,  db_t = g_t,  dh0 = A_1^T g_1.
+ * h is recomputed here from (A, b, h0). */
+void oracle_block_affine_bwd(const double *A, const double *bv, const double *h0,
+                             const double *dh, double *dA, double *db, double *dh0,
+                             int64_t B, int64_t T, int64_t d, int64_t k)
+{
+    int64_t nb = d / k;
+    double *hs = (double *)malloc(sizeof(double) * (size_t)((T + 1) * k));
+    double *g = (double *)malloc(sizeof(double) * (size_t)k);
+    double *w = (double *)malloc(sizeof(double) * (size_t)k); /* A_{t+1}^T g_{t+1} */
+    if (!hs || !g || !w) { free(hs); free(g); free(w); return; }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t j = 0; j < nb; ++j) {
+            for (int64_t r = 0; r < k; ++r)
+                hs[r] = h0 ? h0[b * d + j * k + r] : 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                const double *At = blk(A, b, t, j, T, nb, k);
+                for (int64_t r = 0; r < k; ++r) {
+                    double s = bv[(b * T + t) * d + j * k + r];
+                    for (int64_t c = 0; c < k; ++c) s += At[r * k + c] * hs[t * k + c];
+                    hs[(t + 1) * k + r] = s;
+                }
+            }
+            for (int64_t r = 0; r < k; ++r) w[r] = 0.0;
+            for (int64_t t = T - 1; t >= 0; --t) {
+                for (int64_t r = 0; r < k; ++r)
+                    g[r] = dh[(b * T + t) * d + j * k + r] + w[r];
+                const double *At = blk(A, b, t, j, T, nb, k);
+                double *dAt = dA + (((b * T + t) * nb + j) * k * k);
+                for (int64_t r = 0; r < k; ++r) {
+                    db[(b * T + t) * d + j * k + r] = g[r];
+                    for (int64_t c = 0; c < k; ++c)
+                        dAt[r * k + c] = g[r] * hs[t * k + c];
+                }
+                /* w = A_t^T g_t, used as A_{t}^T g_{t} at step t-1 */
+                for (int64_t c = 0; c < k; ++c) {
+                    double s = 0.0;
+                    for (int64_t r = 0; r < k; ++r) s += At[r * k + c] * g[r];
+                    w[c] = s;
+                }
+            }
+            /* after the loop w = A_1^T g_1 (all zeros if T == 0) */
+            for (int64_t r = 0; r < k; ++r) dh0[b * d + j * k + r] = w[r];
+        }
+    free(hs);
+    free(g);
+    free(w);
+}
+
+/* ----------------------------------------- block cumulative product (b = 0) */
+
+/* Forward: P_0 = I; P_t = A_t P_{t-1}; writes P_1..T. */
+void oracle_block_matrix_fwd(const double *A, double *P,
+                             int64_t B, int64_t T, int64_t d, int64_t k)
+{
+    int64_t nb = d / k;
+    double *cur = (double *)malloc(sizeof(double) * (size_t)(k * k));
+    if (!cur) return;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t j = 0; j < nb; ++j) {
+            for (int64_t r = 0; r < k; ++r)
+                for (int64_t c = 0; c < k; ++c) cur[r * k + c] = (r == c) ? 1.0 : 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                const double *At = blk(A, b, t, j, T, nb, k);
+                double *Pt = P + (((b * T + t) * nb + j) * k * k);
+                for (int64_t r = 0; r < k; ++r)
+                    for (int64_t c = 0; c < k; ++c) {
+                        double s = 0.0;
+                        for (int64_t m = 0; m < k; ++m) s += At[r * k + m] * cur[m * k + c];
+                        Pt[r * k + c] = s;
+                    }
+                memcpy(cur, Pt, sizeof(double) * (size_t)(k * k));
+            }
+        }
+    free(cur);
+}
+
+/* Backward of oracle_block_matrix_fwd under upstream dP:
+ *   G_T = dP_T,  G_t = dP_t + A_{t+1}^T G_{t+1},  dA_t = G_t P_{t-1}^T.
+ * P is recomputed here from A; P_0 = I is a constant (no gradient). */
+void oracle_block_matrix_bwd(const double *A, const double *dP, double *dA,
+                             int64_t B, int64_t T, int64_t d, int64_t k)
+{
+    int64_t nb = d / k;
+    int64_t kk = k * k;
+    double *Ps = (double *)malloc(sizeof(double) * (size_t)((T + 1) * kk));
+    double *G = (double *)malloc(sizeof(double) * (size_t)kk);
+    double *W = (double *)malloc(sizeof(double) * (size_t)kk); /* A_{t+1}^T G_{t+1} */
+    if (!Ps || !G || !W) { free(Ps); free(G); free(W); return; }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t j = 0; j < nb; ++j) {
+            for (int64_t r = 0; r < k; ++r)
+                for (int64_t c = 0; c < k; ++c) Ps[r * k + c] = (r == c) ? 1.0 : 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                const double *At = blk(A, b, t, j, T, nb, k);
+                for (int64_t r = 0; r < k; ++r)
+                    for (int64_t c = 0; c < k; ++c) {
+                        double s = 0.0;
+                        for (int64_t m = 0; m < k; ++m) s += At[r * k + m] * Ps[t * kk + m * k + c];
+                        Ps[(t + 1) * kk + r * k + c] = s;
+                    }
+            }
+            for (int64_t i = 0; i < kk; ++i) W[i] = 0.0;
+            for (int64_t t = T - 1; t >= 0; --t) {
+                const double *dPt = blk(dP, b, t, j, T, nb, k);
+                for (int64_t i = 0; i < kk; ++i) G[i] = dPt[i] + W[i];
+                const double *At = blk(A, b, t, j, T, nb, k);
+                double *dAt = dA + (((b * T + t) * nb + j) * kk);
+                /* dA_t[r][c] = sum_m G_t[r][m] P_{t-1}[c][m] */
+                for (int64_t r = 0; r < k; ++r)
+                    for (int64_t c = 0; c < k; ++c) {
+                        double s = 0.0;
+                        for (int64_t m = 0; m < k; ++m) s += G[r * k + m] * Ps[t * kk + c * k + m];
+                        dAt[r * k + c] = s;
+                    }
+                /* W = A_t^T G_t */
+                for (int64_t r = 0; r < k; ++r)
+                    for (int64_t c = 0; c < k; ++c) {
+                        double s = 0.0;
+                        for (int64_t m = 0; m < k; ++m) s += At[m * k + r] * G[m * k + c];
+                        W[r * k + c] = s;
+                    }
+            }
+        }
+    free(Ps);
+    free(G);
+    free(W);
+}

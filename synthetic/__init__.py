@@ -1,0 +1,137 @@
+"""Seeded synthetic inputs for the minGRU scan engine.
+
+This module is shared by the tests, the benchmark and the smoke check.  It
+holds none of the scan arithmetic: it only draws random numbers and turns them
+into the scan's inputs (gates, transition matrices, upstream gradients).
+
+Recipes (numpy PCG64 ``default_rng(seed)``, every draw in float64, rounded
+once to float32 at the end):
+
+* Log-space minGRU scan (minGRU home page, introduction: the MinGRU gate of
+  Feng et al.).  Draw k, x ~ N(0,1) of shape (B,T,d), then x0 ~ N(0,1) of shape
+  (B,d), then dh ~ N(0,1) of shape (B,T,d).  With a = sigmoid(-k), z = 1 - a
+  and g(x) = x + 0.5 for x >= 0, sigmoid(x) otherwise:
+  log_a = log a, log_b = log(z * g(x)), log_h0 = log g(x0).  Logs are taken
+  in closed form (log sigmoid(u) = -softplus(-u)) so nothing underflows.
+* Block scans (GivensMinGRU on the home page; the Clements rectangular mesh of
+  Givens rotations).  Draw s ~ N(0,1) of shape (B,T,nb), theta ~ U(-pi, pi) of
+  shape (B,T,nb,k(k-1)/2), b ~ N(0,1) of shape (B,T,d), dh ~ N(0,1) of shape
+  (B,T,d), and last (cumulative product only) dP ~ N(0,1) of shape
+  (B,T,nb,k,k).  A_t = sigmoid(s_t) R(theta_t) where R is k layers of disjoint
+  2x2 rotations: layer l acts on pairs (i, i+1) for i = l mod 2, l mod 2 + 2,
+  ... < k-1; layers are applied in order (R = L_{k-1} ... L_0) and angles are
+  consumed in (layer, pair) order.  Each rotation maps (x_i, x_j) to
+  (cos t x_i - sin t x_j, sin t x_i + cos t x_j).  h0 = 0.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+
+def _softplus(u):
+    return np.logaddexp(0.0, u)
+
+
+def _log_g(x):
+    # g(x) = x + 0.5 (x >= 0), sigmoid(x) (x < 0); log sigmoid(x) = -softplus(-x)
+    return np.where(x >= 0, np.log(np.maximum(x, 0.0) + 0.5), -_softplus(-x))
+
+
+@dataclass
+class LogInputs:
+    log_a: np.ndarray   # (B,T,d) float32
+    log_b: np.ndarray   # (B,T,d) float32
+    log_h0: np.ndarray  # (B,d)   float32
+    dh: np.ndarray      # (B,T,d) float32
+
+
+def log_inputs(B: int, T: int, d: int, seed: int = 0) -> LogInputs:
+    """MinGRU gate generator for the log-space scan (see module docstring)."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, T, d))
+    x = rng.standard_normal((B, T, d))
+    x0 = rng.standard_normal((B, d))
+    dh = rng.standard_normal((B, T, d))
+    log_a = -_softplus(k)            # log sigmoid(-k)
+    log_z = -_softplus(-k)           # log (1 - sigmoid(-k)) = log sigmoid(k)
+    log_b = log_z + _log_g(x)
+    log_h0 = _log_g(x0)
+    f = np.float32
+    return LogInputs(log_a.astype(f), log_b.astype(f), log_h0.astype(f), dh.astype(f))
+
+
+def n_angles(k: int) -> int:
+    return k * (k - 1) // 2
+
+
+def givens_mesh(theta: np.ndarray, k: int) -> np.ndarray:
+    """R(theta) in float64 for theta of shape (..., k(k-1)/2): shape (..., k, k)."""
+    theta = np.asarray(theta, dtype=np.float64)
+    assert theta.shape[-1] == n_angles(k)
+    lead = theta.shape[:-1]
+    R = np.broadcast_to(np.eye(k), lead + (k, k)).copy()
+    idx = 0
+    for layer in range(k):
+        for i in range(layer % 2, k - 1, 2):
+            c = np.cos(theta[..., idx])[..., None]
+            s = np.sin(theta[..., idx])[..., None]
+            ri = R[..., i, :].copy()
+            rj = R[..., i + 1, :].copy()
+            R[..., i, :] = c * ri - s * rj
+            R[..., i + 1, :] = s * ri + c * rj
+            idx += 1
+    assert idx == n_angles(k)
+    return R
+
+
+@dataclass
+class BlockInputs:
+    A: np.ndarray                    # (B,T,nb,k,k) float32
+    b: np.ndarray                    # (B,T,d) float32
+    h0: Optional[np.ndarray]         # (B,d) float32 or None (zeros)
+    dh: np.ndarray                   # (B,T,d) float32
+    dP: Optional[np.ndarray]         # (B,T,nb,k,k) float32 (cumulative product only)
+    k: int
+
+
+def block_inputs(B: int, T: int, d: int, k: int = 8, seed: int = 0, *,
+                 gate: bool = True, with_dP: bool = True,
+                 h0: str = "zero") -> BlockInputs:
+    """Gated Givens-mesh generator for the block scans (see module docstring).
+
+    gate=False drops the sigmoid gate (pure rotations, used for the long-T
+    orthogonality checks).  h0="zero" gives h0 = None (zeros, as in the
+    Givens lab configuration); h0="normal" draws h0 ~ N(0,1) after dP.
+    """
+    assert d % k == 0
+    nb = d // k
+    rng = np.random.default_rng(seed)
+    s = rng.standard_normal((B, T, nb))
+    theta = rng.uniform(-math.pi, math.pi, (B, T, nb, n_angles(k)))
+    b = rng.standard_normal((B, T, d))
+    dh = rng.standard_normal((B, T, d))
+    dP = rng.standard_normal((B, T, nb, k, k)) if with_dP else None
+    h0v = rng.standard_normal((B, d)) if h0 == "normal" else None
+    R = givens_mesh(theta, k)
+    if gate:
+        A = (1.0 / (1.0 + np.exp(-s)))[..., None, None] * R
+    else:
+        A = R
+    f = np.float32
+    return BlockInputs(A.astype(f), b.astype(f), None if h0v is None else h0v.astype(f),
+                       dh.astype(f), None if dP is None else dP.astype(f), k)
+
+
+# The five workloads, by name (shapes from the pages' lab and long-T
+# microbenchmark shapes, d = 64 and k = 8 from the Givens memory measurement).
+CONFIGS = {
+    "log_tiny":   dict(op="log", B=2, T=64, d=16),
+    "log_lab":    dict(op="log", B=128, T=64, d=64),
+    "log_longT":  dict(op="log", B=16, T=1024, d=64),
+    "block_lab":  dict(op="block", B=128, T=64, d=64, k=8),
+    "block_longT": dict(op="block", B=16, T=1024, d=64, k=8),
+}

@@ -1,0 +1,26 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_collection_modifyitems(config, items):
+    # GPU tests must run on a GPU machine; without one they fail loudly at the
+    # first device call rather than silently skipping, unless deselected.
+    pass
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("this test needs a GPU (run with -m 'not gpu' on a CPU-only host)")
+    return torch.device("cuda:0")

@@ -1,0 +1,87 @@
+"""The oracle pins must catch plausible slips in the oracle.
+
+Each case compiles a copy of oracle/oracle.c with one planted mistake (on the
+CPU, into a temporary directory), swaps it in for the real oracle library and
+runs the pin tests of test_oracle_pins.py against it.  At least one pin must
+fail for every mutant; a mutant that survives means the pins have a hole.
+"""
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, original text, mutated text); each original must occur exactly once
+MUTANTS = [
+    ("log_fwd drops b", "hp = exp(la[i]) * hp + exp(lb[i]);", "hp = exp(la[i]) * hp;"),
+    ("log_fwd sign", "hp = exp(la[i]) * hp + exp(lb[i]);", "hp = exp(la[i]) * hp - exp(lb[i]);"),
+    ("log_bwd uses a_t not a_{t+1}", "g = dh[i] + a_next * g;\n                double a = exp(la[i]);",
+     "double a = exp(la[i]);\n                g = dh[i] + a * g;"),
+    ("log_bwd h_t for h_{t-1}", "dla[i] = g * a * hs[t];", "dla[i] = g * a * hs[t + 1];"),
+    ("log_bwd drops b in dlb", "dlb[i] = g * exp(lb[i]);", "dlb[i] = g;"),
+    ("log_bwd dlh0 sign", "dlh0[b * d + c] = (T > 0) ? g * a_next * hs[0] : 0.0;",
+     "dlh0[b * d + c] = (T > 0) ? -g * a_next * hs[0] : 0.0;"),
+    ("affine_fwd transposed A", "for (int64_t c = 0; c < k; ++c) s += At[r * k + c] * cur[c];",
+     "for (int64_t c = 0; c < k; ++c) s += At[c * k + r] * cur[c];"),
+    ("affine_bwd A not A^T", "for (int64_t r = 0; r < k; ++r) s += At[r * k + c] * g[r];",
+     "for (int64_t r = 0; r < k; ++r) s += At[c * k + r] * g[r];"),
+    ("affine_bwd h_t for h_{t-1}", "dAt[r * k + c] = g[r] * hs[t * k + c];",
+     "dAt[r * k + c] = g[r] * hs[(t + 1) * k + c];"),
+    ("affine_bwd dA transposed", "dAt[r * k + c] = g[r] * hs[t * k + c];",
+     "dAt[c * k + r] = g[r] * hs[t * k + c];"),
+    ("cumprod_fwd P A order", "for (int64_t m = 0; m < k; ++m) s += At[r * k + m] * cur[m * k + c];",
+     "for (int64_t m = 0; m < k; ++m) s += cur[r * k + m] * At[m * k + c];"),
+    ("cumprod_bwd G P not G P^T", "s += G[r * k + m] * Ps[t * kk + c * k + m];",
+     "s += G[r * k + m] * Ps[t * kk + m * k + c];"),
+    ("cumprod_bwd A not A^T", "s += At[m * k + r] * G[m * k + c];", "s += At[r * k + m] * G[m * k + c];"),
+]
+
+PINS = [
+    pins.test_golden_log_scan,
+    pins.test_golden_block_affine,
+    pins.test_golden_block_cumprod,
+    lambda: pins.test_log_constant_coefficients_geometric(0.7, 0.3, 2.0),
+    pins.test_block_constant_coefficients_geometric,
+    pins.test_log_gradients_finite_difference,
+    pins.test_block_affine_gradients_finite_difference,
+    pins.test_block_cumprod_gradients_finite_difference,
+    pins.test_block_affine_brute_force_products,
+    pins.test_block_cumprod_brute_force_products,
+]
+
+
+def _build(src_text, out_dir):
+    c = os.path.join(out_dir, "mut.c")
+    so = os.path.join(out_dir, "libmut.so")
+    with open(c, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O1", "-std=c99", "-shared", "-fPIC", "-o", so, c, "-lm"], check=True)
+    return so
+
+
+@pytest.mark.parametrize("name,orig,mut", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, orig, mut, monkeypatch):
+    text = open(SRC).read()
+    assert text.count(orig) == 1, f"mutation site not unique for {name!r}"
+    oracle._load()  # make sure the real library and its signatures are set up
+    real = oracle._lib
+    with tempfile.TemporaryDirectory() as tmp:
+        lib = ctypes.CDLL(_build(text.replace(orig, mut), tmp))
+        for fname in ("oracle_log_fwd", "oracle_log_bwd", "oracle_block_affine_fwd",
+                      "oracle_block_affine_bwd", "oracle_block_matrix_fwd", "oracle_block_matrix_bwd"):
+            fn, ref = getattr(lib, fname), getattr(real, fname)
+            fn.argtypes, fn.restype = ref.argtypes, ref.restype
+        monkeypatch.setattr(oracle, "_lib", lib)
+        caught = []
+        for pin in PINS:
+            try:
+                pin()
+            except AssertionError:
+                caught.append(getattr(pin, "__name__", "pin"))
+        assert caught, f"no pin caught mutant {name!r}"
