@@ -1,0 +1,180 @@
+/*
+ * mgs.h -- C ABI of libmgs, the minGRU scan engine for AMD Instinct MI355X (gfx950).
+ *
+ * The library solves the linear recurrence h_t = A_t h_{t-1} + b_t by
+ * associative scan, forward and backward, in three forms:
+ *
+ *   1. log-space elementwise scan (A_t = a_t > 0 diagonal), inputs given as
+ *      log a_t, log b_t, log h_0 and evaluated in log space in the style of
+ *      Heinsen's scan -- the op behind MinGRU / SignedMinGRU
+ *      (minGRU home page, introduction; "Triton on GPU" tutorial, section
+ *      "What you gain (and where you don't)", op parallel_scan_log);
+ *   2. block-affine scan, A_t block-diagonal with k x k blocks -- the op behind
+ *      RotationMinGRU / GivensMinGRU ("Run the benchmarks" how-to, Step 2,
+ *      op matrix_affine_scan);
+ *   3. block cumulative product P_t = A_t P_{t-1}, P_0 = I, the b = 0 case
+ *      (same table, op matrix_scan).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every pointer is a DEVICE pointer (HIP global memory) except
+ *   `bytes` / `flags` out-parameters, which are host pointers.  The caller owns
+ *   every buffer; the library allocates nothing and keeps no per-call state.
+ *   Tensors are fp32, dense, row-major with the last index fastest, 16-byte
+ *   aligned:
+ *     (B,T,d)        sequence tensors; the scan runs over T
+ *     (B,d)          initial states and their gradients
+ *     (B,T,d/k,k,k)  block transitions; block j acts on channels [j*k,(j+1)*k)
+ *                    and (A h)_r = sum_c A[r][c] h[c]
+ * Outputs are fully overwritten (never accumulated) and must not overlap any
+ * input or each other.
+ *
+ * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *   stream-ordered and return once the kernels are queued; errors raised while
+ *   the kernels run surface at the caller's next synchronisation, as in HIP.
+ *
+ * Workspace.  Each op has a `*_workspace_size` query.  The workspace is
+ *   device memory of at least that many bytes that MUST BE ZERO-FILLED BEFORE
+ *   ITS FIRST USE; the library leaves it ready for the next call.  A forward
+ *   call stores there what its backward reads (tile carries), so pass the same
+ *   workspace to the backward of the same inputs.  Calls that share a
+ *   workspace must not run concurrently.
+ *
+ * Errors.  Arguments are validated before any HIP call:
+ *   MGS_ERR_INVALID_VALUE  NULL required pointer, size <= 0, d % k != 0,
+ *                          misaligned pointer, or output aliasing an input;
+ *   MGS_ERR_UNSUPPORTED    outside the envelope (k != 8 for the block ops,
+ *                          or a tensor with 2^31 or more elements); never a
+ *                          silent fallback to another path;
+ *   MGS_ERR_WORKSPACE      workspace NULL or smaller than the query says;
+ *   MGS_ERR_HIP            a HIP launch error; mgs_last_hip_error() gives the
+ *                          hipError_t (per calling thread).
+ * Non-finite inputs propagate; log_b = -inf (b = 0) and log_h0 = -inf
+ * (h_0 = 0) are supported exactly.
+ */
+#ifndef MGS_H
+#define MGS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MGS_OK = 0,
+    MGS_ERR_INVALID_VALUE = 1,
+    MGS_ERR_UNSUPPORTED = 2,
+    MGS_ERR_WORKSPACE = 3,
+    MGS_ERR_HIP = 4
+} mgs_status;
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int mgs_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *mgs_status_string(int status);
+
+/* hipError_t of the last MGS_ERR_HIP returned on the calling thread (0 if none). */
+int mgs_last_hip_error(void);
+
+/* Reads (synchronously, on `stream`) the workspace's device-side error flags
+ * into *flags: 0 = clean; bit 0 = a cross-workgroup wait in a kernel gave up
+ * after its spin limit (results of that call are invalid).  Clears the flags.
+ * Reads a few bytes of `workspace`; it must be a workspace used by this
+ * library. */
+mgs_status mgs_workspace_check(void *workspace, void *stream, int *flags);
+
+/* ------------------------------------------------------ log-space scan --- */
+/*
+ * Forward (minGRU home page, introduction: the log-space MinGRU with Heinsen's
+ * scan; op parallel_scan_log):
+ *     h_0 = exp(log_h0),   h_t = exp(log_a_t) h_{t-1} + exp(log_b_t),  t = 1..T
+ * computed in log space, log h_t = logaddexp(log_a_t + log h_{t-1}, log_b_t),
+ * and written as h (linear, h_1..h_T; h_0 is not written).
+ *   log_a, log_b : (B,T,d) in     log_h0 : (B,d) in     h : (B,T,d) out
+ */
+mgs_status mgs_scan_log_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes);
+
+mgs_status mgs_scan_log_fwd(const float *log_a, const float *log_b, const float *log_h0,
+                            float *h, int64_t B, int64_t T, int64_t d,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of mgs_scan_log_fwd for L = sum_t <dh_t, h_t>.  It recomputes the
+ * forward states (the home page notes the log-space op's backward recomputes
+ * its forward) and runs the reverse scan g_T = dh_T, g_t = dh_t + a_{t+1} g_{t+1}:
+ *     dlog_a_t = g_t a_t h_{t-1},   dlog_b_t = g_t b_t,   dlog_h0 = g_1 a_1 h_0.
+ *   dh : (B,T,d) in;   dlog_a, dlog_b : (B,T,d) out;   dlog_h0 : (B,d) out.
+ * fwd_state_valid != 0 promises that mgs_scan_log_fwd ran on these same inputs
+ * with this workspace since it was last used by another call; with 0 the
+ * backward first recomputes the forward's tile carries itself (one more
+ * kernel launch).
+ */
+mgs_status mgs_scan_log_bwd(const float *log_a, const float *log_b, const float *log_h0,
+                            const float *dh, float *dlog_a, float *dlog_b, float *dlog_h0,
+                            int64_t B, int64_t T, int64_t d,
+                            void *workspace, size_t workspace_bytes, int fwd_state_valid,
+                            void *stream);
+
+/* --------------------------------------------------- block-affine scan --- */
+/*
+ * Forward ("Run the benchmarks" how-to, Step 2, matrix_affine_scan; the
+ * GivensMinGRU / RotationMinGRU recurrences on the home page):
+ *     h_0 = h0 (zeros if h0 == NULL),   h_t = A_t h_{t-1} + b_t
+ * with A_t block-diagonal (d/k blocks of k x k).
+ *   A : (B,T,d/k,k,k) in;  b : (B,T,d) in;  h0 : (B,d) in or NULL;  h : (B,T,d) out.
+ * Envelope: k == 8.
+ */
+mgs_status mgs_block_affine_scan_workspace_size(int64_t B, int64_t T, int64_t d, int64_t k,
+                                                size_t *bytes);
+
+mgs_status mgs_block_affine_scan_fwd(const float *A, const float *b, const float *h0, float *h,
+                                     int64_t B, int64_t T, int64_t d, int64_t k,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of mgs_block_affine_scan_fwd for L = sum_t <dh_t, h_t>: the reverse
+ * scan g_T = dh_T, g_t = dh_t + A_{t+1}^T g_{t+1}, with
+ *     dA_t = g_t h_{t-1}^T (formed in registers, written once),  db_t = g_t,
+ *     dh0 = A_1^T g_1.
+ *   h : (B,T,d) in, the forward's output (it supplies h_{t-1}); b is not read
+ *   and may be NULL; h0 as in the forward;  dh : (B,T,d) in;
+ *   dA : (B,T,d/k,k,k) out;  db : (B,T,d) out;  dh0 : (B,d) out (written even
+ *   when h0 == NULL).
+ */
+mgs_status mgs_block_affine_scan_bwd(const float *A, const float *b, const float *h0,
+                                     const float *h, const float *dh,
+                                     float *dA, float *db, float *dh0,
+                                     int64_t B, int64_t T, int64_t d, int64_t k,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------ block cumulative product --- */
+/*
+ * Forward ("Run the benchmarks" how-to, Step 2, matrix_scan): the b = 0 case,
+ *     P_0 = I,   P_t = A_t P_{t-1}   per k x k block.
+ *   A : (B,T,d/k,k,k) in;   P : (B,T,d/k,k,k) out.   Envelope: k == 8.
+ */
+mgs_status mgs_block_matrix_scan_workspace_size(int64_t B, int64_t T, int64_t d, int64_t k,
+                                                size_t *bytes);
+
+mgs_status mgs_block_matrix_scan_fwd(const float *A, float *P,
+                                     int64_t B, int64_t T, int64_t d, int64_t k,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of mgs_block_matrix_scan_fwd for L = sum_t <dP_t, P_t>:
+ *     G_T = dP_T,  G_t = dP_t + A_{t+1}^T G_{t+1},  dA_t = G_t P_{t-1}^T.
+ *   P : (B,T,d/k,k,k) in, the forward's output (supplies P_{t-1});
+ *   dP : in;  dA : out (same shape).
+ */
+mgs_status mgs_block_matrix_scan_bwd(const float *A, const float *P, const float *dP, float *dA,
+                                     int64_t B, int64_t T, int64_t d, int64_t k,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MGS_H */

@@ -1,0 +1,64 @@
+"""Builds libmgs.so (the C-ABI scan library) in-tree with hipcc for gfx950.
+
+Usage: python -m scan_linear_rnns_amd.build   (or call build()).
+The shared library lands next to this file, where the Python binding loads it.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libmgs.so")
+SOURCES = ["mgs_api.cpp", "log_scan.hip", "block_scan.hip"]
+ARCH = os.environ.get("MGS_OFFLOAD_ARCH", "gfx950")
+
+# Packed fp32 instructions are disabled for every device code object: the
+# compiler would otherwise form them from ordinary float code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the MI355X library cannot be built")
+
+
+def _compile(src: str, obj: str, extra=()) -> None:
+    cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+           "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False, save_temps_dir: str | None = None) -> str:
+    """Compile every HIP/C++ source and link libmgs.so (always rebuilds)."""
+    with tempfile.TemporaryDirectory(prefix="mgs_build_") as tmp:
+        objs = []
+        for name in SOURCES:
+            src = os.path.join(CSRC, name)
+            obj = os.path.join(tmp, name + ".o")
+            extra = []
+            if save_temps_dir:
+                os.makedirs(save_temps_dir, exist_ok=True)
+                extra = ["-save-temps=obj", "-o", obj]
+            if verbose:
+                print("[build]", name, flush=True)
+            _compile(src, obj, extra)
+            objs.append(obj)
+        out_tmp = LIB + ".tmp%d" % os.getpid()
+        subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp, *objs],
+                       check=True)
+        os.replace(out_tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
+    sys.exit(0)

@@ -1,0 +1,908 @@
+// block_scan.hip -- block-affine scan and block cumulative product, forward and
+// fused backward, k = 8, for gfx950.
+//
+// The ops ("Run the benchmarks" how-to, Step 2: matrix_affine_scan and
+// matrix_scan; the RotationMinGRU / GivensMinGRU recurrences on the minGRU
+// home page):
+//     h_t = A_t h_{t-1} + b_t          P_t = A_t P_{t-1},  P_0 = I
+// per chain (b, block j), with A_t an 8 x 8 block.  Backward for
+// L = sum <dh_t, h_t> (resp. <dP_t, P_t>): g_t = dh_t + A_{t+1}^T g_{t+1},
+// dA_t = g_t h_{t-1}^T (resp. G_t P_{t-1}^T), db_t = g_t, dh0 = A_1^T g_1.
+// dA_t is formed in registers from g_t and h_{t-1} and written once; no
+// per-step product or intermediate tensor is ever stored.
+//
+// Register layout ("row lanes"): a chain's 8 x 8 matrices live in 8
+// consecutive lanes, lane v holding row v.  Column slots of a row are rotated
+// by the lane's quad: slot s holds column s ^ (v & 4).  With that rotation,
+// every operand a product needs from another row arrives through one of two
+// wave-uniform DPP patterns -- a quad broadcast (quad_perm [p,p,p,p]) for rows
+// in the lane's own quad, and a half-row mirror followed by a quad broadcast
+// for rows in the other quad -- and the rotation itself costs nothing because
+// loads and stores simply address the two 16-byte halves of a row in swapped
+// order.  An 8 x 8 by 8 x 8 product is 64 FMAs and 8 mirror moves per lane;
+// a matrix-vector product is 8 FMAs and one mirror.
+//
+// Decomposition: a wave holds 4 chains x 2 sub-chunks (lane = 32*sub + 8*chain
+// + row); a workgroup of W waves holds NCH = 2W consecutive chunks of C steps
+// each, i.e. one tile of TT = NCH*C steps of 4 chains.  Each chunk first
+// builds its aggregate (transfer matrix and offset) from a zero state, the
+// aggregates meet in LDS, and tiles along T exchange theirs by single-pass
+// decoupled look-back (tagged words, dispatch-order tickets; see device.hpp).
+// Each chunk then re-runs its recurrence from its true carry-in, keeping the
+// loaded A_t in registers, and writes its outputs.
+#include <hip/hip_runtime.h>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace mgs {
+namespace {
+
+// ------------------------------------------------------ 8-lane row algebra
+
+template <int P>
+__device__ __forceinline__ float qb(float x)   // value of quad position P
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), P | (P << 2) | (P << 4) | (P << 6),
+                                                   0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float hm(float x)   // value of lane 7 - v within the 8-lane group
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+}
+
+// y_v = sum_m R[v][m] x_m + add, R = own row (rotated slots), x one value per lane
+__device__ __forceinline__ float mv8(const float *R, float x, float add)
+{
+    const float mx = hm(x);
+    float a0 = fmaf(R[0], qb<0>(x), add);
+    float a1 = R[1] * qb<1>(x);
+    a0 = fmaf(R[2], qb<2>(x), a0);
+    a1 = fmaf(R[3], qb<3>(x), a1);
+    a0 = fmaf(R[7], qb<0>(mx), a0);
+    a1 = fmaf(R[6], qb<1>(mx), a1);
+    a0 = fmaf(R[5], qb<2>(mx), a0);
+    a1 = fmaf(R[4], qb<3>(mx), a1);
+    return a0 + a1;
+}
+
+// Y = R X : own row of R, rows of X spread over the group.  Y must not alias X.
+__device__ __forceinline__ void mm8(const float *R, const float *X, float *Y)
+{
+    float M[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) M[s] = hm(X[s]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const float xs = X[s];
+        const float ms = M[s ^ 4];
+        float a0 = R[0] * qb<0>(xs);
+        float a1 = R[1] * qb<1>(xs);
+        a0 = fmaf(R[2], qb<2>(xs), a0);
+        a1 = fmaf(R[3], qb<3>(xs), a1);
+        a0 = fmaf(R[7], qb<0>(ms), a0);
+        a1 = fmaf(R[6], qb<1>(ms), a1);
+        a0 = fmaf(R[5], qb<2>(ms), a0);
+        a1 = fmaf(R[4], qb<3>(ms), a1);
+        Y[s] = a0 + a1;
+    }
+}
+
+// Y = G X^T : own row of G, rows of X spread over the group.
+__device__ __forceinline__ void mmT8(const float *G, const float *X, float *Y)
+{
+    float M[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) M[s] = hm(X[s]);
+    float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f, y4 = 0.f, y5 = 0.f, y6 = 0.f, y7 = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        y0 = fmaf(G[s], qb<0>(X[s]), y0);
+        y1 = fmaf(G[s], qb<1>(X[s]), y1);
+        y2 = fmaf(G[s], qb<2>(X[s]), y2);
+        y3 = fmaf(G[s], qb<3>(X[s]), y3);
+        y7 = fmaf(G[s ^ 4], qb<0>(M[s]), y7);
+        y6 = fmaf(G[s ^ 4], qb<1>(M[s]), y6);
+        y5 = fmaf(G[s ^ 4], qb<2>(M[s]), y5);
+        y4 = fmaf(G[s ^ 4], qb<3>(M[s]), y4);
+    }
+    Y[0] = y0; Y[1] = y1; Y[2] = y2; Y[3] = y3; Y[4] = y4; Y[5] = y5; Y[6] = y6; Y[7] = y7;
+}
+
+// Row v of x x'^T scaled: Y[slot] = g * x'_{column(slot)}  (x' one value per lane)
+__device__ __forceinline__ void outer8(float g, float x, float *Y)
+{
+    const float mx = hm(x);
+    Y[0] = g * qb<0>(x);
+    Y[1] = g * qb<1>(x);
+    Y[2] = g * qb<2>(x);
+    Y[3] = g * qb<3>(x);
+    Y[4] = g * qb<3>(mx);
+    Y[5] = g * qb<2>(mx);
+    Y[6] = g * qb<1>(mx);
+    Y[7] = g * qb<0>(mx);
+}
+
+__device__ __forceinline__ void eye_row(int v, float *Y)
+{
+#pragma unroll
+    for (int s = 0; s < 8; ++s) Y[s] = (s == (v & 3)) ? 1.0f : 0.0f;
+}
+
+// row v of a row-major 8x8 block at p (16-byte aligned), into rotated slots
+__device__ __forceinline__ void load_row(const float *p, int v, float *R)
+{
+    const int lo = v & 4;
+    const float4 x0 = *reinterpret_cast<const float4 *>(p + v * 8 + lo);
+    const float4 x1 = *reinterpret_cast<const float4 *>(p + v * 8 + (lo ^ 4));
+    R[0] = x0.x; R[1] = x0.y; R[2] = x0.z; R[3] = x0.w;
+    R[4] = x1.x; R[5] = x1.y; R[6] = x1.z; R[7] = x1.w;
+}
+
+// row v of the TRANSPOSE of the 8x8 block at p (column v), rotated slots
+__device__ __forceinline__ void load_col(const float *p, int v, float *R)
+{
+    const int lo = v & 4;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) R[s] = p[((s ^ lo) * 8) + v];
+}
+
+__device__ __forceinline__ void store_row(float *p, int v, const float *R)
+{
+    const int lo = v & 4;
+    *reinterpret_cast<float4 *>(p + v * 8 + lo) = make_float4(R[0], R[1], R[2], R[3]);
+    *reinterpret_cast<float4 *>(p + v * 8 + (lo ^ 4)) = make_float4(R[4], R[5], R[6], R[7]);
+}
+
+// ------------------------------------------------------------ look-back
+
+// Lanes of wave 0 take part; lanes 32..63 mirror lanes 0..31 (same slot).
+// Returns the nearest tile p (in the direction dir = -1: earlier tiles,
+// +1: later tiles) whose IW-word inclusive state is visible to every lane,
+// with the state in xi; -1 if the spin limit was hit.
+template <int IW>
+__device__ int find_inclusive(const uint64_t *incl, int j, int nT, int nCG, int cg, int slot,
+                              int dir, uint32_t tag, uint32_t *err, float *xi)
+{
+    constexpr int WIN = (IW == 1) ? 8 : 2;
+    for (uint32_t spin = 0;; ++spin) {
+        for (int p0 = j + dir; p0 >= 0 && p0 < nT; p0 += dir * WIN) {
+            uint64_t w[WIN][IW];
+#pragma unroll
+            for (int u = 0; u < WIN; ++u) {
+                const int p = p0 + dir * u;
+                const bool in = p >= 0 && p < nT;
+                const uint64_t *src = incl + ((static_cast<size_t>(in ? p : 0) * nCG + cg) * 32 + slot) * IW;
+#pragma unroll
+                for (int e = 0; e < IW; ++e) w[u][e] = in ? tagged_load(src + e) : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < WIN; ++u) {
+                const int p = p0 + dir * u;
+                if (p < 0 || p >= nT) break;
+                bool ok = true;
+#pragma unroll
+                for (int e = 0; e < IW; ++e) ok = ok && tag_is(w[u][e], tag);
+                if (__all(ok)) {
+#pragma unroll
+                    for (int e = 0; e < IW; ++e) xi[e] = tag_value(w[u][e]);
+                    return p;
+                }
+            }
+        }
+        if (spin >= kSpinLimit) {
+            raise_error(err, kErrSpin);
+            return -1;
+        }
+        backoff();
+    }
+}
+
+// Loads one tile's AW-word aggregate for this lane, waiting for every word.
+template <int AW>
+__device__ __forceinline__ void load_aggregate(const uint64_t *agg, int p, int nCG, int cg, int slot,
+                                               uint32_t tag, uint32_t *err, float *out)
+{
+    const uint64_t *src = agg + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * AW;
+    uint64_t w[AW];
+#pragma unroll
+    for (int e = 0; e < AW; ++e) w[e] = tagged_load(src + e);
+#pragma unroll
+    for (int e = 0; e < AW; ++e) {
+        for (uint32_t spin = 0; !tag_is(w[e], tag); ++spin) {
+            if (spin >= kSpinLimit) {
+                raise_error(err, kErrSpin);
+                break;
+            }
+            backoff();
+            w[e] = tagged_load(src + e);
+        }
+        out[e] = tag_value(w[e]);
+    }
+}
+
+template <int AW>
+__device__ __forceinline__ void publish(uint64_t *dst, int tile, int slot, uint32_t tag, const float *x)
+{
+    uint64_t *p = dst + (static_cast<size_t>(tile) * 32 + slot) * AW;
+#pragma unroll
+    for (int e = 0; e < AW; ++e) tagged_store(p + e, tag, x[e]);
+}
+
+// ------------------------------------------------------------- arguments
+
+struct BlkArgs {
+    const float *A;      // (B,T,nb,8,8)
+    const float *x;      // affine: b (fwd) or h (bwd); cumprod bwd: P
+    const float *y;      // affine bwd: dh; cumprod bwd: dP
+    const float *h0;     // affine: (B,d) or nullptr
+    float *out;          // affine fwd: h; affine bwd: dA; cumprod fwd: P; cumprod bwd: dA
+    float *out2;         // affine bwd: db
+    float *out3;         // affine bwd: dh0
+    int64_t nchain;
+    int T, d, nb, nCG, nT, nTiles;
+    uint32_t *ticket, *err;
+    uint64_t *agg, *incl;
+    uint32_t tag;
+};
+
+struct Tile {
+    int lane, wv, v, cgl, sub, slot, q, j, cg, t0;
+    bool cv;
+    int64_t bb, jb;
+    int64_t ablk0;   // element offset of A block (bb, t=0, jb)
+    int64_t astep;   // elements between consecutive t of the same block
+    int64_t vec0;    // element offset of (bb, t=0, jb*8 + v) in (B,T,d)
+    int64_t vstep;   // = d
+};
+
+template <int C, int W>
+__device__ __forceinline__ Tile make_tile(const BlkArgs &a, int tile, bool reverse)
+{
+    Tile t;
+    t.lane = threadIdx.x & 63;
+    t.wv = threadIdx.x >> 6;
+    t.v = t.lane & 7;
+    t.cgl = (t.lane >> 3) & 3;
+    t.sub = t.lane >> 5;
+    t.slot = t.cgl * 8 + t.v;
+    t.q = t.wv * 2 + t.sub;
+    const int jr = tile / a.nCG;
+    t.cg = tile - jr * a.nCG;
+    t.j = reverse ? a.nT - 1 - jr : jr;
+    const int64_t chain = static_cast<int64_t>(t.cg) * 4 + t.cgl;
+    t.cv = chain < a.nchain;
+    const int64_t cc = t.cv ? chain : 0;
+    t.bb = cc / a.nb;
+    t.jb = cc - t.bb * a.nb;
+    t.astep = static_cast<int64_t>(a.nb) * 64;
+    t.ablk0 = (t.bb * a.T * a.nb + t.jb) * 64;
+    t.vstep = a.d;
+    t.vec0 = t.bb * a.T * a.d + t.jb * 8 + t.v;
+    t.t0 = t.j * (2 * W * C) + t.q * C;
+    return t;
+}
+
+// ======================================================= block-affine fwd
+
+template <int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
+{
+    constexpr int NCH = 2 * W;
+    constexpr int AW = 9;   // row of Phi + one entry of u
+    __shared__ float sAgg[NCH][32][AW];
+    __shared__ float sCarry[32];
+    __shared__ uint32_t sTicket;
+
+    const int tile = MULTI ? static_cast<int>(take_ticket(a.ticket, a.nTiles, a.err, &sTicket))
+                           : static_cast<int>(blockIdx.x);
+    const Tile tl = make_tile<C, W>(a, tile, false);
+    const int ftile = tl.j * a.nCG + tl.cg;
+
+    float Ar[C][8], bv[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = tl.t0 + i;
+        if (tl.cv && t < a.T) {
+            load_row(a.A + tl.ablk0 + t * tl.astep, tl.v, Ar[i]);
+            bv[i] = a.x[tl.vec0 + t * tl.vstep];
+        } else {
+            eye_row(tl.v, Ar[i]);
+            bv[i] = 0.0f;
+        }
+    }
+
+    // chunk aggregate from a zero state: Phi = A_e..A_s, u = local h_e
+    float Phi[8], u = bv[0];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) Phi[s] = Ar[0][s];
+#pragma unroll
+    for (int i = 1; i < C; ++i) {
+        float np[8];
+        mm8(Ar[i], Phi, np);
+        u = mv8(Ar[i], u, bv[i]);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) Phi[s] = np[s];
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sAgg[tl.q][tl.slot][s] = Phi[s];
+    sAgg[tl.q][tl.slot][8] = u;
+    __syncthreads();
+
+    const float xh0 = (tl.cv && a.h0) ? a.h0[tl.bb * a.d + tl.jb * 8 + tl.v] : 0.0f;
+    float x;
+    if constexpr (MULTI) {
+        if (tl.wv == 0) {
+            // tile aggregate; sAgg[q] becomes the composite of chunks 0..q
+            float TP[8], Tu = sAgg[0][tl.slot][8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) TP[s] = sAgg[0][tl.slot][s];
+            for (int q = 1; q < NCH; ++q) {
+                float R[8], np[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) R[s] = sAgg[q][tl.slot][s];
+                mm8(R, TP, np);
+                Tu = mv8(R, Tu, sAgg[q][tl.slot][8]);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) TP[s] = np[s];
+                if (tl.sub == 0) {
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) sAgg[q][tl.slot][s] = TP[s];
+                    sAgg[q][tl.slot][8] = Tu;
+                }
+            }
+            if (tl.sub == 0 && tl.j > 0 && tl.j < a.nT - 1) {
+                float pay[AW];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) pay[s] = TP[s];
+                pay[8] = Tu;
+                publish<AW>(a.agg, ftile, tl.slot, a.tag, pay);
+            }
+            float xin = xh0;
+            if (tl.j > 0) {
+                float xi[1];
+                const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, a.tag, a.err, xi);
+                if (ps >= 0) xin = xi[0];
+                for (int p = ps + 1; p < tl.j; ++p) {
+                    float ag[AW];
+                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, a.tag, a.err, ag);
+                    xin = mv8(ag, xin, ag[8]);
+                }
+            }
+            if (tl.sub == 0 && tl.j < a.nT - 1) {
+                const float xo = mv8(TP, xin, Tu);
+                publish<1>(a.incl, ftile, tl.slot, a.tag, &xo);
+            }
+            if (tl.sub == 0) sCarry[tl.slot] = xin;
+        }
+        __syncthreads();
+        x = sCarry[tl.slot];
+        if (tl.q > 0) x = mv8(sAgg[tl.q - 1][tl.slot], x, sAgg[tl.q - 1][tl.slot][8]);
+    } else {
+        x = xh0;
+        for (int q = 0; q < tl.q; ++q) x = mv8(sAgg[q][tl.slot], x, sAgg[q][tl.slot][8]);
+    }
+
+    // re-run the recurrence from the true state entering the chunk
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        x = mv8(Ar[i], x, bv[i]);
+        const int t = tl.t0 + i;
+        if (tl.cv && t < a.T) a.out[tl.vec0 + t * tl.vstep] = x;
+    }
+}
+
+// ======================================================= block-affine bwd
+// Reverse scan on w_t = A_t^T g_t with g_t = dh_t + w_{t+1}; per chunk [s, e]
+// w_s = Psi w_{e+1} + Wl with Psi = A_s^T .. A_e^T.
+
+template <int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
+{
+    constexpr int NCH = 2 * W;
+    constexpr int AW = 9;
+    __shared__ float sAgg[NCH][32][AW];
+    __shared__ float sCarry[32];
+    __shared__ uint32_t sTicket;
+
+    const int tile = MULTI ? static_cast<int>(take_ticket(a.ticket, a.nTiles, a.err, &sTicket))
+                           : static_cast<int>(blockIdx.x);
+    const Tile tl = make_tile<C, W>(a, tile, true);
+    const int ftile = tl.j * a.nCG + tl.cg;
+
+    float ATr[C][8], gv[C], hp[C];   // rows of A_t^T, upstream dh_t, h_{t-1}
+    const float xh0 = (tl.cv && a.h0) ? a.h0[tl.bb * a.d + tl.jb * 8 + tl.v] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = tl.t0 + i;
+        if (tl.cv && t < a.T) {
+            load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
+            gv[i] = a.y[tl.vec0 + t * tl.vstep];
+            hp[i] = (t > 0) ? a.x[tl.vec0 + (t - 1) * tl.vstep] : xh0;
+        } else {
+            eye_row(tl.v, ATr[i]);
+            gv[i] = 0.0f;
+            hp[i] = 0.0f;
+        }
+    }
+
+    // chunk aggregate from a zero carry, walking t downwards
+    float Psi[8], Wl;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) Psi[s] = ATr[C - 1][s];
+    Wl = mv8(ATr[C - 1], gv[C - 1], 0.0f);
+#pragma unroll
+    for (int i = C - 2; i >= 0; --i) {
+        float np[8];
+        mm8(ATr[i], Psi, np);
+        Wl = mv8(ATr[i], gv[i] + Wl, 0.0f);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) Psi[s] = np[s];
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sAgg[tl.q][tl.slot][s] = Psi[s];
+    sAgg[tl.q][tl.slot][8] = Wl;
+    __syncthreads();
+
+    float w;
+    if constexpr (MULTI) {
+        if (tl.wv == 0) {
+            // tile aggregate; sAgg[q] becomes the composite of chunks q..NCH-1
+            float TP[8], Tw = sAgg[NCH - 1][tl.slot][8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) TP[s] = sAgg[NCH - 1][tl.slot][s];
+            for (int q = NCH - 2; q >= 0; --q) {
+                float R[8], np[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) R[s] = sAgg[q][tl.slot][s];
+                mm8(R, TP, np);
+                Tw = mv8(R, Tw, sAgg[q][tl.slot][8]);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) TP[s] = np[s];
+                if (tl.sub == 0) {
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) sAgg[q][tl.slot][s] = TP[s];
+                    sAgg[q][tl.slot][8] = Tw;
+                }
+            }
+            if (tl.sub == 0 && tl.j > 0 && tl.j < a.nT - 1) {
+                float pay[AW];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) pay[s] = TP[s];
+                pay[8] = Tw;
+                publish<AW>(a.agg, ftile, tl.slot, a.tag, pay);
+            }
+            float win = 0.0f;
+            if (tl.j < a.nT - 1) {
+                float xi[1];
+                const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, a.tag, a.err, xi);
+                int pend = a.nT;
+                if (ps >= 0) { win = xi[0]; pend = ps; }
+                for (int p = pend - 1; p > tl.j; --p) {
+                    float ag[AW];
+                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, a.tag, a.err, ag);
+                    win = mv8(ag, win, ag[8]);
+                }
+            }
+            if (tl.sub == 0 && tl.j > 0) {
+                const float wo = mv8(TP, win, Tw);
+                publish<1>(a.incl, ftile, tl.slot, a.tag, &wo);
+            }
+            if (tl.sub == 0) sCarry[tl.slot] = win;
+        }
+        __syncthreads();
+        w = sCarry[tl.slot];
+        if (tl.q < NCH - 1) w = mv8(sAgg[tl.q + 1][tl.slot], w, sAgg[tl.q + 1][tl.slot][8]);
+    } else {
+        w = 0.0f;
+        for (int q = NCH - 1; q > tl.q; --q) w = mv8(sAgg[q][tl.slot], w, sAgg[q][tl.slot][8]);
+    }
+
+    // re-run the reverse recurrence from the true carry; emit dA, db, dh0
+#pragma unroll
+    for (int i = C - 1; i >= 0; --i) {
+        const float g = gv[i] + w;
+        float dAr[8];
+        outer8(g, hp[i], dAr);
+        w = mv8(ATr[i], g, 0.0f);
+        const int t = tl.t0 + i;
+        if (tl.cv && t < a.T) {
+            a.out2[tl.vec0 + t * tl.vstep] = g;
+            store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, dAr);
+        }
+    }
+    if (tl.cv && tl.t0 == 0) a.out3[tl.bb * a.d + tl.jb * 8 + tl.v] = w;   // A_1^T g_1
+}
+
+// ================================================ block cumulative product
+
+template <int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
+{
+    constexpr int NCH = 2 * W;
+    constexpr int AW = 8;
+    __shared__ float sAgg[NCH][32][AW];
+    __shared__ float sCarry[32][8];
+    __shared__ uint32_t sTicket;
+
+    const int tile = MULTI ? static_cast<int>(take_ticket(a.ticket, a.nTiles, a.err, &sTicket))
+                           : static_cast<int>(blockIdx.x);
+    const Tile tl = make_tile<C, W>(a, tile, false);
+    const int ftile = tl.j * a.nCG + tl.cg;
+
+    float Ar[C][8];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = tl.t0 + i;
+        if (tl.cv && t < a.T)
+            load_row(a.A + tl.ablk0 + t * tl.astep, tl.v, Ar[i]);
+        else
+            eye_row(tl.v, Ar[i]);
+    }
+
+    float Phi[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) Phi[s] = Ar[0][s];
+#pragma unroll
+    for (int i = 1; i < C; ++i) {
+        float np[8];
+        mm8(Ar[i], Phi, np);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) Phi[s] = np[s];
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sAgg[tl.q][tl.slot][s] = Phi[s];
+    __syncthreads();
+
+    // composites of chunks 0..q (wave 0), tile look-back, tile carry
+    if (tl.wv == 0) {
+        float TP[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) TP[s] = sAgg[0][tl.slot][s];
+        for (int q = 1; q < NCH; ++q) {
+            float R[8], np[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) R[s] = sAgg[q][tl.slot][s];
+            mm8(R, TP, np);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) TP[s] = np[s];
+            if (tl.sub == 0) {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) sAgg[q][tl.slot][s] = TP[s];
+            }
+        }
+        float Pin[8];
+        eye_row(tl.v, Pin);
+        if constexpr (MULTI) {
+            if (tl.sub == 0 && tl.j > 0 && tl.j < a.nT - 1) publish<AW>(a.agg, ftile, tl.slot, a.tag, TP);
+            if (tl.j > 0) {
+                float xi[8];
+                const int ps = find_inclusive<8>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, a.tag, a.err, xi);
+                if (ps >= 0) {
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) Pin[s] = xi[s];
+                }
+                for (int p = ps + 1; p < tl.j; ++p) {
+                    float ag[AW], np[8];
+                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, a.tag, a.err, ag);
+                    mm8(ag, Pin, np);
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) Pin[s] = np[s];
+                }
+            }
+            if (tl.sub == 0 && tl.j < a.nT - 1) {
+                float Po[8];
+                mm8(TP, Pin, Po);
+                publish<8>(a.incl, ftile, tl.slot, a.tag, Po);
+            }
+        }
+        if (tl.sub == 0) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) sCarry[tl.slot][s] = Pin[s];
+        }
+    }
+    __syncthreads();
+    float P[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) P[s] = sCarry[tl.slot][s];
+    if (tl.q > 0) {
+        float np[8];
+        mm8(sAgg[tl.q - 1][tl.slot], P, np);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) P[s] = np[s];
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        float np[8];
+        mm8(Ar[i], P, np);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) P[s] = np[s];
+        const int t = tl.t0 + i;
+        if (tl.cv && t < a.T) store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, P);
+    }
+}
+
+// Backward: W_t = A_t^T G_t with G_t = dP_t + W_{t+1}; per chunk [s, e]
+// W_s = Psi W_{e+1} + Wl.  dA_t = G_t P_{t-1}^T with P_{t-1} read from P.
+template <int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
+{
+    constexpr int NCH = 2 * W;
+    constexpr int AW = 16;   // row of Psi, row of Wl
+    __shared__ float sAgg[NCH][32][AW];
+    __shared__ float sCarry[32][8];
+    __shared__ uint32_t sTicket;
+
+    const int tile = MULTI ? static_cast<int>(take_ticket(a.ticket, a.nTiles, a.err, &sTicket))
+                           : static_cast<int>(blockIdx.x);
+    const Tile tl = make_tile<C, W>(a, tile, true);
+    const int ftile = tl.j * a.nCG + tl.cg;
+
+    float ATr[C][8], Gr[C][8];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = tl.t0 + i;
+        if (tl.cv && t < a.T) {
+            load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
+            load_row(a.y + tl.ablk0 + t * tl.astep, tl.v, Gr[i]);
+        } else {
+            eye_row(tl.v, ATr[i]);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) Gr[i][s] = 0.0f;
+        }
+    }
+
+    float Psi[8], Wl[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) Psi[s] = ATr[C - 1][s];
+    mm8(ATr[C - 1], Gr[C - 1], Wl);
+#pragma unroll
+    for (int i = C - 2; i >= 0; --i) {
+        float np[8], gw[8], nw[8];
+        mm8(ATr[i], Psi, np);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) gw[s] = Gr[i][s] + Wl[s];
+        mm8(ATr[i], gw, nw);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) { Psi[s] = np[s]; Wl[s] = nw[s]; }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        sAgg[tl.q][tl.slot][s] = Psi[s];
+        sAgg[tl.q][tl.slot][8 + s] = Wl[s];
+    }
+    __syncthreads();
+
+    if (tl.wv == 0) {
+        float TP[8], TW[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            TP[s] = sAgg[NCH - 1][tl.slot][s];
+            TW[s] = sAgg[NCH - 1][tl.slot][8 + s];
+        }
+        for (int q = NCH - 2; q >= 0; --q) {
+            float R[8], np[8], nw[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) R[s] = sAgg[q][tl.slot][s];
+            mm8(R, TP, np);
+            mm8(R, TW, nw);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                TP[s] = np[s];
+                TW[s] = nw[s] + sAgg[q][tl.slot][8 + s];
+            }
+            if (tl.sub == 0) {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    sAgg[q][tl.slot][s] = TP[s];
+                    sAgg[q][tl.slot][8 + s] = TW[s];
+                }
+            }
+        }
+        float Win[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) Win[s] = 0.0f;
+        if constexpr (MULTI) {
+            if (tl.sub == 0 && tl.j > 0 && tl.j < a.nT - 1) {
+                float pay[AW];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) { pay[s] = TP[s]; pay[8 + s] = TW[s]; }
+                publish<AW>(a.agg, ftile, tl.slot, a.tag, pay);
+            }
+            if (tl.j < a.nT - 1) {
+                float xi[8];
+                const int ps = find_inclusive<8>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, a.tag, a.err, xi);
+                int pend = a.nT;
+                if (ps >= 0) {
+                    pend = ps;
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) Win[s] = xi[s];
+                }
+                for (int p = pend - 1; p > tl.j; --p) {
+                    float ag[AW], np[8];
+                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, a.tag, a.err, ag);
+                    mm8(ag, Win, np);
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) Win[s] = np[s] + ag[8 + s];
+                }
+            }
+            if (tl.sub == 0 && tl.j > 0) {
+                float Wo[8];
+                mm8(TP, Win, Wo);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) Wo[s] += TW[s];
+                publish<8>(a.incl, ftile, tl.slot, a.tag, Wo);
+            }
+        }
+        if (tl.sub == 0) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) sCarry[tl.slot][s] = Win[s];
+        }
+    }
+    __syncthreads();
+    float Wc[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) Wc[s] = sCarry[tl.slot][s];
+    if (tl.q < NCH - 1) {
+        float np[8];
+        mm8(sAgg[tl.q + 1][tl.slot], Wc, np);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) Wc[s] = np[s] + sAgg[tl.q + 1][tl.slot][8 + s];
+    }
+
+#pragma unroll
+    for (int i = C - 1; i >= 0; --i) {
+        const int t = tl.t0 + i;
+        const bool valid = tl.cv && t < a.T;
+        float G[8], Pp[8], dAr[8], nw[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) G[s] = Gr[i][s] + Wc[s];
+        if (valid && t > 0)
+            load_row(a.x + tl.ablk0 + (t - 1) * tl.astep, tl.v, Pp);
+        else
+            eye_row(tl.v, Pp);
+        mmT8(G, Pp, dAr);
+        mm8(ATr[i], G, nw);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) Wc[s] = nw[s];
+        if (valid) store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, dAr);
+    }
+}
+
+__global__ void fill_zero_kernel(float *p, int64_t n)
+{
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+// ------------------------------------------------------------ host side
+
+constexpr int kW = 4;
+
+BlockGeom make_geom(int64_t B, int64_t T, int64_t d, int64_t k, int agg_words, int incl_words,
+                    int max_c)
+{
+    BlockGeom g{};
+    g.T = static_cast<int>(T);
+    g.d = static_cast<int>(d);
+    g.k = static_cast<int>(k);
+    g.nb = static_cast<int>(d / k);
+    g.nchain = B * g.nb;
+    g.G = 4;
+    g.W = kW;
+    const int nch = 2 * kW;
+    int C = 1;
+    while (C < max_c && static_cast<int64_t>(nch) * C < T) C *= 2;
+    g.C = C;
+    g.TT = nch * C;
+    g.nT = static_cast<int>((T + g.TT - 1) / g.TT);
+    g.nCG = static_cast<int>((g.nchain + 3) / 4);
+    g.nTiles = g.nT * g.nCG;
+    g.agg_words = agg_words;
+    g.incl_words = incl_words;
+    size_t off = sizeof(WsHeader);
+    if (g.nT > 1) {
+        const size_t slots = static_cast<size_t>(g.nTiles) * 32;
+        g.off_agg = off;  off = align256(off + slots * agg_words * 8);
+        g.off_incl = off; off = align256(off + slots * incl_words * 8);
+    }
+    g.bytes = off;
+    return g;
+}
+
+BlkArgs base_args(const BlockGeom &g, void *ws, uint32_t tag, bool bwd)
+{
+    char *w = static_cast<char *>(ws);
+    WsHeader *hd = reinterpret_cast<WsHeader *>(w);
+    BlkArgs a{};
+    a.nchain = g.nchain;
+    a.T = g.T; a.d = g.d; a.nb = g.nb; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
+    a.ticket = bwd ? &hd->ticket_bwd : &hd->ticket_fwd;
+    a.err = &hd->err;
+    a.tag = tag;
+    if (g.nT > 1) {
+        a.agg = reinterpret_cast<uint64_t *>(w + g.off_agg);
+        a.incl = reinterpret_cast<uint64_t *>(w + g.off_incl);
+    }
+    return a;
+}
+
+#define MGS_BLOCK_LAUNCH(KERNEL, g, args, s)                                                      \
+    do {                                                                                          \
+        const dim3 grid_(g.nTiles), block_(64 * kW);                                              \
+        const bool multi_ = g.nT > 1;                                                             \
+        switch (g.C) {                                                                            \
+        case 1: if (multi_) hipLaunchKernelGGL((KERNEL<1, kW, true>), grid_, block_, 0, s, args); \
+                else hipLaunchKernelGGL((KERNEL<1, kW, false>), grid_, block_, 0, s, args); break; \
+        case 2: if (multi_) hipLaunchKernelGGL((KERNEL<2, kW, true>), grid_, block_, 0, s, args); \
+                else hipLaunchKernelGGL((KERNEL<2, kW, false>), grid_, block_, 0, s, args); break; \
+        case 4: if (multi_) hipLaunchKernelGGL((KERNEL<4, kW, true>), grid_, block_, 0, s, args); \
+                else hipLaunchKernelGGL((KERNEL<4, kW, false>), grid_, block_, 0, s, args); break; \
+        case 8: if (multi_) hipLaunchKernelGGL((KERNEL<8, kW, true>), grid_, block_, 0, s, args); \
+                else hipLaunchKernelGGL((KERNEL<8, kW, false>), grid_, block_, 0, s, args); break; \
+        default: if (multi_) hipLaunchKernelGGL((KERNEL<16, kW, true>), grid_, block_, 0, s, args); \
+                else hipLaunchKernelGGL((KERNEL<16, kW, false>), grid_, block_, 0, s, args); break; \
+        }                                                                                         \
+    } while (0)
+
+}  // namespace
+
+BlockGeom block_affine_geometry(int64_t B, int64_t T, int64_t d, int64_t k)
+{
+    return make_geom(B, T, d, k, 9, 1, 16);
+}
+
+BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k)
+{
+    return make_geom(B, T, d, k, 16, 8, 8);
+}
+
+hipError_t launch_block_affine_fwd(const BlockGeom &g, const float *A, const float *b,
+                                   const float *h0, float *h, void *ws, uint32_t tag, hipStream_t s)
+{
+    BlkArgs a = base_args(g, ws, tag, false);
+    a.A = A; a.x = b; a.h0 = h0; a.out = h;
+    MGS_BLOCK_LAUNCH(baffine_fwd_kernel, g, a, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_affine_bwd(const BlockGeom &g, const float *A, const float *h0,
+                                   const float *h, const float *dh, float *dA, float *db,
+                                   float *dh0, void *ws, uint32_t tag, hipStream_t s)
+{
+    BlkArgs a = base_args(g, ws, tag, true);
+    a.A = A; a.x = h; a.y = dh; a.h0 = h0; a.out = dA; a.out2 = db; a.out3 = dh0;
+    MGS_BLOCK_LAUNCH(baffine_bwd_kernel, g, a, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_matrix_fwd(const BlockGeom &g, const float *A, float *P, void *ws,
+                                   uint32_t tag, hipStream_t s)
+{
+    BlkArgs a = base_args(g, ws, tag, false);
+    a.A = A; a.out = P;
+    MGS_BLOCK_LAUNCH(bmatrix_fwd_kernel, g, a, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const float *P,
+                                   const float *dP, float *dA, void *ws, uint32_t tag,
+                                   hipStream_t s)
+{
+    BlkArgs a = base_args(g, ws, tag, true);
+    a.A = A; a.x = P; a.y = dP; a.out = dA;
+    MGS_BLOCK_LAUNCH(bmatrix_bwd_kernel, g, a, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    const int threads = 256;
+    const int64_t blocks = (n + threads - 1) / threads;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, s, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace mgs

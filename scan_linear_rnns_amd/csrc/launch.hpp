@@ -1,0 +1,72 @@
+// launch.hpp -- host-side interface between the C ABI (mgs_api.cpp) and the
+// kernel translation units.  Geometry (tiling of T and of the chains) and the
+// workspace layout are decided here once per shape, so the forward and the
+// backward of one op always agree on both.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mgs {
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// ---------------------------------------------------------------- log scan
+struct LogGeom {
+    int64_t S;      // chains = B*d
+    int T, d;
+    int CHW;        // chains per wave row
+    int W;          // waves per workgroup
+    int C;          // steps per lane
+    int TT;         // steps per tile
+    int nT;         // tiles along T
+    int nCG;        // chain groups
+    int nTiles;     // nT * nCG
+    // workspace layout (byte offsets)
+    size_t off_fagg_a, off_fagg_h, off_fincl, off_carry, off_bagg_p, off_bagg_w, off_bincl, bytes;
+};
+
+LogGeom log_geometry(int64_t B, int64_t T, int64_t d);
+
+hipError_t launch_log_fwd(const LogGeom &g, const float *la, const float *lb, const float *lh0,
+                          float *h, void *ws, uint32_t tag, hipStream_t s);
+hipError_t launch_log_bwd(const LogGeom &g, const float *la, const float *lb, const float *lh0,
+                          const float *dh, float *dla, float *dlb, float *dlh0, void *ws,
+                          uint32_t tag, hipStream_t s);
+
+// ------------------------------------------------------------- block scans
+struct BlockGeom {
+    int64_t nchain; // B * d/k
+    int T, d, k, nb;
+    int G;          // chains per wave (64 / k)
+    int C;          // steps per lane group
+    int W;          // waves (chunks) per workgroup
+    int TT;         // steps per tile
+    int nT;         // tiles along T
+    int nCG;        // chain groups (of G chains)
+    int nTiles;
+    size_t off_agg, off_incl, bytes;  // look-back payload (tagged words)
+    int agg_words;  // tagged words per chain per tile in the aggregate
+    int incl_words; // tagged words per chain per tile in the inclusive prefix
+};
+
+BlockGeom block_affine_geometry(int64_t B, int64_t T, int64_t d, int64_t k);
+BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k);
+
+hipError_t launch_block_affine_fwd(const BlockGeom &g, const float *A, const float *b,
+                                   const float *h0, float *h, void *ws, uint32_t tag,
+                                   hipStream_t s);
+hipError_t launch_block_affine_bwd(const BlockGeom &g, const float *A, const float *h0,
+                                   const float *h, const float *dh, float *dA, float *db,
+                                   float *dh0, void *ws, uint32_t tag, hipStream_t s);
+hipError_t launch_block_matrix_fwd(const BlockGeom &g, const float *A, float *P, void *ws,
+                                   uint32_t tag, hipStream_t s);
+hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const float *P,
+                                   const float *dP, float *dA, void *ws, uint32_t tag,
+                                   hipStream_t s);
+
+// zero-fill of n floats (used for gradients of an empty sequence)
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
+
+}  // namespace mgs

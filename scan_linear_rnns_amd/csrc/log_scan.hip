@@ -1,0 +1,471 @@
+// log_scan.hip -- log-space minGRU scan, forward and fused backward, for gfx950.
+//
+// The op (minGRU home page, introduction; "Triton on GPU", section "What you
+// gain (and where you don't)", parallel_scan_log): h_t = a_t h_{t-1} + b_t per
+// chain (b, c), inputs log a, log b, log h0, evaluated in log space after
+// Heinsen (arXiv:2311.06281).
+//
+// Work decomposition (same for forward and backward):
+//   chain   = (b, c), flattened as b*d + c; CHW consecutive chains per wave row
+//             so each per-step load/store of a wave covers CHW*4 contiguous bytes
+//             per row;
+//   chunk   = C consecutive steps of one chain, scanned sequentially in the
+//             registers of one lane;
+//   tile    = one workgroup: W waves x (64/CHW) chunks = NCH chunks = TT steps
+//             of CHW chains.  Chunk aggregates meet in LDS;
+//   T-tiles = when T > TT, the tiles of one chain group pass their carries by
+//             single-pass decoupled look-back (tagged words, tickets; see
+//             device.hpp).
+//
+// Forward state per chunk is the pair (LA, LH) = (sum of log2 a, log2 of the
+// chunk's own output from a zero start); pairs compose with
+//   (LA1, LH1) then (LA2, LH2) = (LA1 + LA2, lae2(LA2 + LH1, LH2)),
+// lae2(x, y) = log2(2^x + 2^y).  Everything is re-based at the chunk start,
+// so no running sum of log a ever grows with T (a single global cumulative
+// sum of log a would lose fp32 digits at long T).  Internally the kernels use
+// base 2 so that exp2/log2 map to the hardware's native transcendentals.
+//
+// The backward recomputes h (linear space, from each tile's carried-in state
+// that the forward left in the workspace) and runs the reverse scan of
+// w_t = a_t g_t with g_t = dh_t + w_{t+1}; per chunk [s, e] the reverse map
+// is w_s = W + P w_{e+1} with P = prod a_t, composed the same way.
+#include <hip/hip_runtime.h>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace mgs {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kInf = __builtin_inff();
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+// log2(2^x + 2^y).  Exact for -inf operands (returns the other one, or -inf
+// for both); NaN propagates.
+__device__ __forceinline__ float lae2(float x, float y)
+{
+    const bool xg = x > y;
+    const float m = xg ? x : y;
+    const float n = xg ? y : x;
+    const float r = m + lg2(1.0f + ex2(n - m));
+    return (m == -kInf || m == kInf) ? m : r;
+}
+
+struct LogFwdArgs {
+    const float *la, *lb, *lh0;
+    float *h;                       // nullptr: carries only (used by the backward)
+    int64_t S;
+    int T, d, nCG, nT, nTiles;
+    uint32_t *ticket, *err;
+    uint64_t *agg_a, *agg_h, *incl; // tagged look-back words, [tile][CHW]
+    float *carry;                   // log2 h at each tile start, [tile][CHW]
+    uint32_t tag;
+};
+
+struct LogBwdArgs {
+    const float *la, *lb, *lh0, *dh;
+    float *dla, *dlb, *dlh0;
+    int64_t S;
+    int T, d, nCG, nT, nTiles;
+    uint32_t *ticket, *err;
+    uint64_t *agg_p, *agg_w, *incl;
+    const float *carry;
+    uint32_t tag;
+};
+
+template <int CHW, int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
+{
+    constexpr int SUB = 64 / CHW;
+    constexpr int NCH = W * SUB;
+    constexpr int TT = NCH * C;
+    __shared__ float sLA[NCH][CHW];
+    __shared__ float sLH[NCH][CHW];
+    __shared__ float sCarry[CHW];
+    __shared__ uint32_t sTicket;
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int ch = lane % CHW;
+    const int q = wv * SUB + lane / CHW;
+
+    int tile;
+    if constexpr (MULTI)
+        tile = static_cast<int>(take_ticket(a.ticket, a.nTiles, a.err, &sTicket));
+    else
+        tile = blockIdx.x;
+    const int j = tile / a.nCG;              // T-tile (tickets run T-major)
+    const int cg = tile - j * a.nCG;
+
+    const int64_t chain = static_cast<int64_t>(cg) * CHW + ch;
+    const bool cv = chain < a.S;
+    const int64_t cc = cv ? chain : 0;
+    const int64_t bb = cc / a.d;
+    const int64_t base = bb * a.T * a.d + (cc - bb * a.d);
+    const int t0 = j * TT + q * C;
+
+    float x[C], y[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = t0 + i;
+        const bool v = cv && t < a.T;
+        const int64_t off = base + static_cast<int64_t>(t) * a.d;
+        x[i] = v ? a.la[off] * kLog2e : 0.0f;       // identity step: a = 1, b = 0
+        y[i] = v ? a.lb[off] * kLog2e : -kInf;
+    }
+
+    // chunk-local pair scan from the identity (0, -inf)
+    float pA[C], pH[C];
+    float LA = 0.0f, LH = -kInf;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        LH = lae2(x[i] + LH, y[i]);
+        LA += x[i];
+        pA[i] = LA;
+        pH[i] = LH;
+    }
+    sLA[q][ch] = LA;
+    sLH[q][ch] = LH;
+    __syncthreads();
+
+    float carry;
+    if constexpr (MULTI) {
+        if (threadIdx.x < CHW) {
+            float TA = 0.0f, TH = -kInf;   // tile aggregate
+#pragma unroll
+            for (int p = 0; p < NCH; ++p) {
+                TH = lae2(sLA[p][ch] + TH, sLH[p][ch]);
+                TA += sLA[p][ch];
+            }
+            const size_t slot = static_cast<size_t>(tile) * CHW + ch;
+            if (j > 0 && j < a.nT - 1) {
+                tagged_store(&a.agg_a[slot], a.tag, TA);
+                tagged_store(&a.agg_h[slot], a.tag, TH);
+            }
+            const float lh0 = cv ? a.lh0[chain] * kLog2e : -kInf;
+            float cin = lh0;
+            if (j > 0) {
+                // walk back: acc composes the aggregates of tiles p+1 .. j-1
+                float accA = 0.0f, accH = -kInf, basev = lh0;
+                for (int p = j - 1; p >= 0; --p) {
+                    const size_t ps = (static_cast<size_t>(p) * a.nCG + cg) * CHW + ch;
+                    bool have = false, moved = false;
+                    for (uint32_t spin = 0;; ++spin) {
+                        uint64_t w;
+                        if (poll(&a.incl[ps], a.tag, w)) {
+                            basev = tag_value(w);
+                            have = true;
+                            break;
+                        }
+                        if (p > 0) {
+                            uint64_t wa, wh;
+                            if (poll(&a.agg_a[ps], a.tag, wa) && poll(&a.agg_h[ps], a.tag, wh)) {
+                                accH = lae2(accA + tag_value(wh), accH);
+                                accA += tag_value(wa);
+                                moved = true;
+                                break;
+                            }
+                        }
+                        if (spin >= kSpinLimit) {
+                            raise_error(a.err, kErrSpin);
+                            break;
+                        }
+                        backoff();
+                    }
+                    if (have || !moved) break;
+                }
+                cin = lae2(accA + basev, accH);
+            }
+            if (j < a.nT - 1)
+                tagged_store(&a.incl[slot], a.tag, lae2(TA + cin, TH));
+            a.carry[slot] = cin;
+            sCarry[ch] = cin;
+        }
+        __syncthreads();
+        carry = sCarry[ch];
+    } else {
+        carry = cv ? a.lh0[chain] * kLog2e : -kInf;
+    }
+
+    if (a.h == nullptr) return;
+
+    // carry into this lane's chunk, then the fix-up in linear space:
+    // h_t = 2^(LA_t + carry) + 2^(LH_t)
+    float cq = carry;
+    for (int p = 0; p < q; ++p) cq = lae2(sLA[p][ch] + cq, sLH[p][ch]);
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = t0 + i;
+        if (cv && t < a.T) a.h[base + static_cast<int64_t>(t) * a.d] = ex2(pA[i] + cq) + ex2(pH[i]);
+    }
+}
+
+template <int CHW, int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
+{
+    constexpr int SUB = 64 / CHW;
+    constexpr int NCH = W * SUB;
+    constexpr int TT = NCH * C;
+    __shared__ float sA[NCH][CHW];   // forward: prod a over the chunk
+    __shared__ float sH[NCH][CHW];   // forward: chunk output from a zero start
+    __shared__ float sP[NCH][CHW];   // reverse: prod a over the chunk
+    __shared__ float sW[NCH][CHW];   // reverse: w at the chunk start from a zero carry
+    __shared__ float sCarry[CHW];
+    __shared__ uint32_t sTicket;
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int ch = lane % CHW;
+    const int q = wv * SUB + lane / CHW;
+
+    int tile;
+    if constexpr (MULTI)
+        tile = static_cast<int>(take_ticket(a.ticket, a.nTiles, a.err, &sTicket));
+    else
+        tile = blockIdx.x;
+    const int jr = tile / a.nCG;             // tickets run from the last T-tile back
+    const int cg = tile - jr * a.nCG;
+    const int j = a.nT - 1 - jr;
+    const int ftile = j * a.nCG + cg;        // the forward's index of this tile
+
+    const int64_t chain = static_cast<int64_t>(cg) * CHW + ch;
+    const bool cv = chain < a.S;
+    const int64_t cc = cv ? chain : 0;
+    const int64_t bb = cc / a.d;
+    const int64_t base = bb * a.T * a.d + (cc - bb * a.d);
+    const int t0 = j * TT + q * C;
+
+    float av[C], bv[C], gv[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = t0 + i;
+        const bool v = cv && t < a.T;
+        const int64_t off = base + static_cast<int64_t>(t) * a.d;
+        av[i] = v ? ex2(a.la[off] * kLog2e) : 1.0f;
+        bv[i] = v ? ex2(a.lb[off] * kLog2e) : 0.0f;
+        gv[i] = v ? a.dh[off] : 0.0f;
+    }
+
+    // forward recompute, chunk-local from a zero start
+    float pA[C], pH[C];
+    float A = 1.0f, H = 0.0f;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        H = av[i] * H + bv[i];
+        A *= av[i];
+        pA[i] = A;
+        pH[i] = H;
+    }
+    // reverse scan, chunk-local from a zero carry
+    float wl = 0.0f;
+#pragma unroll
+    for (int i = C - 1; i >= 0; --i) wl = av[i] * (gv[i] + wl);
+    sA[q][ch] = A;
+    sH[q][ch] = H;
+    sP[q][ch] = A;
+    sW[q][ch] = wl;
+
+    // state entering the tile: h0 for the first tile, else the forward's carry
+    float hin;
+    if (j == 0)
+        hin = cv ? ex2(a.lh0[chain] * kLog2e) : 0.0f;
+    else
+        hin = ex2(a.carry[static_cast<size_t>(ftile) * CHW + ch]);
+    __syncthreads();
+
+    float wcarry;
+    if constexpr (MULTI) {
+        if (threadIdx.x < CHW) {
+            float TP = 1.0f, TW = 0.0f;   // tile aggregate, w_s = TW + TP * w_{e+1}
+#pragma unroll
+            for (int p = NCH - 1; p >= 0; --p) {
+                TW = sW[p][ch] + sP[p][ch] * TW;
+                TP = sP[p][ch] * TP;
+            }
+            const size_t slot = static_cast<size_t>(ftile) * CHW + ch;
+            if (j > 0 && j < a.nT - 1) {
+                tagged_store(&a.agg_p[slot], a.tag, TP);
+                tagged_store(&a.agg_w[slot], a.tag, TW);
+            }
+            float cin = 0.0f;
+            if (j < a.nT - 1) {
+                // walk forward over the later tiles: acc composes tiles j+1 .. p-1
+                float accP = 1.0f, accW = 0.0f, basev = 0.0f;
+                for (int p = j + 1; p < a.nT; ++p) {
+                    const size_t ps = (static_cast<size_t>(p) * a.nCG + cg) * CHW + ch;
+                    bool have = false, moved = false;
+                    for (uint32_t spin = 0;; ++spin) {
+                        uint64_t w;
+                        if (poll(&a.incl[ps], a.tag, w)) {
+                            basev = tag_value(w);
+                            have = true;
+                            break;
+                        }
+                        if (p < a.nT - 1) {
+                            uint64_t wp, ww;
+                            if (poll(&a.agg_p[ps], a.tag, wp) && poll(&a.agg_w[ps], a.tag, ww)) {
+                                accW = accW + accP * tag_value(ww);
+                                accP = accP * tag_value(wp);
+                                moved = true;
+                                break;
+                            }
+                        }
+                        if (spin >= kSpinLimit) {
+                            raise_error(a.err, kErrSpin);
+                            break;
+                        }
+                        backoff();
+                    }
+                    if (have || !moved) break;
+                }
+                cin = accW + accP * basev;
+            }
+            if (j > 0) tagged_store(&a.incl[slot], a.tag, TW + TP * cin);
+            sCarry[ch] = cin;
+        }
+        __syncthreads();
+        wcarry = sCarry[ch];
+    } else {
+        wcarry = 0.0f;
+    }
+
+    // state entering this chunk (forward) and w entering it from the right
+    float hc = hin;
+    for (int p = 0; p < q; ++p) hc = sA[p][ch] * hc + sH[p][ch];
+    float wc = wcarry;
+    for (int p = NCH - 1; p > q; --p) wc = sW[p][ch] + sP[p][ch] * wc;
+
+#pragma unroll
+    for (int i = C - 1; i >= 0; --i) {
+        const float hprev = (i == 0) ? hc : pA[i - 1] * hc + pH[i - 1];
+        const float g = gv[i] + wc;
+        const float ag = av[i] * g;
+        wc = ag;
+        const int t = t0 + i;
+        if (cv && t < a.T) {
+            const int64_t off = base + static_cast<int64_t>(t) * a.d;
+            a.dla[off] = ag * hprev;
+            a.dlb[off] = g * bv[i];
+        }
+    }
+    if (cv && j == 0 && q == 0) a.dlh0[chain] = wc * hin;   // g_1 a_1 h_0
+}
+
+// ------------------------------------------------------------ host side
+
+constexpr int kCHW = 32;
+constexpr int kW = 4;
+
+template <int C>
+hipError_t launch_fwd_c(const LogGeom &g, const LogFwdArgs &args, hipStream_t s)
+{
+    const dim3 grid(g.nTiles), block(64 * kW);
+    if (g.nT > 1)
+        hipLaunchKernelGGL((log_fwd_kernel<kCHW, C, kW, true>), grid, block, 0, s, args);
+    else
+        hipLaunchKernelGGL((log_fwd_kernel<kCHW, C, kW, false>), grid, block, 0, s, args);
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t launch_bwd_c(const LogGeom &g, const LogBwdArgs &args, hipStream_t s)
+{
+    const dim3 grid(g.nTiles), block(64 * kW);
+    if (g.nT > 1)
+        hipLaunchKernelGGL((log_bwd_kernel<kCHW, C, kW, true>), grid, block, 0, s, args);
+    else
+        hipLaunchKernelGGL((log_bwd_kernel<kCHW, C, kW, false>), grid, block, 0, s, args);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+LogGeom log_geometry(int64_t B, int64_t T, int64_t d)
+{
+    LogGeom g{};
+    g.S = B * d;
+    g.T = static_cast<int>(T);
+    g.d = static_cast<int>(d);
+    g.CHW = kCHW;
+    g.W = kW;
+    const int nch = kW * (64 / kCHW);
+    int C = 1;
+    while (C < 16 && static_cast<int64_t>(nch) * C < T) C *= 2;
+    g.C = C;
+    g.TT = nch * C;
+    g.nT = static_cast<int>((T + g.TT - 1) / g.TT);
+    g.nCG = static_cast<int>((g.S + kCHW - 1) / kCHW);
+    g.nTiles = g.nT * g.nCG;
+    const size_t slots = static_cast<size_t>(g.nTiles) * kCHW;
+    size_t off = sizeof(WsHeader);
+    if (g.nT > 1) {
+        g.off_fagg_a = off; off = align256(off + slots * 8);
+        g.off_fagg_h = off; off = align256(off + slots * 8);
+        g.off_fincl = off;  off = align256(off + slots * 8);
+        g.off_carry = off;  off = align256(off + slots * 4);
+        g.off_bagg_p = off; off = align256(off + slots * 8);
+        g.off_bagg_w = off; off = align256(off + slots * 8);
+        g.off_bincl = off;  off = align256(off + slots * 8);
+    }
+    g.bytes = off;
+    return g;
+}
+
+hipError_t launch_log_fwd(const LogGeom &g, const float *la, const float *lb, const float *lh0,
+                          float *h, void *ws, uint32_t tag, hipStream_t s)
+{
+    char *w = static_cast<char *>(ws);
+    WsHeader *hd = reinterpret_cast<WsHeader *>(w);
+    LogFwdArgs a{};
+    a.la = la; a.lb = lb; a.lh0 = lh0; a.h = h;
+    a.S = g.S; a.T = g.T; a.d = g.d; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
+    a.ticket = &hd->ticket_fwd;
+    a.err = &hd->err;
+    a.tag = tag;
+    if (g.nT > 1) {
+        a.agg_a = reinterpret_cast<uint64_t *>(w + g.off_fagg_a);
+        a.agg_h = reinterpret_cast<uint64_t *>(w + g.off_fagg_h);
+        a.incl = reinterpret_cast<uint64_t *>(w + g.off_fincl);
+        a.carry = reinterpret_cast<float *>(w + g.off_carry);
+    }
+    switch (g.C) {
+    case 1: return launch_fwd_c<1>(g, a, s);
+    case 2: return launch_fwd_c<2>(g, a, s);
+    case 4: return launch_fwd_c<4>(g, a, s);
+    case 8: return launch_fwd_c<8>(g, a, s);
+    default: return launch_fwd_c<16>(g, a, s);
+    }
+}
+
+hipError_t launch_log_bwd(const LogGeom &g, const float *la, const float *lb, const float *lh0,
+                          const float *dh, float *dla, float *dlb, float *dlh0, void *ws,
+                          uint32_t tag, hipStream_t s)
+{
+    char *w = static_cast<char *>(ws);
+    WsHeader *hd = reinterpret_cast<WsHeader *>(w);
+    LogBwdArgs a{};
+    a.la = la; a.lb = lb; a.lh0 = lh0; a.dh = dh;
+    a.dla = dla; a.dlb = dlb; a.dlh0 = dlh0;
+    a.S = g.S; a.T = g.T; a.d = g.d; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
+    a.ticket = &hd->ticket_bwd;
+    a.err = &hd->err;
+    a.tag = tag;
+    if (g.nT > 1) {
+        a.agg_p = reinterpret_cast<uint64_t *>(w + g.off_bagg_p);
+        a.agg_w = reinterpret_cast<uint64_t *>(w + g.off_bagg_w);
+        a.incl = reinterpret_cast<uint64_t *>(w + g.off_bincl);
+        a.carry = reinterpret_cast<const float *>(w + g.off_carry);
+    }
+    switch (g.C) {
+    case 1: return launch_bwd_c<1>(g, a, s);
+    case 2: return launch_bwd_c<2>(g, a, s);
+    case 4: return launch_bwd_c<4>(g, a, s);
+    case 8: return launch_bwd_c<8>(g, a, s);
+    default: return launch_bwd_c<16>(g, a, s);
+    }
+}
+
+}  // namespace mgs

@@ -1,0 +1,294 @@
+// mgs_api.cpp -- the C ABI declared in include/mgs.h: argument validation,
+// workspace sizing and kernel dispatch.  Validation happens before any HIP
+// call, so the error paths can be exercised on a host without a GPU.
+#include "mgs.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+std::atomic<uint32_t> g_tag{0};
+
+// A fresh, non-zero tag per launch: tagged look-back words left by earlier
+// calls (or by a zero-filled workspace) never match it.
+uint32_t next_tag()
+{
+    uint32_t t = g_tag.fetch_add(1, std::memory_order_relaxed) + 1;
+    if (t == 0) t = g_tag.fetch_add(1, std::memory_order_relaxed) + 1;
+    return t;
+}
+
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+
+mgs_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return MGS_OK;
+    g_last_hip_error = static_cast<int>(e);
+    return MGS_ERR_HIP;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    const void *p;
+    size_t bytes;
+};
+
+bool overlaps(Range a, Range b)
+{
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// every output must be disjoint from every input and from the other outputs
+bool any_alias(const Range *in, int nin, const Range *out, int nout)
+{
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j)
+            if (overlaps(out[i], in[j])) return true;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlaps(out[i], out[j])) return true;
+    }
+    return false;
+}
+
+bool all_aligned(const Range *r, int n)
+{
+    for (int i = 0; i < n; ++i)
+        if (r[i].p && !aligned16(r[i].p)) return false;
+    return true;
+}
+
+mgs_status check_sizes(int64_t B, int64_t T, int64_t d)
+{
+    if (B < 0 || T < 0 || d < 0) return MGS_ERR_INVALID_VALUE;
+    return MGS_OK;
+}
+
+mgs_status check_workspace(const void *ws, size_t have, size_t need)
+{
+    if (!ws) return MGS_ERR_WORKSPACE;
+    if (have < need) return MGS_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MGS_ERR_INVALID_VALUE;
+    return MGS_OK;
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int mgs_version(void) { return 100; }
+
+const char *mgs_status_string(int status)
+{
+    switch (status) {
+    case MGS_OK: return "MGS_OK: success";
+    case MGS_ERR_INVALID_VALUE: return "MGS_ERR_INVALID_VALUE: null pointer, bad size, misalignment or aliasing";
+    case MGS_ERR_UNSUPPORTED: return "MGS_ERR_UNSUPPORTED: outside the supported envelope";
+    case MGS_ERR_WORKSPACE: return "MGS_ERR_WORKSPACE: workspace missing or too small";
+    case MGS_ERR_HIP: return "MGS_ERR_HIP: HIP runtime error (see mgs_last_hip_error)";
+    default: return "unknown mgs_status";
+    }
+}
+
+int mgs_last_hip_error(void) { return g_last_hip_error; }
+
+mgs_status mgs_workspace_check(void *workspace, void *stream, int *flags)
+{
+    if (!workspace || !flags) return MGS_ERR_INVALID_VALUE;
+    hipStream_t s = as_stream(stream);
+    mgs::WsHeader *hd = static_cast<mgs::WsHeader *>(workspace);
+    uint32_t v = 0;
+    hipError_t e = hipMemcpyAsync(&v, &hd->err, sizeof(v), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e);
+    *flags = static_cast<int>(v);
+    if (v) {
+        const uint32_t zero = 0;
+        e = hipMemcpyAsync(&hd->err, &zero, sizeof(zero), hipMemcpyHostToDevice, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return MGS_OK;
+}
+
+// ------------------------------------------------------------ log scan
+
+mgs_status mgs_scan_log_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes)
+{
+    if (!bytes) return MGS_ERR_INVALID_VALUE;
+    if (mgs_status st = check_sizes(B, T, d)) return st;
+    if (B * T * d > kMaxElems || B * d > kMaxElems) return MGS_ERR_UNSUPPORTED;
+    if (B == 0 || T == 0 || d == 0) { *bytes = sizeof(mgs::WsHeader); return MGS_OK; }
+    *bytes = mgs::log_geometry(B, T, d).bytes;
+    return MGS_OK;
+}
+
+mgs_status mgs_scan_log_fwd(const float *log_a, const float *log_b, const float *log_h0, float *h,
+                            int64_t B, int64_t T, int64_t d, void *workspace,
+                            size_t workspace_bytes, void *stream)
+{
+    if (mgs_status st = check_sizes(B, T, d)) return st;
+    if (B * T * d > kMaxElems || B * d > kMaxElems) return MGS_ERR_UNSUPPORTED;
+    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
+    if (n > 0 && (!log_a || !log_b || !h)) return MGS_ERR_INVALID_VALUE;
+    if (s0 > 0 && !log_h0) return MGS_ERR_INVALID_VALUE;
+    const Range in[] = {{log_a, n}, {log_b, n}, {log_h0, s0}};
+    const Range out[] = {{h, n}};
+    if (!all_aligned(in, 3) || !all_aligned(out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (any_alias(in, 3, out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (n == 0) return MGS_OK;
+    const mgs::LogGeom g = mgs::log_geometry(B, T, d);
+    if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
+    return hip_status(mgs::launch_log_fwd(g, log_a, log_b, log_h0, h, workspace, next_tag(),
+                                          as_stream(stream)));
+}
+
+mgs_status mgs_scan_log_bwd(const float *log_a, const float *log_b, const float *log_h0,
+                            const float *dh, float *dlog_a, float *dlog_b, float *dlog_h0,
+                            int64_t B, int64_t T, int64_t d, void *workspace,
+                            size_t workspace_bytes, int fwd_state_valid, void *stream)
+{
+    if (mgs_status st = check_sizes(B, T, d)) return st;
+    if (B * T * d > kMaxElems || B * d > kMaxElems) return MGS_ERR_UNSUPPORTED;
+    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
+    if (n > 0 && (!log_a || !log_b || !dh || !dlog_a || !dlog_b)) return MGS_ERR_INVALID_VALUE;
+    if (s0 > 0 && (!log_h0 || !dlog_h0)) return MGS_ERR_INVALID_VALUE;
+    const Range in[] = {{log_a, n}, {log_b, n}, {log_h0, s0}, {dh, n}};
+    const Range out[] = {{dlog_a, n}, {dlog_b, n}, {dlog_h0, s0}};
+    if (!all_aligned(in, 4) || !all_aligned(out, 3)) return MGS_ERR_INVALID_VALUE;
+    if (any_alias(in, 4, out, 3)) return MGS_ERR_INVALID_VALUE;
+    if (s0 == 0) return MGS_OK;
+    hipStream_t s = as_stream(stream);
+    if (T == 0)  // L does not depend on h0 when there are no steps
+        return hip_status(mgs::launch_fill_zero(dlog_h0, B * d, s));
+    const mgs::LogGeom g = mgs::log_geometry(B, T, d);
+    if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
+    if (g.nT > 1 && !fwd_state_valid) {
+        hipError_t e = mgs::launch_log_fwd(g, log_a, log_b, log_h0, nullptr, workspace, next_tag(), s);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return hip_status(mgs::launch_log_bwd(g, log_a, log_b, log_h0, dh, dlog_a, dlog_b, dlog_h0,
+                                          workspace, next_tag(), s));
+}
+
+// ---------------------------------------------------------- block scans
+
+static mgs_status check_block_sizes(int64_t B, int64_t T, int64_t d, int64_t k)
+{
+    if (B < 0 || T < 0 || d < 0 || k <= 0) return MGS_ERR_INVALID_VALUE;
+    if (d % k != 0) return MGS_ERR_INVALID_VALUE;
+    if (k != 8) return MGS_ERR_UNSUPPORTED;
+    if (B * T * d * k > kMaxElems) return MGS_ERR_UNSUPPORTED;
+    return MGS_OK;
+}
+
+mgs_status mgs_block_affine_scan_workspace_size(int64_t B, int64_t T, int64_t d, int64_t k,
+                                                size_t *bytes)
+{
+    if (!bytes) return MGS_ERR_INVALID_VALUE;
+    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
+    if (B == 0 || T == 0 || d == 0) { *bytes = sizeof(mgs::WsHeader); return MGS_OK; }
+    *bytes = mgs::block_affine_geometry(B, T, d, k).bytes;
+    return MGS_OK;
+}
+
+mgs_status mgs_block_affine_scan_fwd(const float *A, const float *b, const float *h0, float *h,
+                                     int64_t B, int64_t T, int64_t d, int64_t k, void *workspace,
+                                     size_t workspace_bytes, void *stream)
+{
+    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
+    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
+    const size_t na = n * static_cast<size_t>(k);
+    if (n > 0 && (!A || !b || !h)) return MGS_ERR_INVALID_VALUE;
+    const Range in[] = {{A, na}, {b, n}, {h0, s0}};
+    const Range out[] = {{h, n}};
+    if (!all_aligned(in, 3) || !all_aligned(out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (any_alias(in, 3, out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (n == 0) return MGS_OK;
+    const mgs::BlockGeom g = mgs::block_affine_geometry(B, T, d, k);
+    if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
+    return hip_status(mgs::launch_block_affine_fwd(g, A, b, h0, h, workspace, next_tag(),
+                                                   as_stream(stream)));
+}
+
+mgs_status mgs_block_affine_scan_bwd(const float *A, const float *b, const float *h0,
+                                     const float *h, const float *dh, float *dA, float *db,
+                                     float *dh0, int64_t B, int64_t T, int64_t d, int64_t k,
+                                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
+    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
+    const size_t na = n * static_cast<size_t>(k);
+    if (n > 0 && (!A || !h || !dh || !dA || !db)) return MGS_ERR_INVALID_VALUE;
+    if (s0 > 0 && !dh0) return MGS_ERR_INVALID_VALUE;
+    const Range in[] = {{A, na}, {b, n}, {h0, s0}, {h, n}, {dh, n}};
+    const Range out[] = {{dA, na}, {db, n}, {dh0, s0}};
+    if (!all_aligned(in, 5) || !all_aligned(out, 3)) return MGS_ERR_INVALID_VALUE;
+    if (any_alias(in, 5, out, 3)) return MGS_ERR_INVALID_VALUE;
+    if (s0 == 0) return MGS_OK;
+    hipStream_t s = as_stream(stream);
+    if (T == 0) return hip_status(mgs::launch_fill_zero(dh0, B * d, s));
+    const mgs::BlockGeom g = mgs::block_affine_geometry(B, T, d, k);
+    if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
+    return hip_status(mgs::launch_block_affine_bwd(g, A, h0, h, dh, dA, db, dh0, workspace,
+                                                   next_tag(), s));
+}
+
+mgs_status mgs_block_matrix_scan_workspace_size(int64_t B, int64_t T, int64_t d, int64_t k,
+                                                size_t *bytes)
+{
+    if (!bytes) return MGS_ERR_INVALID_VALUE;
+    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
+    if (B == 0 || T == 0 || d == 0) { *bytes = sizeof(mgs::WsHeader); return MGS_OK; }
+    *bytes = mgs::block_matrix_geometry(B, T, d, k).bytes;
+    return MGS_OK;
+}
+
+mgs_status mgs_block_matrix_scan_fwd(const float *A, float *P, int64_t B, int64_t T, int64_t d,
+                                     int64_t k, void *workspace, size_t workspace_bytes,
+                                     void *stream)
+{
+    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
+    const size_t na = static_cast<size_t>(B * T * d * k) * 4;
+    if (na > 0 && (!A || !P)) return MGS_ERR_INVALID_VALUE;
+    const Range in[] = {{A, na}};
+    const Range out[] = {{P, na}};
+    if (!all_aligned(in, 1) || !all_aligned(out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (any_alias(in, 1, out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (na == 0) return MGS_OK;
+    const mgs::BlockGeom g = mgs::block_matrix_geometry(B, T, d, k);
+    if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
+    return hip_status(mgs::launch_block_matrix_fwd(g, A, P, workspace, next_tag(), as_stream(stream)));
+}
+
+mgs_status mgs_block_matrix_scan_bwd(const float *A, const float *P, const float *dP, float *dA,
+                                     int64_t B, int64_t T, int64_t d, int64_t k, void *workspace,
+                                     size_t workspace_bytes, void *stream)
+{
+    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
+    const size_t na = static_cast<size_t>(B * T * d * k) * 4;
+    if (na > 0 && (!A || !P || !dP || !dA)) return MGS_ERR_INVALID_VALUE;
+    const Range in[] = {{A, na}, {P, na}, {dP, na}};
+    const Range out[] = {{dA, na}};
+    if (!all_aligned(in, 3) || !all_aligned(out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (any_alias(in, 3, out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (na == 0) return MGS_OK;
+    const mgs::BlockGeom g = mgs::block_matrix_geometry(B, T, d, k);
+    if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
+    return hip_status(mgs::launch_block_matrix_bwd(g, A, P, dP, dA, workspace, next_tag(),
+                                                   as_stream(stream)));
+}
+
+}  // extern "C"

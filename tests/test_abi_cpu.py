@@ -1,0 +1,134 @@
+"""C-ABI contract checks that need no GPU.
+
+The library must load on a host without a GPU, export every function that
+include/mgs.h declares, and reject bad arguments with the documented status
+before any HIP call (so these run with fake, never-dereferenced pointers).
+"""
+import ctypes
+import subprocess
+
+import pytest
+
+from scan_linear_rnns_amd import _lib
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+BASE = 0x7F0000000000          # fake, 256-byte aligned device addresses (never dereferenced)
+
+
+def fake(i, off=0):
+    return ctypes.c_void_p(BASE + i * (1 << 32) + off)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _lib.declared_functions()
+    assert len(declared) == 13, declared
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in declared if n not in exported]
+    assert not missing, missing
+    for name in declared:
+        assert hasattr(lib, name)
+        assert name in _lib.SIGNATURES
+
+
+def test_version_and_strings(lib):
+    assert lib.mgs_version() >= 100
+    for s in range(5):
+        assert _lib.status_string(s).startswith(("MGS_OK", "MGS_ERR"))
+    assert "unknown" in _lib.status_string(99)
+    assert lib.mgs_last_hip_error() == 0
+
+
+def _size(lib, fn, *dims):
+    out = ctypes.c_size_t(0)
+    st = getattr(lib, fn)(*dims, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_queries(lib):
+    st, small = _size(lib, "mgs_scan_log_workspace_size", 2, 64, 16)
+    assert st == OK and small >= 256
+    st, big = _size(lib, "mgs_scan_log_workspace_size", 16, 1024, 64)
+    assert st == OK and big > small
+    assert _size(lib, "mgs_scan_log_workspace_size", -1, 4, 4)[0] == INVALID
+    assert lib.mgs_scan_log_workspace_size(2, 3, 4, None) == INVALID
+    assert _size(lib, "mgs_scan_log_workspace_size", 1 << 20, 1 << 10, 1 << 10)[0] == UNSUPPORTED
+    for fn in ("mgs_block_affine_scan_workspace_size", "mgs_block_matrix_scan_workspace_size"):
+        st, b1 = _size(lib, fn, 128, 64, 64, 8)
+        assert st == OK and b1 >= 256
+        st, b2 = _size(lib, fn, 16, 1024, 64, 8)
+        assert st == OK and b2 > 256
+        assert _size(lib, fn, 2, 4, 12, 8)[0] == INVALID       # d % k != 0
+        assert _size(lib, fn, 2, 4, 16, 4)[0] == UNSUPPORTED   # k outside the envelope
+        assert _size(lib, fn, 2, 4, 16, 0)[0] == INVALID
+        assert _size(lib, fn, 1 << 16, 1 << 10, 64, 8)[0] == UNSUPPORTED
+
+
+def test_log_fwd_validation(lib):
+    B, T, d = 2, 8, 16
+    ws = fake(9)
+    args = lambda la=fake(0), lb=fake(1), lh0=fake(2), h=fake(3), B=B, T=T, d=d, ws=ws, nbytes=1 << 20: \
+        lib.mgs_scan_log_fwd(la, lb, lh0, h, B, T, d, ws, nbytes, None)
+    assert args(la=None) == INVALID
+    assert args(h=None) == INVALID
+    assert args(lh0=None) == INVALID
+    assert args(B=-1) == INVALID
+    assert args(h=fake(0)) == INVALID                       # output aliases an input
+    assert args(h=fake(0, 4 * B * T * d - 16)) == INVALID   # partial overlap
+    assert args(lb=fake(1, 4)) == INVALID                   # misaligned
+    assert args(ws=None) == WORKSPACE
+    assert args(nbytes=8) == WORKSPACE
+    assert args(B=0, la=None, lb=None, lh0=None, h=None) == OK   # empty: nothing to do, no HIP call
+    assert args(T=0, la=None, lb=None, h=None) == OK
+
+
+def test_log_bwd_validation(lib):
+    B, T, d = 2, 8, 16
+    call = lambda dla=fake(4), dlh0=fake(6), ws=fake(9), nbytes=1 << 20, B=B: \
+        lib.mgs_scan_log_bwd(fake(0), fake(1), fake(2), fake(3), dla, fake(5), dlh0, B, T, d, ws, nbytes, 1, None)
+    assert call(dla=None) == INVALID
+    assert call(dlh0=None) == INVALID
+    assert call(dla=fake(3)) == INVALID                      # dlog_a aliases dh
+    assert call(dla=fake(5)) == INVALID                      # two outputs overlap
+    assert call(ws=None) == WORKSPACE
+    assert call(nbytes=16) == WORKSPACE
+    assert call(B=-3) == INVALID
+
+
+def test_block_validation(lib):
+    B, T, d, k = 2, 8, 16, 8
+    fwd = lambda A=fake(0), b=fake(1), h0=fake(2), h=fake(3), k=k, d=d, nbytes=1 << 20, ws=fake(9): \
+        lib.mgs_block_affine_scan_fwd(A, b, h0, h, B, T, d, k, ws, nbytes, None)
+    assert fwd(A=None) == INVALID
+    assert fwd(b=None) == INVALID
+    assert fwd(h=fake(1)) == INVALID
+    assert fwd(k=4) == UNSUPPORTED
+    assert fwd(d=12) == INVALID
+    assert fwd(nbytes=0) == WORKSPACE
+    assert fwd(ws=fake(9, 8)) == INVALID                    # misaligned workspace
+    bwd = lambda h=fake(3), dA=fake(5), dh0=fake(7), nbytes=1 << 20: lib.mgs_block_affine_scan_bwd(
+        fake(0), None, None, h, fake(4), dA, fake(6), dh0, B, T, d, k, fake(9), nbytes, None)
+    assert bwd(h=None) == INVALID
+    assert bwd(dA=fake(0)) == INVALID
+    assert bwd(dh0=None) == INVALID
+    assert bwd(nbytes=1) == WORKSPACE
+    mf = lambda P=fake(1), k=k, nbytes=1 << 20: lib.mgs_block_matrix_scan_fwd(fake(0), P, B, T, d, k, fake(9),
+                                                                             nbytes, None)
+    assert mf(P=None) == INVALID
+    assert mf(P=fake(0)) == INVALID
+    assert mf(k=16) == UNSUPPORTED
+    assert mf(nbytes=2) == WORKSPACE
+    mb = lambda P=fake(1), dA=fake(3): lib.mgs_block_matrix_scan_bwd(fake(0), P, fake(2), dA, B, T, d, k,
+                                                                    fake(9), 1 << 20, None)
+    assert mb(P=None) == INVALID
+    assert mb(dA=fake(2)) == INVALID
+
+
+def test_workspace_check_validation(lib):
+    assert lib.mgs_workspace_check(None, None, None) == INVALID

@@ -1,0 +1,271 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every output tensor is compared element by element with the oracle run on the
+same fp32 inputs.  Error measure per tensor (the tolerance rule):
+    err = max_i |x_i - r_i| / max(|r_i|, 1e-3 * max_j |r_j|)
+i.e. relative error with a floor at 1e-3 of the tensor's largest magnitude
+(values that underflow towards zero, such as long cumulative products, are
+judged against the tensor's scale).  Bars: 1e-4 for the log-space scan and
+2e-4 for the block scans (T <= 1024, and the longer edge cases).  Any NaN or
+Inf in an output fails.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synthetic import block_inputs, log_inputs
+
+pytestmark = pytest.mark.gpu
+
+LOG_TOL = 1e-4
+BLOCK_TOL = 2e-4
+
+
+def say(msg):
+    print(f"[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def floored_err(x, r):
+    x = np.asarray(x, np.float64)
+    r = np.asarray(r, np.float64)
+    assert x.shape == r.shape
+    if x.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(x)):
+        return float("inf")
+    scale = np.max(np.abs(r))
+    if scale == 0.0:
+        return float(np.max(np.abs(x)))
+    den = np.maximum(np.abs(r), 1e-3 * scale)
+    return float(np.max(np.abs(x - r) / den))
+
+
+def to_dev(x, dev):
+    import torch
+    return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def ws_clean(ws):
+    import scan_linear_rnns_amd as mgs
+    assert mgs.mgs_workspace_check(ws) == 0, "a look-back wait hit its spin limit"
+
+
+# ------------------------------------------------------------------ log
+
+def run_log(B, T, d, seed, dev, fwd_state_valid=True):
+    import scan_linear_rnns_amd as mgs
+    inp = log_inputs(B, T, d, seed)
+    la, lb, lh0, dh = (to_dev(x, dev) for x in (inp.log_a, inp.log_b, inp.log_h0, inp.dh))
+    h, ws = mgs.mgs_scan_log_fwd(la, lb, lh0)
+    if fwd_state_valid:
+        dla, dlb, dlh0 = mgs.mgs_scan_log_bwd(la, lb, lh0, dh, ws=ws, fwd_state_valid=True)
+    else:
+        ws2 = mgs.workspace(ws.numel(), dev)
+        dla, dlb, dlh0 = mgs.mgs_scan_log_bwd(la, lb, lh0, dh, ws=ws2, fwd_state_valid=False)
+        ws_clean(ws2)
+    ws_clean(ws)
+    out = dict(h=to_np(h), dlog_a=to_np(dla), dlog_b=to_np(dlb), dlog_h0=to_np(dlh0))
+    ref = dict(h=oracle.log_fwd(inp.log_a, inp.log_b, inp.log_h0))
+    ref["dlog_a"], ref["dlog_b"], ref["dlog_h0"] = oracle.log_bwd(inp.log_a, inp.log_b, inp.log_h0, inp.dh)
+    return out, ref
+
+
+LOG_CASES = [
+    ("log_tiny", 2, 64, 16),
+    ("log_lab", 128, 64, 64),
+    ("log_longT", 16, 1024, 64),
+]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("name,B,T,d", LOG_CASES, ids=[c[0] for c in LOG_CASES])
+def test_log_configs(gpu, name, B, T, d, seed):
+    say(f"log {name} B={B} T={T} d={d} seed={seed}")
+    out, ref = run_log(B, T, d, seed, gpu)
+    for key in out:
+        e = floored_err(out[key], ref[key])
+        assert e <= LOG_TOL, (key, e)
+
+
+LOG_EDGES = [(1, 1, 8), (1, 2, 16), (3, 63, 16), (3, 65, 16), (2, 129, 32), (2, 200, 72),
+             (2, 1000, 8), (1, 2048, 40), (5, 7, 1), (4, 300, 100)]
+
+
+@pytest.mark.parametrize("B,T,d", LOG_EDGES)
+def test_log_edges(gpu, B, T, d):
+    say(f"log edge B={B} T={T} d={d}")
+    out, ref = run_log(B, T, d, 5, gpu)
+    for key in out:
+        e = floored_err(out[key], ref[key])
+        assert e <= LOG_TOL, (key, e)
+
+
+@pytest.mark.parametrize("T", [64, 1024])
+def test_log_bwd_without_forward_state(gpu, T):
+    say(f"log bwd recompute-carries T={T}")
+    out, ref = run_log(4, T, 64, 3, gpu, fwd_state_valid=False)
+    for key in out:
+        assert floored_err(out[key], ref[key]) <= LOG_TOL, key
+
+
+def test_log_special_values(gpu):
+    """log h0 = -inf (h0 = 0) and log b = -inf (b = 0) are exact zeros."""
+    import torch
+    import scan_linear_rnns_amd as mgs
+    say("log special values")
+    inp = log_inputs(2, 300, 32, 7)
+    lb = inp.log_b.copy()
+    lb[:, ::3, :5] = -np.inf
+    lh0 = inp.log_h0.copy()
+    lh0[0] = -np.inf
+    la, lbt, lh0t, dh = (to_dev(x, gpu) for x in (inp.log_a, lb, lh0, inp.dh))
+    h, ws = mgs.mgs_scan_log_fwd(la, lbt, lh0t)
+    dla, dlb, dlh0 = mgs.mgs_scan_log_bwd(la, lbt, lh0t, dh, ws=ws, fwd_state_valid=True)
+    ref_h = oracle.log_fwd(inp.log_a, lb, lh0)
+    rdla, rdlb, rdlh0 = oracle.log_bwd(inp.log_a, lb, lh0, inp.dh)
+    assert floored_err(to_np(h), ref_h) <= LOG_TOL
+    assert floored_err(to_np(dla), rdla) <= LOG_TOL
+    assert floored_err(to_np(dlb), rdlb) <= LOG_TOL
+    assert floored_err(to_np(dlh0), rdlh0) <= LOG_TOL
+    assert np.all(to_np(dlb)[:, ::3, :5] == 0.0)
+    assert np.all(to_np(dlh0)[0] == 0.0)
+    torch.cuda.synchronize()
+
+
+def test_log_empty_sequence(gpu):
+    import torch
+    import scan_linear_rnns_amd as mgs
+    say("log T=0")
+    la = torch.empty((3, 0, 8), device=gpu)
+    lh0 = torch.zeros((3, 8), device=gpu)
+    dlh0 = torch.full((3, 8), 7.0, device=gpu)
+    out = (torch.empty((3, 0, 8), device=gpu), torch.empty((3, 0, 8), device=gpu), dlh0)
+    h, ws = mgs.mgs_scan_log_fwd(la, la.clone(), lh0)
+    mgs.mgs_scan_log_bwd(la, la.clone(), lh0, la.clone(), ws=ws, out=out)
+    torch.cuda.synchronize()
+    assert h.shape == (3, 0, 8)
+    assert torch.all(dlh0 == 0)
+
+
+# ---------------------------------------------------------------- blocks
+
+def run_block(B, T, d, seed, dev, *, gate=True, h0="zero", matrix=True):
+    import scan_linear_rnns_amd as mgs
+    inp = block_inputs(B, T, d, k=8, seed=seed, gate=gate, h0=h0, with_dP=matrix)
+    A, b, h0t, dh = (to_dev(x, dev) for x in (inp.A, inp.b, inp.h0, inp.dh))
+    h, ws = mgs.mgs_block_affine_scan_fwd(A, b, h0t)
+    dA, db, dh0 = mgs.mgs_block_affine_scan_bwd(A, b, h0t, h, dh, ws=ws)
+    ws_clean(ws)
+    out = dict(h=to_np(h), dA=to_np(dA), db=to_np(db), dh0=to_np(dh0))
+    ref = dict(h=oracle.block_affine_fwd(inp.A, inp.b, inp.h0, 8))
+    ref["dA"], ref["db"], ref["dh0"] = oracle.block_affine_bwd(inp.A, inp.b, inp.h0, inp.dh, 8)
+    if matrix:
+        dP = to_dev(inp.dP, dev)
+        P, wsm = mgs.mgs_block_matrix_scan_fwd(A)
+        dAm = mgs.mgs_block_matrix_scan_bwd(A, P, dP, ws=wsm)
+        ws_clean(wsm)
+        out["P"], out["dA_matrix"] = to_np(P), to_np(dAm)
+        ref["P"] = oracle.block_matrix_fwd(inp.A, 8)
+        ref["dA_matrix"] = oracle.block_matrix_bwd(inp.A, inp.dP, 8)
+    return out, ref
+
+
+BLOCK_CASES = [
+    ("block_lab", 128, 64, 64),
+    ("block_longT", 16, 1024, 64),
+]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("name,B,T,d", BLOCK_CASES, ids=[c[0] for c in BLOCK_CASES])
+def test_block_configs(gpu, name, B, T, d, seed):
+    say(f"block {name} B={B} T={T} d={d} seed={seed}")
+    out, ref = run_block(B, T, d, seed, gpu)
+    for key in out:
+        e = floored_err(out[key], ref[key])
+        assert e <= BLOCK_TOL, (key, e)
+
+
+BLOCK_EDGES = [(1, 1, 8), (1, 2, 16), (3, 63, 16), (3, 65, 24), (2, 129, 8), (2, 200, 72),
+               (1, 1000, 8), (2, 300, 40), (1, 2048, 8)]
+
+
+@pytest.mark.parametrize("B,T,d", BLOCK_EDGES)
+def test_block_edges(gpu, B, T, d):
+    say(f"block edge B={B} T={T} d={d}")
+    out, ref = run_block(B, T, d, 6, gpu, h0="normal")
+    for key in out:
+        e = floored_err(out[key], ref[key])
+        assert e <= BLOCK_TOL, (key, e)
+
+
+def test_rotation_only_long_T(gpu):
+    """Pure rotations keep P orthogonal, so the long-T product does not decay."""
+    say("block rotation-only T=1024")
+    out, ref = run_block(4, 1024, 64, 9, gpu, gate=False, h0="normal")
+    # P and its gradient stay O(1): the usual floored rule applies.
+    for key in ("P", "dA_matrix"):
+        assert floored_err(out[key], ref[key]) <= BLOCK_TOL, key
+    # Without the gate, h is a random walk (|h| ~ 50 at T = 1024) and small
+    # entries are dominated by the rounding of large partial sums: a plain
+    # sequential fp32 loop scores 9.4e-4 under the floored rule here but
+    # 1.3e-6 normwise, so these outputs are held to a normwise bar.
+    for key in ("h", "dA", "db", "dh0"):
+        x, r = out[key].astype(np.float64), ref[key]
+        assert np.all(np.isfinite(x))
+        assert np.max(np.abs(x - r)) / np.max(np.abs(r)) <= 1e-5, key
+    P = out["P"].astype(np.float64)
+    PtP = np.einsum("btjrc,btjrd->btjcd", P, P)
+    assert np.max(np.abs(PtP - np.eye(8))) < 1e-4
+
+
+def test_determinism(gpu):
+    """Repeated calls give bitwise-identical results (no order-dependent reductions)."""
+    import torch
+    import scan_linear_rnns_amd as mgs
+    say("determinism")
+    inp = log_inputs(16, 1024, 64, 11)
+    la, lb, lh0, dh = (to_dev(x, gpu) for x in (inp.log_a, inp.log_b, inp.log_h0, inp.dh))
+    first = None
+    for _ in range(5):
+        h, ws = mgs.mgs_scan_log_fwd(la, lb, lh0)
+        g = mgs.mgs_scan_log_bwd(la, lb, lh0, dh, ws=ws, fwd_state_valid=True)
+        cur = [h.clone()] + [x.clone() for x in g]
+        if first is None:
+            first = cur
+        else:
+            for a, b in zip(first, cur):
+                assert torch.equal(a, b)
+    binp = block_inputs(16, 1024, 64, seed=12)
+    A, b, dh2, dP = (to_dev(x, gpu) for x in (binp.A, binp.b, binp.dh, binp.dP))
+    firstb = None
+    for _ in range(3):
+        hb, wsb = mgs.mgs_block_affine_scan_fwd(A, b, None)
+        gb = mgs.mgs_block_affine_scan_bwd(A, b, None, hb, dh2, ws=wsb)
+        P, wsm = mgs.mgs_block_matrix_scan_fwd(A)
+        dAm = mgs.mgs_block_matrix_scan_bwd(A, P, dP, ws=wsm)
+        cur = [hb.clone(), P.clone(), dAm.clone()] + [x.clone() for x in gb]
+        if firstb is None:
+            firstb = cur
+        else:
+            for a_, b_ in zip(firstb, cur):
+                assert torch.equal(a_, b_)
+
+
+def test_sequence_continuation(gpu):
+    """scan(T1 + T2) equals scan(T2) started from the last state of scan(T1)."""
+    import scan_linear_rnns_amd as mgs
+    say("sequence continuation")
+    inp = log_inputs(4, 700, 32, 13)
+    la, lb, lh0 = (to_dev(x, gpu) for x in (inp.log_a, inp.log_b, inp.log_h0))
+    h, _ = mgs.mgs_scan_log_fwd(la, lb, lh0)
+    h1, _ = mgs.mgs_scan_log_fwd(la[:, :300].contiguous(), lb[:, :300].contiguous(), lh0)
+    h2, _ = mgs.mgs_scan_log_fwd(la[:, 300:].contiguous(), lb[:, 300:].contiguous(), h1[:, -1].log().contiguous())
+    assert floored_err(to_np(h2), to_np(h)[:, 300:]) <= 1e-5
