@@ -236,15 +236,14 @@ struct BlkArgs {
     const float *A;      // (B,T,nb,8,8)
     const float *x;      // affine: b (fwd) or h (bwd); cumprod bwd: P
     const float *y;      // affine bwd: dh; cumprod bwd: dP
-    const float *h0;     // affine: (B,d) or nullptr
+    const float *h0;     // affine: (B,d), or a zero region of the workspace
     float *out;          // affine fwd: h; affine bwd: dA; cumprod fwd: P; cumprod bwd: dA
     float *out2;         // affine bwd: db
     float *out3;         // affine bwd: dh0
     int64_t nchain;
     int T, d, nb, nCG, nT, nTiles;
-    uint32_t *ticket, *err;
+    WsHeader *hd;
     uint64_t *agg, *incl;
-    uint32_t tag;
 };
 
 struct Tile {
@@ -284,6 +283,18 @@ __device__ __forceinline__ Tile make_tile(const BlkArgs &a, int tile, bool rever
     return t;
 }
 
+__device__ __forceinline__ int clampT(int t, int T) { return t < T ? t : T - 1; }
+
+// h0 entry of this lane.  When the caller passes no h0, a.h0 points at a
+// zero region of the workspace, so the load is unconditional and never sits
+// behind a branch that would force a wait on the loads issued before it.
+// Lanes of chains past the end read chain 0's entry; their results are never
+// stored and their 8-lane groups exchange data only among themselves.
+__device__ __forceinline__ float load_h0(const BlkArgs &a, const Tile &tl)
+{
+    return a.h0[tl.bb * a.d + tl.jb * 8 + tl.v];
+}
+
 // ======================================================= block-affine fwd
 
 template <int C, int W, bool MULTI>
@@ -293,25 +304,33 @@ __global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
     constexpr int AW = 9;   // row of Phi + one entry of u
     __shared__ float sAgg[NCH][32][AW];
     __shared__ float sCarry[32];
-    __shared__ uint32_t sTicket;
+    __shared__ uint32_t sTicket[2];
 
-    const int tile = MULTI ? static_cast<int>(take_ticket(a.ticket, a.nTiles, a.err, &sTicket))
-                           : static_cast<int>(blockIdx.x);
+    int tile = blockIdx.x;
+    uint32_t tag = 0;
+    if constexpr (MULTI) {
+        const TileTicket tk = take_ticket(a.hd, a.nTiles, sTicket);
+        tile = static_cast<int>(tk.tile);
+        tag = tk.tag;
+    }
     const Tile tl = make_tile<C, W>(a, tile, false);
     const int ftile = tl.j * a.nCG + tl.cg;
 
+    // unconditional (clamped) loads keep every load in flight at once
     float Ar[C][8], bv[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) {
-        const int t = tl.t0 + i;
-        if (tl.cv && t < a.T) {
-            load_row(a.A + tl.ablk0 + t * tl.astep, tl.v, Ar[i]);
-            bv[i] = a.x[tl.vec0 + t * tl.vstep];
-        } else {
+        const int t = clampT(tl.t0 + i, a.T);
+        load_row(a.A + tl.ablk0 + t * tl.astep, tl.v, Ar[i]);
+        bv[i] = a.x[tl.vec0 + t * tl.vstep];
+    }
+    const float xh0 = load_h0(a, tl);
+#pragma unroll
+    for (int i = 0; i < C; ++i)
+        if (!(tl.cv && tl.t0 + i < a.T)) {
             eye_row(tl.v, Ar[i]);
             bv[i] = 0.0f;
         }
-    }
 
     // chunk aggregate from a zero state: Phi = A_e..A_s, u = local h_e
     float Phi[8], u = bv[0];
@@ -330,7 +349,6 @@ __global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
     sAgg[tl.q][tl.slot][8] = u;
     __syncthreads();
 
-    const float xh0 = (tl.cv && a.h0) ? a.h0[tl.bb * a.d + tl.jb * 8 + tl.v] : 0.0f;
     float x;
     if constexpr (MULTI) {
         if (tl.wv == 0) {
@@ -357,22 +375,22 @@ __global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
 #pragma unroll
                 for (int s = 0; s < 8; ++s) pay[s] = TP[s];
                 pay[8] = Tu;
-                publish<AW>(a.agg, ftile, tl.slot, a.tag, pay);
+                publish<AW>(a.agg, ftile, tl.slot, tag, pay);
             }
             float xin = xh0;
             if (tl.j > 0) {
                 float xi[1];
-                const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, a.tag, a.err, xi);
+                const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, tag, &a.hd->err, xi);
                 if (ps >= 0) xin = xi[0];
                 for (int p = ps + 1; p < tl.j; ++p) {
                     float ag[AW];
-                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, a.tag, a.err, ag);
+                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
                     xin = mv8(ag, xin, ag[8]);
                 }
             }
             if (tl.sub == 0 && tl.j < a.nT - 1) {
                 const float xo = mv8(TP, xin, Tu);
-                publish<1>(a.incl, ftile, tl.slot, a.tag, &xo);
+                publish<1>(a.incl, ftile, tl.slot, tag, &xo);
             }
             if (tl.sub == 0) sCarry[tl.slot] = xin;
         }
@@ -404,23 +422,32 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
     constexpr int AW = 9;
     __shared__ float sAgg[NCH][32][AW];
     __shared__ float sCarry[32];
-    __shared__ uint32_t sTicket;
+    __shared__ uint32_t sTicket[2];
 
-    const int tile = MULTI ? static_cast<int>(take_ticket(a.ticket, a.nTiles, a.err, &sTicket))
-                           : static_cast<int>(blockIdx.x);
+    int tile = blockIdx.x;
+    uint32_t tag = 0;
+    if constexpr (MULTI) {
+        const TileTicket tk = take_ticket(a.hd, a.nTiles, sTicket);
+        tile = static_cast<int>(tk.tile);
+        tag = tk.tag;
+    }
     const Tile tl = make_tile<C, W>(a, tile, true);
     const int ftile = tl.j * a.nCG + tl.cg;
 
     float ATr[C][8], gv[C], hp[C];   // rows of A_t^T, upstream dh_t, h_{t-1}
-    const float xh0 = (tl.cv && a.h0) ? a.h0[tl.bb * a.d + tl.jb * 8 + tl.v] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = clampT(tl.t0 + i, a.T);
+        load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
+        gv[i] = a.y[tl.vec0 + t * tl.vstep];
+        hp[i] = a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep];
+    }
+    const float xh0 = load_h0(a, tl);
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int t = tl.t0 + i;
-        if (tl.cv && t < a.T) {
-            load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
-            gv[i] = a.y[tl.vec0 + t * tl.vstep];
-            hp[i] = (t > 0) ? a.x[tl.vec0 + (t - 1) * tl.vstep] : xh0;
-        } else {
+        if (t == 0) hp[i] = xh0;
+        if (!(tl.cv && t < a.T)) {
             eye_row(tl.v, ATr[i]);
             gv[i] = 0.0f;
             hp[i] = 0.0f;
@@ -471,23 +498,23 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
 #pragma unroll
                 for (int s = 0; s < 8; ++s) pay[s] = TP[s];
                 pay[8] = Tw;
-                publish<AW>(a.agg, ftile, tl.slot, a.tag, pay);
+                publish<AW>(a.agg, ftile, tl.slot, tag, pay);
             }
             float win = 0.0f;
             if (tl.j < a.nT - 1) {
                 float xi[1];
-                const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, a.tag, a.err, xi);
+                const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, tag, &a.hd->err, xi);
                 int pend = a.nT;
                 if (ps >= 0) { win = xi[0]; pend = ps; }
                 for (int p = pend - 1; p > tl.j; --p) {
                     float ag[AW];
-                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, a.tag, a.err, ag);
+                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
                     win = mv8(ag, win, ag[8]);
                 }
             }
             if (tl.sub == 0 && tl.j > 0) {
                 const float wo = mv8(TP, win, Tw);
-                publish<1>(a.incl, ftile, tl.slot, a.tag, &wo);
+                publish<1>(a.incl, ftile, tl.slot, tag, &wo);
             }
             if (tl.sub == 0) sCarry[tl.slot] = win;
         }
@@ -524,22 +551,25 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
     constexpr int AW = 8;
     __shared__ float sAgg[NCH][32][AW];
     __shared__ float sCarry[32][8];
-    __shared__ uint32_t sTicket;
+    __shared__ uint32_t sTicket[2];
 
-    const int tile = MULTI ? static_cast<int>(take_ticket(a.ticket, a.nTiles, a.err, &sTicket))
-                           : static_cast<int>(blockIdx.x);
+    int tile = blockIdx.x;
+    uint32_t tag = 0;
+    if constexpr (MULTI) {
+        const TileTicket tk = take_ticket(a.hd, a.nTiles, sTicket);
+        tile = static_cast<int>(tk.tile);
+        tag = tk.tag;
+    }
     const Tile tl = make_tile<C, W>(a, tile, false);
     const int ftile = tl.j * a.nCG + tl.cg;
 
     float Ar[C][8];
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int t = tl.t0 + i;
-        if (tl.cv && t < a.T)
-            load_row(a.A + tl.ablk0 + t * tl.astep, tl.v, Ar[i]);
-        else
-            eye_row(tl.v, Ar[i]);
-    }
+    for (int i = 0; i < C; ++i)
+        load_row(a.A + tl.ablk0 + clampT(tl.t0 + i, a.T) * tl.astep, tl.v, Ar[i]);
+#pragma unroll
+    for (int i = 0; i < C; ++i)
+        if (!(tl.cv && tl.t0 + i < a.T)) eye_row(tl.v, Ar[i]);
 
     float Phi[8];
 #pragma unroll
@@ -575,17 +605,17 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
         float Pin[8];
         eye_row(tl.v, Pin);
         if constexpr (MULTI) {
-            if (tl.sub == 0 && tl.j > 0 && tl.j < a.nT - 1) publish<AW>(a.agg, ftile, tl.slot, a.tag, TP);
+            if (tl.sub == 0 && tl.j > 0 && tl.j < a.nT - 1) publish<AW>(a.agg, ftile, tl.slot, tag, TP);
             if (tl.j > 0) {
                 float xi[8];
-                const int ps = find_inclusive<8>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, a.tag, a.err, xi);
+                const int ps = find_inclusive<8>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, tag, &a.hd->err, xi);
                 if (ps >= 0) {
 #pragma unroll
                     for (int s = 0; s < 8; ++s) Pin[s] = xi[s];
                 }
                 for (int p = ps + 1; p < tl.j; ++p) {
                     float ag[AW], np[8];
-                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, a.tag, a.err, ag);
+                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
                     mm8(ag, Pin, np);
 #pragma unroll
                     for (int s = 0; s < 8; ++s) Pin[s] = np[s];
@@ -594,7 +624,7 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
             if (tl.sub == 0 && tl.j < a.nT - 1) {
                 float Po[8];
                 mm8(TP, Pin, Po);
-                publish<8>(a.incl, ftile, tl.slot, a.tag, Po);
+                publish<8>(a.incl, ftile, tl.slot, tag, Po);
             }
         }
         if (tl.sub == 0) {
@@ -632,21 +662,31 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
     constexpr int AW = 16;   // row of Psi, row of Wl
     __shared__ float sAgg[NCH][32][AW];
     __shared__ float sCarry[32][8];
-    __shared__ uint32_t sTicket;
+    __shared__ uint32_t sTicket[2];
 
-    const int tile = MULTI ? static_cast<int>(take_ticket(a.ticket, a.nTiles, a.err, &sTicket))
-                           : static_cast<int>(blockIdx.x);
+    int tile = blockIdx.x;
+    uint32_t tag = 0;
+    if constexpr (MULTI) {
+        const TileTicket tk = take_ticket(a.hd, a.nTiles, sTicket);
+        tile = static_cast<int>(tk.tile);
+        tag = tk.tag;
+    }
     const Tile tl = make_tile<C, W>(a, tile, true);
     const int ftile = tl.j * a.nCG + tl.cg;
 
-    float ATr[C][8], Gr[C][8];
+    float ATr[C][8], Gr[C][8], Pp[C][8];   // rows of A_t^T, dP_t, P_{t-1}
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = clampT(tl.t0 + i, a.T);
+        load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
+        load_row(a.y + tl.ablk0 + t * tl.astep, tl.v, Gr[i]);
+        load_row(a.x + tl.ablk0 + (t > 0 ? t - 1 : 0) * tl.astep, tl.v, Pp[i]);
+    }
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int t = tl.t0 + i;
-        if (tl.cv && t < a.T) {
-            load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
-            load_row(a.y + tl.ablk0 + t * tl.astep, tl.v, Gr[i]);
-        } else {
+        if (t == 0) eye_row(tl.v, Pp[i]);
+        if (!(tl.cv && t < a.T)) {
             eye_row(tl.v, ATr[i]);
 #pragma unroll
             for (int s = 0; s < 8; ++s) Gr[i][s] = 0.0f;
@@ -708,11 +748,11 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
                 float pay[AW];
 #pragma unroll
                 for (int s = 0; s < 8; ++s) { pay[s] = TP[s]; pay[8 + s] = TW[s]; }
-                publish<AW>(a.agg, ftile, tl.slot, a.tag, pay);
+                publish<AW>(a.agg, ftile, tl.slot, tag, pay);
             }
             if (tl.j < a.nT - 1) {
                 float xi[8];
-                const int ps = find_inclusive<8>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, a.tag, a.err, xi);
+                const int ps = find_inclusive<8>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, tag, &a.hd->err, xi);
                 int pend = a.nT;
                 if (ps >= 0) {
                     pend = ps;
@@ -721,7 +761,7 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
                 }
                 for (int p = pend - 1; p > tl.j; --p) {
                     float ag[AW], np[8];
-                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, a.tag, a.err, ag);
+                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
                     mm8(ag, Win, np);
 #pragma unroll
                     for (int s = 0; s < 8; ++s) Win[s] = np[s] + ag[8 + s];
@@ -732,7 +772,7 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
                 mm8(TP, Win, Wo);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) Wo[s] += TW[s];
-                publish<8>(a.incl, ftile, tl.slot, a.tag, Wo);
+                publish<8>(a.incl, ftile, tl.slot, tag, Wo);
             }
         }
         if (tl.sub == 0) {
@@ -755,14 +795,10 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
     for (int i = C - 1; i >= 0; --i) {
         const int t = tl.t0 + i;
         const bool valid = tl.cv && t < a.T;
-        float G[8], Pp[8], dAr[8], nw[8];
+        float G[8], dAr[8], nw[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) G[s] = Gr[i][s] + Wc[s];
-        if (valid && t > 0)
-            load_row(a.x + tl.ablk0 + (t - 1) * tl.astep, tl.v, Pp);
-        else
-            eye_row(tl.v, Pp);
-        mmT8(G, Pp, dAr);
+        mmT8(G, Pp[i], dAr);
         mm8(ATr[i], G, nw);
 #pragma unroll
         for (int s = 0; s < 8; ++s) Wc[s] = nw[s];
@@ -802,6 +838,8 @@ BlockGeom make_geom(int64_t B, int64_t T, int64_t d, int64_t k, int agg_words, i
     g.agg_words = agg_words;
     g.incl_words = incl_words;
     size_t off = sizeof(WsHeader);
+    g.off_zeros = off;   // B*d floats, never written: the h0 of calls that pass none
+    off = align256(off + static_cast<size_t>(B) * d * 4);
     if (g.nT > 1) {
         const size_t slots = static_cast<size_t>(g.nTiles) * 32;
         g.off_agg = off;  off = align256(off + slots * agg_words * 8);
@@ -811,16 +849,14 @@ BlockGeom make_geom(int64_t B, int64_t T, int64_t d, int64_t k, int agg_words, i
     return g;
 }
 
-BlkArgs base_args(const BlockGeom &g, void *ws, uint32_t tag, bool bwd)
+BlkArgs base_args(const BlockGeom &g, void *ws)
 {
     char *w = static_cast<char *>(ws);
     WsHeader *hd = reinterpret_cast<WsHeader *>(w);
     BlkArgs a{};
     a.nchain = g.nchain;
     a.T = g.T; a.d = g.d; a.nb = g.nb; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
-    a.ticket = bwd ? &hd->ticket_bwd : &hd->ticket_fwd;
-    a.err = &hd->err;
-    a.tag = tag;
+    a.hd = hd;
     if (g.nT > 1) {
         a.agg = reinterpret_cast<uint64_t *>(w + g.off_agg);
         a.incl = reinterpret_cast<uint64_t *>(w + g.off_incl);
@@ -859,38 +895,40 @@ BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k)
 }
 
 hipError_t launch_block_affine_fwd(const BlockGeom &g, const float *A, const float *b,
-                                   const float *h0, float *h, void *ws, uint32_t tag, hipStream_t s)
+                                   const float *h0, float *h, void *ws, hipStream_t s)
 {
-    BlkArgs a = base_args(g, ws, tag, false);
-    a.A = A; a.x = b; a.h0 = h0; a.out = h;
+    BlkArgs a = base_args(g, ws);
+    a.A = A; a.x = b; a.out = h;
+    a.h0 = h0 ? h0 : reinterpret_cast<const float *>(static_cast<char *>(ws) + g.off_zeros);
     MGS_BLOCK_LAUNCH(baffine_fwd_kernel, g, a, s);
     return hipGetLastError();
 }
 
 hipError_t launch_block_affine_bwd(const BlockGeom &g, const float *A, const float *h0,
                                    const float *h, const float *dh, float *dA, float *db,
-                                   float *dh0, void *ws, uint32_t tag, hipStream_t s)
+                                   float *dh0, void *ws, hipStream_t s)
 {
-    BlkArgs a = base_args(g, ws, tag, true);
-    a.A = A; a.x = h; a.y = dh; a.h0 = h0; a.out = dA; a.out2 = db; a.out3 = dh0;
+    BlkArgs a = base_args(g, ws);
+    a.A = A; a.x = h; a.y = dh; a.out = dA; a.out2 = db; a.out3 = dh0;
+    a.h0 = h0 ? h0 : reinterpret_cast<const float *>(static_cast<char *>(ws) + g.off_zeros);
     MGS_BLOCK_LAUNCH(baffine_bwd_kernel, g, a, s);
     return hipGetLastError();
 }
 
 hipError_t launch_block_matrix_fwd(const BlockGeom &g, const float *A, float *P, void *ws,
-                                   uint32_t tag, hipStream_t s)
+                                   hipStream_t s)
 {
-    BlkArgs a = base_args(g, ws, tag, false);
+    BlkArgs a = base_args(g, ws);
     a.A = A; a.out = P;
     MGS_BLOCK_LAUNCH(bmatrix_fwd_kernel, g, a, s);
     return hipGetLastError();
 }
 
 hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const float *P,
-                                   const float *dP, float *dA, void *ws, uint32_t tag,
+                                   const float *dP, float *dA, void *ws,
                                    hipStream_t s)
 {
-    BlkArgs a = base_args(g, ws, tag, true);
+    BlkArgs a = base_args(g, ws);
     a.A = A; a.x = P; a.y = dP; a.out = dA;
     MGS_BLOCK_LAUNCH(bmatrix_bwd_kernel, g, a, s);
     return hipGetLastError();

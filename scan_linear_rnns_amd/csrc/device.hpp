@@ -9,8 +9,8 @@
 //  * tile tickets: workgroups take tile indices from an atomic counter in
 //    dispatch order, so a tile only ever waits on tiles whose workgroups
 //    started before it (the single-pass decoupled look-back of Merrill and
-//    Garland needs this for forward progress).  The workgroup that takes the
-//    last ticket resets the counter for the next call.
+//    Garland needs this for forward progress).  The same counter word holds
+//    the launch epoch, which supplies the tag.
 //  * bounded waits: every cross-workgroup wait gives up after kSpinLimit
 //    polls and raises bit 0 of the workspace error word instead of hanging.
 #pragma once
@@ -24,10 +24,13 @@ constexpr uint32_t kErrSpin = 1u;         // a look-back wait hit its spin limit
 constexpr uint32_t kErrTicket = 2u;       // a ticket counter was not reset (workspace not zeroed)
 constexpr uint32_t kSpinLimit = 1u << 20; // polls (each a memory round trip plus a short sleep)
 
-// Workspace header (first 256 bytes of every workspace).
+// Workspace header (first 256 bytes of every workspace).  `ticket` packs
+// (epoch << 32) | count: every multi-tile launch on the workspace takes its
+// tile indices from `count` and its tag from `epoch`, so tags differ between
+// any two launches on one workspace -- also between replays of a captured
+// graph -- and never equal 0 (the value of a zero-filled workspace).
 struct WsHeader {
-    uint32_t ticket_fwd;
-    uint32_t ticket_bwd;
+    unsigned long long ticket;
     uint32_t err;
     uint32_t pad[61];
 };
@@ -59,23 +62,33 @@ __device__ __forceinline__ void raise_error(uint32_t *err, uint32_t bits)
     __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Block-wide: returns this workgroup's tile index (0 .. n_tiles-1), taken in
-// dispatch order from *ctr.  `slot` is a __shared__ word.
-__device__ __forceinline__ uint32_t take_ticket(uint32_t *ctr, uint32_t n_tiles, uint32_t *err,
-                                                uint32_t *slot)
+struct TileTicket {
+    uint32_t tile;
+    uint32_t tag;
+};
+
+// Block-wide: this workgroup's tile index (0 .. n_tiles-1), taken in dispatch
+// order, and the launch's tag.  `slot` is two __shared__ words.  The
+// workgroup that takes the last index starts the next epoch with count 0.
+__device__ __forceinline__ TileTicket take_ticket(WsHeader *hd, uint32_t n_tiles, uint32_t *slot)
 {
     if (threadIdx.x == 0) {
-        uint32_t t = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (t == n_tiles - 1)
-            __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (t >= n_tiles) {
-            raise_error(err, kErrTicket);
-            t %= n_tiles;
+        const unsigned long long old =
+            __hip_atomic_fetch_add(&hd->ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t cnt = static_cast<uint32_t>(old);
+        const uint32_t epoch = static_cast<uint32_t>(old >> 32);
+        if (cnt == n_tiles - 1)
+            __hip_atomic_store(&hd->ticket, static_cast<unsigned long long>(epoch + 1u) << 32,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (cnt >= n_tiles) {
+            raise_error(&hd->err, kErrTicket);
+            cnt %= n_tiles;
         }
-        *slot = t;
+        slot[0] = cnt;
+        slot[1] = epoch % 0xFFFFFFFEu + 1u;
     }
     __syncthreads();
-    return *slot;
+    return TileTicket{slot[0], slot[1]};
 }
 
 // Polls a tagged word until it carries `tag` or the spin limit is reached.

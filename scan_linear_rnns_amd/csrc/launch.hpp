@@ -30,10 +30,10 @@ struct LogGeom {
 LogGeom log_geometry(int64_t B, int64_t T, int64_t d);
 
 hipError_t launch_log_fwd(const LogGeom &g, const float *la, const float *lb, const float *lh0,
-                          float *h, void *ws, uint32_t tag, hipStream_t s);
+                          float *h, void *ws, hipStream_t s);
 hipError_t launch_log_bwd(const LogGeom &g, const float *la, const float *lb, const float *lh0,
                           const float *dh, float *dla, float *dlb, float *dlh0, void *ws,
-                          uint32_t tag, hipStream_t s);
+                          hipStream_t s);
 
 // ------------------------------------------------------------- block scans
 struct BlockGeom {
@@ -46,6 +46,7 @@ struct BlockGeom {
     int nT;         // tiles along T
     int nCG;        // chain groups (of G chains)
     int nTiles;
+    size_t off_zeros;                 // B*d zero floats standing in for an absent h0
     size_t off_agg, off_incl, bytes;  // look-back payload (tagged words)
     int agg_words;  // tagged words per chain per tile in the aggregate
     int incl_words; // tagged words per chain per tile in the inclusive prefix
@@ -55,16 +56,14 @@ BlockGeom block_affine_geometry(int64_t B, int64_t T, int64_t d, int64_t k);
 BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k);
 
 hipError_t launch_block_affine_fwd(const BlockGeom &g, const float *A, const float *b,
-                                   const float *h0, float *h, void *ws, uint32_t tag,
-                                   hipStream_t s);
+                                   const float *h0, float *h, void *ws, hipStream_t s);
 hipError_t launch_block_affine_bwd(const BlockGeom &g, const float *A, const float *h0,
                                    const float *h, const float *dh, float *dA, float *db,
-                                   float *dh0, void *ws, uint32_t tag, hipStream_t s);
+                                   float *dh0, void *ws, hipStream_t s);
 hipError_t launch_block_matrix_fwd(const BlockGeom &g, const float *A, float *P, void *ws,
-                                   uint32_t tag, hipStream_t s);
-hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const float *P,
-                                   const float *dP, float *dA, void *ws, uint32_t tag,
                                    hipStream_t s);
+hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const float *P,
+                                   const float *dP, float *dA, void *ws, hipStream_t s);
 
 // zero-fill of n floats (used for gradients of an empty sequence)
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);

@@ -59,10 +59,9 @@ struct LogFwdArgs {
     float *h;                       // nullptr: carries only (used by the backward)
     int64_t S;
     int T, d, nCG, nT, nTiles;
-    uint32_t *ticket, *err;
+    WsHeader *hd;
     uint64_t *agg_a, *agg_h, *incl; // tagged look-back words, [tile][CHW]
     float *carry;                   // log2 h at each tile start, [tile][CHW]
-    uint32_t tag;
 };
 
 struct LogBwdArgs {
@@ -70,10 +69,9 @@ struct LogBwdArgs {
     float *dla, *dlb, *dlh0;
     int64_t S;
     int T, d, nCG, nT, nTiles;
-    uint32_t *ticket, *err;
+    WsHeader *hd;
     uint64_t *agg_p, *agg_w, *incl;
     const float *carry;
-    uint32_t tag;
 };
 
 template <int CHW, int C, int W, bool MULTI>
@@ -85,18 +83,20 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
     __shared__ float sLA[NCH][CHW];
     __shared__ float sLH[NCH][CHW];
     __shared__ float sCarry[CHW];
-    __shared__ uint32_t sTicket;
+    __shared__ uint32_t sTicket[2];
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int ch = lane % CHW;
     const int q = wv * SUB + lane / CHW;
 
-    int tile;
-    if constexpr (MULTI)
-        tile = static_cast<int>(take_ticket(a.ticket, a.nTiles, a.err, &sTicket));
-    else
-        tile = blockIdx.x;
+    int tile = blockIdx.x;
+    uint32_t tag = 0;
+    if constexpr (MULTI) {
+        const TileTicket tk = take_ticket(a.hd, a.nTiles, sTicket);
+        tile = static_cast<int>(tk.tile);
+        tag = tk.tag;
+    }
     const int j = tile / a.nCG;              // T-tile (tickets run T-major)
     const int cg = tile - j * a.nCG;
 
@@ -107,15 +107,23 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
     const int64_t base = bb * a.T * a.d + (cc - bb * a.d);
     const int t0 = j * TT + q * C;
 
+    // Loads are unconditional (indices clamped into the tensor) so that all of
+    // them are in flight at once; masked steps become the identity afterwards.
     float x[C], y[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int t = t0 + i;
-        const bool v = cv && t < a.T;
-        const int64_t off = base + static_cast<int64_t>(t) * a.d;
-        x[i] = v ? a.la[off] * kLog2e : 0.0f;       // identity step: a = 1, b = 0
-        y[i] = v ? a.lb[off] * kLog2e : -kInf;
+        const int64_t off = base + static_cast<int64_t>(t < a.T ? t : a.T - 1) * a.d;
+        x[i] = a.la[off];
+        y[i] = a.lb[off];
     }
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const bool v = cv && t0 + i < a.T;
+        x[i] = v ? x[i] * kLog2e : 0.0f;       // identity step: a = 1, b = 0
+        y[i] = v ? y[i] * kLog2e : -kInf;
+    }
+    const float lh0v = a.lh0[cc];
 
     // chunk-local pair scan from the identity (0, -inf)
     float pA[C], pH[C];
@@ -142,10 +150,10 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
             }
             const size_t slot = static_cast<size_t>(tile) * CHW + ch;
             if (j > 0 && j < a.nT - 1) {
-                tagged_store(&a.agg_a[slot], a.tag, TA);
-                tagged_store(&a.agg_h[slot], a.tag, TH);
+                tagged_store(&a.agg_a[slot], tag, TA);
+                tagged_store(&a.agg_h[slot], tag, TH);
             }
-            const float lh0 = cv ? a.lh0[chain] * kLog2e : -kInf;
+            const float lh0 = cv ? lh0v * kLog2e : -kInf;
             float cin = lh0;
             if (j > 0) {
                 // walk back: acc composes the aggregates of tiles p+1 .. j-1
@@ -155,14 +163,14 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
                     bool have = false, moved = false;
                     for (uint32_t spin = 0;; ++spin) {
                         uint64_t w;
-                        if (poll(&a.incl[ps], a.tag, w)) {
+                        if (poll(&a.incl[ps], tag, w)) {
                             basev = tag_value(w);
                             have = true;
                             break;
                         }
                         if (p > 0) {
                             uint64_t wa, wh;
-                            if (poll(&a.agg_a[ps], a.tag, wa) && poll(&a.agg_h[ps], a.tag, wh)) {
+                            if (poll(&a.agg_a[ps], tag, wa) && poll(&a.agg_h[ps], tag, wh)) {
                                 accH = lae2(accA + tag_value(wh), accH);
                                 accA += tag_value(wa);
                                 moved = true;
@@ -170,7 +178,7 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
                             }
                         }
                         if (spin >= kSpinLimit) {
-                            raise_error(a.err, kErrSpin);
+                            raise_error(&a.hd->err, kErrSpin);
                             break;
                         }
                         backoff();
@@ -180,14 +188,14 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
                 cin = lae2(accA + basev, accH);
             }
             if (j < a.nT - 1)
-                tagged_store(&a.incl[slot], a.tag, lae2(TA + cin, TH));
+                tagged_store(&a.incl[slot], tag, lae2(TA + cin, TH));
             a.carry[slot] = cin;
             sCarry[ch] = cin;
         }
         __syncthreads();
         carry = sCarry[ch];
     } else {
-        carry = cv ? a.lh0[chain] * kLog2e : -kInf;
+        carry = cv ? lh0v * kLog2e : -kInf;
     }
 
     if (a.h == nullptr) return;
@@ -214,18 +222,20 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
     __shared__ float sP[NCH][CHW];   // reverse: prod a over the chunk
     __shared__ float sW[NCH][CHW];   // reverse: w at the chunk start from a zero carry
     __shared__ float sCarry[CHW];
-    __shared__ uint32_t sTicket;
+    __shared__ uint32_t sTicket[2];
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int ch = lane % CHW;
     const int q = wv * SUB + lane / CHW;
 
-    int tile;
-    if constexpr (MULTI)
-        tile = static_cast<int>(take_ticket(a.ticket, a.nTiles, a.err, &sTicket));
-    else
-        tile = blockIdx.x;
+    int tile = blockIdx.x;
+    uint32_t tag = 0;
+    if constexpr (MULTI) {
+        const TileTicket tk = take_ticket(a.hd, a.nTiles, sTicket);
+        tile = static_cast<int>(tk.tile);
+        tag = tk.tag;
+    }
     const int jr = tile / a.nCG;             // tickets run from the last T-tile back
     const int cg = tile - jr * a.nCG;
     const int j = a.nT - 1 - jr;
@@ -242,11 +252,20 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int t = t0 + i;
-        const bool v = cv && t < a.T;
-        const int64_t off = base + static_cast<int64_t>(t) * a.d;
-        av[i] = v ? ex2(a.la[off] * kLog2e) : 1.0f;
-        bv[i] = v ? ex2(a.lb[off] * kLog2e) : 0.0f;
-        gv[i] = v ? a.dh[off] : 0.0f;
+        const int64_t off = base + static_cast<int64_t>(t < a.T ? t : a.T - 1) * a.d;
+        av[i] = a.la[off];
+        bv[i] = a.lb[off];
+        gv[i] = a.dh[off];
+    }
+    const float lh0v = a.lh0[cc];
+    float cin_f = 0.0f;   // the forward writes a carry for every tile, the first included
+    if constexpr (MULTI) cin_f = a.carry[static_cast<size_t>(ftile) * CHW + ch];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const bool v = cv && t0 + i < a.T;
+        av[i] = v ? ex2(av[i] * kLog2e) : 1.0f;
+        bv[i] = v ? ex2(bv[i] * kLog2e) : 0.0f;
+        gv[i] = v ? gv[i] : 0.0f;
     }
 
     // forward recompute, chunk-local from a zero start
@@ -269,11 +288,7 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
     sW[q][ch] = wl;
 
     // state entering the tile: h0 for the first tile, else the forward's carry
-    float hin;
-    if (j == 0)
-        hin = cv ? ex2(a.lh0[chain] * kLog2e) : 0.0f;
-    else
-        hin = ex2(a.carry[static_cast<size_t>(ftile) * CHW + ch]);
+    const float hin = (j == 0) ? (cv ? ex2(lh0v * kLog2e) : 0.0f) : ex2(cin_f);
     __syncthreads();
 
     float wcarry;
@@ -287,8 +302,8 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
             }
             const size_t slot = static_cast<size_t>(ftile) * CHW + ch;
             if (j > 0 && j < a.nT - 1) {
-                tagged_store(&a.agg_p[slot], a.tag, TP);
-                tagged_store(&a.agg_w[slot], a.tag, TW);
+                tagged_store(&a.agg_p[slot], tag, TP);
+                tagged_store(&a.agg_w[slot], tag, TW);
             }
             float cin = 0.0f;
             if (j < a.nT - 1) {
@@ -299,14 +314,14 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
                     bool have = false, moved = false;
                     for (uint32_t spin = 0;; ++spin) {
                         uint64_t w;
-                        if (poll(&a.incl[ps], a.tag, w)) {
+                        if (poll(&a.incl[ps], tag, w)) {
                             basev = tag_value(w);
                             have = true;
                             break;
                         }
                         if (p < a.nT - 1) {
                             uint64_t wp, ww;
-                            if (poll(&a.agg_p[ps], a.tag, wp) && poll(&a.agg_w[ps], a.tag, ww)) {
+                            if (poll(&a.agg_p[ps], tag, wp) && poll(&a.agg_w[ps], tag, ww)) {
                                 accW = accW + accP * tag_value(ww);
                                 accP = accP * tag_value(wp);
                                 moved = true;
@@ -314,7 +329,7 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
                             }
                         }
                         if (spin >= kSpinLimit) {
-                            raise_error(a.err, kErrSpin);
+                            raise_error(&a.hd->err, kErrSpin);
                             break;
                         }
                         backoff();
@@ -323,7 +338,7 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
                 }
                 cin = accW + accP * basev;
             }
-            if (j > 0) tagged_store(&a.incl[slot], a.tag, TW + TP * cin);
+            if (j > 0) tagged_store(&a.incl[slot], tag, TW + TP * cin);
             sCarry[ch] = cin;
         }
         __syncthreads();
@@ -415,16 +430,14 @@ LogGeom log_geometry(int64_t B, int64_t T, int64_t d)
 }
 
 hipError_t launch_log_fwd(const LogGeom &g, const float *la, const float *lb, const float *lh0,
-                          float *h, void *ws, uint32_t tag, hipStream_t s)
+                          float *h, void *ws, hipStream_t s)
 {
     char *w = static_cast<char *>(ws);
     WsHeader *hd = reinterpret_cast<WsHeader *>(w);
     LogFwdArgs a{};
     a.la = la; a.lb = lb; a.lh0 = lh0; a.h = h;
     a.S = g.S; a.T = g.T; a.d = g.d; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
-    a.ticket = &hd->ticket_fwd;
-    a.err = &hd->err;
-    a.tag = tag;
+    a.hd = hd;
     if (g.nT > 1) {
         a.agg_a = reinterpret_cast<uint64_t *>(w + g.off_fagg_a);
         a.agg_h = reinterpret_cast<uint64_t *>(w + g.off_fagg_h);
@@ -442,7 +455,7 @@ hipError_t launch_log_fwd(const LogGeom &g, const float *la, const float *lb, co
 
 hipError_t launch_log_bwd(const LogGeom &g, const float *la, const float *lb, const float *lh0,
                           const float *dh, float *dla, float *dlb, float *dlh0, void *ws,
-                          uint32_t tag, hipStream_t s)
+                          hipStream_t s)
 {
     char *w = static_cast<char *>(ws);
     WsHeader *hd = reinterpret_cast<WsHeader *>(w);
@@ -450,9 +463,7 @@ hipError_t launch_log_bwd(const LogGeom &g, const float *la, const float *lb, co
     a.la = la; a.lb = lb; a.lh0 = lh0; a.dh = dh;
     a.dla = dla; a.dlb = dlb; a.dlh0 = dlh0;
     a.S = g.S; a.T = g.T; a.d = g.d; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
-    a.ticket = &hd->ticket_bwd;
-    a.err = &hd->err;
-    a.tag = tag;
+    a.hd = hd;
     if (g.nT > 1) {
         a.agg_p = reinterpret_cast<uint64_t *>(w + g.off_bagg_p);
         a.agg_w = reinterpret_cast<uint64_t *>(w + g.off_bagg_w);

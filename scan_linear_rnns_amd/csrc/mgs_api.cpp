@@ -5,7 +5,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cstdint>
 #include <cstring>
 
@@ -15,16 +14,6 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
-std::atomic<uint32_t> g_tag{0};
-
-// A fresh, non-zero tag per launch: tagged look-back words left by earlier
-// calls (or by a zero-filled workspace) never match it.
-uint32_t next_tag()
-{
-    uint32_t t = g_tag.fetch_add(1, std::memory_order_relaxed) + 1;
-    if (t == 0) t = g_tag.fetch_add(1, std::memory_order_relaxed) + 1;
-    return t;
-}
 
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 
@@ -151,7 +140,7 @@ mgs_status mgs_scan_log_fwd(const float *log_a, const float *log_b, const float 
     if (n == 0) return MGS_OK;
     const mgs::LogGeom g = mgs::log_geometry(B, T, d);
     if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
-    return hip_status(mgs::launch_log_fwd(g, log_a, log_b, log_h0, h, workspace, next_tag(),
+    return hip_status(mgs::launch_log_fwd(g, log_a, log_b, log_h0, h, workspace,
                                           as_stream(stream)));
 }
 
@@ -176,11 +165,11 @@ mgs_status mgs_scan_log_bwd(const float *log_a, const float *log_b, const float 
     const mgs::LogGeom g = mgs::log_geometry(B, T, d);
     if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
     if (g.nT > 1 && !fwd_state_valid) {
-        hipError_t e = mgs::launch_log_fwd(g, log_a, log_b, log_h0, nullptr, workspace, next_tag(), s);
+        hipError_t e = mgs::launch_log_fwd(g, log_a, log_b, log_h0, nullptr, workspace, s);
         if (e != hipSuccess) return hip_status(e);
     }
     return hip_status(mgs::launch_log_bwd(g, log_a, log_b, log_h0, dh, dlog_a, dlog_b, dlog_h0,
-                                          workspace, next_tag(), s));
+                                          workspace, s));
 }
 
 // ---------------------------------------------------------- block scans
@@ -219,7 +208,7 @@ mgs_status mgs_block_affine_scan_fwd(const float *A, const float *b, const float
     if (n == 0) return MGS_OK;
     const mgs::BlockGeom g = mgs::block_affine_geometry(B, T, d, k);
     if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
-    return hip_status(mgs::launch_block_affine_fwd(g, A, b, h0, h, workspace, next_tag(),
+    return hip_status(mgs::launch_block_affine_fwd(g, A, b, h0, h, workspace,
                                                    as_stream(stream)));
 }
 
@@ -242,8 +231,7 @@ mgs_status mgs_block_affine_scan_bwd(const float *A, const float *b, const float
     if (T == 0) return hip_status(mgs::launch_fill_zero(dh0, B * d, s));
     const mgs::BlockGeom g = mgs::block_affine_geometry(B, T, d, k);
     if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
-    return hip_status(mgs::launch_block_affine_bwd(g, A, h0, h, dh, dA, db, dh0, workspace,
-                                                   next_tag(), s));
+    return hip_status(mgs::launch_block_affine_bwd(g, A, h0, h, dh, dA, db, dh0, workspace, s));
 }
 
 mgs_status mgs_block_matrix_scan_workspace_size(int64_t B, int64_t T, int64_t d, int64_t k,
@@ -270,7 +258,7 @@ mgs_status mgs_block_matrix_scan_fwd(const float *A, float *P, int64_t B, int64_
     if (na == 0) return MGS_OK;
     const mgs::BlockGeom g = mgs::block_matrix_geometry(B, T, d, k);
     if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
-    return hip_status(mgs::launch_block_matrix_fwd(g, A, P, workspace, next_tag(), as_stream(stream)));
+    return hip_status(mgs::launch_block_matrix_fwd(g, A, P, workspace, as_stream(stream)));
 }
 
 mgs_status mgs_block_matrix_scan_bwd(const float *A, const float *P, const float *dP, float *dA,
@@ -287,7 +275,7 @@ mgs_status mgs_block_matrix_scan_bwd(const float *A, const float *P, const float
     if (na == 0) return MGS_OK;
     const mgs::BlockGeom g = mgs::block_matrix_geometry(B, T, d, k);
     if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
-    return hip_status(mgs::launch_block_matrix_bwd(g, A, P, dP, dA, workspace, next_tag(),
+    return hip_status(mgs::launch_block_matrix_bwd(g, A, P, dP, dA, workspace,
                                                    as_stream(stream)));
 }
 
