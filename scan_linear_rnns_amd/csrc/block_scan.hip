@@ -52,19 +52,77 @@ __device__ __forceinline__ float hm(float x)   // value of lane 7 - v within the
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
 }
 
+// 8 x 8 row algebra with DPP operands folded into the multiply-adds.  The
+// compiler does not fold DPP moves into FMAs, so the products are written as
+// inline-asm blocks of v_fmac_f32_dpp / v_mul_f32_dpp.  Each block keeps 2 or
+// 4 independent accumulators and cycles through them, so consecutive
+// instructions never depend on each other.  Every block opens with 5 wait
+// states (a VALU write of a DPP source, or of EXEC, may come right before it)
+// and closes with 2 (a DPP read of its result may come right after), because
+// the compiler's hazard tracking does not look inside inline asm.
+
 // y_v = sum_m R[v][m] x_m + add, R = own row (rotated slots), x one value per lane
 __device__ __forceinline__ float mv8(const float *R, float x, float add)
 {
     const float mx = hm(x);
-    float a0 = fmaf(R[0], qb<0>(x), add);
-    float a1 = R[1] * qb<1>(x);
-    a0 = fmaf(R[2], qb<2>(x), a0);
-    a1 = fmaf(R[3], qb<3>(x), a1);
-    a0 = fmaf(R[7], qb<0>(mx), a0);
-    a1 = fmaf(R[6], qb<1>(mx), a1);
-    a0 = fmaf(R[5], qb<2>(mx), a0);
-    a1 = fmaf(R[4], qb<3>(mx), a1);
+    float a0 = add, a1;
+    asm("s_nop 4\n\t"
+        "v_fmac_f32_dpp %0, %2, %4 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %2, %5 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %6 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %2, %7 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %3, %11 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %10 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %3, %9 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %8 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "+&v"(a0), "=&v"(a1)
+        : "v"(x), "v"(mx), "v"(R[0]), "v"(R[1]), "v"(R[2]), "v"(R[3]), "v"(R[4]), "v"(R[5]), "v"(R[6]), "v"(R[7]));
     return a0 + a1;
+}
+
+// Four output slots S..S+3 of Y = R X (X rows spread over the group, M = hm(X)).
+template <int S>
+__device__ __forceinline__ void mm8_quarter(const float *R, const float *X, const float *M, float *Y)
+{
+    asm("s_nop 4\n\t"
+        "v_mul_f32_dpp %0, %4, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %5, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %6, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %7, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %13 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %13 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %13 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %13 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %15 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %15 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %15 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %15 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %19 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %9, %19 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %19 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %11, %19 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %18 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %9, %18 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %18 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %11, %18 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %17 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %9, %17 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %17 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %11, %17 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %16 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %9, %16 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %16 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %11, %16 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "=&v"(Y[S]), "=&v"(Y[S + 1]), "=&v"(Y[S + 2]), "=&v"(Y[S + 3])
+        : "v"(X[S]), "v"(X[S + 1]), "v"(X[S + 2]), "v"(X[S + 3]),
+          "v"(M[S ^ 4]), "v"(M[(S + 1) ^ 4]), "v"(M[(S + 2) ^ 4]), "v"(M[(S + 3) ^ 4]),
+          "v"(R[0]), "v"(R[1]), "v"(R[2]), "v"(R[3]), "v"(R[4]), "v"(R[5]), "v"(R[6]), "v"(R[7]));
 }
 
 // Y = R X : own row of R, rows of X spread over the group.  Y must not alias X.
@@ -73,20 +131,53 @@ __device__ __forceinline__ void mm8(const float *R, const float *X, float *Y)
     float M[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) M[s] = hm(X[s]);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const float xs = X[s];
-        const float ms = M[s ^ 4];
-        float a0 = R[0] * qb<0>(xs);
-        float a1 = R[1] * qb<1>(xs);
-        a0 = fmaf(R[2], qb<2>(xs), a0);
-        a1 = fmaf(R[3], qb<3>(xs), a1);
-        a0 = fmaf(R[7], qb<0>(ms), a0);
-        a1 = fmaf(R[6], qb<1>(ms), a1);
-        a0 = fmaf(R[5], qb<2>(ms), a0);
-        a1 = fmaf(R[4], qb<3>(ms), a1);
-        Y[s] = a0 + a1;
-    }
+    mm8_quarter<0>(R, X, M, Y);
+    mm8_quarter<4>(R, X, M, Y);
+}
+
+// Output slots P, P+1, 7-P, 6-P of Y = G X^T.
+template <int P>
+__device__ __forceinline__ void mmT8_quarter(const float *G, const float *X, const float *M, float *Y)
+{
+    asm("s_nop 4\n\t"
+        "v_mul_f32_dpp %0, %4, %20 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %4, %20 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %12, %24 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %12, %24 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %5, %21 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %21 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %13, %25 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %13, %25 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %6, %22 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %6, %22 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %14, %26 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %14, %26 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %7, %23 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %7, %23 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %15, %27 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %15, %27 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %24 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %8, %24 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %16, %20 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %16, %20 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %9, %25 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %9, %25 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %17, %21 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %17, %21 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %10, %26 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %10, %26 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %22 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %18, %22 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %11, %27 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %11, %27 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %19, %23 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %23 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "=&v"(Y[P]), "=&v"(Y[P + 1]), "=&v"(Y[7 - P]), "=&v"(Y[6 - P])
+        : "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]),
+          "v"(M[0]), "v"(M[1]), "v"(M[2]), "v"(M[3]), "v"(M[4]), "v"(M[5]), "v"(M[6]), "v"(M[7]),
+          "v"(G[0]), "v"(G[1]), "v"(G[2]), "v"(G[3]), "v"(G[4]), "v"(G[5]), "v"(G[6]), "v"(G[7]),
+          "n"(P), "n"(P + 1));
 }
 
 // Y = G X^T : own row of G, rows of X spread over the group.
@@ -95,19 +186,8 @@ __device__ __forceinline__ void mmT8(const float *G, const float *X, float *Y)
     float M[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) M[s] = hm(X[s]);
-    float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f, y4 = 0.f, y5 = 0.f, y6 = 0.f, y7 = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        y0 = fmaf(G[s], qb<0>(X[s]), y0);
-        y1 = fmaf(G[s], qb<1>(X[s]), y1);
-        y2 = fmaf(G[s], qb<2>(X[s]), y2);
-        y3 = fmaf(G[s], qb<3>(X[s]), y3);
-        y7 = fmaf(G[s ^ 4], qb<0>(M[s]), y7);
-        y6 = fmaf(G[s ^ 4], qb<1>(M[s]), y6);
-        y5 = fmaf(G[s ^ 4], qb<2>(M[s]), y5);
-        y4 = fmaf(G[s ^ 4], qb<3>(M[s]), y4);
-    }
-    Y[0] = y0; Y[1] = y1; Y[2] = y2; Y[3] = y3; Y[4] = y4; Y[5] = y5; Y[6] = y6; Y[7] = y7;
+    mmT8_quarter<0>(G, X, M, Y);
+    mmT8_quarter<2>(G, X, M, Y);
 }
 
 // Row v of x x'^T scaled: Y[slot] = g * x'_{column(slot)}  (x' one value per lane)
@@ -159,34 +239,46 @@ __device__ __forceinline__ void store_row(float *p, int v, const float *R)
 
 // Lanes of wave 0 take part; lanes 32..63 mirror lanes 0..31 (same slot).
 // Returns the nearest tile p (in the direction dir = -1: earlier tiles,
-// +1: later tiles) whose IW-word inclusive state is visible to every lane,
-// with the state in xi; -1 if the spin limit was hit.
+// +1: later tiles) whose IW-word inclusive state is published, with the state
+// in xi; -1 if the spin limit was hit.  One batch of loads polls the first word
+// of up to WIN tiles at once; the remaining words of the chosen tile follow.
 template <int IW>
 __device__ int find_inclusive(const uint64_t *incl, int j, int nT, int nCG, int cg, int slot,
                               int dir, uint32_t tag, uint32_t *err, float *xi)
 {
-    constexpr int WIN = (IW == 1) ? 8 : 2;
+    constexpr int WIN = 16;
     for (uint32_t spin = 0;; ++spin) {
         for (int p0 = j + dir; p0 >= 0 && p0 < nT; p0 += dir * WIN) {
-            uint64_t w[WIN][IW];
+            uint64_t w[WIN];
 #pragma unroll
             for (int u = 0; u < WIN; ++u) {
                 const int p = p0 + dir * u;
                 const bool in = p >= 0 && p < nT;
-                const uint64_t *src = incl + ((static_cast<size_t>(in ? p : 0) * nCG + cg) * 32 + slot) * IW;
-#pragma unroll
-                for (int e = 0; e < IW; ++e) w[u][e] = in ? tagged_load(src + e) : 0;
+                w[u] = tagged_load(incl + ((static_cast<size_t>(in ? p : p0) * nCG + cg) * 32 + slot) * IW);
             }
 #pragma unroll
             for (int u = 0; u < WIN; ++u) {
                 const int p = p0 + dir * u;
                 if (p < 0 || p >= nT) break;
-                bool ok = true;
+                if (__all(tag_is(w[u], tag))) {
+                    const uint64_t *src = incl + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * IW;
+                    uint64_t r[IW];
+                    r[0] = w[u];
 #pragma unroll
-                for (int e = 0; e < IW; ++e) ok = ok && tag_is(w[u][e], tag);
-                if (__all(ok)) {
+                    for (int e = 1; e < IW; ++e) r[e] = tagged_load(src + e);
 #pragma unroll
-                    for (int e = 0; e < IW; ++e) xi[e] = tag_value(w[u][e]);
+                    for (int e = 1; e < IW; ++e) {
+                        for (uint32_t sp = 0; !tag_is(r[e], tag); ++sp) {
+                            if (sp >= kSpinLimit) {
+                                raise_error(err, kErrSpin);
+                                break;
+                            }
+                            backoff();
+                            r[e] = tagged_load(src + e);
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < IW; ++e) xi[e] = tag_value(r[e]);
                     return p;
                 }
             }
@@ -199,26 +291,38 @@ __device__ int find_inclusive(const uint64_t *incl, int j, int nT, int nCG, int 
     }
 }
 
-// Loads one tile's AW-word aggregate for this lane, waiting for every word.
-template <int AW>
-__device__ __forceinline__ void load_aggregate(const uint64_t *agg, int p, int nCG, int cg, int slot,
-                                               uint32_t tag, uint32_t *err, float *out)
+// Loads the AW-word aggregates of `cnt` (<= NB) tiles p0, p0 + dir, ... for
+// this lane in one batch of loads, then waits for any word not yet published.
+template <int AW, int NB>
+__device__ __forceinline__ void load_aggregates(const uint64_t *agg, int p0, int dir, int cnt, int nCG,
+                                                int cg, int slot, uint32_t tag, uint32_t *err,
+                                                float (&out)[NB][AW])
 {
-    const uint64_t *src = agg + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * AW;
-    uint64_t w[AW];
+    uint64_t w[NB][AW];
 #pragma unroll
-    for (int e = 0; e < AW; ++e) w[e] = tagged_load(src + e);
+    for (int u = 0; u < NB; ++u) {
+        const int p = p0 + dir * (u < cnt ? u : 0);
+        const uint64_t *src = agg + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * AW;
 #pragma unroll
-    for (int e = 0; e < AW; ++e) {
-        for (uint32_t spin = 0; !tag_is(w[e], tag); ++spin) {
-            if (spin >= kSpinLimit) {
-                raise_error(err, kErrSpin);
-                break;
+        for (int e = 0; e < AW; ++e) w[u][e] = tagged_load(src + e);
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        if (u >= cnt) break;
+        const int p = p0 + dir * u;
+        const uint64_t *src = agg + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * AW;
+#pragma unroll
+        for (int e = 0; e < AW; ++e) {
+            for (uint32_t spin = 0; !tag_is(w[u][e], tag); ++spin) {
+                if (spin >= kSpinLimit) {
+                    raise_error(err, kErrSpin);
+                    break;
+                }
+                backoff();
+                w[u][e] = tagged_load(src + e);
             }
-            backoff();
-            w[e] = tagged_load(src + e);
+            out[u][e] = tag_value(w[u][e]);
         }
-        out[e] = tag_value(w[e]);
     }
 }
 
@@ -306,13 +410,9 @@ __global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
     __shared__ float sCarry[32];
     __shared__ uint32_t sTicket[2];
 
-    int tile = blockIdx.x;
-    uint32_t tag = 0;
-    if constexpr (MULTI) {
-        const TileTicket tk = take_ticket(a.hd, a.nTiles, sTicket);
-        tile = static_cast<int>(tk.tile);
-        tag = tk.tag;
-    }
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<C, W>(a, tile, false);
     const int ftile = tl.j * a.nCG + tl.cg;
 
@@ -347,7 +447,9 @@ __global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
 #pragma unroll
     for (int s = 0; s < 8; ++s) sAgg[tl.q][tl.slot][s] = Phi[s];
     sAgg[tl.q][tl.slot][8] = u;
+    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
     __syncthreads();
+    const uint32_t tag = sTicket[0];
 
     float x;
     if constexpr (MULTI) {
@@ -382,10 +484,14 @@ __global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
                 float xi[1];
                 const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, tag, &a.hd->err, xi);
                 if (ps >= 0) xin = xi[0];
-                for (int p = ps + 1; p < tl.j; ++p) {
-                    float ag[AW];
-                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
-                    xin = mv8(ag, xin, ag[8]);
+                constexpr int NB = 4;
+                for (int p = ps + 1; p < tl.j; p += NB) {
+                    const int cnt = min(NB, tl.j - p);
+                    float ag[NB][AW];
+                    load_aggregates<AW, NB>(a.agg, p, +1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
+#pragma unroll
+                    for (int u = 0; u < NB; ++u)
+                        if (u < cnt) xin = mv8(ag[u], xin, ag[u][8]);
                 }
             }
             if (tl.sub == 0 && tl.j < a.nT - 1) {
@@ -424,13 +530,9 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
     __shared__ float sCarry[32];
     __shared__ uint32_t sTicket[2];
 
-    int tile = blockIdx.x;
-    uint32_t tag = 0;
-    if constexpr (MULTI) {
-        const TileTicket tk = take_ticket(a.hd, a.nTiles, sTicket);
-        tile = static_cast<int>(tk.tile);
-        tag = tk.tag;
-    }
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<C, W>(a, tile, true);
     const int ftile = tl.j * a.nCG + tl.cg;
 
@@ -470,7 +572,9 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
 #pragma unroll
     for (int s = 0; s < 8; ++s) sAgg[tl.q][tl.slot][s] = Psi[s];
     sAgg[tl.q][tl.slot][8] = Wl;
+    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
     __syncthreads();
+    const uint32_t tag = sTicket[0];
 
     float w;
     if constexpr (MULTI) {
@@ -506,10 +610,14 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
                 const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, tag, &a.hd->err, xi);
                 int pend = a.nT;
                 if (ps >= 0) { win = xi[0]; pend = ps; }
-                for (int p = pend - 1; p > tl.j; --p) {
-                    float ag[AW];
-                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
-                    win = mv8(ag, win, ag[8]);
+                constexpr int NB = 4;
+                for (int p = pend - 1; p > tl.j; p -= NB) {
+                    const int cnt = min(NB, p - tl.j);
+                    float ag[NB][AW];
+                    load_aggregates<AW, NB>(a.agg, p, -1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
+#pragma unroll
+                    for (int u = 0; u < NB; ++u)
+                        if (u < cnt) win = mv8(ag[u], win, ag[u][8]);
                 }
             }
             if (tl.sub == 0 && tl.j > 0) {
@@ -553,13 +661,9 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
     __shared__ float sCarry[32][8];
     __shared__ uint32_t sTicket[2];
 
-    int tile = blockIdx.x;
-    uint32_t tag = 0;
-    if constexpr (MULTI) {
-        const TileTicket tk = take_ticket(a.hd, a.nTiles, sTicket);
-        tile = static_cast<int>(tk.tile);
-        tag = tk.tag;
-    }
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<C, W>(a, tile, false);
     const int ftile = tl.j * a.nCG + tl.cg;
 
@@ -583,7 +687,9 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) sAgg[tl.q][tl.slot][s] = Phi[s];
+    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
     __syncthreads();
+    const uint32_t tag = sTicket[0];
 
     // composites of chunks 0..q (wave 0), tile look-back, tile carry
     if (tl.wv == 0) {
@@ -613,12 +719,19 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
 #pragma unroll
                     for (int s = 0; s < 8; ++s) Pin[s] = xi[s];
                 }
-                for (int p = ps + 1; p < tl.j; ++p) {
-                    float ag[AW], np[8];
-                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
-                    mm8(ag, Pin, np);
+                constexpr int NB = 4;
+                for (int p = ps + 1; p < tl.j; p += NB) {
+                    const int cnt = min(NB, tl.j - p);
+                    float ag[NB][AW];
+                    load_aggregates<AW, NB>(a.agg, p, +1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
 #pragma unroll
-                    for (int s = 0; s < 8; ++s) Pin[s] = np[s];
+                    for (int u = 0; u < NB; ++u)
+                        if (u < cnt) {
+                            float np[8];
+                            mm8(ag[u], Pin, np);
+#pragma unroll
+                            for (int s = 0; s < 8; ++s) Pin[s] = np[s];
+                        }
                 }
             }
             if (tl.sub == 0 && tl.j < a.nT - 1) {
@@ -664,13 +777,9 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
     __shared__ float sCarry[32][8];
     __shared__ uint32_t sTicket[2];
 
-    int tile = blockIdx.x;
-    uint32_t tag = 0;
-    if constexpr (MULTI) {
-        const TileTicket tk = take_ticket(a.hd, a.nTiles, sTicket);
-        tile = static_cast<int>(tk.tile);
-        tag = tk.tag;
-    }
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<C, W>(a, tile, true);
     const int ftile = tl.j * a.nCG + tl.cg;
 
@@ -712,7 +821,9 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
         sAgg[tl.q][tl.slot][s] = Psi[s];
         sAgg[tl.q][tl.slot][8 + s] = Wl[s];
     }
+    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
     __syncthreads();
+    const uint32_t tag = sTicket[0];
 
     if (tl.wv == 0) {
         float TP[8], TW[8];
@@ -759,12 +870,19 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
 #pragma unroll
                     for (int s = 0; s < 8; ++s) Win[s] = xi[s];
                 }
-                for (int p = pend - 1; p > tl.j; --p) {
-                    float ag[AW], np[8];
-                    load_aggregate<AW>(a.agg, p, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
-                    mm8(ag, Win, np);
+                constexpr int NB = 2;
+                for (int p = pend - 1; p > tl.j; p -= NB) {
+                    const int cnt = min(NB, p - tl.j);
+                    float ag[NB][AW];
+                    load_aggregates<AW, NB>(a.agg, p, -1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
 #pragma unroll
-                    for (int s = 0; s < 8; ++s) Win[s] = np[s] + ag[8 + s];
+                    for (int u = 0; u < NB; ++u)
+                        if (u < cnt) {
+                            float np[8];
+                            mm8(ag[u], Win, np);
+#pragma unroll
+                            for (int s = 0; s < 8; ++s) Win[s] = np[s] + ag[u][8 + s];
+                        }
                 }
             }
             if (tl.sub == 0 && tl.j > 0) {

@@ -6,11 +6,9 @@
 //    accepts a word only when its tag equals the current call's tag, so no
 //    flag/payload ordering (and no L2 writeback or invalidate fence) is
 //    needed, and the workspace never has to be cleared between calls.
-//  * tile tickets: workgroups take tile indices from an atomic counter in
-//    dispatch order, so a tile only ever waits on tiles whose workgroups
-//    started before it (the single-pass decoupled look-back of Merrill and
-//    Garland needs this for forward progress).  The same counter word holds
-//    the launch epoch, which supplies the tag.
+//  * launch epochs: every multi-tile launch draws its tag from a per-workspace
+//    epoch counter on the device (see epoch_begin), so tags never repeat
+//    between launches on one workspace, replays of a captured graph included.
 //  * bounded waits: every cross-workgroup wait gives up after kSpinLimit
 //    polls and raises bit 0 of the workspace error word instead of hanging.
 #pragma once
@@ -62,33 +60,40 @@ __device__ __forceinline__ void raise_error(uint32_t *err, uint32_t bits)
     __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-struct TileTicket {
-    uint32_t tile;
-    uint32_t tag;
-};
-
-// Block-wide: this workgroup's tile index (0 .. n_tiles-1), taken in dispatch
-// order, and the launch's tag.  `slot` is two __shared__ words.  The
-// workgroup that takes the last index starts the next epoch with count 0.
-__device__ __forceinline__ TileTicket take_ticket(WsHeader *hd, uint32_t n_tiles, uint32_t *slot)
+// Launch tag for the decoupled look-back.  Thread 0 of every workgroup of a
+// multi-tile launch adds 1 to the workspace's (epoch << 32 | count) word; the
+// workgroup that brings the count to n_tiles starts the next epoch.  All
+// workgroups of one launch therefore read the same epoch, and any two
+// launches on one workspace (also replays of a captured graph) read different
+// ones.  The atomic is issued at kernel start (epoch_begin) and its result is
+// consumed only when the workgroup first publishes (epoch_end), so its round
+// trip overlaps the tile's loads.
+//
+// Tiles are indexed by blockIdx and wait only on tiles with a smaller index
+// (forward) or a larger one whose blockIdx is smaller (backward, which numbers
+// its tiles from the end of T).  Workgroups are dispatched in blockIdx order,
+// so every tile a resident workgroup waits on has already been dispatched, and
+// the lowest-numbered unfinished tile can always proceed: no deadlock, with no
+// need to take tile indices from a counter.
+__device__ __forceinline__ unsigned long long epoch_begin(WsHeader *hd)
 {
-    if (threadIdx.x == 0) {
-        const unsigned long long old =
-            __hip_atomic_fetch_add(&hd->ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t cnt = static_cast<uint32_t>(old);
-        const uint32_t epoch = static_cast<uint32_t>(old >> 32);
-        if (cnt == n_tiles - 1)
-            __hip_atomic_store(&hd->ticket, static_cast<unsigned long long>(epoch + 1u) << 32,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (cnt >= n_tiles) {
-            raise_error(&hd->err, kErrTicket);
-            cnt %= n_tiles;
-        }
-        slot[0] = cnt;
-        slot[1] = epoch % 0xFFFFFFFEu + 1u;
-    }
-    __syncthreads();
-    return TileTicket{slot[0], slot[1]};
+    unsigned long long old = 0;
+    if (threadIdx.x == 0)
+        old = __hip_atomic_fetch_add(&hd->ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return old;
+}
+
+// Thread 0 only: turns epoch_begin's value into the launch tag, starting the
+// next epoch if this workgroup was the last of the launch to arrive.
+__device__ __forceinline__ uint32_t epoch_end(WsHeader *hd, unsigned long long old, uint32_t n_tiles)
+{
+    const uint32_t cnt = static_cast<uint32_t>(old);
+    const uint32_t epoch = static_cast<uint32_t>(old >> 32);
+    if (cnt == n_tiles - 1)
+        __hip_atomic_store(&hd->ticket, static_cast<unsigned long long>(epoch + 1u) << 32, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    if (cnt >= n_tiles) raise_error(&hd->err, kErrTicket);
+    return epoch % 0xFFFFFFFEu + 1u;
 }
 
 // Polls a tagged word until it carries `tag` or the spin limit is reached.

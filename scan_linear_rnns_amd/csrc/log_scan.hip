@@ -90,14 +90,10 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
     const int ch = lane % CHW;
     const int q = wv * SUB + lane / CHW;
 
-    int tile = blockIdx.x;
-    uint32_t tag = 0;
-    if constexpr (MULTI) {
-        const TileTicket tk = take_ticket(a.hd, a.nTiles, sTicket);
-        tile = static_cast<int>(tk.tile);
-        tag = tk.tag;
-    }
-    const int j = tile / a.nCG;              // T-tile (tickets run T-major)
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
+    const int j = tile / a.nCG;              // T-tile (tiles are numbered T-major)
     const int cg = tile - j * a.nCG;
 
     const int64_t chain = static_cast<int64_t>(cg) * CHW + ch;
@@ -137,7 +133,9 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
     }
     sLA[q][ch] = LA;
     sLH[q][ch] = LH;
+    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
     __syncthreads();
+    const uint32_t tag = sTicket[0];
 
     float carry;
     if constexpr (MULTI) {
@@ -156,34 +154,50 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
             const float lh0 = cv ? lh0v * kLog2e : -kInf;
             float cin = lh0;
             if (j > 0) {
-                // walk back: acc composes the aggregates of tiles p+1 .. j-1
+                // Decoupled look-back over the earlier tiles, nearest first, LB
+                // tiles per batch of loads: stop at the first tile whose
+                // inclusive state is published, composing the aggregates of the
+                // tiles passed on the way (acc covers tiles p+1 .. j-1).
+                constexpr int LB = 8;
                 float accA = 0.0f, accH = -kInf, basev = lh0;
-                for (int p = j - 1; p >= 0; --p) {
-                    const size_t ps = (static_cast<size_t>(p) * a.nCG + cg) * CHW + ch;
-                    bool have = false, moved = false;
-                    for (uint32_t spin = 0;; ++spin) {
-                        uint64_t w;
-                        if (poll(&a.incl[ps], tag, w)) {
-                            basev = tag_value(w);
-                            have = true;
-                            break;
-                        }
-                        if (p > 0) {
-                            uint64_t wa, wh;
-                            if (poll(&a.agg_a[ps], tag, wa) && poll(&a.agg_h[ps], tag, wh)) {
-                                accH = lae2(accA + tag_value(wh), accH);
-                                accA += tag_value(wa);
-                                moved = true;
-                                break;
+                int p0 = j - 1;
+                for (uint32_t spin = 0;;) {
+                    uint64_t wi[LB], wa[LB], wh[LB];
+#pragma unroll
+                    for (int u = 0; u < LB; ++u) {
+                        const int p = p0 - u;
+                        const size_t ps = (static_cast<size_t>(p < 0 ? 0 : p) * a.nCG + cg) * CHW + ch;
+                        wi[u] = tagged_load(&a.incl[ps]);
+                        wa[u] = tagged_load(&a.agg_a[ps]);
+                        wh[u] = tagged_load(&a.agg_h[ps]);
+                    }
+                    bool done = false, stop = false;
+                    int adv = 0;
+#pragma unroll
+                    for (int u = 0; u < LB; ++u) {
+                        const int p = p0 - u;
+                        if (!stop && p >= 0) {
+                            if (tag_is(wi[u], tag)) {
+                                basev = tag_value(wi[u]);
+                                done = stop = true;
+                            } else if (p > 0 && tag_is(wa[u], tag) && tag_is(wh[u], tag)) {
+                                accH = lae2(accA + tag_value(wh[u]), accH);
+                                accA += tag_value(wa[u]);
+                                adv = u + 1;
+                            } else {
+                                stop = true;
                             }
                         }
-                        if (spin >= kSpinLimit) {
+                    }
+                    if (done) break;
+                    p0 -= adv;
+                    if (adv == 0) {
+                        if (++spin >= kSpinLimit) {
                             raise_error(&a.hd->err, kErrSpin);
                             break;
                         }
                         backoff();
                     }
-                    if (have || !moved) break;
                 }
                 cin = lae2(accA + basev, accH);
             }
@@ -229,14 +243,10 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
     const int ch = lane % CHW;
     const int q = wv * SUB + lane / CHW;
 
-    int tile = blockIdx.x;
-    uint32_t tag = 0;
-    if constexpr (MULTI) {
-        const TileTicket tk = take_ticket(a.hd, a.nTiles, sTicket);
-        tile = static_cast<int>(tk.tile);
-        tag = tk.tag;
-    }
-    const int jr = tile / a.nCG;             // tickets run from the last T-tile back
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
+    const int jr = tile / a.nCG;             // tiles are numbered from the last T-tile back
     const int cg = tile - jr * a.nCG;
     const int j = a.nT - 1 - jr;
     const int ftile = j * a.nCG + cg;        // the forward's index of this tile
@@ -286,10 +296,12 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
     sH[q][ch] = H;
     sP[q][ch] = A;
     sW[q][ch] = wl;
+    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
 
     // state entering the tile: h0 for the first tile, else the forward's carry
     const float hin = (j == 0) ? (cv ? ex2(lh0v * kLog2e) : 0.0f) : ex2(cin_f);
     __syncthreads();
+    const uint32_t tag = sTicket[0];
 
     float wcarry;
     if constexpr (MULTI) {
@@ -307,34 +319,48 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
             }
             float cin = 0.0f;
             if (j < a.nT - 1) {
-                // walk forward over the later tiles: acc composes tiles j+1 .. p-1
+                // look-back over the later tiles, nearest first (acc composes
+                // tiles j+1 .. p-1), LB tiles per batch of loads
+                constexpr int LB = 8;
                 float accP = 1.0f, accW = 0.0f, basev = 0.0f;
-                for (int p = j + 1; p < a.nT; ++p) {
-                    const size_t ps = (static_cast<size_t>(p) * a.nCG + cg) * CHW + ch;
-                    bool have = false, moved = false;
-                    for (uint32_t spin = 0;; ++spin) {
-                        uint64_t w;
-                        if (poll(&a.incl[ps], tag, w)) {
-                            basev = tag_value(w);
-                            have = true;
-                            break;
-                        }
-                        if (p < a.nT - 1) {
-                            uint64_t wp, ww;
-                            if (poll(&a.agg_p[ps], tag, wp) && poll(&a.agg_w[ps], tag, ww)) {
-                                accW = accW + accP * tag_value(ww);
-                                accP = accP * tag_value(wp);
-                                moved = true;
-                                break;
+                int p0 = j + 1;
+                for (uint32_t spin = 0;;) {
+                    uint64_t wi[LB], wp[LB], ww[LB];
+#pragma unroll
+                    for (int u = 0; u < LB; ++u) {
+                        const int p = p0 + u;
+                        const size_t ps = (static_cast<size_t>(p < a.nT ? p : a.nT - 1) * a.nCG + cg) * CHW + ch;
+                        wi[u] = tagged_load(&a.incl[ps]);
+                        wp[u] = tagged_load(&a.agg_p[ps]);
+                        ww[u] = tagged_load(&a.agg_w[ps]);
+                    }
+                    bool done = false, stop = false;
+                    int adv = 0;
+#pragma unroll
+                    for (int u = 0; u < LB; ++u) {
+                        const int p = p0 + u;
+                        if (!stop && p < a.nT) {
+                            if (tag_is(wi[u], tag)) {
+                                basev = tag_value(wi[u]);
+                                done = stop = true;
+                            } else if (p < a.nT - 1 && tag_is(wp[u], tag) && tag_is(ww[u], tag)) {
+                                accW = accW + accP * tag_value(ww[u]);
+                                accP = accP * tag_value(wp[u]);
+                                adv = u + 1;
+                            } else {
+                                stop = true;
                             }
                         }
-                        if (spin >= kSpinLimit) {
+                    }
+                    if (done) break;
+                    p0 += adv;
+                    if (adv == 0) {
+                        if (++spin >= kSpinLimit) {
                             raise_error(&a.hd->err, kErrSpin);
                             break;
                         }
                         backoff();
                     }
-                    if (have || !moved) break;
                 }
                 cin = accW + accP * basev;
             }
