@@ -246,19 +246,21 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_key, launches_bytes):
-    """HBM bytes per launch from committed PMC counters, if taken on the current sources."""
-    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+def traffic_from_profiles(kernel_key):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "log_scan_lab_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
-    try:
-        data = json.load(open(path))
-    except Exception:
+    src_hash, value = None, None
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 2 and parts[0] == "source_hash":
+            src_hash = parts[1]
+        if len(parts) == 3 and parts[0] == "traffic_bytes_per_launch" and parts[1] == kernel_key:
+            value = int(parts[2])
+    if src_hash != kernel_source_hash():
         return None
-    rec = data.get(kernel_key)
-    if not rec or rec.get("source_hash") != kernel_source_hash():
-        return None
-    return rec.get("bytes_per_launch")
+    return value
 
 
 def main():
@@ -270,6 +272,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ops", action="store_true", help="time only the headline step")
     ap.add_argument("--only", default=None, help="comma list of op names to time (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a device copy of exactly 64 MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -288,6 +292,14 @@ def main():
     log(f"device {gpu_name}; steps={K} warmup={W}")
 
     only = set(args.only.split(",")) if args.only else None
+    if args.copy_calibration:
+        # a plain copy of known size: 64 MiB read + 64 MiB written per dispatch
+        ca = torch.ones(16 << 20, dtype=torch.float32, device=dev)
+        cb = torch.empty_like(ca)
+        for _ in range(3):
+            cb.copy_(ca)
+        torch.cuda.synchronize()
+        del ca, cb
     specs = [
         ("log_lab", "log", 128, 64, 64),
         ("log_tiny", "log", 2, 64, 16),
@@ -365,7 +377,7 @@ def main():
             "frac": achieved / PEAK_GBPS,
             "algorithmic_bytes_per_launch": run.bwd_bytes,
             "avg_launch_us": bwd,
-            "traffic": traffic_from_profiles("log_bwd_lab", run.bwd_bytes),
+            "traffic": traffic_from_profiles("log_bwd_lab"),
         }
     if not args.no_ops and not only:
         log("copy bandwidth")
