@@ -932,10 +932,28 @@ __global__ void fill_zero_kernel(float *p, int64_t n)
 
 // ------------------------------------------------------------ host side
 
-constexpr int kW = 4;
+// Tile geometry per op: waves per workgroup and the cap on steps per lane
+// group (a lane keeps up to 3C rows of 8 floats in registers).  Eight waves
+// per workgroup measured fastest for both block ops at both shapes.
+#ifndef MGS_AFF_W
+#define MGS_AFF_W 8
+#endif
+#ifndef MGS_AFF_MAXC
+#define MGS_AFF_MAXC 8
+#endif
+#ifndef MGS_MAT_W
+#define MGS_MAT_W 8
+#endif
+#ifndef MGS_MAT_MAXC
+#define MGS_MAT_MAXC 8
+#endif
+constexpr int kAffW = MGS_AFF_W;
+constexpr int kAffMaxC = MGS_AFF_MAXC;
+constexpr int kMatW = MGS_MAT_W;
+constexpr int kMatMaxC = MGS_MAT_MAXC;
 
 BlockGeom make_geom(int64_t B, int64_t T, int64_t d, int64_t k, int agg_words, int incl_words,
-                    int max_c)
+                    int W, int max_c)
 {
     BlockGeom g{};
     g.T = static_cast<int>(T);
@@ -944,8 +962,8 @@ BlockGeom make_geom(int64_t B, int64_t T, int64_t d, int64_t k, int agg_words, i
     g.nb = static_cast<int>(d / k);
     g.nchain = B * g.nb;
     g.G = 4;
-    g.W = kW;
-    const int nch = 2 * kW;
+    g.W = W;
+    const int nch = 2 * W;
     int C = 1;
     while (C < max_c && static_cast<int64_t>(nch) * C < T) C *= 2;
     g.C = C;
@@ -982,34 +1000,43 @@ BlkArgs base_args(const BlockGeom &g, void *ws)
     return a;
 }
 
-#define MGS_BLOCK_LAUNCH(KERNEL, g, args, s)                                                      \
-    do {                                                                                          \
-        const dim3 grid_(g.nTiles), block_(64 * kW);                                              \
-        const bool multi_ = g.nT > 1;                                                             \
+// Launcher of one kernel family for every chunk length C <= MAXC.
+#define MGS_DEFINE_LAUNCHER(NAME, KERNEL)                                                         \
+    template <int W, int C>                                                                       \
+    void NAME##_c(const BlockGeom &g, const BlkArgs &a, hipStream_t s)                            \
+    {                                                                                             \
+        if (g.nT > 1)                                                                             \
+            hipLaunchKernelGGL((KERNEL<C, W, true>), dim3(g.nTiles), dim3(64 * W), 0, s, a);      \
+        else                                                                                      \
+            hipLaunchKernelGGL((KERNEL<C, W, false>), dim3(g.nTiles), dim3(64 * W), 0, s, a);     \
+    }                                                                                             \
+    template <int W, int MAXC>                                                                    \
+    void NAME(const BlockGeom &g, const BlkArgs &a, hipStream_t s)                                \
+    {                                                                                             \
         switch (g.C) {                                                                            \
-        case 1: if (multi_) hipLaunchKernelGGL((KERNEL<1, kW, true>), grid_, block_, 0, s, args); \
-                else hipLaunchKernelGGL((KERNEL<1, kW, false>), grid_, block_, 0, s, args); break; \
-        case 2: if (multi_) hipLaunchKernelGGL((KERNEL<2, kW, true>), grid_, block_, 0, s, args); \
-                else hipLaunchKernelGGL((KERNEL<2, kW, false>), grid_, block_, 0, s, args); break; \
-        case 4: if (multi_) hipLaunchKernelGGL((KERNEL<4, kW, true>), grid_, block_, 0, s, args); \
-                else hipLaunchKernelGGL((KERNEL<4, kW, false>), grid_, block_, 0, s, args); break; \
-        case 8: if (multi_) hipLaunchKernelGGL((KERNEL<8, kW, true>), grid_, block_, 0, s, args); \
-                else hipLaunchKernelGGL((KERNEL<8, kW, false>), grid_, block_, 0, s, args); break; \
-        default: if (multi_) hipLaunchKernelGGL((KERNEL<16, kW, true>), grid_, block_, 0, s, args); \
-                else hipLaunchKernelGGL((KERNEL<16, kW, false>), grid_, block_, 0, s, args); break; \
+        case 1: NAME##_c<W, 1>(g, a, s); break;                                                   \
+        case 2: NAME##_c<W, 2>(g, a, s); break;                                                   \
+        case 4: if constexpr (MAXC >= 4) NAME##_c<W, 4>(g, a, s); break;                          \
+        case 8: if constexpr (MAXC >= 8) NAME##_c<W, 8>(g, a, s); break;                          \
+        default: if constexpr (MAXC >= 16) NAME##_c<W, 16>(g, a, s); break;                       \
         }                                                                                         \
-    } while (0)
+    }
+
+MGS_DEFINE_LAUNCHER(launch_baffine_fwd, baffine_fwd_kernel)
+MGS_DEFINE_LAUNCHER(launch_baffine_bwd, baffine_bwd_kernel)
+MGS_DEFINE_LAUNCHER(launch_bmatrix_fwd, bmatrix_fwd_kernel)
+MGS_DEFINE_LAUNCHER(launch_bmatrix_bwd, bmatrix_bwd_kernel)
 
 }  // namespace
 
 BlockGeom block_affine_geometry(int64_t B, int64_t T, int64_t d, int64_t k)
 {
-    return make_geom(B, T, d, k, 9, 1, 16);
+    return make_geom(B, T, d, k, 9, 1, kAffW, kAffMaxC);
 }
 
 BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k)
 {
-    return make_geom(B, T, d, k, 16, 8, 8);
+    return make_geom(B, T, d, k, 16, 8, kMatW, kMatMaxC);
 }
 
 hipError_t launch_block_affine_fwd(const BlockGeom &g, const float *A, const float *b,
@@ -1018,7 +1045,7 @@ hipError_t launch_block_affine_fwd(const BlockGeom &g, const float *A, const flo
     BlkArgs a = base_args(g, ws);
     a.A = A; a.x = b; a.out = h;
     a.h0 = h0 ? h0 : reinterpret_cast<const float *>(static_cast<char *>(ws) + g.off_zeros);
-    MGS_BLOCK_LAUNCH(baffine_fwd_kernel, g, a, s);
+    launch_baffine_fwd<kAffW, kAffMaxC>(g, a, s);
     return hipGetLastError();
 }
 
@@ -1029,7 +1056,7 @@ hipError_t launch_block_affine_bwd(const BlockGeom &g, const float *A, const flo
     BlkArgs a = base_args(g, ws);
     a.A = A; a.x = h; a.y = dh; a.out = dA; a.out2 = db; a.out3 = dh0;
     a.h0 = h0 ? h0 : reinterpret_cast<const float *>(static_cast<char *>(ws) + g.off_zeros);
-    MGS_BLOCK_LAUNCH(baffine_bwd_kernel, g, a, s);
+    launch_baffine_bwd<kAffW, kAffMaxC>(g, a, s);
     return hipGetLastError();
 }
 
@@ -1038,7 +1065,7 @@ hipError_t launch_block_matrix_fwd(const BlockGeom &g, const float *A, float *P,
 {
     BlkArgs a = base_args(g, ws);
     a.A = A; a.out = P;
-    MGS_BLOCK_LAUNCH(bmatrix_fwd_kernel, g, a, s);
+    launch_bmatrix_fwd<kMatW, kMatMaxC>(g, a, s);
     return hipGetLastError();
 }
 
@@ -1048,7 +1075,7 @@ hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const flo
 {
     BlkArgs a = base_args(g, ws);
     a.A = A; a.x = P; a.y = dP; a.out = dA;
-    MGS_BLOCK_LAUNCH(bmatrix_bwd_kernel, g, a, s);
+    launch_bmatrix_bwd<kMatW, kMatMaxC>(g, a, s);
     return hipGetLastError();
 }
 

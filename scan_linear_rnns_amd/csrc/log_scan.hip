@@ -147,7 +147,7 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
                 TA += sLA[p][ch];
             }
             const size_t slot = static_cast<size_t>(tile) * CHW + ch;
-            if (j > 0 && j < a.nT - 1) {
+            if (j < a.nT - 1) {
                 tagged_store(&a.agg_a[slot], tag, TA);
                 tagged_store(&a.agg_h[slot], tag, TH);
             }
@@ -157,7 +157,10 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
                 // Decoupled look-back over the earlier tiles, nearest first, LB
                 // tiles per batch of loads: stop at the first tile whose
                 // inclusive state is published, composing the aggregates of the
-                // tiles passed on the way (acc covers tiles p+1 .. j-1).
+                // tiles passed on the way (acc covers tiles p+1 .. j-1).  Every
+                // tile publishes its aggregate, so a walk that reaches the start
+                // of the sequence ends there with the known h0: no tile ever
+                // waits for another tile's look-back to finish.
                 constexpr int LB = 8;
                 float accA = 0.0f, accH = -kInf, basev = lh0;
                 int p0 = j - 1;
@@ -176,17 +179,18 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
 #pragma unroll
                     for (int u = 0; u < LB; ++u) {
                         const int p = p0 - u;
-                        if (!stop && p >= 0) {
-                            if (tag_is(wi[u], tag)) {
-                                basev = tag_value(wi[u]);
-                                done = stop = true;
-                            } else if (p > 0 && tag_is(wa[u], tag) && tag_is(wh[u], tag)) {
-                                accH = lae2(accA + tag_value(wh[u]), accH);
-                                accA += tag_value(wa[u]);
-                                adv = u + 1;
-                            } else {
-                                stop = true;
-                            }
+                        if (stop) continue;
+                        if (p < 0) {
+                            done = stop = true;          // reached the start: base is h0
+                        } else if (tag_is(wi[u], tag)) {
+                            basev = tag_value(wi[u]);
+                            done = stop = true;
+                        } else if (tag_is(wa[u], tag) && tag_is(wh[u], tag)) {
+                            accH = lae2(accA + tag_value(wh[u]), accH);
+                            accA += tag_value(wa[u]);
+                            adv = u + 1;
+                        } else {
+                            stop = true;
                         }
                     }
                     if (done) break;
@@ -313,14 +317,15 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
                 TP = sP[p][ch] * TP;
             }
             const size_t slot = static_cast<size_t>(ftile) * CHW + ch;
-            if (j > 0 && j < a.nT - 1) {
+            if (j > 0) {
                 tagged_store(&a.agg_p[slot], tag, TP);
                 tagged_store(&a.agg_w[slot], tag, TW);
             }
             float cin = 0.0f;
             if (j < a.nT - 1) {
                 // look-back over the later tiles, nearest first (acc composes
-                // tiles j+1 .. p-1), LB tiles per batch of loads
+                // tiles j+1 .. p-1), LB tiles per batch of loads; a walk that
+                // passes the last tile ends there (w = 0 beyond the end)
                 constexpr int LB = 8;
                 float accP = 1.0f, accW = 0.0f, basev = 0.0f;
                 int p0 = j + 1;
@@ -339,17 +344,18 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
 #pragma unroll
                     for (int u = 0; u < LB; ++u) {
                         const int p = p0 + u;
-                        if (!stop && p < a.nT) {
-                            if (tag_is(wi[u], tag)) {
-                                basev = tag_value(wi[u]);
-                                done = stop = true;
-                            } else if (p < a.nT - 1 && tag_is(wp[u], tag) && tag_is(ww[u], tag)) {
-                                accW = accW + accP * tag_value(ww[u]);
-                                accP = accP * tag_value(wp[u]);
-                                adv = u + 1;
-                            } else {
-                                stop = true;
-                            }
+                        if (stop) continue;
+                        if (p >= a.nT) {
+                            done = stop = true;          // past the last tile: base is 0
+                        } else if (tag_is(wi[u], tag)) {
+                            basev = tag_value(wi[u]);
+                            done = stop = true;
+                        } else if (tag_is(wp[u], tag) && tag_is(ww[u], tag)) {
+                            accW = accW + accP * tag_value(ww[u]);
+                            accP = accP * tag_value(wp[u]);
+                            adv = u + 1;
+                        } else {
+                            stop = true;
                         }
                     }
                     if (done) break;
@@ -397,30 +403,57 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
 
 // ------------------------------------------------------------ host side
 
-constexpr int kCHW = 32;
-constexpr int kW = 4;
+// Tile geometry.  Sequences that fit one tile (T <= 128) use 32 chains per
+// wave row and 4 waves, which gives the most workgroups at the lab shape;
+// longer sequences use 64 chains per row and 8 waves (fewer, larger tiles
+// along T, hence shorter look-back walks).  Chosen from measured sweeps.
+#ifndef MGS_LOG_SHORT_T
+#define MGS_LOG_SHORT_T 128
+#endif
+constexpr int kShortT = MGS_LOG_SHORT_T;
+constexpr int kMaxC = 16;
 
-template <int C>
+template <int CHW, int W, int C>
 hipError_t launch_fwd_c(const LogGeom &g, const LogFwdArgs &args, hipStream_t s)
 {
-    const dim3 grid(g.nTiles), block(64 * kW);
+    const dim3 grid(g.nTiles), block(64 * W);
     if (g.nT > 1)
-        hipLaunchKernelGGL((log_fwd_kernel<kCHW, C, kW, true>), grid, block, 0, s, args);
+        hipLaunchKernelGGL((log_fwd_kernel<CHW, C, W, true>), grid, block, 0, s, args);
     else
-        hipLaunchKernelGGL((log_fwd_kernel<kCHW, C, kW, false>), grid, block, 0, s, args);
+        hipLaunchKernelGGL((log_fwd_kernel<CHW, C, W, false>), grid, block, 0, s, args);
     return hipGetLastError();
 }
 
-template <int C>
+template <int CHW, int W, int C>
 hipError_t launch_bwd_c(const LogGeom &g, const LogBwdArgs &args, hipStream_t s)
 {
-    const dim3 grid(g.nTiles), block(64 * kW);
+    const dim3 grid(g.nTiles), block(64 * W);
     if (g.nT > 1)
-        hipLaunchKernelGGL((log_bwd_kernel<kCHW, C, kW, true>), grid, block, 0, s, args);
+        hipLaunchKernelGGL((log_bwd_kernel<CHW, C, W, true>), grid, block, 0, s, args);
     else
-        hipLaunchKernelGGL((log_bwd_kernel<kCHW, C, kW, false>), grid, block, 0, s, args);
+        hipLaunchKernelGGL((log_bwd_kernel<CHW, C, W, false>), grid, block, 0, s, args);
     return hipGetLastError();
 }
+
+#define MGS_LOG_DISPATCH(FN, g, a, s)                                                             \
+    do {                                                                                          \
+        if ((g).CHW == 32) {                                                                      \
+            switch ((g).C) {                                                                      \
+            case 1: return FN<32, 4, 1>(g, a, s);                                                 \
+            case 2: return FN<32, 4, 2>(g, a, s);                                                 \
+            case 4: return FN<32, 4, 4>(g, a, s);                                                 \
+            case 8: return FN<32, 4, 8>(g, a, s);                                                 \
+            default: return FN<32, 4, 16>(g, a, s);                                               \
+            }                                                                                     \
+        }                                                                                         \
+        switch ((g).C) {                                                                          \
+        case 1: return FN<64, 8, 1>(g, a, s);                                                     \
+        case 2: return FN<64, 8, 2>(g, a, s);                                                     \
+        case 4: return FN<64, 8, 4>(g, a, s);                                                     \
+        case 8: return FN<64, 8, 8>(g, a, s);                                                     \
+        default: return FN<64, 8, 16>(g, a, s);                                                   \
+        }                                                                                         \
+    } while (0)
 
 }  // namespace
 
@@ -430,17 +463,18 @@ LogGeom log_geometry(int64_t B, int64_t T, int64_t d)
     g.S = B * d;
     g.T = static_cast<int>(T);
     g.d = static_cast<int>(d);
-    g.CHW = kCHW;
-    g.W = kW;
-    const int nch = kW * (64 / kCHW);
+    const bool short_t = T <= kShortT;
+    g.CHW = short_t ? 32 : 64;
+    g.W = short_t ? 4 : 8;
+    const int nch = g.W * (64 / g.CHW);
     int C = 1;
-    while (C < 16 && static_cast<int64_t>(nch) * C < T) C *= 2;
+    while (C < kMaxC && static_cast<int64_t>(nch) * C < T) C *= 2;
     g.C = C;
     g.TT = nch * C;
     g.nT = static_cast<int>((T + g.TT - 1) / g.TT);
-    g.nCG = static_cast<int>((g.S + kCHW - 1) / kCHW);
+    g.nCG = static_cast<int>((g.S + g.CHW - 1) / g.CHW);
     g.nTiles = g.nT * g.nCG;
-    const size_t slots = static_cast<size_t>(g.nTiles) * kCHW;
+    const size_t slots = static_cast<size_t>(g.nTiles) * g.CHW;
     size_t off = sizeof(WsHeader);
     if (g.nT > 1) {
         g.off_fagg_a = off; off = align256(off + slots * 8);
@@ -470,13 +504,7 @@ hipError_t launch_log_fwd(const LogGeom &g, const float *la, const float *lb, co
         a.incl = reinterpret_cast<uint64_t *>(w + g.off_fincl);
         a.carry = reinterpret_cast<float *>(w + g.off_carry);
     }
-    switch (g.C) {
-    case 1: return launch_fwd_c<1>(g, a, s);
-    case 2: return launch_fwd_c<2>(g, a, s);
-    case 4: return launch_fwd_c<4>(g, a, s);
-    case 8: return launch_fwd_c<8>(g, a, s);
-    default: return launch_fwd_c<16>(g, a, s);
-    }
+    MGS_LOG_DISPATCH(launch_fwd_c, g, a, s);
 }
 
 hipError_t launch_log_bwd(const LogGeom &g, const float *la, const float *lb, const float *lh0,
@@ -496,13 +524,7 @@ hipError_t launch_log_bwd(const LogGeom &g, const float *la, const float *lb, co
         a.incl = reinterpret_cast<uint64_t *>(w + g.off_bincl);
         a.carry = reinterpret_cast<const float *>(w + g.off_carry);
     }
-    switch (g.C) {
-    case 1: return launch_bwd_c<1>(g, a, s);
-    case 2: return launch_bwd_c<2>(g, a, s);
-    case 4: return launch_bwd_c<4>(g, a, s);
-    case 8: return launch_bwd_c<8>(g, a, s);
-    default: return launch_bwd_c<16>(g, a, s);
-    }
+    MGS_LOG_DISPATCH(launch_bwd_c, g, a, s);
 }
 
 }  // namespace mgs
