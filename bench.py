@@ -114,7 +114,7 @@ class OpRun:
                 A, b, dh, dP = xs
                 Pm, dA = torch.empty_like(A), torch.empty_like(A)
                 fa = (P(A), P(Pm), B, T, d, 8, P(ws), ws.numel())
-                ba = (P(A), P(Pm), P(dP), P(dA), B, T, d, 8, P(ws), ws.numel())
+                ba = (P(A), P(dP), P(dA), B, T, d, 8, P(ws), ws.numel(), 1)
                 fn_f, fn_b = self.lib.mgs_block_matrix_scan_fwd, self.lib.mgs_block_matrix_scan_bwd
                 keep = xs + [Pm, dA, ws]
             self.sets.append((fn_f, fa, fn_b, ba))

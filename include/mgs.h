@@ -166,12 +166,18 @@ mgs_status mgs_block_matrix_scan_fwd(const float *A, float *P,
 /*
  * Backward of mgs_block_matrix_scan_fwd for L = sum_t <dP_t, P_t>:
  *     G_T = dP_T,  G_t = dP_t + A_{t+1}^T G_{t+1},  dA_t = G_t P_{t-1}^T.
- *   P : (B,T,d/k,k,k) in, the forward's output (supplies P_{t-1});
- *   dP : in;  dA : out (same shape).
+ * P_{t-1} is recomputed from A and the state entering each chunk, which the
+ * forward stores in the workspace (one 8 x 8 block per chain per chunk of
+ * steps); P itself is not read.
+ *   dP : in;  dA : out (shape of A).
+ * fwd_state_valid != 0 promises that mgs_block_matrix_scan_fwd ran on this A
+ * with this workspace since it was last used by another call; with 0 the
+ * backward first recomputes those states itself (one more kernel launch).
  */
-mgs_status mgs_block_matrix_scan_bwd(const float *A, const float *P, const float *dP, float *dA,
+mgs_status mgs_block_matrix_scan_bwd(const float *A, const float *dP, float *dA,
                                      int64_t B, int64_t T, int64_t d, int64_t k,
-                                     void *workspace, size_t workspace_bytes, void *stream);
+                                     void *workspace, size_t workspace_bytes, int fwd_state_valid,
+                                     void *stream);
 
 #ifdef __cplusplus
 }

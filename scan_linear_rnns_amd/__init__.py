@@ -197,17 +197,19 @@ def mgs_block_matrix_scan_fwd(A, k=8, P=None, ws=None, stream=None):
     return P, ws
 
 
-def mgs_block_matrix_scan_bwd(A, P, dP, k=8, ws=None, dA=None, stream=None):
-    """dA for L = sum(dP * P); P is the forward's output."""
+def mgs_block_matrix_scan_bwd(A, dP, k=8, ws=None, fwd_state_valid=False, dA=None, stream=None):
+    """dA for L = sum(dP * P).  Pass the forward's workspace with fwd_state_valid=True
+    to reuse its saved chunk states; otherwise they are recomputed first."""
     import torch
     B, T, d = _block_dims(A, k)
     _check_tensor("A", A, (B, T, d // k, k, k))
-    _check_tensor("P", P, tuple(A.shape), A.device)
     _check_tensor("dP", dP, tuple(A.shape), A.device)
     if dA is None:
         dA = torch.empty_like(A)
     if ws is None:
         ws = workspace(mgs_block_matrix_scan_workspace_size(B, T, d, k), A.device)
-    check(load().mgs_block_matrix_scan_bwd(_ptr(A), _ptr(P), _ptr(dP), _ptr(dA), B, T, d, k, _ptr(ws),
-                                           ws.numel(), _stream(stream)), "mgs_block_matrix_scan_bwd")
+        fwd_state_valid = False
+    check(load().mgs_block_matrix_scan_bwd(_ptr(A), _ptr(dP), _ptr(dA), B, T, d, k, _ptr(ws), ws.numel(),
+                                           int(bool(fwd_state_valid)), _stream(stream)),
+          "mgs_block_matrix_scan_bwd")
     return dA

@@ -348,6 +348,7 @@ struct BlkArgs {
     int T, d, nb, nCG, nT, nTiles;
     WsHeader *hd;
     uint64_t *agg, *incl;
+    float *pstate;       // cumulative product: state entering each chunk, [tile][chunk][slot][8]
 };
 
 struct Tile {
@@ -755,6 +756,13 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
 #pragma unroll
         for (int s = 0; s < 8; ++s) P[s] = np[s];
     }
+    // the state entering this chunk, for the backward's recompute (slot order kept)
+    {
+        float *ps = a.pstate + ((static_cast<size_t>(ftile) * NCH + tl.q) * 32 + tl.slot) * 8;
+        *reinterpret_cast<float4 *>(ps) = make_float4(P[0], P[1], P[2], P[3]);
+        *reinterpret_cast<float4 *>(ps + 4) = make_float4(P[4], P[5], P[6], P[7]);
+    }
+    if (a.out == nullptr) return;   // states only (requested by a backward)
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         float np[8];
@@ -783,24 +791,37 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
     const Tile tl = make_tile<C, W>(a, tile, true);
     const int ftile = tl.j * a.nCG + tl.cg;
 
-    float ATr[C][8], Gr[C][8], Pp[C][8];   // rows of A_t^T, dP_t, P_{t-1}
+    float ATr[C][8], Gr[C][8];   // rows of A_t^T, dP_t
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int t = clampT(tl.t0 + i, a.T);
         load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
         load_row(a.y + tl.ablk0 + t * tl.astep, tl.v, Gr[i]);
-        load_row(a.x + tl.ablk0 + (t > 0 ? t - 1 : 0) * tl.astep, tl.v, Pp[i]);
+    }
+    // row v of P_{s-1}^T (column v of the state entering the chunk), saved by
+    // the forward in its slot order: row m of P sits in lane m's slots, column
+    // c of it at slot c ^ (m & 4)
+    float PT[C][8];
+    {
+        const float *ps = a.pstate + ((static_cast<size_t>(ftile) * NCH + tl.q) * 32 + (tl.slot & ~7)) * 8;
+        const int lo = tl.v & 4;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int m = s ^ lo;
+            PT[0][s] = ps[m * 8 + (tl.v ^ (m & 4))];
+        }
     }
 #pragma unroll
     for (int i = 0; i < C; ++i) {
-        const int t = tl.t0 + i;
-        if (t == 0) eye_row(tl.v, Pp[i]);
-        if (!(tl.cv && t < a.T)) {
+        if (!(tl.cv && tl.t0 + i < a.T)) {
             eye_row(tl.v, ATr[i]);
 #pragma unroll
             for (int s = 0; s < 8; ++s) Gr[i][s] = 0.0f;
         }
     }
+    // recompute P_{t-1}^T = P_{t-2}^T A_{t-1}^T across the chunk
+#pragma unroll
+    for (int i = 1; i < C; ++i) mm8(PT[i - 1], ATr[i - 1], PT[i]);
 
     float Psi[8], Wl[8];
 #pragma unroll
@@ -916,7 +937,7 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
         float G[8], dAr[8], nw[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) G[s] = Gr[i][s] + Wc[s];
-        mmT8(G, Pp[i], dAr);
+        mm8(G, PT[i], dAr);           // dA_t = G_t P_{t-1}^T
         mm8(ATr[i], G, nw);
 #pragma unroll
         for (int s = 0; s < 8; ++s) Wc[s] = nw[s];
@@ -953,7 +974,7 @@ constexpr int kMatW = MGS_MAT_W;
 constexpr int kMatMaxC = MGS_MAT_MAXC;
 
 BlockGeom make_geom(int64_t B, int64_t T, int64_t d, int64_t k, int agg_words, int incl_words,
-                    int W, int max_c)
+                    int W, int max_c, bool pstate)
 {
     BlockGeom g{};
     g.T = static_cast<int>(T);
@@ -976,6 +997,8 @@ BlockGeom make_geom(int64_t B, int64_t T, int64_t d, int64_t k, int agg_words, i
     size_t off = sizeof(WsHeader);
     g.off_zeros = off;   // B*d floats, never written: the h0 of calls that pass none
     off = align256(off + static_cast<size_t>(B) * d * 4);
+    g.off_pstate = off;  // cumulative product: one 8x8 state per chain per chunk
+    if (pstate) off = align256(off + static_cast<size_t>(g.nTiles) * nch * 32 * 8 * 4);
     if (g.nT > 1) {
         const size_t slots = static_cast<size_t>(g.nTiles) * 32;
         g.off_agg = off;  off = align256(off + slots * agg_words * 8);
@@ -997,6 +1020,7 @@ BlkArgs base_args(const BlockGeom &g, void *ws)
         a.agg = reinterpret_cast<uint64_t *>(w + g.off_agg);
         a.incl = reinterpret_cast<uint64_t *>(w + g.off_incl);
     }
+    a.pstate = reinterpret_cast<float *>(w + g.off_pstate);
     return a;
 }
 
@@ -1031,12 +1055,12 @@ MGS_DEFINE_LAUNCHER(launch_bmatrix_bwd, bmatrix_bwd_kernel)
 
 BlockGeom block_affine_geometry(int64_t B, int64_t T, int64_t d, int64_t k)
 {
-    return make_geom(B, T, d, k, 9, 1, kAffW, kAffMaxC);
+    return make_geom(B, T, d, k, 9, 1, kAffW, kAffMaxC, false);
 }
 
 BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k)
 {
-    return make_geom(B, T, d, k, 16, 8, kMatW, kMatMaxC);
+    return make_geom(B, T, d, k, 16, 8, kMatW, kMatMaxC, true);
 }
 
 hipError_t launch_block_affine_fwd(const BlockGeom &g, const float *A, const float *b,
@@ -1069,12 +1093,18 @@ hipError_t launch_block_matrix_fwd(const BlockGeom &g, const float *A, float *P,
     return hipGetLastError();
 }
 
-hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const float *P,
-                                   const float *dP, float *dA, void *ws,
-                                   hipStream_t s)
+hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const float *dP, float *dA,
+                                   void *ws, bool fwd_state_valid, hipStream_t s)
 {
+    if (!fwd_state_valid) {
+        BlkArgs f = base_args(g, ws);
+        f.A = A; f.out = nullptr;    // chunk states only
+        launch_bmatrix_fwd<kMatW, kMatMaxC>(g, f, s);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     BlkArgs a = base_args(g, ws);
-    a.A = A; a.x = P; a.y = dP; a.out = dA;
+    a.A = A; a.y = dP; a.out = dA;
     launch_bmatrix_bwd<kMatW, kMatMaxC>(g, a, s);
     return hipGetLastError();
 }

@@ -47,6 +47,7 @@ struct BlockGeom {
     int nCG;        // chain groups (of G chains)
     int nTiles;
     size_t off_zeros;                 // B*d zero floats standing in for an absent h0
+    size_t off_pstate;                // cumulative product: chunk-entering states
     size_t off_agg, off_incl, bytes;  // look-back payload (tagged words)
     int agg_words;  // tagged words per chain per tile in the aggregate
     int incl_words; // tagged words per chain per tile in the inclusive prefix
@@ -62,8 +63,8 @@ hipError_t launch_block_affine_bwd(const BlockGeom &g, const float *A, const flo
                                    float *dh0, void *ws, hipStream_t s);
 hipError_t launch_block_matrix_fwd(const BlockGeom &g, const float *A, float *P, void *ws,
                                    hipStream_t s);
-hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const float *P,
-                                   const float *dP, float *dA, void *ws, hipStream_t s);
+hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const float *dP, float *dA,
+                                   void *ws, bool fwd_state_valid, hipStream_t s);
 
 // zero-fill of n floats (used for gradients of an empty sequence)
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);

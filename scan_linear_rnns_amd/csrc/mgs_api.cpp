@@ -261,21 +261,21 @@ mgs_status mgs_block_matrix_scan_fwd(const float *A, float *P, int64_t B, int64_
     return hip_status(mgs::launch_block_matrix_fwd(g, A, P, workspace, as_stream(stream)));
 }
 
-mgs_status mgs_block_matrix_scan_bwd(const float *A, const float *P, const float *dP, float *dA,
-                                     int64_t B, int64_t T, int64_t d, int64_t k, void *workspace,
-                                     size_t workspace_bytes, void *stream)
+mgs_status mgs_block_matrix_scan_bwd(const float *A, const float *dP, float *dA, int64_t B, int64_t T,
+                                     int64_t d, int64_t k, void *workspace, size_t workspace_bytes,
+                                     int fwd_state_valid, void *stream)
 {
     if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
     const size_t na = static_cast<size_t>(B * T * d * k) * 4;
-    if (na > 0 && (!A || !P || !dP || !dA)) return MGS_ERR_INVALID_VALUE;
-    const Range in[] = {{A, na}, {P, na}, {dP, na}};
+    if (na > 0 && (!A || !dP || !dA)) return MGS_ERR_INVALID_VALUE;
+    const Range in[] = {{A, na}, {dP, na}};
     const Range out[] = {{dA, na}};
-    if (!all_aligned(in, 3) || !all_aligned(out, 1)) return MGS_ERR_INVALID_VALUE;
-    if (any_alias(in, 3, out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (!all_aligned(in, 2) || !all_aligned(out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (any_alias(in, 2, out, 1)) return MGS_ERR_INVALID_VALUE;
     if (na == 0) return MGS_OK;
     const mgs::BlockGeom g = mgs::block_matrix_geometry(B, T, d, k);
     if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
-    return hip_status(mgs::launch_block_matrix_bwd(g, A, P, dP, dA, workspace,
+    return hip_status(mgs::launch_block_matrix_bwd(g, A, dP, dA, workspace, fwd_state_valid != 0,
                                                    as_stream(stream)));
 }
 

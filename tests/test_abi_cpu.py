@@ -124,10 +124,12 @@ def test_block_validation(lib):
     assert mf(P=fake(0)) == INVALID
     assert mf(k=16) == UNSUPPORTED
     assert mf(nbytes=2) == WORKSPACE
-    mb = lambda P=fake(1), dA=fake(3): lib.mgs_block_matrix_scan_bwd(fake(0), P, fake(2), dA, B, T, d, k,
-                                                                    fake(9), 1 << 20, None)
-    assert mb(P=None) == INVALID
+    mb = lambda dP=fake(2), dA=fake(3), nbytes=1 << 20: lib.mgs_block_matrix_scan_bwd(
+        fake(0), dP, dA, B, T, d, k, fake(9), nbytes, 1, None)
+    assert mb(dP=None) == INVALID
     assert mb(dA=fake(2)) == INVALID
+    assert mb(dA=fake(0)) == INVALID
+    assert mb(nbytes=3) == WORKSPACE
 
 
 def test_workspace_check_validation(lib):

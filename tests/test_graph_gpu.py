@@ -76,7 +76,7 @@ def test_block_scans_graph_replays(gpu):
     h, ws = mgs.mgs_block_affine_scan_fwd(A, b, h0)
     gref = mgs.mgs_block_affine_scan_bwd(A, b, h0, h, dh, ws=ws)
     P, wsm = mgs.mgs_block_matrix_scan_fwd(A)
-    dAm = mgs.mgs_block_matrix_scan_bwd(A, P, dP, ws=wsm)
+    dAm = mgs.mgs_block_matrix_scan_bwd(A, dP, ws=wsm, fwd_state_valid=True)
     ref = [h.clone(), *[x.clone() for x in gref], P.clone(), dAm.clone()]
     outs = [torch.empty_like(h), torch.empty_like(A), torch.empty_like(b), torch.empty_like(h0),
             torch.empty_like(A), torch.empty_like(A)]
@@ -85,7 +85,7 @@ def test_block_scans_graph_replays(gpu):
         mgs.mgs_block_affine_scan_fwd(A, b, h0, h=outs[0], ws=ws)
         mgs.mgs_block_affine_scan_bwd(A, b, h0, outs[0], dh, ws=ws, out=(outs[1], outs[2], outs[3]))
         mgs.mgs_block_matrix_scan_fwd(A, P=outs[4], ws=wsm)
-        mgs.mgs_block_matrix_scan_bwd(A, outs[4], dP, ws=wsm, dA=outs[5])
+        mgs.mgs_block_matrix_scan_bwd(A, dP, ws=wsm, fwd_state_valid=True, dA=outs[5])
 
     for got in _replays(step, outs):
         for a, b_ in zip(got, ref):

@@ -169,7 +169,7 @@ def run_block(B, T, d, seed, dev, *, gate=True, h0="zero", matrix=True):
     if matrix:
         dP = to_dev(inp.dP, dev)
         P, wsm = mgs.mgs_block_matrix_scan_fwd(A)
-        dAm = mgs.mgs_block_matrix_scan_bwd(A, P, dP, ws=wsm)
+        dAm = mgs.mgs_block_matrix_scan_bwd(A, dP, ws=wsm, fwd_state_valid=True)
         ws_clean(wsm)
         out["P"], out["dA_matrix"] = to_np(P), to_np(dAm)
         ref["P"] = oracle.block_matrix_fwd(inp.A, 8)
@@ -204,6 +204,25 @@ def test_block_edges(gpu, B, T, d):
     for key in out:
         e = floored_err(out[key], ref[key])
         assert e <= BLOCK_TOL, (key, e)
+
+
+@pytest.mark.parametrize("B,T,d", [(2, 7, 16), (4, 1024, 64), (1, 2048, 8)])
+def test_matrix_bwd_without_forward_state(gpu, B, T, d):
+    """A fresh workspace: the backward recomputes the chunk states itself and
+    must give the oracle's dA, and the same bits as the path that reuses the
+    forward's states."""
+    import torch
+    import scan_linear_rnns_amd as mgs
+    say(f"matrix bwd recompute-states B={B} T={T} d={d}")
+    inp = block_inputs(B, T, d, k=8, seed=17)
+    A, dP = to_dev(inp.A, gpu), to_dev(inp.dP, gpu)
+    dA_fresh = mgs.mgs_block_matrix_scan_bwd(A, dP)
+    P, wsm = mgs.mgs_block_matrix_scan_fwd(A)
+    dA_reuse = mgs.mgs_block_matrix_scan_bwd(A, dP, ws=wsm, fwd_state_valid=True)
+    ws_clean(wsm)
+    ref = oracle.block_matrix_bwd(inp.A, inp.dP, 8)
+    assert floored_err(to_np(dA_fresh), ref) <= BLOCK_TOL
+    assert torch.equal(dA_fresh, dA_reuse)
 
 
 def test_rotation_only_long_T(gpu):
@@ -249,7 +268,7 @@ def test_determinism(gpu):
         hb, wsb = mgs.mgs_block_affine_scan_fwd(A, b, None)
         gb = mgs.mgs_block_affine_scan_bwd(A, b, None, hb, dh2, ws=wsb)
         P, wsm = mgs.mgs_block_matrix_scan_fwd(A)
-        dAm = mgs.mgs_block_matrix_scan_bwd(A, P, dP, ws=wsm)
+        dAm = mgs.mgs_block_matrix_scan_bwd(A, dP, ws=wsm, fwd_state_valid=True)
         cur = [hb.clone(), P.clone(), dAm.clone()] + [x.clone() for x in gb]
         if firstb is None:
             firstb = cur
