@@ -237,7 +237,7 @@ __device__ __forceinline__ void store_row(float *p, int v, const float *R)
 
 // ------------------------------------------------------------ look-back
 
-// Lanes of wave 0 take part; lanes 32..63 mirror lanes 0..31 (same slot).
+// All lanes of one wave take part; lanes 32..63 mirror lanes 0..31 (same slot).
 // Returns the nearest tile p (in the direction dir = -1: earlier tiles,
 // +1: later tiles) whose IW-word inclusive state is published, with the state
 // in xi; -1 if the spin limit was hit.  One batch of loads polls the first word
@@ -400,14 +400,88 @@ __device__ __forceinline__ float load_h0(const BlkArgs &a, const Tile &tl)
     return a.h0[tl.bb * a.d + tl.jb * 8 + tl.v];
 }
 
+// ============================================ in-tile scan of chunk aggregates
+// Each half-wave holds the aggregate of one chunk q = 2 * wave + sub.  A
+// Kogge-Stone scan over the NCH chunks runs on all waves at once: in round r
+// every chunk composes its running composite with the one 2^r chunks before it
+// (DIR = +1) or after it (DIR = -1), read from one of two LDS buffers in turn,
+// with one barrier per round.  Afterwards chunk q holds the composite of
+// chunks 0..q (DIR = +1) or q..NCH-1 (DIR = -1), and a copy sits in buffer
+// ks_final<NCH>() for the fix-up.  The rule is the same in both directions:
+//     (M, v) o (M', v') = (M M', M v' + v)
+// with v absent (cumulative product), one value per lane (block-affine) or a
+// matrix row (cumulative-product backward).
+
+enum AggKind : int { kMat = 0, kMatVec = 1, kMatMat = 2 };
+
+template <int KIND>
+struct AggShape {
+    static constexpr int words = KIND == kMat ? 8 : (KIND == kMatVec ? 9 : 16);
+    static constexpr int stride = words | 1;   // odd LDS stride: lanes hit distinct banks
+};
+
+template <int NCH>
+__host__ __device__ constexpr int ks_final()
+{
+    int r = 0;
+    while ((1 << r) < NCH) ++r;
+    return r & 1;
+}
+
+template <int KIND>
+__device__ __forceinline__ void compose_into(float *X, const float *R)
+{
+    if constexpr (KIND == kMatVec) X[8] = mv8(X, R[8], X[8]);
+    if constexpr (KIND == kMatMat) {
+        float nw[8];
+        mm8(X, R + 8, nw);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) X[8 + s] += nw[s];
+    }
+    float np[8];
+    mm8(X, R, np);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) X[s] = np[s];
+}
+
+template <int KIND, int NCH>
+__device__ __forceinline__ void ks_store(float (*buf)[32][AggShape<KIND>::stride], int q, int slot, const float *X)
+{
+#pragma unroll
+    for (int e = 0; e < AggShape<KIND>::words; ++e) buf[q][slot][e] = X[e];
+}
+
+// Precondition: buffer 0 holds every chunk's aggregate and a barrier has passed.
+template <int KIND, int NCH, int DIR>
+__device__ __forceinline__ void ks_scan(float (*buf)[NCH][32][AggShape<KIND>::stride], int q, int slot, float *X)
+{
+    constexpr int AW = AggShape<KIND>::words;
+#pragma unroll
+    for (int r = 0; (1 << r) < NCH; ++r) {
+        if (r > 0) {
+            ks_store<KIND, NCH>(buf[r & 1], q, slot, X);
+            __syncthreads();
+        }
+        const int qn = q - DIR * (1 << r);
+        if (qn >= 0 && qn < NCH) {
+            float R[AW];
+#pragma unroll
+            for (int e = 0; e < AW; ++e) R[e] = buf[r & 1][qn][slot][e];
+            compose_into<KIND>(X, R);
+        }
+    }
+    ks_store<KIND, NCH>(buf[ks_final<NCH>()], q, slot, X);
+}
+
 // ======================================================= block-affine fwd
 
 template <int C, int W, bool MULTI>
 __global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
 {
     constexpr int NCH = 2 * W;
-    constexpr int AW = 9;   // row of Phi + one entry of u
-    __shared__ float sAgg[NCH][32][AW];
+    using S = AggShape<kMatVec>;
+    constexpr int FIN = ks_final<NCH>();
+    __shared__ float sKS[2][NCH][32][S::stride];
     __shared__ float sCarry[32];
     __shared__ uint32_t sTicket[2];
 
@@ -433,53 +507,31 @@ __global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
             bv[i] = 0.0f;
         }
 
-    // chunk aggregate from a zero state: Phi = A_e..A_s, u = local h_e
-    float Phi[8], u = bv[0];
+    // chunk aggregate from a zero state: X = (A_e..A_s, local h_e)
+    float X[S::words];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) Phi[s] = Ar[0][s];
+    for (int s = 0; s < 8; ++s) X[s] = Ar[0][s];
+    X[8] = bv[0];
 #pragma unroll
     for (int i = 1; i < C; ++i) {
         float np[8];
-        mm8(Ar[i], Phi, np);
-        u = mv8(Ar[i], u, bv[i]);
+        mm8(Ar[i], X, np);
+        X[8] = mv8(Ar[i], X[8], bv[i]);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) Phi[s] = np[s];
+        for (int s = 0; s < 8; ++s) X[s] = np[s];
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) sAgg[tl.q][tl.slot][s] = Phi[s];
-    sAgg[tl.q][tl.slot][8] = u;
+    ks_store<kMatVec, NCH>(sKS[0], tl.q, tl.slot, X);
     if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
     __syncthreads();
     const uint32_t tag = sTicket[0];
 
     float x;
     if constexpr (MULTI) {
-        if (tl.wv == 0) {
-            // tile aggregate; sAgg[q] becomes the composite of chunks 0..q
-            float TP[8], Tu = sAgg[0][tl.slot][8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) TP[s] = sAgg[0][tl.slot][s];
-            for (int q = 1; q < NCH; ++q) {
-                float R[8], np[8];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) R[s] = sAgg[q][tl.slot][s];
-                mm8(R, TP, np);
-                Tu = mv8(R, Tu, sAgg[q][tl.slot][8]);
-#pragma unroll
-                for (int s = 0; s < 8; ++s) TP[s] = np[s];
-                if (tl.sub == 0) {
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) sAgg[q][tl.slot][s] = TP[s];
-                    sAgg[q][tl.slot][8] = Tu;
-                }
-            }
-            if (tl.sub == 0 && tl.j > 0 && tl.j < a.nT - 1) {
-                float pay[AW];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) pay[s] = TP[s];
-                pay[8] = Tu;
-                publish<AW>(a.agg, ftile, tl.slot, tag, pay);
-            }
+        ks_scan<kMatVec, NCH, +1>(sKS, tl.q, tl.slot, X);
+        // the last wave's upper half holds the tile aggregate and runs the look-back
+        if (tl.wv == W - 1) {
+            const bool owner = tl.sub == 1;
+            if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<S::words>(a.agg, ftile, tl.slot, tag, X);
             float xin = xh0;
             if (tl.j > 0) {
                 float xi[1];
@@ -488,25 +540,25 @@ __global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
                 constexpr int NB = 4;
                 for (int p = ps + 1; p < tl.j; p += NB) {
                     const int cnt = min(NB, tl.j - p);
-                    float ag[NB][AW];
-                    load_aggregates<AW, NB>(a.agg, p, +1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
+                    float ag[NB][S::words];
+                    load_aggregates<S::words, NB>(a.agg, p, +1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
 #pragma unroll
                     for (int u = 0; u < NB; ++u)
                         if (u < cnt) xin = mv8(ag[u], xin, ag[u][8]);
                 }
             }
-            if (tl.sub == 0 && tl.j < a.nT - 1) {
-                const float xo = mv8(TP, xin, Tu);
+            if (owner && tl.j < a.nT - 1) {
+                const float xo = mv8(X, xin, X[8]);
                 publish<1>(a.incl, ftile, tl.slot, tag, &xo);
             }
-            if (tl.sub == 0) sCarry[tl.slot] = xin;
+            if (owner) sCarry[tl.slot] = xin;
         }
         __syncthreads();
         x = sCarry[tl.slot];
-        if (tl.q > 0) x = mv8(sAgg[tl.q - 1][tl.slot], x, sAgg[tl.q - 1][tl.slot][8]);
+        if (tl.q > 0) x = mv8(sKS[FIN][tl.q - 1][tl.slot], x, sKS[FIN][tl.q - 1][tl.slot][8]);
     } else {
         x = xh0;
-        for (int q = 0; q < tl.q; ++q) x = mv8(sAgg[q][tl.slot], x, sAgg[q][tl.slot][8]);
+        for (int q = 0; q < tl.q; ++q) x = mv8(sKS[0][q][tl.slot], x, sKS[0][q][tl.slot][8]);
     }
 
     // re-run the recurrence from the true state entering the chunk
@@ -526,8 +578,9 @@ template <int C, int W, bool MULTI>
 __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
 {
     constexpr int NCH = 2 * W;
-    constexpr int AW = 9;
-    __shared__ float sAgg[NCH][32][AW];
+    using S = AggShape<kMatVec>;
+    constexpr int FIN = ks_final<NCH>();
+    __shared__ float sKS[2][NCH][32][S::stride];
     __shared__ float sCarry[32];
     __shared__ uint32_t sTicket[2];
 
@@ -557,54 +610,31 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
         }
     }
 
-    // chunk aggregate from a zero carry, walking t downwards
-    float Psi[8], Wl;
+    // chunk aggregate from a zero carry, walking t downwards: X = (Psi, Wl)
+    float X[S::words];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) Psi[s] = ATr[C - 1][s];
-    Wl = mv8(ATr[C - 1], gv[C - 1], 0.0f);
+    for (int s = 0; s < 8; ++s) X[s] = ATr[C - 1][s];
+    X[8] = mv8(ATr[C - 1], gv[C - 1], 0.0f);
 #pragma unroll
     for (int i = C - 2; i >= 0; --i) {
         float np[8];
-        mm8(ATr[i], Psi, np);
-        Wl = mv8(ATr[i], gv[i] + Wl, 0.0f);
+        mm8(ATr[i], X, np);
+        X[8] = mv8(ATr[i], gv[i] + X[8], 0.0f);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) Psi[s] = np[s];
+        for (int s = 0; s < 8; ++s) X[s] = np[s];
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) sAgg[tl.q][tl.slot][s] = Psi[s];
-    sAgg[tl.q][tl.slot][8] = Wl;
+    ks_store<kMatVec, NCH>(sKS[0], tl.q, tl.slot, X);
     if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
     __syncthreads();
     const uint32_t tag = sTicket[0];
 
     float w;
     if constexpr (MULTI) {
+        ks_scan<kMatVec, NCH, -1>(sKS, tl.q, tl.slot, X);
+        // wave 0's lower half holds the tile aggregate and runs the look-back
         if (tl.wv == 0) {
-            // tile aggregate; sAgg[q] becomes the composite of chunks q..NCH-1
-            float TP[8], Tw = sAgg[NCH - 1][tl.slot][8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) TP[s] = sAgg[NCH - 1][tl.slot][s];
-            for (int q = NCH - 2; q >= 0; --q) {
-                float R[8], np[8];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) R[s] = sAgg[q][tl.slot][s];
-                mm8(R, TP, np);
-                Tw = mv8(R, Tw, sAgg[q][tl.slot][8]);
-#pragma unroll
-                for (int s = 0; s < 8; ++s) TP[s] = np[s];
-                if (tl.sub == 0) {
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) sAgg[q][tl.slot][s] = TP[s];
-                    sAgg[q][tl.slot][8] = Tw;
-                }
-            }
-            if (tl.sub == 0 && tl.j > 0 && tl.j < a.nT - 1) {
-                float pay[AW];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) pay[s] = TP[s];
-                pay[8] = Tw;
-                publish<AW>(a.agg, ftile, tl.slot, tag, pay);
-            }
+            const bool owner = tl.sub == 0;
+            if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<S::words>(a.agg, ftile, tl.slot, tag, X);
             float win = 0.0f;
             if (tl.j < a.nT - 1) {
                 float xi[1];
@@ -614,25 +644,25 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
                 constexpr int NB = 4;
                 for (int p = pend - 1; p > tl.j; p -= NB) {
                     const int cnt = min(NB, p - tl.j);
-                    float ag[NB][AW];
-                    load_aggregates<AW, NB>(a.agg, p, -1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
+                    float ag[NB][S::words];
+                    load_aggregates<S::words, NB>(a.agg, p, -1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
 #pragma unroll
                     for (int u = 0; u < NB; ++u)
                         if (u < cnt) win = mv8(ag[u], win, ag[u][8]);
                 }
             }
-            if (tl.sub == 0 && tl.j > 0) {
-                const float wo = mv8(TP, win, Tw);
+            if (owner && tl.j > 0) {
+                const float wo = mv8(X, win, X[8]);
                 publish<1>(a.incl, ftile, tl.slot, tag, &wo);
             }
-            if (tl.sub == 0) sCarry[tl.slot] = win;
+            if (owner) sCarry[tl.slot] = win;
         }
         __syncthreads();
         w = sCarry[tl.slot];
-        if (tl.q < NCH - 1) w = mv8(sAgg[tl.q + 1][tl.slot], w, sAgg[tl.q + 1][tl.slot][8]);
+        if (tl.q < NCH - 1) w = mv8(sKS[FIN][tl.q + 1][tl.slot], w, sKS[FIN][tl.q + 1][tl.slot][8]);
     } else {
         w = 0.0f;
-        for (int q = NCH - 1; q > tl.q; --q) w = mv8(sAgg[q][tl.slot], w, sAgg[q][tl.slot][8]);
+        for (int q = NCH - 1; q > tl.q; --q) w = mv8(sKS[0][q][tl.slot], w, sKS[0][q][tl.slot][8]);
     }
 
     // re-run the reverse recurrence from the true carry; emit dA, db, dh0
@@ -657,8 +687,9 @@ template <int C, int W, bool MULTI>
 __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
 {
     constexpr int NCH = 2 * W;
-    constexpr int AW = 8;
-    __shared__ float sAgg[NCH][32][AW];
+    using S = AggShape<kMat>;
+    constexpr int FIN = ks_final<NCH>();
+    __shared__ float sKS[2][NCH][32][S::stride];
     __shared__ float sCarry[32][8];
     __shared__ uint32_t sTicket[2];
 
@@ -676,43 +707,29 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
     for (int i = 0; i < C; ++i)
         if (!(tl.cv && tl.t0 + i < a.T)) eye_row(tl.v, Ar[i]);
 
-    float Phi[8];
+    float X[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) Phi[s] = Ar[0][s];
+    for (int s = 0; s < 8; ++s) X[s] = Ar[0][s];
 #pragma unroll
     for (int i = 1; i < C; ++i) {
         float np[8];
-        mm8(Ar[i], Phi, np);
+        mm8(Ar[i], X, np);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) Phi[s] = np[s];
+        for (int s = 0; s < 8; ++s) X[s] = np[s];
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) sAgg[tl.q][tl.slot][s] = Phi[s];
+    ks_store<kMat, NCH>(sKS[0], tl.q, tl.slot, X);
     if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
     __syncthreads();
     const uint32_t tag = sTicket[0];
 
-    // composites of chunks 0..q (wave 0), tile look-back, tile carry
-    if (tl.wv == 0) {
-        float TP[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) TP[s] = sAgg[0][tl.slot][s];
-        for (int q = 1; q < NCH; ++q) {
-            float R[8], np[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) R[s] = sAgg[q][tl.slot][s];
-            mm8(R, TP, np);
-#pragma unroll
-            for (int s = 0; s < 8; ++s) TP[s] = np[s];
-            if (tl.sub == 0) {
-#pragma unroll
-                for (int s = 0; s < 8; ++s) sAgg[q][tl.slot][s] = TP[s];
-            }
-        }
-        float Pin[8];
-        eye_row(tl.v, Pin);
-        if constexpr (MULTI) {
-            if (tl.sub == 0 && tl.j > 0 && tl.j < a.nT - 1) publish<AW>(a.agg, ftile, tl.slot, tag, TP);
+    ks_scan<kMat, NCH, +1>(sKS, tl.q, tl.slot, X);   // X = composite of chunks 0..q
+    if constexpr (MULTI) {
+        // the last wave's upper half holds the tile aggregate and runs the look-back
+        if (tl.wv == W - 1) {
+            const bool owner = tl.sub == 1;
+            if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<8>(a.agg, ftile, tl.slot, tag, X);
+            float Pin[8];
+            eye_row(tl.v, Pin);
             if (tl.j > 0) {
                 float xi[8];
                 const int ps = find_inclusive<8>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, tag, &a.hd->err, xi);
@@ -723,8 +740,8 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
                 constexpr int NB = 4;
                 for (int p = ps + 1; p < tl.j; p += NB) {
                     const int cnt = min(NB, tl.j - p);
-                    float ag[NB][AW];
-                    load_aggregates<AW, NB>(a.agg, p, +1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
+                    float ag[NB][8];
+                    load_aggregates<8, NB>(a.agg, p, +1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
 #pragma unroll
                     for (int u = 0; u < NB; ++u)
                         if (u < cnt) {
@@ -735,26 +752,35 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
                         }
                 }
             }
-            if (tl.sub == 0 && tl.j < a.nT - 1) {
+            if (owner && tl.j < a.nT - 1) {
                 float Po[8];
-                mm8(TP, Pin, Po);
+                mm8(X, Pin, Po);
                 publish<8>(a.incl, ftile, tl.slot, tag, Po);
             }
-        }
-        if (tl.sub == 0) {
+            if (owner) {
 #pragma unroll
-            for (int s = 0; s < 8; ++s) sCarry[tl.slot][s] = Pin[s];
+                for (int s = 0; s < 8; ++s) sCarry[tl.slot][s] = Pin[s];
+            }
         }
     }
     __syncthreads();
+    // state entering the chunk: (composite of chunks 0..q-1) x (tile carry-in)
     float P[8];
+    if constexpr (MULTI) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) P[s] = sCarry[tl.slot][s];
-    if (tl.q > 0) {
-        float np[8];
-        mm8(sAgg[tl.q - 1][tl.slot], P, np);
+        for (int s = 0; s < 8; ++s) P[s] = sCarry[tl.slot][s];
+        if (tl.q > 0) {
+            float np[8];
+            mm8(sKS[FIN][tl.q - 1][tl.slot], P, np);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) P[s] = np[s];
+            for (int s = 0; s < 8; ++s) P[s] = np[s];
+        }
+    } else {
+        eye_row(tl.v, P);
+        if (tl.q > 0) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) P[s] = sKS[FIN][tl.q - 1][tl.slot][s];
+        }
     }
     // the state entering this chunk, for the backward's recompute (slot order kept)
     {
@@ -775,13 +801,15 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
 }
 
 // Backward: W_t = A_t^T G_t with G_t = dP_t + W_{t+1}; per chunk [s, e]
-// W_s = Psi W_{e+1} + Wl.  dA_t = G_t P_{t-1}^T with P_{t-1} read from P.
+// W_s = Psi W_{e+1} + Wl.  dA_t = G_t P_{t-1}^T, with P_{t-1} recomputed from
+// the state entering the chunk (stored by the forward) and the A_t in hand.
 template <int C, int W, bool MULTI>
 __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
 {
     constexpr int NCH = 2 * W;
-    constexpr int AW = 16;   // row of Psi, row of Wl
-    __shared__ float sAgg[NCH][32][AW];
+    using S = AggShape<kMatMat>;
+    constexpr int FIN = ks_final<NCH>();
+    __shared__ float sKS[2][NCH][32][S::stride];
     __shared__ float sCarry[32][8];
     __shared__ uint32_t sTicket[2];
 
@@ -819,115 +847,95 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
             for (int s = 0; s < 8; ++s) Gr[i][s] = 0.0f;
         }
     }
-    // recompute P_{t-1}^T = P_{t-2}^T A_{t-1}^T across the chunk
-#pragma unroll
-    for (int i = 1; i < C; ++i) mm8(PT[i - 1], ATr[i - 1], PT[i]);
 
-    float Psi[8], Wl[8];
+    // chunk aggregate from a zero carry: X = (Psi, Wl)
+    float X[S::words];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) Psi[s] = ATr[C - 1][s];
-    mm8(ATr[C - 1], Gr[C - 1], Wl);
+    for (int s = 0; s < 8; ++s) X[s] = ATr[C - 1][s];
+    mm8(ATr[C - 1], Gr[C - 1], X + 8);
 #pragma unroll
     for (int i = C - 2; i >= 0; --i) {
         float np[8], gw[8], nw[8];
-        mm8(ATr[i], Psi, np);
+        mm8(ATr[i], X, np);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) gw[s] = Gr[i][s] + Wl[s];
+        for (int s = 0; s < 8; ++s) gw[s] = Gr[i][s] + X[8 + s];
         mm8(ATr[i], gw, nw);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) { Psi[s] = np[s]; Wl[s] = nw[s]; }
+        for (int s = 0; s < 8; ++s) { X[s] = np[s]; X[8 + s] = nw[s]; }
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        sAgg[tl.q][tl.slot][s] = Psi[s];
-        sAgg[tl.q][tl.slot][8 + s] = Wl[s];
-    }
+    ks_store<kMatMat, NCH>(sKS[0], tl.q, tl.slot, X);
     if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
     __syncthreads();
     const uint32_t tag = sTicket[0];
 
-    if (tl.wv == 0) {
-        float TP[8], TW[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            TP[s] = sAgg[NCH - 1][tl.slot][s];
-            TW[s] = sAgg[NCH - 1][tl.slot][8 + s];
-        }
-        for (int q = NCH - 2; q >= 0; --q) {
-            float R[8], np[8], nw[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) R[s] = sAgg[q][tl.slot][s];
-            mm8(R, TP, np);
-            mm8(R, TW, nw);
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                TP[s] = np[s];
-                TW[s] = nw[s] + sAgg[q][tl.slot][8 + s];
-            }
-            if (tl.sub == 0) {
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    sAgg[q][tl.slot][s] = TP[s];
-                    sAgg[q][tl.slot][8 + s] = TW[s];
-                }
-            }
-        }
+    ks_scan<kMatMat, NCH, -1>(sKS, tl.q, tl.slot, X);   // X = composite of chunks q..NCH-1
+    // wave 0's lower half holds the tile aggregate and runs the look-back; the
+    // other waves meanwhile recompute P_{t-1}^T = P_{t-2}^T A_{t-1}^T
+    const bool lb_wave = MULTI && tl.wv == 0;
+    if (lb_wave) {
+        const bool owner = tl.sub == 0;
+        if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<S::words>(a.agg, ftile, tl.slot, tag, X);
         float Win[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) Win[s] = 0.0f;
-        if constexpr (MULTI) {
-            if (tl.sub == 0 && tl.j > 0 && tl.j < a.nT - 1) {
-                float pay[AW];
+        if (tl.j < a.nT - 1) {
+            float xi[8];
+            const int ps = find_inclusive<8>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, tag, &a.hd->err, xi);
+            int pend = a.nT;
+            if (ps >= 0) {
+                pend = ps;
 #pragma unroll
-                for (int s = 0; s < 8; ++s) { pay[s] = TP[s]; pay[8 + s] = TW[s]; }
-                publish<AW>(a.agg, ftile, tl.slot, tag, pay);
+                for (int s = 0; s < 8; ++s) Win[s] = xi[s];
             }
-            if (tl.j < a.nT - 1) {
-                float xi[8];
-                const int ps = find_inclusive<8>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, tag, &a.hd->err, xi);
-                int pend = a.nT;
-                if (ps >= 0) {
-                    pend = ps;
+            constexpr int NB = 2;
+            for (int p = pend - 1; p > tl.j; p -= NB) {
+                const int cnt = min(NB, p - tl.j);
+                float ag[NB][S::words];
+                load_aggregates<S::words, NB>(a.agg, p, -1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
 #pragma unroll
-                    for (int s = 0; s < 8; ++s) Win[s] = xi[s];
-                }
-                constexpr int NB = 2;
-                for (int p = pend - 1; p > tl.j; p -= NB) {
-                    const int cnt = min(NB, p - tl.j);
-                    float ag[NB][AW];
-                    load_aggregates<AW, NB>(a.agg, p, -1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
+                for (int u = 0; u < NB; ++u)
+                    if (u < cnt) {
+                        float np[8];
+                        mm8(ag[u], Win, np);
 #pragma unroll
-                    for (int u = 0; u < NB; ++u)
-                        if (u < cnt) {
-                            float np[8];
-                            mm8(ag[u], Win, np);
-#pragma unroll
-                            for (int s = 0; s < 8; ++s) Win[s] = np[s] + ag[u][8 + s];
-                        }
-                }
-            }
-            if (tl.sub == 0 && tl.j > 0) {
-                float Wo[8];
-                mm8(TP, Win, Wo);
-#pragma unroll
-                for (int s = 0; s < 8; ++s) Wo[s] += TW[s];
-                publish<8>(a.incl, ftile, tl.slot, tag, Wo);
+                        for (int s = 0; s < 8; ++s) Win[s] = np[s] + ag[u][8 + s];
+                    }
             }
         }
-        if (tl.sub == 0) {
+        if (owner && tl.j > 0) {
+            float Wo[8];
+            mm8(X, Win, Wo);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) Wo[s] += X[8 + s];
+            publish<8>(a.incl, ftile, tl.slot, tag, Wo);
+        }
+        if (owner) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) sCarry[tl.slot][s] = Win[s];
         }
+    } else {
+#pragma unroll
+        for (int i = 1; i < C; ++i) mm8(PT[i - 1], ATr[i - 1], PT[i]);
     }
     __syncthreads();
+    if (lb_wave) {
+#pragma unroll
+        for (int i = 1; i < C; ++i) mm8(PT[i - 1], ATr[i - 1], PT[i]);
+    }
+    // carry entering the chunk from its end: (composite of chunks q+1..) x (tile carry-in)
     float Wc[8];
+    if constexpr (MULTI) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) Wc[s] = sCarry[tl.slot][s];
-    if (tl.q < NCH - 1) {
-        float np[8];
-        mm8(sAgg[tl.q + 1][tl.slot], Wc, np);
+        for (int s = 0; s < 8; ++s) Wc[s] = sCarry[tl.slot][s];
+        if (tl.q < NCH - 1) {
+            float np[8];
+            mm8(sKS[FIN][tl.q + 1][tl.slot], Wc, np);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) Wc[s] = np[s] + sAgg[tl.q + 1][tl.slot][8 + s];
+            for (int s = 0; s < 8; ++s) Wc[s] = np[s] + sKS[FIN][tl.q + 1][tl.slot][8 + s];
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) Wc[s] = tl.q < NCH - 1 ? sKS[FIN][tl.q + 1][tl.slot][8 + s] : 0.0f;
     }
 
 #pragma unroll
