@@ -236,19 +236,23 @@ def cpu_baseline(seconds):
                       f"host thread, repeated {n} times over {el:.1f} s"}
 
 
-def kernel_source_hash():
+LOG_SOURCES = ("log_scan.hip", "device.hpp")
+
+
+def kernel_source_hash(names=None):
+    """sha256 prefix over the kernel sources (all of csrc, or the named files)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "scan_linear_rnns_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(names if names is not None else os.listdir(csrc)):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_key):
-    """HBM bytes per launch from the committed PMC summary, if it was taken on the current sources."""
-    path = os.path.join(ROOT, "profiles", "log_scan_lab_hbm_traffic.txt")
+def traffic_from_profiles(kernel_key, profile="log_scan_lab_hbm_traffic.txt", sources=LOG_SOURCES):
+    """HBM bytes per launch from a committed PMC summary, if it was taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
         return None
     src_hash, value = None, None
@@ -258,7 +262,7 @@ def traffic_from_profiles(kernel_key):
             src_hash = parts[1]
         if len(parts) == 3 and parts[0] == "traffic_bytes_per_launch" and parts[1] == kernel_key:
             value = int(parts[2])
-    if src_hash != kernel_source_hash():
+    if src_hash != kernel_source_hash(sources):
         return None
     return value
 
