@@ -12,6 +12,9 @@ What each function follows is stated in ``oracle.c``:
     h_t = a_t h_{t-1} + b_t with inputs log a_t, log b_t, log h_0
     (minGRU home page, introduction: the log-space baseline MinGRU and its
     Heinsen scan); gradients by the chain rule.
+  * ``linear_fwd`` / ``linear_bwd`` -- the same recurrence in linear space,
+    a_t of either sign (linear_scan in the home page's speed-up table and in
+    the how-to's Step 2 table; SignedMinGRU's signed gates on the home page).
   * ``block_affine_fwd`` / ``block_affine_bwd`` -- h_t = A_t h_{t-1} + b_t
     with block-diagonal k x k transitions (matrix_affine_scan in the
     "Run the benchmarks" how-to, Step 2; RotationMinGRU / GivensMinGRU on the
@@ -63,6 +66,8 @@ def _load():
             sig = {
                 "oracle_log_fwd": [_D, _D, _D, _D, _I, _I, _I],
                 "oracle_log_bwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I],
+                "oracle_linear_fwd": [_D, _D, _D, _D, _I, _I, _I],
+                "oracle_linear_bwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I],
                 "oracle_block_affine_fwd": [_D, _D, _D, _D, _I, _I, _I, _I],
                 "oracle_block_affine_bwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I],
                 "oracle_block_matrix_fwd": [_D, _D, _I, _I, _I, _I],
@@ -104,6 +109,28 @@ def log_bwd(log_a, log_b, log_h0, dh):
     dlh0 = np.empty_like(lh0)
     _load().oracle_log_bwd(_p(la), _p(lb), _p(lh0), _p(g), _p(dla), _p(dlb), _p(dlh0), B, T, d)
     return dla, dlb, dlh0
+
+
+def linear_fwd(a, b, h0):
+    """h (B,T,d) of h_t = a_t h_{t-1} + b_t (linear space, a of either sign)."""
+    a, b, h0 = _f64(a), _f64(b), _f64(h0)
+    B, T, d = a.shape
+    assert b.shape == a.shape and h0.shape == (B, d)
+    h = np.empty((B, T, d), np.float64)
+    _load().oracle_linear_fwd(_p(a), _p(b), _p(h0), _p(h), B, T, d)
+    return h
+
+
+def linear_bwd(a, b, h0, dh):
+    """(da, db, dh0) for L = sum(dh * h)."""
+    a, b, h0, g = _f64(a), _f64(b), _f64(h0), _f64(dh)
+    B, T, d = a.shape
+    assert b.shape == a.shape and g.shape == a.shape and h0.shape == (B, d)
+    da = np.empty_like(a)
+    db = np.empty_like(a)
+    dh0 = np.empty_like(h0)
+    _load().oracle_linear_bwd(_p(a), _p(b), _p(h0), _p(g), _p(da), _p(db), _p(dh0), B, T, d)
+    return da, db, dh0
 
 
 def _block_shapes(A, d, k):

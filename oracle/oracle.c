@@ -18,11 +18,16 @@
  *     matrix_affine_scan and matrix_scan in the "Run the benchmarks" how-to,
  *     Step 2 table) replace the scalar a_t by a block-diagonal k x k matrix:
  *     h_t = A_t h_{t-1} + b_t, and the b = 0 product P_t = A_t P_{t-1}, P_0 = I.
+ *   - The linear-space elementwise scan (linear_scan in the same page's
+ *     speed-up table and in the how-to's Step 2 table; the signed gates of
+ *     SignedMinGRU, same page) is the same recurrence with a_t, b_t, h_0 given
+ *     directly and a_t of either sign.
  *   - Gradients are the chain rule applied to these loops for the loss
  *     L = sum_t <dh_t, h_t> (resp. sum_t <dP_t, P_t>).
  *
  * Layouts (row-major, last index fastest):
  *   log scan:   la, lb, h, dh, dla, dlb : (B, T, d);  lh0, dlh0 : (B, d)
+ *   linear scan: a, b, h, dh, da, db : (B, T, d);  h0, dh0 : (B, d)
  *   block ops:  A, dA, P, dP : (B, T, nb, k, k) with nb = d / k and
  *               (A h)_r = sum_c A[r][c] h[c];  b, h, dh, db : (B, T, d);
  *               h0, dh0 : (B, d);  block j owns channels [j*k, (j+1)*k).
@@ -82,6 +87,52 @@ void oracle_log_bwd(const double *la, const double *lb, const double *lh0,
             }
             /* here g = g_1 and a_next = a_1 */
             dlh0[b * d + c] = (T > 0) ? g * a_next * hs[0] : 0.0;
+        }
+    free(hs);
+}
+
+/* ------------------------------------------------------------- linear scan */
+
+/* Forward: h_0 = h0; h_t = a_t h_{t-1} + b_t (a_t of either sign); writes h_1..T. */
+void oracle_linear_fwd(const double *a, const double *bv, const double *h0,
+                       double *h, int64_t B, int64_t T, int64_t d)
+{
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < d; ++c) {
+            double hp = h0[b * d + c];
+            for (int64_t t = 0; t < T; ++t) {
+                int64_t i = (b * T + t) * d + c;
+                hp = a[i] * hp + bv[i];
+                h[i] = hp;
+            }
+        }
+}
+
+/* Backward of oracle_linear_fwd under upstream dh = dL/dh_t:
+ *   g_T = dh_T,  g_t = dh_t + a_{t+1} g_{t+1}
+ *   da_t = g_t h_{t-1},  db_t = g_t,  dh0 = a_1 g_1. */
+void oracle_linear_bwd(const double *a, const double *bv, const double *h0,
+                       const double *dh, double *da, double *db, double *dh0,
+                       int64_t B, int64_t T, int64_t d)
+{
+    double *hs = (double *)malloc(sizeof(double) * (size_t)(T + 1));
+    if (!hs) return;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < d; ++c) {
+            hs[0] = h0[b * d + c];
+            for (int64_t t = 0; t < T; ++t) {
+                int64_t i = (b * T + t) * d + c;
+                hs[t + 1] = a[i] * hs[t] + bv[i];
+            }
+            double g = 0.0, a_next = 0.0;
+            for (int64_t t = T - 1; t >= 0; --t) {
+                int64_t i = (b * T + t) * d + c;
+                g = dh[i] + a_next * g;
+                da[i] = g * hs[t];
+                db[i] = g;
+                a_next = a[i];
+            }
+            dh0[b * d + c] = (T > 0) ? a_next * g : 0.0;
         }
     free(hs);
 }

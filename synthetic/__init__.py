@@ -13,6 +13,11 @@ once to float32 at the end):
   and g(x) = x + 0.5 for x >= 0, sigmoid(x) otherwise:
   log_a = log a, log_b = log(z * g(x)), log_h0 = log g(x0).  Logs are taken
   in closed form (log sigmoid(u) = -softplus(-u)) so nothing underflows.
+* Linear-space scan with signed gates (linear_scan; SignedMinGRU's
+  negative-eigenvalue gates on the home page).  Same draws as the log-space
+  scan (k, x, x0, dh in that order); the MinGRU gate sigmoid(-k) in [0, 1] is
+  stretched to a = 2 sigmoid(-k) - 1 in (-1, 1), b = (1 - sigmoid(-k)) g(x),
+  h0 = g(x0).
 * Block scans (GivensMinGRU on the home page; the Clements rectangular mesh of
   Givens rotations).  Draw s ~ N(0,1) of shape (B,T,nb), theta ~ U(-pi, pi) of
   shape (B,T,nb,k(k-1)/2), b ~ N(0,1) of shape (B,T,d), dh ~ N(0,1) of shape
@@ -62,6 +67,29 @@ def log_inputs(B: int, T: int, d: int, seed: int = 0) -> LogInputs:
     log_h0 = _log_g(x0)
     f = np.float32
     return LogInputs(log_a.astype(f), log_b.astype(f), log_h0.astype(f), dh.astype(f))
+
+
+@dataclass
+class LinearInputs:
+    a: np.ndarray       # (B,T,d) float32, in (-1, 1)
+    b: np.ndarray       # (B,T,d) float32
+    h0: np.ndarray      # (B,d)   float32
+    dh: np.ndarray      # (B,T,d) float32
+
+
+def linear_inputs(B: int, T: int, d: int, seed: int = 0) -> LinearInputs:
+    """Signed-gate generator for the linear-space scan (see module docstring)."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, T, d))
+    x = rng.standard_normal((B, T, d))
+    x0 = rng.standard_normal((B, d))
+    dh = rng.standard_normal((B, T, d))
+    gate = np.exp(-_softplus(k))     # sigmoid(-k)
+    a = 2.0 * gate - 1.0
+    b = (1.0 - gate) * np.exp(_log_g(x))
+    h0 = np.exp(_log_g(x0))
+    f = np.float32
+    return LinearInputs(a.astype(f), b.astype(f), h0.astype(f), dh.astype(f))
 
 
 def n_angles(k: int) -> int:
@@ -132,6 +160,8 @@ CONFIGS = {
     "log_tiny":   dict(op="log", B=2, T=64, d=16),
     "log_lab":    dict(op="log", B=128, T=64, d=64),
     "log_longT":  dict(op="log", B=16, T=1024, d=64),
+    "linear_lab":   dict(op="linear", B=128, T=64, d=64),
+    "linear_longT": dict(op="linear", B=16, T=1024, d=64),
     "block_lab":  dict(op="block", B=128, T=64, d=64, k=8),
     "block_longT": dict(op="block", B=16, T=1024, d=64, k=8),
 }

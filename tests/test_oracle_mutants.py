@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_pins as pins
+from tests import test_oracle_pins_linear as lpins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -27,6 +28,12 @@ MUTANTS = [
     ("log_bwd drops b in dlb", "dlb[i] = g * exp(lb[i]);", "dlb[i] = g;"),
     ("log_bwd dlh0 sign", "dlh0[b * d + c] = (T > 0) ? g * a_next * hs[0] : 0.0;",
      "dlh0[b * d + c] = (T > 0) ? -g * a_next * hs[0] : 0.0;"),
+    ("linear_fwd drops b", "hp = a[i] * hp + bv[i];", "hp = a[i] * hp;"),
+    ("linear_bwd uses a_t not a_{t+1}", "g = dh[i] + a_next * g;\n                da[i] = g * hs[t];",
+     "g = dh[i] + a[i] * g;\n                da[i] = g * hs[t];"),
+    ("linear_bwd h_t for h_{t-1}", "da[i] = g * hs[t];", "da[i] = g * hs[t + 1];"),
+    ("linear_bwd dh0 drops a_1", "dh0[b * d + c] = (T > 0) ? a_next * g : 0.0;",
+     "dh0[b * d + c] = (T > 0) ? g : 0.0;"),
     ("affine_fwd transposed A", "for (int64_t c = 0; c < k; ++c) s += At[r * k + c] * cur[c];",
      "for (int64_t c = 0; c < k; ++c) s += At[c * k + r] * cur[c];"),
     ("affine_bwd A not A^T", "for (int64_t r = 0; r < k; ++r) s += At[r * k + c] * g[r];",
@@ -53,6 +60,9 @@ PINS = [
     pins.test_block_cumprod_gradients_finite_difference,
     pins.test_block_affine_brute_force_products,
     pins.test_block_cumprod_brute_force_products,
+    lpins.test_golden_linear_scan,
+    lambda: lpins.test_constant_coefficients_geometric(-0.8, 1.5, -1.0),
+    lpins.test_gradients_finite_difference,
 ]
 
 
@@ -73,7 +83,8 @@ def test_mutant_is_caught(name, orig, mut, monkeypatch):
     real = oracle._lib
     with tempfile.TemporaryDirectory() as tmp:
         lib = ctypes.CDLL(_build(text.replace(orig, mut), tmp))
-        for fname in ("oracle_log_fwd", "oracle_log_bwd", "oracle_block_affine_fwd",
+        for fname in ("oracle_log_fwd", "oracle_log_bwd", "oracle_linear_fwd", "oracle_linear_bwd",
+                      "oracle_block_affine_fwd",
                       "oracle_block_affine_bwd", "oracle_block_matrix_fwd", "oracle_block_matrix_bwd"):
             fn, ref = getattr(lib, fname), getattr(real, fname)
             fn.argtypes, fn.restype = ref.argtypes, ref.restype
