@@ -13,7 +13,10 @@
  *      RotationMinGRU / GivensMinGRU ("Run the benchmarks" how-to, Step 2,
  *      op matrix_affine_scan);
  *   3. block cumulative product P_t = A_t P_{t-1}, P_0 = I, the b = 0 case
- *      (same table, op matrix_scan).
+ *      (same table, op matrix_scan);
+ *   4. linear-space elementwise scan, a_t of either sign -- the op the pages
+ *      list as linear_scan (home page speed-up table; "Run the benchmarks"
+ *      how-to, Step 2), for gates with negative eigenvalues.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -50,7 +53,7 @@
  *   MGS_ERR_HIP            a HIP launch error; mgs_last_hip_error() gives the
  *                          hipError_t (per calling thread).
  * Non-finite inputs propagate; log_b = -inf (b = 0) and log_h0 = -inf
- * (h_0 = 0) are supported exactly.
+ * (h_0 = 0) are supported exactly by the log-space scan.
  */
 #ifndef MGS_H
 #define MGS_H
@@ -117,6 +120,37 @@ mgs_status mgs_scan_log_bwd(const float *log_a, const float *log_b, const float 
                             int64_t B, int64_t T, int64_t d,
                             void *workspace, size_t workspace_bytes, int fwd_state_valid,
                             void *stream);
+
+/* --------------------------------------------------- linear-space scan --- */
+/*
+ * Forward (linear_scan: home page speed-up table and "Run the benchmarks"
+ * how-to, Step 2; the signed gates of SignedMinGRU, home page):
+ *     h_0 = h0,   h_t = a_t h_{t-1} + b_t,  t = 1..T,   a_t of either sign,
+ * evaluated in linear space (a log form cannot hold a negative a_t) and
+ * written as h (h_1..h_T).
+ *   a, b : (B,T,d) in     h0 : (B,d) in     h : (B,T,d) out
+ * Same workspace rules as the log-space scan (its own size query).
+ */
+mgs_status mgs_scan_linear_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes);
+
+mgs_status mgs_scan_linear_fwd(const float *a, const float *b, const float *h0, float *h,
+                               int64_t B, int64_t T, int64_t d,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of mgs_scan_linear_fwd for L = sum_t <dh_t, h_t>: the reverse scan
+ * g_T = dh_T, g_t = dh_t + a_{t+1} g_{t+1}, with
+ *     da_t = g_t h_{t-1},   db_t = g_t,   dh0 = a_1 g_1.
+ * h_{t-1} is recomputed from a, b, h0 and the tile-start states the forward
+ * left in the workspace.
+ *   dh : (B,T,d) in;   da, db : (B,T,d) out;   dh0 : (B,d) out.
+ * fwd_state_valid as for mgs_scan_log_bwd.
+ */
+mgs_status mgs_scan_linear_bwd(const float *a, const float *b, const float *h0, const float *dh,
+                               float *da, float *db, float *dh0,
+                               int64_t B, int64_t T, int64_t d,
+                               void *workspace, size_t workspace_bytes, int fwd_state_valid,
+                               void *stream);
 
 /* --------------------------------------------------- block-affine scan --- */
 /*

@@ -8,6 +8,7 @@ or PyTorch fallback: without the built library (or a GPU) these calls raise.
 
 Ops (see include/mgs.h for the definitions and their sources on the pages):
   * mgs_scan_log_fwd / mgs_scan_log_bwd                 log-space minGRU scan
+  * mgs_scan_linear_fwd / mgs_scan_linear_bwd           linear-space scan, signed gates
   * mgs_block_affine_scan_fwd / mgs_block_affine_scan_bwd   h_t = A_t h_{t-1} + b_t
   * mgs_block_matrix_scan_fwd / mgs_block_matrix_scan_bwd   P_t = A_t P_{t-1}
 """
@@ -21,6 +22,7 @@ from ._lib import MgsError, check, declared_functions, load, status_string  # no
 __all__ = [
     "MgsError", "load", "workspace", "mgs_workspace_check",
     "mgs_scan_log_workspace_size", "mgs_scan_log_fwd", "mgs_scan_log_bwd",
+    "mgs_scan_linear_workspace_size", "mgs_scan_linear_fwd", "mgs_scan_linear_bwd",
     "mgs_block_affine_scan_workspace_size", "mgs_block_affine_scan_fwd", "mgs_block_affine_scan_bwd",
     "mgs_block_matrix_scan_workspace_size", "mgs_block_matrix_scan_fwd", "mgs_block_matrix_scan_bwd",
 ]
@@ -62,6 +64,10 @@ def _size(fn, *dims):
 
 def mgs_scan_log_workspace_size(B, T, d):
     return _size("mgs_scan_log_workspace_size", B, T, d)
+
+
+def mgs_scan_linear_workspace_size(B, T, d):
+    return _size("mgs_scan_linear_workspace_size", B, T, d)
 
 
 def mgs_block_affine_scan_workspace_size(B, T, d, k):
@@ -126,6 +132,49 @@ def mgs_scan_log_bwd(log_a, log_b, log_h0, dh, ws=None, fwd_state_valid=False, o
                                   _ptr(dlh0), B, T, d, _ptr(ws), ws.numel(), int(bool(fwd_state_valid)),
                                   _stream(stream)), "mgs_scan_log_bwd")
     return dla, dlb, dlh0
+
+
+# ----------------------------------------------------- linear-space scan
+
+def mgs_scan_linear_fwd(a, b, h0, h=None, ws=None, stream=None):
+    """h (B,T,d) of h_t = a_t h_{t-1} + b_t (a of either sign); returns (h, ws)."""
+    import torch
+    B, T, d = a.shape
+    dev = a.device
+    _check_tensor("a", a, (B, T, d))
+    _check_tensor("b", b, (B, T, d), dev)
+    _check_tensor("h0", h0, (B, d), dev)
+    if h is None:
+        h = torch.empty((B, T, d), dtype=torch.float32, device=dev)
+    _check_tensor("h", h, (B, T, d), dev)
+    if ws is None:
+        ws = workspace(mgs_scan_linear_workspace_size(B, T, d), dev)
+    check(load().mgs_scan_linear_fwd(_ptr(a), _ptr(b), _ptr(h0), _ptr(h), B, T, d,
+                                     _ptr(ws), ws.numel(), _stream(stream)), "mgs_scan_linear_fwd")
+    return h, ws
+
+
+def mgs_scan_linear_bwd(a, b, h0, dh, ws=None, fwd_state_valid=False, out=None, stream=None):
+    """(da, db, dh0) for L = sum(dh * h)."""
+    import torch
+    B, T, d = a.shape
+    dev = a.device
+    _check_tensor("a", a, (B, T, d))
+    _check_tensor("b", b, (B, T, d), dev)
+    _check_tensor("h0", h0, (B, d), dev)
+    _check_tensor("dh", dh, (B, T, d), dev)
+    if out is None:
+        out = (torch.empty((B, T, d), dtype=torch.float32, device=dev),
+               torch.empty((B, T, d), dtype=torch.float32, device=dev),
+               torch.empty((B, d), dtype=torch.float32, device=dev))
+    da, db, dh0 = out
+    if ws is None:
+        ws = workspace(mgs_scan_linear_workspace_size(B, T, d), dev)
+        fwd_state_valid = False
+    check(load().mgs_scan_linear_bwd(_ptr(a), _ptr(b), _ptr(h0), _ptr(dh), _ptr(da), _ptr(db), _ptr(dh0),
+                                     B, T, d, _ptr(ws), ws.numel(), int(bool(fwd_state_valid)),
+                                     _stream(stream)), "mgs_scan_linear_bwd")
+    return da, db, dh0
 
 
 # ---------------------------------------------------------- block-affine

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmgs.so")
-SOURCES = ["mgs_api.cpp", "log_scan.hip", "block_scan.hip"]
+SOURCES = ["mgs_api.cpp", "elem_scan.hip", "block_scan.hip"]
 ARCH = os.environ.get("MGS_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 instructions are disabled for every device code object: the

@@ -1,11 +1,13 @@
-// log_scan.hip -- log-space minGRU scan, forward and fused backward, for gfx950.
+// elem_scan.hip -- the elementwise scans h_t = a_t h_{t-1} + b_t, forward and
+// fused backward, for gfx950, in two arithmetics:
+//   * log space (minGRU home page, introduction; "Triton on GPU", section "What
+//     you gain (and where you don't)", parallel_scan_log): inputs log a, log b,
+//     log h0 with a > 0, evaluated in log space after Heinsen (arXiv:2311.06281);
+//   * linear space (linear_scan in the home page's speed-up table and in the
+//     "Run the benchmarks" how-to, Step 2): inputs a, b, h0 with a of either
+//     sign (SignedMinGRU's negative-eigenvalue gates, home page).
 //
-// The op (minGRU home page, introduction; "Triton on GPU", section "What you
-// gain (and where you don't)", parallel_scan_log): h_t = a_t h_{t-1} + b_t per
-// chain (b, c), inputs log a, log b, log h0, evaluated in log space after
-// Heinsen (arXiv:2311.06281).
-//
-// Work decomposition (same for forward and backward):
+// Work decomposition (same for both arithmetics, forward and backward):
 //   chain   = (b, c), flattened as b*d + c; CHW consecutive chains per wave row
 //             so each per-step load/store of a wave covers CHW*4 contiguous bytes
 //             per row;
@@ -17,13 +19,15 @@
 //             single-pass decoupled look-back (tagged words, tickets; see
 //             device.hpp).
 //
-// Forward state per chunk is the pair (LA, LH) = (sum of log2 a, log2 of the
-// chunk's own output from a zero start); pairs compose with
-//   (LA1, LH1) then (LA2, LH2) = (LA1 + LA2, lae2(LA2 + LH1, LH2)),
-// lae2(x, y) = log2(2^x + 2^y).  Everything is re-based at the chunk start,
-// so no running sum of log a ever grows with T (a single global cumulative
-// sum of log a would lose fp32 digits at long T).  Internally the kernels use
-// base 2 so that exp2/log2 map to the hardware's native transcendentals.
+// Forward state per chunk is a pair (A, H): the chunk's transfer factor and its
+// own output from a zero start.  Pairs compose associatively,
+//   (A1, H1) then (A2, H2) = (A1 A2, A2 H1 + H2),
+// and a carry c entering a segment leaves it as A c + H.  In log space the pair
+// is held as (sum of log2 a, log2 H) and the same rules read
+//   (LA1 + LA2, lae2(LA2 + LH1, LH2)),  lae2(x, y) = log2(2^x + 2^y);
+// everything is re-based at the chunk start, so no running sum of log a ever
+// grows with T (a single global cumulative sum of log a would lose fp32 digits
+// at long T).  Base 2 maps exp2/log2 to the hardware's native transcendentals.
 //
 // The backward recomputes h (linear space, from each tile's carried-in state
 // that the forward left in the workspace) and runs the reverse scan of
@@ -54,6 +58,76 @@ __device__ __forceinline__ float lae2(float x, float y)
     return (m == -kInf || m == kInf) ? m : r;
 }
 
+// ------------------------------------------------- the two arithmetics
+
+// Log space, base 2: x = log2 a, y = log2 b; pair (A, H) = (sum x, log2 H).
+struct LogAlg {
+    __device__ static float idA() { return 0.0f; }
+    __device__ static float idH() { return -kInf; }
+    __device__ static void input(float la, float lb, bool valid, float &x, float &y)
+    {
+        x = valid ? la * kLog2e : 0.0f;        // masked step: a = 1, b = 0
+        y = valid ? lb * kLog2e : -kInf;
+    }
+    __device__ static void step(float &A, float &H, float x, float y)
+    {
+        H = lae2(x + H, y);
+        A += x;
+    }
+    // (A1, H1) then (A2, H2)
+    __device__ static void combine(float A1, float H1, float A2, float H2, float &A, float &H)
+    {
+        H = lae2(A2 + H1, H2);
+        A = A1 + A2;
+    }
+    __device__ static float apply(float A, float H, float c) { return lae2(A + c, H); }
+    __device__ static float out(float A, float H, float c) { return ex2(A + c) + ex2(H); }
+    __device__ static float carry0(float lh0, bool valid) { return valid ? lh0 * kLog2e : -kInf; }
+    __device__ static float to_linear(float c) { return ex2(c); }
+    // backward: linear-space a and b of a step
+    __device__ static float lin_a(float la) { return ex2(la * kLog2e); }
+    __device__ static float lin_b(float lb) { return ex2(lb * kLog2e); }
+    __device__ static float lin_h0(float lh0) { return ex2(lh0 * kLog2e); }
+    // gradients: d/dlog a = g a h_{t-1}, d/dlog b = g b, d/dlog h0 = (a_1 g_1) h0
+    __device__ static float grad_a(float g, float ag, float hprev) { return ag * hprev; }
+    __device__ static float grad_b(float g, float b) { return g * b; }
+    __device__ static float grad_h0(float w, float h0) { return w * h0; }
+};
+
+// Linear space: x = a (any sign), y = b; pair (A, H) as is.
+struct LinAlg {
+    __device__ static float idA() { return 1.0f; }
+    __device__ static float idH() { return 0.0f; }
+    __device__ static void input(float a, float b, bool valid, float &x, float &y)
+    {
+        x = valid ? a : 1.0f;
+        y = valid ? b : 0.0f;
+    }
+    __device__ static void step(float &A, float &H, float x, float y)
+    {
+        H = x * H + y;
+        A *= x;
+    }
+    __device__ static void combine(float A1, float H1, float A2, float H2, float &A, float &H)
+    {
+        H = A2 * H1 + H2;
+        A = A1 * A2;
+    }
+    __device__ static float apply(float A, float H, float c) { return A * c + H; }
+    __device__ static float out(float A, float H, float c) { return A * c + H; }
+    __device__ static float carry0(float h0, bool valid) { return valid ? h0 : 0.0f; }
+    __device__ static float to_linear(float c) { return c; }
+    __device__ static float lin_a(float a) { return a; }
+    __device__ static float lin_b(float b) { return b; }
+    __device__ static float lin_h0(float h0) { return h0; }
+    // gradients: d/da = g h_{t-1}, d/db = g, d/dh0 = a_1 g_1
+    __device__ static float grad_a(float g, float ag, float hprev) { return g * hprev; }
+    __device__ static float grad_b(float g, float b) { return g; }
+    __device__ static float grad_h0(float w, float h0) { return w; }
+};
+
+// Argument names follow the log-space op; the linear op passes a, b, h0 in the
+// same slots and receives da, db, dh0.
 struct LogFwdArgs {
     const float *la, *lb, *lh0;
     float *h;                       // nullptr: carries only (used by the backward)
@@ -61,7 +135,7 @@ struct LogFwdArgs {
     int T, d, nCG, nT, nTiles;
     WsHeader *hd;
     uint64_t *agg_a, *agg_h, *incl; // tagged look-back words, [tile][CHW]
-    float *carry;                   // log2 h at each tile start, [tile][CHW]
+    float *carry;                   // state at each tile start (log2 h or h), [tile][CHW]
 };
 
 struct LogBwdArgs {
@@ -74,8 +148,8 @@ struct LogBwdArgs {
     const float *carry;
 };
 
-template <int CHW, int C, int W, bool MULTI>
-__global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
+template <class Alg, int CHW, int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
 {
     constexpr int SUB = 64 / CHW;
     constexpr int NCH = W * SUB;
@@ -114,20 +188,15 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
         y[i] = a.lb[off];
     }
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const bool v = cv && t0 + i < a.T;
-        x[i] = v ? x[i] * kLog2e : 0.0f;       // identity step: a = 1, b = 0
-        y[i] = v ? y[i] * kLog2e : -kInf;
-    }
+    for (int i = 0; i < C; ++i) Alg::input(x[i], y[i], cv && t0 + i < a.T, x[i], y[i]);
     const float lh0v = a.lh0[cc];
 
-    // chunk-local pair scan from the identity (0, -inf)
+    // chunk-local pair scan from the identity
     float pA[C], pH[C];
-    float LA = 0.0f, LH = -kInf;
+    float LA = Alg::idA(), LH = Alg::idH();
 #pragma unroll
     for (int i = 0; i < C; ++i) {
-        LH = lae2(x[i] + LH, y[i]);
-        LA += x[i];
+        Alg::step(LA, LH, x[i], y[i]);
         pA[i] = LA;
         pH[i] = LH;
     }
@@ -140,18 +209,15 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
     float carry;
     if constexpr (MULTI) {
         if (threadIdx.x < CHW) {
-            float TA = 0.0f, TH = -kInf;   // tile aggregate
+            float TA = Alg::idA(), TH = Alg::idH();   // tile aggregate
 #pragma unroll
-            for (int p = 0; p < NCH; ++p) {
-                TH = lae2(sLA[p][ch] + TH, sLH[p][ch]);
-                TA += sLA[p][ch];
-            }
+            for (int p = 0; p < NCH; ++p) Alg::combine(TA, TH, sLA[p][ch], sLH[p][ch], TA, TH);
             const size_t slot = static_cast<size_t>(tile) * CHW + ch;
             if (j < a.nT - 1) {
                 tagged_store(&a.agg_a[slot], tag, TA);
                 tagged_store(&a.agg_h[slot], tag, TH);
             }
-            const float lh0 = cv ? lh0v * kLog2e : -kInf;
+            const float lh0 = Alg::carry0(lh0v, cv);
             float cin = lh0;
             if (j > 0) {
                 // Decoupled look-back over the earlier tiles, nearest first, LB
@@ -162,7 +228,7 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
                 // of the sequence ends there with the known h0: no tile ever
                 // waits for another tile's look-back to finish.
                 constexpr int LB = 8;
-                float accA = 0.0f, accH = -kInf, basev = lh0;
+                float accA = Alg::idA(), accH = Alg::idH(), basev = lh0;
                 int p0 = j - 1;
                 for (uint32_t spin = 0;;) {
                     uint64_t wi[LB], wa[LB], wh[LB];
@@ -186,8 +252,8 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
                             basev = tag_value(wi[u]);
                             done = stop = true;
                         } else if (tag_is(wa[u], tag) && tag_is(wh[u], tag)) {
-                            accH = lae2(accA + tag_value(wh[u]), accH);
-                            accA += tag_value(wa[u]);
+                            // tile p's aggregate, then the tiles after it
+                            Alg::combine(tag_value(wa[u]), tag_value(wh[u]), accA, accH, accA, accH);
                             adv = u + 1;
                         } else {
                             stop = true;
@@ -203,34 +269,34 @@ __global__ void __launch_bounds__(64 * W) log_fwd_kernel(LogFwdArgs a)
                         backoff();
                     }
                 }
-                cin = lae2(accA + basev, accH);
+                cin = Alg::apply(accA, accH, basev);
             }
             if (j < a.nT - 1)
-                tagged_store(&a.incl[slot], tag, lae2(TA + cin, TH));
+                tagged_store(&a.incl[slot], tag, Alg::apply(TA, TH, cin));
             a.carry[slot] = cin;
             sCarry[ch] = cin;
         }
         __syncthreads();
         carry = sCarry[ch];
     } else {
-        carry = cv ? lh0v * kLog2e : -kInf;
+        carry = Alg::carry0(lh0v, cv);
     }
 
     if (a.h == nullptr) return;
 
-    // carry into this lane's chunk, then the fix-up in linear space:
-    // h_t = 2^(LA_t + carry) + 2^(LH_t)
+    // carry into this lane's chunk, then the fix-up (log space: written as
+    // h_t = 2^(LA_t + carry) + 2^(LH_t))
     float cq = carry;
-    for (int p = 0; p < q; ++p) cq = lae2(sLA[p][ch] + cq, sLH[p][ch]);
+    for (int p = 0; p < q; ++p) cq = Alg::apply(sLA[p][ch], sLH[p][ch], cq);
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int t = t0 + i;
-        if (cv && t < a.T) a.h[base + static_cast<int64_t>(t) * a.d] = ex2(pA[i] + cq) + ex2(pH[i]);
+        if (cv && t < a.T) a.h[base + static_cast<int64_t>(t) * a.d] = Alg::out(pA[i], pH[i], cq);
     }
 }
 
-template <int CHW, int C, int W, bool MULTI>
-__global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
+template <class Alg, int CHW, int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
 {
     constexpr int SUB = 64 / CHW;
     constexpr int NCH = W * SUB;
@@ -277,8 +343,8 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const bool v = cv && t0 + i < a.T;
-        av[i] = v ? ex2(av[i] * kLog2e) : 1.0f;
-        bv[i] = v ? ex2(bv[i] * kLog2e) : 0.0f;
+        av[i] = v ? Alg::lin_a(av[i]) : 1.0f;
+        bv[i] = v ? Alg::lin_b(bv[i]) : 0.0f;
         gv[i] = v ? gv[i] : 0.0f;
     }
 
@@ -303,7 +369,7 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
     if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
 
     // state entering the tile: h0 for the first tile, else the forward's carry
-    const float hin = (j == 0) ? (cv ? ex2(lh0v * kLog2e) : 0.0f) : ex2(cin_f);
+    const float hin = (j == 0) ? (cv ? Alg::lin_h0(lh0v) : 0.0f) : Alg::to_linear(cin_f);
     __syncthreads();
     const uint32_t tag = sTicket[0];
 
@@ -394,11 +460,11 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
         const int t = t0 + i;
         if (cv && t < a.T) {
             const int64_t off = base + static_cast<int64_t>(t) * a.d;
-            a.dla[off] = ag * hprev;
-            a.dlb[off] = g * bv[i];
+            a.dla[off] = Alg::grad_a(g, ag, hprev);
+            a.dlb[off] = Alg::grad_b(g, bv[i]);
         }
     }
-    if (cv && j == 0 && q == 0) a.dlh0[chain] = wc * hin;   // g_1 a_1 h_0
+    if (cv && j == 0 && q == 0) a.dlh0[chain] = Alg::grad_h0(wc, hin);   // from a_1 g_1
 }
 
 // ------------------------------------------------------------ host side
@@ -413,47 +479,82 @@ __global__ void __launch_bounds__(64 * W) log_bwd_kernel(LogBwdArgs a)
 constexpr int kShortT = MGS_LOG_SHORT_T;
 constexpr int kMaxC = 16;
 
-template <int CHW, int W, int C>
+template <class Alg, int CHW, int W, int C>
 hipError_t launch_fwd_c(const LogGeom &g, const LogFwdArgs &args, hipStream_t s)
 {
     const dim3 grid(g.nTiles), block(64 * W);
     if (g.nT > 1)
-        hipLaunchKernelGGL((log_fwd_kernel<CHW, C, W, true>), grid, block, 0, s, args);
+        hipLaunchKernelGGL((elem_fwd_kernel<Alg, CHW, C, W, true>), grid, block, 0, s, args);
     else
-        hipLaunchKernelGGL((log_fwd_kernel<CHW, C, W, false>), grid, block, 0, s, args);
+        hipLaunchKernelGGL((elem_fwd_kernel<Alg, CHW, C, W, false>), grid, block, 0, s, args);
     return hipGetLastError();
 }
 
-template <int CHW, int W, int C>
+template <class Alg, int CHW, int W, int C>
 hipError_t launch_bwd_c(const LogGeom &g, const LogBwdArgs &args, hipStream_t s)
 {
     const dim3 grid(g.nTiles), block(64 * W);
     if (g.nT > 1)
-        hipLaunchKernelGGL((log_bwd_kernel<CHW, C, W, true>), grid, block, 0, s, args);
+        hipLaunchKernelGGL((elem_bwd_kernel<Alg, CHW, C, W, true>), grid, block, 0, s, args);
     else
-        hipLaunchKernelGGL((log_bwd_kernel<CHW, C, W, false>), grid, block, 0, s, args);
+        hipLaunchKernelGGL((elem_bwd_kernel<Alg, CHW, C, W, false>), grid, block, 0, s, args);
     return hipGetLastError();
 }
 
-#define MGS_LOG_DISPATCH(FN, g, a, s)                                                             \
+#define MGS_ELEM_DISPATCH(FN, ALG, g, a, s)                                                       \
     do {                                                                                          \
         if ((g).CHW == 32) {                                                                      \
             switch ((g).C) {                                                                      \
-            case 1: return FN<32, 4, 1>(g, a, s);                                                 \
-            case 2: return FN<32, 4, 2>(g, a, s);                                                 \
-            case 4: return FN<32, 4, 4>(g, a, s);                                                 \
-            case 8: return FN<32, 4, 8>(g, a, s);                                                 \
-            default: return FN<32, 4, 16>(g, a, s);                                               \
+            case 1: return FN<ALG, 32, 4, 1>(g, a, s);                                            \
+            case 2: return FN<ALG, 32, 4, 2>(g, a, s);                                            \
+            case 4: return FN<ALG, 32, 4, 4>(g, a, s);                                            \
+            case 8: return FN<ALG, 32, 4, 8>(g, a, s);                                            \
+            default: return FN<ALG, 32, 4, 16>(g, a, s);                                          \
             }                                                                                     \
         }                                                                                         \
         switch ((g).C) {                                                                          \
-        case 1: return FN<64, 8, 1>(g, a, s);                                                     \
-        case 2: return FN<64, 8, 2>(g, a, s);                                                     \
-        case 4: return FN<64, 8, 4>(g, a, s);                                                     \
-        case 8: return FN<64, 8, 8>(g, a, s);                                                     \
-        default: return FN<64, 8, 16>(g, a, s);                                                   \
+        case 1: return FN<ALG, 64, 8, 1>(g, a, s);                                                \
+        case 2: return FN<ALG, 64, 8, 2>(g, a, s);                                                \
+        case 4: return FN<ALG, 64, 8, 4>(g, a, s);                                                \
+        case 8: return FN<ALG, 64, 8, 8>(g, a, s);                                                \
+        default: return FN<ALG, 64, 8, 16>(g, a, s);                                              \
         }                                                                                         \
     } while (0)
+
+LogFwdArgs fwd_args(const LogGeom &g, const float *x1, const float *x2, const float *x0, float *h,
+                    void *ws)
+{
+    char *w = static_cast<char *>(ws);
+    LogFwdArgs a{};
+    a.la = x1; a.lb = x2; a.lh0 = x0; a.h = h;
+    a.S = g.S; a.T = g.T; a.d = g.d; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
+    a.hd = reinterpret_cast<WsHeader *>(w);
+    if (g.nT > 1) {
+        a.agg_a = reinterpret_cast<uint64_t *>(w + g.off_fagg_a);
+        a.agg_h = reinterpret_cast<uint64_t *>(w + g.off_fagg_h);
+        a.incl = reinterpret_cast<uint64_t *>(w + g.off_fincl);
+        a.carry = reinterpret_cast<float *>(w + g.off_carry);
+    }
+    return a;
+}
+
+LogBwdArgs bwd_args(const LogGeom &g, const float *x1, const float *x2, const float *x0,
+                    const float *dh, float *d1, float *d2, float *d0, void *ws)
+{
+    char *w = static_cast<char *>(ws);
+    LogBwdArgs a{};
+    a.la = x1; a.lb = x2; a.lh0 = x0; a.dh = dh;
+    a.dla = d1; a.dlb = d2; a.dlh0 = d0;
+    a.S = g.S; a.T = g.T; a.d = g.d; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
+    a.hd = reinterpret_cast<WsHeader *>(w);
+    if (g.nT > 1) {
+        a.agg_p = reinterpret_cast<uint64_t *>(w + g.off_bagg_p);
+        a.agg_w = reinterpret_cast<uint64_t *>(w + g.off_bagg_w);
+        a.incl = reinterpret_cast<uint64_t *>(w + g.off_bincl);
+        a.carry = reinterpret_cast<const float *>(w + g.off_carry);
+    }
+    return a;
+}
 
 }  // namespace
 
@@ -492,39 +593,31 @@ LogGeom log_geometry(int64_t B, int64_t T, int64_t d)
 hipError_t launch_log_fwd(const LogGeom &g, const float *la, const float *lb, const float *lh0,
                           float *h, void *ws, hipStream_t s)
 {
-    char *w = static_cast<char *>(ws);
-    WsHeader *hd = reinterpret_cast<WsHeader *>(w);
-    LogFwdArgs a{};
-    a.la = la; a.lb = lb; a.lh0 = lh0; a.h = h;
-    a.S = g.S; a.T = g.T; a.d = g.d; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
-    a.hd = hd;
-    if (g.nT > 1) {
-        a.agg_a = reinterpret_cast<uint64_t *>(w + g.off_fagg_a);
-        a.agg_h = reinterpret_cast<uint64_t *>(w + g.off_fagg_h);
-        a.incl = reinterpret_cast<uint64_t *>(w + g.off_fincl);
-        a.carry = reinterpret_cast<float *>(w + g.off_carry);
-    }
-    MGS_LOG_DISPATCH(launch_fwd_c, g, a, s);
+    const LogFwdArgs a = fwd_args(g, la, lb, lh0, h, ws);
+    MGS_ELEM_DISPATCH(launch_fwd_c, LogAlg, g, a, s);
 }
 
 hipError_t launch_log_bwd(const LogGeom &g, const float *la, const float *lb, const float *lh0,
                           const float *dh, float *dla, float *dlb, float *dlh0, void *ws,
                           hipStream_t s)
 {
-    char *w = static_cast<char *>(ws);
-    WsHeader *hd = reinterpret_cast<WsHeader *>(w);
-    LogBwdArgs a{};
-    a.la = la; a.lb = lb; a.lh0 = lh0; a.dh = dh;
-    a.dla = dla; a.dlb = dlb; a.dlh0 = dlh0;
-    a.S = g.S; a.T = g.T; a.d = g.d; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
-    a.hd = hd;
-    if (g.nT > 1) {
-        a.agg_p = reinterpret_cast<uint64_t *>(w + g.off_bagg_p);
-        a.agg_w = reinterpret_cast<uint64_t *>(w + g.off_bagg_w);
-        a.incl = reinterpret_cast<uint64_t *>(w + g.off_bincl);
-        a.carry = reinterpret_cast<const float *>(w + g.off_carry);
-    }
-    MGS_LOG_DISPATCH(launch_bwd_c, g, a, s);
+    const LogBwdArgs a = bwd_args(g, la, lb, lh0, dh, dla, dlb, dlh0, ws);
+    MGS_ELEM_DISPATCH(launch_bwd_c, LogAlg, g, a, s);
+}
+
+hipError_t launch_linear_fwd(const LogGeom &g, const float *a_, const float *b, const float *h0,
+                             float *h, void *ws, hipStream_t s)
+{
+    const LogFwdArgs a = fwd_args(g, a_, b, h0, h, ws);
+    MGS_ELEM_DISPATCH(launch_fwd_c, LinAlg, g, a, s);
+}
+
+hipError_t launch_linear_bwd(const LogGeom &g, const float *a_, const float *b, const float *h0,
+                             const float *dh, float *da, float *db, float *dh0, void *ws,
+                             hipStream_t s)
+{
+    const LogBwdArgs a = bwd_args(g, a_, b, h0, dh, da, db, dh0, ws);
+    MGS_ELEM_DISPATCH(launch_bwd_c, LinAlg, g, a, s);
 }
 
 }  // namespace mgs

@@ -12,7 +12,8 @@ namespace mgs {
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// ---------------------------------------------------------------- log scan
+// ------------------------------------------- elementwise scans (log, linear)
+// One geometry and workspace layout serves both arithmetics.
 struct LogGeom {
     int64_t S;      // chains = B*d
     int T, d;
@@ -34,6 +35,11 @@ hipError_t launch_log_fwd(const LogGeom &g, const float *la, const float *lb, co
 hipError_t launch_log_bwd(const LogGeom &g, const float *la, const float *lb, const float *lh0,
                           const float *dh, float *dla, float *dlb, float *dlh0, void *ws,
                           hipStream_t s);
+hipError_t launch_linear_fwd(const LogGeom &g, const float *a, const float *b, const float *h0,
+                             float *h, void *ws, hipStream_t s);
+hipError_t launch_linear_bwd(const LogGeom &g, const float *a, const float *b, const float *h0,
+                             const float *dh, float *da, float *db, float *dh0, void *ws,
+                             hipStream_t s);
 
 // ------------------------------------------------------------- block scans
 struct BlockGeom {

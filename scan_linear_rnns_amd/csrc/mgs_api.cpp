@@ -112,9 +112,14 @@ mgs_status mgs_workspace_check(void *workspace, void *stream, int *flags)
     return MGS_OK;
 }
 
-// ------------------------------------------------------------ log scan
+// ----------------------------------------- elementwise scans (log, linear)
 
-mgs_status mgs_scan_log_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes)
+using ElemFwd = hipError_t (*)(const mgs::LogGeom &, const float *, const float *, const float *,
+                               float *, void *, hipStream_t);
+using ElemBwd = hipError_t (*)(const mgs::LogGeom &, const float *, const float *, const float *,
+                               const float *, float *, float *, float *, void *, hipStream_t);
+
+static mgs_status elem_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes)
 {
     if (!bytes) return MGS_ERR_INVALID_VALUE;
     if (mgs_status st = check_sizes(B, T, d)) return st;
@@ -124,24 +129,63 @@ mgs_status mgs_scan_log_workspace_size(int64_t B, int64_t T, int64_t d, size_t *
     return MGS_OK;
 }
 
-mgs_status mgs_scan_log_fwd(const float *log_a, const float *log_b, const float *log_h0, float *h,
-                            int64_t B, int64_t T, int64_t d, void *workspace,
-                            size_t workspace_bytes, void *stream)
+static mgs_status elem_fwd(ElemFwd launch, const float *x1, const float *x2, const float *x0, float *h,
+                           int64_t B, int64_t T, int64_t d, void *workspace, size_t workspace_bytes,
+                           void *stream)
 {
     if (mgs_status st = check_sizes(B, T, d)) return st;
     if (B * T * d > kMaxElems || B * d > kMaxElems) return MGS_ERR_UNSUPPORTED;
     const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
-    if (n > 0 && (!log_a || !log_b || !h)) return MGS_ERR_INVALID_VALUE;
-    if (s0 > 0 && !log_h0) return MGS_ERR_INVALID_VALUE;
-    const Range in[] = {{log_a, n}, {log_b, n}, {log_h0, s0}};
+    if (n > 0 && (!x1 || !x2 || !h)) return MGS_ERR_INVALID_VALUE;
+    if (s0 > 0 && !x0) return MGS_ERR_INVALID_VALUE;
+    const Range in[] = {{x1, n}, {x2, n}, {x0, s0}};
     const Range out[] = {{h, n}};
     if (!all_aligned(in, 3) || !all_aligned(out, 1)) return MGS_ERR_INVALID_VALUE;
     if (any_alias(in, 3, out, 1)) return MGS_ERR_INVALID_VALUE;
     if (n == 0) return MGS_OK;
     const mgs::LogGeom g = mgs::log_geometry(B, T, d);
     if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
-    return hip_status(mgs::launch_log_fwd(g, log_a, log_b, log_h0, h, workspace,
-                                          as_stream(stream)));
+    return hip_status(launch(g, x1, x2, x0, h, workspace, as_stream(stream)));
+}
+
+static mgs_status elem_bwd(ElemFwd launch_f, ElemBwd launch_b, const float *x1, const float *x2,
+                           const float *x0, const float *dh, float *d1, float *d2, float *d0,
+                           int64_t B, int64_t T, int64_t d, void *workspace, size_t workspace_bytes,
+                           int fwd_state_valid, void *stream)
+{
+    if (mgs_status st = check_sizes(B, T, d)) return st;
+    if (B * T * d > kMaxElems || B * d > kMaxElems) return MGS_ERR_UNSUPPORTED;
+    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
+    if (n > 0 && (!x1 || !x2 || !dh || !d1 || !d2)) return MGS_ERR_INVALID_VALUE;
+    if (s0 > 0 && (!x0 || !d0)) return MGS_ERR_INVALID_VALUE;
+    const Range in[] = {{x1, n}, {x2, n}, {x0, s0}, {dh, n}};
+    const Range out[] = {{d1, n}, {d2, n}, {d0, s0}};
+    if (!all_aligned(in, 4) || !all_aligned(out, 3)) return MGS_ERR_INVALID_VALUE;
+    if (any_alias(in, 4, out, 3)) return MGS_ERR_INVALID_VALUE;
+    if (s0 == 0) return MGS_OK;
+    hipStream_t s = as_stream(stream);
+    if (T == 0)  // L does not depend on h0 when there are no steps
+        return hip_status(mgs::launch_fill_zero(d0, B * d, s));
+    const mgs::LogGeom g = mgs::log_geometry(B, T, d);
+    if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
+    if (g.nT > 1 && !fwd_state_valid) {
+        hipError_t e = launch_f(g, x1, x2, x0, nullptr, workspace, s);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return hip_status(launch_b(g, x1, x2, x0, dh, d1, d2, d0, workspace, s));
+}
+
+mgs_status mgs_scan_log_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes)
+{
+    return elem_workspace_size(B, T, d, bytes);
+}
+
+mgs_status mgs_scan_log_fwd(const float *log_a, const float *log_b, const float *log_h0, float *h,
+                            int64_t B, int64_t T, int64_t d, void *workspace,
+                            size_t workspace_bytes, void *stream)
+{
+    return elem_fwd(mgs::launch_log_fwd, log_a, log_b, log_h0, h, B, T, d, workspace, workspace_bytes,
+                    stream);
 }
 
 mgs_status mgs_scan_log_bwd(const float *log_a, const float *log_b, const float *log_h0,
@@ -149,27 +193,29 @@ mgs_status mgs_scan_log_bwd(const float *log_a, const float *log_b, const float 
                             int64_t B, int64_t T, int64_t d, void *workspace,
                             size_t workspace_bytes, int fwd_state_valid, void *stream)
 {
-    if (mgs_status st = check_sizes(B, T, d)) return st;
-    if (B * T * d > kMaxElems || B * d > kMaxElems) return MGS_ERR_UNSUPPORTED;
-    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
-    if (n > 0 && (!log_a || !log_b || !dh || !dlog_a || !dlog_b)) return MGS_ERR_INVALID_VALUE;
-    if (s0 > 0 && (!log_h0 || !dlog_h0)) return MGS_ERR_INVALID_VALUE;
-    const Range in[] = {{log_a, n}, {log_b, n}, {log_h0, s0}, {dh, n}};
-    const Range out[] = {{dlog_a, n}, {dlog_b, n}, {dlog_h0, s0}};
-    if (!all_aligned(in, 4) || !all_aligned(out, 3)) return MGS_ERR_INVALID_VALUE;
-    if (any_alias(in, 4, out, 3)) return MGS_ERR_INVALID_VALUE;
-    if (s0 == 0) return MGS_OK;
-    hipStream_t s = as_stream(stream);
-    if (T == 0)  // L does not depend on h0 when there are no steps
-        return hip_status(mgs::launch_fill_zero(dlog_h0, B * d, s));
-    const mgs::LogGeom g = mgs::log_geometry(B, T, d);
-    if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
-    if (g.nT > 1 && !fwd_state_valid) {
-        hipError_t e = mgs::launch_log_fwd(g, log_a, log_b, log_h0, nullptr, workspace, s);
-        if (e != hipSuccess) return hip_status(e);
-    }
-    return hip_status(mgs::launch_log_bwd(g, log_a, log_b, log_h0, dh, dlog_a, dlog_b, dlog_h0,
-                                          workspace, s));
+    return elem_bwd(mgs::launch_log_fwd, mgs::launch_log_bwd, log_a, log_b, log_h0, dh, dlog_a, dlog_b,
+                    dlog_h0, B, T, d, workspace, workspace_bytes, fwd_state_valid, stream);
+}
+
+mgs_status mgs_scan_linear_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes)
+{
+    return elem_workspace_size(B, T, d, bytes);
+}
+
+mgs_status mgs_scan_linear_fwd(const float *a, const float *b, const float *h0, float *h,
+                               int64_t B, int64_t T, int64_t d, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    return elem_fwd(mgs::launch_linear_fwd, a, b, h0, h, B, T, d, workspace, workspace_bytes, stream);
+}
+
+mgs_status mgs_scan_linear_bwd(const float *a, const float *b, const float *h0, const float *dh,
+                               float *da, float *db, float *dh0, int64_t B, int64_t T, int64_t d,
+                               void *workspace, size_t workspace_bytes, int fwd_state_valid,
+                               void *stream)
+{
+    return elem_bwd(mgs::launch_linear_fwd, mgs::launch_linear_bwd, a, b, h0, dh, da, db, dh0, B, T, d,
+                    workspace, workspace_bytes, fwd_state_valid, stream);
 }
 
 // ---------------------------------------------------------- block scans

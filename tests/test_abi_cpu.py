@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.declared_functions()
-    assert len(declared) == 13, declared
+    assert len(declared) == 16, declared
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -52,6 +52,9 @@ def _size(lib, fn, *dims):
 
 
 def test_workspace_queries(lib):
+    for shape in ((2, 64, 16), (16, 1024, 64)):   # one layout serves both elementwise scans
+        assert _size(lib, "mgs_scan_linear_workspace_size", *shape) == \
+            _size(lib, "mgs_scan_log_workspace_size", *shape)
     st, small = _size(lib, "mgs_scan_log_workspace_size", 2, 64, 16)
     assert st == OK and small >= 256
     st, big = _size(lib, "mgs_scan_log_workspace_size", 16, 1024, 64)
@@ -70,11 +73,13 @@ def test_workspace_queries(lib):
         assert _size(lib, fn, 1 << 16, 1 << 10, 64, 8)[0] == UNSUPPORTED
 
 
-def test_log_fwd_validation(lib):
+@pytest.mark.parametrize("op", ["log", "linear"])
+def test_elementwise_fwd_validation(lib, op):
     B, T, d = 2, 8, 16
     ws = fake(9)
+    fn = getattr(lib, f"mgs_scan_{op}_fwd")
     args = lambda la=fake(0), lb=fake(1), lh0=fake(2), h=fake(3), B=B, T=T, d=d, ws=ws, nbytes=1 << 20: \
-        lib.mgs_scan_log_fwd(la, lb, lh0, h, B, T, d, ws, nbytes, None)
+        fn(la, lb, lh0, h, B, T, d, ws, nbytes, None)
     assert args(la=None) == INVALID
     assert args(h=None) == INVALID
     assert args(lh0=None) == INVALID
@@ -88,10 +93,12 @@ def test_log_fwd_validation(lib):
     assert args(T=0, la=None, lb=None, h=None) == OK
 
 
-def test_log_bwd_validation(lib):
+@pytest.mark.parametrize("op", ["log", "linear"])
+def test_elementwise_bwd_validation(lib, op):
     B, T, d = 2, 8, 16
+    fn = getattr(lib, f"mgs_scan_{op}_bwd")
     call = lambda dla=fake(4), dlh0=fake(6), ws=fake(9), nbytes=1 << 20, B=B: \
-        lib.mgs_scan_log_bwd(fake(0), fake(1), fake(2), fake(3), dla, fake(5), dlh0, B, T, d, ws, nbytes, 1, None)
+        fn(fake(0), fake(1), fake(2), fake(3), dla, fake(5), dlh0, B, T, d, ws, nbytes, 1, None)
     assert call(dla=None) == INVALID
     assert call(dlh0=None) == INVALID
     assert call(dla=fake(3)) == INVALID                      # dlog_a aliases dh
