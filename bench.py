@@ -53,7 +53,7 @@ def log(msg):
 
 def compulsory_bytes(op, B, T, d, k=8):
     N, S = B * T * d, B * d
-    if op == "log":
+    if op in ("log", "linear"):
         return 12 * N + 4 * S, 20 * N + 8 * S
     if op == "affine":  # h0 = 0 is passed as NULL: not read; dh0 written
         return 4 * N * (k + 2), 4 * N * (2 * k + 3) + 4 * S
@@ -70,7 +70,7 @@ class OpRun:
         import torch
 
         import scan_linear_rnns_amd as mgs
-        from synthetic import block_inputs, log_inputs
+        from synthetic import block_inputs, linear_inputs, log_inputs
 
         self.name, self.op, self.B, self.T, self.d = name, op, B, T, d
         self.N = B * T * d
@@ -82,6 +82,10 @@ class OpRun:
             inp = log_inputs(B, T, d, 0)
             base = [t(inp.log_a), t(inp.log_b), t(inp.log_h0), t(inp.dh)]
             ws_bytes = mgs.mgs_scan_log_workspace_size(B, T, d)
+        elif op == "linear":
+            inp = linear_inputs(B, T, d, 0)
+            base = [t(inp.a), t(inp.b), t(inp.h0), t(inp.dh)]
+            ws_bytes = mgs.mgs_scan_linear_workspace_size(B, T, d)
         else:
             inp = block_inputs(B, T, d, k=8, seed=0, with_dP=(op == "matrix"))
             base = [t(inp.A), t(inp.b), t(inp.dh)] + ([t(inp.dP)] if op == "matrix" else [])
@@ -94,13 +98,14 @@ class OpRun:
         for _ in range(self.M):
             xs = [x.clone() for x in base]
             ws = mgs.workspace(ws_bytes, dev)
-            if op == "log":
+            if op in ("log", "linear"):
                 la, lb, lh0, dh = xs
                 h = torch.empty_like(la)
                 dla, dlb, dlh0 = torch.empty_like(la), torch.empty_like(la), torch.empty_like(lh0)
                 fa = (P(la), P(lb), P(lh0), P(h), B, T, d, P(ws), ws.numel())
                 ba = (P(la), P(lb), P(lh0), P(dh), P(dla), P(dlb), P(dlh0), B, T, d, P(ws), ws.numel(), 1)
-                fn_f, fn_b = self.lib.mgs_scan_log_fwd, self.lib.mgs_scan_log_bwd
+                fn_f = getattr(self.lib, f"mgs_scan_{op}_fwd")
+                fn_b = getattr(self.lib, f"mgs_scan_{op}_bwd")
                 keep = xs + [h, dla, dlb, dlh0, ws]
             elif op == "affine":
                 A, b, dh = xs
@@ -236,7 +241,7 @@ def cpu_baseline(seconds):
                       f"host thread, repeated {n} times over {el:.1f} s"}
 
 
-LOG_SOURCES = ("log_scan.hip", "device.hpp")
+LOG_SOURCES = ("elem_scan.hip", "device.hpp")
 
 
 def kernel_source_hash(names=None):
@@ -308,6 +313,8 @@ def main():
         ("log_lab", "log", 128, 64, 64),
         ("log_tiny", "log", 2, 64, 16),
         ("log_longT", "log", 16, 1024, 64),
+        ("linear_lab", "linear", 128, 64, 64),
+        ("linear_longT", "linear", 16, 1024, 64),
         ("affine_lab", "affine", 128, 64, 64),
         ("affine_longT", "affine", 16, 1024, 64),
         ("matrix_longT", "matrix", 16, 1024, 64),
@@ -348,6 +355,8 @@ def main():
             rec["op"] = "block cumulative product (b = 0), k = 8"
         elif op == "affine":
             rec["op"] = "block-affine scan, k = 8"
+        elif op == "linear":
+            rec["op"] = "linear-space scan, signed gates"
         else:
             rec["op"] = "log-space scan"
         ops[name] = rec

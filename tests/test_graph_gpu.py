@@ -12,7 +12,7 @@ import ctypes
 import numpy as np
 import pytest
 
-from synthetic import block_inputs, log_inputs
+from synthetic import block_inputs, linear_inputs, log_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -91,3 +91,23 @@ def test_block_scans_graph_replays(gpu):
         for a, b_ in zip(got, ref):
             assert torch.equal(a, b_)
     assert mgs.mgs_workspace_check(ws) == 0 and mgs.mgs_workspace_check(wsm) == 0
+
+
+def test_linear_scan_graph_replays(gpu):
+    import torch
+    import scan_linear_rnns_amd as mgs
+    print("[graph] linear scan B=16 T=1024 d=64", flush=True)
+    inp = linear_inputs(16, 1024, 64, 23)
+    a, b, h0, dh = (_t(x, gpu) for x in (inp.a, inp.b, inp.h0, inp.dh))
+    h, ws = mgs.mgs_scan_linear_fwd(a, b, h0)
+    ref = [h.clone(), *[x.clone() for x in mgs.mgs_scan_linear_bwd(a, b, h0, dh, ws=ws, fwd_state_valid=True)]]
+    outs = [torch.empty_like(a), torch.empty_like(a), torch.empty_like(a), torch.empty_like(h0)]
+
+    def step():
+        mgs.mgs_scan_linear_fwd(a, b, h0, h=outs[0], ws=ws)
+        mgs.mgs_scan_linear_bwd(a, b, h0, dh, ws=ws, fwd_state_valid=True, out=tuple(outs[1:]))
+
+    for got in _replays(step, outs):
+        for x, y in zip(got, ref):
+            assert torch.equal(x, y)
+    assert mgs.mgs_workspace_check(ws) == 0
