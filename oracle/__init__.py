@@ -15,6 +15,9 @@ What each function follows is stated in ``oracle.c``:
   * ``linear_fwd`` / ``linear_bwd`` -- the same recurrence in linear space,
     a_t of either sign (linear_scan in the home page's speed-up table and in
     the how-to's Step 2 table; SignedMinGRU's signed gates on the home page).
+  * ``mingru_fwd`` / ``mingru_bwd`` -- the minGRU cell ahead of the scan
+    (a = sigmoid(-k), b = (1 - a) g(x), h_0 = g(x0); home page, introduction)
+    followed by the same recurrence; gradients for k, x, x0.
   * ``block_affine_fwd`` / ``block_affine_bwd`` -- h_t = A_t h_{t-1} + b_t
     with block-diagonal k x k transitions (matrix_affine_scan in the
     "Run the benchmarks" how-to, Step 2; RotationMinGRU / GivensMinGRU on the
@@ -68,6 +71,8 @@ def _load():
                 "oracle_log_bwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I],
                 "oracle_linear_fwd": [_D, _D, _D, _D, _I, _I, _I],
                 "oracle_linear_bwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I],
+                "oracle_mingru_fwd": [_D, _D, _D, _D, _I, _I, _I],
+                "oracle_mingru_bwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I],
                 "oracle_block_affine_fwd": [_D, _D, _D, _D, _I, _I, _I, _I],
                 "oracle_block_affine_bwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I],
                 "oracle_block_matrix_fwd": [_D, _D, _I, _I, _I, _I],
@@ -131,6 +136,28 @@ def linear_bwd(a, b, h0, dh):
     dh0 = np.empty_like(h0)
     _load().oracle_linear_bwd(_p(a), _p(b), _p(h0), _p(g), _p(da), _p(db), _p(dh0), B, T, d)
     return da, db, dh0
+
+
+def mingru_fwd(k, x, x0):
+    """h (B,T,d) of the minGRU cell + scan from pre-activations k, x (B,T,d) and x0 (B,d)."""
+    k, x, x0 = _f64(k), _f64(x), _f64(x0)
+    B, T, d = k.shape
+    assert x.shape == k.shape and x0.shape == (B, d)
+    h = np.empty((B, T, d), np.float64)
+    _load().oracle_mingru_fwd(_p(k), _p(x), _p(x0), _p(h), B, T, d)
+    return h
+
+
+def mingru_bwd(k, x, x0, dh):
+    """(dk, dx, dx0) for L = sum(dh * h)."""
+    k, x, x0, g = _f64(k), _f64(x), _f64(x0), _f64(dh)
+    B, T, d = k.shape
+    assert x.shape == k.shape and g.shape == k.shape and x0.shape == (B, d)
+    dk = np.empty_like(k)
+    dx = np.empty_like(k)
+    dx0 = np.empty_like(x0)
+    _load().oracle_mingru_bwd(_p(k), _p(x), _p(x0), _p(g), _p(dk), _p(dx), _p(dx0), B, T, d)
+    return dk, dx, dx0
 
 
 def _block_shapes(A, d, k):

@@ -22,12 +22,18 @@
  *     speed-up table and in the how-to's Step 2 table; the signed gates of
  *     SignedMinGRU, same page) is the same recurrence with a_t, b_t, h_0 given
  *     directly and a_t of either sign.
+ *   - The minGRU cell ahead of the log-space scan (same page, introduction:
+ *     minGRU of Feng et al.): from pre-activations k_t, x_t and x_0,
+ *     a_t = sigmoid(-k_t), z_t = 1 - a_t, b_t = z_t g(x_t), h_0 = g(x_0), with
+ *     g(x) = x + 0.5 for x >= 0 and sigmoid(x) for x < 0 (the pages do not
+ *     write g out; this is the reading taken), then the same recurrence.
  *   - Gradients are the chain rule applied to these loops for the loss
  *     L = sum_t <dh_t, h_t> (resp. sum_t <dP_t, P_t>).
  *
  * Layouts (row-major, last index fastest):
  *   log scan:   la, lb, h, dh, dla, dlb : (B, T, d);  lh0, dlh0 : (B, d)
  *   linear scan: a, b, h, dh, da, db : (B, T, d);  h0, dh0 : (B, d)
+ *   minGRU cell: k, x, h, dh, dk, dx : (B, T, d);  x0, dx0 : (B, d)
  *   block ops:  A, dA, P, dP : (B, T, nb, k, k) with nb = d / k and
  *               (A h)_r = sum_c A[r][c] h[c];  b, h, dh, db : (B, T, d);
  *               h0, dh0 : (B, d);  block j owns channels [j*k, (j+1)*k).
@@ -133,6 +139,63 @@ void oracle_linear_bwd(const double *a, const double *bv, const double *h0,
                 a_next = a[i];
             }
             dh0[b * d + c] = (T > 0) ? a_next * g : 0.0;
+        }
+    free(hs);
+}
+
+/* ------------------------------------------------------ minGRU cell + scan */
+
+static double sigm(double u) { return 1.0 / (1.0 + exp(-u)); }
+
+/* g(x) = x + 0.5 (x >= 0), sigmoid(x) (x < 0), and its derivative */
+static double gpos(double x) { return x >= 0.0 ? x + 0.5 : sigm(x); }
+static double gpos_d(double x) { return x >= 0.0 ? 1.0 : sigm(x) * (1.0 - sigm(x)); }
+
+/* Forward: a_t = sigmoid(-k_t), b_t = (1 - a_t) g(x_t), h_0 = g(x_0);
+ * h_t = a_t h_{t-1} + b_t; writes h_1..T. */
+void oracle_mingru_fwd(const double *k, const double *x, const double *x0,
+                       double *h, int64_t B, int64_t T, int64_t d)
+{
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < d; ++c) {
+            double hp = gpos(x0[b * d + c]);
+            for (int64_t t = 0; t < T; ++t) {
+                int64_t i = (b * T + t) * d + c;
+                double a = sigm(-k[i]);
+                hp = a * hp + (1.0 - a) * gpos(x[i]);
+                h[i] = hp;
+            }
+        }
+}
+
+/* Backward of oracle_mingru_fwd under upstream dh = dL/dh_t, with
+ * g_T = dh_T, g_t = dh_t + a_{t+1} g_{t+1} as for the scan, and
+ *   dh_t/dk_t = a_t (1 - a_t) (g(x_t) - h_{t-1})   (da/dk = -a(1-a), dz/dk = a(1-a)),
+ *   dh_t/dx_t = (1 - a_t) g'(x_t),   dh_1/dx_0 = a_1 g'(x_0). */
+void oracle_mingru_bwd(const double *k, const double *x, const double *x0,
+                       const double *dh, double *dk, double *dx, double *dx0,
+                       int64_t B, int64_t T, int64_t d)
+{
+    double *hs = (double *)malloc(sizeof(double) * (size_t)(T + 1));
+    if (!hs) return;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < d; ++c) {
+            hs[0] = gpos(x0[b * d + c]);
+            for (int64_t t = 0; t < T; ++t) {
+                int64_t i = (b * T + t) * d + c;
+                double a = sigm(-k[i]);
+                hs[t + 1] = a * hs[t] + (1.0 - a) * gpos(x[i]);
+            }
+            double g = 0.0, a_next = 0.0;
+            for (int64_t t = T - 1; t >= 0; --t) {
+                int64_t i = (b * T + t) * d + c;
+                g = dh[i] + a_next * g;
+                double a = sigm(-k[i]);
+                dk[i] = g * a * (1.0 - a) * (gpos(x[i]) - hs[t]);
+                dx[i] = g * (1.0 - a) * gpos_d(x[i]);
+                a_next = a;
+            }
+            dx0[b * d + c] = (T > 0) ? g * a_next * gpos_d(x0[b * d + c]) : 0.0;
         }
     free(hs);
 }

@@ -13,6 +13,8 @@ once to float32 at the end):
   and g(x) = x + 0.5 for x >= 0, sigmoid(x) otherwise:
   log_a = log a, log_b = log(z * g(x)), log_h0 = log g(x0).  Logs are taken
   in closed form (log sigmoid(u) = -softplus(-u)) so nothing underflows.
+* MinGRU cell fused ahead of the log-space scan: the same draws k, x, x0, dh,
+  passed as pre-activations (the kernel forms log a, log b, log h0 itself).
 * Linear-space scan with signed gates (linear_scan; SignedMinGRU's
   negative-eigenvalue gates on the home page).  Same draws as the log-space
   scan (k, x, x0, dh in that order); the MinGRU gate sigmoid(-k) in [0, 1] is
@@ -54,6 +56,14 @@ class LogInputs:
     dh: np.ndarray      # (B,T,d) float32
 
 
+def mingru_logs(k, x, x0):
+    """(log a, log b, log h0) in float64 of the MinGRU gate recipe, from pre-activations."""
+    k, x, x0 = (np.asarray(v, dtype=np.float64) for v in (k, x, x0))
+    log_a = -_softplus(k)            # log sigmoid(-k)
+    log_z = -_softplus(-k)           # log (1 - sigmoid(-k)) = log sigmoid(k)
+    return log_a, log_z + _log_g(x), _log_g(x0)
+
+
 def log_inputs(B: int, T: int, d: int, seed: int = 0) -> LogInputs:
     """MinGRU gate generator for the log-space scan (see module docstring)."""
     rng = np.random.default_rng(seed)
@@ -61,12 +71,28 @@ def log_inputs(B: int, T: int, d: int, seed: int = 0) -> LogInputs:
     x = rng.standard_normal((B, T, d))
     x0 = rng.standard_normal((B, d))
     dh = rng.standard_normal((B, T, d))
-    log_a = -_softplus(k)            # log sigmoid(-k)
-    log_z = -_softplus(-k)           # log (1 - sigmoid(-k)) = log sigmoid(k)
-    log_b = log_z + _log_g(x)
-    log_h0 = _log_g(x0)
+    log_a, log_b, log_h0 = mingru_logs(k, x, x0)
     f = np.float32
     return LogInputs(log_a.astype(f), log_b.astype(f), log_h0.astype(f), dh.astype(f))
+
+
+@dataclass
+class MinGRUInputs:
+    k: np.ndarray       # (B,T,d) float32, gate pre-activation
+    x: np.ndarray       # (B,T,d) float32, candidate pre-activation
+    x0: np.ndarray      # (B,d)   float32, initial-state pre-activation
+    dh: np.ndarray      # (B,T,d) float32
+
+
+def mingru_inputs(B: int, T: int, d: int, seed: int = 0) -> MinGRUInputs:
+    """The log-space scan's draws before the gate recipe (same seed, same values)."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, T, d))
+    x = rng.standard_normal((B, T, d))
+    x0 = rng.standard_normal((B, d))
+    dh = rng.standard_normal((B, T, d))
+    f = np.float32
+    return MinGRUInputs(k.astype(f), x.astype(f), x0.astype(f), dh.astype(f))
 
 
 @dataclass
@@ -160,6 +186,8 @@ CONFIGS = {
     "log_tiny":   dict(op="log", B=2, T=64, d=16),
     "log_lab":    dict(op="log", B=128, T=64, d=64),
     "log_longT":  dict(op="log", B=16, T=1024, d=64),
+    "mingru_lab":   dict(op="mingru", B=128, T=64, d=64),
+    "mingru_longT": dict(op="mingru", B=16, T=1024, d=64),
     "linear_lab":   dict(op="linear", B=128, T=64, d=64),
     "linear_longT": dict(op="linear", B=16, T=1024, d=64),
     "block_lab":  dict(op="block", B=128, T=64, d=64, k=8),

@@ -15,6 +15,7 @@ import pytest
 import oracle
 from tests import test_oracle_pins as pins
 from tests import test_oracle_pins_linear as lpins
+from tests import test_oracle_pins_mingru as mpins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -34,6 +35,12 @@ MUTANTS = [
     ("linear_bwd h_t for h_{t-1}", "da[i] = g * hs[t];", "da[i] = g * hs[t + 1];"),
     ("linear_bwd dh0 drops a_1", "dh0[b * d + c] = (T > 0) ? a_next * g : 0.0;",
      "dh0[b * d + c] = (T > 0) ? g : 0.0;"),
+    ("mingru_fwd b uses a not 1 - a", "hp = a * hp + (1.0 - a) * gpos(x[i]);", "hp = a * hp + a * gpos(x[i]);"),
+    ("mingru_bwd dk drops h_{t-1}", "dk[i] = g * a * (1.0 - a) * (gpos(x[i]) - hs[t]);",
+     "dk[i] = g * a * (1.0 - a) * gpos(x[i]);"),
+    ("mingru_bwd dx uses a not 1 - a", "dx[i] = g * (1.0 - a) * gpos_d(x[i]);", "dx[i] = g * a * gpos_d(x[i]);"),
+    ("mingru_bwd dx0 drops g'", "dx0[b * d + c] = (T > 0) ? g * a_next * gpos_d(x0[b * d + c]) : 0.0;",
+     "dx0[b * d + c] = (T > 0) ? g * a_next : 0.0;"),
     ("affine_fwd transposed A", "for (int64_t c = 0; c < k; ++c) s += At[r * k + c] * cur[c];",
      "for (int64_t c = 0; c < k; ++c) s += At[c * k + r] * cur[c];"),
     ("affine_bwd A not A^T", "for (int64_t r = 0; r < k; ++r) s += At[r * k + c] * g[r];",
@@ -63,6 +70,8 @@ PINS = [
     lpins.test_golden_linear_scan,
     lambda: lpins.test_constant_coefficients_geometric(-0.8, 1.5, -1.0),
     lpins.test_gradients_finite_difference,
+    mpins.test_golden_mingru_cell,
+    mpins.test_gradients_finite_difference,
 ]
 
 
@@ -84,6 +93,7 @@ def test_mutant_is_caught(name, orig, mut, monkeypatch):
     with tempfile.TemporaryDirectory() as tmp:
         lib = ctypes.CDLL(_build(text.replace(orig, mut), tmp))
         for fname in ("oracle_log_fwd", "oracle_log_bwd", "oracle_linear_fwd", "oracle_linear_bwd",
+                      "oracle_mingru_fwd", "oracle_mingru_bwd",
                       "oracle_block_affine_fwd",
                       "oracle_block_affine_bwd", "oracle_block_matrix_fwd", "oracle_block_matrix_bwd"):
             fn, ref = getattr(lib, fname), getattr(real, fname)
