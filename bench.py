@@ -53,7 +53,7 @@ def log(msg):
 
 def compulsory_bytes(op, B, T, d, k=8):
     N, S = B * T * d, B * d
-    if op in ("log", "linear"):
+    if op in ("log", "linear", "mingru"):
         return 12 * N + 4 * S, 20 * N + 8 * S
     if op == "affine":  # h0 = 0 is passed as NULL: not read; dh0 written
         return 4 * N * (k + 2), 4 * N * (2 * k + 3) + 4 * S
@@ -70,7 +70,7 @@ class OpRun:
         import torch
 
         import scan_linear_rnns_amd as mgs
-        from synthetic import block_inputs, linear_inputs, log_inputs
+        from synthetic import block_inputs, linear_inputs, log_inputs, mingru_inputs
 
         self.name, self.op, self.B, self.T, self.d = name, op, B, T, d
         self.N = B * T * d
@@ -82,6 +82,10 @@ class OpRun:
             inp = log_inputs(B, T, d, 0)
             base = [t(inp.log_a), t(inp.log_b), t(inp.log_h0), t(inp.dh)]
             ws_bytes = mgs.mgs_scan_log_workspace_size(B, T, d)
+        elif op == "mingru":
+            inp = mingru_inputs(B, T, d, 0)
+            base = [t(inp.k), t(inp.x), t(inp.x0), t(inp.dh)]
+            ws_bytes = mgs.mgs_scan_mingru_workspace_size(B, T, d)
         elif op == "linear":
             inp = linear_inputs(B, T, d, 0)
             base = [t(inp.a), t(inp.b), t(inp.h0), t(inp.dh)]
@@ -98,7 +102,7 @@ class OpRun:
         for _ in range(self.M):
             xs = [x.clone() for x in base]
             ws = mgs.workspace(ws_bytes, dev)
-            if op in ("log", "linear"):
+            if op in ("log", "linear", "mingru"):
                 la, lb, lh0, dh = xs
                 h = torch.empty_like(la)
                 dla, dlb, dlh0 = torch.empty_like(la), torch.empty_like(la), torch.empty_like(lh0)
@@ -313,6 +317,8 @@ def main():
         ("log_lab", "log", 128, 64, 64),
         ("log_tiny", "log", 2, 64, 16),
         ("log_longT", "log", 16, 1024, 64),
+        ("mingru_lab", "mingru", 128, 64, 64),
+        ("mingru_longT", "mingru", 16, 1024, 64),
         ("linear_lab", "linear", 128, 64, 64),
         ("linear_longT", "linear", 16, 1024, 64),
         ("affine_lab", "affine", 128, 64, 64),
@@ -357,6 +363,8 @@ def main():
             rec["op"] = "block-affine scan, k = 8"
         elif op == "linear":
             rec["op"] = "linear-space scan, signed gates"
+        elif op == "mingru":
+            rec["op"] = "minGRU cell fused ahead of the log-space scan (inputs k, x, x0)"
         else:
             rec["op"] = "log-space scan"
         ops[name] = rec

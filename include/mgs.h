@@ -14,6 +14,8 @@
  *      op matrix_affine_scan);
  *   3. block cumulative product P_t = A_t P_{t-1}, P_0 = I, the b = 0 case
  *      (same table, op matrix_scan);
+ *   1b. the same scan with the minGRU cell fused ahead of it (inputs are the
+ *      pre-activations; gradients are returned for them);
  *   4. linear-space elementwise scan, a_t of either sign -- the op the pages
  *      list as linear_scan (home page speed-up table; "Run the benchmarks"
  *      how-to, Step 2), for gates with negative eigenvalues.
@@ -120,6 +122,38 @@ mgs_status mgs_scan_log_bwd(const float *log_a, const float *log_b, const float 
                             int64_t B, int64_t T, int64_t d,
                             void *workspace, size_t workspace_bytes, int fwd_state_valid,
                             void *stream);
+
+/* ------------------------------------ minGRU cell + log-space scan --- */
+/*
+ * The minGRU cell fused ahead of the log-space scan (minGRU home page,
+ * introduction: minGRU of Feng et al.; the pages do not write the cell out,
+ * so this is the reading taken).  From pre-activations k, x (B,T,d), x0 (B,d):
+ *     a_t = sigmoid(-k_t),  b_t = (1 - a_t) g(x_t),  h_0 = g(x0),
+ *     g(u) = u + 0.5 (u >= 0), sigmoid(u) (u < 0),
+ * then h_t = a_t h_{t-1} + b_t evaluated in log space exactly as
+ * mgs_scan_log_fwd does; log a, log b and log h0 are formed in registers and
+ * never stored.  Same workspace rules as the log-space scan.
+ *   k, x : (B,T,d) in     x0 : (B,d) in     h : (B,T,d) out
+ */
+mgs_status mgs_scan_mingru_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes);
+
+mgs_status mgs_scan_mingru_fwd(const float *k, const float *x, const float *x0, float *h,
+                               int64_t B, int64_t T, int64_t d,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of mgs_scan_mingru_fwd for L = sum_t <dh_t, h_t>: with the reverse
+ * scan g_T = dh_T, g_t = dh_t + a_{t+1} g_{t+1} and z_t = 1 - a_t,
+ *     dk_t = g_t a_t z_t (g(x_t) - h_{t-1}),   dx_t = g_t z_t g'(x_t),
+ *     dx0 = g_1 a_1 g'(x0).
+ *   dh : (B,T,d) in;   dk, dx : (B,T,d) out;   dx0 : (B,d) out.
+ * fwd_state_valid as for mgs_scan_log_bwd.
+ */
+mgs_status mgs_scan_mingru_bwd(const float *k, const float *x, const float *x0, const float *dh,
+                               float *dk, float *dx, float *dx0,
+                               int64_t B, int64_t T, int64_t d,
+                               void *workspace, size_t workspace_bytes, int fwd_state_valid,
+                               void *stream);
 
 /* --------------------------------------------------- linear-space scan --- */
 /*

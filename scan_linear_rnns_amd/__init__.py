@@ -8,6 +8,7 @@ or PyTorch fallback: without the built library (or a GPU) these calls raise.
 
 Ops (see include/mgs.h for the definitions and their sources on the pages):
   * mgs_scan_log_fwd / mgs_scan_log_bwd                 log-space minGRU scan
+  * mgs_scan_mingru_fwd / mgs_scan_mingru_bwd           minGRU cell fused ahead of the log-space scan
   * mgs_scan_linear_fwd / mgs_scan_linear_bwd           linear-space scan, signed gates
   * mgs_block_affine_scan_fwd / mgs_block_affine_scan_bwd   h_t = A_t h_{t-1} + b_t
   * mgs_block_matrix_scan_fwd / mgs_block_matrix_scan_bwd   P_t = A_t P_{t-1}
@@ -22,6 +23,7 @@ from ._lib import MgsError, check, declared_functions, load, status_string  # no
 __all__ = [
     "MgsError", "load", "workspace", "mgs_workspace_check",
     "mgs_scan_log_workspace_size", "mgs_scan_log_fwd", "mgs_scan_log_bwd",
+    "mgs_scan_mingru_workspace_size", "mgs_scan_mingru_fwd", "mgs_scan_mingru_bwd",
     "mgs_scan_linear_workspace_size", "mgs_scan_linear_fwd", "mgs_scan_linear_bwd",
     "mgs_block_affine_scan_workspace_size", "mgs_block_affine_scan_fwd", "mgs_block_affine_scan_bwd",
     "mgs_block_matrix_scan_workspace_size", "mgs_block_matrix_scan_fwd", "mgs_block_matrix_scan_bwd",
@@ -64,6 +66,10 @@ def _size(fn, *dims):
 
 def mgs_scan_log_workspace_size(B, T, d):
     return _size("mgs_scan_log_workspace_size", B, T, d)
+
+
+def mgs_scan_mingru_workspace_size(B, T, d):
+    return _size("mgs_scan_mingru_workspace_size", B, T, d)
 
 
 def mgs_scan_linear_workspace_size(B, T, d):
@@ -132,6 +138,58 @@ def mgs_scan_log_bwd(log_a, log_b, log_h0, dh, ws=None, fwd_state_valid=False, o
                                   _ptr(dlh0), B, T, d, _ptr(ws), ws.numel(), int(bool(fwd_state_valid)),
                                   _stream(stream)), "mgs_scan_log_bwd")
     return dla, dlb, dlh0
+
+
+# ------------------------------------------ minGRU cell + log-space scan
+
+def _elem_fwd(fn, names, x1, x2, x0, h, ws, stream, size_fn):
+    import torch
+    B, T, d = x1.shape
+    dev = x1.device
+    _check_tensor(names[0], x1, (B, T, d))
+    _check_tensor(names[1], x2, (B, T, d), dev)
+    _check_tensor(names[2], x0, (B, d), dev)
+    if h is None:
+        h = torch.empty((B, T, d), dtype=torch.float32, device=dev)
+    _check_tensor("h", h, (B, T, d), dev)
+    if ws is None:
+        ws = workspace(size_fn(B, T, d), dev)
+    check(getattr(load(), fn)(_ptr(x1), _ptr(x2), _ptr(x0), _ptr(h), B, T, d, _ptr(ws), ws.numel(),
+                              _stream(stream)), fn)
+    return h, ws
+
+
+def _elem_bwd(fn, names, x1, x2, x0, dh, ws, fwd_state_valid, out, stream, size_fn):
+    import torch
+    B, T, d = x1.shape
+    dev = x1.device
+    _check_tensor(names[0], x1, (B, T, d))
+    _check_tensor(names[1], x2, (B, T, d), dev)
+    _check_tensor(names[2], x0, (B, d), dev)
+    _check_tensor("dh", dh, (B, T, d), dev)
+    if out is None:
+        out = (torch.empty((B, T, d), dtype=torch.float32, device=dev),
+               torch.empty((B, T, d), dtype=torch.float32, device=dev),
+               torch.empty((B, d), dtype=torch.float32, device=dev))
+    d1, d2, d0 = out
+    if ws is None:
+        ws = workspace(size_fn(B, T, d), dev)
+        fwd_state_valid = False
+    check(getattr(load(), fn)(_ptr(x1), _ptr(x2), _ptr(x0), _ptr(dh), _ptr(d1), _ptr(d2), _ptr(d0),
+                              B, T, d, _ptr(ws), ws.numel(), int(bool(fwd_state_valid)), _stream(stream)), fn)
+    return d1, d2, d0
+
+
+def mgs_scan_mingru_fwd(k, x, x0, h=None, ws=None, stream=None):
+    """h (B,T,d) of the minGRU cell + log-space scan from pre-activations; returns (h, ws)."""
+    return _elem_fwd("mgs_scan_mingru_fwd", ("k", "x", "x0"), k, x, x0, h, ws, stream,
+                     mgs_scan_mingru_workspace_size)
+
+
+def mgs_scan_mingru_bwd(k, x, x0, dh, ws=None, fwd_state_valid=False, out=None, stream=None):
+    """(dk, dx, dx0) for L = sum(dh * h)."""
+    return _elem_bwd("mgs_scan_mingru_bwd", ("k", "x", "x0"), k, x, x0, dh, ws, fwd_state_valid, out,
+                     stream, mgs_scan_mingru_workspace_size)
 
 
 # ----------------------------------------------------- linear-space scan

@@ -27,6 +27,9 @@ SIGNATURES = {
     "mgs_scan_log_workspace_size": ([_I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),
     "mgs_scan_log_fwd": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
     "mgs_scan_log_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _INT, _P], _INT),
+    "mgs_scan_mingru_workspace_size": ([_I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),
+    "mgs_scan_mingru_fwd": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
+    "mgs_scan_mingru_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _INT, _P], _INT),
     "mgs_scan_linear_workspace_size": ([_I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),
     "mgs_scan_linear_fwd": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
     "mgs_scan_linear_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _INT, _P], _INT),

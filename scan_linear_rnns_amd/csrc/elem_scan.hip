@@ -3,6 +3,8 @@
 //   * log space (minGRU home page, introduction; "Triton on GPU", section "What
 //     you gain (and where you don't)", parallel_scan_log): inputs log a, log b,
 //     log h0 with a > 0, evaluated in log space after Heinsen (arXiv:2311.06281);
+//   * log space with the minGRU cell fused ahead of it: inputs are the
+//     pre-activations k, x, x0 and the kernels form log a, log b, log h0;
 //   * linear space (linear_scan in the home page's speed-up table and in the
 //     "Run the benchmarks" how-to, Step 2): inputs a, b, h0 with a of either
 //     sign (SignedMinGRU's negative-eigenvalue gates, home page).
@@ -84,14 +86,20 @@ struct LogAlg {
     __device__ static float out(float A, float H, float c) { return ex2(A + c) + ex2(H); }
     __device__ static float carry0(float lh0, bool valid) { return valid ? lh0 * kLog2e : -kInf; }
     __device__ static float to_linear(float c) { return ex2(c); }
-    // backward: linear-space a and b of a step
-    __device__ static float lin_a(float la) { return ex2(la * kLog2e); }
-    __device__ static float lin_b(float lb) { return ex2(lb * kLog2e); }
+    // backward: linear-space a and b of a step from its inputs
+    __device__ static void lin_ab(float la, float lb, float &a, float &b)
+    {
+        a = ex2(la * kLog2e);
+        b = ex2(lb * kLog2e);
+    }
     __device__ static float lin_h0(float lh0) { return ex2(lh0 * kLog2e); }
     // gradients: d/dlog a = g a h_{t-1}, d/dlog b = g b, d/dlog h0 = (a_1 g_1) h0
-    __device__ static float grad_a(float g, float ag, float hprev) { return ag * hprev; }
-    __device__ static float grad_b(float g, float b) { return g * b; }
-    __device__ static float grad_h0(float w, float h0) { return w * h0; }
+    __device__ static void grads(float, float, float a, float b, float g, float hprev, float &d1, float &d2)
+    {
+        d1 = a * g * hprev;
+        d2 = g * b;
+    }
+    __device__ static float grad_h0(float w, float h0, float) { return w * h0; }
 };
 
 // Linear space: x = a (any sign), y = b; pair (A, H) as is.
@@ -117,13 +125,99 @@ struct LinAlg {
     __device__ static float out(float A, float H, float c) { return A * c + H; }
     __device__ static float carry0(float h0, bool valid) { return valid ? h0 : 0.0f; }
     __device__ static float to_linear(float c) { return c; }
-    __device__ static float lin_a(float a) { return a; }
-    __device__ static float lin_b(float b) { return b; }
+    __device__ static void lin_ab(float a_in, float b_in, float &a, float &b)
+    {
+        a = a_in;
+        b = b_in;
+    }
     __device__ static float lin_h0(float h0) { return h0; }
     // gradients: d/da = g h_{t-1}, d/db = g, d/dh0 = a_1 g_1
-    __device__ static float grad_a(float g, float ag, float hprev) { return g * hprev; }
-    __device__ static float grad_b(float g, float b) { return g; }
-    __device__ static float grad_h0(float w, float h0) { return w; }
+    __device__ static void grads(float, float, float, float, float g, float hprev, float &d1, float &d2)
+    {
+        d1 = g * hprev;
+        d2 = g;
+    }
+    __device__ static float grad_h0(float w, float, float) { return w; }
+};
+
+// The minGRU cell ahead of the log-space scan (minGRU home page, introduction:
+// Feng et al.'s minGRU): inputs are the pre-activations k, x, x0 and
+//     a = sigmoid(-k),  z = 1 - a = sigmoid(k),  b = z g(x),  h_0 = g(x0),
+// g(x) = x + 0.5 (x >= 0), sigmoid(x) (x < 0).  The forward forms log2 a,
+// log2 b, log2 h_0 in registers and scans them as LogAlg does; the backward
+// returns dk, dx, dx0, so no log a / log b tensor or its gradient ever exists.
+struct GateAlg : LogAlg {
+    __device__ static float rcp(float u) { return __builtin_amdgcn_rcpf(u); }
+
+    // log2 a = log2 sigmoid(-k), log2 b = log2 sigmoid(k) + log2 g(x): one exp2
+    // and one log2 for the gate (log2 sigmoid(k) - log2 sigmoid(-k) = k log2 e),
+    // one of each for g
+    __device__ static void input(float k, float x, bool valid, float &la, float &lb)
+    {
+        const float kl = k * kLog2e;
+        const float tail = lg2(1.0f + ex2(-__builtin_fabsf(kl)));   // log2(1 + e^-|k|)
+        const float l2a = __builtin_fminf(-kl, 0.0f) - tail;
+        const float xl = x * kLog2e;
+        const bool pos = x >= 0.0f;
+        const float L = lg2(pos ? x + 0.5f : 1.0f + ex2(xl));          // x < 0: log2(1 + e^x)
+        const float l2g = pos ? L : xl - L;                              // log2 sigmoid(x) = x log2 e - L
+        la = valid ? l2a : 0.0f;
+        lb = valid ? l2a + kl + l2g : -kInf;
+    }
+    __device__ static float log2_g(float x)
+    {
+        const float xl = x * kLog2e;
+        const bool pos = x >= 0.0f;
+        const float L = lg2(pos ? x + 0.5f : 1.0f + ex2(xl));
+        return pos ? L : xl - L;
+    }
+    __device__ static float carry0(float x0, bool valid) { return valid ? log2_g(x0) : -kInf; }
+
+    // sigmoid(-k), sigmoid(k) without cancellation
+    __device__ static void gate(float k, float &a, float &z)
+    {
+        const float e = ex2(-__builtin_fabsf(k) * kLog2e);   // e^-|k|
+        const float r = rcp(1.0f + e);
+        a = k >= 0.0f ? e * r : r;
+        z = k >= 0.0f ? r : e * r;
+    }
+    // g(x) and g'(x)
+    __device__ static void gpos(float x, float &gv, float &gd)
+    {
+        const float e = ex2(x * kLog2e);                      // x < 0: e^x < 1
+        const float r = rcp(1.0f + e);
+        const bool pos = x >= 0.0f;
+        gv = pos ? x + 0.5f : e * r;                          // sigmoid(x)
+        gd = pos ? 1.0f : e * r * r;                          // sigmoid(x) sigmoid(-x)
+    }
+    __device__ static void lin_ab(float k, float x, float &a, float &b)
+    {
+        float z, gv, gd;
+        gate(k, a, z);
+        gpos(x, gv, gd);
+        b = z * gv;
+    }
+    __device__ static float lin_h0(float x0)
+    {
+        float gv, gd;
+        gpos(x0, gv, gd);
+        return gv;
+    }
+    // dk = g a z (g(x) - h_{t-1}),  dx = g z g'(x),  dx0 = (a_1 g_1) g'(x0)
+    __device__ static void grads(float k, float x, float a, float, float gr, float hprev, float &d1, float &d2)
+    {
+        float a2, z, gv, gd;
+        gate(k, a2, z);
+        gpos(x, gv, gd);
+        d1 = gr * a * z * (gv - hprev);
+        d2 = gr * z * gd;
+    }
+    __device__ static float grad_h0(float w, float, float x0)
+    {
+        float gv, gd;
+        gpos(x0, gv, gd);
+        return w * gd;
+    }
 };
 
 // Argument names follow the log-space op; the linear op passes a, b, h0 in the
@@ -328,13 +422,13 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
     const int64_t base = bb * a.T * a.d + (cc - bb * a.d);
     const int t0 = j * TT + q * C;
 
-    float av[C], bv[C], gv[C];
+    float r1[C], r2[C], av[C], bv[C], gv[C];   // raw inputs, linear a and b, upstream dh
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int t = t0 + i;
         const int64_t off = base + static_cast<int64_t>(t < a.T ? t : a.T - 1) * a.d;
-        av[i] = a.la[off];
-        bv[i] = a.lb[off];
+        r1[i] = a.la[off];
+        r2[i] = a.lb[off];
         gv[i] = a.dh[off];
     }
     const float lh0v = a.lh0[cc];
@@ -343,8 +437,9 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const bool v = cv && t0 + i < a.T;
-        av[i] = v ? Alg::lin_a(av[i]) : 1.0f;
-        bv[i] = v ? Alg::lin_b(bv[i]) : 0.0f;
+        Alg::lin_ab(r1[i], r2[i], av[i], bv[i]);
+        av[i] = v ? av[i] : 1.0f;
+        bv[i] = v ? bv[i] : 0.0f;
         gv[i] = v ? gv[i] : 0.0f;
     }
 
@@ -460,11 +555,13 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
         const int t = t0 + i;
         if (cv && t < a.T) {
             const int64_t off = base + static_cast<int64_t>(t) * a.d;
-            a.dla[off] = Alg::grad_a(g, ag, hprev);
-            a.dlb[off] = Alg::grad_b(g, bv[i]);
+            float d1, d2;
+            Alg::grads(r1[i], r2[i], av[i], bv[i], g, hprev, d1, d2);
+            a.dla[off] = d1;
+            a.dlb[off] = d2;
         }
     }
-    if (cv && j == 0 && q == 0) a.dlh0[chain] = Alg::grad_h0(wc, hin);   // from a_1 g_1
+    if (cv && j == 0 && q == 0) a.dlh0[chain] = Alg::grad_h0(wc, hin, lh0v);   // from a_1 g_1
 }
 
 // ------------------------------------------------------------ host side
@@ -603,6 +700,21 @@ hipError_t launch_log_bwd(const LogGeom &g, const float *la, const float *lb, co
 {
     const LogBwdArgs a = bwd_args(g, la, lb, lh0, dh, dla, dlb, dlh0, ws);
     MGS_ELEM_DISPATCH(launch_bwd_c, LogAlg, g, a, s);
+}
+
+hipError_t launch_mingru_fwd(const LogGeom &g, const float *k, const float *x, const float *x0,
+                             float *h, void *ws, hipStream_t s)
+{
+    const LogFwdArgs a = fwd_args(g, k, x, x0, h, ws);
+    MGS_ELEM_DISPATCH(launch_fwd_c, GateAlg, g, a, s);
+}
+
+hipError_t launch_mingru_bwd(const LogGeom &g, const float *k, const float *x, const float *x0,
+                             const float *dh, float *dk, float *dx, float *dx0, void *ws,
+                             hipStream_t s)
+{
+    const LogBwdArgs a = bwd_args(g, k, x, x0, dh, dk, dx, dx0, ws);
+    MGS_ELEM_DISPATCH(launch_bwd_c, GateAlg, g, a, s);
 }
 
 hipError_t launch_linear_fwd(const LogGeom &g, const float *a_, const float *b, const float *h0,

@@ -12,8 +12,8 @@ namespace mgs {
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// ------------------------------------------- elementwise scans (log, linear)
-// One geometry and workspace layout serves both arithmetics.
+// ----------------------------- elementwise scans (log, minGRU cell + log, linear)
+// One geometry and workspace layout serves every arithmetic.
 struct LogGeom {
     int64_t S;      // chains = B*d
     int T, d;
@@ -35,6 +35,11 @@ hipError_t launch_log_fwd(const LogGeom &g, const float *la, const float *lb, co
 hipError_t launch_log_bwd(const LogGeom &g, const float *la, const float *lb, const float *lh0,
                           const float *dh, float *dla, float *dlb, float *dlh0, void *ws,
                           hipStream_t s);
+hipError_t launch_mingru_fwd(const LogGeom &g, const float *k, const float *x, const float *x0,
+                             float *h, void *ws, hipStream_t s);
+hipError_t launch_mingru_bwd(const LogGeom &g, const float *k, const float *x, const float *x0,
+                             const float *dh, float *dk, float *dx, float *dx0, void *ws,
+                             hipStream_t s);
 hipError_t launch_linear_fwd(const LogGeom &g, const float *a, const float *b, const float *h0,
                              float *h, void *ws, hipStream_t s);
 hipError_t launch_linear_bwd(const LogGeom &g, const float *a, const float *b, const float *h0,

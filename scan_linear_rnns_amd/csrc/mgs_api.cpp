@@ -112,7 +112,7 @@ mgs_status mgs_workspace_check(void *workspace, void *stream, int *flags)
     return MGS_OK;
 }
 
-// ----------------------------------------- elementwise scans (log, linear)
+// --------------------------- elementwise scans (log, minGRU cell + log, linear)
 
 using ElemFwd = hipError_t (*)(const mgs::LogGeom &, const float *, const float *, const float *,
                                float *, void *, hipStream_t);
@@ -195,6 +195,27 @@ mgs_status mgs_scan_log_bwd(const float *log_a, const float *log_b, const float 
 {
     return elem_bwd(mgs::launch_log_fwd, mgs::launch_log_bwd, log_a, log_b, log_h0, dh, dlog_a, dlog_b,
                     dlog_h0, B, T, d, workspace, workspace_bytes, fwd_state_valid, stream);
+}
+
+mgs_status mgs_scan_mingru_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes)
+{
+    return elem_workspace_size(B, T, d, bytes);
+}
+
+mgs_status mgs_scan_mingru_fwd(const float *k, const float *x, const float *x0, float *h,
+                               int64_t B, int64_t T, int64_t d, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    return elem_fwd(mgs::launch_mingru_fwd, k, x, x0, h, B, T, d, workspace, workspace_bytes, stream);
+}
+
+mgs_status mgs_scan_mingru_bwd(const float *k, const float *x, const float *x0, const float *dh,
+                               float *dk, float *dx, float *dx0, int64_t B, int64_t T, int64_t d,
+                               void *workspace, size_t workspace_bytes, int fwd_state_valid,
+                               void *stream)
+{
+    return elem_bwd(mgs::launch_mingru_fwd, mgs::launch_mingru_bwd, k, x, x0, dh, dk, dx, dx0, B, T, d,
+                    workspace, workspace_bytes, fwd_state_valid, stream);
 }
 
 mgs_status mgs_scan_linear_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes)

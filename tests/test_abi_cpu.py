@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.declared_functions()
-    assert len(declared) == 16, declared
+    assert len(declared) == 19, declared
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -73,7 +73,7 @@ def test_workspace_queries(lib):
         assert _size(lib, fn, 1 << 16, 1 << 10, 64, 8)[0] == UNSUPPORTED
 
 
-@pytest.mark.parametrize("op", ["log", "linear"])
+@pytest.mark.parametrize("op", ["log", "linear", "mingru"])
 def test_elementwise_fwd_validation(lib, op):
     B, T, d = 2, 8, 16
     ws = fake(9)
@@ -93,7 +93,7 @@ def test_elementwise_fwd_validation(lib, op):
     assert args(T=0, la=None, lb=None, h=None) == OK
 
 
-@pytest.mark.parametrize("op", ["log", "linear"])
+@pytest.mark.parametrize("op", ["log", "linear", "mingru"])
 def test_elementwise_bwd_validation(lib, op):
     B, T, d = 2, 8, 16
     fn = getattr(lib, f"mgs_scan_{op}_bwd")

@@ -12,7 +12,7 @@ import ctypes
 import numpy as np
 import pytest
 
-from synthetic import block_inputs, linear_inputs, log_inputs
+from synthetic import block_inputs, linear_inputs, log_inputs, mingru_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -110,4 +110,24 @@ def test_linear_scan_graph_replays(gpu):
     for got in _replays(step, outs):
         for x, y in zip(got, ref):
             assert torch.equal(x, y)
+    assert mgs.mgs_workspace_check(ws) == 0
+
+
+def test_mingru_scan_graph_replays(gpu):
+    import torch
+    import scan_linear_rnns_amd as mgs
+    print("[graph] minGRU cell + scan B=16 T=1024 d=64", flush=True)
+    inp = mingru_inputs(16, 1024, 64, 24)
+    k, x, x0, dh = (_t(v, gpu) for v in (inp.k, inp.x, inp.x0, inp.dh))
+    h, ws = mgs.mgs_scan_mingru_fwd(k, x, x0)
+    ref = [h.clone(), *[v.clone() for v in mgs.mgs_scan_mingru_bwd(k, x, x0, dh, ws=ws, fwd_state_valid=True)]]
+    outs = [torch.empty_like(k), torch.empty_like(k), torch.empty_like(k), torch.empty_like(x0)]
+
+    def step():
+        mgs.mgs_scan_mingru_fwd(k, x, x0, h=outs[0], ws=ws)
+        mgs.mgs_scan_mingru_bwd(k, x, x0, dh, ws=ws, fwd_state_valid=True, out=tuple(outs[1:]))
+
+    for got in _replays(step, outs):
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b)
     assert mgs.mgs_workspace_check(ws) == 0
