@@ -259,7 +259,7 @@ def kernel_source_hash(names=None):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_key, profile="log_scan_lab_hbm_traffic.txt", sources=LOG_SOURCES):
+def traffic_from_profiles(kernel_key, profile="elem_scans_lab_hbm_traffic.txt", sources=LOG_SOURCES):
     """HBM bytes per launch from a committed PMC summary, if it was taken on the current sources."""
     path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
