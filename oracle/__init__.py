@@ -18,6 +18,10 @@ What each function follows is stated in ``oracle.c``:
   * ``mingru_fwd`` / ``mingru_bwd`` -- the minGRU cell ahead of the scan
     (a = sigmoid(-k), b = (1 - a) g(x), h_0 = g(x0); home page, introduction)
     followed by the same recurrence; gradients for k, x, x0.
+  * ``givens_fwd`` / ``givens_bwd`` -- the block-affine scan with
+    A_t = sigmoid(s_t) R(theta_t) formed from angles and gate (GivensMinGRU on
+    the home page; the fused backward of the how-to's Step 3); gradients for
+    theta, s, b, h0.
   * ``block_affine_fwd`` / ``block_affine_bwd`` -- h_t = A_t h_{t-1} + b_t
     with block-diagonal k x k transitions (matrix_affine_scan in the
     "Run the benchmarks" how-to, Step 2; RotationMinGRU / GivensMinGRU on the
@@ -73,6 +77,8 @@ def _load():
                 "oracle_linear_bwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I],
                 "oracle_mingru_fwd": [_D, _D, _D, _D, _I, _I, _I],
                 "oracle_mingru_bwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I],
+                "oracle_givens_fwd": [_D, _D, _D, _D, _D, _I, _I, _I, _I],
+                "oracle_givens_bwd": [_D, _D, _D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I],
                 "oracle_block_affine_fwd": [_D, _D, _D, _D, _I, _I, _I, _I],
                 "oracle_block_affine_bwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I],
                 "oracle_block_matrix_fwd": [_D, _D, _I, _I, _I, _I],
@@ -212,3 +218,53 @@ def block_matrix_bwd(A, dP, k):
     dA = np.empty_like(A64)
     _load().oracle_block_matrix_bwd(_p(A64), _p(g), _p(dA), B, T, d, k)
     return dA
+
+
+def _givens_shapes(theta, s, d, k):
+    B, T, nb, na = theta.shape
+    assert nb * k == d and na == k * (k - 1) // 2 and s.shape == (B, T, nb)
+    return B, T
+
+
+def givens_fwd(theta, s, b, h0, k):
+    """h (B,T,d) of h_t = sigmoid(s_t) R(theta_t) h_{t-1} + b_t (per block); h0 may be None."""
+    theta, s, b = _f64(theta), _f64(s), _f64(b)
+    h0 = None if h0 is None else _f64(h0)
+    d = b.shape[2]
+    B, T = _givens_shapes(theta, s, d, k)
+    h = np.empty((B, T, d), np.float64)
+    _load().oracle_givens_fwd(_p(theta), _p(s), _p(b), _p(h0), _p(h), B, T, d, k)
+    return h
+
+
+def givens_bwd(theta, s, b, h0, dh, k):
+    """(dtheta, ds, db, dh0) for L = sum(dh * h)."""
+    theta, s, b, g = _f64(theta), _f64(s), _f64(b), _f64(dh)
+    h0 = None if h0 is None else _f64(h0)
+    B, T, d = b.shape
+    _givens_shapes(theta, s, d, k)
+    dtheta = np.empty_like(theta)
+    ds = np.empty_like(s)
+    db = np.empty_like(b)
+    dh0 = np.empty((B, d), np.float64)
+    _load().oracle_givens_bwd(_p(theta), _p(s), _p(b), _p(h0), _p(g), _p(dtheta), _p(ds), _p(db), _p(dh0),
+                              B, T, d, k)
+    return dtheta, ds, db, dh0
+
+
+def givens_matrix(theta, s, k):
+    """A = sigmoid(s) R(theta) per block, as the Givens oracle forms it: (B,T,nb,k,k)."""
+    theta, s = _f64(theta), _f64(s)
+    B, T, nb, na = theta.shape
+    eye = np.broadcast_to(np.eye(k), (B, T, nb, k, k)).copy()
+    # P_t = A_t with h-columns: run the forward on unit vectors through the public loop
+    out = np.empty((B, T, nb, k, k))
+    for c in range(k):
+        b0 = np.zeros((B, 1, nb * k))
+        h0 = np.zeros((B, nb * k))
+        h0[:, c::k] = 1.0
+        for t in range(T):
+            col = givens_fwd(theta[:, t:t + 1], s[:, t:t + 1], b0, h0, k)[:, 0]
+            out[:, t, :, :, c] = col.reshape(B, nb, k)
+    return out
+

@@ -27,6 +27,14 @@
  *     a_t = sigmoid(-k_t), z_t = 1 - a_t, b_t = z_t g(x_t), h_0 = g(x_0), with
  *     g(x) = x + 0.5 for x >= 0 and sigmoid(x) for x < 0 (the pages do not
  *     write g out; this is the reading taken), then the same recurrence.
+ *   - The Givens angle-fused block scan (GivensMinGRU, same page; the fused
+ *     backward whose memory the how-to's Step 3 measures): A_t per block is
+ *     sigmoid(s_t) R(theta_t), R a brick-wall mesh of k layers of disjoint 2 x 2
+ *     rotations (Clements et al. / EUNN, cited on the home page): layer l acts
+ *     on pairs (i, i+1), i = l mod 2, l mod 2 + 2, ... < k - 1, R = L_{k-1}..L_0,
+ *     angles taken in (layer, pair) order, each rotation mapping (x_i, x_j) to
+ *     (cos x_i - sin x_j, sin x_i + cos x_j).  The pages name the mesh but do
+ *     not fix these conventions; this is the reading taken.
  *   - Gradients are the chain rule applied to these loops for the loss
  *     L = sum_t <dh_t, h_t> (resp. sum_t <dP_t, P_t>).
  *
@@ -34,6 +42,8 @@
  *   log scan:   la, lb, h, dh, dla, dlb : (B, T, d);  lh0, dlh0 : (B, d)
  *   linear scan: a, b, h, dh, da, db : (B, T, d);  h0, dh0 : (B, d)
  *   minGRU cell: k, x, h, dh, dk, dx : (B, T, d);  x0, dx0 : (B, d)
+ *   Givens scan: theta, dtheta : (B, T, nb, k(k-1)/2);  s, ds : (B, T, nb);
+ *                b, h, dh, db : (B, T, d);  h0, dh0 : (B, d)
  *   block ops:  A, dA, P, dP : (B, T, nb, k, k) with nb = d / k and
  *               (A h)_r = sum_c A[r][c] h[c];  b, h, dh, db : (B, T, d);
  *               h0, dh0 : (B, d);  block j owns channels [j*k, (j+1)*k).
@@ -366,4 +376,148 @@ void oracle_block_matrix_bwd(const double *A, const double *dP, double *dA,
     free(Ps);
     free(G);
     free(W);
+}
+
+/* ------------------------------------------------ Givens angle-fused scan */
+
+/* Applies the mesh's layers to the k x k matrix M from the left, in order
+ * L_0 .. L_{k-1}.  If rho >= 0, the layer holding angle rho is replaced by its
+ * derivative with respect to that angle: the rotation's block becomes
+ * d/dtheta [[c, -s], [s, c]] = [[-s, -c], [c, -s]] and every other row of the
+ * layer's matrix is zero. */
+static void mesh_apply(const double *theta, int64_t k, int64_t rho, double *M)
+{
+    int64_t idx = 0; /* angle index of the layer's first pair */
+    for (int64_t l = 0; l < k; ++l) {
+        int64_t n_pairs = 0;
+        for (int64_t i = l % 2; i + 1 < k; i += 2) ++n_pairs;
+        if (rho >= idx && rho < idx + n_pairs) {
+            int64_t i = l % 2 + 2 * (rho - idx), j = i + 1;
+            double c = cos(theta[rho]), s = sin(theta[rho]);
+            for (int64_t col = 0; col < k; ++col) {
+                double xi = M[i * k + col], xj = M[j * k + col];
+                for (int64_t r = 0; r < k; ++r) M[r * k + col] = 0.0;
+                M[i * k + col] = -s * xi - c * xj;
+                M[j * k + col] = c * xi - s * xj;
+            }
+        } else {
+            int64_t a = idx;
+            for (int64_t i = l % 2; i + 1 < k; i += 2, ++a) {
+                int64_t j = i + 1;
+                double c = cos(theta[a]), s = sin(theta[a]);
+                for (int64_t col = 0; col < k; ++col) {
+                    double xi = M[i * k + col], xj = M[j * k + col];
+                    M[i * k + col] = c * xi - s * xj;
+                    M[j * k + col] = s * xi + c * xj;
+                }
+            }
+        }
+        idx += n_pairs;
+    }
+}
+
+/* R(theta) (rho < 0) or dR/dtheta_rho into R (k x k) */
+static void mesh_matrix(const double *theta, int64_t k, int64_t rho, double *R)
+{
+    for (int64_t r = 0; r < k; ++r)
+        for (int64_t c = 0; c < k; ++c) R[r * k + c] = (r == c) ? 1.0 : 0.0;
+    mesh_apply(theta, k, rho, R);
+}
+
+static double sigmoid_d(double u) { return 1.0 / (1.0 + exp(-u)); }
+
+/* Forward: A_t = sigmoid(s_t) R(theta_t) per block; h_0 = h0 (zero if NULL);
+ * h_t = A_t h_{t-1} + b_t; writes h_1..T. */
+void oracle_givens_fwd(const double *theta, const double *sg, const double *bv, const double *h0,
+                       double *h, int64_t B, int64_t T, int64_t d, int64_t k)
+{
+    int64_t nb = d / k, na = k * (k - 1) / 2;
+    double *R = (double *)malloc(sizeof(double) * (size_t)(k * k));
+    double *cur = (double *)malloc(sizeof(double) * (size_t)k);
+    double *nxt = (double *)malloc(sizeof(double) * (size_t)k);
+    if (!R || !cur || !nxt) { free(R); free(cur); free(nxt); return; }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t j = 0; j < nb; ++j) {
+            for (int64_t r = 0; r < k; ++r) cur[r] = h0 ? h0[b * d + j * k + r] : 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                int64_t blkid = (b * T + t) * nb + j;
+                mesh_matrix(theta + blkid * na, k, -1, R);
+                double sig = sigmoid_d(sg[blkid]);
+                for (int64_t r = 0; r < k; ++r) {
+                    double acc = bv[(b * T + t) * d + j * k + r];
+                    for (int64_t c = 0; c < k; ++c) acc += sig * R[r * k + c] * cur[c];
+                    nxt[r] = acc;
+                }
+                for (int64_t r = 0; r < k; ++r) {
+                    cur[r] = nxt[r];
+                    h[(b * T + t) * d + j * k + r] = cur[r];
+                }
+            }
+        }
+    free(R);
+    free(cur);
+    free(nxt);
+}
+
+/* Backward of oracle_givens_fwd for L = sum_t <dh_t, h_t>: the block-affine
+ * reverse scan g_t = dh_t + A_{t+1}^T g_{t+1} gives dA_t = g_t h_{t-1}^T,
+ * db_t = g_t, dh0 = A_1^T g_1; then, through A = sigmoid(s) R(theta),
+ *   ds_t = sigmoid'(s_t) <dA_t, R>,   dtheta_rho = sigmoid(s_t) <dA_t, dR/dtheta_rho>,
+ * with dR/dtheta_rho formed explicitly for every angle. */
+void oracle_givens_bwd(const double *theta, const double *sg, const double *bv, const double *h0,
+                       const double *dh, double *dtheta, double *dsg, double *db, double *dh0,
+                       int64_t B, int64_t T, int64_t d, int64_t k)
+{
+    int64_t nb = d / k, na = k * (k - 1) / 2;
+    double *hs = (double *)malloc(sizeof(double) * (size_t)((T + 1) * k));
+    double *R = (double *)malloc(sizeof(double) * (size_t)(k * k));
+    double *dR = (double *)malloc(sizeof(double) * (size_t)(k * k));
+    double *g = (double *)malloc(sizeof(double) * (size_t)k);
+    double *w = (double *)malloc(sizeof(double) * (size_t)k);
+    if (!hs || !R || !dR || !g || !w) { free(hs); free(R); free(dR); free(g); free(w); return; }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t j = 0; j < nb; ++j) {
+            for (int64_t r = 0; r < k; ++r) hs[r] = h0 ? h0[b * d + j * k + r] : 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                int64_t blkid = (b * T + t) * nb + j;
+                mesh_matrix(theta + blkid * na, k, -1, R);
+                double sig = sigmoid_d(sg[blkid]);
+                for (int64_t r = 0; r < k; ++r) {
+                    double acc = bv[(b * T + t) * d + j * k + r];
+                    for (int64_t c = 0; c < k; ++c) acc += sig * R[r * k + c] * hs[t * k + c];
+                    hs[(t + 1) * k + r] = acc;
+                }
+            }
+            for (int64_t r = 0; r < k; ++r) w[r] = 0.0;
+            for (int64_t t = T - 1; t >= 0; --t) {
+                int64_t blkid = (b * T + t) * nb + j;
+                for (int64_t r = 0; r < k; ++r) g[r] = dh[(b * T + t) * d + j * k + r] + w[r];
+                mesh_matrix(theta + blkid * na, k, -1, R);
+                double sig = sigmoid_d(sg[blkid]);
+                /* <dA, R> with dA = g h_{t-1}^T */
+                double acc = 0.0;
+                for (int64_t r = 0; r < k; ++r)
+                    for (int64_t c = 0; c < k; ++c) acc += g[r] * hs[t * k + c] * R[r * k + c];
+                dsg[blkid] = sig * (1.0 - sig) * acc;
+                for (int64_t rho = 0; rho < na; ++rho) {
+                    mesh_matrix(theta + blkid * na, k, rho, dR);
+                    double a2 = 0.0;
+                    for (int64_t r = 0; r < k; ++r)
+                        for (int64_t c = 0; c < k; ++c) a2 += g[r] * hs[t * k + c] * dR[r * k + c];
+                    dtheta[blkid * na + rho] = sig * a2;
+                }
+                for (int64_t r = 0; r < k; ++r) db[(b * T + t) * d + j * k + r] = g[r];
+                for (int64_t c = 0; c < k; ++c) {
+                    double acc2 = 0.0;
+                    for (int64_t r = 0; r < k; ++r) acc2 += sig * R[r * k + c] * g[r];
+                    w[c] = acc2;
+                }
+            }
+            for (int64_t r = 0; r < k; ++r) dh0[b * d + j * k + r] = w[r];
+        }
+    free(hs);
+    free(R);
+    free(dR);
+    free(g);
+    free(w);
 }

@@ -150,16 +150,20 @@ class BlockInputs:
     dh: np.ndarray                   # (B,T,d) float32
     dP: Optional[np.ndarray]         # (B,T,nb,k,k) float32 (cumulative product only)
     k: int
+    theta: Optional[np.ndarray] = None  # (B,T,nb,k(k-1)/2) float32 angles (Givens angle-fused scan)
+    s: Optional[np.ndarray] = None      # (B,T,nb) float32 gate pre-activations (Givens angle-fused scan)
 
 
 def block_inputs(B: int, T: int, d: int, k: int = 8, seed: int = 0, *,
                  gate: bool = True, with_dP: bool = True,
-                 h0: str = "zero") -> BlockInputs:
+                 h0: str = "zero", return_angles: bool = False) -> BlockInputs:
     """Gated Givens-mesh generator for the block scans (see module docstring).
 
     gate=False drops the sigmoid gate (pure rotations, used for the long-T
     orthogonality checks).  h0="zero" gives h0 = None (zeros, as in the
     Givens lab configuration); h0="normal" draws h0 ~ N(0,1) after dP.
+    return_angles=True also returns theta and s rounded to float32 (the inputs
+    of the Givens angle-fused scan, which forms A from them itself).
     """
     assert d % k == 0
     nb = d // k
@@ -177,7 +181,8 @@ def block_inputs(B: int, T: int, d: int, k: int = 8, seed: int = 0, *,
         A = R
     f = np.float32
     return BlockInputs(A.astype(f), b.astype(f), None if h0v is None else h0v.astype(f),
-                       dh.astype(f), None if dP is None else dP.astype(f), k)
+                       dh.astype(f), None if dP is None else dP.astype(f), k,
+                       theta.astype(f) if return_angles else None, s.astype(f) if return_angles else None)
 
 
 # The five workloads, by name (shapes from the pages' lab and long-T

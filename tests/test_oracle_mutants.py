@@ -16,6 +16,7 @@ import oracle
 from tests import test_oracle_pins as pins
 from tests import test_oracle_pins_linear as lpins
 from tests import test_oracle_pins_mingru as mpins
+from tests import test_oracle_pins_givens as gpins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -41,6 +42,11 @@ MUTANTS = [
     ("mingru_bwd dx uses a not 1 - a", "dx[i] = g * (1.0 - a) * gpos_d(x[i]);", "dx[i] = g * a * gpos_d(x[i]);"),
     ("mingru_bwd dx0 drops g'", "dx0[b * d + c] = (T > 0) ? g * a_next * gpos_d(x0[b * d + c]) : 0.0;",
      "dx0[b * d + c] = (T > 0) ? g * a_next : 0.0;"),
+    ("givens mesh rotation sign", "M[i * k + col] = c * xi - s * xj;\n                    M[j * k + col] = s * xi + c * xj;",
+     "M[i * k + col] = c * xi + s * xj;\n                    M[j * k + col] = -s * xi + c * xj;"),
+    ("givens mesh derivative sign", "M[i * k + col] = -s * xi - c * xj;", "M[i * k + col] = -s * xi + c * xj;"),
+    ("givens ds drops sigmoid'", "dsg[blkid] = sig * (1.0 - sig) * acc;", "dsg[blkid] = sig * acc;"),
+    ("givens dtheta drops the gate", "dtheta[blkid * na + rho] = sig * a2;", "dtheta[blkid * na + rho] = a2;"),
     ("affine_fwd transposed A", "for (int64_t c = 0; c < k; ++c) s += At[r * k + c] * cur[c];",
      "for (int64_t c = 0; c < k; ++c) s += At[c * k + r] * cur[c];"),
     ("affine_bwd A not A^T", "for (int64_t r = 0; r < k; ++r) s += At[r * k + c] * g[r];",
@@ -72,6 +78,9 @@ PINS = [
     lpins.test_gradients_finite_difference,
     mpins.test_golden_mingru_cell,
     mpins.test_gradients_finite_difference,
+    gpins.test_golden_k2,
+    gpins.test_matrices_match_numpy_mesh,
+    gpins.test_gradients_finite_difference,
 ]
 
 
@@ -93,7 +102,7 @@ def test_mutant_is_caught(name, orig, mut, monkeypatch):
     with tempfile.TemporaryDirectory() as tmp:
         lib = ctypes.CDLL(_build(text.replace(orig, mut), tmp))
         for fname in ("oracle_log_fwd", "oracle_log_bwd", "oracle_linear_fwd", "oracle_linear_bwd",
-                      "oracle_mingru_fwd", "oracle_mingru_bwd",
+                      "oracle_mingru_fwd", "oracle_mingru_bwd", "oracle_givens_fwd", "oracle_givens_bwd",
                       "oracle_block_affine_fwd",
                       "oracle_block_affine_bwd", "oracle_block_matrix_fwd", "oracle_block_matrix_bwd"):
             fn, ref = getattr(lib, fname), getattr(real, fname)
