@@ -59,6 +59,10 @@ def compulsory_bytes(op, B, T, d, k=8):
         return 4 * N * (k + 2), 4 * N * (2 * k + 3) + 4 * S
     if op == "matrix":
         return 8 * N * k, 12 * N * k
+    if op == "givens":  # angles (k(k-1)/2 per block) and gate instead of A; h0 = NULL
+        na = k * (k - 1) // 2
+        th, sg = 4 * N * na // k, 4 * N // k
+        return th + sg + 8 * N, 2 * (th + sg) + 12 * N + 4 * S
     raise ValueError(op)
 
 
@@ -86,6 +90,10 @@ class OpRun:
             inp = mingru_inputs(B, T, d, 0)
             base = [t(inp.k), t(inp.x), t(inp.x0), t(inp.dh)]
             ws_bytes = mgs.mgs_scan_mingru_workspace_size(B, T, d)
+        elif op == "givens":
+            inp = block_inputs(B, T, d, k=8, seed=0, with_dP=False, return_angles=True)
+            base = [t(inp.theta), t(inp.s), t(inp.b), t(inp.dh)]
+            ws_bytes = mgs.mgs_givens_scan_workspace_size(B, T, d, 8)
         elif op == "linear":
             inp = linear_inputs(B, T, d, 0)
             base = [t(inp.a), t(inp.b), t(inp.h0), t(inp.dh)]
@@ -111,6 +119,15 @@ class OpRun:
                 fn_f = getattr(self.lib, f"mgs_scan_{op}_fwd")
                 fn_b = getattr(self.lib, f"mgs_scan_{op}_bwd")
                 keep = xs + [h, dla, dlb, dlh0, ws]
+            elif op == "givens":
+                th, sg, b, dh = xs
+                h = torch.empty_like(b)
+                dth, dsg, db, dh0 = (torch.empty_like(th), torch.empty_like(sg), torch.empty_like(b),
+                                     torch.empty((B, d), device=dev))
+                fa = (P(th), P(sg), P(b), None, P(h), B, T, d, 8, P(ws), ws.numel())
+                ba = (P(th), P(sg), None, P(h), P(dh), P(dth), P(dsg), P(db), P(dh0), B, T, d, 8, P(ws), ws.numel())
+                fn_f, fn_b = self.lib.mgs_givens_scan_fwd, self.lib.mgs_givens_scan_bwd
+                keep = xs + [h, dth, dsg, db, dh0, ws]
             elif op == "affine":
                 A, b, dh = xs
                 h = torch.empty_like(b)
@@ -323,6 +340,8 @@ def main():
         ("linear_longT", "linear", 16, 1024, 64),
         ("affine_lab", "affine", 128, 64, 64),
         ("affine_longT", "affine", 16, 1024, 64),
+        ("givens_lab", "givens", 128, 64, 64),
+        ("givens_longT", "givens", 16, 1024, 64),
         ("matrix_longT", "matrix", 16, 1024, 64),
     ]
     if args.no_ops:
@@ -361,6 +380,8 @@ def main():
             rec["op"] = "block cumulative product (b = 0), k = 8"
         elif op == "affine":
             rec["op"] = "block-affine scan, k = 8"
+        elif op == "givens":
+            rec["op"] = "Givens angle-fused block-affine scan (inputs theta, s), k = 8"
         elif op == "linear":
             rec["op"] = "linear-space scan, signed gates"
         elif op == "mingru":

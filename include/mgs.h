@@ -16,6 +16,8 @@
  *      (same table, op matrix_scan);
  *   1b. the same scan with the minGRU cell fused ahead of it (inputs are the
  *      pre-activations; gradients are returned for them);
+ *   2b. the same with A_t = sigmoid(s_t) R(theta_t) formed from Givens angles
+ *      and a gate inside the kernels (GivensMinGRU, home page);
  *   4. linear-space elementwise scan, a_t of either sign -- the op the pages
  *      list as linear_scan (home page speed-up table; "Run the benchmarks"
  *      how-to, Step 2), for gates with negative eigenvalues.
@@ -217,6 +219,43 @@ mgs_status mgs_block_affine_scan_bwd(const float *A, const float *b, const float
                                      float *dA, float *db, float *dh0,
                                      int64_t B, int64_t T, int64_t d, int64_t k,
                                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------ Givens angle-fused scan --- */
+/*
+ * The block-affine scan with each transition formed from angles and a gate
+ * (GivensMinGRU on the minGRU home page; its fused backward is the memory
+ * saving measured in the "Run the benchmarks" how-to, Step 3):
+ *     A_t = sigmoid(s_t) R(theta_t),   h_t = A_t h_{t-1} + b_t   per block,
+ * R a brick-wall mesh of k layers of 2 x 2 rotations: layer l rotates the
+ * pairs (i, i+1), i = l mod 2, l mod 2 + 2, ... < k - 1; R = L_{k-1} .. L_0;
+ * angles in (layer, pair) order; each rotation maps (x_i, x_j) to
+ * (cos x_i - sin x_j, sin x_i + cos x_j) (the pages name the mesh, not these
+ * conventions; this is the reading taken).  A and dA are formed only in
+ * registers, never in memory.
+ *   theta : (B,T,d/k,k(k-1)/2) in;  s : (B,T,d/k) in;  b : (B,T,d) in;
+ *   h0 : (B,d) in or NULL;  h : (B,T,d) out.   Envelope: k == 8.
+ * Same workspace rules as the block-affine scan (its own size query).
+ */
+mgs_status mgs_givens_scan_workspace_size(int64_t B, int64_t T, int64_t d, int64_t k, size_t *bytes);
+
+mgs_status mgs_givens_scan_fwd(const float *theta, const float *s, const float *b, const float *h0,
+                               float *h, int64_t B, int64_t T, int64_t d, int64_t k,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of mgs_givens_scan_fwd for L = sum_t <dh_t, h_t>: the block-affine
+ * reverse scan g_t = dh_t + A_{t+1}^T g_{t+1} with dA_t = g_t h_{t-1}^T
+ * contracted in registers:
+ *     dtheta_t = sigmoid(s_t) <dA_t, dR/dtheta>,   ds_t = sigmoid'(s_t) <dA_t, R>,
+ *     db_t = g_t,   dh0 = A_1^T g_1.
+ *   h : (B,T,d) in, the forward's output;  h0 as in the forward;  dh : (B,T,d) in;
+ *   dtheta : shape of theta, out;  ds : shape of s, out;  db : (B,T,d) out;
+ *   dh0 : (B,d) out (written even when h0 == NULL).
+ */
+mgs_status mgs_givens_scan_bwd(const float *theta, const float *s, const float *h0, const float *h,
+                               const float *dh, float *dtheta, float *ds, float *db, float *dh0,
+                               int64_t B, int64_t T, int64_t d, int64_t k,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------ block cumulative product --- */
 /*

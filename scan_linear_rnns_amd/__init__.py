@@ -11,6 +11,7 @@ Ops (see include/mgs.h for the definitions and their sources on the pages):
   * mgs_scan_mingru_fwd / mgs_scan_mingru_bwd           minGRU cell fused ahead of the log-space scan
   * mgs_scan_linear_fwd / mgs_scan_linear_bwd           linear-space scan, signed gates
   * mgs_block_affine_scan_fwd / mgs_block_affine_scan_bwd   h_t = A_t h_{t-1} + b_t
+  * mgs_givens_scan_fwd / mgs_givens_scan_bwd           same, A_t = sigmoid(s_t) R(theta_t) formed in-kernel
   * mgs_block_matrix_scan_fwd / mgs_block_matrix_scan_bwd   P_t = A_t P_{t-1}
 """
 from __future__ import annotations
@@ -26,6 +27,7 @@ __all__ = [
     "mgs_scan_mingru_workspace_size", "mgs_scan_mingru_fwd", "mgs_scan_mingru_bwd",
     "mgs_scan_linear_workspace_size", "mgs_scan_linear_fwd", "mgs_scan_linear_bwd",
     "mgs_block_affine_scan_workspace_size", "mgs_block_affine_scan_fwd", "mgs_block_affine_scan_bwd",
+    "mgs_givens_scan_workspace_size", "mgs_givens_scan_fwd", "mgs_givens_scan_bwd",
     "mgs_block_matrix_scan_workspace_size", "mgs_block_matrix_scan_fwd", "mgs_block_matrix_scan_bwd",
 ]
 
@@ -285,6 +287,62 @@ def mgs_block_affine_scan_bwd(A, b, h0, h, dh, k=8, ws=None, out=None, stream=No
                                            _ptr(dh0), B, T, d, k, _ptr(ws), ws.numel(), _stream(stream)),
           "mgs_block_affine_scan_bwd")
     return dA, db, dh0
+
+
+# ---------------------------------------------- Givens angle-fused scan
+
+def mgs_givens_scan_workspace_size(B, T, d, k):
+    return _size("mgs_givens_scan_workspace_size", B, T, d, k)
+
+
+def _givens_dims(theta, k):
+    B, T, nb, na = theta.shape
+    if na != k * (k - 1) // 2:
+        raise ValueError(f"theta must have trailing dim {k * (k - 1) // 2}, got {tuple(theta.shape)}")
+    return B, T, nb * k
+
+
+def mgs_givens_scan_fwd(theta, s, b, h0, k=8, h=None, ws=None, stream=None):
+    """h (B,T,d) of h_t = sigmoid(s_t) R(theta_t) h_{t-1} + b_t; h0 may be None; returns (h, ws)."""
+    import torch
+    B, T, d = _givens_dims(theta, k)
+    dev = theta.device
+    _check_tensor("theta", theta, tuple(theta.shape))
+    _check_tensor("s", s, (B, T, d // k), dev)
+    _check_tensor("b", b, (B, T, d), dev)
+    if h0 is not None:
+        _check_tensor("h0", h0, (B, d), dev)
+    if h is None:
+        h = torch.empty((B, T, d), dtype=torch.float32, device=dev)
+    _check_tensor("h", h, (B, T, d), dev)
+    if ws is None:
+        ws = workspace(mgs_givens_scan_workspace_size(B, T, d, k), dev)
+    check(load().mgs_givens_scan_fwd(_ptr(theta), _ptr(s), _ptr(b), _ptr(h0), _ptr(h), B, T, d, k, _ptr(ws),
+                                     ws.numel(), _stream(stream)), "mgs_givens_scan_fwd")
+    return h, ws
+
+
+def mgs_givens_scan_bwd(theta, s, h0, h, dh, k=8, ws=None, out=None, stream=None):
+    """(dtheta, ds, db, dh0) for L = sum(dh * h); h is the forward's output."""
+    import torch
+    B, T, d = _givens_dims(theta, k)
+    dev = theta.device
+    _check_tensor("theta", theta, tuple(theta.shape))
+    _check_tensor("s", s, (B, T, d // k), dev)
+    if h0 is not None:
+        _check_tensor("h0", h0, (B, d), dev)
+    _check_tensor("h", h, (B, T, d), dev)
+    _check_tensor("dh", dh, (B, T, d), dev)
+    if out is None:
+        out = (torch.empty_like(theta), torch.empty_like(s), torch.empty((B, T, d), dtype=torch.float32, device=dev),
+               torch.empty((B, d), dtype=torch.float32, device=dev))
+    dth, ds, db, dh0 = out
+    if ws is None:
+        ws = workspace(mgs_givens_scan_workspace_size(B, T, d, k), dev)
+    check(load().mgs_givens_scan_bwd(_ptr(theta), _ptr(s), _ptr(h0), _ptr(h), _ptr(dh), _ptr(dth), _ptr(ds),
+                                     _ptr(db), _ptr(dh0), B, T, d, k, _ptr(ws), ws.numel(), _stream(stream)),
+          "mgs_givens_scan_bwd")
+    return dth, ds, db, dh0
 
 
 # ------------------------------------------------- block cumulative product

@@ -349,12 +349,17 @@ struct BlkArgs {
     WsHeader *hd;
     uint64_t *agg, *incl;
     float *pstate;       // cumulative product: state entering each chunk, [tile][chunk][slot][8]
+    const float *theta;  // Givens angle-fused: angles (B,T,nb,28)
+    const float *sg;     // Givens angle-fused: gate pre-activations (B,T,nb)
+    float *dtheta;       // Givens angle-fused backward: d angles
+    float *dsg;          // Givens angle-fused backward: d gate
 };
 
 struct Tile {
     int lane, wv, v, cgl, sub, slot, q, j, cg, t0;
     bool cv;
     int64_t bb, jb;
+    int64_t blk0;    // block index (bb, t=0, jb) in (B,T,nb)
     int64_t ablk0;   // element offset of A block (bb, t=0, jb)
     int64_t astep;   // elements between consecutive t of the same block
     int64_t vec0;    // element offset of (bb, t=0, jb*8 + v) in (B,T,d)
@@ -381,7 +386,8 @@ __device__ __forceinline__ Tile make_tile(const BlkArgs &a, int tile, bool rever
     t.bb = cc / a.nb;
     t.jb = cc - t.bb * a.nb;
     t.astep = static_cast<int64_t>(a.nb) * 64;
-    t.ablk0 = (t.bb * a.T * a.nb + t.jb) * 64;
+    t.blk0 = t.bb * a.T * a.nb + t.jb;
+    t.ablk0 = t.blk0 * 64;
     t.vstep = a.d;
     t.vec0 = t.bb * a.T * a.d + t.jb * 8 + t.v;
     t.t0 = t.j * (2 * W * C) + t.q * C;
@@ -473,53 +479,149 @@ __device__ __forceinline__ void ks_scan(float (*buf)[NCH][32][AggShape<KIND>::st
     ks_store<KIND, NCH>(buf[ks_final<NCH>()], q, slot, X);
 }
 
-// ======================================================= block-affine fwd
+// ===================================================== Givens mesh in lanes
+// The angle-fused kernels form A_t = sigmoid(s_t) R(theta_t) in registers.  R is
+// the brick-wall mesh of 8 layers of 2 x 2 rotations (GivensMinGRU on the
+// minGRU home page; the Clements / EUNN mesh it cites): layer l rotates the
+// pairs (i, i+1), i = l mod 2, l mod 2 + 2, ..., R = L_7 .. L_0, angles in
+// (layer, pair) order, each rotation mapping (x_i, x_j) to
+// (c x_i - s x_j, s x_i + c x_j).  Lane p of a chain's 8 lanes loads angles
+// 4p..4p+3 (lane 7 none), and the chain shares their cosines and sines through
+// LDS, so every angle is loaded once and turned into sin / cos once.
 
+constexpr int kAngles = 28;
+
+__host__ __device__ constexpr int mesh_first(int l) { return (l / 2) * 7 + (l & 1) * 4; }
+
+// cosines and sines of a chain's 28 angles in every lane of the chain
+__device__ __forceinline__ void mesh_share(float4 th, float (*cs)[8], int lane, float (&cc)[kAngles],
+                                           float (&ss)[kAngles])
+{
+    // correctly rounded to within an ulp (the hardware's native sin / cos lose
+    // ~1e-6 absolute, which the 28 rotations and the scan then carry)
+    float4 c4, s4;
+    sincosf(th.x, &s4.x, &c4.x);
+    sincosf(th.y, &s4.y, &c4.y);
+    sincosf(th.z, &s4.z, &c4.z);
+    sincosf(th.w, &s4.w, &c4.w);
+    *reinterpret_cast<float4 *>(&cs[lane][0]) = c4;
+    *reinterpret_cast<float4 *>(&cs[lane][4]) = s4;
+    const int base = lane & ~7;
+#pragma unroll
+    for (int p = 0; p < 7; ++p) {
+        const float4 c = *reinterpret_cast<const float4 *>(&cs[base + p][0]);
+        const float4 s = *reinterpret_cast<const float4 *>(&cs[base + p][4]);
+        cc[4 * p] = c.x; cc[4 * p + 1] = c.y; cc[4 * p + 2] = c.z; cc[4 * p + 3] = c.w;
+        ss[4 * p] = s.x; ss[4 * p + 1] = s.y; ss[4 * p + 2] = s.z; ss[4 * p + 3] = s.w;
+    }
+}
+
+// row v of R in natural column order: e_v^T L_7 .. L_0
+__device__ __forceinline__ void mesh_row(const float (&cc)[kAngles], const float (&ss)[kAngles], int v, float (&r)[8])
+{
+#pragma unroll
+    for (int c = 0; c < 8; ++c) r[c] = (c == v) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int l = 7; l >= 0; --l)
+#pragma unroll
+        for (int i = l & 1, a = mesh_first(l); i + 1 < 8; i += 2, ++a) {
+            const float ri = r[i], rj = r[i + 1];
+            r[i] = cc[a] * ri + ss[a] * rj;
+            r[i + 1] = cc[a] * rj - ss[a] * ri;
+        }
+}
+
+// column v of R in natural row order: L_7 .. L_0 e_v
+__device__ __forceinline__ void mesh_col(const float (&cc)[kAngles], const float (&ss)[kAngles], int v, float (&y)[8])
+{
+#pragma unroll
+    for (int r = 0; r < 8; ++r) y[r] = (r == v) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int l = 0; l < 8; ++l)
+#pragma unroll
+        for (int i = l & 1, a = mesh_first(l); i + 1 < 8; i += 2, ++a) {
+            const float yi = y[i], yj = y[i + 1];
+            y[i] = cc[a] * yi - ss[a] * yj;
+            y[i + 1] = ss[a] * yi + cc[a] * yj;
+        }
+}
+
+// Reverse pass through mesh_col: y is the built column, dy the gradient on it;
+// writes d(column)/d(angle) contracted with dy into part.  Each layer is undone
+// by its inverse rotation, so no intermediate column is stored.
+__device__ __forceinline__ void mesh_col_adjoint(const float (&cc)[kAngles], const float (&ss)[kAngles],
+                                                 float (&y)[8], float (&dy)[8], float (&part)[kAngles])
+{
+#pragma unroll
+    for (int l = 7; l >= 0; --l)
+#pragma unroll
+        for (int i = l & 1, a = mesh_first(l); i + 1 < 8; i += 2, ++a) {
+            const float yi = y[i], yj = y[i + 1], gi = dy[i], gj = dy[i + 1];
+            part[a] = gj * yi - gi * yj;
+            y[i] = cc[a] * yi + ss[a] * yj;
+            y[i + 1] = cc[a] * yj - ss[a] * yi;
+            dy[i] = cc[a] * gi + ss[a] * gj;
+            dy[i + 1] = cc[a] * gj - ss[a] * gi;
+        }
+}
+
+// natural order <-> this lane's rotated slots (slot s holds entry s ^ (v & 4)).
+// Written as a bitwise blend of two fixed-index registers: a select between
+// x[s] and x[s ^ 4] would be folded into a lane-dependent index, which sends
+// the array to scratch memory.
+__device__ __forceinline__ float blend(float a, float b, int mask)
+{
+    return __int_as_float((__float_as_int(b) & mask) | (__float_as_int(a) & ~mask));
+}
+
+__device__ __forceinline__ void to_slots(const float (&x)[8], int v, float scale, float *y)
+{
+    const int m = -((v >> 2) & 1);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) y[s] = scale * blend(x[s], x[s ^ 4], m);
+}
+
+__device__ __forceinline__ void from_slots(const float *x, int v, float scale, float (&y)[8])
+{
+    const int m = -((v >> 2) & 1);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) y[s] = scale * blend(x[s], x[s ^ 4], m);
+}
+
+__device__ __forceinline__ float sigmoidf_(float u) { return 1.0f / (1.0f + __expf(-u)); }
+
+// Pins eight values in registers at this point of the program: work that
+// produces them cannot sink below it, so one step's 56 cosines and sines are
+// dead before the next step's are loaded (with a scheduling barrier after it).
+__device__ __forceinline__ void settle8(float *x)
+{
+    asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                 "+v"(x[7]));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// angle slice and gate of this lane's chain at step t (indices clamped in range)
+__device__ __forceinline__ float4 load_angles(const BlkArgs &a, const Tile &tl, int t)
+{
+    const int64_t blk = tl.blk0 + static_cast<int64_t>(t) * a.nb;
+    return *reinterpret_cast<const float4 *>(a.theta + blk * kAngles + 4 * min(tl.v, 6));
+}
+
+// ============================================ block-affine carry phases
+// Shared by the kernels that load A and the kernels that form it from angles.
+
+// Forward: X = (row of Phi, entry of u) is the chunk's aggregate.  Stores it,
+// scans the tile's chunks, runs the look-back (multi-tile launches) and
+// returns the state entering this lane's chunk.
 template <int C, int W, bool MULTI>
-__global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
+__device__ __forceinline__ float affine_fwd_carry(const BlkArgs &a, const Tile &tl, int ftile, unsigned long long ep,
+                                                  float (&X)[9], float xh0,
+                                                  float (&sKS)[2][2 * W][32][AggShape<kMatVec>::stride],
+                                                  float (&sCarry)[32], uint32_t (&sTicket)[2])
 {
     constexpr int NCH = 2 * W;
     using S = AggShape<kMatVec>;
     constexpr int FIN = ks_final<NCH>();
-    __shared__ float sKS[2][NCH][32][S::stride];
-    __shared__ float sCarry[32];
-    __shared__ uint32_t sTicket[2];
-
-    const int tile = blockIdx.x;
-    unsigned long long ep = 0;
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
-    const Tile tl = make_tile<C, W>(a, tile, false);
-    const int ftile = tl.j * a.nCG + tl.cg;
-
-    // unconditional (clamped) loads keep every load in flight at once
-    float Ar[C][8], bv[C];
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int t = clampT(tl.t0 + i, a.T);
-        load_row(a.A + tl.ablk0 + t * tl.astep, tl.v, Ar[i]);
-        bv[i] = a.x[tl.vec0 + t * tl.vstep];
-    }
-    const float xh0 = load_h0(a, tl);
-#pragma unroll
-    for (int i = 0; i < C; ++i)
-        if (!(tl.cv && tl.t0 + i < a.T)) {
-            eye_row(tl.v, Ar[i]);
-            bv[i] = 0.0f;
-        }
-
-    // chunk aggregate from a zero state: X = (A_e..A_s, local h_e)
-    float X[S::words];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) X[s] = Ar[0][s];
-    X[8] = bv[0];
-#pragma unroll
-    for (int i = 1; i < C; ++i) {
-        float np[8];
-        mm8(Ar[i], X, np);
-        X[8] = mv8(Ar[i], X[8], bv[i]);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) X[s] = np[s];
-    }
     ks_store<kMatVec, NCH>(sKS[0], tl.q, tl.slot, X);
     if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
     __syncthreads();
@@ -560,69 +662,20 @@ __global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
         x = xh0;
         for (int q = 0; q < tl.q; ++q) x = mv8(sKS[0][q][tl.slot], x, sKS[0][q][tl.slot][8]);
     }
-
-    // re-run the recurrence from the true state entering the chunk
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        x = mv8(Ar[i], x, bv[i]);
-        const int t = tl.t0 + i;
-        if (tl.cv && t < a.T) a.out[tl.vec0 + t * tl.vstep] = x;
-    }
+    return x;
 }
 
-// ======================================================= block-affine bwd
-// Reverse scan on w_t = A_t^T g_t with g_t = dh_t + w_{t+1}; per chunk [s, e]
-// w_s = Psi w_{e+1} + Wl with Psi = A_s^T .. A_e^T.
-
+// Backward: X = (row of Psi, entry of Wl) is the chunk's reverse aggregate.
+// Returns w entering this lane's chunk from its end.
 template <int C, int W, bool MULTI>
-__global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
+__device__ __forceinline__ float affine_bwd_carry(const BlkArgs &a, const Tile &tl, int ftile, unsigned long long ep,
+                                                  float (&X)[9],
+                                                  float (&sKS)[2][2 * W][32][AggShape<kMatVec>::stride],
+                                                  float (&sCarry)[32], uint32_t (&sTicket)[2])
 {
     constexpr int NCH = 2 * W;
     using S = AggShape<kMatVec>;
     constexpr int FIN = ks_final<NCH>();
-    __shared__ float sKS[2][NCH][32][S::stride];
-    __shared__ float sCarry[32];
-    __shared__ uint32_t sTicket[2];
-
-    const int tile = blockIdx.x;
-    unsigned long long ep = 0;
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
-    const Tile tl = make_tile<C, W>(a, tile, true);
-    const int ftile = tl.j * a.nCG + tl.cg;
-
-    float ATr[C][8], gv[C], hp[C];   // rows of A_t^T, upstream dh_t, h_{t-1}
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int t = clampT(tl.t0 + i, a.T);
-        load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
-        gv[i] = a.y[tl.vec0 + t * tl.vstep];
-        hp[i] = a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep];
-    }
-    const float xh0 = load_h0(a, tl);
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int t = tl.t0 + i;
-        if (t == 0) hp[i] = xh0;
-        if (!(tl.cv && t < a.T)) {
-            eye_row(tl.v, ATr[i]);
-            gv[i] = 0.0f;
-            hp[i] = 0.0f;
-        }
-    }
-
-    // chunk aggregate from a zero carry, walking t downwards: X = (Psi, Wl)
-    float X[S::words];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) X[s] = ATr[C - 1][s];
-    X[8] = mv8(ATr[C - 1], gv[C - 1], 0.0f);
-#pragma unroll
-    for (int i = C - 2; i >= 0; --i) {
-        float np[8];
-        mm8(ATr[i], X, np);
-        X[8] = mv8(ATr[i], gv[i] + X[8], 0.0f);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) X[s] = np[s];
-    }
     ks_store<kMatVec, NCH>(sKS[0], tl.q, tl.slot, X);
     if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
     __syncthreads();
@@ -664,6 +717,152 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
         w = 0.0f;
         for (int q = NCH - 1; q > tl.q; --q) w = mv8(sKS[0][q][tl.slot], w, sKS[0][q][tl.slot][8]);
     }
+    return w;
+}
+
+// ======================================================= block-affine fwd
+// GIV = false: A_t is loaded; GIV = true: A_t = sigmoid(s_t) R(theta_t) is
+// formed from the angles and the gate (the Givens angle-fused scan).
+
+template <bool GIV, int C, int W, bool MULTI>
+__device__ __forceinline__ void affine_fwd_body(const BlkArgs &a)
+{
+    constexpr int NCH = 2 * W;
+    __shared__ float sKS[2][NCH][32][AggShape<kMatVec>::stride];
+    __shared__ float sCarry[32];
+    __shared__ uint32_t sTicket[2];
+    __shared__ float sCS[GIV ? W : 1][64][8];
+
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
+    const Tile tl = make_tile<C, W>(a, tile, false);
+    const int ftile = tl.j * a.nCG + tl.cg;
+
+    // unconditional (clamped) loads keep every load in flight at once
+    float Ar[C][8], bv[C];
+    if constexpr (!GIV) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int t = clampT(tl.t0 + i, a.T);
+            load_row(a.A + tl.ablk0 + t * tl.astep, tl.v, Ar[i]);
+            bv[i] = a.x[tl.vec0 + t * tl.vstep];
+        }
+    } else {
+        float4 th[C];
+        float sv[C];
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int t = clampT(tl.t0 + i, a.T);
+            th[i] = load_angles(a, tl, t);
+            sv[i] = a.sg[tl.blk0 + static_cast<int64_t>(t) * a.nb];
+            bv[i] = a.x[tl.vec0 + t * tl.vstep];
+        }
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            float cc[kAngles], ss[kAngles], r[8];
+            mesh_share(th[i], sCS[tl.wv % (GIV ? W : 1)], tl.lane, cc, ss);
+            mesh_row(cc, ss, tl.v, r);
+            to_slots(r, tl.v, sigmoidf_(sv[i]), Ar[i]);
+            settle8(Ar[i]);
+        }
+    }
+    const float xh0 = load_h0(a, tl);
+#pragma unroll
+    for (int i = 0; i < C; ++i)
+        if (!(tl.cv && tl.t0 + i < a.T)) {
+            eye_row(tl.v, Ar[i]);
+            bv[i] = 0.0f;
+        }
+
+    // chunk aggregate from a zero state: X = (A_e..A_s, local h_e)
+    float X[9];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) X[s] = Ar[0][s];
+    X[8] = bv[0];
+#pragma unroll
+    for (int i = 1; i < C; ++i) {
+        float np[8];
+        mm8(Ar[i], X, np);
+        X[8] = mv8(Ar[i], X[8], bv[i]);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) X[s] = np[s];
+    }
+    float x = affine_fwd_carry<C, W, MULTI>(a, tl, ftile, ep, X, xh0, sKS, sCarry, sTicket);
+
+    // re-run the recurrence from the true state entering the chunk
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        x = mv8(Ar[i], x, bv[i]);
+        const int t = tl.t0 + i;
+        if (tl.cv && t < a.T) a.out[tl.vec0 + t * tl.vstep] = x;
+    }
+}
+
+template <int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
+{
+    affine_fwd_body<false, C, W, MULTI>(a);
+}
+
+template <int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) bgivens_fwd_kernel(BlkArgs a)
+{
+    affine_fwd_body<true, C, W, MULTI>(a);
+}
+
+// ======================================================= block-affine bwd
+// Reverse scan on w_t = A_t^T g_t with g_t = dh_t + w_{t+1}; per chunk [s, e]
+// w_s = Psi w_{e+1} + Wl with Psi = A_s^T .. A_e^T.
+
+template <int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
+{
+    constexpr int NCH = 2 * W;
+    __shared__ float sKS[2][NCH][32][AggShape<kMatVec>::stride];
+    __shared__ float sCarry[32];
+    __shared__ uint32_t sTicket[2];
+
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
+    const Tile tl = make_tile<C, W>(a, tile, true);
+    const int ftile = tl.j * a.nCG + tl.cg;
+
+    float ATr[C][8], gv[C], hp[C];   // rows of A_t^T, upstream dh_t, h_{t-1}
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = clampT(tl.t0 + i, a.T);
+        load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
+        gv[i] = a.y[tl.vec0 + t * tl.vstep];
+        hp[i] = a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep];
+    }
+    const float xh0 = load_h0(a, tl);
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = tl.t0 + i;
+        if (t == 0) hp[i] = xh0;
+        if (!(tl.cv && t < a.T)) {
+            eye_row(tl.v, ATr[i]);
+            gv[i] = 0.0f;
+            hp[i] = 0.0f;
+        }
+    }
+
+    // chunk aggregate from a zero carry, walking t downwards: X = (Psi, Wl)
+    float X[9];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) X[s] = ATr[C - 1][s];
+    X[8] = mv8(ATr[C - 1], gv[C - 1], 0.0f);
+#pragma unroll
+    for (int i = C - 2; i >= 0; --i) {
+        float np[8];
+        mm8(ATr[i], X, np);
+        X[8] = mv8(ATr[i], gv[i] + X[8], 0.0f);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) X[s] = np[s];
+    }
+    float w = affine_bwd_carry<C, W, MULTI>(a, tl, ftile, ep, X, sKS, sCarry, sTicket);
 
     // re-run the reverse recurrence from the true carry; emit dA, db, dh0
 #pragma unroll
@@ -677,6 +876,127 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
             a.out2[tl.vec0 + t * tl.vstep] = g;
             store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, dAr);
         }
+    }
+    if (tl.cv && tl.t0 == 0) a.out3[tl.bb * a.d + tl.jb * 8 + tl.v] = w;   // A_1^T g_1
+}
+
+// =============================================== Givens angle-fused bwd
+// Same reverse scan with A_t = sigmoid(s_t) R(theta_t) formed in registers
+// (unscaled columns of R, the gate applied as a scalar).  dA_t = g_t h_{t-1}^T
+// is never formed as a tensor: lane v holds column v of it, contracts it with
+// the derivative of column v of A (the reverse pass through the mesh) and with
+// column v of R (for the gate), and the chain's 8 lanes add their shares in LDS:
+//     dtheta_t = sigmoid(s_t) <dA_t, dR/dtheta>,  ds_t = sigmoid'(s_t) <dA_t, R>.
+
+template <int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
+{
+    constexpr int NCH = 2 * W;
+    constexpr int PW = 32;   // words per lane in the reduction buffer: 28 angles, the gate, padding
+    __shared__ float sKS[2][NCH][32][AggShape<kMatVec>::stride];
+    __shared__ float sCarry[32];
+    __shared__ uint32_t sTicket[2];
+    __shared__ float sCS[W][64][8];
+    __shared__ float sPart[W][64][PW];
+
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
+    const Tile tl = make_tile<C, W>(a, tile, true);
+    const int ftile = tl.j * a.nCG + tl.cg;
+
+    float4 th[C];
+    float RTr[C][8], sig[C], gv[C], hp[C];   // rows of R^T (unscaled), gate, dh_t, h_{t-1}
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = clampT(tl.t0 + i, a.T);
+        th[i] = load_angles(a, tl, t);
+        sig[i] = a.sg[tl.blk0 + static_cast<int64_t>(t) * a.nb];
+        gv[i] = a.y[tl.vec0 + t * tl.vstep];
+        hp[i] = a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep];
+    }
+    const float xh0 = load_h0(a, tl);
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        float cc[kAngles], ss[kAngles], y[8];
+        mesh_share(th[i], sCS[tl.wv], tl.lane, cc, ss);
+        mesh_col(cc, ss, tl.v, y);
+        to_slots(y, tl.v, 1.0f, RTr[i]);
+        sig[i] = sigmoidf_(sig[i]);
+        settle8(RTr[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = tl.t0 + i;
+        if (t == 0) hp[i] = xh0;
+        if (!(tl.cv && t < a.T)) {
+            eye_row(tl.v, RTr[i]);
+            sig[i] = 1.0f;
+            gv[i] = 0.0f;
+            hp[i] = 0.0f;
+        }
+    }
+
+    // chunk aggregate from a zero carry, walking t downwards: X = (Psi, Wl)
+    float X[9];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) X[s] = sig[C - 1] * RTr[C - 1][s];
+    X[8] = sig[C - 1] * mv8(RTr[C - 1], gv[C - 1], 0.0f);
+#pragma unroll
+    for (int i = C - 2; i >= 0; --i) {
+        float np[8];
+        mm8(RTr[i], X, np);
+        X[8] = sig[i] * mv8(RTr[i], gv[i] + X[8], 0.0f);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) X[s] = sig[i] * np[s];
+    }
+    float w = affine_bwd_carry<C, W, MULTI>(a, tl, ftile, ep, X, sKS, sCarry, sTicket);
+
+    float (*part)[PW] = sPart[tl.wv];
+    const int base = tl.lane & ~7;
+    // the angles are read again here (an L2 hit) rather than kept in registers
+    // since the build; one step ahead
+    float4 thn = load_angles(a, tl, clampT(tl.t0 + C - 1, a.T));
+#pragma unroll
+    for (int i = C - 1; i >= 0; --i) {
+        const float4 thc = thn;
+        if (i > 0) thn = load_angles(a, tl, clampT(tl.t0 + i - 1, a.T));
+        const float g = gv[i] + w;
+        float dAc[8];
+        outer8(hp[i], g, dAc);              // column v of dA_t = g_t h_{t-1}^T (rotated slots)
+        w = sig[i] * mv8(RTr[i], g, 0.0f);  // A_t^T g_t
+        // lane v's share of dtheta_t and ds_t, through column v of A_t
+        float cc[kAngles], ss[kAngles], y[8], dy[8], pt[kAngles];
+        mesh_share(thc, sCS[tl.wv], tl.lane, cc, ss);
+        from_slots(RTr[i], tl.v, 1.0f, y);
+        from_slots(dAc, tl.v, sig[i], dy);
+        float gate = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) gate += dy[r] * y[r];
+        mesh_col_adjoint(cc, ss, y, dy, pt);
+#pragma unroll
+        for (int q = 0; q < 7; ++q)
+            *reinterpret_cast<float4 *>(&part[tl.lane][4 * q]) =
+                make_float4(pt[4 * q], pt[4 * q + 1], pt[4 * q + 2], pt[4 * q + 3]);
+        *reinterpret_cast<float4 *>(&part[tl.lane][28]) = make_float4((1.0f - sig[i]) * gate, 0.0f, 0.0f, 0.0f);
+        // lane v (< 7) adds up angles 4v..4v+3 over the chain; lane 7 the gate
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const float4 u = *reinterpret_cast<const float4 *>(&part[base + p][4 * tl.v]);
+            acc.x += u.x; acc.y += u.y; acc.z += u.z; acc.w += u.w;
+        }
+        const int t = tl.t0 + i;
+        if (tl.cv && t < a.T) {
+            const int64_t blk = tl.blk0 + static_cast<int64_t>(t) * a.nb;
+            a.out2[tl.vec0 + t * tl.vstep] = g;
+            if (tl.v < 7)
+                *reinterpret_cast<float4 *>(a.dtheta + blk * kAngles + 4 * tl.v) = acc;
+            else
+                a.dsg[blk] = acc.x;
+        }
+        asm volatile("" : "+v"(w));
+        __builtin_amdgcn_sched_barrier(0);
     }
     if (tl.cv && tl.t0 == 0) a.out3[tl.bb * a.d + tl.jb * 8 + tl.v] = w;   // A_1^T g_1
 }
@@ -1056,6 +1376,8 @@ BlkArgs base_args(const BlockGeom &g, void *ws)
 
 MGS_DEFINE_LAUNCHER(launch_baffine_fwd, baffine_fwd_kernel)
 MGS_DEFINE_LAUNCHER(launch_baffine_bwd, baffine_bwd_kernel)
+MGS_DEFINE_LAUNCHER(launch_bgivens_fwd, bgivens_fwd_kernel)
+MGS_DEFINE_LAUNCHER(launch_bgivens_bwd, bgivens_bwd_kernel)
 MGS_DEFINE_LAUNCHER(launch_bmatrix_fwd, bmatrix_fwd_kernel)
 MGS_DEFINE_LAUNCHER(launch_bmatrix_bwd, bmatrix_bwd_kernel)
 
@@ -1089,6 +1411,28 @@ hipError_t launch_block_affine_bwd(const BlockGeom &g, const float *A, const flo
     a.A = A; a.x = h; a.y = dh; a.out = dA; a.out2 = db; a.out3 = dh0;
     a.h0 = h0 ? h0 : reinterpret_cast<const float *>(static_cast<char *>(ws) + g.off_zeros);
     launch_baffine_bwd<kAffW, kAffMaxC>(g, a, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_givens_fwd(const BlockGeom &g, const float *theta, const float *sg, const float *b,
+                             const float *h0, float *h, void *ws, hipStream_t s)
+{
+    BlkArgs a = base_args(g, ws);
+    a.theta = theta; a.sg = sg; a.x = b; a.out = h;
+    a.h0 = h0 ? h0 : reinterpret_cast<const float *>(static_cast<char *>(ws) + g.off_zeros);
+    launch_bgivens_fwd<kAffW, kAffMaxC>(g, a, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_givens_bwd(const BlockGeom &g, const float *theta, const float *sg, const float *h0,
+                             const float *h, const float *dh, float *dtheta, float *dsg, float *db,
+                             float *dh0, void *ws, hipStream_t s)
+{
+    BlkArgs a = base_args(g, ws);
+    a.theta = theta; a.sg = sg; a.x = h; a.y = dh;
+    a.dtheta = dtheta; a.dsg = dsg; a.out2 = db; a.out3 = dh0;
+    a.h0 = h0 ? h0 : reinterpret_cast<const float *>(static_cast<char *>(ws) + g.off_zeros);
+    launch_bgivens_bwd<kAffW, kAffMaxC>(g, a, s);
     return hipGetLastError();
 }
 

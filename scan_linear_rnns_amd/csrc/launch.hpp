@@ -72,6 +72,11 @@ hipError_t launch_block_affine_fwd(const BlockGeom &g, const float *A, const flo
 hipError_t launch_block_affine_bwd(const BlockGeom &g, const float *A, const float *h0,
                                    const float *h, const float *dh, float *dA, float *db,
                                    float *dh0, void *ws, hipStream_t s);
+hipError_t launch_givens_fwd(const BlockGeom &g, const float *theta, const float *sg, const float *b,
+                             const float *h0, float *h, void *ws, hipStream_t s);
+hipError_t launch_givens_bwd(const BlockGeom &g, const float *theta, const float *sg, const float *h0,
+                             const float *h, const float *dh, float *dtheta, float *dsg, float *db,
+                             float *dh0, void *ws, hipStream_t s);
 hipError_t launch_block_matrix_fwd(const BlockGeom &g, const float *A, float *P, void *ws,
                                    hipStream_t s);
 hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const float *dP, float *dA,

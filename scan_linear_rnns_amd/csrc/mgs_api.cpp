@@ -301,6 +301,61 @@ mgs_status mgs_block_affine_scan_bwd(const float *A, const float *b, const float
     return hip_status(mgs::launch_block_affine_bwd(g, A, h0, h, dh, dA, db, dh0, workspace, s));
 }
 
+// Givens angle-fused: theta (B,T,nb,28), s (B,T,nb); sizes in bytes
+static void givens_bytes(int64_t B, int64_t T, int64_t d, int64_t k, size_t &nth, size_t &ns)
+{
+    const int64_t nb = d / k;
+    nth = static_cast<size_t>(B * T * nb * (k * (k - 1) / 2)) * 4;
+    ns = static_cast<size_t>(B * T * nb) * 4;
+}
+
+mgs_status mgs_givens_scan_workspace_size(int64_t B, int64_t T, int64_t d, int64_t k, size_t *bytes)
+{
+    return mgs_block_affine_scan_workspace_size(B, T, d, k, bytes);
+}
+
+mgs_status mgs_givens_scan_fwd(const float *theta, const float *s, const float *b, const float *h0,
+                               float *h, int64_t B, int64_t T, int64_t d, int64_t k, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
+    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
+    size_t nth, ns;
+    givens_bytes(B, T, d, k, nth, ns);
+    if (n > 0 && (!theta || !s || !b || !h)) return MGS_ERR_INVALID_VALUE;
+    const Range in[] = {{theta, nth}, {s, ns}, {b, n}, {h0, s0}};
+    const Range out[] = {{h, n}};
+    if (!all_aligned(in, 4) || !all_aligned(out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (any_alias(in, 4, out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (n == 0) return MGS_OK;
+    const mgs::BlockGeom g = mgs::block_affine_geometry(B, T, d, k);
+    if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
+    return hip_status(mgs::launch_givens_fwd(g, theta, s, b, h0, h, workspace, as_stream(stream)));
+}
+
+mgs_status mgs_givens_scan_bwd(const float *theta, const float *s, const float *h0, const float *h,
+                               const float *dh, float *dtheta, float *ds, float *db, float *dh0,
+                               int64_t B, int64_t T, int64_t d, int64_t k, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
+    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
+    size_t nth, ns;
+    givens_bytes(B, T, d, k, nth, ns);
+    if (n > 0 && (!theta || !s || !h || !dh || !dtheta || !ds || !db)) return MGS_ERR_INVALID_VALUE;
+    if (s0 > 0 && !dh0) return MGS_ERR_INVALID_VALUE;
+    const Range in[] = {{theta, nth}, {s, ns}, {h0, s0}, {h, n}, {dh, n}};
+    const Range out[] = {{dtheta, nth}, {ds, ns}, {db, n}, {dh0, s0}};
+    if (!all_aligned(in, 5) || !all_aligned(out, 4)) return MGS_ERR_INVALID_VALUE;
+    if (any_alias(in, 5, out, 4)) return MGS_ERR_INVALID_VALUE;
+    if (s0 == 0) return MGS_OK;
+    hipStream_t st = as_stream(stream);
+    if (T == 0) return hip_status(mgs::launch_fill_zero(dh0, B * d, st));
+    const mgs::BlockGeom g = mgs::block_affine_geometry(B, T, d, k);
+    if (mgs_status e = check_workspace(workspace, workspace_bytes, g.bytes)) return e;
+    return hip_status(mgs::launch_givens_bwd(g, theta, s, h0, h, dh, dtheta, ds, db, dh0, workspace, st));
+}
+
 mgs_status mgs_block_matrix_scan_workspace_size(int64_t B, int64_t T, int64_t d, int64_t k,
                                                 size_t *bytes)
 {

@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.declared_functions()
-    assert len(declared) == 19, declared
+    assert len(declared) == 22, declared
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -137,6 +137,26 @@ def test_block_validation(lib):
     assert mb(dA=fake(2)) == INVALID
     assert mb(dA=fake(0)) == INVALID
     assert mb(nbytes=3) == WORKSPACE
+
+
+def test_givens_validation(lib):
+    B, T, d, k = 2, 8, 16, 8
+    st, nb = _size(lib, "mgs_givens_scan_workspace_size", B, T, d, k)
+    assert st == OK and (st, nb) == _size(lib, "mgs_block_affine_scan_workspace_size", B, T, d, k)
+    assert _size(lib, "mgs_givens_scan_workspace_size", B, T, 16, 4)[0] == UNSUPPORTED
+    fwd = lambda th=fake(0), s=fake(1), h=fake(3), k=k, nbytes=1 << 20: lib.mgs_givens_scan_fwd(
+        th, s, fake(2), None, h, B, T, d, k, fake(9), nbytes, None)
+    assert fwd(th=None) == INVALID
+    assert fwd(s=None) == INVALID
+    assert fwd(h=fake(1)) == INVALID                        # output aliases the gate
+    assert fwd(k=4) == UNSUPPORTED
+    assert fwd(nbytes=0) == WORKSPACE
+    bwd = lambda dth=fake(5), ds=fake(6), nbytes=1 << 20: lib.mgs_givens_scan_bwd(
+        fake(0), fake(1), None, fake(3), fake(4), dth, ds, fake(7), fake(8), B, T, d, k, fake(9), nbytes, None)
+    assert bwd(dth=None) == INVALID
+    assert bwd(ds=fake(5)) == INVALID                       # two outputs overlap
+    assert bwd(dth=fake(0)) == INVALID                      # d theta aliases theta
+    assert bwd(nbytes=4) == WORKSPACE
 
 
 def test_workspace_check_validation(lib):

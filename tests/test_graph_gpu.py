@@ -131,3 +131,24 @@ def test_mingru_scan_graph_replays(gpu):
         for a, b in zip(got, ref):
             assert torch.equal(a, b)
     assert mgs.mgs_workspace_check(ws) == 0
+
+
+def test_givens_scan_graph_replays(gpu):
+    import torch
+    import scan_linear_rnns_amd as mgs
+    print("[graph] givens scan B=16 T=1024 d=64", flush=True)
+    inp = block_inputs(16, 1024, 64, seed=25, h0="normal", with_dP=False, return_angles=True)
+    th, s, b, h0, dh = (_t(x, gpu) for x in (inp.theta, inp.s, inp.b, inp.h0, inp.dh))
+    h, ws = mgs.mgs_givens_scan_fwd(th, s, b, h0)
+    ref = [h.clone(), *[x.clone() for x in mgs.mgs_givens_scan_bwd(th, s, h0, h, dh, ws=ws)]]
+    outs = [torch.empty_like(h), torch.empty_like(th), torch.empty_like(s), torch.empty_like(b),
+            torch.empty_like(h0)]
+
+    def step():
+        mgs.mgs_givens_scan_fwd(th, s, b, h0, h=outs[0], ws=ws)
+        mgs.mgs_givens_scan_bwd(th, s, h0, outs[0], dh, ws=ws, out=tuple(outs[1:]))
+
+    for got in _replays(step, outs):
+        for x, y in zip(got, ref):
+            assert torch.equal(x, y)
+    assert mgs.mgs_workspace_check(ws) == 0

@@ -1,0 +1,99 @@
+"""GPU parity of the Givens angle-fused block scan (mgs_givens_scan_*).
+
+Every output (h, dtheta, ds, db, dh0) element by element against the fp64
+oracle (oracle.givens_fwd / givens_bwd) on the same fp32 angles, gates and
+vectors, with the floored relative rule of tests/test_parity_gpu.py and the
+block scans' bar of 2e-4.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from synthetic import block_inputs
+from tests.test_parity_gpu import BLOCK_TOL, floored_err, say, to_dev, to_np, ws_clean
+
+pytestmark = pytest.mark.gpu
+
+
+def run_givens(theta, s, b, h0, dh, dev):
+    import scan_linear_rnns_amd as mgs
+    tht, st, bt, h0t, dht = (to_dev(x, dev) for x in (theta, s, b, h0, dh))
+    h, ws = mgs.mgs_givens_scan_fwd(tht, st, bt, h0t)
+    dth, ds, db, dh0 = mgs.mgs_givens_scan_bwd(tht, st, h0t, h, dht, ws=ws)
+    ws_clean(ws)
+    out = dict(h=to_np(h), dtheta=to_np(dth), ds=to_np(ds), db=to_np(db), dh0=to_np(dh0))
+    ref = dict(h=oracle.givens_fwd(theta, s, b, h0, 8))
+    ref["dtheta"], ref["ds"], ref["db"], ref["dh0"] = oracle.givens_bwd(theta, s, b, h0, dh, 8)
+    return out, ref
+
+
+def check(out, ref):
+    for key in out:
+        e = floored_err(out[key], ref[key])
+        assert e <= BLOCK_TOL, (key, e)
+
+
+def _inp(B, T, d, seed, h0="zero"):
+    inp = block_inputs(B, T, d, k=8, seed=seed, h0=h0, with_dP=False, return_angles=True)
+    return inp.theta, inp.s, inp.b, inp.h0, inp.dh
+
+
+CASES = [("givens_lab", 128, 64, 64), ("givens_longT", 16, 1024, 64)]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("name,B,T,d", CASES, ids=[c[0] for c in CASES])
+def test_givens_configs(gpu, name, B, T, d, seed):
+    say(f"givens {name} B={B} T={T} d={d} seed={seed}")
+    check(*run_givens(*_inp(B, T, d, seed), gpu))
+
+
+@pytest.mark.parametrize("B,T,d", [(1, 1, 8), (1, 2, 16), (3, 63, 16), (3, 65, 24), (2, 129, 8),
+                                   (2, 200, 72), (1, 1000, 8), (2, 300, 40)])
+def test_givens_edges(gpu, B, T, d):
+    say(f"givens edge B={B} T={T} d={d}")
+    check(*run_givens(*_inp(B, T, d, 6, h0="normal"), gpu))
+
+
+def test_givens_saturated_gates_and_wide_angles(gpu):
+    """Gates near 0 and 1 (|s| up to 30) and angles beyond (-pi, pi)."""
+    say("givens saturated gates / wide angles")
+    theta, s, b, h0, dh = _inp(4, 300, 32, 7, h0="normal")
+    s = s.copy()
+    theta = theta.copy()
+    s[:, ::5] = 30.0
+    s[:, 1::5] = -30.0
+    theta[:, ::3] *= 3.0
+    check(*run_givens(theta, s, b, h0, dh, gpu))
+
+
+def test_givens_matches_block_affine_on_formed_matrices(gpu):
+    """The fused op and the block-affine op on A = sigmoid(s) R(theta) (formed on the host)
+    agree on h, db, dh0 -- two GPU paths, one input."""
+    import scan_linear_rnns_amd as mgs
+    say("givens vs block-affine")
+    theta, s, b, h0, dh = _inp(8, 256, 64, 8, h0="normal")
+    A = oracle.givens_matrix(theta, s, 8).astype(np.float32)
+    At, bt, h0t, dht = (to_dev(x, gpu) for x in (A, b, h0, dh))
+    h_ref, ws = mgs.mgs_block_affine_scan_fwd(At, bt, h0t)
+    _, db_ref, dh0_ref = mgs.mgs_block_affine_scan_bwd(At, bt, h0t, h_ref, dht, ws=ws)
+    out, _ = run_givens(theta, s, b, h0, dh, gpu)
+    for key, ref in (("h", h_ref), ("db", db_ref), ("dh0", dh0_ref)):
+        assert floored_err(out[key], to_np(ref)) <= BLOCK_TOL, key
+
+
+def test_givens_determinism(gpu):
+    import torch
+    import scan_linear_rnns_amd as mgs
+    say("givens determinism")
+    theta, s, b, h0, dh = (to_dev(x, gpu) for x in _inp(16, 1024, 64, 9))
+    first = None
+    for _ in range(3):
+        h, ws = mgs.mgs_givens_scan_fwd(theta, s, b, None)
+        g = mgs.mgs_givens_scan_bwd(theta, s, None, h, dh, ws=ws)
+        cur = [h.clone()] + [x.clone() for x in g]
+        if first is None:
+            first = cur
+        else:
+            for x, y in zip(first, cur):
+                assert torch.equal(x, y)
