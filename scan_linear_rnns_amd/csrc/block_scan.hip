@@ -493,17 +493,48 @@ constexpr int kAngles = 28;
 
 __host__ __device__ constexpr int mesh_first(int l) { return (l / 2) * 7 + (l & 1) * 4; }
 
+// sin x and cos x for |x| up to a few thousand: Cody and Waite's reduction
+// x = q pi/2 + r with pi/2 split into a float head and tail (fused multiply-
+// adds keep q * head exact enough), |r| <= pi/4, then the Taylor series of sin
+// to r^9 and of cos to r^10 (truncation below 2e-9) and the quadrant's
+// swap / sign.  A few ulp, against the dozens of instructions (and a
+// large-argument path) of a general-range sincos.
+__device__ __forceinline__ void sincos_cw(float x, float &sn, float &cs)
+{
+    constexpr float kTwoOverPi = 0.636619772367581f;
+    constexpr float kPiHalfHi = 1.57079637050628662f;      // float(pi / 2)
+    constexpr float kPiHalfLo = -4.37113900018624e-08f;     // pi / 2 - kPiHalfHi
+    const float q = __builtin_rintf(x * kTwoOverPi);
+    float r = __builtin_fmaf(q, -kPiHalfHi, x);
+    r = __builtin_fmaf(q, -kPiHalfLo, r);
+    const float r2 = r * r;
+    float ps = __builtin_fmaf(r2, 1.0f / 362880.0f, -1.0f / 5040.0f);
+    ps = __builtin_fmaf(r2, ps, 1.0f / 120.0f);
+    ps = __builtin_fmaf(r2, ps, -1.0f / 6.0f);
+    const float sr = __builtin_fmaf(r * r2, ps, r);
+    float pc = __builtin_fmaf(r2, -1.0f / 3628800.0f, 1.0f / 40320.0f);
+    pc = __builtin_fmaf(r2, pc, -1.0f / 720.0f);
+    pc = __builtin_fmaf(r2, pc, 1.0f / 24.0f);
+    pc = __builtin_fmaf(r2, pc, -0.5f);
+    const float cr = __builtin_fmaf(r2, pc, 1.0f);
+    const int n = static_cast<int>(q);
+    const bool swap = (n & 1) != 0;
+    const float s0 = swap ? cr : sr, c0 = swap ? sr : cr;
+    sn = (n & 2) ? -s0 : s0;
+    cs = ((n + 1) & 2) ? -c0 : c0;
+}
+
 // cosines and sines of a chain's 28 angles in every lane of the chain
 __device__ __forceinline__ void mesh_share(float4 th, float (*cs)[8], int lane, float (&cc)[kAngles],
                                            float (&ss)[kAngles])
 {
-    // correctly rounded to within an ulp (the hardware's native sin / cos lose
-    // ~1e-6 absolute, which the 28 rotations and the scan then carry)
+    // within a few ulp (the hardware's native sin / cos lose ~1e-6 absolute,
+    // which the 28 rotations and the scan then carry)
     float4 c4, s4;
-    sincosf(th.x, &s4.x, &c4.x);
-    sincosf(th.y, &s4.y, &c4.y);
-    sincosf(th.z, &s4.z, &c4.z);
-    sincosf(th.w, &s4.w, &c4.w);
+    sincos_cw(th.x, s4.x, c4.x);
+    sincos_cw(th.y, s4.y, c4.y);
+    sincos_cw(th.z, s4.z, c4.z);
+    sincos_cw(th.w, s4.w, c4.w);
     *reinterpret_cast<float4 *>(&cs[lane][0]) = c4;
     *reinterpret_cast<float4 *>(&cs[lane][4]) = s4;
     const int base = lane & ~7;
