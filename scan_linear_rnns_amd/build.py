@@ -21,7 +21,13 @@ ARCH = os.environ.get("MGS_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 instructions are disabled for every device code object: the
 # compiler would otherwise form them from ordinary float code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# No packed fp32 instructions anywhere.  No atomic optimizer: it turns the
+# one-lane launch-epoch atomic each multi-tile kernel issues at its start into a
+# wave-reduced form whose readfirstlane waits for the atomic's round trip
+# before the wave's loads go out (and the workgroup then waits for that wave at
+# its first barrier).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
 def hipcc() -> str:
