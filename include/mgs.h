@@ -50,9 +50,10 @@
  * Errors.  Arguments are validated before any HIP call:
  *   MGS_ERR_INVALID_VALUE  NULL required pointer, size <= 0, d % k != 0,
  *                          misaligned pointer, or output aliasing an input;
- *   MGS_ERR_UNSUPPORTED    outside the envelope (k != 8 for the block ops,
- *                          or a tensor with 2^31 or more elements); never a
- *                          silent fallback to another path;
+ *   MGS_ERR_UNSUPPORTED    outside the envelope (block ops: k not in
+ *                          {1, 2, 4, 8, 16}; Givens scan: k != 8; or a tensor
+ *                          with 2^31 or more elements); never a silent
+ *                          fallback to another path;
  *   MGS_ERR_WORKSPACE      workspace NULL or smaller than the query says;
  *   MGS_ERR_HIP            a HIP launch error; mgs_last_hip_error() gives the
  *                          hipError_t (per calling thread).
@@ -195,7 +196,8 @@ mgs_status mgs_scan_linear_bwd(const float *a, const float *b, const float *h0, 
  *     h_0 = h0 (zeros if h0 == NULL),   h_t = A_t h_{t-1} + b_t
  * with A_t block-diagonal (d/k blocks of k x k).
  *   A : (B,T,d/k,k,k) in;  b : (B,T,d) in;  h0 : (B,d) in or NULL;  h : (B,T,d) out.
- * Envelope: k == 8.
+ * Envelope: k in {1, 2, 4, 8, 16} (k = 1 is the elementwise linear-space scan
+ * with A of shape (B,T,d,1,1)).
  */
 mgs_status mgs_block_affine_scan_workspace_size(int64_t B, int64_t T, int64_t d, int64_t k,
                                                 size_t *bytes);
@@ -261,7 +263,7 @@ mgs_status mgs_givens_scan_bwd(const float *theta, const float *s, const float *
 /*
  * Forward ("Run the benchmarks" how-to, Step 2, matrix_scan): the b = 0 case,
  *     P_0 = I,   P_t = A_t P_{t-1}   per k x k block.
- *   A : (B,T,d/k,k,k) in;   P : (B,T,d/k,k,k) out.   Envelope: k == 8.
+ *   A : (B,T,d/k,k,k) in;   P : (B,T,d/k,k,k) out.   Envelope: k in {1, 2, 4, 8, 16}.
  */
 mgs_status mgs_block_matrix_scan_workspace_size(int64_t B, int64_t T, int64_t d, int64_t k,
                                                 size_t *bytes);
@@ -274,7 +276,7 @@ mgs_status mgs_block_matrix_scan_fwd(const float *A, float *P,
  * Backward of mgs_block_matrix_scan_fwd for L = sum_t <dP_t, P_t>:
  *     G_T = dP_T,  G_t = dP_t + A_{t+1}^T G_{t+1},  dA_t = G_t P_{t-1}^T.
  * P_{t-1} is recomputed from A and the state entering each chunk, which the
- * forward stores in the workspace (one 8 x 8 block per chain per chunk of
+ * forward stores in the workspace (one k x k block per chain per chunk of
  * steps); P itself is not read.
  *   dP : in;  dA : out (shape of A).
  * fwd_state_valid != 0 promises that mgs_block_matrix_scan_fwd ran on this A

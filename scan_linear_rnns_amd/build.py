@@ -5,6 +5,7 @@ The shared library lands next to this file, where the Python binding loads it.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -16,7 +17,13 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmgs.so")
-SOURCES = ["mgs_api.cpp", "elem_scan.hip", "block_scan.hip"]
+# (source, object name, extra flags): block_scan_k.hip is built once per block
+# size it serves, each object holding that size's kernels only.
+SOURCES = [("mgs_api.cpp", "mgs_api", ()),
+           ("elem_scan.hip", "elem_scan", ()),
+           ("block_scan.hip", "block_scan", ())] + [
+          ("block_scan_k.hip", f"block_scan_k{k}", (f"-DMGS_ROWS_K={k}",)) for k in (1, 2, 4, 16)]
+JOBS = int(os.environ.get("MGS_BUILD_JOBS", "8"))
 ARCH = os.environ.get("MGS_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 instructions are disabled for every device code object: the
@@ -46,18 +53,25 @@ def _compile(src: str, obj: str, extra=()) -> None:
 def build(verbose: bool = False, save_temps_dir: str | None = None) -> str:
     """Compile every HIP/C++ source and link libmgs.so (always rebuilds)."""
     with tempfile.TemporaryDirectory(prefix="mgs_build_") as tmp:
-        objs = []
-        for name in SOURCES:
+        jobs = []
+        for name, oname, flags in SOURCES:
             src = os.path.join(CSRC, name)
-            obj = os.path.join(tmp, name + ".o")
-            extra = []
+            obj = os.path.join(tmp, oname + ".o")
+            extra = list(flags)
             if save_temps_dir:
                 os.makedirs(save_temps_dir, exist_ok=True)
-                extra = ["-save-temps=obj", "-o", obj]
+                extra += ["-save-temps=obj", "-o", obj]
+            jobs.append((src, obj, extra, oname))
+
+        def run(job):
+            src, obj, extra, oname = job
             if verbose:
-                print("[build]", name, flush=True)
+                print("[build]", oname, flush=True)
             _compile(src, obj, extra)
-            objs.append(obj)
+            return obj
+
+        with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, JOBS)) as pool:
+            objs = list(pool.map(run, jobs))
         out_tmp = LIB + ".tmp%d" % os.getpid()
         subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp, *objs],
                        check=True)

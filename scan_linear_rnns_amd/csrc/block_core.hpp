@@ -1,0 +1,1887 @@
+// block_core.hpp -- device code of the block scans (block-affine scan, block
+// cumulative product, Givens angle-fused scan), forward and fused backward,
+// for gfx950, written once for every block size k in {1, 2, 4, 8, 16}.
+//
+// The ops ("Run the benchmarks" how-to, Step 2: matrix_affine_scan and
+// matrix_scan; the RotationMinGRU / GivensMinGRU recurrences on the minGRU
+// home page):
+//     h_t = A_t h_{t-1} + b_t          P_t = A_t P_{t-1},  P_0 = I
+// per chain (b, block j), with A_t a k x k block.  Backward for
+// L = sum <dh_t, h_t> (resp. <dP_t, P_t>): g_t = dh_t + A_{t+1}^T g_{t+1},
+// dA_t = g_t h_{t-1}^T (resp. G_t P_{t-1}^T), db_t = g_t, dh0 = A_1^T g_1.
+// dA_t is formed in registers from g_t and h_{t-1} and written once; no
+// per-step product or intermediate tensor is ever stored.
+//
+// Register layout ("row lanes"): a chain's k x k matrices live in k
+// consecutive lanes, lane v holding row v, and a half-wave holds 32 / k
+// chains.  A product needs, in every lane, the rows held by the chain's other
+// lanes; they arrive through DPP broadcasts within the chain's lanes:
+//   k = 8:  column slots of a row are rotated by the lane's quad (slot s holds
+//           column s ^ (v & 4)), so every operand comes through one of two
+//           wave-uniform patterns -- a quad broadcast for rows in the lane's own
+//           quad, a half-row mirror plus a quad broadcast for the other quad --
+//           and the rotation costs nothing because loads and stores address the
+//           two 16-byte halves of a row in swapped order.  An 8 x 8 by 8 x 8
+//           product is 64 FMAs with DPP operands plus 8 mirror moves per lane.
+//   k = 16: a chain is one DPP row; row_newbcast:m broadcasts row m.
+//   k = 4:  quad broadcast;  k = 2: quad_perm [m, m, m+2, m+2];  k = 1: none.
+//
+// Decomposition: a wave holds 2 sub-chunks of 32 lanes (lane = 32*sub +
+// k*chain + row); a workgroup of W waves holds NCH = 2W consecutive chunks of C
+// steps each, i.e. one tile of TT = NCH*C steps of 32 / k chains.  Each chunk
+// first builds its aggregate (transfer matrix and offset) from a zero state,
+// the aggregates meet in LDS, and tiles along T exchange theirs by single-pass
+// decoupled look-back (tagged words, launch epochs; see device.hpp).  Each
+// chunk then re-runs its recurrence from its true carry-in, keeping the loaded
+// A_t in registers, and writes its outputs.
+//
+// Included by block_scan.hip (k = 8, the Givens scan, host entry points) and
+// by block_scan_k.hip (one other k per object file).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <utility>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace mgs {
+
+// Kernel arguments of every block op (one struct, fields used per op).
+struct BlkArgs {
+    const float *A;      // (B,T,nb,k,k)
+    const float *x;      // affine: b (fwd) or h (bwd)
+    const float *y;      // affine bwd: dh; cumprod bwd: dP
+    const float *h0;     // affine: (B,d), or a zero region of the workspace
+    float *out;          // affine fwd: h; affine bwd: dA; cumprod fwd: P (NULL: chunk states only); cumprod bwd: dA
+    float *out2;         // affine bwd: db
+    float *out3;         // affine bwd: dh0
+    int64_t nchain;
+    int T, d, nb, nCG, nT, nTiles;
+    WsHeader *hd;
+    uint64_t *agg, *incl;
+    float *pstate;       // cumulative product: state entering each chunk, [tile][chunk][slot][k]
+    const float *theta;  // Givens angle-fused: angles (B,T,nb,28)
+    const float *sg;     // Givens angle-fused: gate pre-activations (B,T,nb)
+    float *dtheta;       // Givens angle-fused backward: d angles
+    float *dsg;          // Givens angle-fused backward: d gate
+};
+
+// Tile shape per op and block size: waves per workgroup and the cap on steps
+// per lane group (a lane keeps up to 3C rows of k floats in registers).  For
+// k = 8, eight waves and C <= 8 measured fastest for both ops at both shapes.
+#ifndef MGS_AFF_W
+#define MGS_AFF_W 8
+#endif
+#ifndef MGS_AFF_MAXC
+#define MGS_AFF_MAXC 8
+#endif
+#ifndef MGS_MAT_W
+#define MGS_MAT_W 8
+#endif
+#ifndef MGS_MAT_MAXC
+#define MGS_MAT_MAXC 8
+#endif
+struct BlkShape {
+    int W, max_c;
+};
+constexpr BlkShape affine_shape(int k)
+{
+    return k == 8 ? BlkShape{MGS_AFF_W, MGS_AFF_MAXC} : k == 16 ? BlkShape{8, 4} : BlkShape{8, 8};
+}
+constexpr BlkShape matrix_shape(int k)
+{
+    // k = 16: the backward's reverse aggregate is two 16 x 16 rows per lane;
+    // four waves keep its LDS buffers at 68 KB
+    return k == 8 ? BlkShape{MGS_MAT_W, MGS_MAT_MAXC} : k == 16 ? BlkShape{4, 2} : BlkShape{8, 8};
+}
+
+enum class BlkOp : int { AffineFwd, AffineBwd, MatrixFwd, MatrixBwd };
+
+// Launches one block op for block size K; each K's kernels are instantiated
+// in one object file (k = 8 in block_scan.hip, the others in block_scan_k.hip).
+template <int K>
+void launch_blk(BlkOp op, const BlockGeom &g, const BlkArgs &a, hipStream_t s);
+template <> void launch_blk<1>(BlkOp, const BlockGeom &, const BlkArgs &, hipStream_t);
+template <> void launch_blk<2>(BlkOp, const BlockGeom &, const BlkArgs &, hipStream_t);
+template <> void launch_blk<4>(BlkOp, const BlockGeom &, const BlkArgs &, hipStream_t);
+template <> void launch_blk<8>(BlkOp, const BlockGeom &, const BlkArgs &, hipStream_t);
+template <> void launch_blk<16>(BlkOp, const BlockGeom &, const BlkArgs &, hipStream_t);
+
+namespace {
+
+// ------------------------------------------------------ 8-lane row algebra (k = 8)
+
+template <int P>
+__device__ __forceinline__ float qb(float x)   // value of quad position P
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), P | (P << 2) | (P << 4) | (P << 6),
+                                                   0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float hm(float x)   // value of lane 7 - v within the 8-lane group
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+}
+
+// 8 x 8 row algebra with DPP operands folded into the multiply-adds.  The
+// compiler does not fold DPP moves into FMAs, so the products are written as
+// inline-asm blocks of v_fmac_f32_dpp / v_mul_f32_dpp.  Each block keeps 2 or
+// 4 independent accumulators and cycles through them, so consecutive
+// instructions never depend on each other.  Every block opens with 5 wait
+// states (a VALU write of a DPP source, or of EXEC, may come right before it)
+// and closes with 2 (a DPP read of its result may come right after), because
+// the compiler's hazard tracking does not look inside inline asm.
+
+// y_v = sum_m R[v][m] x_m + add, R = own row (rotated slots), x one value per lane
+__device__ __forceinline__ float mv8(const float *R, float x, float add)
+{
+    const float mx = hm(x);
+    float a0 = add, a1;
+    asm("s_nop 4\n\t"
+        "v_fmac_f32_dpp %0, %2, %4 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %2, %5 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %6 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %2, %7 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %3, %11 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %10 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %3, %9 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %8 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "+&v"(a0), "=&v"(a1)
+        : "v"(x), "v"(mx), "v"(R[0]), "v"(R[1]), "v"(R[2]), "v"(R[3]), "v"(R[4]), "v"(R[5]), "v"(R[6]), "v"(R[7]));
+    return a0 + a1;
+}
+
+// Four output slots S..S+3 of Y = R X (X rows spread over the group, M = hm(X)).
+template <int S>
+__device__ __forceinline__ void mm8_quarter(const float *R, const float *X, const float *M, float *Y)
+{
+    asm("s_nop 4\n\t"
+        "v_mul_f32_dpp %0, %4, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %5, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %6, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %7, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %13 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %13 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %13 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %13 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %15 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %15 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %15 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %15 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %19 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %9, %19 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %19 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %11, %19 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %18 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %9, %18 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %18 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %11, %18 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %17 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %9, %17 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %17 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %11, %17 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %16 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %9, %16 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %16 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %11, %16 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "=&v"(Y[S]), "=&v"(Y[S + 1]), "=&v"(Y[S + 2]), "=&v"(Y[S + 3])
+        : "v"(X[S]), "v"(X[S + 1]), "v"(X[S + 2]), "v"(X[S + 3]),
+          "v"(M[S ^ 4]), "v"(M[(S + 1) ^ 4]), "v"(M[(S + 2) ^ 4]), "v"(M[(S + 3) ^ 4]),
+          "v"(R[0]), "v"(R[1]), "v"(R[2]), "v"(R[3]), "v"(R[4]), "v"(R[5]), "v"(R[6]), "v"(R[7]));
+}
+
+// Y = R X : own row of R, rows of X spread over the group.  Y must not alias X.
+__device__ __forceinline__ void mm8(const float *R, const float *X, float *Y)
+{
+    float M[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) M[s] = hm(X[s]);
+    mm8_quarter<0>(R, X, M, Y);
+    mm8_quarter<4>(R, X, M, Y);
+}
+
+// Output slots P, P+1, 7-P, 6-P of Y = G X^T.
+template <int P>
+__device__ __forceinline__ void mmT8_quarter(const float *G, const float *X, const float *M, float *Y)
+{
+    asm("s_nop 4\n\t"
+        "v_mul_f32_dpp %0, %4, %20 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %4, %20 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %12, %24 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %12, %24 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %5, %21 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %21 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %13, %25 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %13, %25 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %6, %22 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %6, %22 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %14, %26 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %14, %26 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %7, %23 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %7, %23 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %15, %27 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %15, %27 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %24 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %8, %24 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %16, %20 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %16, %20 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %9, %25 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %9, %25 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %17, %21 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %17, %21 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %10, %26 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %10, %26 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %22 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %18, %22 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %11, %27 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %11, %27 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %19, %23 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %23 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "=&v"(Y[P]), "=&v"(Y[P + 1]), "=&v"(Y[7 - P]), "=&v"(Y[6 - P])
+        : "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]),
+          "v"(M[0]), "v"(M[1]), "v"(M[2]), "v"(M[3]), "v"(M[4]), "v"(M[5]), "v"(M[6]), "v"(M[7]),
+          "v"(G[0]), "v"(G[1]), "v"(G[2]), "v"(G[3]), "v"(G[4]), "v"(G[5]), "v"(G[6]), "v"(G[7]),
+          "n"(P), "n"(P + 1));
+}
+
+// Y = G X^T : own row of G, rows of X spread over the group.
+__device__ __forceinline__ void mmT8(const float *G, const float *X, float *Y)
+{
+    float M[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) M[s] = hm(X[s]);
+    mmT8_quarter<0>(G, X, M, Y);
+    mmT8_quarter<2>(G, X, M, Y);
+}
+
+// Row v of x x'^T scaled: Y[slot] = g * x'_{column(slot)}  (x' one value per lane)
+__device__ __forceinline__ void outer8(float g, float x, float *Y)
+{
+    const float mx = hm(x);
+    Y[0] = g * qb<0>(x);
+    Y[1] = g * qb<1>(x);
+    Y[2] = g * qb<2>(x);
+    Y[3] = g * qb<3>(x);
+    Y[4] = g * qb<3>(mx);
+    Y[5] = g * qb<2>(mx);
+    Y[6] = g * qb<1>(mx);
+    Y[7] = g * qb<0>(mx);
+}
+
+__device__ __forceinline__ void eye_row8(int v, float *Y)
+{
+#pragma unroll
+    for (int s = 0; s < 8; ++s) Y[s] = (s == (v & 3)) ? 1.0f : 0.0f;
+}
+
+// row v of a row-major 8x8 block at p (16-byte aligned), into rotated slots
+__device__ __forceinline__ void load_row8(const float *p, int v, float *R)
+{
+    const int lo = v & 4;
+    const float4 x0 = *reinterpret_cast<const float4 *>(p + v * 8 + lo);
+    const float4 x1 = *reinterpret_cast<const float4 *>(p + v * 8 + (lo ^ 4));
+    R[0] = x0.x; R[1] = x0.y; R[2] = x0.z; R[3] = x0.w;
+    R[4] = x1.x; R[5] = x1.y; R[6] = x1.z; R[7] = x1.w;
+}
+
+// row v of the TRANSPOSE of the 8x8 block at p (column v), rotated slots
+__device__ __forceinline__ void load_col8(const float *p, int v, float *R)
+{
+    const int lo = v & 4;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) R[s] = p[((s ^ lo) * 8) + v];
+}
+
+__device__ __forceinline__ void store_row8(float *p, int v, const float *R)
+{
+    const int lo = v & 4;
+    *reinterpret_cast<float4 *>(p + v * 8 + lo) = make_float4(R[0], R[1], R[2], R[3]);
+    *reinterpret_cast<float4 *>(p + v * 8 + (lo ^ 4)) = make_float4(R[4], R[5], R[6], R[7]);
+}
+
+// ----------------------------------------------------- 16-lane row algebra (k = 16)
+// A chain is one DPP row of 16 lanes; row_newbcast:m hands every lane of the
+// row the value of its lane m.  Products are inline-asm blocks of
+// v_fmac_f32_dpp / v_mul_f32_dpp for the reason given for k = 8 (same wait
+// states around each block).
+
+// Y = R X : own row of R, rows of X spread over the chain (16 x 16).  One
+// block of 256 multiply-adds with row_newbcast operands; consecutive
+// instructions write different accumulators.  Y must not alias X.
+__device__ __forceinline__ void mm16(const float *R, const float *X, float *Y)
+{
+    asm("s_nop 4\n\t"
+        "v_mul_f32_dpp %0, %16, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %17, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %18, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %19, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %20, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %5, %21, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %6, %22, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %7, %23, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %8, %24, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %9, %25, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %10, %26, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %11, %27, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %12, %28, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %13, %29, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %14, %30, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %15, %31, %32 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %33 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %34 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %35 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %36 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %37 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %38 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %39 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %40 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %41 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %42 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %43 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %44 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %45 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %46 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %16, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %17, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %18, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %19, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %20, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %21, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %22, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %23, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %24, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %25, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %26, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %27, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %28, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %29, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %30, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %31, %47 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "=&v"(Y[0]), "=&v"(Y[1]), "=&v"(Y[2]), "=&v"(Y[3]), "=&v"(Y[4]), "=&v"(Y[5]), "=&v"(Y[6]), "=&v"(Y[7]), "=&v"(Y[8]), "=&v"(Y[9]), "=&v"(Y[10]), "=&v"(Y[11]), "=&v"(Y[12]), "=&v"(Y[13]), "=&v"(Y[14]), "=&v"(Y[15])
+        : "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]), "v"(X[8]), "v"(X[9]), "v"(X[10]), "v"(X[11]), "v"(X[12]), "v"(X[13]), "v"(X[14]), "v"(X[15]),
+          "v"(R[0]), "v"(R[1]), "v"(R[2]), "v"(R[3]), "v"(R[4]), "v"(R[5]), "v"(R[6]), "v"(R[7]), "v"(R[8]), "v"(R[9]), "v"(R[10]), "v"(R[11]), "v"(R[12]), "v"(R[13]), "v"(R[14]), "v"(R[15]));
+}
+
+// y_v = sum_m R[m] x_m + add (16 x 16), four accumulators
+__device__ __forceinline__ float mv16(const float *R, float x, float add)
+{
+    float a0 = add, a1, a2, a3;
+    asm("s_nop 4\n\t"
+        "v_fmac_f32_dpp %0, %4, %5 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %4, %6 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %4, %7 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %4, %8 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %9 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %4, %10 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %4, %11 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %4, %12 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %13 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %4, %14 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %4, %15 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %4, %16 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %17 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %4, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %4, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %4, %20 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "+&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+        : "v"(x), "v"(R[0]), "v"(R[1]), "v"(R[2]), "v"(R[3]), "v"(R[4]), "v"(R[5]), "v"(R[6]), "v"(R[7]), "v"(R[8]), "v"(R[9]), "v"(R[10]), "v"(R[11]), "v"(R[12]), "v"(R[13]), "v"(R[14]), "v"(R[15]));
+    return (a0 + a1) + (a2 + a3);
+}
+
+// row v of g x^T (16 x 16): Y[c] = g * x_c
+__device__ __forceinline__ void outer16(float g, float x, float *Y)
+{
+    asm("s_nop 4\n\t"
+        "v_mul_f32_dpp %0, %16, %17 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %16, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %16, %17 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %16, %17 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %16, %17 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %5, %16, %17 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %6, %16, %17 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %7, %16, %17 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %8, %16, %17 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %9, %16, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %10, %16, %17 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %11, %16, %17 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %12, %16, %17 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %13, %16, %17 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %14, %16, %17 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %15, %16, %17 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "=&v"(Y[0]), "=&v"(Y[1]), "=&v"(Y[2]), "=&v"(Y[3]), "=&v"(Y[4]), "=&v"(Y[5]), "=&v"(Y[6]), "=&v"(Y[7]), "=&v"(Y[8]), "=&v"(Y[9]), "=&v"(Y[10]), "=&v"(Y[11]), "=&v"(Y[12]), "=&v"(Y[13]), "=&v"(Y[14]), "=&v"(Y[15])
+        : "v"(x), "v"(g));
+}
+
+// --------------------------------------------- row algebra for every k
+// Rows<K> gathers what the kernels need of a chain's K x K matrices held one
+// row per lane (the primary template serves k = 1, 2, 4 with DPP moves the
+// compiler places; k = 8 and k = 16 are specialised with inline-asm blocks): products with another matrix or vector spread over the
+// chain's lanes, the outer product, the identity row, and loads / stores of a
+// row of a row-major block in the lane's slot order.  col(v, s) is the column
+// that slot s of lane v holds (an involution in s).
+
+// f(0), f(1), ..., f(N - 1) with compile-time arguments (DPP controls must be
+// constants, so the loops over source rows are unrolled at the source level).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_(f, std::make_integer_sequence<int, N>{});
+}
+
+// Value of x in the lane holding row M of this lane's chain (K in {1, 2, 4}:
+// the chain sits inside one quad, so a quad permutation reaches every row).
+template <int K, int M>
+__device__ __forceinline__ float row_bcast(float x)
+{
+    static_assert(M >= 0 && M < K, "row index");
+    static_assert(K == 1 || K == 2 || K == 4, "block size");
+    if constexpr (K == 1) {
+        return x;
+    } else {
+        constexpr int ctrl = K == 2 ? (M | (M << 2) | ((M + 2) << 4) | ((M + 2) << 6))   // quad_perm [M,M,M+2,M+2]
+                                    : M * 0x55;                                          // quad_perm [M,M,M,M]
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, true));
+    }
+}
+
+// K contiguous floats at p (16-byte aligned when K >= 4) <-> registers
+template <int K>
+__device__ __forceinline__ void load_vec(const float *p, float *x)
+{
+    if constexpr (K == 1) {
+        x[0] = p[0];
+    } else if constexpr (K == 2) {
+        const float2 u = *reinterpret_cast<const float2 *>(p);
+        x[0] = u.x; x[1] = u.y;
+    } else {
+#pragma unroll
+        for (int q = 0; q < K / 4; ++q) {
+            const float4 u = *reinterpret_cast<const float4 *>(p + 4 * q);
+            x[4 * q] = u.x; x[4 * q + 1] = u.y; x[4 * q + 2] = u.z; x[4 * q + 3] = u.w;
+        }
+    }
+}
+
+template <int K>
+__device__ __forceinline__ void store_vec(float *p, const float *x)
+{
+    if constexpr (K == 1) {
+        p[0] = x[0];
+    } else if constexpr (K == 2) {
+        *reinterpret_cast<float2 *>(p) = make_float2(x[0], x[1]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < K / 4; ++q)
+            *reinterpret_cast<float4 *>(p + 4 * q) = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+    }
+}
+
+template <int K>
+struct Rows {
+    static constexpr int k = K;
+    // y_v = sum_m R[m] x_m + add  (x one value per lane)
+    static __device__ __forceinline__ float mv(const float *R, float x, float add)
+    {
+        float a0 = add, a1 = 0.0f;
+        static_for<K>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            if constexpr (m % 2 == 0) a0 = __builtin_fmaf(R[m], row_bcast<K, m>(x), a0);
+            else a1 = __builtin_fmaf(R[m], row_bcast<K, m>(x), a1);
+        });
+        return K == 1 ? a0 : a0 + a1;
+    }
+    // Y = R X : own row of R, rows of X spread over the chain.  Y must not alias X.
+    static __device__ __forceinline__ void mm(const float *R, const float *X, float *Y)
+    {
+#pragma unroll
+        for (int c = 0; c < K; ++c) Y[c] = 0.0f;
+        static_for<K>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+#pragma unroll
+            for (int c = 0; c < K; ++c) Y[c] = __builtin_fmaf(R[m], row_bcast<K, m>(X[c]), Y[c]);
+        });
+    }
+    // row v of g x^T: Y[c] = g * x_c  (x one value per lane)
+    static __device__ __forceinline__ void outer(float g, float x, float *Y)
+    {
+        static_for<K>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            Y[c] = g * row_bcast<K, c>(x);
+        });
+    }
+    static __device__ __forceinline__ void eye(int v, float *Y)
+    {
+#pragma unroll
+        for (int s = 0; s < K; ++s) Y[s] = (s == v) ? 1.0f : 0.0f;
+    }
+    static __device__ __forceinline__ int col(int, int s) { return s; }
+    // row v of the row-major K x K block at p
+    static __device__ __forceinline__ void load_row(const float *p, int v, float *R) { load_vec<K>(p + v * K, R); }
+    // row v of the transpose of the block at p (column v)
+    static __device__ __forceinline__ void load_col(const float *p, int v, float *R)
+    {
+#pragma unroll
+        for (int s = 0; s < K; ++s) R[s] = p[s * K + v];
+    }
+    static __device__ __forceinline__ void store_row(float *p, int v, const float *R) { store_vec<K>(p + v * K, R); }
+};
+
+template <>
+struct Rows<16> {
+    static constexpr int k = 16;
+    static __device__ __forceinline__ float mv(const float *R, float x, float add) { return mv16(R, x, add); }
+    static __device__ __forceinline__ void mm(const float *R, const float *X, float *Y) { mm16(R, X, Y); }
+    static __device__ __forceinline__ void outer(float g, float x, float *Y) { outer16(g, x, Y); }
+    static __device__ __forceinline__ void eye(int v, float *Y)
+    {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) Y[s] = (s == v) ? 1.0f : 0.0f;
+    }
+    static __device__ __forceinline__ int col(int, int s) { return s; }
+    static __device__ __forceinline__ void load_row(const float *p, int v, float *R) { load_vec<16>(p + v * 16, R); }
+    static __device__ __forceinline__ void load_col(const float *p, int v, float *R)
+    {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) R[s] = p[s * 16 + v];
+    }
+    static __device__ __forceinline__ void store_row(float *p, int v, const float *R) { store_vec<16>(p + v * 16, R); }
+};
+
+template <>
+struct Rows<8> {
+    static constexpr int k = 8;
+    static __device__ __forceinline__ float mv(const float *R, float x, float add) { return mv8(R, x, add); }
+    static __device__ __forceinline__ void mm(const float *R, const float *X, float *Y) { mm8(R, X, Y); }
+    static __device__ __forceinline__ void outer(float g, float x, float *Y) { outer8(g, x, Y); }
+    static __device__ __forceinline__ void eye(int v, float *Y) { eye_row8(v, Y); }
+    static __device__ __forceinline__ int col(int v, int s) { return s ^ (v & 4); }
+    static __device__ __forceinline__ void load_row(const float *p, int v, float *R) { load_row8(p, v, R); }
+    static __device__ __forceinline__ void load_col(const float *p, int v, float *R) { load_col8(p, v, R); }
+    static __device__ __forceinline__ void store_row(float *p, int v, const float *R) { store_row8(p, v, R); }
+};
+
+// ------------------------------------------------------------ look-back
+
+// All lanes of one wave take part; lanes 32..63 mirror lanes 0..31 (same slot).
+// Returns the nearest tile p (in the direction dir = -1: earlier tiles,
+// +1: later tiles) whose IW-word inclusive state is published, with the state
+// in xi; -1 if the spin limit was hit.  One batch of loads polls the first word
+// of up to WIN tiles at once; the remaining words of the chosen tile follow.
+template <int IW>
+__device__ __forceinline__ int find_inclusive(const uint64_t *incl, int j, int nT, int nCG, int cg, int slot,
+                              int dir, uint32_t tag, uint32_t *err, float *xi)
+{
+    constexpr int WIN = 16;
+    for (uint32_t spin = 0;; ++spin) {
+        for (int p0 = j + dir; p0 >= 0 && p0 < nT; p0 += dir * WIN) {
+            uint64_t w[WIN];
+#pragma unroll
+            for (int u = 0; u < WIN; ++u) {
+                const int p = p0 + dir * u;
+                const bool in = p >= 0 && p < nT;
+                w[u] = tagged_load(incl + ((static_cast<size_t>(in ? p : p0) * nCG + cg) * 32 + slot) * IW);
+            }
+#pragma unroll
+            for (int u = 0; u < WIN; ++u) {
+                const int p = p0 + dir * u;
+                if (p < 0 || p >= nT) break;
+                if (__all(tag_is(w[u], tag))) {
+                    const uint64_t *src = incl + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * IW;
+                    uint64_t r[IW];
+                    r[0] = w[u];
+#pragma unroll
+                    for (int e = 1; e < IW; ++e) r[e] = tagged_load(src + e);
+#pragma unroll
+                    for (int e = 1; e < IW; ++e) {
+                        for (uint32_t sp = 0; !tag_is(r[e], tag); ++sp) {
+                            if (sp >= kSpinLimit) {
+                                raise_error(err, kErrSpin);
+                                break;
+                            }
+                            backoff();
+                            r[e] = tagged_load(src + e);
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < IW; ++e) xi[e] = tag_value(r[e]);
+                    return p;
+                }
+            }
+        }
+        if (spin >= kSpinLimit) {
+            raise_error(err, kErrSpin);
+            return -1;
+        }
+        backoff();
+    }
+}
+
+// Loads the AW-word aggregates of `cnt` (<= NB) tiles p0, p0 + dir, ... for
+// this lane in one batch of loads, then waits for any word not yet published.
+template <int AW, int NB>
+__device__ __forceinline__ void load_aggregates(const uint64_t *agg, int p0, int dir, int cnt, int nCG,
+                                                int cg, int slot, uint32_t tag, uint32_t *err,
+                                                float (&out)[NB][AW])
+{
+    uint64_t w[NB][AW];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const int p = p0 + dir * (u < cnt ? u : 0);
+        const uint64_t *src = agg + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * AW;
+#pragma unroll
+        for (int e = 0; e < AW; ++e) w[u][e] = tagged_load(src + e);
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        if (u >= cnt) break;
+        const int p = p0 + dir * u;
+        const uint64_t *src = agg + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * AW;
+#pragma unroll
+        for (int e = 0; e < AW; ++e) {
+            for (uint32_t spin = 0; !tag_is(w[u][e], tag); ++spin) {
+                if (spin >= kSpinLimit) {
+                    raise_error(err, kErrSpin);
+                    break;
+                }
+                backoff();
+                w[u][e] = tagged_load(src + e);
+            }
+            out[u][e] = tag_value(w[u][e]);
+        }
+    }
+}
+
+template <int AW>
+__device__ __forceinline__ void publish(uint64_t *dst, int tile, int slot, uint32_t tag, const float *x)
+{
+    uint64_t *p = dst + (static_cast<size_t>(tile) * 32 + slot) * AW;
+#pragma unroll
+    for (int e = 0; e < AW; ++e) tagged_store(p + e, tag, x[e]);
+}
+
+struct Tile {
+    int lane, wv, v, cgl, sub, slot, q, j, cg, t0;
+    bool cv;
+    int64_t bb, jb;
+    int64_t blk0;    // block index (bb, t=0, jb) in (B,T,nb)
+    int64_t ablk0;   // element offset of A block (bb, t=0, jb)
+    int64_t astep;   // elements between consecutive t of the same block
+    int64_t vec0;    // element offset of (bb, t=0, jb*k + v) in (B,T,d)
+    int64_t vstep;   // = d
+};
+
+// lane = 32 * sub + K * (chain in the half-wave) + row
+template <int K, int C, int W>
+__device__ __forceinline__ Tile make_tile(const BlkArgs &a, int tile, bool reverse)
+{
+    Tile t;
+    t.lane = threadIdx.x & 63;
+    t.wv = threadIdx.x >> 6;
+    t.v = t.lane & (K - 1);
+    t.slot = t.lane & 31;
+    t.cgl = t.slot / K;
+    t.sub = t.lane >> 5;
+    t.q = t.wv * 2 + t.sub;
+    const int jr = tile / a.nCG;
+    t.cg = tile - jr * a.nCG;
+    t.j = reverse ? a.nT - 1 - jr : jr;
+    const int64_t chain = static_cast<int64_t>(t.cg) * (32 / K) + t.cgl;
+    t.cv = chain < a.nchain;
+    const int64_t cc = t.cv ? chain : 0;
+    t.bb = cc / a.nb;
+    t.jb = cc - t.bb * a.nb;
+    t.astep = static_cast<int64_t>(a.nb) * K * K;
+    t.blk0 = t.bb * a.T * a.nb + t.jb;
+    t.ablk0 = t.blk0 * K * K;
+    t.vstep = a.d;
+    t.vec0 = t.bb * a.T * a.d + t.jb * K + t.v;
+    t.t0 = t.j * (2 * W * C) + t.q * C;
+    return t;
+}
+
+__device__ __forceinline__ int clampT(int t, int T) { return t < T ? t : T - 1; }
+
+// h0 entry of this lane.  When the caller passes no h0, a.h0 points at a
+// zero region of the workspace, so the load is unconditional and never sits
+// behind a branch that would force a wait on the loads issued before it.
+// Lanes of chains past the end read chain 0's entry; their results are never
+// stored and their k-lane groups exchange data only among themselves.
+template <int K>
+__device__ __forceinline__ float load_h0(const BlkArgs &a, const Tile &tl)
+{
+    return a.h0[tl.bb * a.d + tl.jb * K + tl.v];
+}
+
+// ============================================ in-tile scan of chunk aggregates
+// Each half-wave holds the aggregate of one chunk q = 2 * wave + sub.  A
+// Kogge-Stone scan over the NCH chunks runs on all waves at once: in round r
+// every chunk composes its running composite with the one 2^r chunks before it
+// (DIR = +1) or after it (DIR = -1), read from one of two LDS buffers in turn,
+// with one barrier per round.  Afterwards chunk q holds the composite of
+// chunks 0..q (DIR = +1) or q..NCH-1 (DIR = -1), and a copy sits in buffer
+// ks_final<NCH>() for the fix-up.  The rule is the same in both directions:
+//     (M, v) o (M', v') = (M M', M v' + v)
+// with v absent (cumulative product), one value per lane (block-affine) or a
+// matrix row (cumulative-product backward).
+
+enum AggKind : int { kMat = 0, kMatVec = 1, kMatMat = 2 };
+
+template <int KIND, int K>
+struct AggShape {
+    static constexpr int words = KIND == kMat ? K : (KIND == kMatVec ? K + 1 : 2 * K);
+    static constexpr int stride = words | 1;   // odd LDS stride: lanes hit distinct banks
+};
+
+template <int NCH>
+__host__ __device__ constexpr int ks_final()
+{
+    int r = 0;
+    while ((1 << r) < NCH) ++r;
+    return r & 1;
+}
+
+template <int KIND, int K>
+__device__ __forceinline__ void compose_into(float *X, const float *R)
+{
+    using Rw = Rows<K>;
+    if constexpr (KIND == kMatVec) X[K] = Rw::mv(X, R[K], X[K]);
+    if constexpr (KIND == kMatMat) {
+        float nw[K];
+        Rw::mm(X, R + K, nw);
+#pragma unroll
+        for (int s = 0; s < K; ++s) X[K + s] += nw[s];
+    }
+    float np[K];
+    Rw::mm(X, R, np);
+#pragma unroll
+    for (int s = 0; s < K; ++s) X[s] = np[s];
+}
+
+template <int KIND, int K, int NCH>
+__device__ __forceinline__ void ks_store(float (*buf)[32][(AggShape<KIND, K>::stride)], int q, int slot, const float *X)
+{
+#pragma unroll
+    for (int e = 0; e < AggShape<KIND, K>::words; ++e) buf[q][slot][e] = X[e];
+}
+
+// Precondition: buffer 0 holds every chunk's aggregate and a barrier has passed.
+template <int KIND, int K, int NCH, int DIR>
+__device__ __forceinline__ void ks_scan(float (*buf)[NCH][32][(AggShape<KIND, K>::stride)], int q, int slot, float *X)
+{
+    constexpr int AW = AggShape<KIND, K>::words;
+#pragma unroll
+    for (int r = 0; (1 << r) < NCH; ++r) {
+        if (r > 0) {
+            ks_store<KIND, K, NCH>(buf[r & 1], q, slot, X);
+            __syncthreads();
+        }
+        const int qn = q - DIR * (1 << r);
+        if (qn >= 0 && qn < NCH) {
+            float R[AW];
+#pragma unroll
+            for (int e = 0; e < AW; ++e) R[e] = buf[r & 1][qn][slot][e];
+            compose_into<KIND, K>(X, R);
+        }
+    }
+    ks_store<KIND, K, NCH>(buf[ks_final<NCH>()], q, slot, X);
+}
+
+// ===================================================== Givens mesh in lanes
+// The angle-fused kernels form A_t = sigmoid(s_t) R(theta_t) in registers.  R is
+// the brick-wall mesh of 8 layers of 2 x 2 rotations (GivensMinGRU on the
+// minGRU home page; the Clements / EUNN mesh it cites): layer l rotates the
+// pairs (i, i+1), i = l mod 2, l mod 2 + 2, ..., R = L_7 .. L_0, angles in
+// (layer, pair) order, each rotation mapping (x_i, x_j) to
+// (c x_i - s x_j, s x_i + c x_j).  Lane p of a chain's 8 lanes loads angles
+// 4p..4p+3 (lane 7 none), and the chain shares their cosines and sines through
+// LDS, so every angle is loaded once and turned into sin / cos once.
+
+constexpr int kAngles = 28;
+
+__host__ __device__ constexpr int mesh_first(int l) { return (l / 2) * 7 + (l & 1) * 4; }
+
+// sin x and cos x for |x| up to a few thousand: Cody and Waite's reduction
+// x = q pi/2 + r with pi/2 split into a float head and tail (fused multiply-
+// adds keep q * head exact enough), |r| <= pi/4, then the Taylor series of sin
+// to r^9 and of cos to r^10 (truncation below 2e-9) and the quadrant's
+// swap / sign.  A few ulp, against the dozens of instructions (and a
+// large-argument path) of a general-range sincos.
+__device__ __forceinline__ void sincos_cw(float x, float &sn, float &cs)
+{
+    constexpr float kTwoOverPi = 0.636619772367581f;
+    constexpr float kPiHalfHi = 1.57079637050628662f;      // float(pi / 2)
+    constexpr float kPiHalfLo = -4.37113900018624e-08f;     // pi / 2 - kPiHalfHi
+    const float q = __builtin_rintf(x * kTwoOverPi);
+    float r = __builtin_fmaf(q, -kPiHalfHi, x);
+    r = __builtin_fmaf(q, -kPiHalfLo, r);
+    const float r2 = r * r;
+    float ps = __builtin_fmaf(r2, 1.0f / 362880.0f, -1.0f / 5040.0f);
+    ps = __builtin_fmaf(r2, ps, 1.0f / 120.0f);
+    ps = __builtin_fmaf(r2, ps, -1.0f / 6.0f);
+    const float sr = __builtin_fmaf(r * r2, ps, r);
+    float pc = __builtin_fmaf(r2, -1.0f / 3628800.0f, 1.0f / 40320.0f);
+    pc = __builtin_fmaf(r2, pc, -1.0f / 720.0f);
+    pc = __builtin_fmaf(r2, pc, 1.0f / 24.0f);
+    pc = __builtin_fmaf(r2, pc, -0.5f);
+    const float cr = __builtin_fmaf(r2, pc, 1.0f);
+    const int n = static_cast<int>(q);
+    const bool swap = (n & 1) != 0;
+    const float s0 = swap ? cr : sr, c0 = swap ? sr : cr;
+    sn = (n & 2) ? -s0 : s0;
+    cs = ((n + 1) & 2) ? -c0 : c0;
+}
+
+// cosines and sines of a chain's 28 angles in every lane of the chain
+__device__ __forceinline__ void mesh_share(float4 th, float (*cs)[8], int lane, float (&cc)[kAngles],
+                                           float (&ss)[kAngles])
+{
+    // within a few ulp (the hardware's native sin / cos lose ~1e-6 absolute,
+    // which the 28 rotations and the scan then carry)
+    float4 c4, s4;
+    sincos_cw(th.x, s4.x, c4.x);
+    sincos_cw(th.y, s4.y, c4.y);
+    sincos_cw(th.z, s4.z, c4.z);
+    sincos_cw(th.w, s4.w, c4.w);
+    *reinterpret_cast<float4 *>(&cs[lane][0]) = c4;
+    *reinterpret_cast<float4 *>(&cs[lane][4]) = s4;
+    const int base = lane & ~7;
+#pragma unroll
+    for (int p = 0; p < 7; ++p) {
+        const float4 c = *reinterpret_cast<const float4 *>(&cs[base + p][0]);
+        const float4 s = *reinterpret_cast<const float4 *>(&cs[base + p][4]);
+        cc[4 * p] = c.x; cc[4 * p + 1] = c.y; cc[4 * p + 2] = c.z; cc[4 * p + 3] = c.w;
+        ss[4 * p] = s.x; ss[4 * p + 1] = s.y; ss[4 * p + 2] = s.z; ss[4 * p + 3] = s.w;
+    }
+}
+
+// row v of R in natural column order: e_v^T L_7 .. L_0
+__device__ __forceinline__ void mesh_row(const float (&cc)[kAngles], const float (&ss)[kAngles], int v, float (&r)[8])
+{
+#pragma unroll
+    for (int c = 0; c < 8; ++c) r[c] = (c == v) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int l = 7; l >= 0; --l)
+#pragma unroll
+        for (int i = l & 1, a = mesh_first(l); i + 1 < 8; i += 2, ++a) {
+            const float ri = r[i], rj = r[i + 1];
+            r[i] = cc[a] * ri + ss[a] * rj;
+            r[i + 1] = cc[a] * rj - ss[a] * ri;
+        }
+}
+
+// column v of R in natural row order: L_7 .. L_0 e_v
+__device__ __forceinline__ void mesh_col(const float (&cc)[kAngles], const float (&ss)[kAngles], int v, float (&y)[8])
+{
+#pragma unroll
+    for (int r = 0; r < 8; ++r) y[r] = (r == v) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int l = 0; l < 8; ++l)
+#pragma unroll
+        for (int i = l & 1, a = mesh_first(l); i + 1 < 8; i += 2, ++a) {
+            const float yi = y[i], yj = y[i + 1];
+            y[i] = cc[a] * yi - ss[a] * yj;
+            y[i + 1] = ss[a] * yi + cc[a] * yj;
+        }
+}
+
+// Reverse pass through mesh_col: y is the built column, dy the gradient on it;
+// writes d(column)/d(angle) contracted with dy into part.  Each layer is undone
+// by its inverse rotation, so no intermediate column is stored.
+__device__ __forceinline__ void mesh_col_adjoint(const float (&cc)[kAngles], const float (&ss)[kAngles],
+                                                 float (&y)[8], float (&dy)[8], float (&part)[kAngles])
+{
+#pragma unroll
+    for (int l = 7; l >= 0; --l)
+#pragma unroll
+        for (int i = l & 1, a = mesh_first(l); i + 1 < 8; i += 2, ++a) {
+            const float yi = y[i], yj = y[i + 1], gi = dy[i], gj = dy[i + 1];
+            part[a] = gj * yi - gi * yj;
+            y[i] = cc[a] * yi + ss[a] * yj;
+            y[i + 1] = cc[a] * yj - ss[a] * yi;
+            dy[i] = cc[a] * gi + ss[a] * gj;
+            dy[i + 1] = cc[a] * gj - ss[a] * gi;
+        }
+}
+
+// natural order <-> this lane's rotated slots (slot s holds entry s ^ (v & 4)).
+// Written as a bitwise blend of two fixed-index registers: a select between
+// x[s] and x[s ^ 4] would be folded into a lane-dependent index, which sends
+// the array to scratch memory.
+__device__ __forceinline__ float blend(float a, float b, int mask)
+{
+    return __int_as_float((__float_as_int(b) & mask) | (__float_as_int(a) & ~mask));
+}
+
+__device__ __forceinline__ void to_slots(const float (&x)[8], int v, float scale, float *y)
+{
+    const int m = -((v >> 2) & 1);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) y[s] = scale * blend(x[s], x[s ^ 4], m);
+}
+
+__device__ __forceinline__ void from_slots(const float *x, int v, float scale, float (&y)[8])
+{
+    const int m = -((v >> 2) & 1);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) y[s] = scale * blend(x[s], x[s ^ 4], m);
+}
+
+__device__ __forceinline__ float sigmoidf_(float u) { return 1.0f / (1.0f + __expf(-u)); }
+
+// Pins eight values in registers at this point of the program: work that
+// produces them cannot sink below it, so one step's 56 cosines and sines are
+// dead before the next step's are loaded (with a scheduling barrier after it).
+__device__ __forceinline__ void settle8(float *x)
+{
+    asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                 "+v"(x[7]));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// angle slice and gate of this lane's chain at step t (indices clamped in range)
+__device__ __forceinline__ float4 load_angles(const BlkArgs &a, const Tile &tl, int t)
+{
+    const int64_t blk = tl.blk0 + static_cast<int64_t>(t) * a.nb;
+    return *reinterpret_cast<const float4 *>(a.theta + blk * kAngles + 4 * min(tl.v, 6));
+}
+
+// ============================================ block-affine carry phases
+// Shared by the kernels that load A and the kernels that form it from angles.
+
+// Forward: X = (row of Phi, entry of u) is the chunk's aggregate.  Stores it,
+// scans the tile's chunks, runs the look-back (multi-tile launches) and
+// returns the state entering this lane's chunk.
+template <int K, int C, int W, bool MULTI>
+__device__ __forceinline__ float affine_fwd_carry(const BlkArgs &a, const Tile &tl, int ftile, unsigned long long ep,
+                                                  float (&X)[K + 1], float xh0,
+                                                  float (&sKS)[2][2 * W][32][(AggShape<kMatVec, K>::stride)],
+                                                  float (&sCarry)[32], uint32_t (&sTicket)[2])
+{
+    constexpr int NCH = 2 * W;
+    using S = AggShape<kMatVec, K>;
+    using Rw = Rows<K>;
+    constexpr int FIN = ks_final<NCH>();
+    ks_store<kMatVec, K, NCH>(sKS[0], tl.q, tl.slot, X);
+    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
+    __syncthreads();
+    const uint32_t tag = sTicket[0];
+
+    float x;
+    if constexpr (MULTI) {
+        ks_scan<kMatVec, K, NCH, +1>(sKS, tl.q, tl.slot, X);
+        // the last wave's upper half holds the tile aggregate and runs the look-back
+        if (tl.wv == W - 1) {
+            const bool owner = tl.sub == 1;
+            if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<S::words>(a.agg, ftile, tl.slot, tag, X);
+            float xin = xh0;
+            if (tl.j > 0) {
+                float xi[1];
+                const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, tag, &a.hd->err, xi);
+                if (ps >= 0) xin = xi[0];
+                constexpr int NB = K >= 16 ? 2 : 4;
+                for (int p = ps + 1; p < tl.j; p += NB) {
+                    const int cnt = min(NB, tl.j - p);
+                    float ag[NB][S::words];
+                    load_aggregates<S::words, NB>(a.agg, p, +1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
+#pragma unroll
+                    for (int u = 0; u < NB; ++u)
+                        if (u < cnt) xin = Rw::mv(ag[u], xin, ag[u][K]);
+                }
+            }
+            if (owner && tl.j < a.nT - 1) {
+                const float xo = Rw::mv(X, xin, X[K]);
+                publish<1>(a.incl, ftile, tl.slot, tag, &xo);
+            }
+            if (owner) sCarry[tl.slot] = xin;
+        }
+        __syncthreads();
+        x = sCarry[tl.slot];
+        if (tl.q > 0) x = Rw::mv(sKS[FIN][tl.q - 1][tl.slot], x, sKS[FIN][tl.q - 1][tl.slot][K]);
+    } else {
+        x = xh0;
+        for (int q = 0; q < tl.q; ++q) x = Rw::mv(sKS[0][q][tl.slot], x, sKS[0][q][tl.slot][K]);
+    }
+    return x;
+}
+
+// Backward: X = (row of Psi, entry of Wl) is the chunk's reverse aggregate.
+// Returns w entering this lane's chunk from its end.
+template <int K, int C, int W, bool MULTI>
+__device__ __forceinline__ float affine_bwd_carry(const BlkArgs &a, const Tile &tl, int ftile, unsigned long long ep,
+                                                  float (&X)[K + 1],
+                                                  float (&sKS)[2][2 * W][32][(AggShape<kMatVec, K>::stride)],
+                                                  float (&sCarry)[32], uint32_t (&sTicket)[2])
+{
+    constexpr int NCH = 2 * W;
+    using S = AggShape<kMatVec, K>;
+    using Rw = Rows<K>;
+    constexpr int FIN = ks_final<NCH>();
+    ks_store<kMatVec, K, NCH>(sKS[0], tl.q, tl.slot, X);
+    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
+    __syncthreads();
+    const uint32_t tag = sTicket[0];
+
+    float w;
+    if constexpr (MULTI) {
+        ks_scan<kMatVec, K, NCH, -1>(sKS, tl.q, tl.slot, X);
+        // wave 0's lower half holds the tile aggregate and runs the look-back
+        if (tl.wv == 0) {
+            const bool owner = tl.sub == 0;
+            if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<S::words>(a.agg, ftile, tl.slot, tag, X);
+            float win = 0.0f;
+            if (tl.j < a.nT - 1) {
+                float xi[1];
+                const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, tag, &a.hd->err, xi);
+                int pend = a.nT;
+                if (ps >= 0) { win = xi[0]; pend = ps; }
+                constexpr int NB = K >= 16 ? 2 : 4;
+                for (int p = pend - 1; p > tl.j; p -= NB) {
+                    const int cnt = min(NB, p - tl.j);
+                    float ag[NB][S::words];
+                    load_aggregates<S::words, NB>(a.agg, p, -1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
+#pragma unroll
+                    for (int u = 0; u < NB; ++u)
+                        if (u < cnt) win = Rw::mv(ag[u], win, ag[u][K]);
+                }
+            }
+            if (owner && tl.j > 0) {
+                const float wo = Rw::mv(X, win, X[K]);
+                publish<1>(a.incl, ftile, tl.slot, tag, &wo);
+            }
+            if (owner) sCarry[tl.slot] = win;
+        }
+        __syncthreads();
+        w = sCarry[tl.slot];
+        if (tl.q < NCH - 1) w = Rw::mv(sKS[FIN][tl.q + 1][tl.slot], w, sKS[FIN][tl.q + 1][tl.slot][K]);
+    } else {
+        w = 0.0f;
+        for (int q = NCH - 1; q > tl.q; --q) w = Rw::mv(sKS[0][q][tl.slot], w, sKS[0][q][tl.slot][K]);
+    }
+    return w;
+}
+
+// ======================================================= block-affine fwd
+// GIV = false: A_t is loaded; GIV = true: A_t = sigmoid(s_t) R(theta_t) is
+// formed from the angles and the gate (the Givens angle-fused scan).
+
+template <int K, bool GIV, int C, int W, bool MULTI>
+__device__ __forceinline__ void affine_fwd_body(const BlkArgs &a)
+{
+    static_assert(!GIV || K == 8, "the Givens angle-fused scan is built for k = 8");
+    constexpr int NCH = 2 * W;
+    using Rw = Rows<K>;
+    __shared__ float sKS[2][NCH][32][(AggShape<kMatVec, K>::stride)];
+    __shared__ float sCarry[32];
+    __shared__ uint32_t sTicket[2];
+    __shared__ float sCS[GIV ? W : 1][64][8];
+
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
+    const Tile tl = make_tile<K, C, W>(a, tile, false);
+    const int ftile = tl.j * a.nCG + tl.cg;
+
+    // unconditional (clamped) loads keep every load in flight at once
+    float Ar[C][K], bv[C];
+    if constexpr (!GIV) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int t = clampT(tl.t0 + i, a.T);
+            Rw::load_row(a.A + tl.ablk0 + t * tl.astep, tl.v, Ar[i]);
+            bv[i] = a.x[tl.vec0 + t * tl.vstep];
+        }
+    } else {
+        float4 th[C];
+        float sv[C];
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int t = clampT(tl.t0 + i, a.T);
+            th[i] = load_angles(a, tl, t);
+            sv[i] = a.sg[tl.blk0 + static_cast<int64_t>(t) * a.nb];
+            bv[i] = a.x[tl.vec0 + t * tl.vstep];
+        }
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            float cc[kAngles], ss[kAngles], r[8];
+            mesh_share(th[i], sCS[tl.wv % (GIV ? W : 1)], tl.lane, cc, ss);
+            mesh_row(cc, ss, tl.v, r);
+            to_slots(r, tl.v, sigmoidf_(sv[i]), Ar[i]);
+            settle8(Ar[i]);
+        }
+    }
+    const float xh0 = load_h0<K>(a, tl);
+#pragma unroll
+    for (int i = 0; i < C; ++i)
+        if (!(tl.cv && tl.t0 + i < a.T)) {
+            Rw::eye(tl.v, Ar[i]);
+            bv[i] = 0.0f;
+        }
+
+    // chunk aggregate from a zero state: X = (A_e..A_s, local h_e)
+    float X[K + 1];
+#pragma unroll
+    for (int s = 0; s < K; ++s) X[s] = Ar[0][s];
+    X[K] = bv[0];
+#pragma unroll
+    for (int i = 1; i < C; ++i) {
+        float np[K];
+        Rw::mm(Ar[i], X, np);
+        X[K] = Rw::mv(Ar[i], X[K], bv[i]);
+#pragma unroll
+        for (int s = 0; s < K; ++s) X[s] = np[s];
+    }
+    float x = affine_fwd_carry<K, C, W, MULTI>(a, tl, ftile, ep, X, xh0, sKS, sCarry, sTicket);
+
+    // re-run the recurrence from the true state entering the chunk
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        x = Rw::mv(Ar[i], x, bv[i]);
+        const int t = tl.t0 + i;
+        if (tl.cv && t < a.T) a.out[tl.vec0 + t * tl.vstep] = x;
+    }
+}
+
+template <int K, int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
+{
+    affine_fwd_body<K, false, C, W, MULTI>(a);
+}
+
+template <int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) bgivens_fwd_kernel(BlkArgs a)
+{
+    affine_fwd_body<8, true, C, W, MULTI>(a);
+}
+
+// ======================================================= block-affine bwd
+// Reverse scan on w_t = A_t^T g_t with g_t = dh_t + w_{t+1}; per chunk [s, e]
+// w_s = Psi w_{e+1} + Wl with Psi = A_s^T .. A_e^T.
+
+template <int K, int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
+{
+    constexpr int NCH = 2 * W;
+    using Rw = Rows<K>;
+    __shared__ float sKS[2][NCH][32][(AggShape<kMatVec, K>::stride)];
+    __shared__ float sCarry[32];
+    __shared__ uint32_t sTicket[2];
+
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
+    const Tile tl = make_tile<K, C, W>(a, tile, true);
+    const int ftile = tl.j * a.nCG + tl.cg;
+
+    float ATr[C][K], gv[C], hp[C];   // rows of A_t^T, upstream dh_t, h_{t-1}
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = clampT(tl.t0 + i, a.T);
+        Rw::load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
+        gv[i] = a.y[tl.vec0 + t * tl.vstep];
+        hp[i] = a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep];
+    }
+    const float xh0 = load_h0<K>(a, tl);
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = tl.t0 + i;
+        if (t == 0) hp[i] = xh0;
+        if (!(tl.cv && t < a.T)) {
+            Rw::eye(tl.v, ATr[i]);
+            gv[i] = 0.0f;
+            hp[i] = 0.0f;
+        }
+    }
+
+    // chunk aggregate from a zero carry, walking t downwards: X = (Psi, Wl)
+    float X[K + 1];
+#pragma unroll
+    for (int s = 0; s < K; ++s) X[s] = ATr[C - 1][s];
+    X[K] = Rw::mv(ATr[C - 1], gv[C - 1], 0.0f);
+#pragma unroll
+    for (int i = C - 2; i >= 0; --i) {
+        float np[K];
+        Rw::mm(ATr[i], X, np);
+        X[K] = Rw::mv(ATr[i], gv[i] + X[K], 0.0f);
+#pragma unroll
+        for (int s = 0; s < K; ++s) X[s] = np[s];
+    }
+    float w = affine_bwd_carry<K, C, W, MULTI>(a, tl, ftile, ep, X, sKS, sCarry, sTicket);
+
+    // re-run the reverse recurrence from the true carry; emit dA, db, dh0
+#pragma unroll
+    for (int i = C - 1; i >= 0; --i) {
+        const float g = gv[i] + w;
+        float dAr[K];
+        Rw::outer(g, hp[i], dAr);
+        w = Rw::mv(ATr[i], g, 0.0f);
+        const int t = tl.t0 + i;
+        if (tl.cv && t < a.T) {
+            a.out2[tl.vec0 + t * tl.vstep] = g;
+            Rw::store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, dAr);
+        }
+    }
+    if (tl.cv && tl.t0 == 0) a.out3[tl.bb * a.d + tl.jb * K + tl.v] = w;   // A_1^T g_1
+}
+
+// =============================================== Givens angle-fused bwd
+// Same reverse scan with A_t = sigmoid(s_t) R(theta_t) formed in registers
+// (unscaled columns of R, the gate applied as a scalar).  dA_t = g_t h_{t-1}^T
+// is never formed as a tensor: lane v holds column v of it, contracts it with
+// the derivative of column v of A (the reverse pass through the mesh) and with
+// column v of R (for the gate), and the chain's 8 lanes add their shares in LDS:
+//     dtheta_t = sigmoid(s_t) <dA_t, dR/dtheta>,  ds_t = sigmoid'(s_t) <dA_t, R>.
+
+template <int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
+{
+    constexpr int NCH = 2 * W;
+    constexpr int PW = 32;   // words per lane in the reduction buffer: 28 angles, the gate, padding
+    __shared__ float sKS[2][NCH][32][(AggShape<kMatVec, 8>::stride)];
+    __shared__ float sCarry[32];
+    __shared__ uint32_t sTicket[2];
+    __shared__ float sCS[W][64][8];
+    __shared__ float sPart[W][64][PW];
+
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
+    const Tile tl = make_tile<8, C, W>(a, tile, true);
+    const int ftile = tl.j * a.nCG + tl.cg;
+
+    float4 th[C];
+    float RTr[C][8], sig[C], gv[C], hp[C];   // rows of R^T (unscaled), gate, dh_t, h_{t-1}
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = clampT(tl.t0 + i, a.T);
+        th[i] = load_angles(a, tl, t);
+        sig[i] = a.sg[tl.blk0 + static_cast<int64_t>(t) * a.nb];
+        gv[i] = a.y[tl.vec0 + t * tl.vstep];
+        hp[i] = a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep];
+    }
+    const float xh0 = load_h0<8>(a, tl);
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        float cc[kAngles], ss[kAngles], y[8];
+        mesh_share(th[i], sCS[tl.wv], tl.lane, cc, ss);
+        mesh_col(cc, ss, tl.v, y);
+        to_slots(y, tl.v, 1.0f, RTr[i]);
+        sig[i] = sigmoidf_(sig[i]);
+        settle8(RTr[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = tl.t0 + i;
+        if (t == 0) hp[i] = xh0;
+        if (!(tl.cv && t < a.T)) {
+            eye_row8(tl.v, RTr[i]);
+            sig[i] = 1.0f;
+            gv[i] = 0.0f;
+            hp[i] = 0.0f;
+        }
+    }
+
+    // chunk aggregate from a zero carry, walking t downwards: X = (Psi, Wl)
+    float X[9];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) X[s] = sig[C - 1] * RTr[C - 1][s];
+    X[8] = sig[C - 1] * mv8(RTr[C - 1], gv[C - 1], 0.0f);
+#pragma unroll
+    for (int i = C - 2; i >= 0; --i) {
+        float np[8];
+        mm8(RTr[i], X, np);
+        X[8] = sig[i] * mv8(RTr[i], gv[i] + X[8], 0.0f);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) X[s] = sig[i] * np[s];
+    }
+    float w = affine_bwd_carry<8, C, W, MULTI>(a, tl, ftile, ep, X, sKS, sCarry, sTicket);
+
+    float (*part)[PW] = sPart[tl.wv];
+    const int base = tl.lane & ~7;
+    // the angles are read again here (an L2 hit) rather than kept in registers
+    // since the build; one step ahead
+    float4 thn = load_angles(a, tl, clampT(tl.t0 + C - 1, a.T));
+#pragma unroll
+    for (int i = C - 1; i >= 0; --i) {
+        const float4 thc = thn;
+        if (i > 0) thn = load_angles(a, tl, clampT(tl.t0 + i - 1, a.T));
+        const float g = gv[i] + w;
+        float dAc[8];
+        outer8(hp[i], g, dAc);              // column v of dA_t = g_t h_{t-1}^T (rotated slots)
+        w = sig[i] * mv8(RTr[i], g, 0.0f);  // A_t^T g_t
+        // lane v's share of dtheta_t and ds_t, through column v of A_t
+        float cc[kAngles], ss[kAngles], y[8], dy[8], pt[kAngles];
+        mesh_share(thc, sCS[tl.wv], tl.lane, cc, ss);
+        from_slots(RTr[i], tl.v, 1.0f, y);
+        from_slots(dAc, tl.v, sig[i], dy);
+        float gate = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) gate += dy[r] * y[r];
+        mesh_col_adjoint(cc, ss, y, dy, pt);
+#pragma unroll
+        for (int q = 0; q < 7; ++q)
+            *reinterpret_cast<float4 *>(&part[tl.lane][4 * q]) =
+                make_float4(pt[4 * q], pt[4 * q + 1], pt[4 * q + 2], pt[4 * q + 3]);
+        *reinterpret_cast<float4 *>(&part[tl.lane][28]) = make_float4((1.0f - sig[i]) * gate, 0.0f, 0.0f, 0.0f);
+        // lane v (< 7) adds up angles 4v..4v+3 over the chain; lane 7 the gate
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const float4 u = *reinterpret_cast<const float4 *>(&part[base + p][4 * tl.v]);
+            acc.x += u.x; acc.y += u.y; acc.z += u.z; acc.w += u.w;
+        }
+        const int t = tl.t0 + i;
+        if (tl.cv && t < a.T) {
+            const int64_t blk = tl.blk0 + static_cast<int64_t>(t) * a.nb;
+            a.out2[tl.vec0 + t * tl.vstep] = g;
+            if (tl.v < 7)
+                *reinterpret_cast<float4 *>(a.dtheta + blk * kAngles + 4 * tl.v) = acc;
+            else
+                a.dsg[blk] = acc.x;
+        }
+        asm volatile("" : "+v"(w));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (tl.cv && tl.t0 == 0) a.out3[tl.bb * a.d + tl.jb * 8 + tl.v] = w;   // A_1^T g_1
+}
+
+// ================================================ block cumulative product
+
+template <int K, int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
+{
+    constexpr int NCH = 2 * W;
+    using S = AggShape<kMat, K>;
+    using Rw = Rows<K>;
+    constexpr int FIN = ks_final<NCH>();
+    __shared__ float sKS[2][NCH][32][S::stride];
+    __shared__ float sCarry[32][K];
+    __shared__ uint32_t sTicket[2];
+
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
+    const Tile tl = make_tile<K, C, W>(a, tile, false);
+    const int ftile = tl.j * a.nCG + tl.cg;
+
+    float Ar[C][K];
+#pragma unroll
+    for (int i = 0; i < C; ++i)
+        Rw::load_row(a.A + tl.ablk0 + clampT(tl.t0 + i, a.T) * tl.astep, tl.v, Ar[i]);
+#pragma unroll
+    for (int i = 0; i < C; ++i)
+        if (!(tl.cv && tl.t0 + i < a.T)) Rw::eye(tl.v, Ar[i]);
+
+    float X[K];
+#pragma unroll
+    for (int s = 0; s < K; ++s) X[s] = Ar[0][s];
+#pragma unroll
+    for (int i = 1; i < C; ++i) {
+        float np[K];
+        Rw::mm(Ar[i], X, np);
+#pragma unroll
+        for (int s = 0; s < K; ++s) X[s] = np[s];
+    }
+    ks_store<kMat, K, NCH>(sKS[0], tl.q, tl.slot, X);
+    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
+    __syncthreads();
+    const uint32_t tag = sTicket[0];
+
+    ks_scan<kMat, K, NCH, +1>(sKS, tl.q, tl.slot, X);   // X = composite of chunks 0..q
+    if constexpr (MULTI) {
+        // the last wave's upper half holds the tile aggregate and runs the look-back
+        if (tl.wv == W - 1) {
+            const bool owner = tl.sub == 1;
+            if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<K>(a.agg, ftile, tl.slot, tag, X);
+            float Pin[K];
+            Rw::eye(tl.v, Pin);
+            if (tl.j > 0) {
+                float xi[K];
+                const int ps = find_inclusive<K>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, tag, &a.hd->err, xi);
+                if (ps >= 0) {
+#pragma unroll
+                    for (int s = 0; s < K; ++s) Pin[s] = xi[s];
+                }
+                constexpr int NB = K >= 16 ? 2 : 4;
+                for (int p = ps + 1; p < tl.j; p += NB) {
+                    const int cnt = min(NB, tl.j - p);
+                    float ag[NB][K];
+                    load_aggregates<K, NB>(a.agg, p, +1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
+#pragma unroll
+                    for (int u = 0; u < NB; ++u)
+                        if (u < cnt) {
+                            float np[K];
+                            Rw::mm(ag[u], Pin, np);
+#pragma unroll
+                            for (int s = 0; s < K; ++s) Pin[s] = np[s];
+                        }
+                }
+            }
+            if (owner && tl.j < a.nT - 1) {
+                float Po[K];
+                Rw::mm(X, Pin, Po);
+                publish<K>(a.incl, ftile, tl.slot, tag, Po);
+            }
+            if (owner) {
+#pragma unroll
+                for (int s = 0; s < K; ++s) sCarry[tl.slot][s] = Pin[s];
+            }
+        }
+    }
+    __syncthreads();
+    // state entering the chunk: (composite of chunks 0..q-1) x (tile carry-in)
+    float P[K];
+    if constexpr (MULTI) {
+#pragma unroll
+        for (int s = 0; s < K; ++s) P[s] = sCarry[tl.slot][s];
+        if (tl.q > 0) {
+            float np[K];
+            Rw::mm(sKS[FIN][tl.q - 1][tl.slot], P, np);
+#pragma unroll
+            for (int s = 0; s < K; ++s) P[s] = np[s];
+        }
+    } else {
+        Rw::eye(tl.v, P);
+        if (tl.q > 0) {
+#pragma unroll
+            for (int s = 0; s < K; ++s) P[s] = sKS[FIN][tl.q - 1][tl.slot][s];
+        }
+    }
+    // the state entering this chunk, for the backward's recompute (slot order kept)
+    store_vec<K>(a.pstate + ((static_cast<size_t>(ftile) * NCH + tl.q) * 32 + tl.slot) * K, P);
+    if (a.out == nullptr) return;   // states only (requested by a backward)
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        float np[K];
+        Rw::mm(Ar[i], P, np);
+#pragma unroll
+        for (int s = 0; s < K; ++s) P[s] = np[s];
+        const int t = tl.t0 + i;
+        if (tl.cv && t < a.T) Rw::store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, P);
+    }
+}
+
+// Backward: W_t = A_t^T G_t with G_t = dP_t + W_{t+1}; per chunk [s, e]
+// W_s = Psi W_{e+1} + Wl.  dA_t = G_t P_{t-1}^T, with P_{t-1} recomputed from
+// the state entering the chunk (stored by the forward) and the A_t in hand.
+template <int K, int C, int W, bool MULTI>
+__global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
+{
+    constexpr int NCH = 2 * W;
+    using S = AggShape<kMatMat, K>;
+    using Rw = Rows<K>;
+    constexpr int FIN = ks_final<NCH>();
+    __shared__ float sKS[2][NCH][32][S::stride];
+    __shared__ float sCarry[32][K];
+    __shared__ uint32_t sTicket[2];
+
+    const int tile = blockIdx.x;
+    unsigned long long ep = 0;
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
+    const Tile tl = make_tile<K, C, W>(a, tile, true);
+    const int ftile = tl.j * a.nCG + tl.cg;
+
+    float ATr[C][K], Gr[C][K];   // rows of A_t^T, dP_t
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int t = clampT(tl.t0 + i, a.T);
+        Rw::load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
+        Rw::load_row(a.y + tl.ablk0 + t * tl.astep, tl.v, Gr[i]);
+    }
+    // row v of P_{s-1}^T (column v of the state entering the chunk), saved by
+    // the forward in its slot order: row m of P sits in lane m's slots, column
+    // c of it at slot col(m, c)
+    float PT[C][K];
+    {
+        const float *ps = a.pstate + ((static_cast<size_t>(ftile) * NCH + tl.q) * 32 + (tl.slot & ~(K - 1))) * K;
+#pragma unroll
+        for (int s = 0; s < K; ++s) {
+            const int m = Rw::col(tl.v, s);
+            PT[0][s] = ps[m * K + Rw::col(m, tl.v)];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        if (!(tl.cv && tl.t0 + i < a.T)) {
+            Rw::eye(tl.v, ATr[i]);
+#pragma unroll
+            for (int s = 0; s < K; ++s) Gr[i][s] = 0.0f;
+        }
+    }
+
+    // chunk aggregate from a zero carry: X = (Psi, Wl)
+    float X[S::words];
+#pragma unroll
+    for (int s = 0; s < K; ++s) X[s] = ATr[C - 1][s];
+    Rw::mm(ATr[C - 1], Gr[C - 1], X + K);
+#pragma unroll
+    for (int i = C - 2; i >= 0; --i) {
+        float np[K], gw[K], nw[K];
+        Rw::mm(ATr[i], X, np);
+#pragma unroll
+        for (int s = 0; s < K; ++s) gw[s] = Gr[i][s] + X[K + s];
+        Rw::mm(ATr[i], gw, nw);
+#pragma unroll
+        for (int s = 0; s < K; ++s) { X[s] = np[s]; X[K + s] = nw[s]; }
+    }
+    ks_store<kMatMat, K, NCH>(sKS[0], tl.q, tl.slot, X);
+    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
+    __syncthreads();
+    const uint32_t tag = sTicket[0];
+
+    ks_scan<kMatMat, K, NCH, -1>(sKS, tl.q, tl.slot, X);   // X = composite of chunks q..NCH-1
+    // wave 0's lower half holds the tile aggregate and runs the look-back; the
+    // other waves meanwhile recompute P_{t-1}^T = P_{t-2}^T A_{t-1}^T
+    const bool lb_wave = MULTI && tl.wv == 0;
+    if (lb_wave) {
+        const bool owner = tl.sub == 0;
+        if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<S::words>(a.agg, ftile, tl.slot, tag, X);
+        float Win[K];
+#pragma unroll
+        for (int s = 0; s < K; ++s) Win[s] = 0.0f;
+        if (tl.j < a.nT - 1) {
+            float xi[K];
+            const int ps = find_inclusive<K>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, tag, &a.hd->err, xi);
+            int pend = a.nT;
+            if (ps >= 0) {
+                pend = ps;
+#pragma unroll
+                for (int s = 0; s < K; ++s) Win[s] = xi[s];
+            }
+            constexpr int NB = K >= 16 ? 1 : 2;
+            for (int p = pend - 1; p > tl.j; p -= NB) {
+                const int cnt = min(NB, p - tl.j);
+                float ag[NB][S::words];
+                load_aggregates<S::words, NB>(a.agg, p, -1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
+#pragma unroll
+                for (int u = 0; u < NB; ++u)
+                    if (u < cnt) {
+                        float np[K];
+                        Rw::mm(ag[u], Win, np);
+#pragma unroll
+                        for (int s = 0; s < K; ++s) Win[s] = np[s] + ag[u][K + s];
+                    }
+            }
+        }
+        if (owner && tl.j > 0) {
+            float Wo[K];
+            Rw::mm(X, Win, Wo);
+#pragma unroll
+            for (int s = 0; s < K; ++s) Wo[s] += X[K + s];
+            publish<K>(a.incl, ftile, tl.slot, tag, Wo);
+        }
+        if (owner) {
+#pragma unroll
+            for (int s = 0; s < K; ++s) sCarry[tl.slot][s] = Win[s];
+        }
+    } else {
+#pragma unroll
+        for (int i = 1; i < C; ++i) Rw::mm(PT[i - 1], ATr[i - 1], PT[i]);
+    }
+    __syncthreads();
+    if (lb_wave) {
+#pragma unroll
+        for (int i = 1; i < C; ++i) Rw::mm(PT[i - 1], ATr[i - 1], PT[i]);
+    }
+    // carry entering the chunk from its end: (composite of chunks q+1..) x (tile carry-in)
+    float Wc[K];
+    if constexpr (MULTI) {
+#pragma unroll
+        for (int s = 0; s < K; ++s) Wc[s] = sCarry[tl.slot][s];
+        if (tl.q < NCH - 1) {
+            float np[K];
+            Rw::mm(sKS[FIN][tl.q + 1][tl.slot], Wc, np);
+#pragma unroll
+            for (int s = 0; s < K; ++s) Wc[s] = np[s] + sKS[FIN][tl.q + 1][tl.slot][K + s];
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < K; ++s) Wc[s] = tl.q < NCH - 1 ? sKS[FIN][tl.q + 1][tl.slot][K + s] : 0.0f;
+    }
+
+#pragma unroll
+    for (int i = C - 1; i >= 0; --i) {
+        const int t = tl.t0 + i;
+        const bool valid = tl.cv && t < a.T;
+        float G[K], dAr[K], nw[K];
+#pragma unroll
+        for (int s = 0; s < K; ++s) G[s] = Gr[i][s] + Wc[s];
+        Rw::mm(G, PT[i], dAr);           // dA_t = G_t P_{t-1}^T
+        Rw::mm(ATr[i], G, nw);
+#pragma unroll
+        for (int s = 0; s < K; ++s) Wc[s] = nw[s];
+        if (valid) Rw::store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, dAr);
+    }
+}
+
+// ------------------------------------------------------------ launchers
+
+// NAME<K, W, MAXC>(g, a, s) launches KERNEL<K, C, W, MULTI> for the
+// geometry's chunk length C (<= MAXC), multi-tile or single-tile.
+#define MGS_DEFINE_BLOCK_LAUNCHER(NAME, KERNEL)                                                   \
+    template <int K, int W, int C>                                                                \
+    void NAME##_c(const BlockGeom &g, const BlkArgs &a, hipStream_t s)                            \
+    {                                                                                             \
+        if (g.nT > 1)                                                                             \
+            hipLaunchKernelGGL((KERNEL<K, C, W, true>), dim3(g.nTiles), dim3(64 * W), 0, s, a);   \
+        else                                                                                      \
+            hipLaunchKernelGGL((KERNEL<K, C, W, false>), dim3(g.nTiles), dim3(64 * W), 0, s, a);  \
+    }                                                                                             \
+    template <int K, int W, int MAXC>                                                             \
+    void NAME(const BlockGeom &g, const BlkArgs &a, hipStream_t s)                                \
+    {                                                                                             \
+        switch (g.C) {                                                                            \
+        case 1: NAME##_c<K, W, 1>(g, a, s); break;                                                \
+        case 2: if constexpr (MAXC >= 2) NAME##_c<K, W, 2>(g, a, s); break;                       \
+        case 4: if constexpr (MAXC >= 4) NAME##_c<K, W, 4>(g, a, s); break;                       \
+        case 8: if constexpr (MAXC >= 8) NAME##_c<K, W, 8>(g, a, s); break;                       \
+        default: if constexpr (MAXC >= 16) NAME##_c<K, W, 16>(g, a, s); break;                    \
+        }                                                                                         \
+    }
+
+MGS_DEFINE_BLOCK_LAUNCHER(launch_baffine_fwd, baffine_fwd_kernel)
+MGS_DEFINE_BLOCK_LAUNCHER(launch_baffine_bwd, baffine_bwd_kernel)
+MGS_DEFINE_BLOCK_LAUNCHER(launch_bmatrix_fwd, bmatrix_fwd_kernel)
+MGS_DEFINE_BLOCK_LAUNCHER(launch_bmatrix_bwd, bmatrix_bwd_kernel)
+
+template <int K>
+void launch_blk_impl(BlkOp op, const BlockGeom &g, const BlkArgs &a, hipStream_t s)
+{
+    constexpr BlkShape af = affine_shape(K);
+    constexpr BlkShape mt = matrix_shape(K);
+    switch (op) {
+    case BlkOp::AffineFwd: launch_baffine_fwd<K, af.W, af.max_c>(g, a, s); break;
+    case BlkOp::AffineBwd: launch_baffine_bwd<K, af.W, af.max_c>(g, a, s); break;
+    case BlkOp::MatrixFwd: launch_bmatrix_fwd<K, mt.W, mt.max_c>(g, a, s); break;
+    case BlkOp::MatrixBwd: launch_bmatrix_bwd<K, mt.W, mt.max_c>(g, a, s); break;
+    }
+}
+
+}  // namespace
+}  // namespace mgs

@@ -1,1308 +1,14 @@
-// block_scan.hip -- block-affine scan and block cumulative product, forward and
-// fused backward, k = 8, for gfx950.
-//
-// The ops ("Run the benchmarks" how-to, Step 2: matrix_affine_scan and
-// matrix_scan; the RotationMinGRU / GivensMinGRU recurrences on the minGRU
-// home page):
-//     h_t = A_t h_{t-1} + b_t          P_t = A_t P_{t-1},  P_0 = I
-// per chain (b, block j), with A_t an 8 x 8 block.  Backward for
-// L = sum <dh_t, h_t> (resp. <dP_t, P_t>): g_t = dh_t + A_{t+1}^T g_{t+1},
-// dA_t = g_t h_{t-1}^T (resp. G_t P_{t-1}^T), db_t = g_t, dh0 = A_1^T g_1.
-// dA_t is formed in registers from g_t and h_{t-1} and written once; no
-// per-step product or intermediate tensor is ever stored.
-//
-// Register layout ("row lanes"): a chain's 8 x 8 matrices live in 8
-// consecutive lanes, lane v holding row v.  Column slots of a row are rotated
-// by the lane's quad: slot s holds column s ^ (v & 4).  With that rotation,
-// every operand a product needs from another row arrives through one of two
-// wave-uniform DPP patterns -- a quad broadcast (quad_perm [p,p,p,p]) for rows
-// in the lane's own quad, and a half-row mirror followed by a quad broadcast
-// for rows in the other quad -- and the rotation itself costs nothing because
-// loads and stores simply address the two 16-byte halves of a row in swapped
-// order.  An 8 x 8 by 8 x 8 product is 64 FMAs and 8 mirror moves per lane;
-// a matrix-vector product is 8 FMAs and one mirror.
-//
-// Decomposition: a wave holds 4 chains x 2 sub-chunks (lane = 32*sub + 8*chain
-// + row); a workgroup of W waves holds NCH = 2W consecutive chunks of C steps
-// each, i.e. one tile of TT = NCH*C steps of 4 chains.  Each chunk first
-// builds its aggregate (transfer matrix and offset) from a zero state, the
-// aggregates meet in LDS, and tiles along T exchange theirs by single-pass
-// decoupled look-back (tagged words, dispatch-order tickets; see device.hpp).
-// Each chunk then re-runs its recurrence from its true carry-in, keeping the
-// loaded A_t in registers, and writes its outputs.
+// block_scan.hip -- host side of the block scans: geometry and workspace
+// layout, entry points for every block size, the k = 8 kernels and the
+// Givens angle-fused kernels (k = 8).  The device code is in block_core.hpp;
+// the kernels of the other block sizes are instantiated in block_scan_k.hip,
+// one object file per k.
 #include <hip/hip_runtime.h>
 
-#include "device.hpp"
-#include "launch.hpp"
+#include "block_core.hpp"
 
 namespace mgs {
 namespace {
-
-// ------------------------------------------------------ 8-lane row algebra
-
-template <int P>
-__device__ __forceinline__ float qb(float x)   // value of quad position P
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), P | (P << 2) | (P << 4) | (P << 6),
-                                                   0xF, 0xF, true));
-}
-
-__device__ __forceinline__ float hm(float x)   // value of lane 7 - v within the 8-lane group
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
-}
-
-// 8 x 8 row algebra with DPP operands folded into the multiply-adds.  The
-// compiler does not fold DPP moves into FMAs, so the products are written as
-// inline-asm blocks of v_fmac_f32_dpp / v_mul_f32_dpp.  Each block keeps 2 or
-// 4 independent accumulators and cycles through them, so consecutive
-// instructions never depend on each other.  Every block opens with 5 wait
-// states (a VALU write of a DPP source, or of EXEC, may come right before it)
-// and closes with 2 (a DPP read of its result may come right after), because
-// the compiler's hazard tracking does not look inside inline asm.
-
-// y_v = sum_m R[v][m] x_m + add, R = own row (rotated slots), x one value per lane
-__device__ __forceinline__ float mv8(const float *R, float x, float add)
-{
-    const float mx = hm(x);
-    float a0 = add, a1;
-    asm("s_nop 4\n\t"
-        "v_fmac_f32_dpp %0, %2, %4 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %1, %2, %5 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %6 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %2, %7 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %3, %11 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %10 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %3, %9 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %8 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 1"
-        : "+&v"(a0), "=&v"(a1)
-        : "v"(x), "v"(mx), "v"(R[0]), "v"(R[1]), "v"(R[2]), "v"(R[3]), "v"(R[4]), "v"(R[5]), "v"(R[6]), "v"(R[7]));
-    return a0 + a1;
-}
-
-// Four output slots S..S+3 of Y = R X (X rows spread over the group, M = hm(X)).
-template <int S>
-__device__ __forceinline__ void mm8_quarter(const float *R, const float *X, const float *M, float *Y)
-{
-    asm("s_nop 4\n\t"
-        "v_mul_f32_dpp %0, %4, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %1, %5, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %2, %6, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %3, %7, %12 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %13 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %13 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %13 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %13 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %14 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %15 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %15 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %15 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %15 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %8, %19 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %9, %19 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %10, %19 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %11, %19 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %8, %18 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %9, %18 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %10, %18 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %11, %18 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %8, %17 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %9, %17 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %10, %17 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %11, %17 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %8, %16 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %9, %16 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %10, %16 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %11, %16 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 1"
-        : "=&v"(Y[S]), "=&v"(Y[S + 1]), "=&v"(Y[S + 2]), "=&v"(Y[S + 3])
-        : "v"(X[S]), "v"(X[S + 1]), "v"(X[S + 2]), "v"(X[S + 3]),
-          "v"(M[S ^ 4]), "v"(M[(S + 1) ^ 4]), "v"(M[(S + 2) ^ 4]), "v"(M[(S + 3) ^ 4]),
-          "v"(R[0]), "v"(R[1]), "v"(R[2]), "v"(R[3]), "v"(R[4]), "v"(R[5]), "v"(R[6]), "v"(R[7]));
-}
-
-// Y = R X : own row of R, rows of X spread over the group.  Y must not alias X.
-__device__ __forceinline__ void mm8(const float *R, const float *X, float *Y)
-{
-    float M[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) M[s] = hm(X[s]);
-    mm8_quarter<0>(R, X, M, Y);
-    mm8_quarter<4>(R, X, M, Y);
-}
-
-// Output slots P, P+1, 7-P, 6-P of Y = G X^T.
-template <int P>
-__device__ __forceinline__ void mmT8_quarter(const float *G, const float *X, const float *M, float *Y)
-{
-    asm("s_nop 4\n\t"
-        "v_mul_f32_dpp %0, %4, %20 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %1, %4, %20 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %2, %12, %24 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %3, %12, %24 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %5, %21 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %21 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %13, %25 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %13, %25 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %6, %22 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %6, %22 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %14, %26 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %14, %26 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %7, %23 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %7, %23 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %15, %27 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %15, %27 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %8, %24 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %8, %24 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %16, %20 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %16, %20 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %9, %25 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %9, %25 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %17, %21 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %17, %21 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %10, %26 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %10, %26 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %18, %22 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %18, %22 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %11, %27 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %11, %27 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %19, %23 quad_perm:[%28,%28,%28,%28] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %19, %23 quad_perm:[%29,%29,%29,%29] row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 1"
-        : "=&v"(Y[P]), "=&v"(Y[P + 1]), "=&v"(Y[7 - P]), "=&v"(Y[6 - P])
-        : "v"(X[0]), "v"(X[1]), "v"(X[2]), "v"(X[3]), "v"(X[4]), "v"(X[5]), "v"(X[6]), "v"(X[7]),
-          "v"(M[0]), "v"(M[1]), "v"(M[2]), "v"(M[3]), "v"(M[4]), "v"(M[5]), "v"(M[6]), "v"(M[7]),
-          "v"(G[0]), "v"(G[1]), "v"(G[2]), "v"(G[3]), "v"(G[4]), "v"(G[5]), "v"(G[6]), "v"(G[7]),
-          "n"(P), "n"(P + 1));
-}
-
-// Y = G X^T : own row of G, rows of X spread over the group.
-__device__ __forceinline__ void mmT8(const float *G, const float *X, float *Y)
-{
-    float M[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) M[s] = hm(X[s]);
-    mmT8_quarter<0>(G, X, M, Y);
-    mmT8_quarter<2>(G, X, M, Y);
-}
-
-// Row v of x x'^T scaled: Y[slot] = g * x'_{column(slot)}  (x' one value per lane)
-__device__ __forceinline__ void outer8(float g, float x, float *Y)
-{
-    const float mx = hm(x);
-    Y[0] = g * qb<0>(x);
-    Y[1] = g * qb<1>(x);
-    Y[2] = g * qb<2>(x);
-    Y[3] = g * qb<3>(x);
-    Y[4] = g * qb<3>(mx);
-    Y[5] = g * qb<2>(mx);
-    Y[6] = g * qb<1>(mx);
-    Y[7] = g * qb<0>(mx);
-}
-
-__device__ __forceinline__ void eye_row(int v, float *Y)
-{
-#pragma unroll
-    for (int s = 0; s < 8; ++s) Y[s] = (s == (v & 3)) ? 1.0f : 0.0f;
-}
-
-// row v of a row-major 8x8 block at p (16-byte aligned), into rotated slots
-__device__ __forceinline__ void load_row(const float *p, int v, float *R)
-{
-    const int lo = v & 4;
-    const float4 x0 = *reinterpret_cast<const float4 *>(p + v * 8 + lo);
-    const float4 x1 = *reinterpret_cast<const float4 *>(p + v * 8 + (lo ^ 4));
-    R[0] = x0.x; R[1] = x0.y; R[2] = x0.z; R[3] = x0.w;
-    R[4] = x1.x; R[5] = x1.y; R[6] = x1.z; R[7] = x1.w;
-}
-
-// row v of the TRANSPOSE of the 8x8 block at p (column v), rotated slots
-__device__ __forceinline__ void load_col(const float *p, int v, float *R)
-{
-    const int lo = v & 4;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) R[s] = p[((s ^ lo) * 8) + v];
-}
-
-__device__ __forceinline__ void store_row(float *p, int v, const float *R)
-{
-    const int lo = v & 4;
-    *reinterpret_cast<float4 *>(p + v * 8 + lo) = make_float4(R[0], R[1], R[2], R[3]);
-    *reinterpret_cast<float4 *>(p + v * 8 + (lo ^ 4)) = make_float4(R[4], R[5], R[6], R[7]);
-}
-
-// ------------------------------------------------------------ look-back
-
-// All lanes of one wave take part; lanes 32..63 mirror lanes 0..31 (same slot).
-// Returns the nearest tile p (in the direction dir = -1: earlier tiles,
-// +1: later tiles) whose IW-word inclusive state is published, with the state
-// in xi; -1 if the spin limit was hit.  One batch of loads polls the first word
-// of up to WIN tiles at once; the remaining words of the chosen tile follow.
-template <int IW>
-__device__ int find_inclusive(const uint64_t *incl, int j, int nT, int nCG, int cg, int slot,
-                              int dir, uint32_t tag, uint32_t *err, float *xi)
-{
-    constexpr int WIN = 16;
-    for (uint32_t spin = 0;; ++spin) {
-        for (int p0 = j + dir; p0 >= 0 && p0 < nT; p0 += dir * WIN) {
-            uint64_t w[WIN];
-#pragma unroll
-            for (int u = 0; u < WIN; ++u) {
-                const int p = p0 + dir * u;
-                const bool in = p >= 0 && p < nT;
-                w[u] = tagged_load(incl + ((static_cast<size_t>(in ? p : p0) * nCG + cg) * 32 + slot) * IW);
-            }
-#pragma unroll
-            for (int u = 0; u < WIN; ++u) {
-                const int p = p0 + dir * u;
-                if (p < 0 || p >= nT) break;
-                if (__all(tag_is(w[u], tag))) {
-                    const uint64_t *src = incl + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * IW;
-                    uint64_t r[IW];
-                    r[0] = w[u];
-#pragma unroll
-                    for (int e = 1; e < IW; ++e) r[e] = tagged_load(src + e);
-#pragma unroll
-                    for (int e = 1; e < IW; ++e) {
-                        for (uint32_t sp = 0; !tag_is(r[e], tag); ++sp) {
-                            if (sp >= kSpinLimit) {
-                                raise_error(err, kErrSpin);
-                                break;
-                            }
-                            backoff();
-                            r[e] = tagged_load(src + e);
-                        }
-                    }
-#pragma unroll
-                    for (int e = 0; e < IW; ++e) xi[e] = tag_value(r[e]);
-                    return p;
-                }
-            }
-        }
-        if (spin >= kSpinLimit) {
-            raise_error(err, kErrSpin);
-            return -1;
-        }
-        backoff();
-    }
-}
-
-// Loads the AW-word aggregates of `cnt` (<= NB) tiles p0, p0 + dir, ... for
-// this lane in one batch of loads, then waits for any word not yet published.
-template <int AW, int NB>
-__device__ __forceinline__ void load_aggregates(const uint64_t *agg, int p0, int dir, int cnt, int nCG,
-                                                int cg, int slot, uint32_t tag, uint32_t *err,
-                                                float (&out)[NB][AW])
-{
-    uint64_t w[NB][AW];
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-        const int p = p0 + dir * (u < cnt ? u : 0);
-        const uint64_t *src = agg + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * AW;
-#pragma unroll
-        for (int e = 0; e < AW; ++e) w[u][e] = tagged_load(src + e);
-    }
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-        if (u >= cnt) break;
-        const int p = p0 + dir * u;
-        const uint64_t *src = agg + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * AW;
-#pragma unroll
-        for (int e = 0; e < AW; ++e) {
-            for (uint32_t spin = 0; !tag_is(w[u][e], tag); ++spin) {
-                if (spin >= kSpinLimit) {
-                    raise_error(err, kErrSpin);
-                    break;
-                }
-                backoff();
-                w[u][e] = tagged_load(src + e);
-            }
-            out[u][e] = tag_value(w[u][e]);
-        }
-    }
-}
-
-template <int AW>
-__device__ __forceinline__ void publish(uint64_t *dst, int tile, int slot, uint32_t tag, const float *x)
-{
-    uint64_t *p = dst + (static_cast<size_t>(tile) * 32 + slot) * AW;
-#pragma unroll
-    for (int e = 0; e < AW; ++e) tagged_store(p + e, tag, x[e]);
-}
-
-// ------------------------------------------------------------- arguments
-
-struct BlkArgs {
-    const float *A;      // (B,T,nb,8,8)
-    const float *x;      // affine: b (fwd) or h (bwd); cumprod bwd: P
-    const float *y;      // affine bwd: dh; cumprod bwd: dP
-    const float *h0;     // affine: (B,d), or a zero region of the workspace
-    float *out;          // affine fwd: h; affine bwd: dA; cumprod fwd: P; cumprod bwd: dA
-    float *out2;         // affine bwd: db
-    float *out3;         // affine bwd: dh0
-    int64_t nchain;
-    int T, d, nb, nCG, nT, nTiles;
-    WsHeader *hd;
-    uint64_t *agg, *incl;
-    float *pstate;       // cumulative product: state entering each chunk, [tile][chunk][slot][8]
-    const float *theta;  // Givens angle-fused: angles (B,T,nb,28)
-    const float *sg;     // Givens angle-fused: gate pre-activations (B,T,nb)
-    float *dtheta;       // Givens angle-fused backward: d angles
-    float *dsg;          // Givens angle-fused backward: d gate
-};
-
-struct Tile {
-    int lane, wv, v, cgl, sub, slot, q, j, cg, t0;
-    bool cv;
-    int64_t bb, jb;
-    int64_t blk0;    // block index (bb, t=0, jb) in (B,T,nb)
-    int64_t ablk0;   // element offset of A block (bb, t=0, jb)
-    int64_t astep;   // elements between consecutive t of the same block
-    int64_t vec0;    // element offset of (bb, t=0, jb*8 + v) in (B,T,d)
-    int64_t vstep;   // = d
-};
-
-template <int C, int W>
-__device__ __forceinline__ Tile make_tile(const BlkArgs &a, int tile, bool reverse)
-{
-    Tile t;
-    t.lane = threadIdx.x & 63;
-    t.wv = threadIdx.x >> 6;
-    t.v = t.lane & 7;
-    t.cgl = (t.lane >> 3) & 3;
-    t.sub = t.lane >> 5;
-    t.slot = t.cgl * 8 + t.v;
-    t.q = t.wv * 2 + t.sub;
-    const int jr = tile / a.nCG;
-    t.cg = tile - jr * a.nCG;
-    t.j = reverse ? a.nT - 1 - jr : jr;
-    const int64_t chain = static_cast<int64_t>(t.cg) * 4 + t.cgl;
-    t.cv = chain < a.nchain;
-    const int64_t cc = t.cv ? chain : 0;
-    t.bb = cc / a.nb;
-    t.jb = cc - t.bb * a.nb;
-    t.astep = static_cast<int64_t>(a.nb) * 64;
-    t.blk0 = t.bb * a.T * a.nb + t.jb;
-    t.ablk0 = t.blk0 * 64;
-    t.vstep = a.d;
-    t.vec0 = t.bb * a.T * a.d + t.jb * 8 + t.v;
-    t.t0 = t.j * (2 * W * C) + t.q * C;
-    return t;
-}
-
-__device__ __forceinline__ int clampT(int t, int T) { return t < T ? t : T - 1; }
-
-// h0 entry of this lane.  When the caller passes no h0, a.h0 points at a
-// zero region of the workspace, so the load is unconditional and never sits
-// behind a branch that would force a wait on the loads issued before it.
-// Lanes of chains past the end read chain 0's entry; their results are never
-// stored and their 8-lane groups exchange data only among themselves.
-__device__ __forceinline__ float load_h0(const BlkArgs &a, const Tile &tl)
-{
-    return a.h0[tl.bb * a.d + tl.jb * 8 + tl.v];
-}
-
-// ============================================ in-tile scan of chunk aggregates
-// Each half-wave holds the aggregate of one chunk q = 2 * wave + sub.  A
-// Kogge-Stone scan over the NCH chunks runs on all waves at once: in round r
-// every chunk composes its running composite with the one 2^r chunks before it
-// (DIR = +1) or after it (DIR = -1), read from one of two LDS buffers in turn,
-// with one barrier per round.  Afterwards chunk q holds the composite of
-// chunks 0..q (DIR = +1) or q..NCH-1 (DIR = -1), and a copy sits in buffer
-// ks_final<NCH>() for the fix-up.  The rule is the same in both directions:
-//     (M, v) o (M', v') = (M M', M v' + v)
-// with v absent (cumulative product), one value per lane (block-affine) or a
-// matrix row (cumulative-product backward).
-
-enum AggKind : int { kMat = 0, kMatVec = 1, kMatMat = 2 };
-
-template <int KIND>
-struct AggShape {
-    static constexpr int words = KIND == kMat ? 8 : (KIND == kMatVec ? 9 : 16);
-    static constexpr int stride = words | 1;   // odd LDS stride: lanes hit distinct banks
-};
-
-template <int NCH>
-__host__ __device__ constexpr int ks_final()
-{
-    int r = 0;
-    while ((1 << r) < NCH) ++r;
-    return r & 1;
-}
-
-template <int KIND>
-__device__ __forceinline__ void compose_into(float *X, const float *R)
-{
-    if constexpr (KIND == kMatVec) X[8] = mv8(X, R[8], X[8]);
-    if constexpr (KIND == kMatMat) {
-        float nw[8];
-        mm8(X, R + 8, nw);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) X[8 + s] += nw[s];
-    }
-    float np[8];
-    mm8(X, R, np);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) X[s] = np[s];
-}
-
-template <int KIND, int NCH>
-__device__ __forceinline__ void ks_store(float (*buf)[32][AggShape<KIND>::stride], int q, int slot, const float *X)
-{
-#pragma unroll
-    for (int e = 0; e < AggShape<KIND>::words; ++e) buf[q][slot][e] = X[e];
-}
-
-// Precondition: buffer 0 holds every chunk's aggregate and a barrier has passed.
-template <int KIND, int NCH, int DIR>
-__device__ __forceinline__ void ks_scan(float (*buf)[NCH][32][AggShape<KIND>::stride], int q, int slot, float *X)
-{
-    constexpr int AW = AggShape<KIND>::words;
-#pragma unroll
-    for (int r = 0; (1 << r) < NCH; ++r) {
-        if (r > 0) {
-            ks_store<KIND, NCH>(buf[r & 1], q, slot, X);
-            __syncthreads();
-        }
-        const int qn = q - DIR * (1 << r);
-        if (qn >= 0 && qn < NCH) {
-            float R[AW];
-#pragma unroll
-            for (int e = 0; e < AW; ++e) R[e] = buf[r & 1][qn][slot][e];
-            compose_into<KIND>(X, R);
-        }
-    }
-    ks_store<KIND, NCH>(buf[ks_final<NCH>()], q, slot, X);
-}
-
-// ===================================================== Givens mesh in lanes
-// The angle-fused kernels form A_t = sigmoid(s_t) R(theta_t) in registers.  R is
-// the brick-wall mesh of 8 layers of 2 x 2 rotations (GivensMinGRU on the
-// minGRU home page; the Clements / EUNN mesh it cites): layer l rotates the
-// pairs (i, i+1), i = l mod 2, l mod 2 + 2, ..., R = L_7 .. L_0, angles in
-// (layer, pair) order, each rotation mapping (x_i, x_j) to
-// (c x_i - s x_j, s x_i + c x_j).  Lane p of a chain's 8 lanes loads angles
-// 4p..4p+3 (lane 7 none), and the chain shares their cosines and sines through
-// LDS, so every angle is loaded once and turned into sin / cos once.
-
-constexpr int kAngles = 28;
-
-__host__ __device__ constexpr int mesh_first(int l) { return (l / 2) * 7 + (l & 1) * 4; }
-
-// sin x and cos x for |x| up to a few thousand: Cody and Waite's reduction
-// x = q pi/2 + r with pi/2 split into a float head and tail (fused multiply-
-// adds keep q * head exact enough), |r| <= pi/4, then the Taylor series of sin
-// to r^9 and of cos to r^10 (truncation below 2e-9) and the quadrant's
-// swap / sign.  A few ulp, against the dozens of instructions (and a
-// large-argument path) of a general-range sincos.
-__device__ __forceinline__ void sincos_cw(float x, float &sn, float &cs)
-{
-    constexpr float kTwoOverPi = 0.636619772367581f;
-    constexpr float kPiHalfHi = 1.57079637050628662f;      // float(pi / 2)
-    constexpr float kPiHalfLo = -4.37113900018624e-08f;     // pi / 2 - kPiHalfHi
-    const float q = __builtin_rintf(x * kTwoOverPi);
-    float r = __builtin_fmaf(q, -kPiHalfHi, x);
-    r = __builtin_fmaf(q, -kPiHalfLo, r);
-    const float r2 = r * r;
-    float ps = __builtin_fmaf(r2, 1.0f / 362880.0f, -1.0f / 5040.0f);
-    ps = __builtin_fmaf(r2, ps, 1.0f / 120.0f);
-    ps = __builtin_fmaf(r2, ps, -1.0f / 6.0f);
-    const float sr = __builtin_fmaf(r * r2, ps, r);
-    float pc = __builtin_fmaf(r2, -1.0f / 3628800.0f, 1.0f / 40320.0f);
-    pc = __builtin_fmaf(r2, pc, -1.0f / 720.0f);
-    pc = __builtin_fmaf(r2, pc, 1.0f / 24.0f);
-    pc = __builtin_fmaf(r2, pc, -0.5f);
-    const float cr = __builtin_fmaf(r2, pc, 1.0f);
-    const int n = static_cast<int>(q);
-    const bool swap = (n & 1) != 0;
-    const float s0 = swap ? cr : sr, c0 = swap ? sr : cr;
-    sn = (n & 2) ? -s0 : s0;
-    cs = ((n + 1) & 2) ? -c0 : c0;
-}
-
-// cosines and sines of a chain's 28 angles in every lane of the chain
-__device__ __forceinline__ void mesh_share(float4 th, float (*cs)[8], int lane, float (&cc)[kAngles],
-                                           float (&ss)[kAngles])
-{
-    // within a few ulp (the hardware's native sin / cos lose ~1e-6 absolute,
-    // which the 28 rotations and the scan then carry)
-    float4 c4, s4;
-    sincos_cw(th.x, s4.x, c4.x);
-    sincos_cw(th.y, s4.y, c4.y);
-    sincos_cw(th.z, s4.z, c4.z);
-    sincos_cw(th.w, s4.w, c4.w);
-    *reinterpret_cast<float4 *>(&cs[lane][0]) = c4;
-    *reinterpret_cast<float4 *>(&cs[lane][4]) = s4;
-    const int base = lane & ~7;
-#pragma unroll
-    for (int p = 0; p < 7; ++p) {
-        const float4 c = *reinterpret_cast<const float4 *>(&cs[base + p][0]);
-        const float4 s = *reinterpret_cast<const float4 *>(&cs[base + p][4]);
-        cc[4 * p] = c.x; cc[4 * p + 1] = c.y; cc[4 * p + 2] = c.z; cc[4 * p + 3] = c.w;
-        ss[4 * p] = s.x; ss[4 * p + 1] = s.y; ss[4 * p + 2] = s.z; ss[4 * p + 3] = s.w;
-    }
-}
-
-// row v of R in natural column order: e_v^T L_7 .. L_0
-__device__ __forceinline__ void mesh_row(const float (&cc)[kAngles], const float (&ss)[kAngles], int v, float (&r)[8])
-{
-#pragma unroll
-    for (int c = 0; c < 8; ++c) r[c] = (c == v) ? 1.0f : 0.0f;
-#pragma unroll
-    for (int l = 7; l >= 0; --l)
-#pragma unroll
-        for (int i = l & 1, a = mesh_first(l); i + 1 < 8; i += 2, ++a) {
-            const float ri = r[i], rj = r[i + 1];
-            r[i] = cc[a] * ri + ss[a] * rj;
-            r[i + 1] = cc[a] * rj - ss[a] * ri;
-        }
-}
-
-// column v of R in natural row order: L_7 .. L_0 e_v
-__device__ __forceinline__ void mesh_col(const float (&cc)[kAngles], const float (&ss)[kAngles], int v, float (&y)[8])
-{
-#pragma unroll
-    for (int r = 0; r < 8; ++r) y[r] = (r == v) ? 1.0f : 0.0f;
-#pragma unroll
-    for (int l = 0; l < 8; ++l)
-#pragma unroll
-        for (int i = l & 1, a = mesh_first(l); i + 1 < 8; i += 2, ++a) {
-            const float yi = y[i], yj = y[i + 1];
-            y[i] = cc[a] * yi - ss[a] * yj;
-            y[i + 1] = ss[a] * yi + cc[a] * yj;
-        }
-}
-
-// Reverse pass through mesh_col: y is the built column, dy the gradient on it;
-// writes d(column)/d(angle) contracted with dy into part.  Each layer is undone
-// by its inverse rotation, so no intermediate column is stored.
-__device__ __forceinline__ void mesh_col_adjoint(const float (&cc)[kAngles], const float (&ss)[kAngles],
-                                                 float (&y)[8], float (&dy)[8], float (&part)[kAngles])
-{
-#pragma unroll
-    for (int l = 7; l >= 0; --l)
-#pragma unroll
-        for (int i = l & 1, a = mesh_first(l); i + 1 < 8; i += 2, ++a) {
-            const float yi = y[i], yj = y[i + 1], gi = dy[i], gj = dy[i + 1];
-            part[a] = gj * yi - gi * yj;
-            y[i] = cc[a] * yi + ss[a] * yj;
-            y[i + 1] = cc[a] * yj - ss[a] * yi;
-            dy[i] = cc[a] * gi + ss[a] * gj;
-            dy[i + 1] = cc[a] * gj - ss[a] * gi;
-        }
-}
-
-// natural order <-> this lane's rotated slots (slot s holds entry s ^ (v & 4)).
-// Written as a bitwise blend of two fixed-index registers: a select between
-// x[s] and x[s ^ 4] would be folded into a lane-dependent index, which sends
-// the array to scratch memory.
-__device__ __forceinline__ float blend(float a, float b, int mask)
-{
-    return __int_as_float((__float_as_int(b) & mask) | (__float_as_int(a) & ~mask));
-}
-
-__device__ __forceinline__ void to_slots(const float (&x)[8], int v, float scale, float *y)
-{
-    const int m = -((v >> 2) & 1);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) y[s] = scale * blend(x[s], x[s ^ 4], m);
-}
-
-__device__ __forceinline__ void from_slots(const float *x, int v, float scale, float (&y)[8])
-{
-    const int m = -((v >> 2) & 1);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) y[s] = scale * blend(x[s], x[s ^ 4], m);
-}
-
-__device__ __forceinline__ float sigmoidf_(float u) { return 1.0f / (1.0f + __expf(-u)); }
-
-// Pins eight values in registers at this point of the program: work that
-// produces them cannot sink below it, so one step's 56 cosines and sines are
-// dead before the next step's are loaded (with a scheduling barrier after it).
-__device__ __forceinline__ void settle8(float *x)
-{
-    asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
-                 "+v"(x[7]));
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// angle slice and gate of this lane's chain at step t (indices clamped in range)
-__device__ __forceinline__ float4 load_angles(const BlkArgs &a, const Tile &tl, int t)
-{
-    const int64_t blk = tl.blk0 + static_cast<int64_t>(t) * a.nb;
-    return *reinterpret_cast<const float4 *>(a.theta + blk * kAngles + 4 * min(tl.v, 6));
-}
-
-// ============================================ block-affine carry phases
-// Shared by the kernels that load A and the kernels that form it from angles.
-
-// Forward: X = (row of Phi, entry of u) is the chunk's aggregate.  Stores it,
-// scans the tile's chunks, runs the look-back (multi-tile launches) and
-// returns the state entering this lane's chunk.
-template <int C, int W, bool MULTI>
-__device__ __forceinline__ float affine_fwd_carry(const BlkArgs &a, const Tile &tl, int ftile, unsigned long long ep,
-                                                  float (&X)[9], float xh0,
-                                                  float (&sKS)[2][2 * W][32][AggShape<kMatVec>::stride],
-                                                  float (&sCarry)[32], uint32_t (&sTicket)[2])
-{
-    constexpr int NCH = 2 * W;
-    using S = AggShape<kMatVec>;
-    constexpr int FIN = ks_final<NCH>();
-    ks_store<kMatVec, NCH>(sKS[0], tl.q, tl.slot, X);
-    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
-    __syncthreads();
-    const uint32_t tag = sTicket[0];
-
-    float x;
-    if constexpr (MULTI) {
-        ks_scan<kMatVec, NCH, +1>(sKS, tl.q, tl.slot, X);
-        // the last wave's upper half holds the tile aggregate and runs the look-back
-        if (tl.wv == W - 1) {
-            const bool owner = tl.sub == 1;
-            if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<S::words>(a.agg, ftile, tl.slot, tag, X);
-            float xin = xh0;
-            if (tl.j > 0) {
-                float xi[1];
-                const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, tag, &a.hd->err, xi);
-                if (ps >= 0) xin = xi[0];
-                constexpr int NB = 4;
-                for (int p = ps + 1; p < tl.j; p += NB) {
-                    const int cnt = min(NB, tl.j - p);
-                    float ag[NB][S::words];
-                    load_aggregates<S::words, NB>(a.agg, p, +1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
-#pragma unroll
-                    for (int u = 0; u < NB; ++u)
-                        if (u < cnt) xin = mv8(ag[u], xin, ag[u][8]);
-                }
-            }
-            if (owner && tl.j < a.nT - 1) {
-                const float xo = mv8(X, xin, X[8]);
-                publish<1>(a.incl, ftile, tl.slot, tag, &xo);
-            }
-            if (owner) sCarry[tl.slot] = xin;
-        }
-        __syncthreads();
-        x = sCarry[tl.slot];
-        if (tl.q > 0) x = mv8(sKS[FIN][tl.q - 1][tl.slot], x, sKS[FIN][tl.q - 1][tl.slot][8]);
-    } else {
-        x = xh0;
-        for (int q = 0; q < tl.q; ++q) x = mv8(sKS[0][q][tl.slot], x, sKS[0][q][tl.slot][8]);
-    }
-    return x;
-}
-
-// Backward: X = (row of Psi, entry of Wl) is the chunk's reverse aggregate.
-// Returns w entering this lane's chunk from its end.
-template <int C, int W, bool MULTI>
-__device__ __forceinline__ float affine_bwd_carry(const BlkArgs &a, const Tile &tl, int ftile, unsigned long long ep,
-                                                  float (&X)[9],
-                                                  float (&sKS)[2][2 * W][32][AggShape<kMatVec>::stride],
-                                                  float (&sCarry)[32], uint32_t (&sTicket)[2])
-{
-    constexpr int NCH = 2 * W;
-    using S = AggShape<kMatVec>;
-    constexpr int FIN = ks_final<NCH>();
-    ks_store<kMatVec, NCH>(sKS[0], tl.q, tl.slot, X);
-    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
-    __syncthreads();
-    const uint32_t tag = sTicket[0];
-
-    float w;
-    if constexpr (MULTI) {
-        ks_scan<kMatVec, NCH, -1>(sKS, tl.q, tl.slot, X);
-        // wave 0's lower half holds the tile aggregate and runs the look-back
-        if (tl.wv == 0) {
-            const bool owner = tl.sub == 0;
-            if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<S::words>(a.agg, ftile, tl.slot, tag, X);
-            float win = 0.0f;
-            if (tl.j < a.nT - 1) {
-                float xi[1];
-                const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, tag, &a.hd->err, xi);
-                int pend = a.nT;
-                if (ps >= 0) { win = xi[0]; pend = ps; }
-                constexpr int NB = 4;
-                for (int p = pend - 1; p > tl.j; p -= NB) {
-                    const int cnt = min(NB, p - tl.j);
-                    float ag[NB][S::words];
-                    load_aggregates<S::words, NB>(a.agg, p, -1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
-#pragma unroll
-                    for (int u = 0; u < NB; ++u)
-                        if (u < cnt) win = mv8(ag[u], win, ag[u][8]);
-                }
-            }
-            if (owner && tl.j > 0) {
-                const float wo = mv8(X, win, X[8]);
-                publish<1>(a.incl, ftile, tl.slot, tag, &wo);
-            }
-            if (owner) sCarry[tl.slot] = win;
-        }
-        __syncthreads();
-        w = sCarry[tl.slot];
-        if (tl.q < NCH - 1) w = mv8(sKS[FIN][tl.q + 1][tl.slot], w, sKS[FIN][tl.q + 1][tl.slot][8]);
-    } else {
-        w = 0.0f;
-        for (int q = NCH - 1; q > tl.q; --q) w = mv8(sKS[0][q][tl.slot], w, sKS[0][q][tl.slot][8]);
-    }
-    return w;
-}
-
-// ======================================================= block-affine fwd
-// GIV = false: A_t is loaded; GIV = true: A_t = sigmoid(s_t) R(theta_t) is
-// formed from the angles and the gate (the Givens angle-fused scan).
-
-template <bool GIV, int C, int W, bool MULTI>
-__device__ __forceinline__ void affine_fwd_body(const BlkArgs &a)
-{
-    constexpr int NCH = 2 * W;
-    __shared__ float sKS[2][NCH][32][AggShape<kMatVec>::stride];
-    __shared__ float sCarry[32];
-    __shared__ uint32_t sTicket[2];
-    __shared__ float sCS[GIV ? W : 1][64][8];
-
-    const int tile = blockIdx.x;
-    unsigned long long ep = 0;
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
-    const Tile tl = make_tile<C, W>(a, tile, false);
-    const int ftile = tl.j * a.nCG + tl.cg;
-
-    // unconditional (clamped) loads keep every load in flight at once
-    float Ar[C][8], bv[C];
-    if constexpr (!GIV) {
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            const int t = clampT(tl.t0 + i, a.T);
-            load_row(a.A + tl.ablk0 + t * tl.astep, tl.v, Ar[i]);
-            bv[i] = a.x[tl.vec0 + t * tl.vstep];
-        }
-    } else {
-        float4 th[C];
-        float sv[C];
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            const int t = clampT(tl.t0 + i, a.T);
-            th[i] = load_angles(a, tl, t);
-            sv[i] = a.sg[tl.blk0 + static_cast<int64_t>(t) * a.nb];
-            bv[i] = a.x[tl.vec0 + t * tl.vstep];
-        }
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            float cc[kAngles], ss[kAngles], r[8];
-            mesh_share(th[i], sCS[tl.wv % (GIV ? W : 1)], tl.lane, cc, ss);
-            mesh_row(cc, ss, tl.v, r);
-            to_slots(r, tl.v, sigmoidf_(sv[i]), Ar[i]);
-            settle8(Ar[i]);
-        }
-    }
-    const float xh0 = load_h0(a, tl);
-#pragma unroll
-    for (int i = 0; i < C; ++i)
-        if (!(tl.cv && tl.t0 + i < a.T)) {
-            eye_row(tl.v, Ar[i]);
-            bv[i] = 0.0f;
-        }
-
-    // chunk aggregate from a zero state: X = (A_e..A_s, local h_e)
-    float X[9];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) X[s] = Ar[0][s];
-    X[8] = bv[0];
-#pragma unroll
-    for (int i = 1; i < C; ++i) {
-        float np[8];
-        mm8(Ar[i], X, np);
-        X[8] = mv8(Ar[i], X[8], bv[i]);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) X[s] = np[s];
-    }
-    float x = affine_fwd_carry<C, W, MULTI>(a, tl, ftile, ep, X, xh0, sKS, sCarry, sTicket);
-
-    // re-run the recurrence from the true state entering the chunk
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        x = mv8(Ar[i], x, bv[i]);
-        const int t = tl.t0 + i;
-        if (tl.cv && t < a.T) a.out[tl.vec0 + t * tl.vstep] = x;
-    }
-}
-
-template <int C, int W, bool MULTI>
-__global__ void __launch_bounds__(64 * W) baffine_fwd_kernel(BlkArgs a)
-{
-    affine_fwd_body<false, C, W, MULTI>(a);
-}
-
-template <int C, int W, bool MULTI>
-__global__ void __launch_bounds__(64 * W) bgivens_fwd_kernel(BlkArgs a)
-{
-    affine_fwd_body<true, C, W, MULTI>(a);
-}
-
-// ======================================================= block-affine bwd
-// Reverse scan on w_t = A_t^T g_t with g_t = dh_t + w_{t+1}; per chunk [s, e]
-// w_s = Psi w_{e+1} + Wl with Psi = A_s^T .. A_e^T.
-
-template <int C, int W, bool MULTI>
-__global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
-{
-    constexpr int NCH = 2 * W;
-    __shared__ float sKS[2][NCH][32][AggShape<kMatVec>::stride];
-    __shared__ float sCarry[32];
-    __shared__ uint32_t sTicket[2];
-
-    const int tile = blockIdx.x;
-    unsigned long long ep = 0;
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
-    const Tile tl = make_tile<C, W>(a, tile, true);
-    const int ftile = tl.j * a.nCG + tl.cg;
-
-    float ATr[C][8], gv[C], hp[C];   // rows of A_t^T, upstream dh_t, h_{t-1}
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int t = clampT(tl.t0 + i, a.T);
-        load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
-        gv[i] = a.y[tl.vec0 + t * tl.vstep];
-        hp[i] = a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep];
-    }
-    const float xh0 = load_h0(a, tl);
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int t = tl.t0 + i;
-        if (t == 0) hp[i] = xh0;
-        if (!(tl.cv && t < a.T)) {
-            eye_row(tl.v, ATr[i]);
-            gv[i] = 0.0f;
-            hp[i] = 0.0f;
-        }
-    }
-
-    // chunk aggregate from a zero carry, walking t downwards: X = (Psi, Wl)
-    float X[9];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) X[s] = ATr[C - 1][s];
-    X[8] = mv8(ATr[C - 1], gv[C - 1], 0.0f);
-#pragma unroll
-    for (int i = C - 2; i >= 0; --i) {
-        float np[8];
-        mm8(ATr[i], X, np);
-        X[8] = mv8(ATr[i], gv[i] + X[8], 0.0f);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) X[s] = np[s];
-    }
-    float w = affine_bwd_carry<C, W, MULTI>(a, tl, ftile, ep, X, sKS, sCarry, sTicket);
-
-    // re-run the reverse recurrence from the true carry; emit dA, db, dh0
-#pragma unroll
-    for (int i = C - 1; i >= 0; --i) {
-        const float g = gv[i] + w;
-        float dAr[8];
-        outer8(g, hp[i], dAr);
-        w = mv8(ATr[i], g, 0.0f);
-        const int t = tl.t0 + i;
-        if (tl.cv && t < a.T) {
-            a.out2[tl.vec0 + t * tl.vstep] = g;
-            store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, dAr);
-        }
-    }
-    if (tl.cv && tl.t0 == 0) a.out3[tl.bb * a.d + tl.jb * 8 + tl.v] = w;   // A_1^T g_1
-}
-
-// =============================================== Givens angle-fused bwd
-// Same reverse scan with A_t = sigmoid(s_t) R(theta_t) formed in registers
-// (unscaled columns of R, the gate applied as a scalar).  dA_t = g_t h_{t-1}^T
-// is never formed as a tensor: lane v holds column v of it, contracts it with
-// the derivative of column v of A (the reverse pass through the mesh) and with
-// column v of R (for the gate), and the chain's 8 lanes add their shares in LDS:
-//     dtheta_t = sigmoid(s_t) <dA_t, dR/dtheta>,  ds_t = sigmoid'(s_t) <dA_t, R>.
-
-template <int C, int W, bool MULTI>
-__global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
-{
-    constexpr int NCH = 2 * W;
-    constexpr int PW = 32;   // words per lane in the reduction buffer: 28 angles, the gate, padding
-    __shared__ float sKS[2][NCH][32][AggShape<kMatVec>::stride];
-    __shared__ float sCarry[32];
-    __shared__ uint32_t sTicket[2];
-    __shared__ float sCS[W][64][8];
-    __shared__ float sPart[W][64][PW];
-
-    const int tile = blockIdx.x;
-    unsigned long long ep = 0;
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
-    const Tile tl = make_tile<C, W>(a, tile, true);
-    const int ftile = tl.j * a.nCG + tl.cg;
-
-    float4 th[C];
-    float RTr[C][8], sig[C], gv[C], hp[C];   // rows of R^T (unscaled), gate, dh_t, h_{t-1}
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int t = clampT(tl.t0 + i, a.T);
-        th[i] = load_angles(a, tl, t);
-        sig[i] = a.sg[tl.blk0 + static_cast<int64_t>(t) * a.nb];
-        gv[i] = a.y[tl.vec0 + t * tl.vstep];
-        hp[i] = a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep];
-    }
-    const float xh0 = load_h0(a, tl);
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        float cc[kAngles], ss[kAngles], y[8];
-        mesh_share(th[i], sCS[tl.wv], tl.lane, cc, ss);
-        mesh_col(cc, ss, tl.v, y);
-        to_slots(y, tl.v, 1.0f, RTr[i]);
-        sig[i] = sigmoidf_(sig[i]);
-        settle8(RTr[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int t = tl.t0 + i;
-        if (t == 0) hp[i] = xh0;
-        if (!(tl.cv && t < a.T)) {
-            eye_row(tl.v, RTr[i]);
-            sig[i] = 1.0f;
-            gv[i] = 0.0f;
-            hp[i] = 0.0f;
-        }
-    }
-
-    // chunk aggregate from a zero carry, walking t downwards: X = (Psi, Wl)
-    float X[9];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) X[s] = sig[C - 1] * RTr[C - 1][s];
-    X[8] = sig[C - 1] * mv8(RTr[C - 1], gv[C - 1], 0.0f);
-#pragma unroll
-    for (int i = C - 2; i >= 0; --i) {
-        float np[8];
-        mm8(RTr[i], X, np);
-        X[8] = sig[i] * mv8(RTr[i], gv[i] + X[8], 0.0f);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) X[s] = sig[i] * np[s];
-    }
-    float w = affine_bwd_carry<C, W, MULTI>(a, tl, ftile, ep, X, sKS, sCarry, sTicket);
-
-    float (*part)[PW] = sPart[tl.wv];
-    const int base = tl.lane & ~7;
-    // the angles are read again here (an L2 hit) rather than kept in registers
-    // since the build; one step ahead
-    float4 thn = load_angles(a, tl, clampT(tl.t0 + C - 1, a.T));
-#pragma unroll
-    for (int i = C - 1; i >= 0; --i) {
-        const float4 thc = thn;
-        if (i > 0) thn = load_angles(a, tl, clampT(tl.t0 + i - 1, a.T));
-        const float g = gv[i] + w;
-        float dAc[8];
-        outer8(hp[i], g, dAc);              // column v of dA_t = g_t h_{t-1}^T (rotated slots)
-        w = sig[i] * mv8(RTr[i], g, 0.0f);  // A_t^T g_t
-        // lane v's share of dtheta_t and ds_t, through column v of A_t
-        float cc[kAngles], ss[kAngles], y[8], dy[8], pt[kAngles];
-        mesh_share(thc, sCS[tl.wv], tl.lane, cc, ss);
-        from_slots(RTr[i], tl.v, 1.0f, y);
-        from_slots(dAc, tl.v, sig[i], dy);
-        float gate = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) gate += dy[r] * y[r];
-        mesh_col_adjoint(cc, ss, y, dy, pt);
-#pragma unroll
-        for (int q = 0; q < 7; ++q)
-            *reinterpret_cast<float4 *>(&part[tl.lane][4 * q]) =
-                make_float4(pt[4 * q], pt[4 * q + 1], pt[4 * q + 2], pt[4 * q + 3]);
-        *reinterpret_cast<float4 *>(&part[tl.lane][28]) = make_float4((1.0f - sig[i]) * gate, 0.0f, 0.0f, 0.0f);
-        // lane v (< 7) adds up angles 4v..4v+3 over the chain; lane 7 the gate
-        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const float4 u = *reinterpret_cast<const float4 *>(&part[base + p][4 * tl.v]);
-            acc.x += u.x; acc.y += u.y; acc.z += u.z; acc.w += u.w;
-        }
-        const int t = tl.t0 + i;
-        if (tl.cv && t < a.T) {
-            const int64_t blk = tl.blk0 + static_cast<int64_t>(t) * a.nb;
-            a.out2[tl.vec0 + t * tl.vstep] = g;
-            if (tl.v < 7)
-                *reinterpret_cast<float4 *>(a.dtheta + blk * kAngles + 4 * tl.v) = acc;
-            else
-                a.dsg[blk] = acc.x;
-        }
-        asm volatile("" : "+v"(w));
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if (tl.cv && tl.t0 == 0) a.out3[tl.bb * a.d + tl.jb * 8 + tl.v] = w;   // A_1^T g_1
-}
-
-// ================================================ block cumulative product
-
-template <int C, int W, bool MULTI>
-__global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
-{
-    constexpr int NCH = 2 * W;
-    using S = AggShape<kMat>;
-    constexpr int FIN = ks_final<NCH>();
-    __shared__ float sKS[2][NCH][32][S::stride];
-    __shared__ float sCarry[32][8];
-    __shared__ uint32_t sTicket[2];
-
-    const int tile = blockIdx.x;
-    unsigned long long ep = 0;
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
-    const Tile tl = make_tile<C, W>(a, tile, false);
-    const int ftile = tl.j * a.nCG + tl.cg;
-
-    float Ar[C][8];
-#pragma unroll
-    for (int i = 0; i < C; ++i)
-        load_row(a.A + tl.ablk0 + clampT(tl.t0 + i, a.T) * tl.astep, tl.v, Ar[i]);
-#pragma unroll
-    for (int i = 0; i < C; ++i)
-        if (!(tl.cv && tl.t0 + i < a.T)) eye_row(tl.v, Ar[i]);
-
-    float X[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) X[s] = Ar[0][s];
-#pragma unroll
-    for (int i = 1; i < C; ++i) {
-        float np[8];
-        mm8(Ar[i], X, np);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) X[s] = np[s];
-    }
-    ks_store<kMat, NCH>(sKS[0], tl.q, tl.slot, X);
-    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
-    __syncthreads();
-    const uint32_t tag = sTicket[0];
-
-    ks_scan<kMat, NCH, +1>(sKS, tl.q, tl.slot, X);   // X = composite of chunks 0..q
-    if constexpr (MULTI) {
-        // the last wave's upper half holds the tile aggregate and runs the look-back
-        if (tl.wv == W - 1) {
-            const bool owner = tl.sub == 1;
-            if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<8>(a.agg, ftile, tl.slot, tag, X);
-            float Pin[8];
-            eye_row(tl.v, Pin);
-            if (tl.j > 0) {
-                float xi[8];
-                const int ps = find_inclusive<8>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, tag, &a.hd->err, xi);
-                if (ps >= 0) {
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) Pin[s] = xi[s];
-                }
-                constexpr int NB = 4;
-                for (int p = ps + 1; p < tl.j; p += NB) {
-                    const int cnt = min(NB, tl.j - p);
-                    float ag[NB][8];
-                    load_aggregates<8, NB>(a.agg, p, +1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
-#pragma unroll
-                    for (int u = 0; u < NB; ++u)
-                        if (u < cnt) {
-                            float np[8];
-                            mm8(ag[u], Pin, np);
-#pragma unroll
-                            for (int s = 0; s < 8; ++s) Pin[s] = np[s];
-                        }
-                }
-            }
-            if (owner && tl.j < a.nT - 1) {
-                float Po[8];
-                mm8(X, Pin, Po);
-                publish<8>(a.incl, ftile, tl.slot, tag, Po);
-            }
-            if (owner) {
-#pragma unroll
-                for (int s = 0; s < 8; ++s) sCarry[tl.slot][s] = Pin[s];
-            }
-        }
-    }
-    __syncthreads();
-    // state entering the chunk: (composite of chunks 0..q-1) x (tile carry-in)
-    float P[8];
-    if constexpr (MULTI) {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) P[s] = sCarry[tl.slot][s];
-        if (tl.q > 0) {
-            float np[8];
-            mm8(sKS[FIN][tl.q - 1][tl.slot], P, np);
-#pragma unroll
-            for (int s = 0; s < 8; ++s) P[s] = np[s];
-        }
-    } else {
-        eye_row(tl.v, P);
-        if (tl.q > 0) {
-#pragma unroll
-            for (int s = 0; s < 8; ++s) P[s] = sKS[FIN][tl.q - 1][tl.slot][s];
-        }
-    }
-    // the state entering this chunk, for the backward's recompute (slot order kept)
-    {
-        float *ps = a.pstate + ((static_cast<size_t>(ftile) * NCH + tl.q) * 32 + tl.slot) * 8;
-        *reinterpret_cast<float4 *>(ps) = make_float4(P[0], P[1], P[2], P[3]);
-        *reinterpret_cast<float4 *>(ps + 4) = make_float4(P[4], P[5], P[6], P[7]);
-    }
-    if (a.out == nullptr) return;   // states only (requested by a backward)
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        float np[8];
-        mm8(Ar[i], P, np);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) P[s] = np[s];
-        const int t = tl.t0 + i;
-        if (tl.cv && t < a.T) store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, P);
-    }
-}
-
-// Backward: W_t = A_t^T G_t with G_t = dP_t + W_{t+1}; per chunk [s, e]
-// W_s = Psi W_{e+1} + Wl.  dA_t = G_t P_{t-1}^T, with P_{t-1} recomputed from
-// the state entering the chunk (stored by the forward) and the A_t in hand.
-template <int C, int W, bool MULTI>
-__global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
-{
-    constexpr int NCH = 2 * W;
-    using S = AggShape<kMatMat>;
-    constexpr int FIN = ks_final<NCH>();
-    __shared__ float sKS[2][NCH][32][S::stride];
-    __shared__ float sCarry[32][8];
-    __shared__ uint32_t sTicket[2];
-
-    const int tile = blockIdx.x;
-    unsigned long long ep = 0;
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
-    const Tile tl = make_tile<C, W>(a, tile, true);
-    const int ftile = tl.j * a.nCG + tl.cg;
-
-    float ATr[C][8], Gr[C][8];   // rows of A_t^T, dP_t
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int t = clampT(tl.t0 + i, a.T);
-        load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
-        load_row(a.y + tl.ablk0 + t * tl.astep, tl.v, Gr[i]);
-    }
-    // row v of P_{s-1}^T (column v of the state entering the chunk), saved by
-    // the forward in its slot order: row m of P sits in lane m's slots, column
-    // c of it at slot c ^ (m & 4)
-    float PT[C][8];
-    {
-        const float *ps = a.pstate + ((static_cast<size_t>(ftile) * NCH + tl.q) * 32 + (tl.slot & ~7)) * 8;
-        const int lo = tl.v & 4;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int m = s ^ lo;
-            PT[0][s] = ps[m * 8 + (tl.v ^ (m & 4))];
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        if (!(tl.cv && tl.t0 + i < a.T)) {
-            eye_row(tl.v, ATr[i]);
-#pragma unroll
-            for (int s = 0; s < 8; ++s) Gr[i][s] = 0.0f;
-        }
-    }
-
-    // chunk aggregate from a zero carry: X = (Psi, Wl)
-    float X[S::words];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) X[s] = ATr[C - 1][s];
-    mm8(ATr[C - 1], Gr[C - 1], X + 8);
-#pragma unroll
-    for (int i = C - 2; i >= 0; --i) {
-        float np[8], gw[8], nw[8];
-        mm8(ATr[i], X, np);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) gw[s] = Gr[i][s] + X[8 + s];
-        mm8(ATr[i], gw, nw);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) { X[s] = np[s]; X[8 + s] = nw[s]; }
-    }
-    ks_store<kMatMat, NCH>(sKS[0], tl.q, tl.slot, X);
-    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
-    __syncthreads();
-    const uint32_t tag = sTicket[0];
-
-    ks_scan<kMatMat, NCH, -1>(sKS, tl.q, tl.slot, X);   // X = composite of chunks q..NCH-1
-    // wave 0's lower half holds the tile aggregate and runs the look-back; the
-    // other waves meanwhile recompute P_{t-1}^T = P_{t-2}^T A_{t-1}^T
-    const bool lb_wave = MULTI && tl.wv == 0;
-    if (lb_wave) {
-        const bool owner = tl.sub == 0;
-        if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<S::words>(a.agg, ftile, tl.slot, tag, X);
-        float Win[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) Win[s] = 0.0f;
-        if (tl.j < a.nT - 1) {
-            float xi[8];
-            const int ps = find_inclusive<8>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, tag, &a.hd->err, xi);
-            int pend = a.nT;
-            if (ps >= 0) {
-                pend = ps;
-#pragma unroll
-                for (int s = 0; s < 8; ++s) Win[s] = xi[s];
-            }
-            constexpr int NB = 2;
-            for (int p = pend - 1; p > tl.j; p -= NB) {
-                const int cnt = min(NB, p - tl.j);
-                float ag[NB][S::words];
-                load_aggregates<S::words, NB>(a.agg, p, -1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
-#pragma unroll
-                for (int u = 0; u < NB; ++u)
-                    if (u < cnt) {
-                        float np[8];
-                        mm8(ag[u], Win, np);
-#pragma unroll
-                        for (int s = 0; s < 8; ++s) Win[s] = np[s] + ag[u][8 + s];
-                    }
-            }
-        }
-        if (owner && tl.j > 0) {
-            float Wo[8];
-            mm8(X, Win, Wo);
-#pragma unroll
-            for (int s = 0; s < 8; ++s) Wo[s] += X[8 + s];
-            publish<8>(a.incl, ftile, tl.slot, tag, Wo);
-        }
-        if (owner) {
-#pragma unroll
-            for (int s = 0; s < 8; ++s) sCarry[tl.slot][s] = Win[s];
-        }
-    } else {
-#pragma unroll
-        for (int i = 1; i < C; ++i) mm8(PT[i - 1], ATr[i - 1], PT[i]);
-    }
-    __syncthreads();
-    if (lb_wave) {
-#pragma unroll
-        for (int i = 1; i < C; ++i) mm8(PT[i - 1], ATr[i - 1], PT[i]);
-    }
-    // carry entering the chunk from its end: (composite of chunks q+1..) x (tile carry-in)
-    float Wc[8];
-    if constexpr (MULTI) {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) Wc[s] = sCarry[tl.slot][s];
-        if (tl.q < NCH - 1) {
-            float np[8];
-            mm8(sKS[FIN][tl.q + 1][tl.slot], Wc, np);
-#pragma unroll
-            for (int s = 0; s < 8; ++s) Wc[s] = np[s] + sKS[FIN][tl.q + 1][tl.slot][8 + s];
-        }
-    } else {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) Wc[s] = tl.q < NCH - 1 ? sKS[FIN][tl.q + 1][tl.slot][8 + s] : 0.0f;
-    }
-
-#pragma unroll
-    for (int i = C - 1; i >= 0; --i) {
-        const int t = tl.t0 + i;
-        const bool valid = tl.cv && t < a.T;
-        float G[8], dAr[8], nw[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) G[s] = Gr[i][s] + Wc[s];
-        mm8(G, PT[i], dAr);           // dA_t = G_t P_{t-1}^T
-        mm8(ATr[i], G, nw);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) Wc[s] = nw[s];
-        if (valid) store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, dAr);
-    }
-}
 
 __global__ void fill_zero_kernel(float *p, int64_t n)
 {
@@ -1310,30 +16,8 @@ __global__ void fill_zero_kernel(float *p, int64_t n)
     if (i < n) p[i] = 0.0f;
 }
 
-// ------------------------------------------------------------ host side
-
-// Tile geometry per op: waves per workgroup and the cap on steps per lane
-// group (a lane keeps up to 3C rows of 8 floats in registers).  Eight waves
-// per workgroup measured fastest for both block ops at both shapes.
-#ifndef MGS_AFF_W
-#define MGS_AFF_W 8
-#endif
-#ifndef MGS_AFF_MAXC
-#define MGS_AFF_MAXC 8
-#endif
-#ifndef MGS_MAT_W
-#define MGS_MAT_W 8
-#endif
-#ifndef MGS_MAT_MAXC
-#define MGS_MAT_MAXC 8
-#endif
-constexpr int kAffW = MGS_AFF_W;
-constexpr int kAffMaxC = MGS_AFF_MAXC;
-constexpr int kMatW = MGS_MAT_W;
-constexpr int kMatMaxC = MGS_MAT_MAXC;
-
 BlockGeom make_geom(int64_t B, int64_t T, int64_t d, int64_t k, int agg_words, int incl_words,
-                    int W, int max_c, bool pstate)
+                    BlkShape shape, bool pstate)
 {
     BlockGeom g{};
     g.T = static_cast<int>(T);
@@ -1341,23 +25,23 @@ BlockGeom make_geom(int64_t B, int64_t T, int64_t d, int64_t k, int agg_words, i
     g.k = static_cast<int>(k);
     g.nb = static_cast<int>(d / k);
     g.nchain = B * g.nb;
-    g.G = 4;
-    g.W = W;
-    const int nch = 2 * W;
+    g.G = static_cast<int>(32 / k);   // chains per half-wave
+    g.W = shape.W;
+    const int nch = 2 * shape.W;
     int C = 1;
-    while (C < max_c && static_cast<int64_t>(nch) * C < T) C *= 2;
+    while (C < shape.max_c && static_cast<int64_t>(nch) * C < T) C *= 2;
     g.C = C;
     g.TT = nch * C;
     g.nT = static_cast<int>((T + g.TT - 1) / g.TT);
-    g.nCG = static_cast<int>((g.nchain + 3) / 4);
+    g.nCG = static_cast<int>((g.nchain + g.G - 1) / g.G);
     g.nTiles = g.nT * g.nCG;
     g.agg_words = agg_words;
     g.incl_words = incl_words;
     size_t off = sizeof(WsHeader);
     g.off_zeros = off;   // B*d floats, never written: the h0 of calls that pass none
     off = align256(off + static_cast<size_t>(B) * d * 4);
-    g.off_pstate = off;  // cumulative product: one 8x8 state per chain per chunk
-    if (pstate) off = align256(off + static_cast<size_t>(g.nTiles) * nch * 32 * 8 * 4);
+    g.off_pstate = off;  // cumulative product: one k x k state per chain per chunk
+    if (pstate) off = align256(off + static_cast<size_t>(g.nTiles) * nch * 32 * k * 4);
     if (g.nT > 1) {
         const size_t slots = static_cast<size_t>(g.nTiles) * 32;
         g.off_agg = off;  off = align256(off + slots * agg_words * 8);
@@ -1383,8 +67,13 @@ BlkArgs base_args(const BlockGeom &g, void *ws)
     return a;
 }
 
-// Launcher of one kernel family for every chunk length C <= MAXC.
-#define MGS_DEFINE_LAUNCHER(NAME, KERNEL)                                                         \
+const float *zeros_or(const BlockGeom &g, void *ws, const float *h0)
+{
+    return h0 ? h0 : reinterpret_cast<const float *>(static_cast<char *>(ws) + g.off_zeros);
+}
+
+// Givens kernels: template <int C, int W, bool MULTI>, k = 8.
+#define MGS_DEFINE_GIVENS_LAUNCHER(NAME, KERNEL)                                                  \
     template <int W, int C>                                                                       \
     void NAME##_c(const BlockGeom &g, const BlkArgs &a, hipStream_t s)                            \
     {                                                                                             \
@@ -1405,23 +94,43 @@ BlkArgs base_args(const BlockGeom &g, void *ws)
         }                                                                                         \
     }
 
-MGS_DEFINE_LAUNCHER(launch_baffine_fwd, baffine_fwd_kernel)
-MGS_DEFINE_LAUNCHER(launch_baffine_bwd, baffine_bwd_kernel)
-MGS_DEFINE_LAUNCHER(launch_bgivens_fwd, bgivens_fwd_kernel)
-MGS_DEFINE_LAUNCHER(launch_bgivens_bwd, bgivens_bwd_kernel)
-MGS_DEFINE_LAUNCHER(launch_bmatrix_fwd, bmatrix_fwd_kernel)
-MGS_DEFINE_LAUNCHER(launch_bmatrix_bwd, bmatrix_bwd_kernel)
+MGS_DEFINE_GIVENS_LAUNCHER(launch_bgivens_fwd, bgivens_fwd_kernel)
+MGS_DEFINE_GIVENS_LAUNCHER(launch_bgivens_bwd, bgivens_bwd_kernel)
+
+// one block op for the geometry's block size
+void launch_blk_any(BlkOp op, const BlockGeom &g, const BlkArgs &a, hipStream_t s)
+{
+    switch (g.k) {
+    case 1: launch_blk<1>(op, g, a, s); break;
+    case 2: launch_blk<2>(op, g, a, s); break;
+    case 4: launch_blk<4>(op, g, a, s); break;
+    case 8: launch_blk<8>(op, g, a, s); break;
+    default: launch_blk<16>(op, g, a, s); break;
+    }
+}
 
 }  // namespace
 
+template <>
+void launch_blk<8>(BlkOp op, const BlockGeom &g, const BlkArgs &a, hipStream_t s)
+{
+    launch_blk_impl<8>(op, g, a, s);
+}
+
+bool block_k_supported(int64_t k)
+{
+    return k == 1 || k == 2 || k == 4 || k == 8 || k == 16;
+}
+
 BlockGeom block_affine_geometry(int64_t B, int64_t T, int64_t d, int64_t k)
 {
-    return make_geom(B, T, d, k, 9, 1, kAffW, kAffMaxC, false);
+    return make_geom(B, T, d, k, static_cast<int>(k) + 1, 1, affine_shape(static_cast<int>(k)), false);
 }
 
 BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k)
 {
-    return make_geom(B, T, d, k, 16, 8, kMatW, kMatMaxC, true);
+    return make_geom(B, T, d, k, 2 * static_cast<int>(k), static_cast<int>(k), matrix_shape(static_cast<int>(k)),
+                     true);
 }
 
 hipError_t launch_block_affine_fwd(const BlockGeom &g, const float *A, const float *b,
@@ -1429,8 +138,8 @@ hipError_t launch_block_affine_fwd(const BlockGeom &g, const float *A, const flo
 {
     BlkArgs a = base_args(g, ws);
     a.A = A; a.x = b; a.out = h;
-    a.h0 = h0 ? h0 : reinterpret_cast<const float *>(static_cast<char *>(ws) + g.off_zeros);
-    launch_baffine_fwd<kAffW, kAffMaxC>(g, a, s);
+    a.h0 = zeros_or(g, ws, h0);
+    launch_blk_any(BlkOp::AffineFwd, g, a, s);
     return hipGetLastError();
 }
 
@@ -1440,18 +149,19 @@ hipError_t launch_block_affine_bwd(const BlockGeom &g, const float *A, const flo
 {
     BlkArgs a = base_args(g, ws);
     a.A = A; a.x = h; a.y = dh; a.out = dA; a.out2 = db; a.out3 = dh0;
-    a.h0 = h0 ? h0 : reinterpret_cast<const float *>(static_cast<char *>(ws) + g.off_zeros);
-    launch_baffine_bwd<kAffW, kAffMaxC>(g, a, s);
+    a.h0 = zeros_or(g, ws, h0);
+    launch_blk_any(BlkOp::AffineBwd, g, a, s);
     return hipGetLastError();
 }
 
 hipError_t launch_givens_fwd(const BlockGeom &g, const float *theta, const float *sg, const float *b,
                              const float *h0, float *h, void *ws, hipStream_t s)
 {
+    constexpr BlkShape af = affine_shape(8);
     BlkArgs a = base_args(g, ws);
     a.theta = theta; a.sg = sg; a.x = b; a.out = h;
-    a.h0 = h0 ? h0 : reinterpret_cast<const float *>(static_cast<char *>(ws) + g.off_zeros);
-    launch_bgivens_fwd<kAffW, kAffMaxC>(g, a, s);
+    a.h0 = zeros_or(g, ws, h0);
+    launch_bgivens_fwd<af.W, af.max_c>(g, a, s);
     return hipGetLastError();
 }
 
@@ -1459,11 +169,12 @@ hipError_t launch_givens_bwd(const BlockGeom &g, const float *theta, const float
                              const float *h, const float *dh, float *dtheta, float *dsg, float *db,
                              float *dh0, void *ws, hipStream_t s)
 {
+    constexpr BlkShape af = affine_shape(8);
     BlkArgs a = base_args(g, ws);
     a.theta = theta; a.sg = sg; a.x = h; a.y = dh;
     a.dtheta = dtheta; a.dsg = dsg; a.out2 = db; a.out3 = dh0;
-    a.h0 = h0 ? h0 : reinterpret_cast<const float *>(static_cast<char *>(ws) + g.off_zeros);
-    launch_bgivens_bwd<kAffW, kAffMaxC>(g, a, s);
+    a.h0 = zeros_or(g, ws, h0);
+    launch_bgivens_bwd<af.W, af.max_c>(g, a, s);
     return hipGetLastError();
 }
 
@@ -1472,7 +183,7 @@ hipError_t launch_block_matrix_fwd(const BlockGeom &g, const float *A, float *P,
 {
     BlkArgs a = base_args(g, ws);
     a.A = A; a.out = P;
-    launch_bmatrix_fwd<kMatW, kMatMaxC>(g, a, s);
+    launch_blk_any(BlkOp::MatrixFwd, g, a, s);
     return hipGetLastError();
 }
 
@@ -1482,13 +193,13 @@ hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const flo
     if (!fwd_state_valid) {
         BlkArgs f = base_args(g, ws);
         f.A = A; f.out = nullptr;    // chunk states only
-        launch_bmatrix_fwd<kMatW, kMatMaxC>(g, f, s);
+        launch_blk_any(BlkOp::MatrixFwd, g, f, s);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     BlkArgs a = base_args(g, ws);
     a.A = A; a.y = dP; a.out = dA;
-    launch_bmatrix_bwd<kMatW, kMatMaxC>(g, a, s);
+    launch_blk_any(BlkOp::MatrixBwd, g, a, s);
     return hipGetLastError();
 }
 

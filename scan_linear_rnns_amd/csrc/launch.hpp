@@ -50,7 +50,7 @@ hipError_t launch_linear_bwd(const LogGeom &g, const float *a, const float *b, c
 struct BlockGeom {
     int64_t nchain; // B * d/k
     int T, d, k, nb;
-    int G;          // chains per wave (64 / k)
+    int G;          // chains per half-wave (32 / k)
     int C;          // steps per lane group
     int W;          // waves (chunks) per workgroup
     int TT;         // steps per tile
@@ -63,6 +63,9 @@ struct BlockGeom {
     int agg_words;  // tagged words per chain per tile in the aggregate
     int incl_words; // tagged words per chain per tile in the inclusive prefix
 };
+
+// block sizes the block ops are built for: k in {1, 2, 4, 8, 16}
+bool block_k_supported(int64_t k);
 
 BlockGeom block_affine_geometry(int64_t B, int64_t T, int64_t d, int64_t k);
 BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k);

@@ -245,9 +245,16 @@ static mgs_status check_block_sizes(int64_t B, int64_t T, int64_t d, int64_t k)
 {
     if (B < 0 || T < 0 || d < 0 || k <= 0) return MGS_ERR_INVALID_VALUE;
     if (d % k != 0) return MGS_ERR_INVALID_VALUE;
-    if (k != 8) return MGS_ERR_UNSUPPORTED;
+    if (!mgs::block_k_supported(k)) return MGS_ERR_UNSUPPORTED;
     if (B * T * d * k > kMaxElems) return MGS_ERR_UNSUPPORTED;
     return MGS_OK;
+}
+
+// The Givens angle-fused scan is built for 8 x 8 blocks (28 angles) only.
+static mgs_status check_givens_sizes(int64_t B, int64_t T, int64_t d, int64_t k)
+{
+    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
+    return k == 8 ? MGS_OK : MGS_ERR_UNSUPPORTED;
 }
 
 mgs_status mgs_block_affine_scan_workspace_size(int64_t B, int64_t T, int64_t d, int64_t k,
@@ -311,6 +318,8 @@ static void givens_bytes(int64_t B, int64_t T, int64_t d, int64_t k, size_t &nth
 
 mgs_status mgs_givens_scan_workspace_size(int64_t B, int64_t T, int64_t d, int64_t k, size_t *bytes)
 {
+    if (!bytes) return MGS_ERR_INVALID_VALUE;
+    if (mgs_status st = check_givens_sizes(B, T, d, k)) return st;
     return mgs_block_affine_scan_workspace_size(B, T, d, k, bytes);
 }
 
@@ -318,7 +327,7 @@ mgs_status mgs_givens_scan_fwd(const float *theta, const float *s, const float *
                                float *h, int64_t B, int64_t T, int64_t d, int64_t k, void *workspace,
                                size_t workspace_bytes, void *stream)
 {
-    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
+    if (mgs_status st = check_givens_sizes(B, T, d, k)) return st;
     const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
     size_t nth, ns;
     givens_bytes(B, T, d, k, nth, ns);
@@ -338,7 +347,7 @@ mgs_status mgs_givens_scan_bwd(const float *theta, const float *s, const float *
                                int64_t B, int64_t T, int64_t d, int64_t k, void *workspace,
                                size_t workspace_bytes, void *stream)
 {
-    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
+    if (mgs_status st = check_givens_sizes(B, T, d, k)) return st;
     const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
     size_t nth, ns;
     givens_bytes(B, T, d, k, nth, ns);

@@ -68,7 +68,11 @@ def test_workspace_queries(lib):
         st, b2 = _size(lib, fn, 16, 1024, 64, 8)
         assert st == OK and b2 > 256
         assert _size(lib, fn, 2, 4, 12, 8)[0] == INVALID       # d % k != 0
-        assert _size(lib, fn, 2, 4, 16, 4)[0] == UNSUPPORTED   # k outside the envelope
+        for k in (1, 2, 4, 8, 16):                             # the envelope
+            st, bk = _size(lib, fn, 16, 1024, 64, k)
+            assert st == OK and bk > 256, k
+        assert _size(lib, fn, 2, 4, 12, 6)[0] == UNSUPPORTED   # k outside the envelope
+        assert _size(lib, fn, 2, 4, 64, 32)[0] == UNSUPPORTED
         assert _size(lib, fn, 2, 4, 16, 0)[0] == INVALID
         assert _size(lib, fn, 1 << 16, 1 << 10, 64, 8)[0] == UNSUPPORTED
 
@@ -115,7 +119,8 @@ def test_block_validation(lib):
     assert fwd(A=None) == INVALID
     assert fwd(b=None) == INVALID
     assert fwd(h=fake(1)) == INVALID
-    assert fwd(k=4) == UNSUPPORTED
+    assert fwd(k=32, d=64) == UNSUPPORTED
+    assert fwd(k=3, d=12) == UNSUPPORTED
     assert fwd(d=12) == INVALID
     assert fwd(nbytes=0) == WORKSPACE
     assert fwd(ws=fake(9, 8)) == INVALID                    # misaligned workspace
@@ -125,11 +130,11 @@ def test_block_validation(lib):
     assert bwd(dA=fake(0)) == INVALID
     assert bwd(dh0=None) == INVALID
     assert bwd(nbytes=1) == WORKSPACE
-    mf = lambda P=fake(1), k=k, nbytes=1 << 20: lib.mgs_block_matrix_scan_fwd(fake(0), P, B, T, d, k, fake(9),
-                                                                             nbytes, None)
+    mf = lambda P=fake(1), k=k, d=d, nbytes=1 << 20: lib.mgs_block_matrix_scan_fwd(fake(0), P, B, T, d, k,
+                                                                                  fake(9), nbytes, None)
     assert mf(P=None) == INVALID
     assert mf(P=fake(0)) == INVALID
-    assert mf(k=16) == UNSUPPORTED
+    assert mf(k=32, d=64) == UNSUPPORTED
     assert mf(nbytes=2) == WORKSPACE
     mb = lambda dP=fake(2), dA=fake(3), nbytes=1 << 20: lib.mgs_block_matrix_scan_bwd(
         fake(0), dP, dA, B, T, d, k, fake(9), nbytes, 1, None)

@@ -67,25 +67,26 @@ def test_log_scan_graph_replays(gpu):
     assert mgs.mgs_workspace_check(ws) == 0
 
 
-def test_block_scans_graph_replays(gpu):
+@pytest.mark.parametrize("k", [8, 16, 2])
+def test_block_scans_graph_replays(gpu, k):
     import torch
     import scan_linear_rnns_amd as mgs
-    print("[graph] block scans B=16 T=1024 d=64", flush=True)
-    inp = block_inputs(16, 1024, 64, seed=22, h0="normal")
+    print(f"[graph] block scans B=16 T=1024 d=64 k={k}", flush=True)
+    inp = block_inputs(16, 1024, 64, k=k, seed=22, h0="normal")
     A, b, h0, dh, dP = (_t(x, gpu) for x in (inp.A, inp.b, inp.h0, inp.dh, inp.dP))
-    h, ws = mgs.mgs_block_affine_scan_fwd(A, b, h0)
-    gref = mgs.mgs_block_affine_scan_bwd(A, b, h0, h, dh, ws=ws)
-    P, wsm = mgs.mgs_block_matrix_scan_fwd(A)
-    dAm = mgs.mgs_block_matrix_scan_bwd(A, dP, ws=wsm, fwd_state_valid=True)
+    h, ws = mgs.mgs_block_affine_scan_fwd(A, b, h0, k=k)
+    gref = mgs.mgs_block_affine_scan_bwd(A, b, h0, h, dh, k=k, ws=ws)
+    P, wsm = mgs.mgs_block_matrix_scan_fwd(A, k=k)
+    dAm = mgs.mgs_block_matrix_scan_bwd(A, dP, k=k, ws=wsm, fwd_state_valid=True)
     ref = [h.clone(), *[x.clone() for x in gref], P.clone(), dAm.clone()]
     outs = [torch.empty_like(h), torch.empty_like(A), torch.empty_like(b), torch.empty_like(h0),
             torch.empty_like(A), torch.empty_like(A)]
 
     def step():
-        mgs.mgs_block_affine_scan_fwd(A, b, h0, h=outs[0], ws=ws)
-        mgs.mgs_block_affine_scan_bwd(A, b, h0, outs[0], dh, ws=ws, out=(outs[1], outs[2], outs[3]))
-        mgs.mgs_block_matrix_scan_fwd(A, P=outs[4], ws=wsm)
-        mgs.mgs_block_matrix_scan_bwd(A, dP, ws=wsm, fwd_state_valid=True, dA=outs[5])
+        mgs.mgs_block_affine_scan_fwd(A, b, h0, k=k, h=outs[0], ws=ws)
+        mgs.mgs_block_affine_scan_bwd(A, b, h0, outs[0], dh, k=k, ws=ws, out=(outs[1], outs[2], outs[3]))
+        mgs.mgs_block_matrix_scan_fwd(A, k=k, P=outs[4], ws=wsm)
+        mgs.mgs_block_matrix_scan_bwd(A, dP, k=k, ws=wsm, fwd_state_valid=True, dA=outs[5])
 
     for got in _replays(step, outs):
         for a, b_ in zip(got, ref):
