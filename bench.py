@@ -69,17 +69,17 @@ def compulsory_bytes(op, B, T, d, k=8):
 class OpRun:
     """M rotated buffer sets of one op with prebuilt ctypes argument lists."""
 
-    def __init__(self, name, op, B, T, d, dev, rotate=True):
+    def __init__(self, name, op, B, T, d, dev, rotate=True, k=8):
         import numpy as np
         import torch
 
         import scan_linear_rnns_amd as mgs
         from synthetic import block_inputs, linear_inputs, log_inputs, mingru_inputs
 
-        self.name, self.op, self.B, self.T, self.d = name, op, B, T, d
+        self.name, self.op, self.B, self.T, self.d, self.k = name, op, B, T, d, k
         self.N = B * T * d
         self.lib = mgs.load()
-        self.fwd_bytes, self.bwd_bytes = compulsory_bytes(op, B, T, d)
+        self.fwd_bytes, self.bwd_bytes = compulsory_bytes(op, B, T, d, k)
         t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
         P = lambda x: ctypes.c_void_p(x.data_ptr())
         if op == "log":
@@ -99,10 +99,10 @@ class OpRun:
             base = [t(inp.a), t(inp.b), t(inp.h0), t(inp.dh)]
             ws_bytes = mgs.mgs_scan_linear_workspace_size(B, T, d)
         else:
-            inp = block_inputs(B, T, d, k=8, seed=0, with_dP=(op == "matrix"))
+            inp = block_inputs(B, T, d, k=k, seed=0, with_dP=(op == "matrix"))
             base = [t(inp.A), t(inp.b), t(inp.dh)] + ([t(inp.dP)] if op == "matrix" else [])
             sz = mgs.mgs_block_affine_scan_workspace_size if op == "affine" else mgs.mgs_block_matrix_scan_workspace_size
-            ws_bytes = sz(B, T, d, 8)
+            ws_bytes = sz(B, T, d, k)
         per_set = sum(x.numel() * 4 for x in base) * 2
         self.M = max(1, math.ceil(ROTATE_BYTES / per_set)) if rotate else 1
         self.sets = []
@@ -132,15 +132,15 @@ class OpRun:
                 A, b, dh = xs
                 h = torch.empty_like(b)
                 dA, db, dh0 = torch.empty_like(A), torch.empty_like(b), torch.empty((B, d), device=dev)
-                fa = (P(A), P(b), None, P(h), B, T, d, 8, P(ws), ws.numel())
-                ba = (P(A), None, None, P(h), P(dh), P(dA), P(db), P(dh0), B, T, d, 8, P(ws), ws.numel())
+                fa = (P(A), P(b), None, P(h), B, T, d, k, P(ws), ws.numel())
+                ba = (P(A), None, None, P(h), P(dh), P(dA), P(db), P(dh0), B, T, d, k, P(ws), ws.numel())
                 fn_f, fn_b = self.lib.mgs_block_affine_scan_fwd, self.lib.mgs_block_affine_scan_bwd
                 keep = xs + [h, dA, db, dh0, ws]
             else:
                 A, b, dh, dP = xs
                 Pm, dA = torch.empty_like(A), torch.empty_like(A)
-                fa = (P(A), P(Pm), B, T, d, 8, P(ws), ws.numel())
-                ba = (P(A), P(dP), P(dA), B, T, d, 8, P(ws), ws.numel(), 1)
+                fa = (P(A), P(Pm), B, T, d, k, P(ws), ws.numel())
+                ba = (P(A), P(dP), P(dA), B, T, d, k, P(ws), ws.numel(), 1)
                 fn_f, fn_b = self.lib.mgs_block_matrix_scan_fwd, self.lib.mgs_block_matrix_scan_bwd
                 keep = xs + [Pm, dA, ws]
             self.sets.append((fn_f, fa, fn_b, ba))
@@ -343,6 +343,11 @@ def main():
         ("givens_lab", "givens", 128, 64, 64),
         ("givens_longT", "givens", 16, 1024, 64),
         ("matrix_longT", "matrix", 16, 1024, 64),
+        # the block ops at the other block sizes of the envelope, long-T shape
+        ("affine_k16_longT", "affine", 16, 1024, 64, 16),
+        ("matrix_k16_longT", "matrix", 16, 1024, 64, 16),
+        ("affine_k4_longT", "affine", 16, 1024, 64, 4),
+        ("affine_k1_longT", "affine", 16, 1024, 64, 1),
     ]
     if args.no_ops:
         specs = specs[:1]
@@ -351,22 +356,24 @@ def main():
 
     ops = {}
     head = None
-    for name, op, B, T, d in specs:
+    for name, op, B, T, d, *kk in specs:
+        k = kk[0] if kk else 8
         log(f"op {name}: building buffers")
-        run = OpRun(name, op, B, T, d, dev)
+        run = OpRun(name, op, B, T, d, dev, k=k)
         run.prime()
         steps = K if name == "log_lab" else max(20, K // 2)
         pair = graph_time(run, "pair", steps, W)
         fwd = graph_time(run, "fwd", steps, W)
         bwd = graph_time(run, "bwd", steps, W)
         eager = stream_time(run, "pair", steps, W)
-        warm_run = OpRun(name + "_warm", op, B, T, d, dev, rotate=False)
+        warm_run = OpRun(name + "_warm", op, B, T, d, dev, rotate=False, k=k)
         warm_run.prime()
         warm = graph_time(warm_run, "pair", steps, W)
         del warm_run
         tot = run.fwd_bytes + run.bwd_bytes
         rec = {
-            "B": B, "T": T, "d": d, "buffer_sets": run.M, "steps": steps,
+            "B": B, "T": T, "d": d, "k": k if op in ("affine", "matrix", "givens") else None,
+            "buffer_sets": run.M, "steps": steps,
             "us_per_fwd_bwd": pair, "us_fwd": fwd, "us_bwd": bwd,
             "us_per_fwd_bwd_eager_launch": eager, "us_per_fwd_bwd_warm": warm,
             "elems_per_s": run.N / (pair * 1e-6),
@@ -377,9 +384,9 @@ def main():
             "bwd_roofline_frac": run.bwd_bytes / (bwd * 1e-6) / 1e9 / PEAK_GBPS,
         }
         if op == "matrix":
-            rec["op"] = "block cumulative product (b = 0), k = 8"
+            rec["op"] = f"block cumulative product (b = 0), k = {k}"
         elif op == "affine":
-            rec["op"] = "block-affine scan, k = 8"
+            rec["op"] = f"block-affine scan, k = {k}"
         elif op == "givens":
             rec["op"] = "Givens angle-fused block-affine scan (inputs theta, s), k = 8"
         elif op == "linear":
