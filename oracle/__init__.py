@@ -28,6 +28,9 @@ What each function follows is stated in ``oracle.c``:
     home page).
   * ``block_matrix_fwd`` / ``block_matrix_bwd`` -- P_t = A_t P_{t-1},
     P_0 = I (matrix_scan in the same table).
+  * ``delta_fwd`` -- the delta rule of DeltaMinGRU (home page: DeltaNet's
+    recurrence, whose chunked WY form is the parallel forward):
+    S_t = S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T, o_t = S_t q_t.
 
 Parity pins: every function here is pinned against closed forms, special
 cases reducing to numpy routines, brute-force products, finite differences and
@@ -83,6 +86,7 @@ def _load():
                 "oracle_block_affine_bwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I],
                 "oracle_block_matrix_fwd": [_D, _D, _I, _I, _I, _I],
                 "oracle_block_matrix_bwd": [_D, _D, _D, _I, _I, _I, _I],
+                "oracle_delta_fwd": [_D, _D, _D, _D, _D, _D, _D, _I, _I, _I, _I],
             }
             for name, args in sig.items():
                 fn = getattr(lib, name)
@@ -268,3 +272,17 @@ def givens_matrix(theta, s, k):
             out[:, t, :, :, c] = col.reshape(B, nb, k)
     return out
 
+
+
+def delta_fwd(q, k, v, beta, S0=None):
+    """(o (B,T,dv), S_T (B,dv,dk)) of the delta rule; S0 (B,dv,dk) or None (zeros)."""
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    S0 = None if S0 is None else _f64(S0)
+    B, T, dk = k.shape
+    dv = v.shape[2]
+    assert q.shape == k.shape and v.shape[:2] == (B, T) and beta.shape == (B, T)
+    assert S0 is None or S0.shape == (B, dv, dk)
+    o = np.empty((B, T, dv), np.float64)
+    ST = np.empty((B, dv, dk), np.float64)
+    _load().oracle_delta_fwd(_p(q), _p(k), _p(v), _p(beta), _p(S0), _p(o), _p(ST), B, T, dk, dv)
+    return o, ST

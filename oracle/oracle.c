@@ -35,6 +35,15 @@
  *     angles taken in (layer, pair) order, each rotation mapping (x_i, x_j) to
  *     (cos x_i - sin x_j, sin x_i + cos x_j).  The pages name the mesh but do
  *     not fix these conventions; this is the reading taken.
+ *   - The delta-rule recurrence of DeltaMinGRU (same page: DeltaMinGRU
+ *     reimplements DeltaNet, Yang et al. 2024, arXiv:2406.06484, and uses its
+ *     chunked WY representation as the parallel forward).  The pages do not
+ *     write the recurrence out; the reading taken is DeltaNet's delta rule
+ *     with a matrix state S (dv x dk):
+ *         S_t = S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T,   o_t = S_t q_t,
+ *     i.e. S_t = S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.  The
+ *     chunked WY form is a re-association of this loop (exact in real
+ *     arithmetic), so the oracle runs the loop itself.
  *   - Gradients are the chain rule applied to these loops for the loss
  *     L = sum_t <dh_t, h_t> (resp. sum_t <dP_t, P_t>).
  *
@@ -47,6 +56,8 @@
  *   block ops:  A, dA, P, dP : (B, T, nb, k, k) with nb = d / k and
  *               (A h)_r = sum_c A[r][c] h[c];  b, h, dh, db : (B, T, d);
  *               h0, dh0 : (B, d);  block j owns channels [j*k, (j+1)*k).
+ *   delta rule: q, k : (B, T, dk);  v, o : (B, T, dv);  beta : (B, T);
+ *               S0, ST : (B, dv, dk), (S k)_r = sum_c S[r][c] k[c].
  * Inputs are the same fp32 arrays the GPU sees, widened exactly to double.
  * Loops over t are sequential; there is no blocking, fusion or reordering.
  */
@@ -520,4 +531,44 @@ void oracle_givens_bwd(const double *theta, const double *sg, const double *bv, 
     free(dR);
     free(g);
     free(w);
+}
+
+/* ----------------------------------------------------------- delta rule */
+
+/* Forward: S_0 = S0 (zero if S0 == NULL); for t = 1..T
+ *     p = S_{t-1} k_t,   S_t = S_{t-1} + beta_t (v_t - p) k_t^T,   o_t = S_t q_t;
+ * writes o_1..T and, if ST != NULL, the final state S_T. */
+void oracle_delta_fwd(const double *q, const double *k, const double *v, const double *beta,
+                      const double *S0, double *o, double *ST,
+                      int64_t B, int64_t T, int64_t dk, int64_t dv)
+{
+    double *S = (double *)malloc(sizeof(double) * (size_t)(dv * dk));
+    double *p = (double *)malloc(sizeof(double) * (size_t)dv);
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t i = 0; i < dv * dk; ++i) S[i] = S0 ? S0[b * dv * dk + i] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const double *kt = k + (b * T + t) * dk;
+            const double *qt = q + (b * T + t) * dk;
+            const double *vt = v + (b * T + t) * dv;
+            double bt = beta[b * T + t];
+            for (int64_t r = 0; r < dv; ++r) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < dk; ++c) acc += S[r * dk + c] * kt[c];
+                p[r] = acc;
+            }
+            for (int64_t r = 0; r < dv; ++r) {
+                double e = bt * (vt[r] - p[r]);
+                for (int64_t c = 0; c < dk; ++c) S[r * dk + c] += e * kt[c];
+            }
+            for (int64_t r = 0; r < dv; ++r) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < dk; ++c) acc += S[r * dk + c] * qt[c];
+                o[(b * T + t) * dv + r] = acc;
+            }
+        }
+        if (ST)
+            for (int64_t i = 0; i < dv * dk; ++i) ST[b * dv * dk + i] = S[i];
+    }
+    free(S);
+    free(p);
 }

@@ -20,6 +20,8 @@ once to float32 at the end):
   scan (k, x, x0, dh in that order); the MinGRU gate sigmoid(-k) in [0, 1] is
   stretched to a = 2 sigmoid(-k) - 1 in (-1, 1), b = (1 - sigmoid(-k)) g(x),
   h0 = g(x0).
+* Delta rule (DeltaMinGRU on the home page, DeltaNet's recurrence): see
+  delta_inputs.
 * Block scans (GivensMinGRU on the home page; the Clements rectangular mesh of
   Givens rotations).  Draw s ~ N(0,1) of shape (B,T,nb), theta ~ U(-pi, pi) of
   shape (B,T,nb,k(k-1)/2), b ~ N(0,1) of shape (B,T,d), dh ~ N(0,1) of shape
@@ -185,6 +187,34 @@ def block_inputs(B: int, T: int, d: int, k: int = 8, seed: int = 0, *,
                        theta.astype(f) if return_angles else None, s.astype(f) if return_angles else None)
 
 
+@dataclass
+class DeltaInputs:
+    q: np.ndarray       # (B,T,d) float32, unit rows
+    k: np.ndarray       # (B,T,d) float32, unit rows
+    v: np.ndarray       # (B,T,d) float32
+    beta: np.ndarray    # (B,T)   float32, in (0, 1)
+    S0: Optional[np.ndarray]  # (B,d,d) float32 or None (zeros)
+
+
+def delta_inputs(B: int, T: int, d: int, seed: int = 0, *, s0: str = "zero") -> DeltaInputs:
+    """Delta-rule generator (DeltaMinGRU on the home page; DeltaNet's
+    normalisation): q, k, v ~ N(0,1) of shape (B,T,d) in that order, then
+    u ~ N(0,1) of shape (B,T), then (s0="normal") S0 ~ N(0,1) of shape (B,d,d).
+    q and k are scaled to unit L2 norm per step, beta = sigmoid(u)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, T, d))
+    k = rng.standard_normal((B, T, d))
+    v = rng.standard_normal((B, T, d))
+    u = rng.standard_normal((B, T))
+    S0 = rng.standard_normal((B, d, d)) if s0 == "normal" else None
+    q = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    k = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    beta = 1.0 / (1.0 + np.exp(-u))
+    f = np.float32
+    return DeltaInputs(q.astype(f), k.astype(f), v.astype(f), beta.astype(f),
+                       None if S0 is None else S0.astype(f))
+
+
 # The five workloads, by name (shapes from the pages' lab and long-T
 # microbenchmark shapes, d = 64 and k = 8 from the Givens memory measurement).
 CONFIGS = {
@@ -197,4 +227,6 @@ CONFIGS = {
     "linear_longT": dict(op="linear", B=16, T=1024, d=64),
     "block_lab":  dict(op="block", B=128, T=64, d=64, k=8),
     "block_longT": dict(op="block", B=16, T=1024, d=64, k=8),
+    "delta_lab":   dict(op="delta", B=128, T=64, d=64),
+    "delta_longT": dict(op="delta", B=16, T=1024, d=64),
 }

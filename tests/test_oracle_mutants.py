@@ -17,6 +17,7 @@ from tests import test_oracle_pins as pins
 from tests import test_oracle_pins_linear as lpins
 from tests import test_oracle_pins_mingru as mpins
 from tests import test_oracle_pins_givens as gpins
+from tests import test_oracle_pins_delta as dpins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -60,6 +61,23 @@ MUTANTS = [
     ("cumprod_bwd G P not G P^T", "s += G[r * k + m] * Ps[t * kk + c * k + m];",
      "s += G[r * k + m] * Ps[t * kk + m * k + c];"),
     ("cumprod_bwd A not A^T", "s += At[m * k + r] * G[m * k + c];", "s += At[r * k + m] * G[m * k + c];"),
+    ("delta drops beta", "double e = bt * (vt[r] - p[r]);", "double e = (vt[r] - p[r]);"),
+    ("delta correction sign", "double e = bt * (vt[r] - p[r]);", "double e = bt * (vt[r] + p[r]);"),
+    ("delta reads with q", "for (int64_t c = 0; c < dk; ++c) acc += S[r * dk + c] * kt[c];",
+     "for (int64_t c = 0; c < dk; ++c) acc += S[r * dk + c] * qt[c];"),
+    ("delta writes along q", "for (int64_t c = 0; c < dk; ++c) S[r * dk + c] += e * kt[c];",
+     "for (int64_t c = 0; c < dk; ++c) S[r * dk + c] += e * qt[c];"),
+    ("delta output from S_{t-1}",
+     "            for (int64_t r = 0; r < dv; ++r) {\n                double e = bt * (vt[r] - p[r]);\n"
+     "                for (int64_t c = 0; c < dk; ++c) S[r * dk + c] += e * kt[c];\n            }\n"
+     "            for (int64_t r = 0; r < dv; ++r) {\n                double acc = 0.0;\n"
+     "                for (int64_t c = 0; c < dk; ++c) acc += S[r * dk + c] * qt[c];\n"
+     "                o[(b * T + t) * dv + r] = acc;\n            }\n",
+     "            for (int64_t r = 0; r < dv; ++r) {\n                double acc = 0.0;\n"
+     "                for (int64_t c = 0; c < dk; ++c) acc += S[r * dk + c] * qt[c];\n"
+     "                o[(b * T + t) * dv + r] = acc;\n            }\n"
+     "            for (int64_t r = 0; r < dv; ++r) {\n                double e = bt * (vt[r] - p[r]);\n"
+     "                for (int64_t c = 0; c < dk; ++c) S[r * dk + c] += e * kt[c];\n            }\n"),
 ]
 
 PINS = [
@@ -81,6 +99,9 @@ PINS = [
     gpins.test_golden_k2,
     gpins.test_matrices_match_numpy_mesh,
     gpins.test_gradients_finite_difference,
+    dpins.test_golden_delta_rule,
+    dpins.test_closed_form_householder_products,
+    dpins.test_unit_key_full_write,
 ]
 
 
@@ -104,7 +125,8 @@ def test_mutant_is_caught(name, orig, mut, monkeypatch):
         for fname in ("oracle_log_fwd", "oracle_log_bwd", "oracle_linear_fwd", "oracle_linear_bwd",
                       "oracle_mingru_fwd", "oracle_mingru_bwd", "oracle_givens_fwd", "oracle_givens_bwd",
                       "oracle_block_affine_fwd",
-                      "oracle_block_affine_bwd", "oracle_block_matrix_fwd", "oracle_block_matrix_bwd"):
+                      "oracle_block_affine_bwd", "oracle_block_matrix_fwd", "oracle_block_matrix_bwd",
+                      "oracle_delta_fwd"):
             fn, ref = getattr(lib, fname), getattr(real, fname)
             fn.argtypes, fn.restype = ref.argtypes, ref.restype
         monkeypatch.setattr(oracle, "_lib", lib)
