@@ -288,6 +288,30 @@ mgs_status mgs_block_matrix_scan_bwd(const float *A, const float *dP, float *dA,
                                      void *workspace, size_t workspace_bytes, int fwd_state_valid,
                                      void *stream);
 
+/* ------------------------------------------------------------ delta rule --- */
+/*
+ * Forward of the delta rule of DeltaMinGRU (minGRU home page: DeltaMinGRU
+ * reimplements DeltaNet and runs DeltaNet's chunked WY representation as its
+ * parallel forward; the pages do not write the recurrence out, this is
+ * DeltaNet's):
+ *     S_0 = S0 (zeros if S0 == NULL),
+ *     S_t = S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T,     o_t = S_t q_t,
+ * one state S (d x d, (S k)_r = sum_c S[r][c] k[c]) per sequence, evaluated in
+ * chunks of 64 steps in the WY form.  q and k are used as given (DeltaNet
+ * scales them to unit norm beforehand; the op does not).
+ *   q, k, v : (B,T,d) in;  beta : (B,T) in;  S0 : (B,d,d) in or NULL;
+ *   o : (B,T,d) out;  ST : (B,d,d) out (the final state S_T) or NULL.
+ * Envelope: d == 64.  The workspace holds per (sequence, chunk) the chunk's
+ * state-free WY factors; it carries nothing between calls (zero-filling is
+ * not needed, though harmless).
+ */
+mgs_status mgs_delta_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes);
+
+mgs_status mgs_delta_fwd(const float *q, const float *k, const float *v, const float *beta,
+                         const float *S0, float *o, float *ST,
+                         int64_t B, int64_t T, int64_t d,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

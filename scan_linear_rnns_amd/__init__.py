@@ -13,6 +13,7 @@ Ops (see include/mgs.h for the definitions and their sources on the pages):
   * mgs_block_affine_scan_fwd / mgs_block_affine_scan_bwd   h_t = A_t h_{t-1} + b_t
   * mgs_givens_scan_fwd / mgs_givens_scan_bwd           same, A_t = sigmoid(s_t) R(theta_t) formed in-kernel
   * mgs_block_matrix_scan_fwd / mgs_block_matrix_scan_bwd   P_t = A_t P_{t-1}
+  * mgs_delta_fwd                                       delta rule (DeltaNet), chunked WY forward
 """
 from __future__ import annotations
 
@@ -29,6 +30,7 @@ __all__ = [
     "mgs_block_affine_scan_workspace_size", "mgs_block_affine_scan_fwd", "mgs_block_affine_scan_bwd",
     "mgs_givens_scan_workspace_size", "mgs_givens_scan_fwd", "mgs_givens_scan_bwd",
     "mgs_block_matrix_scan_workspace_size", "mgs_block_matrix_scan_fwd", "mgs_block_matrix_scan_bwd",
+    "mgs_delta_workspace_size", "mgs_delta_fwd",
 ]
 
 
@@ -378,3 +380,34 @@ def mgs_block_matrix_scan_bwd(A, dP, k=8, ws=None, fwd_state_valid=False, dA=Non
                                            int(bool(fwd_state_valid)), _stream(stream)),
           "mgs_block_matrix_scan_bwd")
     return dA
+
+
+# ------------------------------------------------------------ delta rule
+
+def mgs_delta_workspace_size(B, T, d):
+    return _size("mgs_delta_workspace_size", B, T, d)
+
+
+def mgs_delta_fwd(q, k, v, beta, S0=None, o=None, ST=None, ws=None, want_state=True, stream=None):
+    """(o (B,T,d), S_T (B,d,d) or None, ws) of S_t = S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T,
+    o_t = S_t q_t; S0 (B,d,d) or None (zeros)."""
+    import torch
+    B, T, d = k.shape
+    dev = k.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, (B, T, d), dev)
+    _check_tensor("beta", beta, (B, T), dev)
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, d, d), dev)
+    if o is None:
+        o = torch.empty((B, T, d), dtype=torch.float32, device=dev)
+    _check_tensor("o", o, (B, T, d), dev)
+    if ST is None and want_state:
+        ST = torch.empty((B, d, d), dtype=torch.float32, device=dev)
+    if ST is not None:
+        _check_tensor("ST", ST, (B, d, d), dev)
+    if ws is None:
+        ws = workspace(mgs_delta_workspace_size(B, T, d), dev)
+    check(load().mgs_delta_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o), _ptr(ST), B, T, d,
+                               _ptr(ws), ws.numel(), _stream(stream)), "mgs_delta_fwd")
+    return o, ST, ws

@@ -43,6 +43,8 @@ SIGNATURES = {
     "mgs_block_matrix_scan_workspace_size": ([_I64, _I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),
     "mgs_block_matrix_scan_fwd": ([_P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P], _INT),
     "mgs_block_matrix_scan_bwd": ([_P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _INT, _P], _INT),
+    "mgs_delta_workspace_size": ([_I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),
+    "mgs_delta_fwd": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
 }
 
 _lib = None

@@ -21,7 +21,8 @@ LIB = os.path.join(HERE, "libmgs.so")
 # size it serves, each object holding that size's kernels only.
 SOURCES = [("mgs_api.cpp", "mgs_api", ()),
            ("elem_scan.hip", "elem_scan", ()),
-           ("block_scan.hip", "block_scan", ())] + [
+           ("block_scan.hip", "block_scan", ()),
+           ("delta_scan.hip", "delta_scan", ())] + [
           ("block_scan_k.hip", f"block_scan_k{k}", (f"-DMGS_ROWS_K={k}",)) for k in (1, 2, 4, 16)]
 JOBS = int(os.environ.get("MGS_BUILD_JOBS", "8"))
 ARCH = os.environ.get("MGS_OFFLOAD_ARCH", "gfx950")

@@ -85,6 +85,19 @@ hipError_t launch_block_matrix_fwd(const BlockGeom &g, const float *A, float *P,
 hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const float *dP, float *dA,
                                    void *ws, bool fwd_state_valid, hipStream_t s);
 
+// ------------------------------------------------------------- delta rule
+struct DeltaGeom {
+    int64_t B;
+    int T, d;
+    int nC;            // chunks of 64 steps
+    size_t off_wum;    // W, U, causal(Q K^T) per (sequence, chunk)
+    size_t bytes;
+};
+
+DeltaGeom delta_geometry(int64_t B, int64_t T, int64_t d);
+hipError_t launch_delta_fwd(const DeltaGeom &g, const float *q, const float *k, const float *v,
+                            const float *beta, const float *S0, float *o, float *ST, void *ws, hipStream_t s);
+
 // zero-fill of n floats (used for gradients of an empty sequence)
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 

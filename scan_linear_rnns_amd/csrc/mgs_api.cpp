@@ -410,4 +410,40 @@ mgs_status mgs_block_matrix_scan_bwd(const float *A, const float *dP, float *dA,
                                                    as_stream(stream)));
 }
 
+// ------------------------------------------------------------ delta rule
+
+static mgs_status check_delta_sizes(int64_t B, int64_t T, int64_t d)
+{
+    if (B < 0 || T < 0 || d <= 0) return MGS_ERR_INVALID_VALUE;
+    if (d != 64) return MGS_ERR_UNSUPPORTED;
+    if (B * T * d > kMaxElems || B * d * d > kMaxElems) return MGS_ERR_UNSUPPORTED;
+    return MGS_OK;
+}
+
+mgs_status mgs_delta_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes)
+{
+    if (!bytes) return MGS_ERR_INVALID_VALUE;
+    if (mgs_status st = check_delta_sizes(B, T, d)) return st;
+    *bytes = mgs::delta_geometry(B, T, d).bytes;
+    return MGS_OK;
+}
+
+mgs_status mgs_delta_fwd(const float *q, const float *k, const float *v, const float *beta,
+                         const float *S0, float *o, float *ST, int64_t B, int64_t T, int64_t d,
+                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (mgs_status st = check_delta_sizes(B, T, d)) return st;
+    const size_t n = static_cast<size_t>(B * T * d) * 4, nb = static_cast<size_t>(B * T) * 4;
+    const size_t ns = static_cast<size_t>(B * d * d) * 4;
+    if (n > 0 && (!q || !k || !v || !beta || !o)) return MGS_ERR_INVALID_VALUE;
+    const Range in[] = {{q, n}, {k, n}, {v, n}, {beta, nb}, {S0, ns}};
+    const Range out[] = {{o, n}, {ST, ns}};
+    if (!all_aligned(in, 5) || !all_aligned(out, 2)) return MGS_ERR_INVALID_VALUE;
+    if (any_alias(in, 5, out, 2)) return MGS_ERR_INVALID_VALUE;
+    if (B == 0 || (T == 0 && !ST)) return MGS_OK;
+    const mgs::DeltaGeom g = mgs::delta_geometry(B, T, d);
+    if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
+    return hip_status(mgs::launch_delta_fwd(g, q, k, v, beta, S0, o, ST, workspace, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.declared_functions()
-    assert len(declared) == 22, declared
+    assert len(declared) == 24, declared
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -166,3 +166,23 @@ def test_givens_validation(lib):
 
 def test_workspace_check_validation(lib):
     assert lib.mgs_workspace_check(None, None, None) == INVALID
+
+
+def test_delta_validation(lib):
+    B, T, d = 2, 100, 64
+    st, nb = _size(lib, "mgs_delta_workspace_size", B, T, d)
+    assert st == OK and nb >= 256 + B * 2 * 3 * 64 * 64 * 4     # two chunks of 64 steps
+    assert _size(lib, "mgs_delta_workspace_size", B, T, 32)[0] == UNSUPPORTED
+    assert _size(lib, "mgs_delta_workspace_size", -1, T, d)[0] == INVALID
+    fwd = lambda q=fake(0), k=fake(1), v=fake(2), beta=fake(3), S0=None, o=fake(5), ST=fake(6), d=d, T=T, \
+        ws=fake(9), nbytes=1 << 24: lib.mgs_delta_fwd(q, k, v, beta, S0, o, ST, B, T, d, ws, nbytes, None)
+    assert fwd(q=None) == INVALID
+    assert fwd(beta=None) == INVALID
+    assert fwd(o=None) == INVALID
+    assert fwd(o=fake(1)) == INVALID                        # output aliases k
+    assert fwd(ST=fake(5, 1024)) == INVALID                 # the two outputs overlap
+    assert fwd(S0=fake(4, 8)) == INVALID                    # misaligned
+    assert fwd(d=48) == UNSUPPORTED
+    assert fwd(ws=None) == WORKSPACE
+    assert fwd(nbytes=1024) == WORKSPACE
+    assert fwd(T=0, ST=None) == OK                          # nothing to do, no HIP call

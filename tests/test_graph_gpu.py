@@ -12,7 +12,7 @@ import ctypes
 import numpy as np
 import pytest
 
-from synthetic import block_inputs, linear_inputs, log_inputs, mingru_inputs
+from synthetic import block_inputs, delta_inputs, linear_inputs, log_inputs, mingru_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -153,3 +153,21 @@ def test_givens_scan_graph_replays(gpu):
         for x, y in zip(got, ref):
             assert torch.equal(x, y)
     assert mgs.mgs_workspace_check(ws) == 0
+
+
+def test_delta_graph_replays(gpu):
+    import torch
+    import scan_linear_rnns_amd as mgs
+    print("[graph] delta rule B=16 T=1024 d=64", flush=True)
+    inp = delta_inputs(16, 1024, 64, 26, s0="normal")
+    q, k, v, beta, S0 = (_t(x, gpu) for x in (inp.q, inp.k, inp.v, inp.beta, inp.S0))
+    o, ST, ws = mgs.mgs_delta_fwd(q, k, v, beta, S0)
+    ref = [o.clone(), ST.clone()]
+    outs = [torch.empty_like(o), torch.empty_like(ST)]
+
+    def step():
+        mgs.mgs_delta_fwd(q, k, v, beta, S0, o=outs[0], ST=outs[1], ws=ws)
+
+    for got in _replays(step, outs):
+        for x, y in zip(got, ref):
+            assert torch.equal(x, y)
