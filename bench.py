@@ -41,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 MFMA
 PEAK_GBPS = 8000.0
 ROTATE_BYTES = 512 << 20
 
@@ -59,6 +60,8 @@ def compulsory_bytes(op, B, T, d, k=8):
         return 4 * N * (k + 2), 4 * N * (2 * k + 3) + 4 * S
     if op == "matrix":
         return 8 * N * k, 12 * N * k
+    if op == "delta":  # forward only: q, k, v, beta read, o written (S0 = NULL, final state not requested)
+        return 16 * N + 4 * B * T, 0
     if op == "givens":  # angles (k(k-1)/2 per block) and gate instead of A; h0 = NULL
         na = k * (k - 1) // 2
         th, sg = 4 * N * na // k, 4 * N // k
@@ -74,7 +77,7 @@ class OpRun:
         import torch
 
         import scan_linear_rnns_amd as mgs
-        from synthetic import block_inputs, linear_inputs, log_inputs, mingru_inputs
+        from synthetic import block_inputs, delta_inputs, linear_inputs, log_inputs, mingru_inputs
 
         self.name, self.op, self.B, self.T, self.d, self.k = name, op, B, T, d, k
         self.N = B * T * d
@@ -94,6 +97,10 @@ class OpRun:
             inp = block_inputs(B, T, d, k=8, seed=0, with_dP=False, return_angles=True)
             base = [t(inp.theta), t(inp.s), t(inp.b), t(inp.dh)]
             ws_bytes = mgs.mgs_givens_scan_workspace_size(B, T, d, 8)
+        elif op == "delta":
+            inp = delta_inputs(B, T, d, 0)
+            base = [t(inp.q), t(inp.k), t(inp.v), t(inp.beta)]
+            ws_bytes = mgs.mgs_delta_workspace_size(B, T, d)
         elif op == "linear":
             inp = linear_inputs(B, T, d, 0)
             base = [t(inp.a), t(inp.b), t(inp.h0), t(inp.dh)]
@@ -119,6 +126,13 @@ class OpRun:
                 fn_f = getattr(self.lib, f"mgs_scan_{op}_fwd")
                 fn_b = getattr(self.lib, f"mgs_scan_{op}_bwd")
                 keep = xs + [h, dla, dlb, dlh0, ws]
+            elif op == "delta":
+                q, kk, v, beta = xs
+                o = torch.empty_like(q)
+                fa = (P(q), P(kk), P(v), P(beta), None, P(o), None, B, T, d, P(ws), ws.numel())
+                ba = None
+                fn_f, fn_b = self.lib.mgs_delta_fwd, None
+                keep = xs + [o, ws]
             elif op == "givens":
                 th, sg, b, dh = xs
                 h = torch.empty_like(b)
@@ -153,7 +167,7 @@ class OpRun:
             rc = fn_f(*fa, stream)
             if rc:
                 raise RuntimeError(f"{self.name} fwd status {rc}")
-        if which in ("bwd", "pair"):
+        if which in ("bwd", "pair") and fn_b is not None:
             rc = fn_b(*ba, stream)
             if rc:
                 raise RuntimeError(f"{self.name} bwd status {rc}")
@@ -348,6 +362,9 @@ def main():
         ("matrix_k16_longT", "matrix", 16, 1024, 64, 16),
         ("affine_k4_longT", "affine", 16, 1024, 64, 4),
         ("affine_k1_longT", "affine", 16, 1024, 64, 1),
+        # the delta rule's chunked-WY forward
+        ("delta_lab", "delta", 128, 64, 64),
+        ("delta_longT", "delta", 16, 1024, 64),
     ]
     if args.no_ops:
         specs = specs[:1]
@@ -362,9 +379,10 @@ def main():
         run = OpRun(name, op, B, T, d, dev, k=k)
         run.prime()
         steps = K if name == "log_lab" else max(20, K // 2)
+        fwd_only = op == "delta"
         pair = graph_time(run, "pair", steps, W)
         fwd = graph_time(run, "fwd", steps, W)
-        bwd = graph_time(run, "bwd", steps, W)
+        bwd = None if fwd_only else graph_time(run, "bwd", steps, W)
         eager = stream_time(run, "pair", steps, W)
         warm_run = OpRun(name + "_warm", op, B, T, d, dev, rotate=False, k=k)
         warm_run.prime()
@@ -381,14 +399,22 @@ def main():
             "GBps": tot / (pair * 1e-6) / 1e9,
             "roofline_frac": tot / (pair * 1e-6) / 1e9 / PEAK_GBPS,
             "fwd_roofline_frac": run.fwd_bytes / (fwd * 1e-6) / 1e9 / PEAK_GBPS,
-            "bwd_roofline_frac": run.bwd_bytes / (bwd * 1e-6) / 1e9 / PEAK_GBPS,
+            "bwd_roofline_frac": None if fwd_only else run.bwd_bytes / (bwd * 1e-6) / 1e9 / PEAK_GBPS,
         }
+        if fwd_only:
+            # the recurrence's own work: S k, the rank-1 update and S q, 6 d^2 flops per step
+            flops = 6 * d * d * B * T
+            rec["algorithmic_flops"] = flops
+            rec["TFLOPs"] = flops / (fwd * 1e-6) / 1e12
+            rec["mfma_fp32_frac"] = rec["TFLOPs"] / PEAK_FP32_TFLOPS
         if op == "matrix":
             rec["op"] = f"block cumulative product (b = 0), k = {k}"
         elif op == "affine":
             rec["op"] = f"block-affine scan, k = {k}"
         elif op == "givens":
             rec["op"] = "Givens angle-fused block-affine scan (inputs theta, s), k = 8"
+        elif op == "delta":
+            rec["op"] = "delta rule (DeltaNet), chunked-WY forward only (pair = forward), d = 64"
         elif op == "linear":
             rec["op"] = "linear-space scan, signed gates"
         elif op == "mingru":
@@ -396,7 +422,8 @@ def main():
         else:
             rec["op"] = "log-space scan"
         ops[name] = rec
-        log(f"op {name}: pair {pair:.2f} us (fwd {fwd:.2f}, bwd {bwd:.2f}; eager {eager:.2f}; warm {warm:.2f}) "
+        bwd_txt = "-" if bwd is None else f"{bwd:.2f}"
+        log(f"op {name}: pair {pair:.2f} us (fwd {fwd:.2f}, bwd {bwd_txt}; eager {eager:.2f}; warm {warm:.2f}) "
             f"-> {rec['elems_per_s']:.3e} elem/s, {rec['roofline_frac']*100:.1f}% of HBM roofline")
         if name == "log_lab":
             head = (run, pair, bwd)

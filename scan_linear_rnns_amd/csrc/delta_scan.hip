@@ -56,17 +56,41 @@ __device__ __forceinline__ f4v mfma4(float4 a, float4 b, f4v c)
 struct DeltaArgs {
     const float *q, *k, *v, *beta, *S0;
     float *o, *ST;
-    float *wum;   // per (sequence, chunk): W, U, M, each 64 x 64 row-major
+    float *wum;   // per (sequence, chunk): W, U, Qt = Q - M W, P = M U, each 64 x 64 row-major
     int T, nC;
 };
 
 __device__ __forceinline__ float4 f4zero() { return make_float4(0.0f, 0.0f, 0.0f, 0.0f); }
 
+// Workgroup barrier that waits only for this wave's LDS operations.  Global
+// loads issued before it stay in flight (__syncthreads() also waits for them,
+// which would stall the prefetch of the next chunk's operands at every
+// barrier).  Only LDS carries data between the waves here.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ------------------------------------------------------------- prep kernel
+// Per chunk, with R = diag(beta) [K V] (64 x 128) and L = I + A,
+// A = strict_lower(diag(beta) K K^T), in 16-row blocks i, j:
+//     [W U]_i = X_ii (R_i - sum_{j<i} A_ij [W U]_j),   X_ii = L_ii^{-1},
+// then the state-free parts of the outputs, M = causal(Q K^T):
+//     Qt = Q - M W,   P = M U,
+// so that the state kernel's output is O = Qt S^T + P.  Wave w owns columns
+// 32w .. 32w+31 of [W U] (two 16-wide tiles) through all four row blocks, so
+// the block solve and the products with M keep every block in registers: an
+// MFMA result (accumulator layout, rows 4 (l/16) + r) is directly the B
+// operand of the next MFMA under the permuted reduction index.
+
+// Tiles of G (first ten) and M (last ten) on or below the diagonal, dealt to
+// the four waves five apiece: tile = 4 * i + j.
+__constant__ int kPrepTiles[20] = {0, 4, 5, 8, 9, 10, 12, 13, 14, 15, 0, 4, 5, 8, 9, 10, 12, 13, 14, 15};
 
 __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
 {
-    __shared__ float sK[kCh][kLd], sV[kCh][kLd], sQ[kCh][kLd], sG[kCh][kLd];
+    __shared__ float sK[kCh][kLd], sV[kCh][kLd], sQ[kCh][kLd], sA[kCh][kLd], sM[kCh][kLd];
+    __shared__ float sX[4][16][20];   // the inverses of the diagonal blocks of L
     __shared__ float sB[kCh];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
@@ -76,83 +100,188 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
     const int nrow = min(kCh, a.T - t0);
     const int64_t row0 = static_cast<int64_t>(b) * a.T + t0;
 
-    // the chunk's rows of k, v, q (zero past the end of the sequence)
-    for (int e = tid; e < kCh * 16; e += 256) {
-        const int r = e >> 4, c4 = (e & 15) * 4;
-        float4 kk = f4zero(), vv = f4zero(), qq = f4zero();
-        if (r < nrow) {
-            const int64_t off = (row0 + r) * kDD + c4;
-            kk = *reinterpret_cast<const float4 *>(a.k + off);
-            vv = *reinterpret_cast<const float4 *>(a.v + off);
-            qq = *reinterpret_cast<const float4 *>(a.q + off);
+    // the chunk's rows of k, v, q (zero past the end of the sequence).  Loads
+    // are unconditional from a clamped row, so all twelve are in flight at
+    // once; rows past the end are zeroed after the load.
+    {
+        float4 kk[4], vv[4], qq[4];
+        const int c4 = (tid & 15) * 4;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int r = (tid >> 4) + 16 * it;
+            const int64_t off = (row0 + min(r, nrow - 1)) * kDD + c4;
+            kk[it] = *reinterpret_cast<const float4 *>(a.k + off);
+            vv[it] = *reinterpret_cast<const float4 *>(a.v + off);
+            qq[it] = *reinterpret_cast<const float4 *>(a.q + off);
         }
-        *reinterpret_cast<float4 *>(&sK[r][c4]) = kk;
-        *reinterpret_cast<float4 *>(&sV[r][c4]) = vv;
-        *reinterpret_cast<float4 *>(&sQ[r][c4]) = qq;
+        const float bt = a.beta[row0 + min(tid & 63, nrow - 1)];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int r = (tid >> 4) + 16 * it;
+            const bool in = r < nrow;
+            *reinterpret_cast<float4 *>(&sK[r][c4]) = in ? kk[it] : f4zero();
+            *reinterpret_cast<float4 *>(&sV[r][c4]) = in ? vv[it] : f4zero();
+            *reinterpret_cast<float4 *>(&sQ[r][c4]) = in ? qq[it] : f4zero();
+        }
+        if (tid < kCh) sB[tid] = tid < nrow ? bt : 0.0f;
     }
-    if (tid < kCh) sB[tid] = tid < nrow ? a.beta[row0 + tid] : 0.0f;
     __syncthreads();
 
-    float *wum = a.wum + static_cast<int64_t>(bc) * 3 * kCh * kDD;
-    float *gW = wum, *gU = wum + kCh * kDD, *gM = wum + 2 * kCh * kDD;
-
-    // G = K K^T (all 16 tiles: row i of G is then row i of the symmetric G,
-    // read contiguously by the substitution) and M = causal(Q K^T) (tiles on
-    // or below the diagonal).  Wave wv owns row block wv.
+    // A = strict_lower(diag(beta) K K^T) and M = causal(Q K^T), lower tiles
+    // only; all five tiles' MFMAs first, each reduction in two halves, so ten
+    // independent MFMA chains interleave
     {
-        float4 ak[4], aq[4];
+        f4v acc[5][2];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            ak[kb] = *reinterpret_cast<const float4 *>(&sK[16 * wv + li][16 * kb + 4 * lq]);
-            aq[kb] = *reinterpret_cast<const float4 *>(&sQ[16 * wv + li][16 * kb + 4 * lq]);
-        }
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            f4v g = {0.0f, 0.0f, 0.0f, 0.0f}, m = {0.0f, 0.0f, 0.0f, 0.0f};
-            const bool causal = cb <= wv;   // wave-uniform
+        for (int n = 0; n < 5; ++n) {
+            const int slot = wv + 4 * n;
+            const int tile = kPrepTiles[slot];
+            const int bi = tile >> 2, bj = tile & 3;
+            float(*L)[kLd] = slot >= 10 ? sQ : sK;   // wave-uniform
+            acc[n][0] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
+            acc[n][1] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const float4 bk = *reinterpret_cast<const float4 *>(&sK[16 * cb + li][16 * kb + 4 * lq]);
-                g = mfma4(ak[kb], bk, g);
-                if (causal) m = mfma4(aq[kb], bk, m);
+                const float4 x = *reinterpret_cast<const float4 *>(&L[16 * bi + li][16 * kb + 4 * lq]);
+                const float4 y = *reinterpret_cast<const float4 *>(&sK[16 * bj + li][16 * kb + 4 * lq]);
+                acc[n][kb >> 1] = mfma4(x, y, acc[n][kb >> 1]);
             }
+        }
+#pragma unroll
+        for (int n = 0; n < 5; ++n) {
+            const int slot = wv + 4 * n;
+            const int tile = kPrepTiles[slot];
+            const int bi = tile >> 2, bj = tile & 3;
+            const f4v g = acc[n][0] + acc[n][1];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * wv + 4 * lq + r, j = 16 * cb + li;
-                sG[i][j] = g[r];
-                gM[i * kDD + j] = (causal && j <= i) ? m[r] : 0.0f;
+                const int i = 16 * bi + 4 * lq + r, j = 16 * bj + li;
+                if (slot >= 10) sM[i][j] = j <= i ? g[r] : 0.0f;
+                else sA[i][j] = j < i ? sB[i] * g[r] : 0.0f;
             }
         }
     }
     __syncthreads();
 
-    // forward substitution, lane per column: columns 0..63 of K give W,
-    // columns 0..63 of V give U.  At step i the lane's running right-hand side
-    // y_i is final: x_i = beta_i y_i, then y_r -= G[r][i] x_i for r > i.
-    if (tid < 128) {
-        const int c = tid & 63;
-        float(*X)[kLd] = tid < 64 ? sK : sV;
-        float *dst = tid < 64 ? gW : gU;
-        float y[kCh];
+    // X_ww = (I + A_ww)^{-1}: lane c < 16 solves column c, row by row
+    if (lane < 16) {
+        const int o = 16 * wv;
+        float x[16];
 #pragma unroll
-        for (int i = 0; i < kCh; ++i) y[i] = X[i][c];
+        for (int i = 0; i < 16; ++i) {
+            float s0 = (i == li) ? 1.0f : 0.0f, s1 = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kCh; ++i) {
-            const float x = sB[i] * y[i];
-            dst[i * kDD + c] = x;
-#pragma unroll
-            for (int r4 = (i + 1) & ~3; r4 < kCh; r4 += 4) {
-                const float4 g = *reinterpret_cast<const float4 *>(&sG[i][r4]);
-                if (r4 + 0 > i) y[r4 + 0] = __builtin_fmaf(-g.x, x, y[r4 + 0]);
-                if (r4 + 1 > i) y[r4 + 1] = __builtin_fmaf(-g.y, x, y[r4 + 1]);
-                if (r4 + 2 > i) y[r4 + 2] = __builtin_fmaf(-g.z, x, y[r4 + 2]);
-                if (r4 + 3 > i) y[r4 + 3] = __builtin_fmaf(-g.w, x, y[r4 + 3]);
+            for (int j = 0; j < i; ++j) {
+                if (j & 1) s1 = __builtin_fmaf(-sA[o + i][o + j], x[j], s1);
+                else s0 = __builtin_fmaf(-sA[o + i][o + j], x[j], s0);
             }
+            x[i] = s0 + s1;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sX[wv][i][li] = x[i];
+    }
+    __syncthreads();
+
+    // block solve of this wave's two column tiles of [W U]
+    const bool isU = wv >= 2;                      // wave-uniform: columns of V give U
+    const int cbase = 32 * (wv & 1);               // first column within K or V
+    float(*R)[kLd] = isU ? sV : sK;
+    f4v Y[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f4v t;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * i + 4 * lq + r;
+                t[r] = sB[row] * R[row][cbase + 16 * h + li];
+            }
+#pragma unroll
+            for (int j = 0; j < i; ++j) {
+                const float4 av = *reinterpret_cast<const float4 *>(&sA[16 * i + li][16 * j + 4 * lq]);
+                const float4 na = make_float4(-av.x, -av.y, -av.z, -av.w);
+                t = __builtin_amdgcn_mfma_f32_16x16x4f32(na.x, Y[j][h][0], t, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_16x16x4f32(na.y, Y[j][h][1], t, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_16x16x4f32(na.z, Y[j][h][2], t, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_16x16x4f32(na.w, Y[j][h][3], t, 0, 0, 0);
+            }
+            const float4 xv = *reinterpret_cast<const float4 *>(&sX[i][li][4 * lq]);
+            f4v y = {0.0f, 0.0f, 0.0f, 0.0f};
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.x, t[0], y, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.y, t[1], y, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.z, t[2], y, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.w, t[3], y, 0, 0, 0);
+            Y[i][h] = y;
+        }
+    }
+
+    // outputs: W or U, then Qt = Q - M W (W waves) or P = M U (U waves)
+    float *wum = a.wum + static_cast<int64_t>(bc) * 4 * kCh * kDD;
+    float *gY = wum + (isU ? kCh * kDD : 0);
+    float *gZ = wum + (isU ? 3 : 2) * kCh * kDD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int col = cbase + 16 * h + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gY[(16 * i + 4 * lq + r) * kDD + col] = Y[i][h][r];
+            f4v z;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) z[r] = isU ? 0.0f : sQ[16 * i + 4 * lq + r][col];
+#pragma unroll
+            for (int k2 = 0; k2 <= i; ++k2) {
+                const float4 mv = *reinterpret_cast<const float4 *>(&sM[16 * i + li][16 * k2 + 4 * lq]);
+                const float4 m = isU ? mv : make_float4(-mv.x, -mv.y, -mv.z, -mv.w);
+                z = __builtin_amdgcn_mfma_f32_16x16x4f32(m.x, Y[k2][h][0], z, 0, 0, 0);
+                z = __builtin_amdgcn_mfma_f32_16x16x4f32(m.y, Y[k2][h][1], z, 0, 0, 0);
+                z = __builtin_amdgcn_mfma_f32_16x16x4f32(m.z, Y[k2][h][2], z, 0, 0, 0);
+                z = __builtin_amdgcn_mfma_f32_16x16x4f32(m.w, Y[k2][h][3], z, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gZ[(16 * i + 4 * lq + r) * kDD + col] = z[r];
         }
     }
 }
 
 // ------------------------------------------------------------ state kernel
+// Per chunk, for the 16 rows of S this workgroup owns (B operand: S[16 sl + li][c]):
+//     U' = U - W S^T,   O = Qt S^T + P,   S += U'^T K.
+// The operands of the next chunk are loaded while this chunk computes.
+
+struct StateOps {
+    float4 w4[4], q4[4];   // rows 16 wv + li of W and Qt, reduction slices 16 kb + 4 lq
+    f4v u, p;              // tiles U, P [16 wv + 4 lq + r][16 sl + li]
+    float kr[16];          // K[16 kb + 4 lq + j][16 wv + li], j fastest (raw, clamped rows)
+};
+
+__device__ __forceinline__ void load_state_ops(const DeltaArgs &a, int b, int sl, int wv, int li, int lq, int ch,
+                                               StateOps &op)
+{
+    const int t0 = ch * kCh;
+    const int nrow = min(kCh, a.T - t0);
+    const int64_t row0 = static_cast<int64_t>(b) * a.T + t0;
+    const float *wum = a.wum + (static_cast<int64_t>(b) * a.nC + ch) * 4 * kCh * kDD;
+    const float *gW = wum, *gU = wum + kCh * kDD, *gQ = wum + 2 * kCh * kDD, *gP = wum + 3 * kCh * kDD;
+    const int ra = 16 * wv + li;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int c = 16 * kb + 4 * lq;
+        op.w4[kb] = *reinterpret_cast<const float4 *>(gW + ra * kDD + c);
+        op.q4[kb] = *reinterpret_cast<const float4 *>(gQ + ra * kDD + c);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        op.u[r] = gU[(16 * wv + 4 * lq + r) * kDD + 16 * sl + li];
+        op.p[r] = gP[(16 * wv + 4 * lq + r) * kDD + 16 * sl + li];
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int t = 16 * (e >> 2) + 4 * lq + (e & 3);
+        op.kr[e] = a.k[(row0 + min(t, nrow - 1)) * kDD + 16 * wv + li];
+    }
+}
 
 __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
 {
@@ -170,72 +299,73 @@ __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sS[4 * lq + r][16 * wv + li] = S[r];
 
-    for (int ch = 0; ch < a.nC; ++ch) {
+    // one chunk: U' = U - W S^T, O = Qt S^T + P, S += U'^T K
+    auto chunk = [&](int ch, const StateOps &cur) {
         const int t0 = ch * kCh;
         const int nrow = min(kCh, a.T - t0);
         const int64_t row0 = static_cast<int64_t>(b) * a.T + t0;
-        const float *wum = a.wum + (static_cast<int64_t>(b) * a.nC + ch) * 3 * kCh * kDD;
-        const float *gW = wum, *gU = wum + kCh * kDD, *gM = wum + 2 * kCh * kDD;
+        lds_barrier();   // sS holds the entering state; sUp is free
 
-        // operands: chunk rows 16 wv + li (A layout), reduction slices 16 kb + 4 lq
-        const int ra = 16 * wv + li;
-        float4 w4[4], q4[4], m4[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int c = 16 * kb + 4 * lq;
-            w4[kb] = *reinterpret_cast<const float4 *>(gW + ra * kDD + c);
-            m4[kb] = *reinterpret_cast<const float4 *>(gM + ra * kDD + c);
-            q4[kb] = ra < nrow ? *reinterpret_cast<const float4 *>(a.q + (row0 + ra) * kDD + c) : f4zero();
-        }
-        f4v up;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) up[r] = gU[(16 * wv + 4 * lq + r) * kDD + 16 * sl + li];
-        float4 kc[4];   // K[16 kb + 4 lq + j][16 wv + li]
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int t = 16 * kb + 4 * lq;
-            const float *kp = a.k + (row0 + t) * kDD + 16 * wv + li;
-            kc[kb].x = t + 0 < nrow ? kp[0] : 0.0f;
-            kc[kb].y = t + 1 < nrow ? kp[kDD] : 0.0f;
-            kc[kb].z = t + 2 < nrow ? kp[2 * kDD] : 0.0f;
-            kc[kb].w = t + 3 < nrow ? kp[3 * kDD] : 0.0f;
-        }
-        __syncthreads();   // sS holds the entering state; sUp is free
-
-        // U' = U - W S^T and O = Q S^T (B operand: S[16 sl + li][c])
-        f4v o = {0.0f, 0.0f, 0.0f, 0.0f};
+        // two accumulators per product, so four independent MFMA chains interleave
+        f4v up = cur.u, o = cur.p, up2 = {0.0f, 0.0f, 0.0f, 0.0f}, o2 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const float4 s4 = *reinterpret_cast<const float4 *>(&sS[li][16 * kb + 4 * lq]);
-            const float4 nw = make_float4(-w4[kb].x, -w4[kb].y, -w4[kb].z, -w4[kb].w);
-            up = mfma4(nw, s4, up);
-            o = mfma4(q4[kb], s4, o);
+            const float4 nw = make_float4(-cur.w4[kb].x, -cur.w4[kb].y, -cur.w4[kb].z, -cur.w4[kb].w);
+            if (kb < 2) {
+                up = mfma4(nw, s4, up);
+                o = mfma4(cur.q4[kb], s4, o);
+            } else {
+                up2 = mfma4(nw, s4, up2);
+                o2 = mfma4(cur.q4[kb], s4, o2);
+            }
         }
+        up += up2;
+        o += o2;
 #pragma unroll
         for (int r = 0; r < 4; ++r) sUp[16 * wv + 4 * lq + r][li] = up[r];
-        __syncthreads();
-
-        // U'[16 kb + 4 lq + j][16 sl + li]: B operand of M U', A operand of U'^T K
-        float4 uu[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int t = 16 * kb + 4 * lq;
-            uu[kb] = make_float4(sUp[t][li], sUp[t + 1][li], sUp[t + 2][li], sUp[t + 3][li]);
-        }
-        // O += causal(Q K^T) U'  (rows of this wave see chunk rows <= 16 wv + 15)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-            if (kb <= wv) o = mfma4(m4[kb], uu[kb], o);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * wv + 4 * lq + r;
             if (t < nrow) a.o[(row0 + t) * kDD + 16 * sl + li] = o[r];
         }
-        // S += U'^T K on this wave's columns
+        lds_barrier();
+
+        // S += U'^T K on this wave's columns (A: U'[t][16 sl + li], B: K[t][16 wv + li])
+        f4v dS = {0.0f, 0.0f, 0.0f, 0.0f}, dS2 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) S = mfma4(uu[kb], kc[kb], S);
+        for (int kb = 0; kb < 4; ++kb) {
+            const int t = 16 * kb + 4 * lq;
+            const float4 uu = make_float4(sUp[t][li], sUp[t + 1][li], sUp[t + 2][li], sUp[t + 3][li]);
+            const float4 kc = make_float4(t + 0 < nrow ? cur.kr[4 * kb + 0] : 0.0f, t + 1 < nrow ? cur.kr[4 * kb + 1] : 0.0f,
+                                          t + 2 < nrow ? cur.kr[4 * kb + 2] : 0.0f, t + 3 < nrow ? cur.kr[4 * kb + 3] : 0.0f);
+            if (kb < 2) dS = mfma4(uu, kc, dS);
+            else dS2 = mfma4(uu, kc, dS2);
+        }
+        S += dS + dS2;
 #pragma unroll
         for (int r = 0; r < 4; ++r) sS[4 * lq + r][16 * wv + li] = S[r];
+    };
+
+    // two operand sets in turn: the next chunk's loads are issued before this
+    // chunk computes and are never copied (a copy would wait for them); the
+    // loads are unconditional (past the last chunk they reload it), since a
+    // conditional load makes the compiler wait for it at the first use of the
+    // other set
+    if (a.nC == 1) {
+        StateOps A;
+        load_state_ops(a, b, sl, wv, li, lq, 0, A);
+        chunk(0, A);
+    } else if (a.nC > 1) {
+        StateOps A, B;
+        load_state_ops(a, b, sl, wv, li, lq, 0, A);
+        for (int ch = 0; ch < a.nC; ch += 2) {
+            load_state_ops(a, b, sl, wv, li, lq, min(ch + 1, a.nC - 1), B);
+            chunk(ch, A);
+            if (ch + 1 >= a.nC) break;
+            load_state_ops(a, b, sl, wv, li, lq, min(ch + 2, a.nC - 1), A);
+            chunk(ch + 1, B);
+        }
     }
     if (a.ST) {
 #pragma unroll
@@ -253,7 +383,7 @@ DeltaGeom delta_geometry(int64_t B, int64_t T, int64_t d)
     g.d = static_cast<int>(d);
     g.nC = static_cast<int>((T + kCh - 1) / kCh);
     g.off_wum = 256;   // after a header kept for the common workspace check
-    g.bytes = g.off_wum + static_cast<size_t>(B) * g.nC * 3 * kCh * kDD * sizeof(float);
+    g.bytes = g.off_wum + static_cast<size_t>(B) * g.nC * 4 * kCh * kDD * sizeof(float);
     return g;
 }
 
