@@ -56,7 +56,7 @@ __device__ __forceinline__ f4v mfma4(float4 a, float4 b, f4v c)
 struct DeltaArgs {
     const float *q, *k, *v, *beta, *S0;
     float *o, *ST;
-    float *wum;   // per (sequence, chunk): W, U, Qt = Q - M W, P = M U, each 64 x 64 row-major
+    float *wum;   // per (sequence, chunk): W, U^T, Qt = Q - M W, P^T = (M U)^T, K^T, each 64 x 64
     int T, nC;
 };
 
@@ -216,20 +216,28 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
         }
     }
 
-    // outputs: W or U, then Qt = Q - M W (W waves) or P = M U (U waves)
-    float *wum = a.wum + static_cast<int64_t>(bc) * 4 * kCh * kDD;
-    float *gY = wum + (isU ? kCh * kDD : 0);
-    float *gZ = wum + (isU ? 3 : 2) * kCh * kDD;
+    // outputs, per chunk: W and Qt = Q - M W row-major (the state kernel reads
+    // their rows), U^T, P^T = (M U)^T and K^T (it reads their columns), so
+    // that every operand of the state kernel is a 16-byte load per lane
+    float *wum = a.wum + static_cast<int64_t>(bc) * 5 * kCh * kDD;
+    float *gW = wum, *gUT = wum + kCh * kDD, *gQ = wum + 2 * kCh * kDD, *gPT = wum + 3 * kCh * kDD;
+    float *gKT = wum + 4 * kCh * kDD;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int col = cbase + 16 * h + li;
+            const int row = 16 * i + 4 * lq;
+            if (isU) {
+                *reinterpret_cast<float4 *>(gUT + col * kCh + row) =
+                    make_float4(Y[i][h][0], Y[i][h][1], Y[i][h][2], Y[i][h][3]);
+            } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) gY[(16 * i + 4 * lq + r) * kDD + col] = Y[i][h][r];
+                for (int r = 0; r < 4; ++r) gW[(row + r) * kDD + col] = Y[i][h][r];
+            }
             f4v z;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) z[r] = isU ? 0.0f : sQ[16 * i + 4 * lq + r][col];
+            for (int r = 0; r < 4; ++r) z[r] = isU ? 0.0f : sQ[row + r][col];
 #pragma unroll
             for (int k2 = 0; k2 <= i; ++k2) {
                 const float4 mv = *reinterpret_cast<const float4 *>(&sM[16 * i + li][16 * k2 + 4 * lq]);
@@ -239,9 +247,21 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
                 z = __builtin_amdgcn_mfma_f32_16x16x4f32(m.z, Y[k2][h][2], z, 0, 0, 0);
                 z = __builtin_amdgcn_mfma_f32_16x16x4f32(m.w, Y[k2][h][3], z, 0, 0, 0);
             }
+            if (isU) {
+                *reinterpret_cast<float4 *>(gPT + col * kCh + row) = make_float4(z[0], z[1], z[2], z[3]);
+            } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) gZ[(16 * i + 4 * lq + r) * kDD + col] = z[r];
+                for (int r = 0; r < 4; ++r) gQ[(row + r) * kDD + col] = z[r];
+            }
         }
+    }
+    // K^T (zero past the end of the sequence, as staged)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int e = tid + 256 * it;          // 1024 float4 = 64 columns x 16 row groups
+        const int c = e >> 4, t4 = (e & 15) * 4;
+        *reinterpret_cast<float4 *>(gKT + c * kCh + t4) =
+            make_float4(sK[t4][c], sK[t4 + 1][c], sK[t4 + 2][c], sK[t4 + 3][c]);
     }
 }
 
@@ -252,35 +272,26 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
 
 struct StateOps {
     float4 w4[4], q4[4];   // rows 16 wv + li of W and Qt, reduction slices 16 kb + 4 lq
-    f4v u, p;              // tiles U, P [16 wv + 4 lq + r][16 sl + li]
-    float kr[16];          // K[16 kb + 4 lq + j][16 wv + li], j fastest (raw, clamped rows)
+    float4 u, p;           // U, P [16 wv + 4 lq + r][16 sl + li], r = 0..3
+    float4 kc[4];          // K[16 kb + 4 lq + j][16 wv + li], j = 0..3 (zero past the end)
 };
 
 __device__ __forceinline__ void load_state_ops(const DeltaArgs &a, int b, int sl, int wv, int li, int lq, int ch,
                                                StateOps &op)
 {
-    const int t0 = ch * kCh;
-    const int nrow = min(kCh, a.T - t0);
-    const int64_t row0 = static_cast<int64_t>(b) * a.T + t0;
-    const float *wum = a.wum + (static_cast<int64_t>(b) * a.nC + ch) * 4 * kCh * kDD;
-    const float *gW = wum, *gU = wum + kCh * kDD, *gQ = wum + 2 * kCh * kDD, *gP = wum + 3 * kCh * kDD;
+    const float *wum = a.wum + (static_cast<int64_t>(b) * a.nC + ch) * 5 * kCh * kDD;
+    const float *gW = wum, *gUT = wum + kCh * kDD, *gQ = wum + 2 * kCh * kDD, *gPT = wum + 3 * kCh * kDD;
+    const float *gKT = wum + 4 * kCh * kDD;
     const int ra = 16 * wv + li;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         const int c = 16 * kb + 4 * lq;
         op.w4[kb] = *reinterpret_cast<const float4 *>(gW + ra * kDD + c);
         op.q4[kb] = *reinterpret_cast<const float4 *>(gQ + ra * kDD + c);
+        op.kc[kb] = *reinterpret_cast<const float4 *>(gKT + ra * kCh + c);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        op.u[r] = gU[(16 * wv + 4 * lq + r) * kDD + 16 * sl + li];
-        op.p[r] = gP[(16 * wv + 4 * lq + r) * kDD + 16 * sl + li];
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int t = 16 * (e >> 2) + 4 * lq + (e & 3);
-        op.kr[e] = a.k[(row0 + min(t, nrow - 1)) * kDD + 16 * wv + li];
-    }
+    op.u = *reinterpret_cast<const float4 *>(gUT + (16 * sl + li) * kCh + 16 * wv + 4 * lq);
+    op.p = *reinterpret_cast<const float4 *>(gPT + (16 * sl + li) * kCh + 16 * wv + 4 * lq);
 }
 
 __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
@@ -307,7 +318,8 @@ __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
         lds_barrier();   // sS holds the entering state; sUp is free
 
         // two accumulators per product, so four independent MFMA chains interleave
-        f4v up = cur.u, o = cur.p, up2 = {0.0f, 0.0f, 0.0f, 0.0f}, o2 = {0.0f, 0.0f, 0.0f, 0.0f};
+        f4v up = {cur.u.x, cur.u.y, cur.u.z, cur.u.w}, o = {cur.p.x, cur.p.y, cur.p.z, cur.p.w};
+        f4v up2 = {0.0f, 0.0f, 0.0f, 0.0f}, o2 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const float4 s4 = *reinterpret_cast<const float4 *>(&sS[li][16 * kb + 4 * lq]);
@@ -337,10 +349,8 @@ __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
         for (int kb = 0; kb < 4; ++kb) {
             const int t = 16 * kb + 4 * lq;
             const float4 uu = make_float4(sUp[t][li], sUp[t + 1][li], sUp[t + 2][li], sUp[t + 3][li]);
-            const float4 kc = make_float4(t + 0 < nrow ? cur.kr[4 * kb + 0] : 0.0f, t + 1 < nrow ? cur.kr[4 * kb + 1] : 0.0f,
-                                          t + 2 < nrow ? cur.kr[4 * kb + 2] : 0.0f, t + 3 < nrow ? cur.kr[4 * kb + 3] : 0.0f);
-            if (kb < 2) dS = mfma4(uu, kc, dS);
-            else dS2 = mfma4(uu, kc, dS2);
+            if (kb < 2) dS = mfma4(uu, cur.kc[kb], dS);
+            else dS2 = mfma4(uu, cur.kc[kb], dS2);
         }
         S += dS + dS2;
 #pragma unroll
@@ -350,8 +360,9 @@ __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
     // two operand sets in turn: the next chunk's loads are issued before this
     // chunk computes and are never copied (a copy would wait for them); the
     // loads are unconditional (past the last chunk they reload it), since a
-    // conditional load makes the compiler wait for it at the first use of the
-    // other set
+    // conditional load makes the compiler wait for it at the first use of
+    // the other set
+    const int last = a.nC - 1;
     if (a.nC == 1) {
         StateOps A;
         load_state_ops(a, b, sl, wv, li, lq, 0, A);
@@ -360,10 +371,10 @@ __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
         StateOps A, B;
         load_state_ops(a, b, sl, wv, li, lq, 0, A);
         for (int ch = 0; ch < a.nC; ch += 2) {
-            load_state_ops(a, b, sl, wv, li, lq, min(ch + 1, a.nC - 1), B);
+            load_state_ops(a, b, sl, wv, li, lq, min(ch + 1, last), B);
             chunk(ch, A);
-            if (ch + 1 >= a.nC) break;
-            load_state_ops(a, b, sl, wv, li, lq, min(ch + 2, a.nC - 1), A);
+            if (ch + 1 > last) break;
+            load_state_ops(a, b, sl, wv, li, lq, min(ch + 2, last), A);
             chunk(ch + 1, B);
         }
     }
@@ -383,7 +394,7 @@ DeltaGeom delta_geometry(int64_t B, int64_t T, int64_t d)
     g.d = static_cast<int>(d);
     g.nC = static_cast<int>((T + kCh - 1) / kCh);
     g.off_wum = 256;   // after a header kept for the common workspace check
-    g.bytes = g.off_wum + static_cast<size_t>(B) * g.nC * 4 * kCh * kDD * sizeof(float);
+    g.bytes = g.off_wum + static_cast<size_t>(B) * g.nC * 5 * kCh * kDD * sizeof(float);
     return g;
 }
 
