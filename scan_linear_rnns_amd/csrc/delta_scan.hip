@@ -19,8 +19,8 @@
 //     forward substitution for the 128 columns of [W U] (one lane per column,
 //     column-oriented so each step is a row of independent multiply-adds).
 //     Writes W, U, M (3 x 64 x 64 floats per chunk) to the workspace.
-//   * delta_state_kernel, one workgroup per (sequence, 16 rows of S), chunks in
-//     order: U' = U - W S^T and O = Q S^T + M U' and S += U'^T K, all on MFMA;
+//   * delta_state_kernel, one workgroup per (sequence, 16 rows of S; the four
+//     of a sequence on one XCD), chunks in order: U' = U - W S^T and O = Q S^T + M U' and S += U'^T K, all on MFMA;
 //     the wave w of 4 owns chunk rows 16w..16w+15 for U' and O, and columns
 //     16w..16w+15 of its 16 x 64 slice of S, kept in accumulator registers
 //     across chunks.  Slices of S are independent (the recurrence mixes the
@@ -58,6 +58,7 @@ struct DeltaArgs {
     float *o, *ST;
     float *wum;   // per (sequence, chunk): W, U^T, Qt = Q - M W, P^T = (M U)^T, K^T, each 64 x 64
     int T, nC;
+    int B;
 };
 
 __device__ __forceinline__ float4 f4zero() { return make_float4(0.0f, 0.0f, 0.0f, 0.0f); }
@@ -300,7 +301,13 @@ __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
     __shared__ float sUp[kCh][17];   // U' of the chunk, this slice's 16 columns
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
-    const int b = blockIdx.x >> 2, sl = blockIdx.x & 3;
+    // XCD-aware numbering: workgroups are dealt to the 8 XCDs round-robin
+    // (XCD = blockIdx mod 8), so the four slices of sequence b get blockIdx
+    // 32 (b / 8) + 8 sl + b % 8 and share one XCD's L2 for the rows of W, Qt
+    // and K^T that all four read.  The grid is padded to a multiple of 32.
+    const int xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
+    const int sl = rest & 3, b = (rest >> 2) * 8 + xcd;
+    if (b >= a.B) return;   // padding workgroup (whole workgroup, before any barrier)
 
     // this wave's tile of the state: S[16 sl + 4 lq + r][16 wv + li]
     const int64_t sbase = (static_cast<int64_t>(b) * kDD + 16 * sl + 4 * lq) * kDD + 16 * wv + li;
@@ -411,7 +418,9 @@ hipError_t launch_delta_fwd(const DeltaGeom &g, const float *q, const float *k, 
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(delta_state_kernel, dim3(static_cast<unsigned>(g.B * 4)), dim3(256), 0, s, a);
+    a.B = static_cast<int>(g.B);
+    const unsigned groups = static_cast<unsigned>((g.B + 7) / 8) * 32;   // 4 slices x padded sequences
+    hipLaunchKernelGGL(delta_state_kernel, dim3(groups), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
