@@ -321,9 +321,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only: the scan's chains are independent, "
-                                   "so N GPUs would each run the same kernels on their own B/N shard "
-                                   "(see DESIGN.md); run with --gpus 1"}), flush=True)
+        print(json.dumps({"error": "one GPU only: the scan's chains are independent, so N GPUs would each "
+                                   "run the same kernels on their own B/N shard with no exchange; run with "
+                                   "--gpus 1"}), flush=True)
         sys.exit(2)
 
     import torch

@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests must run on a GPU machine; without one they fail loudly at the
+    # GPU tests must run on a GPU host; without one they fail loudly at the
     # first device call rather than silently skipping, unless deselected.
     pass
 

@@ -4,7 +4,7 @@ Same rule as the other parity tests (tests/test_parity_gpu.py): every output
 tensor element by element against the fp64 oracle on the same fp32 inputs,
 err = max_i |x_i - r_i| / max(|r_i|, 1e-3 * max_j |r_j|).  Bar: 1e-4, the
 elementwise scan's bar (the pages fix none for this op; the fp32 evaluation
-with |a| < 1 loses only a few ulps per step, see DESIGN.md).
+with |a| < 1 loses only a few ulps per step).
 """
 import numpy as np
 import pytest
