@@ -1024,6 +1024,9 @@ __device__ __forceinline__ void ks_scan(float (*buf)[NCH][32][(AggShape<KIND, K>
 // LDS, so every angle is loaded once and turned into sin / cos once.
 
 constexpr int kAngles = 28;
+// row stride (floats) of the per-lane cos / sin exchange buffer: 8 values, padded
+// to 12 so that 16 consecutive lanes' 16-byte stores fall on distinct banks
+constexpr int kCSLd = 12;
 
 __host__ __device__ constexpr int mesh_first(int l) { return (l / 2) * 7 + (l & 1) * 4; }
 
@@ -1059,7 +1062,7 @@ __device__ __forceinline__ void sincos_cw(float x, float &sn, float &cs)
 }
 
 // cosines and sines of a chain's 28 angles in every lane of the chain
-__device__ __forceinline__ void mesh_share(float4 th, float (*cs)[8], int lane, float (&cc)[kAngles],
+__device__ __forceinline__ void mesh_share(float4 th, float (*cs)[kCSLd], int lane, float (&cc)[kAngles],
                                            float (&ss)[kAngles])
 {
     // within a few ulp (the hardware's native sin / cos lose ~1e-6 absolute,
@@ -1300,7 +1303,7 @@ __device__ __forceinline__ void affine_fwd_body(const BlkArgs &a)
     __shared__ float sKS[2][NCH][32][(AggShape<kMatVec, K>::stride)];
     __shared__ float sCarry[32];
     __shared__ uint32_t sTicket[2];
-    __shared__ float sCS[GIV ? W : 1][64][8];
+    __shared__ float sCS[GIV ? W : 1][64][kCSLd];
 
     const int tile = blockIdx.x;
     unsigned long long ep = 0;
@@ -1462,11 +1465,14 @@ template <int C, int W, bool MULTI>
 __global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
 {
     constexpr int NCH = 2 * W;
-    constexpr int PW = 32;   // words per lane in the reduction buffer: 28 angles, the gate, padding
+    // words per lane in the reduction buffer: 28 angles, the gate, padding to a
+    // stride of 36 (a multiple of 4 for 16-byte accesses; 36 l mod 64 differs for 16
+    // consecutive lanes, so a 16-byte access by 16 lanes touches every bank once)
+    constexpr int PW = 36;
     __shared__ float sKS[2][NCH][32][(AggShape<kMatVec, 8>::stride)];
     __shared__ float sCarry[32];
     __shared__ uint32_t sTicket[2];
-    __shared__ float sCS[W][64][8];
+    __shared__ float sCS[W][64][kCSLd];
     __shared__ float sPart[W][64][PW];
 
     const int tile = blockIdx.x;
