@@ -1530,13 +1530,14 @@ __global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
 
     float (*part)[PW] = sPart[tl.wv];
     const int base = tl.lane & ~7;
-    // the angles are read again here (an L2 hit) rather than kept in registers
-    // since the build; one step ahead
-    float4 thn = load_angles(a, tl, clampT(tl.t0 + C - 1, a.T));
+    // with up to 4 steps per lane group the angles loaded for the build stay in
+    // registers; with 8 they are read again here (an L2 hit), one step ahead
+    constexpr bool kKeep = C <= 4;
+    float4 thn = kKeep ? th[C - 1] : load_angles(a, tl, clampT(tl.t0 + C - 1, a.T));
 #pragma unroll
     for (int i = C - 1; i >= 0; --i) {
         const float4 thc = thn;
-        if (i > 0) thn = load_angles(a, tl, clampT(tl.t0 + i - 1, a.T));
+        if (i > 0) thn = kKeep ? th[i - 1] : load_angles(a, tl, clampT(tl.t0 + i - 1, a.T));
         const float g = gv[i] + w;
         float dAc[8];
         outer8(hp[i], g, dAc);              // column v of dA_t = g_t h_{t-1}^T (rotated slots)
