@@ -13,7 +13,7 @@
 // (the WY representation), so
 //     O = Q S^T + causal(Q K^T) U',     S <- S + U'^T K.
 //
-// Two kernels:
+// Two kernels (one when every sequence is a single chunk entered from S = 0):
 //   * delta_prep_kernel, one workgroup per (sequence, chunk), all chunks at
 //     once: G = K K^T and M = causal(Q K^T) on MFMA (fp32 16x16x4), then the
 //     forward substitution for the 128 columns of [W U] (one lane per column,
@@ -88,6 +88,10 @@ __device__ __forceinline__ void lds_barrier()
 // the four waves five apiece: tile = 4 * i + j.
 __constant__ int kPrepTiles[20] = {0, 4, 5, 8, 9, 10, 12, 13, 14, 15, 0, 4, 5, 8, 9, 10, 12, 13, 14, 15};
 
+// DIRECT: a sequence of one chunk entered with S = 0 (no S0): the state pass
+// reduces to O = M U and S_T = U^T K, written here; only U is solved, one
+// 16-column tile per wave, and nothing goes through the workspace.
+template <bool DIRECT>
 __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
 {
     __shared__ float sK[kCh][kLd], sV[kCh][kLd], sQ[kCh][kLd], sA[kCh][kLd], sM[kCh][kLd];
@@ -183,15 +187,16 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
     }
     __syncthreads();
 
-    // block solve of this wave's two column tiles of [W U]
-    const bool isU = wv >= 2;                      // wave-uniform: columns of V give U
-    const int cbase = 32 * (wv & 1);               // first column within K or V
+    // block solve of this wave's column tiles of [W U] (two; DIRECT: one tile of U)
+    constexpr int NH = DIRECT ? 1 : 2;
+    const bool isU = DIRECT || wv >= 2;            // wave-uniform: columns of V give U
+    const int cbase = DIRECT ? 16 * wv : 32 * (wv & 1);   // first column within K or V
     float(*R)[kLd] = isU ? sV : sK;
-    f4v Y[4][2];
+    f4v Y[4][NH];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < NH; ++h) {
             f4v t;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -215,6 +220,43 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
             y = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.w, t[3], y, 0, 0, 0);
             Y[i][h] = y;
         }
+    }
+
+    if constexpr (DIRECT) {
+        // O = M U (rows past the end not stored), S_T = U^T K if requested
+        const int64_t orow0 = static_cast<int64_t>(b) * a.T;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f4v z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k2 = 0; k2 <= i; ++k2) {
+                const float4 m = *reinterpret_cast<const float4 *>(&sM[16 * i + li][16 * k2 + 4 * lq]);
+                z = mfma4(m, make_float4(Y[k2][0][0], Y[k2][0][1], Y[k2][0][2], Y[k2][0][3]), z);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * i + 4 * lq + r;
+                if (t < nrow) a.o[(orow0 + t) * kDD + cbase + li] = z[r];
+            }
+        }
+        if (a.ST) {
+            // A: U^T (lane: U[16 kb + 4 lq + j][cbase + li] = Y[kb] register j), B: K[t][16 cb + li]
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                f4v st = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const int t = 16 * kb + 4 * lq;
+                    const float4 kk = make_float4(sK[t][16 * cb + li], sK[t + 1][16 * cb + li], sK[t + 2][16 * cb + li],
+                                                  sK[t + 3][16 * cb + li]);
+                    st = mfma4(make_float4(Y[kb][0][0], Y[kb][0][1], Y[kb][0][2], Y[kb][0][3]), kk, st);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    a.ST[(static_cast<int64_t>(b) * kDD + cbase + 4 * lq + r) * kDD + 16 * cb + li] = st[r];
+            }
+        }
+        return;
     }
 
     // outputs, per chunk: W and Qt = Q - M W row-major (the state kernel reads
@@ -413,8 +455,12 @@ hipError_t launch_delta_fwd(const DeltaGeom &g, const float *q, const float *k, 
     a.wum = reinterpret_cast<float *>(static_cast<char *>(ws) + g.off_wum);
     a.T = g.T;
     a.nC = g.nC;
+    if (g.nC == 1 && S0 == nullptr) {   // one chunk from a zero state: no state pass
+        hipLaunchKernelGGL(delta_prep_kernel<true>, dim3(static_cast<unsigned>(g.B)), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     if (g.nC > 0) {
-        hipLaunchKernelGGL(delta_prep_kernel, dim3(static_cast<unsigned>(g.B * g.nC)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(delta_prep_kernel<false>, dim3(static_cast<unsigned>(g.B * g.nC)), dim3(256), 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

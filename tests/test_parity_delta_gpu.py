@@ -125,3 +125,22 @@ def test_delta_determinism(gpu):
             first = (o.clone(), ST.clone())
         else:
             assert torch.equal(first[0], o) and torch.equal(first[1], ST)
+
+
+@pytest.mark.parametrize("B,T", [(3, 1), (2, 37), (128, 64)])
+def test_delta_single_chunk_from_zero(gpu, B, T):
+    """Sequences of one chunk entered from S = 0 take a one-kernel path (the
+    state pass reduces to O = M U, S_T = U^T K): against the oracle, and against
+    the two-kernel path taken when the same zero state is passed explicitly."""
+    import torch
+    import scan_linear_rnns_amd as mgs
+    say(f"delta single chunk from zero B={B} T={T}")
+    inp = delta_inputs(B, T, 64, 12)
+    q, k, v, beta = (to_dev(x, gpu) for x in (inp.q, inp.k, inp.v, inp.beta))
+    o1, S1, _ = mgs.mgs_delta_fwd(q, k, v, beta, None)
+    o2, S2, _ = mgs.mgs_delta_fwd(q, k, v, beta, torch.zeros(B, 64, 64, device=gpu))
+    ro, rS = oracle.delta_fwd(inp.q, inp.k, inp.v, inp.beta, None)
+    check(dict(o=to_np(o1), ST=to_np(S1)), dict(o=ro, ST=rS))
+    assert normwise(to_np(o1), to_np(o2)) <= 1e-6 and normwise(to_np(S1), to_np(S2)) <= 1e-6
+    o3, S3, _ = mgs.mgs_delta_fwd(q, k, v, beta, None, want_state=False)
+    assert S3 is None and torch.equal(o3, o1)
