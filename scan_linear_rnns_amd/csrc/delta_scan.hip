@@ -340,7 +340,7 @@ __device__ __forceinline__ void load_state_ops(const DeltaArgs &a, int b, int sl
 __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
 {
     __shared__ float sS[16][kLd];    // rows 16 sl .. 16 sl + 15 of the state entering the chunk
-    __shared__ float sUp[kCh][17];   // U' of the chunk, this slice's 16 columns
+    __shared__ float sUpT[16][kLd];  // U'^T of the chunk: this slice's 16 columns, chunk rows along a row
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
     // XCD-aware numbering: workgroups are dealt to the 8 XCDs round-robin
@@ -364,7 +364,7 @@ __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
         const int t0 = ch * kCh;
         const int nrow = min(kCh, a.T - t0);
         const int64_t row0 = static_cast<int64_t>(b) * a.T + t0;
-        lds_barrier();   // sS holds the entering state; sUp is free
+        lds_barrier();   // sS holds the entering state; sUpT is free
 
         // two accumulators per product, so four independent MFMA chains interleave
         f4v up = {cur.u.x, cur.u.y, cur.u.z, cur.u.w}, o = {cur.p.x, cur.p.y, cur.p.z, cur.p.w};
@@ -383,8 +383,7 @@ __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
         }
         up += up2;
         o += o2;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sUp[16 * wv + 4 * lq + r][li] = up[r];
+        *reinterpret_cast<float4 *>(&sUpT[li][16 * wv + 4 * lq]) = make_float4(up[0], up[1], up[2], up[3]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * wv + 4 * lq + r;
@@ -397,7 +396,7 @@ __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int t = 16 * kb + 4 * lq;
-            const float4 uu = make_float4(sUp[t][li], sUp[t + 1][li], sUp[t + 2][li], sUp[t + 3][li]);
+            const float4 uu = *reinterpret_cast<const float4 *>(&sUpT[li][t]);
             if (kb < 2) dS = mfma4(uu, cur.kc[kb], dS);
             else dS2 = mfma4(uu, cur.kc[kb], dS2);
         }
