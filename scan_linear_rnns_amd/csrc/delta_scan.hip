@@ -13,19 +13,23 @@
 // (the WY representation), so
 //     O = Q S^T + causal(Q K^T) U',     S <- S + U'^T K.
 //
-// Two kernels (one when every sequence is a single chunk entered from S = 0):
-//   * delta_prep_kernel, one workgroup per (sequence, chunk), all chunks at
-//     once: G = K K^T and M = causal(Q K^T) on MFMA (fp32 16x16x4), then the
-//     forward substitution for the 128 columns of [W U] (one lane per column,
-//     column-oriented so each step is a row of independent multiply-adds).
-//     Writes W, U, M (3 x 64 x 64 floats per chunk) to the workspace.
-//   * delta_state_kernel, one workgroup per (sequence, 16 rows of S; the four
-//     of a sequence on one XCD), chunks in order: U' = U - W S^T and O = Q S^T + M U' and S += U'^T K, all on MFMA;
-//     the wave w of 4 owns chunk rows 16w..16w+15 for U' and O, and columns
-//     16w..16w+15 of its 16 x 64 slice of S, kept in accumulator registers
-//     across chunks.  Slices of S are independent (the recurrence mixes the
-//     columns of S, never its rows), so the 4 slices run in parallel.
+// Across chunks the state follows an affine map per chunk:
+//     S <- S + U'^T K = S (I - W^T K) + U^T K = S A + Bc.
 //
+// Three kernels (one when every sequence is a single chunk entered from S = 0):
+//   * delta_prep_kernel, one workgroup per (sequence, chunk), all chunks at
+//     once: A = strict_lower(diag(beta) K K^T) and M = causal(Q K^T) on MFMA
+//     (fp32 16x16x4), the four 16 x 16 diagonal blocks of I + A inverted by
+//     substitution, the block solve for [W U] kept in MFMA accumulator
+//     registers, then Qt = Q - M W, P = M U, A^T and Bc^T.
+//   * delta_state_kernel, one workgroup per (sequence, 16 rows of S; the four
+//     of a sequence on one XCD), chunks in order: S <- S A + Bc, one
+//     16 x 64 x 64 MFMA product per chunk and one barrier; stores the state
+//     entering each chunk.  Rows of S never mix, so the 4 slices run in
+//     parallel.
+//   * delta_out_kernel, one workgroup per (sequence, chunk), all at once:
+//     O = Qt S^T + P from the state entering the chunk.
+
 // MFMA operand layout (v_mfma_f32_16x16x4f32, measured): lane l supplies
 // A[l % 16][l / 16] and B[l / 16][l % 16]; accumulator register r of lane l is
 // D[4 (l / 16) + r][l % 16].  The reduction index is permuted so that lane l
@@ -41,6 +45,9 @@ namespace {
 constexpr int kDD = 64;   // dk = dv
 constexpr int kCh = 64;   // steps per chunk
 constexpr int kLd = 68;   // LDS row stride (floats) of 64-wide tiles (16-byte aligned rows)
+// 64 x 64 tiles per (sequence, chunk) in the workspace: Qt, P^T, A^T, Bc^T and
+// the state entering the chunk
+constexpr int kWsTiles = 5;
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 
@@ -56,7 +63,7 @@ __device__ __forceinline__ f4v mfma4(float4 a, float4 b, f4v c)
 struct DeltaArgs {
     const float *q, *k, *v, *beta, *S0;
     float *o, *ST;
-    float *wum;   // per (sequence, chunk): W, U^T, Qt = Q - M W, P^T = (M U)^T, K^T, each 64 x 64
+    float *wum;   // per (sequence, chunk): Qt, P^T, A^T, Bc^T, entering state, each 64 x 64
     int T, nC;
     int B;
 };
@@ -259,25 +266,18 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
         return;
     }
 
-    // outputs, per chunk: W and Qt = Q - M W row-major (the state kernel reads
-    // their rows), U^T, P^T = (M U)^T and K^T (it reads their columns), so
-    // that every operand of the state kernel is a 16-byte load per lane
-    float *wum = a.wum + static_cast<int64_t>(bc) * 5 * kCh * kDD;
-    float *gW = wum, *gUT = wum + kCh * kDD, *gQ = wum + 2 * kCh * kDD, *gPT = wum + 3 * kCh * kDD;
-    float *gKT = wum + 4 * kCh * kDD;
+    // outputs, per chunk (row-major 64 x 64 each): Qt = Q - M W and P^T = (M U)^T
+    // for the output kernel; the chunk's affine map of the state,
+    //     S -> S A + Bc,   A = I - W^T K,   Bc = U^T K,
+    // as A^T = I - K^T W and Bc^T = K^T U for the state pass
+    float *wum = a.wum + static_cast<int64_t>(bc) * kWsTiles * kCh * kDD;
+    float *gQ = wum, *gPT = wum + kCh * kDD, *gAT = wum + 2 * kCh * kDD, *gBT = wum + 3 * kCh * kDD;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int col = cbase + 16 * h + li;
             const int row = 16 * i + 4 * lq;
-            if (isU) {
-                *reinterpret_cast<float4 *>(gUT + col * kCh + row) =
-                    make_float4(Y[i][h][0], Y[i][h][1], Y[i][h][2], Y[i][h][3]);
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) gW[(row + r) * kDD + col] = Y[i][h][r];
-            }
             f4v z;
 #pragma unroll
             for (int r = 0; r < 4; ++r) z[r] = isU ? 0.0f : sQ[row + r][col];
@@ -298,55 +298,69 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
             }
         }
     }
-    // K^T (zero past the end of the sequence, as staged)
+    // A^T = I - K^T W (W waves) or Bc^T = K^T U (U waves): tile rows 16 cb of
+    // the key index, columns this wave's W or U columns; A operand K^T[16 cb +
+    // li][t] = K[t][16 cb + li], B operand the solved block registers
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int e = tid + 256 * it;          // 1024 float4 = 64 columns x 16 row groups
-        const int c = e >> 4, t4 = (e & 15) * 4;
-        *reinterpret_cast<float4 *>(gKT + c * kCh + t4) =
-            make_float4(sK[t4][c], sK[t4 + 1][c], sK[t4 + 2][c], sK[t4 + 3][c]);
+    for (int cb = 0; cb < 4; ++cb) {
+        float4 kt[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int t = 16 * kb + 4 * lq;
+            kt[kb] = make_float4(sK[t][16 * cb + li], sK[t + 1][16 * cb + li], sK[t + 2][16 * cb + li],
+                                 sK[t + 3][16 * cb + li]);
+            if (!isU) kt[kb] = make_float4(-kt[kb].x, -kt[kb].y, -kt[kb].z, -kt[kb].w);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int col = cbase + 16 * h + li;
+            f4v z;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) z[r] = (!isU && 16 * cb + 4 * lq + r == col) ? 1.0f : 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                z = mfma4(kt[kb], make_float4(Y[kb][h][0], Y[kb][h][1], Y[kb][h][2], Y[kb][h][3]), z);
+            float *g = isU ? gBT : gAT;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) g[(16 * cb + 4 * lq + r) * kDD + col] = z[r];
+        }
     }
 }
 
 // ------------------------------------------------------------ state kernel
-// Per chunk, for the 16 rows of S this workgroup owns (B operand: S[16 sl + li][c]):
-//     U' = U - W S^T,   O = Qt S^T + P,   S += U'^T K.
-// The operands of the next chunk are loaded while this chunk computes.
+// The chunks' affine maps in order: S <- S A + Bc.  Each workgroup owns 16
+// rows of S (rows of S never mix), wave w the columns 16w .. 16w+15 of them,
+// kept in accumulator registers; before each chunk the state entering it is
+// stored for the output kernel.  One barrier per chunk: the slice of S is
+// exchanged through two LDS buffers in turn.  The next chunk's operands are
+// loaded while this chunk computes.
 
 struct StateOps {
-    float4 w4[4], q4[4];   // rows 16 wv + li of W and Qt, reduction slices 16 kb + 4 lq
-    float4 u, p;           // U, P [16 wv + 4 lq + r][16 sl + li], r = 0..3
-    float4 kc[4];          // K[16 kb + 4 lq + j][16 wv + li], j = 0..3 (zero past the end)
+    float4 at[4];   // A^T[16 wv + li][16 kb + 4 lq .. +3] = A[16 kb + 4 lq + j][16 wv + li]
+    float4 bt;      // Bc^T[16 wv + li][16 sl + 4 lq .. +3] = Bc[16 sl + 4 lq + r][16 wv + li]
 };
 
 __device__ __forceinline__ void load_state_ops(const DeltaArgs &a, int b, int sl, int wv, int li, int lq, int ch,
                                                StateOps &op)
 {
-    const float *wum = a.wum + (static_cast<int64_t>(b) * a.nC + ch) * 5 * kCh * kDD;
-    const float *gW = wum, *gUT = wum + kCh * kDD, *gQ = wum + 2 * kCh * kDD, *gPT = wum + 3 * kCh * kDD;
-    const float *gKT = wum + 4 * kCh * kDD;
+    const float *wum = a.wum + (static_cast<int64_t>(b) * a.nC + ch) * kWsTiles * kCh * kDD;
+    const float *gAT = wum + 2 * kCh * kDD, *gBT = wum + 3 * kCh * kDD;
     const int ra = 16 * wv + li;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        const int c = 16 * kb + 4 * lq;
-        op.w4[kb] = *reinterpret_cast<const float4 *>(gW + ra * kDD + c);
-        op.q4[kb] = *reinterpret_cast<const float4 *>(gQ + ra * kDD + c);
-        op.kc[kb] = *reinterpret_cast<const float4 *>(gKT + ra * kCh + c);
-    }
-    op.u = *reinterpret_cast<const float4 *>(gUT + (16 * sl + li) * kCh + 16 * wv + 4 * lq);
-    op.p = *reinterpret_cast<const float4 *>(gPT + (16 * sl + li) * kCh + 16 * wv + 4 * lq);
+    for (int kb = 0; kb < 4; ++kb)
+        op.at[kb] = *reinterpret_cast<const float4 *>(gAT + ra * kDD + 16 * kb + 4 * lq);
+    op.bt = *reinterpret_cast<const float4 *>(gBT + ra * kDD + 16 * sl + 4 * lq);
 }
 
 __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
 {
-    __shared__ float sS[16][kLd];    // rows 16 sl .. 16 sl + 15 of the state entering the chunk
-    __shared__ float sUpT[16][kLd];  // U'^T of the chunk: this slice's 16 columns, chunk rows along a row
+    __shared__ float sS[2][16][kLd];   // rows 16 sl .. 16 sl + 15 of the state, two buffers in turn
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
     // XCD-aware numbering: workgroups are dealt to the 8 XCDs round-robin
     // (XCD = blockIdx mod 8), so the four slices of sequence b get blockIdx
-    // 32 (b / 8) + 8 sl + b % 8 and share one XCD's L2 for the rows of W, Qt
-    // and K^T that all four read.  The grid is padded to a multiple of 32.
+    // 32 (b / 8) + 8 sl + b % 8 and share one XCD's L2 for the rows of A^T they
+    // all read.  The grid is padded to a multiple of 32.
     const int xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
     const int sl = rest & 3, b = (rest >> 2) * 8 + xcd;
     if (b >= a.B) return;   // padding workgroup (whole workgroup, before any barrier)
@@ -356,53 +370,25 @@ __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
     f4v S;
 #pragma unroll
     for (int r = 0; r < 4; ++r) S[r] = a.S0 ? a.S0[sbase + r * kDD] : 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sS[4 * lq + r][16 * wv + li] = S[r];
 
-    // one chunk: U' = U - W S^T, O = Qt S^T + P, S += U'^T K
+    // one chunk: store the entering state, then S <- S A + Bc
     auto chunk = [&](int ch, const StateOps &cur) {
-        const int t0 = ch * kCh;
-        const int nrow = min(kCh, a.T - t0);
-        const int64_t row0 = static_cast<int64_t>(b) * a.T + t0;
-        lds_barrier();   // sS holds the entering state; sUpT is free
-
-        // two accumulators per product, so four independent MFMA chains interleave
-        f4v up = {cur.u.x, cur.u.y, cur.u.z, cur.u.w}, o = {cur.p.x, cur.p.y, cur.p.z, cur.p.w};
-        f4v up2 = {0.0f, 0.0f, 0.0f, 0.0f}, o2 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const float4 s4 = *reinterpret_cast<const float4 *>(&sS[li][16 * kb + 4 * lq]);
-            const float4 nw = make_float4(-cur.w4[kb].x, -cur.w4[kb].y, -cur.w4[kb].z, -cur.w4[kb].w);
-            if (kb < 2) {
-                up = mfma4(nw, s4, up);
-                o = mfma4(cur.q4[kb], s4, o);
-            } else {
-                up2 = mfma4(nw, s4, up2);
-                o2 = mfma4(cur.q4[kb], s4, o2);
-            }
-        }
-        up += up2;
-        o += o2;
-        *reinterpret_cast<float4 *>(&sUpT[li][16 * wv + 4 * lq]) = make_float4(up[0], up[1], up[2], up[3]);
+        float *sj = a.wum + ((static_cast<int64_t>(b) * a.nC + ch) * kWsTiles + 4) * kCh * kDD;
+        float(*buf)[kLd] = sS[ch & 1];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = 16 * wv + 4 * lq + r;
-            if (t < nrow) a.o[(row0 + t) * kDD + 16 * sl + li] = o[r];
+            buf[4 * lq + r][16 * wv + li] = S[r];
+            sj[(16 * sl + 4 * lq + r) * kDD + 16 * wv + li] = S[r];
         }
         lds_barrier();
-
-        // S += U'^T K on this wave's columns (A: U'[t][16 sl + li], B: K[t][16 wv + li])
-        f4v dS = {0.0f, 0.0f, 0.0f, 0.0f}, dS2 = {0.0f, 0.0f, 0.0f, 0.0f};
+        f4v n1 = {cur.bt.x, cur.bt.y, cur.bt.z, cur.bt.w}, n2 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const int t = 16 * kb + 4 * lq;
-            const float4 uu = *reinterpret_cast<const float4 *>(&sUpT[li][t]);
-            if (kb < 2) dS = mfma4(uu, cur.kc[kb], dS);
-            else dS2 = mfma4(uu, cur.kc[kb], dS2);
+            const float4 s4 = *reinterpret_cast<const float4 *>(&buf[li][16 * kb + 4 * lq]);
+            if (kb < 2) n1 = mfma4(s4, cur.at[kb], n1);
+            else n2 = mfma4(s4, cur.at[kb], n2);
         }
-        S += dS + dS2;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sS[4 * lq + r][16 * wv + li] = S[r];
+        S = n1 + n2;
     };
 
     // two operand sets in turn: the next chunk's loads are issued before this
@@ -432,6 +418,43 @@ __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
     }
 }
 
+// ----------------------------------------------------------- output kernel
+// O = Qt S^T + P per chunk, all chunks at once, from the state entering each
+// chunk: one workgroup per (sequence, chunk), wave w the chunk rows 16w ..
+// 16w+15 (A operand: rows of Qt; B operand: S[16 cb + li][c], rows of S).
+__global__ void __launch_bounds__(256) delta_out_kernel(DeltaArgs a)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const int bc = blockIdx.x;   // sequence * nC + chunk
+    const int b = bc / a.nC, ch = bc - b * a.nC;
+    const int t0 = ch * kCh;
+    const int nrow = min(kCh, a.T - t0);
+    const int64_t row0 = static_cast<int64_t>(b) * a.T + t0;
+    const float *wum = a.wum + static_cast<int64_t>(bc) * kWsTiles * kCh * kDD;
+    const float *gQ = wum, *gPT = wum + kCh * kDD, *gS = wum + 4 * kCh * kDD;
+    float4 q4[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) q4[kb] = *reinterpret_cast<const float4 *>(gQ + (16 * wv + li) * kDD + 16 * kb + 4 * lq);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const float4 p = *reinterpret_cast<const float4 *>(gPT + (16 * cb + li) * kCh + 16 * wv + 4 * lq);
+        f4v o1 = {p.x, p.y, p.z, p.w}, o2 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const float4 s4 = *reinterpret_cast<const float4 *>(gS + (16 * cb + li) * kDD + 16 * kb + 4 * lq);
+            if (kb < 2) o1 = mfma4(q4[kb], s4, o1);
+            else o2 = mfma4(q4[kb], s4, o2);
+        }
+        const f4v o = o1 + o2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * wv + 4 * lq + r;
+            if (t < nrow) a.o[(row0 + t) * kDD + 16 * cb + li] = o[r];
+        }
+    }
+}
+
 }  // namespace
 
 DeltaGeom delta_geometry(int64_t B, int64_t T, int64_t d)
@@ -442,7 +465,7 @@ DeltaGeom delta_geometry(int64_t B, int64_t T, int64_t d)
     g.d = static_cast<int>(d);
     g.nC = static_cast<int>((T + kCh - 1) / kCh);
     g.off_wum = 256;   // after a header kept for the common workspace check
-    g.bytes = g.off_wum + static_cast<size_t>(B) * g.nC * 5 * kCh * kDD * sizeof(float);
+    g.bytes = g.off_wum + static_cast<size_t>(B) * g.nC * kWsTiles * kCh * kDD * sizeof(float);
     return g;
 }
 
@@ -466,6 +489,11 @@ hipError_t launch_delta_fwd(const DeltaGeom &g, const float *q, const float *k, 
     a.B = static_cast<int>(g.B);
     const unsigned groups = static_cast<unsigned>((g.B + 7) / 8) * 32;   // 4 slices x padded sequences
     hipLaunchKernelGGL(delta_state_kernel, dim3(groups), dim3(256), 0, s, a);
+    if (g.nC > 0) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(delta_out_kernel, dim3(static_cast<unsigned>(g.B * g.nC)), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
