@@ -253,6 +253,43 @@ def copy_bandwidth(dev):
     return 2 * n * 4 / sec / 1e9
 
 
+def cold_copy_floor(dev, nbytes, steps, warmup):
+    """A device copy moving `nbytes` in total (nbytes/2 read + nbytes/2 written), on
+    buffers rotated through >= 512 MiB like the ops' inputs, captured in a graph:
+    microseconds per copy.  The streaming rate this chip reaches for a transfer of
+    this size from cold memory, for comparison with a step that moves as much."""
+    import torch
+    n = max(1, nbytes // 8)   # floats per buffer
+    m = max(1, math.ceil(ROTATE_BYTES / (8 * n)))
+    src = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(m)]
+    dst = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(m)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(max(warmup, 1)):
+            dst[i % m].copy_(src[i % m])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            dst[i % m].copy_(src[i % m])
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / steps)
+    times.sort()
+    del g, src, dst
+    torch.cuda.empty_cache()
+    return times[1]
+
+
 def cpu_baseline(seconds):
     import numpy as np
 
@@ -458,6 +495,23 @@ def main():
     if not args.no_ops and not only:
         log("copy bandwidth")
         out["copy_GBps"] = copy_bandwidth(dev)
+        if head is not None:
+            # the chip's cold streaming rate at the headline step's size: one copy
+            # moving the step's compulsory bytes (two of them stand for the step's two
+            # dependent launches, each moving about half)
+            run = head[0]
+            tot = run.fwd_bytes + run.bwd_bytes
+            one = cold_copy_floor(dev, tot, max(20, K // 2), W)
+            half = cold_copy_floor(dev, tot // 2, max(20, K // 2), W)
+            out["cold_copy_reference"] = {
+                "bytes": tot, "us_one_copy_of_step_bytes": one,
+                "GBps_one_copy": tot / (one * 1e-6) / 1e9,
+                "us_two_copies_of_half": 2 * half,
+                "step_us": head[1],
+                "step_over_two_copies": head[1] / (2 * half),
+            }
+            log(f"cold copy of the step's {tot / 1e6:.1f} MB: {one:.2f} us ({tot / (one * 1e-6) / 1e12:.2f} TB/s); "
+                f"two copies of half: {2 * half:.2f} us; the step: {head[1]:.2f} us")
     out["ops"] = ops
     out["kernel_source_hash"] = kernel_source_hash()
     if not args.no_cpu_baseline and head is not None:
