@@ -568,13 +568,33 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
 
 // Tile geometry.  Sequences that fit one tile (T <= 128) use 32 chains per
 // wave row and 4 waves, which gives the most workgroups at the lab shape;
-// longer sequences use 64 chains per row and 8 waves (fewer, larger tiles
-// along T, hence shorter look-back walks).  Chosen from measured sweeps.
+// longer sequences use 64 chains per row, 8 waves and up to 16 steps per lane
+// (fewer, larger tiles along T, hence shorter look-back walks).  Chosen from
+// measured sweeps over chains per row {32, 64}, waves {2, 4, 8, 16} and steps
+// per lane {8, 16}; the macros below let a build try other shapes.
 #ifndef MGS_LOG_SHORT_T
 #define MGS_LOG_SHORT_T 128
 #endif
+#ifndef MGS_SHORT_CHW
+#define MGS_SHORT_CHW 32
+#endif
+#ifndef MGS_SHORT_W
+#define MGS_SHORT_W 4
+#endif
+#ifndef MGS_LONG_CHW
+#define MGS_LONG_CHW 64
+#endif
+#ifndef MGS_LONG_W
+#define MGS_LONG_W 8
+#endif
+#ifndef MGS_LONG_MAXC
+#define MGS_LONG_MAXC 16
+#endif
 constexpr int kShortT = MGS_LOG_SHORT_T;
+constexpr int kShortChw = MGS_SHORT_CHW, kShortW = MGS_SHORT_W;
+constexpr int kLongChw = MGS_LONG_CHW, kLongW = MGS_LONG_W;
 constexpr int kMaxC = 16;
+constexpr int kLongMaxC = MGS_LONG_MAXC;
 
 template <class Alg, int CHW, int W, int C>
 hipError_t launch_fwd_c(const LogGeom &g, const LogFwdArgs &args, hipStream_t s)
@@ -600,21 +620,21 @@ hipError_t launch_bwd_c(const LogGeom &g, const LogBwdArgs &args, hipStream_t s)
 
 #define MGS_ELEM_DISPATCH(FN, ALG, g, a, s)                                                       \
     do {                                                                                          \
-        if ((g).CHW == 32) {                                                                      \
+        if ((g).CHW == kShortChw && (g).W == kShortW) {                                           \
             switch ((g).C) {                                                                      \
-            case 1: return FN<ALG, 32, 4, 1>(g, a, s);                                            \
-            case 2: return FN<ALG, 32, 4, 2>(g, a, s);                                            \
-            case 4: return FN<ALG, 32, 4, 4>(g, a, s);                                            \
-            case 8: return FN<ALG, 32, 4, 8>(g, a, s);                                            \
-            default: return FN<ALG, 32, 4, 16>(g, a, s);                                          \
+            case 1: return FN<ALG, kShortChw, kShortW, 1>(g, a, s);                               \
+            case 2: return FN<ALG, kShortChw, kShortW, 2>(g, a, s);                               \
+            case 4: return FN<ALG, kShortChw, kShortW, 4>(g, a, s);                               \
+            case 8: return FN<ALG, kShortChw, kShortW, 8>(g, a, s);                               \
+            default: return FN<ALG, kShortChw, kShortW, 16>(g, a, s);                             \
             }                                                                                     \
         }                                                                                         \
         switch ((g).C) {                                                                          \
-        case 1: return FN<ALG, 64, 8, 1>(g, a, s);                                                \
-        case 2: return FN<ALG, 64, 8, 2>(g, a, s);                                                \
-        case 4: return FN<ALG, 64, 8, 4>(g, a, s);                                                \
-        case 8: return FN<ALG, 64, 8, 8>(g, a, s);                                                \
-        default: return FN<ALG, 64, 8, 16>(g, a, s);                                              \
+        case 1: return FN<ALG, kLongChw, kLongW, 1>(g, a, s);                                     \
+        case 2: return FN<ALG, kLongChw, kLongW, 2>(g, a, s);                                     \
+        case 4: return FN<ALG, kLongChw, kLongW, 4>(g, a, s);                                     \
+        case 8: return FN<ALG, kLongChw, kLongW, 8>(g, a, s);                                     \
+        default: return FN<ALG, kLongChw, kLongW, 16>(g, a, s);                                   \
         }                                                                                         \
     } while (0)
 
@@ -662,11 +682,12 @@ LogGeom log_geometry(int64_t B, int64_t T, int64_t d)
     g.T = static_cast<int>(T);
     g.d = static_cast<int>(d);
     const bool short_t = T <= kShortT;
-    g.CHW = short_t ? 32 : 64;
-    g.W = short_t ? 4 : 8;
+    g.CHW = short_t ? kShortChw : kLongChw;
+    g.W = short_t ? kShortW : kLongW;
     const int nch = g.W * (64 / g.CHW);
+    const int maxc = short_t ? kMaxC : kLongMaxC;
     int C = 1;
-    while (C < kMaxC && static_cast<int64_t>(nch) * C < T) C *= 2;
+    while (C < maxc && static_cast<int64_t>(nch) * C < T) C *= 2;
     g.C = C;
     g.TT = nch * C;
     g.nT = static_cast<int>((T + g.TT - 1) / g.TT);
