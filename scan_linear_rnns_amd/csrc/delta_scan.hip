@@ -91,9 +91,11 @@ __device__ __forceinline__ void lds_barrier()
 // MFMA result (accumulator layout, rows 4 (l/16) + r) is directly the B
 // operand of the next MFMA under the permuted reduction index.
 
-// Tiles of G (first ten) and M (last ten) on or below the diagonal, dealt to
-// the four waves five apiece: tile = 4 * i + j.
-__constant__ int kPrepTiles[20] = {0, 4, 5, 8, 9, 10, 12, 13, 14, 15, 0, 4, 5, 8, 9, 10, 12, 13, 14, 15};
+// The ten 16 x 16 tiles on or below the diagonal, tile = 4 i + j, one per
+// nibble (slot s in bits 4s .. 4s+3): slots 0-9 are tiles of G, 10-19 the same
+// tiles of M, dealt to the four waves five apiece and decoded with scalar
+// shifts of a wave-uniform slot.
+constexpr uint64_t kPrepTiles = 0xFEDCA98540ull;
 
 // DIRECT: a sequence of one chunk entered with S = 0 (no S0): the state pass
 // reduces to O = M U and S_T = U^T K, written here; only U is solved, one
@@ -103,7 +105,7 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
 {
     __shared__ float sK[kCh][kLd], sV[kCh][kLd], sQ[kCh][kLd], sA[kCh][kLd], sM[kCh][kLd];
     __shared__ float sX[4][16][20];   // the inverses of the diagonal blocks of L
-    __shared__ float sB[kCh];
+    __shared__ __align__(16) float sB[kCh];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
     const int bc = blockIdx.x;   // sequence * nC + chunk
@@ -140,37 +142,59 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
     __syncthreads();
 
     // A = strict_lower(diag(beta) K K^T) and M = causal(Q K^T), lower tiles
-    // only; all five tiles' MFMAs first, each reduction in two halves, so ten
-    // independent MFMA chains interleave
+    // only, five tiles per wave: each step of the reduction issues one MFMA
+    // of every tile in turn, so consecutive MFMAs do not depend on each other
     {
-        f4v acc[5][2];
+        f4v acc[5];
+        const int wvu = __builtin_amdgcn_readfirstlane(wv);
+        int rowL[5], rowK[5];
+        bool isM[5];
 #pragma unroll
         for (int n = 0; n < 5; ++n) {
-            const int slot = wv + 4 * n;
-            const int tile = kPrepTiles[slot];
-            const int bi = tile >> 2, bj = tile & 3;
-            float(*L)[kLd] = slot >= 10 ? sQ : sK;   // wave-uniform
-            acc[n][0] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
-            acc[n][1] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const float4 x = *reinterpret_cast<const float4 *>(&L[16 * bi + li][16 * kb + 4 * lq]);
-                const float4 y = *reinterpret_cast<const float4 *>(&sK[16 * bj + li][16 * kb + 4 * lq]);
-                acc[n][kb >> 1] = mfma4(x, y, acc[n][kb >> 1]);
-            }
+            const int slot = wvu + 4 * n;
+            const int tile = static_cast<int>((kPrepTiles >> (4 * (slot % 10))) & 15);
+            rowL[n] = 16 * (tile >> 2) + li;
+            rowK[n] = 16 * (tile & 3) + li;
+            isM[n] = slot >= 10;   // wave-uniform
+            acc[n] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
         }
+        // beta of the tiles' rows, read up front
+        float4 bq[5];
+#pragma unroll
+        for (int n = 0; n < 5; ++n) bq[n] = *reinterpret_cast<const float4 *>(&sB[rowL[n] - li + 4 * lq]);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            float4 x[5], y[5];
+#pragma unroll
+            for (int n = 0; n < 5; ++n) {
+                const float(*L)[kLd] = isM[n] ? sQ : sK;
+                x[n] = *reinterpret_cast<const float4 *>(&L[rowL[n]][16 * kb + 4 * lq]);
+                y[n] = *reinterpret_cast<const float4 *>(&sK[rowK[n]][16 * kb + 4 * lq]);
+            }
+#pragma unroll
+            for (int n = 0; n < 5; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[n].x, y[n].x, acc[n], 0, 0, 0);
+#pragma unroll
+            for (int n = 0; n < 5; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[n].y, y[n].y, acc[n], 0, 0, 0);
+#pragma unroll
+            for (int n = 0; n < 5; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[n].z, y[n].z, acc[n], 0, 0, 0);
+#pragma unroll
+            for (int n = 0; n < 5; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[n].w, y[n].w, acc[n], 0, 0, 0);
+        }
+        // lower parts of the tiles (rows scaled by beta for A), stored without
+        // branches: the destination and the row scale are chosen per tile (the
+        // row scales are pinned in registers first, so that their reads are not
+        // sunk into the stores as conditional reads with a wait apiece)
+#pragma unroll
+        for (int n = 0; n < 5; ++n) asm volatile("" : "+v"(bq[n].x), "+v"(bq[n].y), "+v"(bq[n].z), "+v"(bq[n].w));
 #pragma unroll
         for (int n = 0; n < 5; ++n) {
-            const int slot = wv + 4 * n;
-            const int tile = kPrepTiles[slot];
-            const int bi = tile >> 2, bj = tile & 3;
-            const f4v g = acc[n][0] + acc[n][1];
+            const int i0 = rowL[n] - li + 4 * lq, j = rowK[n];
+            const float sc[4] = {isM[n] ? 1.0f : bq[n].x, isM[n] ? 1.0f : bq[n].y, isM[n] ? 1.0f : bq[n].z,
+                                 isM[n] ? 1.0f : bq[n].w};
+            float(*dst)[kLd] = isM[n] ? sM : sA;
+            const int diag = isM[n] ? 1 : 0;   // M keeps its diagonal, A does not
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * bi + 4 * lq + r, j = 16 * bj + li;
-                if (slot >= 10) sM[i][j] = j <= i ? g[r] : 0.0f;
-                else sA[i][j] = j < i ? sB[i] * g[r] : 0.0f;
-            }
+            for (int r = 0; r < 4; ++r) dst[i0 + r][j] = (j < i0 + r + diag) ? sc[r] * acc[n][r] : 0.0f;
         }
     }
     __syncthreads();
@@ -230,38 +254,59 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
     }
 
     if constexpr (DIRECT) {
-        // O = M U (rows past the end not stored), S_T = U^T K if requested
+        // O = M U (rows past the end not stored), S_T = U^T K if requested;
+        // the row blocks' (column blocks') products advance together, one MFMA
+        // of each in turn
         const int64_t orow0 = static_cast<int64_t>(b) * a.T;
+        f4v z[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+            float4 m[4];
+#pragma unroll
+            for (int i = k2; i < 4; ++i) m[i] = *reinterpret_cast<const float4 *>(&sM[16 * i + li][16 * k2 + 4 * lq]);
+#pragma unroll
+            for (int i = k2; i < 4; ++i) z[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(m[i].x, Y[k2][0][0], z[i], 0, 0, 0);
+#pragma unroll
+            for (int i = k2; i < 4; ++i) z[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(m[i].y, Y[k2][0][1], z[i], 0, 0, 0);
+#pragma unroll
+            for (int i = k2; i < 4; ++i) z[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(m[i].z, Y[k2][0][2], z[i], 0, 0, 0);
+#pragma unroll
+            for (int i = k2; i < 4; ++i) z[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(m[i].w, Y[k2][0][3], z[i], 0, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            f4v z = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int k2 = 0; k2 <= i; ++k2) {
-                const float4 m = *reinterpret_cast<const float4 *>(&sM[16 * i + li][16 * k2 + 4 * lq]);
-                z = mfma4(m, make_float4(Y[k2][0][0], Y[k2][0][1], Y[k2][0][2], Y[k2][0][3]), z);
-            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * i + 4 * lq + r;
-                if (t < nrow) a.o[(orow0 + t) * kDD + cbase + li] = z[r];
+                if (t < nrow) a.o[(orow0 + t) * kDD + cbase + li] = z[i][r];
             }
         }
         if (a.ST) {
             // A: U^T (lane: U[16 kb + 4 lq + j][cbase + li] = Y[kb] register j), B: K[t][16 cb + li]
+            f4v st[4];
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                f4v st = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int cb = 0; cb < 4; ++cb) st[cb] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    const int t = 16 * kb + 4 * lq;
-                    const float4 kk = make_float4(sK[t][16 * cb + li], sK[t + 1][16 * cb + li], sK[t + 2][16 * cb + li],
-                                                  sK[t + 3][16 * cb + li]);
-                    st = mfma4(make_float4(Y[kb][0][0], Y[kb][0][1], Y[kb][0][2], Y[kb][0][3]), kk, st);
-                }
+            for (int kb = 0; kb < 4; ++kb) {
+                const int t = 16 * kb + 4 * lq;
+                float kk[4][4];
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) kk[cb][j] = sK[t + j][16 * cb + li];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb)
+                        st[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(Y[kb][0][j], kk[cb][j], st[cb], 0, 0, 0);
+            }
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    a.ST[(static_cast<int64_t>(b) * kDD + cbase + 4 * lq + r) * kDD + 16 * cb + li] = st[r];
-            }
+                    a.ST[(static_cast<int64_t>(b) * kDD + cbase + 4 * lq + r) * kDD + 16 * cb + li] = st[cb][r];
         }
         return;
     }
@@ -272,58 +317,87 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
     // as A^T = I - K^T W and Bc^T = K^T U for the state pass
     float *wum = a.wum + static_cast<int64_t>(bc) * kWsTiles * kCh * kDD;
     float *gQ = wum, *gPT = wum + kCh * kDD, *gAT = wum + 2 * kCh * kDD, *gBT = wum + 3 * kCh * kDD;
+    // the eight (row block, column tile) products advance together, one MFMA
+    // of each in turn
+    {
+        f4v z[4][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int col = cbase + 16 * h + li;
-            const int row = 16 * i + 4 * lq;
-            f4v z;
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) z[r] = isU ? 0.0f : sQ[row + r][col];
+                for (int r = 0; r < 4; ++r) z[i][h][r] = isU ? 0.0f : sQ[16 * i + 4 * lq + r][cbase + 16 * h + li];
 #pragma unroll
-            for (int k2 = 0; k2 <= i; ++k2) {
+        for (int k2 = 0; k2 < 4; ++k2) {
+            float4 m[4];
+#pragma unroll
+            for (int i = k2; i < 4; ++i) {
                 const float4 mv = *reinterpret_cast<const float4 *>(&sM[16 * i + li][16 * k2 + 4 * lq]);
-                const float4 m = isU ? mv : make_float4(-mv.x, -mv.y, -mv.z, -mv.w);
-                z = __builtin_amdgcn_mfma_f32_16x16x4f32(m.x, Y[k2][h][0], z, 0, 0, 0);
-                z = __builtin_amdgcn_mfma_f32_16x16x4f32(m.y, Y[k2][h][1], z, 0, 0, 0);
-                z = __builtin_amdgcn_mfma_f32_16x16x4f32(m.z, Y[k2][h][2], z, 0, 0, 0);
-                z = __builtin_amdgcn_mfma_f32_16x16x4f32(m.w, Y[k2][h][3], z, 0, 0, 0);
+                m[i] = isU ? mv : make_float4(-mv.x, -mv.y, -mv.z, -mv.w);
             }
-            if (isU) {
-                *reinterpret_cast<float4 *>(gPT + col * kCh + row) = make_float4(z[0], z[1], z[2], z[3]);
-            } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) gQ[(row + r) * kDD + col] = z[r];
-            }
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = k2; i < 4; ++i)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const float mj = j == 0 ? m[i].x : j == 1 ? m[i].y : j == 2 ? m[i].z : m[i].w;
+                        z[i][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(mj, Y[k2][h][j], z[i][h], 0, 0, 0);
+                    }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int col = cbase + 16 * h + li;
+                const int row = 16 * i + 4 * lq;
+                if (isU) {
+                    *reinterpret_cast<float4 *>(gPT + col * kCh + row) =
+                        make_float4(z[i][h][0], z[i][h][1], z[i][h][2], z[i][h][3]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) gQ[(row + r) * kDD + col] = z[i][h][r];
+                }
+            }
     }
     // A^T = I - K^T W (W waves) or Bc^T = K^T U (U waves): tile rows 16 cb of
     // the key index, columns this wave's W or U columns; A operand K^T[16 cb +
     // li][t] = K[t][16 cb + li], B operand the solved block registers
+    {
+        f4v z[4][2];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        float4 kt[4];
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    z[cb][h][r] = (!isU && 16 * cb + 4 * lq + r == cbase + 16 * h + li) ? 1.0f : 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int t = 16 * kb + 4 * lq;
-            kt[kb] = make_float4(sK[t][16 * cb + li], sK[t + 1][16 * cb + li], sK[t + 2][16 * cb + li],
-                                 sK[t + 3][16 * cb + li]);
-            if (!isU) kt[kb] = make_float4(-kt[kb].x, -kt[kb].y, -kt[kb].z, -kt[kb].w);
+            float kt[4][4];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float x = sK[t + j][16 * cb + li];
+                    kt[cb][j] = isU ? x : -x;
+                }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        z[cb][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[cb][j], Y[kb][h][j], z[cb][h], 0, 0, 0);
         }
+        float *g = isU ? gBT : gAT;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int col = cbase + 16 * h + li;
-            f4v z;
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) z[r] = (!isU && 16 * cb + 4 * lq + r == col) ? 1.0f : 0.0f;
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                z = mfma4(kt[kb], make_float4(Y[kb][h][0], Y[kb][h][1], Y[kb][h][2], Y[kb][h][3]), z);
-            float *g = isU ? gBT : gAT;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) g[(16 * cb + 4 * lq + r) * kDD + col] = z[r];
-        }
+                for (int r = 0; r < 4; ++r) g[(16 * cb + 4 * lq + r) * kDD + cbase + 16 * h + li] = z[cb][h][r];
     }
 }
 
