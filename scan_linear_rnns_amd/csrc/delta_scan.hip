@@ -199,17 +199,26 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
     }
     __syncthreads();
 
-    // X_ww = (I + A_ww)^{-1}: lane c < 16 solves column c, row by row
+    // X_ww = (I + A_ww)^{-1}: lane c < 16 solves column c, row by row, from
+    // the block's rows read up front (16-byte reads, the same address in every
+    // lane)
     if (lane < 16) {
         const int o = 16 * wv;
+        float4 rw[16][4];
+#pragma unroll
+        for (int i = 1; i < 16; ++i)
+#pragma unroll
+            for (int q = 0; 4 * q < i; ++q) rw[i][q] = *reinterpret_cast<const float4 *>(&sA[o + i][o + 4 * q]);
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             float s0 = (i == li) ? 1.0f : 0.0f, s1 = 0.0f;
 #pragma unroll
             for (int j = 0; j < i; ++j) {
-                if (j & 1) s1 = __builtin_fmaf(-sA[o + i][o + j], x[j], s1);
-                else s0 = __builtin_fmaf(-sA[o + i][o + j], x[j], s0);
+                const float4 r4 = rw[i][j >> 2];
+                const float aij = (j & 3) == 0 ? r4.x : (j & 3) == 1 ? r4.y : (j & 3) == 2 ? r4.z : r4.w;
+                if (j & 1) s1 = __builtin_fmaf(-aij, x[j], s1);
+                else s0 = __builtin_fmaf(-aij, x[j], s0);
             }
             x[i] = s0 + s1;
         }
