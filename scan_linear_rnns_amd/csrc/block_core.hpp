@@ -301,11 +301,29 @@ __device__ __forceinline__ void load_col8(const float *p, int v, float *R)
     for (int s = 0; s < 8; ++s) R[s] = p[((s ^ lo) * 8) + v];
 }
 
+__device__ __forceinline__ float xq(float x)   // value of lane v ^ 4 within the 8-lane group
+{
+    const float m = hm(x);   // lane 7 - v, then reversed within the quad
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x1B, 0xF, 0xF, true));
+}
+
+// row v of a row-major 8x8 block at p (16-byte aligned) from rotated slots.
+// Lanes v and v ^ 4 first swap slots 4-7, so that the first 16-byte store of
+// the chain's eight lanes covers rows 0-3 (128 contiguous bytes) and the second
+// rows 4-7: no 32-byte sector is split between two stores, which matters for
+// the nontemporal stores (a split sector would reach HBM twice).  Lane v < 4
+// writes row v, columns 0-3, then row v + 4, columns 0-3 (the partner's slots
+// 4-7); lane v >= 4 writes row v - 4, columns 4-7 (the partner's slots 4-7),
+// then row v, columns 4-7.  Call with all eight lanes of the chain active.
 __device__ __forceinline__ void store_row8(float *p, int v, const float *R)
 {
-    const int lo = v & 4;
-    *reinterpret_cast<float4 *>(p + v * 8 + lo) = make_float4(R[0], R[1], R[2], R[3]);
-    *reinterpret_cast<float4 *>(p + v * 8 + (lo ^ 4)) = make_float4(R[4], R[5], R[6], R[7]);
+    float X[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) X[j] = xq(R[4 + j]);
+    const bool low = v < 4;
+    float *p1 = p + (v & 3) * 8 + (v & 4);
+    store_out4(p1, low ? R[0] : X[0], low ? R[1] : X[1], low ? R[2] : X[2], low ? R[3] : X[3]);
+    store_out4(p1 + 32, low ? X[0] : R[0], low ? X[1] : R[1], low ? X[2] : R[2], low ? X[3] : R[3]);
 }
 
 // ----------------------------------------------------- 16-lane row algebra (k = 16)
@@ -689,13 +707,21 @@ __device__ __forceinline__ void load_vec(const float *p, float *x)
     }
 }
 
+// K consecutive floats at p (aligned to their size, at most 16 bytes).  The
+// lanes of a half-wave store consecutive K-float vectors, so for K <= 4 one
+// store instruction covers whole 32-byte sectors and takes the nontemporal
+// hint; for K = 8 and 16 each lane's vector spans several 16-byte stores whose
+// sectors are completed by the lane's next store, so those stay ordinary
+// stores that L2 merges.
 template <int K>
 __device__ __forceinline__ void store_vec(float *p, const float *x)
 {
     if constexpr (K == 1) {
-        p[0] = x[0];
+        store_out(p, x[0]);
     } else if constexpr (K == 2) {
-        *reinterpret_cast<float2 *>(p) = make_float2(x[0], x[1]);
+        store_out2(p, x[0], x[1]);
+    } else if constexpr (K == 4) {
+        store_out4(p, x[0], x[1], x[2], x[3]);
     } else {
 #pragma unroll
         for (int q = 0; q < K / 4; ++q)
@@ -1367,7 +1393,7 @@ __device__ __forceinline__ void affine_fwd_body(const BlkArgs &a)
     for (int i = 0; i < C; ++i) {
         x = Rw::mv(Ar[i], x, bv[i]);
         const int t = tl.t0 + i;
-        if (tl.cv && t < a.T) a.out[tl.vec0 + t * tl.vstep] = x;
+        if (tl.cv && t < a.T) store_out(&a.out[tl.vec0 + t * tl.vstep], x);
     }
 }
 
@@ -1446,11 +1472,11 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
         w = Rw::mv(ATr[i], g, 0.0f);
         const int t = tl.t0 + i;
         if (tl.cv && t < a.T) {
-            a.out2[tl.vec0 + t * tl.vstep] = g;
+            store_out(&a.out2[tl.vec0 + t * tl.vstep], g);
             Rw::store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, dAr);
         }
     }
-    if (tl.cv && tl.t0 == 0) a.out3[tl.bb * a.d + tl.jb * K + tl.v] = w;   // A_1^T g_1
+    if (tl.cv && tl.t0 == 0) store_out(&a.out3[tl.bb * a.d + tl.jb * K + tl.v], w);   // A_1^T g_1
 }
 
 // =============================================== Givens angle-fused bwd
@@ -1566,16 +1592,16 @@ __global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
         const int t = tl.t0 + i;
         if (tl.cv && t < a.T) {
             const int64_t blk = tl.blk0 + static_cast<int64_t>(t) * a.nb;
-            a.out2[tl.vec0 + t * tl.vstep] = g;
+            store_out(&a.out2[tl.vec0 + t * tl.vstep], g);
             if (tl.v < 7)
-                *reinterpret_cast<float4 *>(a.dtheta + blk * kAngles + 4 * tl.v) = acc;
+                store_out4(a.dtheta + blk * kAngles + 4 * tl.v, acc.x, acc.y, acc.z, acc.w);
             else
-                a.dsg[blk] = acc.x;
+                store_out(&a.dsg[blk], acc.x);
         }
         asm volatile("" : "+v"(w));
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (tl.cv && tl.t0 == 0) a.out3[tl.bb * a.d + tl.jb * 8 + tl.v] = w;   // A_1^T g_1
+    if (tl.cv && tl.t0 == 0) store_out(&a.out3[tl.bb * a.d + tl.jb * 8 + tl.v], w);   // A_1^T g_1
 }
 
 // ================================================ block cumulative product

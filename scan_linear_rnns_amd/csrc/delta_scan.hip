@@ -37,6 +37,7 @@
 // load then feeds four MFMAs.
 #include <hip/hip_runtime.h>
 
+#include "device.hpp"
 #include "launch.hpp"
 
 namespace mgs {
@@ -289,7 +290,7 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * i + 4 * lq + r;
-                if (t < nrow) a.o[(orow0 + t) * kDD + cbase + li] = z[i][r];
+                if (t < nrow) store_out(&a.o[(orow0 + t) * kDD + cbase + li], z[i][r]);
             }
         }
         if (a.ST) {
@@ -315,7 +316,7 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
             for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    a.ST[(static_cast<int64_t>(b) * kDD + cbase + 4 * lq + r) * kDD + 16 * cb + li] = st[cb][r];
+                    store_out(&a.ST[(static_cast<int64_t>(b) * kDD + cbase + 4 * lq + r) * kDD + 16 * cb + li], st[cb][r]);
         }
         return;
     }
@@ -497,7 +498,7 @@ __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
     }
     if (a.ST) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) a.ST[sbase + r * kDD] = S[r];
+        for (int r = 0; r < 4; ++r) store_out(&a.ST[sbase + r * kDD], S[r]);
     }
 }
 
@@ -533,7 +534,7 @@ __global__ void __launch_bounds__(256) delta_out_kernel(DeltaArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * wv + 4 * lq + r;
-            if (t < nrow) a.o[(row0 + t) * kDD + 16 * cb + li] = o[r];
+            if (t < nrow) store_out(&a.o[(row0 + t) * kDD + 16 * cb + li], o[r]);
         }
     }
 }

@@ -34,6 +34,38 @@ struct WsHeader {
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
 
+// Output stores.  Every output element (and every chunk state a forward saves
+// for its backward) is written exactly once and never read back by the kernel
+// that writes it, so the stores carry the nontemporal hint: the lines drain to
+// HBM while the kernel runs instead of staying dirty in L2 until the
+// write-back at the end of the kernel, which the next kernel on the stream
+// waits for.  Measured on the log-space pair at B=128, T=64, d=64: 8.4 -> 7.5 us.
+__device__ __forceinline__ void store_out(float *p, float v) { __builtin_nontemporal_store(v, p); }
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// p 8-byte aligned
+__device__ __forceinline__ void store_out2(float *p, float x, float y)
+{
+    const f32x2 v = {x, y};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x2 *>(p));
+}
+
+// p 16-byte aligned
+__device__ __forceinline__ void store_out4(float *p, float x, float y, float z, float w)
+{
+    const f32x4 v = {x, y, z, w};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+}
+
+// Loads of an input that the kernel reads exactly once, at unit stride across
+// the lanes of a wave: the nontemporal hint keeps these lines from displacing
+// others in L2 (measured on the log-space backward at B=128, T=64, d=64:
+// 4.1 -> 3.9 us).  Not for loads that read a line piecewise over several
+// instructions (the block kernels' column loads), which the hint slows down.
+__device__ __forceinline__ float load_once(const float *p) { return __builtin_nontemporal_load(p); }
+
 __device__ __forceinline__ uint64_t tagged_load(const uint64_t *p)
 {
     return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

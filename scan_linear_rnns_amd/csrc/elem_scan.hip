@@ -385,7 +385,7 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int t = t0 + i;
-        if (cv && t < a.T) a.h[base + static_cast<int64_t>(t) * a.d] = Alg::out(pA[i], pH[i], cq);
+        if (cv && t < a.T) store_out(&a.h[base + static_cast<int64_t>(t) * a.d], Alg::out(pA[i], pH[i], cq));
     }
 }
 
@@ -427,9 +427,9 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
     for (int i = 0; i < C; ++i) {
         const int t = t0 + i;
         const int64_t off = base + static_cast<int64_t>(t < a.T ? t : a.T - 1) * a.d;
-        r1[i] = a.la[off];
-        r2[i] = a.lb[off];
-        gv[i] = a.dh[off];
+        r1[i] = load_once(&a.la[off]);
+        r2[i] = load_once(&a.lb[off]);
+        gv[i] = load_once(&a.dh[off]);
     }
     const float lh0v = a.lh0[cc];
     float cin_f = 0.0f;   // the forward writes a carry for every tile, the first included
@@ -557,11 +557,11 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
             const int64_t off = base + static_cast<int64_t>(t) * a.d;
             float d1, d2;
             Alg::grads(r1[i], r2[i], av[i], bv[i], g, hprev, d1, d2);
-            a.dla[off] = d1;
-            a.dlb[off] = d2;
+            store_out(&a.dla[off], d1);
+            store_out(&a.dlb[off], d2);
         }
     }
-    if (cv && j == 0 && q == 0) a.dlh0[chain] = Alg::grad_h0(wc, hin, lh0v);   // from a_1 g_1
+    if (cv && j == 0 && q == 0) store_out(&a.dlh0[chain], Alg::grad_h0(wc, hin, lh0v));   // from a_1 g_1
 }
 
 // ------------------------------------------------------------ host side
