@@ -1344,7 +1344,7 @@ __device__ __forceinline__ void affine_fwd_body(const BlkArgs &a)
         for (int i = 0; i < C; ++i) {
             const int t = clampT(tl.t0 + i, a.T);
             Rw::load_row(a.A + tl.ablk0 + t * tl.astep, tl.v, Ar[i]);
-            bv[i] = a.x[tl.vec0 + t * tl.vstep];
+            bv[i] = load_once(&a.x[tl.vec0 + t * tl.vstep]);
         }
     } else {
         float4 th[C];
@@ -1354,7 +1354,7 @@ __device__ __forceinline__ void affine_fwd_body(const BlkArgs &a)
             const int t = clampT(tl.t0 + i, a.T);
             th[i] = load_angles(a, tl, t);
             sv[i] = a.sg[tl.blk0 + static_cast<int64_t>(t) * a.nb];
-            bv[i] = a.x[tl.vec0 + t * tl.vstep];
+            bv[i] = load_once(&a.x[tl.vec0 + t * tl.vstep]);
         }
 #pragma unroll
         for (int i = 0; i < C; ++i) {
@@ -1433,8 +1433,8 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
     for (int i = 0; i < C; ++i) {
         const int t = clampT(tl.t0 + i, a.T);
         Rw::load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
-        gv[i] = a.y[tl.vec0 + t * tl.vstep];
-        hp[i] = a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep];
+        gv[i] = load_once(&a.y[tl.vec0 + t * tl.vstep]);
+        hp[i] = load_once(&a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep]);
     }
     const float xh0 = load_h0<K>(a, tl);
 #pragma unroll
@@ -1514,8 +1514,8 @@ __global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
         const int t = clampT(tl.t0 + i, a.T);
         th[i] = load_angles(a, tl, t);
         sig[i] = a.sg[tl.blk0 + static_cast<int64_t>(t) * a.nb];
-        gv[i] = a.y[tl.vec0 + t * tl.vstep];
-        hp[i] = a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep];
+        gv[i] = load_once(&a.y[tl.vec0 + t * tl.vstep]);
+        hp[i] = load_once(&a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep]);
     }
     const float xh0 = load_h0<8>(a, tl);
 #pragma unroll

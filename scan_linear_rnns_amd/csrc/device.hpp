@@ -61,9 +61,11 @@ __device__ __forceinline__ void store_out4(float *p, float x, float y, float z, 
 
 // Loads of an input that the kernel reads exactly once, at unit stride across
 // the lanes of a wave: the nontemporal hint keeps these lines from displacing
-// others in L2 (measured on the log-space backward at B=128, T=64, d=64:
-// 4.1 -> 3.9 us).  Not for loads that read a line piecewise over several
-// instructions (the block kernels' column loads), which the hint slows down.
+// others in L2.  Measured: log-space backward at B=128, T=64, d=64
+// 4.1 -> 3.9 us; the block-affine pair's vector inputs (b, h, dh) at k = 8
+// 16.0 -> 15.4 us (lab shape) and 40.2 -> 38.6 us (B=16, T=1024).  Not for
+// loads that read a line piecewise over several instructions (the block
+// kernels' matrix rows and columns), which the hint slows down.
 __device__ __forceinline__ float load_once(const float *p) { return __builtin_nontemporal_load(p); }
 
 __device__ __forceinline__ uint64_t tagged_load(const uint64_t *p)
