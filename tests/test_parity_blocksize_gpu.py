@@ -88,13 +88,15 @@ def test_blocksize_matrix_bwd_without_forward_state(gpu, k, B, T, d):
     assert torch.equal(dA_fresh, dA_reuse)
 
 
-@pytest.mark.parametrize("k", [2, 4, 16])
-def test_blocksize_rotation_only_long_T(gpu, k):
-    """Pure rotations (no gate): P stays orthogonal over 1024 steps.  Held to the
+@pytest.mark.parametrize("k,T", [(2, 1024), (4, 1024), (16, 1024), (4, 2000)])
+def test_blocksize_rotation_only_long_T(gpu, k, T):
+    """Pure rotations (no gate): P stays orthogonal over T steps.  Held to the
     normwise bar of the k = 8 rotation-only test (entries near zero carry the
-    rounding of O(1) partial results, see there)."""
-    say(f"block k={k} rotation-only T=1024")
-    out, ref = run_block_k(2, 1024, 32, k, 9, gpu, gate=False, h0="normal")
+    rounding of O(1) partial results, see there).  k = 16 at T = 1024 and
+    k = 4 at T = 2000 have more tiles along T than waves per workgroup, so the
+    look-back also composes far tiles."""
+    say(f"block k={k} rotation-only T={T}")
+    out, ref = run_block_k(2, T, 32, k, 9, gpu, gate=False, h0="normal")
     for key in out:
         x, r = out[key].astype(np.float64), ref[key]
         assert np.all(np.isfinite(x))

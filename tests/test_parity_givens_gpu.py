@@ -67,6 +67,23 @@ def test_givens_saturated_gates_and_wide_angles(gpu):
     check(*run_givens(theta, s, b, h0, dh, gpu))
 
 
+def test_givens_long_T_without_decay(gpu):
+    """Gates saturated at 1 (s = 30) so nothing decays over T = 2000 steps (16
+    tiles along T): every carry, the far tiles' included, shows in the later
+    outputs.  h is a random walk there, so h and the gradients are held to the
+    normwise bar of the rotation-only block tests."""
+    say("givens no-decay T=2000")
+    theta, s, b, h0, dh = _inp(2, 2000, 16, 8, h0="normal")
+    s = np.full_like(s, 30.0)
+    out, ref = run_givens(theta, s, b, h0, dh, gpu)
+    for key in out:
+        x, r = out[key].astype(np.float64), ref[key]
+        assert np.all(np.isfinite(x)), key
+        if key == "ds":
+            continue   # sigma'(30) ~ 1e-13 lies below fp32 resolution next to sigma = 1: not comparable here
+        assert np.max(np.abs(x - r)) / np.max(np.abs(r)) <= 2e-5, key
+
+
 def test_givens_matches_block_affine_on_formed_matrices(gpu):
     """The fused op and the block-affine op on A = sigmoid(s) R(theta) (formed on the host)
     agree on h, db, dh0 -- two GPU paths, one input."""

@@ -225,10 +225,16 @@ def test_matrix_bwd_without_forward_state(gpu, B, T, d):
     assert torch.equal(dA_fresh, dA_reuse)
 
 
-def test_rotation_only_long_T(gpu):
-    """Pure rotations keep P orthogonal, so the long-T product does not decay."""
-    say("block rotation-only T=1024")
-    out, ref = run_block(4, 1024, 64, 9, gpu, gate=False, h0="normal")
+@pytest.mark.parametrize("B,T", [(4, 1024), (2, 2000)])
+def test_rotation_only_long_T(gpu, B, T):
+    """Pure rotations keep P orthogonal, so the long-T product does not decay.
+    T = 2000 gives 16 tiles along T, more than the eight waves of a
+    workgroup: the look-back then composes tiles farther back than the
+    aggregates the idle waves fetch, in batches of which the last is partial
+    (seven far tiles, batches of four).  Without decay a skipped or repeated
+    tile would show in every later output."""
+    say(f"block rotation-only B={B} T={T}")
+    out, ref = run_block(B, T, 64, 9, gpu, gate=False, h0="normal")
     # Without the gate nothing contracts: h is a random walk (|h| ~ 50 at
     # T = 1024) and P is a product of 1024 rotations, so entries near zero
     # carry the rounding of O(1)..O(50) partial results.  A plain sequential
