@@ -181,7 +181,7 @@ class OpRun:
         torch.cuda.synchronize()
 
 
-def graph_time(run: OpRun, which: str, steps: int, warmup: int, repeats: int = 3):
+def graph_time(run: OpRun, which: str, steps: int, warmup: int, repeats: int = 5):
     """Median over `repeats` of (elapsed / steps) in microseconds for a graph of
     `steps` consecutive calls (cycling the buffer sets), after `warmup` calls."""
     import torch
@@ -277,7 +277,7 @@ def cold_copy_floor(dev, nbytes, steps, warmup):
     g.replay()
     torch.cuda.synchronize()
     times = []
-    for _ in range(3):
+    for _ in range(5):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         g.replay()
@@ -287,7 +287,7 @@ def cold_copy_floor(dev, nbytes, steps, warmup):
     times.sort()
     del g, src, dst
     torch.cuda.empty_cache()
-    return times[1]
+    return times[len(times) // 2]
 
 
 def cpu_baseline(seconds):
