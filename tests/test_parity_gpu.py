@@ -107,6 +107,33 @@ def test_log_edges(gpu, B, T, d):
         assert e <= LOG_TOL, (key, e)
 
 
+def test_log_no_decay_long_T(gpu):
+    """a = 1 exactly (log a = 0) over T = 2000 steps, 16 tiles along T: h_t = h_0 +
+    sum of b, so every tile's carry shows in every later output, and the
+    look-back walks past more tiles than one batch of its loads covers.  h is
+    positive and held to the floored bar; the gradients contain g_t, a reverse
+    running sum of signed dh (a random walk whose small entries carry the
+    rounding of large partial sums, as in the undamped linear-scan test), so
+    they are held to the normwise bar of 2e-5."""
+    import scan_linear_rnns_amd as mgs
+    say("log no-decay B=2 T=2000 d=16")
+    rng = np.random.default_rng(21)
+    B, T, d = 2, 2000, 16
+    la = np.zeros((B, T, d), np.float32)
+    lb = np.log(rng.uniform(0.5, 1.5, (B, T, d))).astype(np.float32)
+    lh0 = np.log(rng.uniform(0.5, 1.5, (B, d))).astype(np.float32)
+    dh = rng.standard_normal((B, T, d)).astype(np.float32)
+    t = [to_dev(x, gpu) for x in (la, lb, lh0, dh)]
+    h, ws = mgs.mgs_scan_log_fwd(t[0], t[1], t[2])
+    g = mgs.mgs_scan_log_bwd(t[0], t[1], t[2], t[3], ws=ws, fwd_state_valid=True)
+    ws_clean(ws)
+    assert floored_err(to_np(h), oracle.log_fwd(la, lb, lh0)) <= LOG_TOL
+    for x, r in zip(g, oracle.log_bwd(la, lb, lh0, dh)):
+        x = to_np(x).astype(np.float64)
+        assert np.all(np.isfinite(x))
+        assert np.max(np.abs(x - r)) / np.max(np.abs(r)) <= 2e-5
+
+
 @pytest.mark.parametrize("T", [64, 1024])
 def test_log_bwd_without_forward_state(gpu, T):
     say(f"log bwd recompute-carries T={T}")

@@ -111,16 +111,19 @@ def test_linear_undamped_gates(gpu):
         assert floored_err(x[..., damped], r[..., damped]) <= LIN_TOL, key
 
 
-def test_linear_gates_around_one(gpu):
-    """|a| on both sides of 1, either sign, across 8 tiles: no contraction hides a carry error.
+@pytest.mark.parametrize("T", [1024, 2000])
+def test_linear_gates_around_one(gpu, T):
+    """|a| on both sides of 1, either sign, across 8 (T = 1024) or 16 (T = 2000)
+    tiles: no contraction hides a carry error, and at T = 2000 the look-back walks
+    past more tiles than one batch of its loads covers.
 
     Nothing decays, so (as for a = +-1) small entries carry the rounding of large
     partial results: on this input a plain sequential fp32 loop scores 3.0e-4
     (h) and 2.5e-4 (db) under the floored rule but <= 1.7e-6 normwise.  Held to
     a normwise bar of 2e-5."""
-    say("linear |a| ~ 1")
+    say(f"linear |a| ~ 1, T={T}")
     rng = np.random.default_rng(10)
-    B, T, d = 2, 1024, 16
+    B, d = 2, 16
     a = (rng.choice([-1.0, 1.0], (B, T, d)) * rng.uniform(0.99, 1.01, (B, T, d))).astype(np.float32)
     b = rng.standard_normal((B, T, d)).astype(np.float32)
     h0 = rng.standard_normal((B, d)).astype(np.float32)
