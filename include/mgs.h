@@ -48,15 +48,22 @@
  *   workspace must not run concurrently.
  *
  * Errors.  Arguments are validated before any HIP call:
- *   MGS_ERR_INVALID_VALUE  NULL required pointer, size <= 0, d % k != 0,
- *                          misaligned pointer, or output aliasing an input;
+ *   MGS_ERR_INVALID_VALUE  NULL required pointer, negative size, k <= 0,
+ *                          d % k != 0, misaligned pointer, or output aliasing
+ *                          an input;
  *   MGS_ERR_UNSUPPORTED    outside the envelope (block ops: k not in
- *                          {1, 2, 4, 8, 16}; Givens scan: k != 8; or a tensor
- *                          with 2^31 or more elements); never a silent
- *                          fallback to another path;
+ *                          {1, 2, 4, 8, 16}; Givens scan: k != 8; delta rule:
+ *                          d != 64; or a tensor with 2^31 or more elements --
+ *                          sizes are bounded one by one and their products are
+ *                          overflow-checked, so no combination of sizes wraps
+ *                          around); never a silent fallback to another path;
  *   MGS_ERR_WORKSPACE      workspace NULL or smaller than the query says;
  *   MGS_ERR_HIP            a HIP launch error; mgs_last_hip_error() gives the
  *                          hipError_t (per calling thread).
+ * Empty tensors.  A size of 0 is valid: the call computes nothing and
+ *   returns MGS_OK, except that a backward with T == 0 (and B*d > 0) writes
+ *   zeros to the gradient of the initial state (the loss does not depend on
+ *   it).  Pointers to empty tensors may be NULL.
  * Non-finite inputs propagate; log_b = -inf (b = 0) and log_h0 = -inf
  * (h_0 = 0) are supported exactly by the log-space scan.
  */

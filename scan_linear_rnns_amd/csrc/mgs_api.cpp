@@ -7,6 +7,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 
 #include "device.hpp"
 #include "launch.hpp"
@@ -57,9 +58,31 @@ bool all_aligned(const Range *r, int n)
     return true;
 }
 
-mgs_status check_sizes(int64_t B, int64_t T, int64_t d)
+// Product of non-negative tensor dimensions, or -1 when a dimension or the
+// product exceeds kMaxElems.  Each factor is bounded before it is multiplied
+// and the multiplications are overflow-checked, so caller-supplied sizes can
+// never wrap around to a small (or zero) element count.
+int64_t bounded_product(std::initializer_list<int64_t> dims)
+{
+    int64_t n = 1;
+    for (int64_t x : dims)
+        if (x > kMaxElems) return -1;
+    for (int64_t x : dims)
+        if (__builtin_mul_overflow(n, x, &n) || n > kMaxElems) return -1;
+    return n;
+}
+
+// Element counts of the (B,T,d) and (B,d) tensors of an elementwise op.
+struct ElemSizes {
+    int64_t n, s;
+};
+
+mgs_status check_sizes(int64_t B, int64_t T, int64_t d, ElemSizes *out)
 {
     if (B < 0 || T < 0 || d < 0) return MGS_ERR_INVALID_VALUE;
+    const int64_t n = bounded_product({B, T, d}), s = bounded_product({B, d});
+    if (n < 0 || s < 0) return MGS_ERR_UNSUPPORTED;
+    *out = ElemSizes{n, s};
     return MGS_OK;
 }
 
@@ -122,9 +145,9 @@ using ElemBwd = hipError_t (*)(const mgs::LogGeom &, const float *, const float 
 static mgs_status elem_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes)
 {
     if (!bytes) return MGS_ERR_INVALID_VALUE;
-    if (mgs_status st = check_sizes(B, T, d)) return st;
-    if (B * T * d > kMaxElems || B * d > kMaxElems) return MGS_ERR_UNSUPPORTED;
-    if (B == 0 || T == 0 || d == 0) { *bytes = sizeof(mgs::WsHeader); return MGS_OK; }
+    ElemSizes z;
+    if (mgs_status st = check_sizes(B, T, d, &z)) return st;
+    if (z.n == 0) { *bytes = sizeof(mgs::WsHeader); return MGS_OK; }
     *bytes = mgs::log_geometry(B, T, d).bytes;
     return MGS_OK;
 }
@@ -133,9 +156,9 @@ static mgs_status elem_fwd(ElemFwd launch, const float *x1, const float *x2, con
                            int64_t B, int64_t T, int64_t d, void *workspace, size_t workspace_bytes,
                            void *stream)
 {
-    if (mgs_status st = check_sizes(B, T, d)) return st;
-    if (B * T * d > kMaxElems || B * d > kMaxElems) return MGS_ERR_UNSUPPORTED;
-    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
+    ElemSizes z;
+    if (mgs_status st = check_sizes(B, T, d, &z)) return st;
+    const size_t n = static_cast<size_t>(z.n) * 4, s0 = static_cast<size_t>(z.s) * 4;
     if (n > 0 && (!x1 || !x2 || !h)) return MGS_ERR_INVALID_VALUE;
     if (s0 > 0 && !x0) return MGS_ERR_INVALID_VALUE;
     const Range in[] = {{x1, n}, {x2, n}, {x0, s0}};
@@ -153,9 +176,9 @@ static mgs_status elem_bwd(ElemFwd launch_f, ElemBwd launch_b, const float *x1, 
                            int64_t B, int64_t T, int64_t d, void *workspace, size_t workspace_bytes,
                            int fwd_state_valid, void *stream)
 {
-    if (mgs_status st = check_sizes(B, T, d)) return st;
-    if (B * T * d > kMaxElems || B * d > kMaxElems) return MGS_ERR_UNSUPPORTED;
-    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
+    ElemSizes z;
+    if (mgs_status st = check_sizes(B, T, d, &z)) return st;
+    const size_t n = static_cast<size_t>(z.n) * 4, s0 = static_cast<size_t>(z.s) * 4;
     if (n > 0 && (!x1 || !x2 || !dh || !d1 || !d2)) return MGS_ERR_INVALID_VALUE;
     if (s0 > 0 && (!x0 || !d0)) return MGS_ERR_INVALID_VALUE;
     const Range in[] = {{x1, n}, {x2, n}, {x0, s0}, {dh, n}};
@@ -165,7 +188,7 @@ static mgs_status elem_bwd(ElemFwd launch_f, ElemBwd launch_b, const float *x1, 
     if (s0 == 0) return MGS_OK;
     hipStream_t s = as_stream(stream);
     if (T == 0)  // L does not depend on h0 when there are no steps
-        return hip_status(mgs::launch_fill_zero(d0, B * d, s));
+        return hip_status(mgs::launch_fill_zero(d0, z.s, s));
     const mgs::LogGeom g = mgs::log_geometry(B, T, d);
     if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
     if (g.nT > 1 && !fwd_state_valid) {
@@ -241,19 +264,29 @@ mgs_status mgs_scan_linear_bwd(const float *a, const float *b, const float *h0, 
 
 // ---------------------------------------------------------- block scans
 
-static mgs_status check_block_sizes(int64_t B, int64_t T, int64_t d, int64_t k)
+// Element counts of a block op's tensors: n of (B,T,d), s of (B,d), na of
+// (B,T,d/k,k,k); for the Givens scan nth of the angles (B,T,d/k,k(k-1)/2) and
+// ns of the gates (B,T,d/k).  na bounds the others, so none can overflow.
+struct BlockSizes {
+    int64_t n, s, na, nth, ns;
+};
+
+static mgs_status check_block_sizes(int64_t B, int64_t T, int64_t d, int64_t k, BlockSizes *out)
 {
     if (B < 0 || T < 0 || d < 0 || k <= 0) return MGS_ERR_INVALID_VALUE;
     if (d % k != 0) return MGS_ERR_INVALID_VALUE;
     if (!mgs::block_k_supported(k)) return MGS_ERR_UNSUPPORTED;
-    if (B * T * d * k > kMaxElems) return MGS_ERR_UNSUPPORTED;
+    const int64_t na = bounded_product({B, T, d, k});
+    if (na < 0) return MGS_ERR_UNSUPPORTED;
+    const int64_t n = B * T * d, nbt = B * T * (d / k);
+    *out = BlockSizes{n, B * d, na, nbt * (k * (k - 1) / 2), nbt};
     return MGS_OK;
 }
 
 // The Givens angle-fused scan is built for 8 x 8 blocks (28 angles) only.
-static mgs_status check_givens_sizes(int64_t B, int64_t T, int64_t d, int64_t k)
+static mgs_status check_givens_sizes(int64_t B, int64_t T, int64_t d, int64_t k, BlockSizes *out)
 {
-    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
+    if (mgs_status st = check_block_sizes(B, T, d, k, out)) return st;
     return k == 8 ? MGS_OK : MGS_ERR_UNSUPPORTED;
 }
 
@@ -261,8 +294,9 @@ mgs_status mgs_block_affine_scan_workspace_size(int64_t B, int64_t T, int64_t d,
                                                 size_t *bytes)
 {
     if (!bytes) return MGS_ERR_INVALID_VALUE;
-    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
-    if (B == 0 || T == 0 || d == 0) { *bytes = sizeof(mgs::WsHeader); return MGS_OK; }
+    BlockSizes z;
+    if (mgs_status st = check_block_sizes(B, T, d, k, &z)) return st;
+    if (z.n == 0) { *bytes = sizeof(mgs::WsHeader); return MGS_OK; }
     *bytes = mgs::block_affine_geometry(B, T, d, k).bytes;
     return MGS_OK;
 }
@@ -271,9 +305,10 @@ mgs_status mgs_block_affine_scan_fwd(const float *A, const float *b, const float
                                      int64_t B, int64_t T, int64_t d, int64_t k, void *workspace,
                                      size_t workspace_bytes, void *stream)
 {
-    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
-    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
-    const size_t na = n * static_cast<size_t>(k);
+    BlockSizes z;
+    if (mgs_status st = check_block_sizes(B, T, d, k, &z)) return st;
+    const size_t n = static_cast<size_t>(z.n) * 4, s0 = static_cast<size_t>(z.s) * 4;
+    const size_t na = static_cast<size_t>(z.na) * 4;
     if (n > 0 && (!A || !b || !h)) return MGS_ERR_INVALID_VALUE;
     const Range in[] = {{A, na}, {b, n}, {h0, s0}};
     const Range out[] = {{h, n}};
@@ -291,9 +326,10 @@ mgs_status mgs_block_affine_scan_bwd(const float *A, const float *b, const float
                                      float *dh0, int64_t B, int64_t T, int64_t d, int64_t k,
                                      void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
-    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
-    const size_t na = n * static_cast<size_t>(k);
+    BlockSizes z;
+    if (mgs_status st = check_block_sizes(B, T, d, k, &z)) return st;
+    const size_t n = static_cast<size_t>(z.n) * 4, s0 = static_cast<size_t>(z.s) * 4;
+    const size_t na = static_cast<size_t>(z.na) * 4;
     if (n > 0 && (!A || !h || !dh || !dA || !db)) return MGS_ERR_INVALID_VALUE;
     if (s0 > 0 && !dh0) return MGS_ERR_INVALID_VALUE;
     const Range in[] = {{A, na}, {b, n}, {h0, s0}, {h, n}, {dh, n}};
@@ -302,24 +338,17 @@ mgs_status mgs_block_affine_scan_bwd(const float *A, const float *b, const float
     if (any_alias(in, 5, out, 3)) return MGS_ERR_INVALID_VALUE;
     if (s0 == 0) return MGS_OK;
     hipStream_t s = as_stream(stream);
-    if (T == 0) return hip_status(mgs::launch_fill_zero(dh0, B * d, s));
+    if (T == 0) return hip_status(mgs::launch_fill_zero(dh0, z.s, s));
     const mgs::BlockGeom g = mgs::block_affine_geometry(B, T, d, k);
     if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
     return hip_status(mgs::launch_block_affine_bwd(g, A, h0, h, dh, dA, db, dh0, workspace, s));
 }
 
-// Givens angle-fused: theta (B,T,nb,28), s (B,T,nb); sizes in bytes
-static void givens_bytes(int64_t B, int64_t T, int64_t d, int64_t k, size_t &nth, size_t &ns)
-{
-    const int64_t nb = d / k;
-    nth = static_cast<size_t>(B * T * nb * (k * (k - 1) / 2)) * 4;
-    ns = static_cast<size_t>(B * T * nb) * 4;
-}
-
 mgs_status mgs_givens_scan_workspace_size(int64_t B, int64_t T, int64_t d, int64_t k, size_t *bytes)
 {
     if (!bytes) return MGS_ERR_INVALID_VALUE;
-    if (mgs_status st = check_givens_sizes(B, T, d, k)) return st;
+    BlockSizes z;
+    if (mgs_status st = check_givens_sizes(B, T, d, k, &z)) return st;
     return mgs_block_affine_scan_workspace_size(B, T, d, k, bytes);
 }
 
@@ -327,10 +356,10 @@ mgs_status mgs_givens_scan_fwd(const float *theta, const float *s, const float *
                                float *h, int64_t B, int64_t T, int64_t d, int64_t k, void *workspace,
                                size_t workspace_bytes, void *stream)
 {
-    if (mgs_status st = check_givens_sizes(B, T, d, k)) return st;
-    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
-    size_t nth, ns;
-    givens_bytes(B, T, d, k, nth, ns);
+    BlockSizes z;
+    if (mgs_status st = check_givens_sizes(B, T, d, k, &z)) return st;
+    const size_t n = static_cast<size_t>(z.n) * 4, s0 = static_cast<size_t>(z.s) * 4;
+    const size_t nth = static_cast<size_t>(z.nth) * 4, ns = static_cast<size_t>(z.ns) * 4;
     if (n > 0 && (!theta || !s || !b || !h)) return MGS_ERR_INVALID_VALUE;
     const Range in[] = {{theta, nth}, {s, ns}, {b, n}, {h0, s0}};
     const Range out[] = {{h, n}};
@@ -347,10 +376,10 @@ mgs_status mgs_givens_scan_bwd(const float *theta, const float *s, const float *
                                int64_t B, int64_t T, int64_t d, int64_t k, void *workspace,
                                size_t workspace_bytes, void *stream)
 {
-    if (mgs_status st = check_givens_sizes(B, T, d, k)) return st;
-    const size_t n = static_cast<size_t>(B * T * d) * 4, s0 = static_cast<size_t>(B * d) * 4;
-    size_t nth, ns;
-    givens_bytes(B, T, d, k, nth, ns);
+    BlockSizes z;
+    if (mgs_status st = check_givens_sizes(B, T, d, k, &z)) return st;
+    const size_t n = static_cast<size_t>(z.n) * 4, s0 = static_cast<size_t>(z.s) * 4;
+    const size_t nth = static_cast<size_t>(z.nth) * 4, ns = static_cast<size_t>(z.ns) * 4;
     if (n > 0 && (!theta || !s || !h || !dh || !dtheta || !ds || !db)) return MGS_ERR_INVALID_VALUE;
     if (s0 > 0 && !dh0) return MGS_ERR_INVALID_VALUE;
     const Range in[] = {{theta, nth}, {s, ns}, {h0, s0}, {h, n}, {dh, n}};
@@ -359,7 +388,7 @@ mgs_status mgs_givens_scan_bwd(const float *theta, const float *s, const float *
     if (any_alias(in, 5, out, 4)) return MGS_ERR_INVALID_VALUE;
     if (s0 == 0) return MGS_OK;
     hipStream_t st = as_stream(stream);
-    if (T == 0) return hip_status(mgs::launch_fill_zero(dh0, B * d, st));
+    if (T == 0) return hip_status(mgs::launch_fill_zero(dh0, z.s, st));
     const mgs::BlockGeom g = mgs::block_affine_geometry(B, T, d, k);
     if (mgs_status e = check_workspace(workspace, workspace_bytes, g.bytes)) return e;
     return hip_status(mgs::launch_givens_bwd(g, theta, s, h0, h, dh, dtheta, ds, db, dh0, workspace, st));
@@ -369,8 +398,9 @@ mgs_status mgs_block_matrix_scan_workspace_size(int64_t B, int64_t T, int64_t d,
                                                 size_t *bytes)
 {
     if (!bytes) return MGS_ERR_INVALID_VALUE;
-    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
-    if (B == 0 || T == 0 || d == 0) { *bytes = sizeof(mgs::WsHeader); return MGS_OK; }
+    BlockSizes z;
+    if (mgs_status st = check_block_sizes(B, T, d, k, &z)) return st;
+    if (z.n == 0) { *bytes = sizeof(mgs::WsHeader); return MGS_OK; }
     *bytes = mgs::block_matrix_geometry(B, T, d, k).bytes;
     return MGS_OK;
 }
@@ -379,8 +409,9 @@ mgs_status mgs_block_matrix_scan_fwd(const float *A, float *P, int64_t B, int64_
                                      int64_t k, void *workspace, size_t workspace_bytes,
                                      void *stream)
 {
-    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
-    const size_t na = static_cast<size_t>(B * T * d * k) * 4;
+    BlockSizes z;
+    if (mgs_status st = check_block_sizes(B, T, d, k, &z)) return st;
+    const size_t na = static_cast<size_t>(z.na) * 4;
     if (na > 0 && (!A || !P)) return MGS_ERR_INVALID_VALUE;
     const Range in[] = {{A, na}};
     const Range out[] = {{P, na}};
@@ -396,8 +427,9 @@ mgs_status mgs_block_matrix_scan_bwd(const float *A, const float *dP, float *dA,
                                      int64_t d, int64_t k, void *workspace, size_t workspace_bytes,
                                      int fwd_state_valid, void *stream)
 {
-    if (mgs_status st = check_block_sizes(B, T, d, k)) return st;
-    const size_t na = static_cast<size_t>(B * T * d * k) * 4;
+    BlockSizes z;
+    if (mgs_status st = check_block_sizes(B, T, d, k, &z)) return st;
+    const size_t na = static_cast<size_t>(z.na) * 4;
     if (na > 0 && (!A || !dP || !dA)) return MGS_ERR_INVALID_VALUE;
     const Range in[] = {{A, na}, {dP, na}};
     const Range out[] = {{dA, na}};
@@ -412,18 +444,27 @@ mgs_status mgs_block_matrix_scan_bwd(const float *A, const float *dP, float *dA,
 
 // ------------------------------------------------------------ delta rule
 
-static mgs_status check_delta_sizes(int64_t B, int64_t T, int64_t d)
+// Element counts of the delta rule's tensors: n of (B,T,d), nb of (B,T),
+// ns of (B,d,d).
+struct DeltaSizes {
+    int64_t n, nb, ns;
+};
+
+static mgs_status check_delta_sizes(int64_t B, int64_t T, int64_t d, DeltaSizes *out)
 {
     if (B < 0 || T < 0 || d <= 0) return MGS_ERR_INVALID_VALUE;
     if (d != 64) return MGS_ERR_UNSUPPORTED;
-    if (B * T * d > kMaxElems || B * d * d > kMaxElems) return MGS_ERR_UNSUPPORTED;
+    const int64_t n = bounded_product({B, T, d}), ns = bounded_product({B, d, d});
+    if (n < 0 || ns < 0) return MGS_ERR_UNSUPPORTED;
+    *out = DeltaSizes{n, B * T, ns};
     return MGS_OK;
 }
 
 mgs_status mgs_delta_workspace_size(int64_t B, int64_t T, int64_t d, size_t *bytes)
 {
     if (!bytes) return MGS_ERR_INVALID_VALUE;
-    if (mgs_status st = check_delta_sizes(B, T, d)) return st;
+    DeltaSizes z;
+    if (mgs_status st = check_delta_sizes(B, T, d, &z)) return st;
     *bytes = mgs::delta_geometry(B, T, d).bytes;
     return MGS_OK;
 }
@@ -432,9 +473,10 @@ mgs_status mgs_delta_fwd(const float *q, const float *k, const float *v, const f
                          const float *S0, float *o, float *ST, int64_t B, int64_t T, int64_t d,
                          void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (mgs_status st = check_delta_sizes(B, T, d)) return st;
-    const size_t n = static_cast<size_t>(B * T * d) * 4, nb = static_cast<size_t>(B * T) * 4;
-    const size_t ns = static_cast<size_t>(B * d * d) * 4;
+    DeltaSizes z;
+    if (mgs_status st = check_delta_sizes(B, T, d, &z)) return st;
+    const size_t n = static_cast<size_t>(z.n) * 4, nb = static_cast<size_t>(z.nb) * 4;
+    const size_t ns = static_cast<size_t>(z.ns) * 4;
     if (n > 0 && (!q || !k || !v || !beta || !o)) return MGS_ERR_INVALID_VALUE;
     const Range in[] = {{q, n}, {k, n}, {v, n}, {beta, nb}, {S0, ns}};
     const Range out[] = {{o, n}, {ST, ns}};

@@ -186,3 +186,65 @@ def test_delta_validation(lib):
     assert fwd(ws=None) == WORKSPACE
     assert fwd(nbytes=1024) == WORKSPACE
     assert fwd(T=0, ST=None) == OK                          # nothing to do, no HIP call
+
+
+# Sizes whose products overflow int64 (or wrap to 0): each must be refused as out of
+# envelope before any HIP call, never accepted as an empty no-op.
+OVERFLOWING_ELEM = [(1, 1 << 40, 1 << 24),          # B*T*d = 2^64: wraps to exactly 0
+                    (1 << 21, 1 << 21, 1 << 22),     # 2^64 again, spread over the three sizes
+                    (3, (1 << 62) // 3 + 1, 4),      # signed overflow of a product
+                    (1, 1 << 31, 1),                 # one dimension past the envelope
+                    (1 << 16, 1 << 16, 1)]           # 2^32 elements, no int64 overflow
+
+
+@pytest.mark.parametrize("B,T,d", OVERFLOWING_ELEM)
+@pytest.mark.parametrize("op", ["log", "linear", "mingru"])
+def test_elementwise_overflowing_sizes(lib, op, B, T, d):
+    assert _size(lib, f"mgs_scan_{op}_workspace_size", B, T, d)[0] == UNSUPPORTED
+    fwd = getattr(lib, f"mgs_scan_{op}_fwd")
+    assert fwd(fake(0), fake(1), fake(2), fake(3), B, T, d, fake(9), 1 << 20, None) == UNSUPPORTED
+    bwd = getattr(lib, f"mgs_scan_{op}_bwd")
+    assert bwd(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), B, T, d, fake(9), 1 << 20, 1,
+               None) == UNSUPPORTED
+
+
+OVERFLOWING_BLOCK = [(1, 1 << 40, 1 << 24, 8),      # B*T*d*k = 2^67; B*T*d alone wraps to 0
+                     (1, 1 << 37, 1 << 24, 8),      # B*T*d*k = 2^64: wraps to exactly 0
+                     (1 << 20, 1 << 20, 1 << 24, 16),
+                     (1, 1 << 28, 64, 8)]           # 2^37 elements of A, no int64 overflow
+
+
+@pytest.mark.parametrize("B,T,d,k", OVERFLOWING_BLOCK)
+def test_block_overflowing_sizes(lib, B, T, d, k):
+    for fn in ("mgs_block_affine_scan_workspace_size", "mgs_block_matrix_scan_workspace_size"):
+        assert _size(lib, fn, B, T, d, k)[0] == UNSUPPORTED
+    assert lib.mgs_block_affine_scan_fwd(fake(0), fake(1), None, fake(3), B, T, d, k, fake(9), 1 << 20,
+                                         None) == UNSUPPORTED
+    assert lib.mgs_block_affine_scan_bwd(fake(0), None, None, fake(3), fake(4), fake(5), fake(6), fake(7),
+                                         B, T, d, k, fake(9), 1 << 20, None) == UNSUPPORTED
+    assert lib.mgs_block_matrix_scan_fwd(fake(0), fake(1), B, T, d, k, fake(9), 1 << 20, None) == UNSUPPORTED
+    assert lib.mgs_block_matrix_scan_bwd(fake(0), fake(1), fake(2), B, T, d, k, fake(9), 1 << 20, 1,
+                                         None) == UNSUPPORTED
+    if k == 8:
+        assert _size(lib, "mgs_givens_scan_workspace_size", B, T, d, k)[0] == UNSUPPORTED
+        assert lib.mgs_givens_scan_fwd(fake(0), fake(1), fake(2), None, fake(3), B, T, d, k, fake(9), 1 << 20,
+                                       None) == UNSUPPORTED
+        assert lib.mgs_givens_scan_bwd(fake(0), fake(1), None, fake(3), fake(4), fake(5), fake(6), fake(7),
+                                       fake(8), B, T, d, k, fake(9), 1 << 20, None) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("B,T", [(1, 1 << 58), (1 << 52, 1 << 10), (1 << 20, 1 << 20), (1 << 20, 0)])
+def test_delta_overflowing_sizes(lib, B, T):
+    # (B,T,64) or the (B,64,64) state past 2^31 elements, with and without int64 wrap-around
+    assert _size(lib, "mgs_delta_workspace_size", B, T, 64)[0] == UNSUPPORTED
+    assert lib.mgs_delta_fwd(fake(0), fake(1), fake(2), fake(3), None, fake(5), fake(6), B, T, 64, fake(9),
+                             1 << 24, None) == UNSUPPORTED
+
+
+def test_empty_tensors_are_valid(lib):
+    # a size of 0 is an empty tensor (documented): nothing to compute, no HIP call
+    assert _size(lib, "mgs_scan_log_workspace_size", 0, 1 << 40, 16) == (UNSUPPORTED, 0)
+    assert _size(lib, "mgs_scan_log_workspace_size", 0, 64, 16) == (OK, 256)
+    assert _size(lib, "mgs_block_affine_scan_workspace_size", 4, 0, 64, 8) == (OK, 256)
+    assert lib.mgs_block_affine_scan_fwd(None, None, None, None, 4, 0, 64, 8, None, 0, None) == OK
+    assert lib.mgs_block_matrix_scan_fwd(None, None, 0, 16, 64, 8, None, 0, None) == OK
