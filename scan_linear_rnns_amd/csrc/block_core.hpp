@@ -1203,10 +1203,211 @@ __device__ __forceinline__ float4 load_angles(const BlkArgs &a, const Tile &tl, 
 
 // ============================================ block-affine carry phases
 // Shared by the kernels that load A and the kernels that form it from angles.
+//
+// A tile's NCH chunk aggregates (M, v) -- the chunk's transfer matrix row and
+// offset entry in each lane -- meet in a tree: node (l, i) composes chunks
+// [i 2^l, (i+1) 2^l), level 0 being the chunks themselves.  The forward
+// composes a later segment after an earlier one, (M2, v2) o (M1, v1) =
+// (M2 M1, M2 v1 + v2); the backward's reverse aggregates compose the other
+// way round.  The root is the tile aggregate, published for the look-back as
+// soon as it exists; once the state entering the tile is known, each chunk
+// reaches its own entering state by applying at most log2(NCH) tree nodes to
+// it (matrix-vector products only), so no matrix prefix is ever formed.
 
-// Forward: X = (row of Phi, entry of u) is the chunk's aggregate.  Stores it,
-// scans the tile's chunks, runs the look-back (multi-tile launches) and
-// returns the state entering this lane's chunk.
+template <int NCH>
+__device__ __forceinline__ constexpr int tree_node(int l, int i)   // level l starts after 2 NCH - 2 NCH / 2^l nodes
+{
+    return 2 * NCH - ((2 * NCH) >> l) + i;
+}
+
+template <int NCH>
+__host__ __device__ constexpr int tree_levels()
+{
+    int l = 0;
+    while ((1 << l) < NCH) ++l;
+    return l;
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations: tagged
+// stores of the look-back stay in flight across it (a __syncthreads() would
+// wait for their acknowledgement from memory).  Only LDS carries data between
+// the waves here.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Builds the tree of the tile's chunk aggregates in `nodes` (X holds chunk
+// tl.q's aggregate on entry) and leaves the root in X of wave 0 (both
+// halves).  DIR = +1: forward composition; DIR = -1: reverse.  Nodes of the
+// root's level are not stored.  Ends with every stored node visible to the
+// whole workgroup except the root.
+template <int K, int NCH, int DIR>
+__device__ __forceinline__ void tree_build(float (*nodes)[32][(AggShape<kMatVec, K>::stride)], const Tile &tl,
+                                           float (&X)[K + 1])
+{
+    constexpr int AW = K + 1;
+    constexpr int L = tree_levels<NCH>();
+#pragma unroll
+    for (int e = 0; e < AW; ++e) nodes[tree_node<NCH>(0, tl.q)][tl.slot][e] = X[e];
+    // level 1 inside each wave: its halves hold chunks 2w and 2w + 1 (lanes l
+    // and l ^ 32 serve the same row of the same chain)
+    {
+        const bool own_outer = DIR > 0 ? tl.sub == 1 : tl.sub == 0;   // the factor applied last
+        float Y[AW], R[AW];
+#pragma unroll
+        for (int e = 0; e < AW; ++e) {
+            const float p = __shfl_xor(X[e], 32);
+            Y[e] = own_outer ? X[e] : p;
+            R[e] = own_outer ? p : X[e];
+        }
+        compose_into<kMatVec, K>(Y, R);
+#pragma unroll
+        for (int e = 0; e < AW; ++e) X[e] = Y[e];
+        if (L > 1 && tl.sub == 0)
+#pragma unroll
+            for (int e = 0; e < AW; ++e) nodes[tree_node<NCH>(1, tl.wv)][tl.slot][e] = X[e];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int l = 2; l <= L; ++l) {
+        if (tl.wv < (NCH >> l)) {
+            const float *lo = nodes[tree_node<NCH>(l - 1, 2 * tl.wv)][tl.slot];
+            const float *hi = nodes[tree_node<NCH>(l - 1, 2 * tl.wv + 1)][tl.slot];
+            float R[AW];
+#pragma unroll
+            for (int e = 0; e < AW; ++e) {
+                X[e] = DIR > 0 ? hi[e] : lo[e];
+                R[e] = DIR > 0 ? lo[e] : hi[e];
+            }
+            compose_into<kMatVec, K>(X, R);
+            if (l < L && tl.sub == 0)
+#pragma unroll
+                for (int e = 0; e < AW; ++e) nodes[tree_node<NCH>(l, tl.wv)][tl.slot][e] = X[e];
+        }
+        if (l < L) lds_barrier();
+    }
+}
+
+// State entering chunk tl.q from the state c entering the tile: the nodes
+// covering chunks [0, q) in order (forward), or [q + 1, NCH) from the end
+// (reverse).
+template <int K, int NCH, int DIR>
+__device__ __forceinline__ float tree_apply(float (*nodes)[32][(AggShape<kMatVec, K>::stride)], const Tile &tl,
+                                            float c)
+{
+    using Rw = Rows<K>;
+    constexpr int L = tree_levels<NCH>();
+    const int r = DIR > 0 ? tl.q : NCH - 1 - tl.q;   // chunks to cover
+    int at = DIR > 0 ? 0 : NCH;                        // forward: next start; reverse: current end
+#pragma unroll
+    for (int l = L - 1; l >= 0; --l) {
+        if ((r >> l) & 1) {
+            const int i = DIR > 0 ? (at >> l) : ((at >> l) - 1);
+            const float *nd = nodes[tree_node<NCH>(l, i)][tl.slot];
+            c = Rw::mv(nd, c, nd[K]);
+            at += DIR * (1 << l);
+        }
+    }
+    return c;
+}
+
+// Aggregate words in the workspace are word-major per tile ([tile][word][slot]),
+// so a word of all 32 slots is 256 contiguous bytes for a tile's loads and stores.
+template <int AW>
+__device__ __forceinline__ void publish_wm(uint64_t *dst, int tile, int slot, uint32_t tag, const float *x)
+{
+    uint64_t *p = dst + static_cast<size_t>(tile) * AW * 32 + slot;
+#pragma unroll
+    for (int e = 0; e < AW; ++e) tagged_store(p + e * 32, tag, x[e]);
+}
+
+// Look-back of a tile whose tree is built (X: the tile aggregate in wave 0).
+// Each half-wave of waves 1 .. W-1 polls one predecessor (the nearest 2(W-1)
+// tiles in the scan direction: earlier tiles for DIR = +1, later ones for
+// DIR = -1) for its inclusive state and its aggregate in one batch of loads and
+// stages what it finds in LDS; wave 0 then walks from the nearest predecessor:
+// it stops at the first published inclusive state (or past the end of the
+// sequence, whose state base0 is known) and applies the aggregates of the
+// tiles passed on the way.  A tile that shows neither, or a window without an
+// inclusive state that does not reach the end of the sequence, means another
+// round.  Returns the state entering the tile (every lane, its slot);
+// publishes the tile's inclusive state.
+template <int K, int W, int DIR>
+__device__ __forceinline__ float affine_lookback(const BlkArgs &a, const Tile &tl, int ftile, uint32_t tag,
+                                                 const float (&X)[K + 1], float base0, bool publish_incl)
+{
+    using Rw = Rows<K>;
+    constexpr int AW = K + 1;
+    constexpr int NU = 2 * (W - 1);
+    constexpr int SW = (AW + 1) | 1;
+    static_assert(NU > 0, "the look-back needs more than one wave");
+    __shared__ float sLB[NU][32][SW];
+    __shared__ int sStat[NU];
+    __shared__ float sCar[32];
+    __shared__ int sDone;
+    float c = base0;
+    for (uint32_t spin = 0;; ++spin) {
+        if (tl.wv > 0) {
+            const int u = 2 * (tl.wv - 1) + tl.sub;
+            const int p = tl.j - DIR * (1 + u);
+            const bool in = p >= 0 && p < a.nT;
+            const size_t ti = static_cast<size_t>(in ? p : tl.j) * a.nCG + tl.cg;
+            const uint64_t wi = tagged_load(a.incl + ti * 32 + tl.slot);
+            uint64_t wa[AW];
+#pragma unroll
+            for (int e = 0; e < AW; ++e) wa[e] = tagged_load(a.agg + (ti * AW + e) * 32 + tl.slot);
+            bool okA = true;
+#pragma unroll
+            for (int e = 0; e < AW; ++e) okA = okA && tag_is(wa[e], tag);
+            const uint32_t hA = static_cast<uint32_t>(__ballot(okA) >> (32 * tl.sub));
+            const uint32_t hI = static_cast<uint32_t>(__ballot(tag_is(wi, tag)) >> (32 * tl.sub));
+#pragma unroll
+            for (int e = 0; e < AW; ++e) sLB[u][tl.slot][e] = tag_value(wa[e]);
+            sLB[u][tl.slot][AW] = tag_value(wi);
+            if (tl.slot == 0) sStat[u] = in ? ((hA == 0xFFFFFFFFu ? 1 : 0) | (hI == 0xFFFFFFFFu ? 2 : 0)) : 4;
+        }
+        lds_barrier();
+        if (tl.wv == 0) {
+            // nearest first: 4 = past the end of the sequence, 2 = inclusive, 1 = aggregate
+            int stop = -1;
+            bool ok = true;
+            for (int u = 0; u < NU; ++u) {
+                const int st = sStat[u];
+                if (st & 6) { stop = u; break; }
+                if (!(st & 1)) { ok = false; break; }
+            }
+            ok = ok && stop >= 0;
+            if (ok) {
+                c = (sStat[stop] & 4) ? base0 : sLB[stop][tl.slot][AW];
+                for (int u = stop - 1; u >= 0; --u) c = Rw::mv(sLB[u][tl.slot], c, sLB[u][tl.slot][K]);
+                if (tl.sub == 0) sCar[tl.slot] = c;
+            }
+            if (tl.lane == 0) sDone = ok ? 1 : 0;
+        }
+        lds_barrier();
+        if (sDone) break;
+        if (spin >= kSpinLimit) {
+            if (threadIdx.x == 0) raise_error(&a.hd->err, kErrSpin);
+            if (tl.wv == 0 && tl.sub == 0) sCar[tl.slot] = base0;
+            lds_barrier();
+            break;
+        }
+        backoff();
+    }
+    if (tl.wv == 0) {
+        if (publish_incl && tl.sub == 0) {
+            const float xo = Rw::mv(X, c, X[K]);
+            tagged_store(a.incl + static_cast<size_t>(ftile) * 32 + tl.slot, tag, xo);
+        }
+        return c;
+    }
+    return sCar[tl.slot];
+}
+
+// Forward: X = (row of Phi, entry of u) is the chunk's aggregate.  Builds the
+// tile's tree, runs the look-back (multi-tile launches) and returns the state
+// entering this lane's chunk.
 template <int K, int C, int W, bool MULTI>
 __device__ __forceinline__ float affine_fwd_carry(const BlkArgs &a, const Tile &tl, int ftile, unsigned long long ep,
                                                   float (&X)[K + 1], float xh0,
@@ -1216,52 +1417,26 @@ __device__ __forceinline__ float affine_fwd_carry(const BlkArgs &a, const Tile &
     constexpr int NCH = 2 * W;
     using S = AggShape<kMatVec, K>;
     using Rw = Rows<K>;
-    constexpr int FIN = ks_final<NCH>();
-    ks_store<kMatVec, K, NCH>(sKS[0], tl.q, tl.slot, X);
-    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
-    __syncthreads();
-    const uint32_t tag = sTicket[0];
-
-    float x;
     if constexpr (MULTI) {
-        ks_scan<kMatVec, K, NCH, +1>(sKS, tl.q, tl.slot, X);
-        // the last wave's upper half holds the tile aggregate and runs the look-back
-        if (tl.wv == W - 1) {
-            const bool owner = tl.sub == 1;
-            if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<S::words>(a.agg, ftile, tl.slot, tag, X);
-            float xin = xh0;
-            if (tl.j > 0) {
-                float xi[1];
-                const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, tag, &a.hd->err, xi);
-                if (ps >= 0) xin = xi[0];
-                // aggregates per batch of loads: six (k <= 8), so that with eight tiles
-                // along T every tile needs at most one batch after the inclusive
-                // (measured at B=16, T=1024: forward 17.8 -> 17.2 us); the backward's
-                // helper keeps four, as six would spill in the Givens backward
-                constexpr int NB = K >= 16 ? 2 : 6;
-                for (int p = ps + 1; p < tl.j; p += NB) {
-                    const int cnt = min(NB, tl.j - p);
-                    float ag[NB][S::words];
-                    load_aggregates<S::words, NB>(a.agg, p, +1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
-#pragma unroll
-                    for (int u = 0; u < NB; ++u)
-                        if (u < cnt) xin = Rw::mv(ag[u], xin, ag[u][K]);
-                }
-            }
-            if (owner && tl.j < a.nT - 1) {
-                const float xo = Rw::mv(X, xin, X[K]);
-                publish<1>(a.incl, ftile, tl.slot, tag, &xo);
-            }
-            if (owner) sCarry[tl.slot] = xin;
+        float (*nodes)[32][S::stride] = reinterpret_cast<float (*)[32][S::stride]>(&sKS[0][0][0][0]);
+        if (threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
+        tree_build<K, NCH, +1>(nodes, tl, X);   // its first barrier also shares the tag
+        const uint32_t tag = sTicket[0];
+        if (tl.wv == 0 && tl.sub == 0 && tl.j < a.nT - 1) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
+        float c = xh0;
+        if (tl.j > 0) c = affine_lookback<K, W, +1>(a, tl, ftile, tag, X, xh0, tl.j < a.nT - 1);
+        else if (tl.wv == 0 && tl.sub == 0 && a.nT > 1) {
+            const float xo = Rw::mv(X, xh0, X[K]);
+            tagged_store(a.incl + static_cast<size_t>(ftile) * 32 + tl.slot, tag, xo);
         }
-        __syncthreads();
-        x = sCarry[tl.slot];
-        if (tl.q > 0) x = Rw::mv(sKS[FIN][tl.q - 1][tl.slot], x, sKS[FIN][tl.q - 1][tl.slot][K]);
+        return tree_apply<K, NCH, +1>(nodes, tl, c);
     } else {
-        x = xh0;
+        ks_store<kMatVec, K, NCH>(sKS[0], tl.q, tl.slot, X);
+        __syncthreads();
+        float x = xh0;
         for (int q = 0; q < tl.q; ++q) x = Rw::mv(sKS[0][q][tl.slot], x, sKS[0][q][tl.slot][K]);
+        return x;
     }
-    return x;
 }
 
 // Backward: X = (row of Psi, entry of Wl) is the chunk's reverse aggregate.
@@ -1275,49 +1450,24 @@ __device__ __forceinline__ float affine_bwd_carry(const BlkArgs &a, const Tile &
     constexpr int NCH = 2 * W;
     using S = AggShape<kMatVec, K>;
     using Rw = Rows<K>;
-    constexpr int FIN = ks_final<NCH>();
-    ks_store<kMatVec, K, NCH>(sKS[0], tl.q, tl.slot, X);
-    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
-    __syncthreads();
-    const uint32_t tag = sTicket[0];
-
-    float w;
     if constexpr (MULTI) {
-        ks_scan<kMatVec, K, NCH, -1>(sKS, tl.q, tl.slot, X);
-        // wave 0's lower half holds the tile aggregate and runs the look-back
-        if (tl.wv == 0) {
-            const bool owner = tl.sub == 0;
-            if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<S::words>(a.agg, ftile, tl.slot, tag, X);
-            float win = 0.0f;
-            if (tl.j < a.nT - 1) {
-                float xi[1];
-                const int ps = find_inclusive<1>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, tag, &a.hd->err, xi);
-                int pend = a.nT;
-                if (ps >= 0) { win = xi[0]; pend = ps; }
-                constexpr int NB = K >= 16 ? 2 : 4;
-                for (int p = pend - 1; p > tl.j; p -= NB) {
-                    const int cnt = min(NB, p - tl.j);
-                    float ag[NB][S::words];
-                    load_aggregates<S::words, NB>(a.agg, p, -1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
-#pragma unroll
-                    for (int u = 0; u < NB; ++u)
-                        if (u < cnt) win = Rw::mv(ag[u], win, ag[u][K]);
-                }
-            }
-            if (owner && tl.j > 0) {
-                const float wo = Rw::mv(X, win, X[K]);
-                publish<1>(a.incl, ftile, tl.slot, tag, &wo);
-            }
-            if (owner) sCarry[tl.slot] = win;
-        }
-        __syncthreads();
-        w = sCarry[tl.slot];
-        if (tl.q < NCH - 1) w = Rw::mv(sKS[FIN][tl.q + 1][tl.slot], w, sKS[FIN][tl.q + 1][tl.slot][K]);
+        float (*nodes)[32][S::stride] = reinterpret_cast<float (*)[32][S::stride]>(&sKS[0][0][0][0]);
+        if (threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
+        tree_build<K, NCH, -1>(nodes, tl, X);
+        const uint32_t tag = sTicket[0];
+        if (tl.wv == 0 && tl.sub == 0 && tl.j > 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
+        float w = 0.0f;
+        if (tl.j < a.nT - 1) w = affine_lookback<K, W, -1>(a, tl, ftile, tag, X, 0.0f, tl.j > 0);
+        else if (tl.wv == 0 && tl.sub == 0 && a.nT > 1)
+            tagged_store(a.incl + static_cast<size_t>(ftile) * 32 + tl.slot, tag, X[K]);   // Psi 0 + Wl
+        return tree_apply<K, NCH, -1>(nodes, tl, w);
     } else {
-        w = 0.0f;
+        ks_store<kMatVec, K, NCH>(sKS[0], tl.q, tl.slot, X);
+        __syncthreads();
+        float w = 0.0f;
         for (int q = NCH - 1; q > tl.q; --q) w = Rw::mv(sKS[0][q][tl.slot], w, sKS[0][q][tl.slot][K]);
+        return w;
     }
-    return w;
 }
 
 // ======================================================= block-affine fwd

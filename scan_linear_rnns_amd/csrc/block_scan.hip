@@ -16,8 +16,11 @@ __global__ void fill_zero_kernel(float *p, int64_t n)
     if (i < n) p[i] = 0.0f;
 }
 
+// zeros_bytes: size of the zero region that stands in for an absent h0 (at
+// least B*d floats; a caller that shares one workspace between shapes passes a
+// fixed capacity, so the region never moves onto words another shape wrote).
 BlockGeom make_geom(int64_t B, int64_t T, int64_t d, int64_t k, int agg_words, int incl_words,
-                    BlkShape shape, bool pstate)
+                    BlkShape shape, bool pstate, size_t zeros_bytes = 0)
 {
     BlockGeom g{};
     g.T = static_cast<int>(T);
@@ -39,7 +42,8 @@ BlockGeom make_geom(int64_t B, int64_t T, int64_t d, int64_t k, int agg_words, i
     g.incl_words = incl_words;
     size_t off = sizeof(WsHeader);
     g.off_zeros = off;   // B*d floats, never written: the h0 of calls that pass none
-    off = align256(off + static_cast<size_t>(B) * d * 4);
+    const size_t zb = static_cast<size_t>(B) * d * 4;
+    off = align256(off + (zeros_bytes > zb ? zeros_bytes : zb));
     g.off_pstate = off;  // cumulative product: one k x k state per chain per chunk
     if (pstate) off = align256(off + static_cast<size_t>(g.nTiles) * nch * 32 * k * 4);
     if (g.nT > 1) {
@@ -125,6 +129,12 @@ bool block_k_supported(int64_t k)
 BlockGeom block_affine_geometry(int64_t B, int64_t T, int64_t d, int64_t k)
 {
     return make_geom(B, T, d, k, static_cast<int>(k) + 1, 1, affine_shape(static_cast<int>(k)), false);
+}
+
+BlockGeom block_affine_geometry_fixed_zeros(int64_t B, int64_t T, int64_t d, int64_t k, size_t zeros_bytes)
+{
+    return make_geom(B, T, d, k, static_cast<int>(k) + 1, 1, affine_shape(static_cast<int>(k)), false,
+                     zeros_bytes);
 }
 
 BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k)

@@ -69,6 +69,9 @@ bool block_k_supported(int64_t k);
 
 BlockGeom block_affine_geometry(int64_t B, int64_t T, int64_t d, int64_t k);
 BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k);
+// the block-affine layout with a zero region of at least zeros_bytes at a fixed
+// offset (for a workspace shared by calls of different shapes)
+BlockGeom block_affine_geometry_fixed_zeros(int64_t B, int64_t T, int64_t d, int64_t k, size_t zeros_bytes);
 
 hipError_t launch_block_affine_fwd(const BlockGeom &g, const float *A, const float *b,
                                    const float *h0, float *h, void *ws, hipStream_t s);
