@@ -65,3 +65,36 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     line = r.stdout.strip().splitlines()[-1]
     assert "one GPU only" in json.loads(line)["error"]
+
+
+@pytest.mark.parametrize("calls", [1, 5, 7, 20, 40, 43, 100, 200])
+@pytest.mark.parametrize("set_bytes", [80 << 20, 12 << 20, 33 << 20, 600 << 20, 50_000])
+def test_rotation_continues_across_replays(calls, set_bytes):
+    """Every timed replay has exactly `calls` calls, and over consecutive replays
+    (graph g holds calls g*K .. g*K+K-1, graphs replayed in turn) each buffer set
+    is reused only after >= 512 MiB of other sets, unless the set count is capped
+    for tiny workloads; every set is touched."""
+    M, G = bench.rotation_plan(calls, set_bytes)
+    seq = []
+    for r in range(3 * G + 2):
+        g = r % G
+        seq += [(g * calls + i) % M for i in range(calls)]
+    assert set(seq) == set(range(M))
+    last = {}
+    gaps = []
+    for pos, s in enumerate(seq):
+        if s in last:
+            gaps.append(pos - last[s])
+        last[s] = pos
+    want = min(bench.MAX_SETS, -(-bench.ROTATE_BYTES // set_bytes))
+    assert min(gaps) == M >= want
+    if M < bench.MAX_SETS:
+        assert M * set_bytes >= bench.ROTATE_BYTES
+
+
+def test_rotation_of_the_headline():
+    # block-affine long T: A, b, dh, h, dA, db, dh0 = 80 MiB + 4 KiB per set
+    set_bytes = (8 + 1 + 1 + 1 + 8 + 1) * 4 * 16 * 1024 * 64 + 4 * 16 * 64
+    assert bench.rotation_plan(20, set_bytes) == (10, 1)
+    assert bench.rotation_plan(40, set_bytes) == (8, 1)
+    assert bench.rotation_plan(5, set_bytes) == (10, 2)
