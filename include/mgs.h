@@ -214,6 +214,26 @@ mgs_status mgs_block_affine_scan_fwd(const float *A, const float *b, const float
                                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mgs_block_affine_scan_fwd for callers that cannot allocate device memory --
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation: the same computation and kernels, with no workspace argument.
+ * Its workspace is a 16 MiB array in the library's device code, one copy per
+ * GPU, zero-filled when that code is loaded and held until the process ends;
+ * the call itself allocates nothing (no hipMalloc, no allocating library call).
+ *   A, b, h0, h, B, T, d, k, stream : as for mgs_block_affine_scan_fwd.
+ * Limits: B*d <= 262144 and the shape's look-back words must fit the rest of
+ * the array (at k = 8 and B*d/8 = 128 chains, T up to 24448); larger shapes
+ * return MGS_ERR_UNSUPPORTED before any HIP call.  Every call on one GPU shares
+ * that GPU's array and keeps it ready for the next call, so nothing needs
+ * clearing between calls; calls that overlap in time on one GPU (on different
+ * streams, or from different threads) race on it and must not be issued.  The
+ * array's error word (a look-back wait that hit its spin limit) is not
+ * readable through this interface.
+ */
+mgs_status mgs_block_affine_scan_fwd_noalloc(const float *A, const float *b, const float *h0, float *h,
+                                             int64_t B, int64_t T, int64_t d, int64_t k, void *stream);
+
+/*
  * Backward of mgs_block_affine_scan_fwd for L = sum_t <dh_t, h_t>: the reverse
  * scan g_T = dh_T, g_t = dh_t + A_{t+1}^T g_{t+1}, with
  *     dA_t = g_t h_{t-1}^T (formed in registers, written once),  db_t = g_t,

@@ -267,6 +267,24 @@ def mgs_block_affine_scan_fwd(A, b, h0, k=8, h=None, ws=None, stream=None):
     return h, ws
 
 
+def mgs_block_affine_scan_fwd_noalloc(A, b, h0, k=8, h=None, stream=None):
+    """mgs_block_affine_scan_fwd without a workspace (the library's own device
+    scratch); returns h.  Pass a preallocated h to allocate nothing here either."""
+    import torch
+    B, T, d = _block_dims(A, k)
+    dev = A.device
+    _check_tensor("A", A, (B, T, d // k, k, k))
+    _check_tensor("b", b, (B, T, d), dev)
+    if h0 is not None:
+        _check_tensor("h0", h0, (B, d), dev)
+    if h is None:
+        h = torch.empty((B, T, d), dtype=torch.float32, device=dev)
+    _check_tensor("h", h, (B, T, d), dev)
+    check(load().mgs_block_affine_scan_fwd_noalloc(_ptr(A), _ptr(b), _ptr(h0), _ptr(h), B, T, d, k,
+                                                   _stream(stream)), "mgs_block_affine_scan_fwd_noalloc")
+    return h
+
+
 def mgs_block_affine_scan_bwd(A, b, h0, h, dh, k=8, ws=None, out=None, stream=None):
     """(dA, db, dh0) for L = sum(dh * h); h is the forward's output."""
     import torch

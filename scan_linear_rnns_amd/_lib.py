@@ -35,6 +35,7 @@ SIGNATURES = {
     "mgs_scan_linear_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _INT, _P], _INT),
     "mgs_block_affine_scan_workspace_size": ([_I64, _I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),
     "mgs_block_affine_scan_fwd": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P], _INT),
+    "mgs_block_affine_scan_fwd_noalloc": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "mgs_block_affine_scan_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P],
                                   _INT),
     "mgs_givens_scan_workspace_size": ([_I64, _I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),

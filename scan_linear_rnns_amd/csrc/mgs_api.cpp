@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 
 #include "device.hpp"
 #include "launch.hpp"
@@ -95,6 +96,45 @@ mgs_status check_workspace(const void *ws, size_t have, size_t need)
 }
 
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+// ------------------------------------------------ scratch of the no-allocation entry point
+// mgs_block_affine_scan_fwd_noalloc keeps its workspace in this file-scope
+// device array: one copy per GPU, at that GPU's own address, zero-filled when
+// the library's device code is loaded and held until the process ends.  Its
+// layout: the 256-byte header, a fixed zero region of kNoAllocZerosBytes (the
+// h0 of calls that pass none; never written, whatever the shape), then the
+// look-back words of the call's shape.  The kernels leave the header ready for
+// the next call (the launch counter returns to zero, epochs only grow), so
+// nothing is cleared per call; words left by an earlier call carry an older
+// launch tag and are never taken for the current call's.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+constexpr size_t kNoAllocZerosBytes = size_t(1) << 20;   // B*d <= 262144
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, set up on first use
+
+// Device address of the current device's `scratch`.  In host code the array's
+// name is only a host-side stand-in, so kernels receive this address instead.
+mgs_status noalloc_scratch(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return MGS_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return MGS_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MGS_OK;
+}
 
 }  // namespace
 
@@ -319,6 +359,27 @@ mgs_status mgs_block_affine_scan_fwd(const float *A, const float *b, const float
     if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
     return hip_status(mgs::launch_block_affine_fwd(g, A, b, h0, h, workspace,
                                                    as_stream(stream)));
+}
+
+mgs_status mgs_block_affine_scan_fwd_noalloc(const float *A, const float *b, const float *h0, float *h,
+                                             int64_t B, int64_t T, int64_t d, int64_t k, void *stream)
+{
+    BlockSizes z;
+    if (mgs_status st = check_block_sizes(B, T, d, k, &z)) return st;
+    const size_t n = static_cast<size_t>(z.n) * 4, s0 = static_cast<size_t>(z.s) * 4;
+    const size_t na = static_cast<size_t>(z.na) * 4;
+    if (n > 0 && (!A || !b || !h)) return MGS_ERR_INVALID_VALUE;
+    const Range in[] = {{A, na}, {b, n}, {h0, s0}};
+    const Range out[] = {{h, n}};
+    if (!all_aligned(in, 3) || !all_aligned(out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (any_alias(in, 3, out, 1)) return MGS_ERR_INVALID_VALUE;
+    if (n == 0) return MGS_OK;
+    if (s0 > kNoAllocZerosBytes) return MGS_ERR_UNSUPPORTED;
+    const mgs::BlockGeom g = mgs::block_affine_geometry_fixed_zeros(B, T, d, k, kNoAllocZerosBytes);
+    if (g.bytes > kNoAllocScratchBytes) return MGS_ERR_UNSUPPORTED;
+    void *ws = nullptr;
+    if (mgs_status st = noalloc_scratch(&ws)) return st;
+    return hip_status(mgs::launch_block_affine_fwd(g, A, b, h0, h, ws, as_stream(stream)));
 }
 
 mgs_status mgs_block_affine_scan_bwd(const float *A, const float *b, const float *h0,

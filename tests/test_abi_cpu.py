@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.declared_functions()
-    assert len(declared) == 24, declared
+    assert len(declared) == 25, declared
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -248,3 +248,22 @@ def test_empty_tensors_are_valid(lib):
     assert _size(lib, "mgs_block_affine_scan_workspace_size", 4, 0, 64, 8) == (OK, 256)
     assert lib.mgs_block_affine_scan_fwd(None, None, None, None, 4, 0, 64, 8, None, 0, None) == OK
     assert lib.mgs_block_matrix_scan_fwd(None, None, 0, 16, 64, 8, None, 0, None) == OK
+
+
+def test_noalloc_validation(lib):
+    """The entry point that allocates nothing validates like the forward it
+    mirrors and refuses shapes beyond its scratch before any HIP call."""
+    B, T, d, k = 2, 8, 16, 8
+    f = lambda A=fake(0), b=fake(1), h0=None, h=fake(3), B=B, T=T, d=d, k=k: \
+        lib.mgs_block_affine_scan_fwd_noalloc(A, b, h0, h, B, T, d, k, None)
+    assert f(A=None) == INVALID
+    assert f(h=None) == INVALID
+    assert f(h=fake(1)) == INVALID                 # output aliases b
+    assert f(b=fake(1, 4)) == INVALID              # misaligned
+    assert f(d=12) == INVALID                      # d % k != 0
+    assert f(k=3, d=12) == UNSUPPORTED
+    assert f(B=-1) == INVALID
+    assert f(T=0, A=None, b=None, h=None) == OK    # empty: nothing to do
+    assert f(B=1, T=1 << 40, d=1 << 24) == UNSUPPORTED   # overflowing sizes
+    assert f(B=4097, T=8, d=64) == UNSUPPORTED     # B*d past the scratch's zero region (262144)
+    assert f(B=16, T=1 << 16, d=64) == UNSUPPORTED  # look-back words past the scratch
