@@ -48,7 +48,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# MGS_ORACLE_LIBRARY: an already built copy of oracle.c to load instead (the
+# sanitizer test loads one built with address and undefined-behaviour checks)
+_LIB = os.environ.get("MGS_ORACLE_LIBRARY", os.path.join(_HERE, "liboracle.so"))
 _lock = threading.Lock()
 _lib = None
 
@@ -58,6 +60,8 @@ _I = ctypes.c_int64
 
 def build(force: bool = False) -> str:
     """Compile oracle.c with gcc (no fast-math; IEEE double arithmetic)."""
+    if "MGS_ORACLE_LIBRARY" in os.environ:
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c99",

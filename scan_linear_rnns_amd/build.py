@@ -17,6 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmgs.so")
+OBJ_DIR = os.path.join(HERE, "_build")   # object files of the last build (the sanitizer test links against them)
 # (source, object name, extra flags): block_scan_k.hip is built once per block
 # size it serves, each object holding that size's kernels only.
 SOURCES = [("mgs_api.cpp", "mgs_api", ()),
@@ -45,10 +46,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the MI355X library cannot be built")
 
 
+def compile_cmd(src: str, obj: str, extra=()) -> list:
+    return [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
+
+
 def _compile(src: str, obj: str, extra=()) -> None:
-    cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-           "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
-    subprocess.run(cmd, check=True)
+    subprocess.run(compile_cmd(src, obj, extra), check=True)
 
 
 def build(verbose: bool = False, save_temps_dir: str | None = None) -> str:
@@ -77,6 +81,10 @@ def build(verbose: bool = False, save_temps_dir: str | None = None) -> str:
         subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp, *objs],
                        check=True)
         os.replace(out_tmp, LIB)
+        if not save_temps_dir:
+            os.makedirs(OBJ_DIR, exist_ok=True)
+            for obj in objs:
+                shutil.copyfile(obj, os.path.join(OBJ_DIR, os.path.basename(obj)))
     return LIB
 
 

@@ -267,3 +267,4 @@ def test_noalloc_validation(lib):
     assert f(B=1, T=1 << 40, d=1 << 24) == UNSUPPORTED   # overflowing sizes
     assert f(B=4097, T=8, d=64) == UNSUPPORTED     # B*d past the scratch's zero region (262144)
     assert f(B=16, T=1 << 16, d=64) == UNSUPPORTED  # look-back words past the scratch
+    assert f(B=16, T=24449, d=64) == UNSUPPORTED     # just past the documented limit at 128 chains
