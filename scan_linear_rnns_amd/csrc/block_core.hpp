@@ -813,105 +813,6 @@ struct Rows<8> {
     static __device__ __forceinline__ void store_row(float *p, int v, const float *R) { store_row8(p, v, R); }
 };
 
-// ------------------------------------------------------------ look-back
-
-// All lanes of one wave take part; lanes 32..63 mirror lanes 0..31 (same slot).
-// Returns the nearest tile p (in the direction dir = -1: earlier tiles,
-// +1: later tiles) whose IW-word inclusive state is published, with the state
-// in xi; -1 if the spin limit was hit.  One batch of loads polls the first word
-// of up to WIN tiles at once; the remaining words of the chosen tile follow.
-template <int IW>
-__device__ __forceinline__ int find_inclusive(const uint64_t *incl, int j, int nT, int nCG, int cg, int slot,
-                              int dir, uint32_t tag, uint32_t *err, float *xi)
-{
-    constexpr int WIN = 16;
-    for (uint32_t spin = 0;; ++spin) {
-        for (int p0 = j + dir; p0 >= 0 && p0 < nT; p0 += dir * WIN) {
-            uint64_t w[WIN];
-#pragma unroll
-            for (int u = 0; u < WIN; ++u) {
-                const int p = p0 + dir * u;
-                const bool in = p >= 0 && p < nT;
-                w[u] = tagged_load(incl + ((static_cast<size_t>(in ? p : p0) * nCG + cg) * 32 + slot) * IW);
-            }
-#pragma unroll
-            for (int u = 0; u < WIN; ++u) {
-                const int p = p0 + dir * u;
-                if (p < 0 || p >= nT) break;
-                if (__all(tag_is(w[u], tag))) {
-                    const uint64_t *src = incl + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * IW;
-                    uint64_t r[IW];
-                    r[0] = w[u];
-#pragma unroll
-                    for (int e = 1; e < IW; ++e) r[e] = tagged_load(src + e);
-#pragma unroll
-                    for (int e = 1; e < IW; ++e) {
-                        for (uint32_t sp = 0; !tag_is(r[e], tag); ++sp) {
-                            if (sp >= kSpinLimit) {
-                                raise_error(err, kErrSpin);
-                                break;
-                            }
-                            backoff();
-                            r[e] = tagged_load(src + e);
-                        }
-                    }
-#pragma unroll
-                    for (int e = 0; e < IW; ++e) xi[e] = tag_value(r[e]);
-                    return p;
-                }
-            }
-        }
-        if (spin >= kSpinLimit) {
-            raise_error(err, kErrSpin);
-            return -1;
-        }
-        backoff();
-    }
-}
-
-// Loads the AW-word aggregates of `cnt` (<= NB) tiles p0, p0 + dir, ... for
-// this lane in one batch of loads, then waits for any word not yet published.
-template <int AW, int NB>
-__device__ __forceinline__ void load_aggregates(const uint64_t *agg, int p0, int dir, int cnt, int nCG,
-                                                int cg, int slot, uint32_t tag, uint32_t *err,
-                                                float (&out)[NB][AW])
-{
-    uint64_t w[NB][AW];
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-        const int p = p0 + dir * (u < cnt ? u : 0);
-        const uint64_t *src = agg + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * AW;
-#pragma unroll
-        for (int e = 0; e < AW; ++e) w[u][e] = tagged_load(src + e);
-    }
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-        if (u >= cnt) break;
-        const int p = p0 + dir * u;
-        const uint64_t *src = agg + ((static_cast<size_t>(p) * nCG + cg) * 32 + slot) * AW;
-#pragma unroll
-        for (int e = 0; e < AW; ++e) {
-            for (uint32_t spin = 0; !tag_is(w[u][e], tag); ++spin) {
-                if (spin >= kSpinLimit) {
-                    raise_error(err, kErrSpin);
-                    break;
-                }
-                backoff();
-                w[u][e] = tagged_load(src + e);
-            }
-            out[u][e] = tag_value(w[u][e]);
-        }
-    }
-}
-
-template <int AW>
-__device__ __forceinline__ void publish(uint64_t *dst, int tile, int slot, uint32_t tag, const float *x)
-{
-    uint64_t *p = dst + (static_cast<size_t>(tile) * 32 + slot) * AW;
-#pragma unroll
-    for (int e = 0; e < AW; ++e) tagged_store(p + e, tag, x[e]);
-}
-
 struct Tile {
     int lane, wv, v, cgl, sub, slot, q, j, cg, t0;
     bool cv;
@@ -965,17 +866,14 @@ __device__ __forceinline__ float load_h0(const BlkArgs &a, const Tile &tl)
     return a.h0[tl.bb * a.d + tl.jb * K + tl.v];
 }
 
-// ============================================ in-tile scan of chunk aggregates
-// Each half-wave holds the aggregate of one chunk q = 2 * wave + sub.  A
-// Kogge-Stone scan over the NCH chunks runs on all waves at once: in round r
-// every chunk composes its running composite with the one 2^r chunks before it
-// (DIR = +1) or after it (DIR = -1), read from one of two LDS buffers in turn,
-// with one barrier per round.  Afterwards chunk q holds the composite of
-// chunks 0..q (DIR = +1) or q..NCH-1 (DIR = -1), and a copy sits in buffer
-// ks_final<NCH>() for the fix-up.  The rule is the same in both directions:
+// ============================================ chunk aggregates
+// Each half-wave holds the aggregate of one chunk q = 2 * wave + sub: the
+// chunk's transfer matrix row and, for the block-affine scan (one value per
+// lane) and the cumulative-product backward (a matrix row), its offset.  Two
+// aggregates compose as
 //     (M, v) o (M', v') = (M M', M v' + v)
-// with v absent (cumulative product), one value per lane (block-affine) or a
-// matrix row (cumulative-product backward).
+// in either direction: (later o earlier) forward, (earlier o later) for the
+// reverse aggregates of the backward.
 
 enum AggKind : int { kMat = 0, kMatVec = 1, kMatMat = 2 };
 
@@ -984,14 +882,6 @@ struct AggShape {
     static constexpr int words = KIND == kMat ? K : (KIND == kMatVec ? K + 1 : 2 * K);
     static constexpr int stride = words | 1;   // odd LDS stride: lanes hit distinct banks
 };
-
-template <int NCH>
-__host__ __device__ constexpr int ks_final()
-{
-    int r = 0;
-    while ((1 << r) < NCH) ++r;
-    return r & 1;
-}
 
 template <int KIND, int K>
 __device__ __forceinline__ void compose_into(float *X, const float *R)
@@ -1015,28 +905,6 @@ __device__ __forceinline__ void ks_store(float (*buf)[32][(AggShape<KIND, K>::st
 {
 #pragma unroll
     for (int e = 0; e < AggShape<KIND, K>::words; ++e) buf[q][slot][e] = X[e];
-}
-
-// Precondition: buffer 0 holds every chunk's aggregate and a barrier has passed.
-template <int KIND, int K, int NCH, int DIR>
-__device__ __forceinline__ void ks_scan(float (*buf)[NCH][32][(AggShape<KIND, K>::stride)], int q, int slot, float *X)
-{
-    constexpr int AW = AggShape<KIND, K>::words;
-#pragma unroll
-    for (int r = 0; (1 << r) < NCH; ++r) {
-        if (r > 0) {
-            ks_store<KIND, K, NCH>(buf[r & 1], q, slot, X);
-            __syncthreads();
-        }
-        const int qn = q - DIR * (1 << r);
-        if (qn >= 0 && qn < NCH) {
-            float R[AW];
-#pragma unroll
-            for (int e = 0; e < AW; ++e) R[e] = buf[r & 1][qn][slot][e];
-            compose_into<KIND, K>(X, R);
-        }
-    }
-    ks_store<KIND, K, NCH>(buf[ks_final<NCH>()], q, slot, X);
 }
 
 // ===================================================== Givens mesh in lanes
@@ -1201,18 +1069,18 @@ __device__ __forceinline__ float4 load_angles(const BlkArgs &a, const Tile &tl, 
     return *reinterpret_cast<const float4 *>(a.theta + blk * kAngles + 4 * min(tl.v, 6));
 }
 
-// ============================================ block-affine carry phases
-// Shared by the kernels that load A and the kernels that form it from angles.
+// ====================================================== carry phases
+// Shared by every multi-chunk kernel of the block ops.
 //
-// A tile's NCH chunk aggregates (M, v) -- the chunk's transfer matrix row and
-// offset entry in each lane -- meet in a tree: node (l, i) composes chunks
-// [i 2^l, (i+1) 2^l), level 0 being the chunks themselves.  The forward
-// composes a later segment after an earlier one, (M2, v2) o (M1, v1) =
-// (M2 M1, M2 v1 + v2); the backward's reverse aggregates compose the other
-// way round.  The root is the tile aggregate, published for the look-back as
-// soon as it exists; once the state entering the tile is known, each chunk
-// reaches its own entering state by applying at most log2(NCH) tree nodes to
-// it (matrix-vector products only), so no matrix prefix is ever formed.
+// A tile's NCH chunk aggregates -- per lane, the chunk's transfer matrix row
+// and (block-affine, cumulative-product backward) its offset -- meet in a
+// tree: node (l, i) composes chunks [i 2^l, (i+1) 2^l), level 0 being the
+// chunks themselves.  The forward composes a later segment after an earlier
+// one, (M2, v2) o (M1, v1) = (M2 M1, M2 v1 + v2); the backward's reverse
+// aggregates compose the other way round.  The root is the tile aggregate,
+// published for the look-back as soon as it exists; once the state entering
+// the tile is known, each chunk reaches its own entering state by applying at
+// most log2(NCH) tree nodes to it, so no prefix of every chunk is ever formed.
 
 template <int NCH>
 __device__ __forceinline__ constexpr int tree_node(int l, int i)   // level l starts after 2 NCH - 2 NCH / 2^l nodes
@@ -1228,6 +1096,27 @@ __host__ __device__ constexpr int tree_levels()
     return l;
 }
 
+// The state a lane carries across chunks and tiles (CW words: the block-affine
+// scan's vector entry, or a row of the cumulative product's matrix state) and
+// how an aggregate (AW words at g) acts on it.
+template <int KIND, int K>
+struct Carry {
+    static constexpr int CW = KIND == kMatVec ? 1 : K;
+    static constexpr int AW = AggShape<KIND, K>::words;
+    static __device__ __forceinline__ void apply(const float *g, float *c)
+    {
+        using Rw = Rows<K>;
+        if constexpr (KIND == kMatVec) {
+            c[0] = Rw::mv(g, c[0], g[K]);
+        } else {
+            float np[K];
+            Rw::mm(g, c, np);
+#pragma unroll
+            for (int s = 0; s < K; ++s) c[s] = KIND == kMatMat ? np[s] + g[K + s] : np[s];
+        }
+    }
+};
+
 // Workgroup barrier that waits only for this wave's LDS operations: tagged
 // stores of the look-back stay in flight across it (a __syncthreads() would
 // wait for their acknowledgement from memory).  Only LDS carries data between
@@ -1239,14 +1128,14 @@ __device__ __forceinline__ void lds_barrier()
 
 // Builds the tree of the tile's chunk aggregates in `nodes` (X holds chunk
 // tl.q's aggregate on entry) and leaves the root in X of wave 0 (both
-// halves).  DIR = +1: forward composition; DIR = -1: reverse.  Nodes of the
-// root's level are not stored.  Ends with every stored node visible to the
-// whole workgroup except the root.
-template <int K, int NCH, int DIR>
-__device__ __forceinline__ void tree_build(float (*nodes)[32][(AggShape<kMatVec, K>::stride)], const Tile &tl,
-                                           float (&X)[K + 1])
+// halves) and in node (L, 0), written by wave 0's lower half and read only by
+// it.  DIR = +1: forward composition; DIR = -1: reverse.  Ends with every
+// other node visible to the whole workgroup.
+template <int KIND, int K, int NCH, int DIR>
+__device__ __forceinline__ void tree_build(float (*nodes)[32][(AggShape<KIND, K>::stride)], const Tile &tl,
+                                           float (&X)[AggShape<KIND, K>::words])
 {
-    constexpr int AW = K + 1;
+    constexpr int AW = AggShape<KIND, K>::words;
     constexpr int L = tree_levels<NCH>();
 #pragma unroll
     for (int e = 0; e < AW; ++e) nodes[tree_node<NCH>(0, tl.q)][tl.slot][e] = X[e];
@@ -1261,7 +1150,7 @@ __device__ __forceinline__ void tree_build(float (*nodes)[32][(AggShape<kMatVec,
             Y[e] = own_outer ? X[e] : p;
             R[e] = own_outer ? p : X[e];
         }
-        compose_into<kMatVec, K>(Y, R);
+        compose_into<KIND, K>(Y, R);
 #pragma unroll
         for (int e = 0; e < AW; ++e) X[e] = Y[e];
         if (L > 1 && tl.sub == 0)
@@ -1280,23 +1169,27 @@ __device__ __forceinline__ void tree_build(float (*nodes)[32][(AggShape<kMatVec,
                 X[e] = DIR > 0 ? hi[e] : lo[e];
                 R[e] = DIR > 0 ? lo[e] : hi[e];
             }
-            compose_into<kMatVec, K>(X, R);
+            compose_into<KIND, K>(X, R);
             if (l < L && tl.sub == 0)
 #pragma unroll
                 for (int e = 0; e < AW; ++e) nodes[tree_node<NCH>(l, tl.wv)][tl.slot][e] = X[e];
         }
         if (l < L) lds_barrier();
     }
+    // the root, for wave 0 alone (publishing the tile's inclusive state later),
+    // so that no wave keeps it in registers across the look-back
+    if (tl.wv == 0 && tl.sub == 0)
+#pragma unroll
+        for (int e = 0; e < AW; ++e) nodes[tree_node<NCH>(L, 0)][tl.slot][e] = X[e];
 }
 
 // State entering chunk tl.q from the state c entering the tile: the nodes
 // covering chunks [0, q) in order (forward), or [q + 1, NCH) from the end
 // (reverse).
-template <int K, int NCH, int DIR>
-__device__ __forceinline__ float tree_apply(float (*nodes)[32][(AggShape<kMatVec, K>::stride)], const Tile &tl,
-                                            float c)
+template <int KIND, int K, int NCH, int DIR>
+__device__ __forceinline__ void tree_apply(float (*nodes)[32][(AggShape<KIND, K>::stride)], const Tile &tl,
+                                           float *c)
 {
-    using Rw = Rows<K>;
     constexpr int L = tree_levels<NCH>();
     const int r = DIR > 0 ? tl.q : NCH - 1 - tl.q;   // chunks to cover
     int at = DIR > 0 ? 0 : NCH;                        // forward: next start; reverse: current end
@@ -1304,68 +1197,84 @@ __device__ __forceinline__ float tree_apply(float (*nodes)[32][(AggShape<kMatVec
     for (int l = L - 1; l >= 0; --l) {
         if ((r >> l) & 1) {
             const int i = DIR > 0 ? (at >> l) : ((at >> l) - 1);
-            const float *nd = nodes[tree_node<NCH>(l, i)][tl.slot];
-            c = Rw::mv(nd, c, nd[K]);
+            Carry<KIND, K>::apply(nodes[tree_node<NCH>(l, i)][tl.slot], c);
             at += DIR * (1 << l);
         }
     }
-    return c;
 }
 
-// Aggregate words in the workspace are word-major per tile ([tile][word][slot]),
+// Look-back words in the workspace are word-major per tile ([tile][word][slot]),
 // so a word of all 32 slots is 256 contiguous bytes for a tile's loads and stores.
-template <int AW>
+template <int NW>
 __device__ __forceinline__ void publish_wm(uint64_t *dst, int tile, int slot, uint32_t tag, const float *x)
 {
-    uint64_t *p = dst + static_cast<size_t>(tile) * AW * 32 + slot;
+    uint64_t *p = dst + static_cast<size_t>(tile) * NW * 32 + slot;
 #pragma unroll
-    for (int e = 0; e < AW; ++e) tagged_store(p + e * 32, tag, x[e]);
+    for (int e = 0; e < NW; ++e) tagged_store(p + e * 32, tag, x[e]);
 }
 
-// Look-back of a tile whose tree is built (X: the tile aggregate in wave 0).
-// Each half-wave of waves 1 .. W-1 polls one predecessor (the nearest 2(W-1)
-// tiles in the scan direction: earlier tiles for DIR = +1, later ones for
-// DIR = -1) for its inclusive state and its aggregate in one batch of loads and
-// stages what it finds in LDS; wave 0 then walks from the nearest predecessor:
-// it stops at the first published inclusive state (or past the end of the
-// sequence, whose state base0 is known) and applies the aggregates of the
-// tiles passed on the way.  A tile that shows neither, or a window without an
-// inclusive state that does not reach the end of the sequence, means another
-// round.  Returns the state entering the tile (every lane, its slot);
-// publishes the tile's inclusive state.
-template <int K, int W, int DIR>
-__device__ __forceinline__ float affine_lookback(const BlkArgs &a, const Tile &tl, int ftile, uint32_t tag,
-                                                 const float (&X)[K + 1], float base0, bool publish_incl)
+// Look-back of a tile whose tree is built (X: the tile aggregate, read by
+// wave 0's lower half alone, from LDS).
+// Polling units -- half-waves of waves 1 .. W-1 when a tile's CW + AW words
+// are few, else whole waves whose halves split the words -- each poll one
+// predecessor (the nearest units in the scan direction: earlier tiles for
+// DIR = +1, later ones for DIR = -1) for its inclusive state and its
+// aggregate in one batch of loads, and stage what they find in LDS.  Wave 0
+// then walks from the nearest predecessor: it stops at the first published
+// inclusive state (or past the end of the sequence, whose state base0 is
+// known) and applies the aggregates of the tiles passed on the way.  A tile
+// that shows neither, or a window without an inclusive state that does not
+// reach the end of the sequence, means another round.  `overlap` runs once on
+// every wave while the first round's loads are in flight (wave 0: after the
+// walk).  Leaves the state entering the tile in c (every lane, its slot) and
+// publishes the tile's inclusive state when publish_incl.
+template <int KIND, int K, int W, int DIR, typename F>
+__device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl, int ftile, uint32_t tag,
+                                               const float *X, const float *base0, bool publish_incl,
+                                               float *c, F &&overlap)
 {
-    using Rw = Rows<K>;
-    constexpr int AW = K + 1;
-    constexpr int NU = 2 * (W - 1);
-    constexpr int SW = (AW + 1) | 1;
+    using Cr = Carry<KIND, K>;
+    constexpr int CW = Cr::CW, AW = Cr::AW, NWD = CW + AW;
+    constexpr bool HALF = NWD <= 12;
+    constexpr int NU = HALF ? 2 * (W - 1) : W - 1;
+    constexpr int PER = HALF ? NWD : (NWD + 1) / 2;   // words one lane loads
+    constexpr int SW = NWD | 1;
     static_assert(NU > 0, "the look-back needs more than one wave");
     __shared__ float sLB[NU][32][SW];
     __shared__ int sStat[NU];
-    __shared__ float sCar[32];
+    __shared__ float sCar[32][CW];
     __shared__ int sDone;
-    float c = base0;
+#pragma unroll
+    for (int e = 0; e < CW; ++e) c[e] = base0[e];
     for (uint32_t spin = 0;; ++spin) {
         if (tl.wv > 0) {
-            const int u = 2 * (tl.wv - 1) + tl.sub;
+            const int u = HALF ? 2 * (tl.wv - 1) + tl.sub : tl.wv - 1;
             const int p = tl.j - DIR * (1 + u);
             const bool in = p >= 0 && p < a.nT;
             const size_t ti = static_cast<size_t>(in ? p : tl.j) * a.nCG + tl.cg;
-            const uint64_t wi = tagged_load(a.incl + ti * 32 + tl.slot);
-            uint64_t wa[AW];
+            const int e0 = HALF ? 0 : tl.sub * PER;
+            uint64_t wd[PER];
 #pragma unroll
-            for (int e = 0; e < AW; ++e) wa[e] = tagged_load(a.agg + (ti * AW + e) * 32 + tl.slot);
-            bool okA = true;
+            for (int i = 0; i < PER; ++i) {
+                const int e = e0 + i < NWD ? e0 + i : NWD - 1;
+                wd[i] = e < CW ? tagged_load(a.incl + (ti * CW + e) * 32 + tl.slot)
+                               : tagged_load(a.agg + (ti * AW + (e - CW)) * 32 + tl.slot);
+            }
+            if (spin == 0) overlap();
+            bool okI = true, okA = true;
 #pragma unroll
-            for (int e = 0; e < AW; ++e) okA = okA && tag_is(wa[e], tag);
-            const uint32_t hA = static_cast<uint32_t>(__ballot(okA) >> (32 * tl.sub));
-            const uint32_t hI = static_cast<uint32_t>(__ballot(tag_is(wi, tag)) >> (32 * tl.sub));
+            for (int i = 0; i < PER; ++i) {
+                const int e = e0 + i;
+                if (e < CW) okI = okI && tag_is(wd[i], tag);
+                else if (e < NWD) okA = okA && tag_is(wd[i], tag);
+            }
+            const uint64_t bI = __ballot(okI), bA = __ballot(okA);
+            const bool rI = HALF ? static_cast<uint32_t>(bI >> (32 * tl.sub)) == 0xFFFFFFFFu : bI == ~0ull;
+            const bool rA = HALF ? static_cast<uint32_t>(bA >> (32 * tl.sub)) == 0xFFFFFFFFu : bA == ~0ull;
 #pragma unroll
-            for (int e = 0; e < AW; ++e) sLB[u][tl.slot][e] = tag_value(wa[e]);
-            sLB[u][tl.slot][AW] = tag_value(wi);
-            if (tl.slot == 0) sStat[u] = in ? ((hA == 0xFFFFFFFFu ? 1 : 0) | (hI == 0xFFFFFFFFu ? 2 : 0)) : 4;
+            for (int i = 0; i < PER; ++i)
+                if (e0 + i < NWD) sLB[u][tl.slot][e0 + i] = tag_value(wd[i]);
+            if (HALF ? tl.slot == 0 : tl.lane == 0) sStat[u] = in ? ((rA ? 1 : 0) | (rI ? 2 : 0)) : 4;
         }
         lds_barrier();
         if (tl.wv == 0) {
@@ -1379,9 +1288,13 @@ __device__ __forceinline__ float affine_lookback(const BlkArgs &a, const Tile &t
             }
             ok = ok && stop >= 0;
             if (ok) {
-                c = (sStat[stop] & 4) ? base0 : sLB[stop][tl.slot][AW];
-                for (int u = stop - 1; u >= 0; --u) c = Rw::mv(sLB[u][tl.slot], c, sLB[u][tl.slot][K]);
-                if (tl.sub == 0) sCar[tl.slot] = c;
+                if (!(sStat[stop] & 4))
+#pragma unroll
+                    for (int e = 0; e < CW; ++e) c[e] = sLB[stop][tl.slot][e];
+                for (int u = stop - 1; u >= 0; --u) Cr::apply(&sLB[u][tl.slot][CW], c);
+                if (tl.sub == 0)
+#pragma unroll
+                    for (int e = 0; e < CW; ++e) sCar[tl.slot][e] = c[e];
             }
             if (tl.lane == 0) sDone = ok ? 1 : 0;
         }
@@ -1389,7 +1302,9 @@ __device__ __forceinline__ float affine_lookback(const BlkArgs &a, const Tile &t
         if (sDone) break;
         if (spin >= kSpinLimit) {
             if (threadIdx.x == 0) raise_error(&a.hd->err, kErrSpin);
-            if (tl.wv == 0 && tl.sub == 0) sCar[tl.slot] = base0;
+            if (tl.wv == 0 && tl.sub == 0)
+#pragma unroll
+                for (int e = 0; e < CW; ++e) sCar[tl.slot][e] = base0[e];
             lds_barrier();
             break;
         }
@@ -1397,12 +1312,33 @@ __device__ __forceinline__ float affine_lookback(const BlkArgs &a, const Tile &t
     }
     if (tl.wv == 0) {
         if (publish_incl && tl.sub == 0) {
-            const float xo = Rw::mv(X, c, X[K]);
-            tagged_store(a.incl + static_cast<size_t>(ftile) * 32 + tl.slot, tag, xo);
+            float xo[CW];
+#pragma unroll
+            for (int e = 0; e < CW; ++e) xo[e] = c[e];
+            Cr::apply(X, xo);
+            publish_wm<CW>(a.incl, ftile, tl.slot, tag, xo);
         }
-        return c;
+        overlap();
+    } else {
+#pragma unroll
+        for (int e = 0; e < CW; ++e) c[e] = sCar[tl.slot][e];
     }
-    return sCar[tl.slot];
+}
+
+// A tile with no predecessor in the scan direction publishes its inclusive
+// state, the tile aggregate applied to the known state base0 entering it.
+template <int KIND, int K>
+__device__ __forceinline__ void publish_first(const BlkArgs &a, const Tile &tl, int ftile, uint32_t tag,
+                                              const float *X, const float *base0)
+{
+    using Cr = Carry<KIND, K>;
+    if (tl.wv == 0 && tl.sub == 0) {
+        float xo[Cr::CW];
+#pragma unroll
+        for (int e = 0; e < Cr::CW; ++e) xo[e] = base0[e];
+        Cr::apply(X, xo);
+        publish_wm<Cr::CW>(a.incl, ftile, tl.slot, tag, xo);
+    }
 }
 
 // Forward: X = (row of Phi, entry of u) is the chunk's aggregate.  Builds the
@@ -1420,16 +1356,17 @@ __device__ __forceinline__ float affine_fwd_carry(const BlkArgs &a, const Tile &
     if constexpr (MULTI) {
         float (*nodes)[32][S::stride] = reinterpret_cast<float (*)[32][S::stride]>(&sKS[0][0][0][0]);
         if (threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
-        tree_build<K, NCH, +1>(nodes, tl, X);   // its first barrier also shares the tag
+        tree_build<kMatVec, K, NCH, +1>(nodes, tl, X);   // its first barrier also shares the tag
         const uint32_t tag = sTicket[0];
         if (tl.wv == 0 && tl.sub == 0 && tl.j < a.nT - 1) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
+        const float *root = nodes[tree_node<NCH>(tree_levels<NCH>(), 0)][tl.slot];
         float c = xh0;
-        if (tl.j > 0) c = affine_lookback<K, W, +1>(a, tl, ftile, tag, X, xh0, tl.j < a.nT - 1);
-        else if (tl.wv == 0 && tl.sub == 0 && a.nT > 1) {
-            const float xo = Rw::mv(X, xh0, X[K]);
-            tagged_store(a.incl + static_cast<size_t>(ftile) * 32 + tl.slot, tag, xo);
-        }
-        return tree_apply<K, NCH, +1>(nodes, tl, c);
+        if (tl.j > 0)
+            block_lookback<kMatVec, K, W, +1>(a, tl, ftile, tag, root, &xh0, tl.j < a.nT - 1, &c, [] {});
+        else if (a.nT > 1)
+            publish_first<kMatVec, K>(a, tl, ftile, tag, root, &xh0);
+        tree_apply<kMatVec, K, NCH, +1>(nodes, tl, &c);
+        return c;
     } else {
         ks_store<kMatVec, K, NCH>(sKS[0], tl.q, tl.slot, X);
         __syncthreads();
@@ -1453,14 +1390,18 @@ __device__ __forceinline__ float affine_bwd_carry(const BlkArgs &a, const Tile &
     if constexpr (MULTI) {
         float (*nodes)[32][S::stride] = reinterpret_cast<float (*)[32][S::stride]>(&sKS[0][0][0][0]);
         if (threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
-        tree_build<K, NCH, -1>(nodes, tl, X);
+        tree_build<kMatVec, K, NCH, -1>(nodes, tl, X);
         const uint32_t tag = sTicket[0];
         if (tl.wv == 0 && tl.sub == 0 && tl.j > 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
+        const float *root = nodes[tree_node<NCH>(tree_levels<NCH>(), 0)][tl.slot];
+        const float zero = 0.0f;
         float w = 0.0f;
-        if (tl.j < a.nT - 1) w = affine_lookback<K, W, -1>(a, tl, ftile, tag, X, 0.0f, tl.j > 0);
-        else if (tl.wv == 0 && tl.sub == 0 && a.nT > 1)
-            tagged_store(a.incl + static_cast<size_t>(ftile) * 32 + tl.slot, tag, X[K]);   // Psi 0 + Wl
-        return tree_apply<K, NCH, -1>(nodes, tl, w);
+        if (tl.j < a.nT - 1)
+            block_lookback<kMatVec, K, W, -1>(a, tl, ftile, tag, root, &zero, tl.j > 0, &w, [] {});
+        else if (a.nT > 1)
+            publish_first<kMatVec, K>(a, tl, ftile, tag, root, &zero);
+        tree_apply<kMatVec, K, NCH, -1>(nodes, tl, &w);
+        return w;
     } else {
         ks_store<kMatVec, K, NCH>(sKS[0], tl.q, tl.slot, X);
         __syncthreads();
@@ -1766,9 +1707,7 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
     constexpr int NCH = 2 * W;
     using S = AggShape<kMat, K>;
     using Rw = Rows<K>;
-    constexpr int FIN = ks_final<NCH>();
     __shared__ float sKS[2][NCH][32][S::stride];
-    __shared__ float sCarry[32][K];
     __shared__ uint32_t sTicket[2];
 
     const int tile = blockIdx.x;
@@ -1795,71 +1734,24 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
 #pragma unroll
         for (int s = 0; s < K; ++s) X[s] = np[s];
     }
-    ks_store<kMat, K, NCH>(sKS[0], tl.q, tl.slot, X);
+    float (*nodes)[32][S::stride] = reinterpret_cast<float (*)[32][S::stride]>(&sKS[0][0][0][0]);
     if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
-    __syncthreads();
-    const uint32_t tag = sTicket[0];
-
-    ks_scan<kMat, K, NCH, +1>(sKS, tl.q, tl.slot, X);   // X = composite of chunks 0..q
+    tree_build<kMat, K, NCH, +1>(nodes, tl, X);   // its first barrier also shares the tag
+    // state entering the tile (P_0 = I before the first), then entering the chunk
+    float P[K], eye[K];
+    Rw::eye(tl.v, eye);
+#pragma unroll
+    for (int s = 0; s < K; ++s) P[s] = eye[s];
     if constexpr (MULTI) {
-        // the last wave's upper half holds the tile aggregate and runs the look-back
-        if (tl.wv == W - 1) {
-            const bool owner = tl.sub == 1;
-            if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<K>(a.agg, ftile, tl.slot, tag, X);
-            float Pin[K];
-            Rw::eye(tl.v, Pin);
-            if (tl.j > 0) {
-                float xi[K];
-                const int ps = find_inclusive<K>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, -1, tag, &a.hd->err, xi);
-                if (ps >= 0) {
-#pragma unroll
-                    for (int s = 0; s < K; ++s) Pin[s] = xi[s];
-                }
-                constexpr int NB = K >= 16 ? 2 : 4;
-                for (int p = ps + 1; p < tl.j; p += NB) {
-                    const int cnt = min(NB, tl.j - p);
-                    float ag[NB][K];
-                    load_aggregates<K, NB>(a.agg, p, +1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
-#pragma unroll
-                    for (int u = 0; u < NB; ++u)
-                        if (u < cnt) {
-                            float np[K];
-                            Rw::mm(ag[u], Pin, np);
-#pragma unroll
-                            for (int s = 0; s < K; ++s) Pin[s] = np[s];
-                        }
-                }
-            }
-            if (owner && tl.j < a.nT - 1) {
-                float Po[K];
-                Rw::mm(X, Pin, Po);
-                publish<K>(a.incl, ftile, tl.slot, tag, Po);
-            }
-            if (owner) {
-#pragma unroll
-                for (int s = 0; s < K; ++s) sCarry[tl.slot][s] = Pin[s];
-            }
-        }
+        const uint32_t tag = sTicket[0];
+        if (tl.wv == 0 && tl.sub == 0 && tl.j < a.nT - 1) publish_wm<K>(a.agg, ftile, tl.slot, tag, X);
+        const float *root = nodes[tree_node<NCH>(tree_levels<NCH>(), 0)][tl.slot];
+        if (tl.j > 0)
+            block_lookback<kMat, K, W, +1>(a, tl, ftile, tag, root, eye, tl.j < a.nT - 1, P, [] {});
+        else
+            publish_first<kMat, K>(a, tl, ftile, tag, root, eye);
     }
-    __syncthreads();
-    // state entering the chunk: (composite of chunks 0..q-1) x (tile carry-in)
-    float P[K];
-    if constexpr (MULTI) {
-#pragma unroll
-        for (int s = 0; s < K; ++s) P[s] = sCarry[tl.slot][s];
-        if (tl.q > 0) {
-            float np[K];
-            Rw::mm(sKS[FIN][tl.q - 1][tl.slot], P, np);
-#pragma unroll
-            for (int s = 0; s < K; ++s) P[s] = np[s];
-        }
-    } else {
-        Rw::eye(tl.v, P);
-        if (tl.q > 0) {
-#pragma unroll
-            for (int s = 0; s < K; ++s) P[s] = sKS[FIN][tl.q - 1][tl.slot][s];
-        }
-    }
+    tree_apply<kMat, K, NCH, +1>(nodes, tl, P);
     // the state entering this chunk, for the backward's recompute (slot order kept)
     store_vec<K>(a.pstate + ((static_cast<size_t>(ftile) * NCH + tl.q) * 32 + tl.slot) * K, P);
     if (a.out == nullptr) return;   // states only (requested by a backward)
@@ -1876,16 +1768,15 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
 
 // Backward: W_t = A_t^T G_t with G_t = dP_t + W_{t+1}; per chunk [s, e]
 // W_s = Psi W_{e+1} + Wl.  dA_t = G_t P_{t-1}^T, with P_{t-1} recomputed from
-// the state entering the chunk (stored by the forward) and the A_t in hand.
+// the state entering the chunk (stored by the forward) and the A_t in hand,
+// while the look-back's loads are in flight.
 template <int K, int C, int W, bool MULTI>
 __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
 {
     constexpr int NCH = 2 * W;
     using S = AggShape<kMatMat, K>;
     using Rw = Rows<K>;
-    constexpr int FIN = ks_final<NCH>();
     __shared__ float sKS[2][NCH][32][S::stride];
-    __shared__ float sCarry[32][K];
     __shared__ uint32_t sTicket[2];
 
     const int tile = blockIdx.x;
@@ -1937,80 +1828,31 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
 #pragma unroll
         for (int s = 0; s < K; ++s) { X[s] = np[s]; X[K + s] = nw[s]; }
     }
-    ks_store<kMatMat, K, NCH>(sKS[0], tl.q, tl.slot, X);
+    float (*nodes)[32][S::stride] = reinterpret_cast<float (*)[32][S::stride]>(&sKS[0][0][0][0]);
     if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
-    __syncthreads();
-    const uint32_t tag = sTicket[0];
-
-    ks_scan<kMatMat, K, NCH, -1>(sKS, tl.q, tl.slot, X);   // X = composite of chunks q..NCH-1
-    // wave 0's lower half holds the tile aggregate and runs the look-back; the
-    // other waves meanwhile recompute P_{t-1}^T = P_{t-2}^T A_{t-1}^T
-    const bool lb_wave = MULTI && tl.wv == 0;
-    if (lb_wave) {
-        const bool owner = tl.sub == 0;
-        if (owner && tl.j > 0 && tl.j < a.nT - 1) publish<S::words>(a.agg, ftile, tl.slot, tag, X);
-        float Win[K];
-#pragma unroll
-        for (int s = 0; s < K; ++s) Win[s] = 0.0f;
-        if (tl.j < a.nT - 1) {
-            float xi[K];
-            const int ps = find_inclusive<K>(a.incl, tl.j, a.nT, a.nCG, tl.cg, tl.slot, +1, tag, &a.hd->err, xi);
-            int pend = a.nT;
-            if (ps >= 0) {
-                pend = ps;
-#pragma unroll
-                for (int s = 0; s < K; ++s) Win[s] = xi[s];
-            }
-            constexpr int NB = K >= 16 ? 1 : 2;
-            for (int p = pend - 1; p > tl.j; p -= NB) {
-                const int cnt = min(NB, p - tl.j);
-                float ag[NB][S::words];
-                load_aggregates<S::words, NB>(a.agg, p, -1, cnt, a.nCG, tl.cg, tl.slot, tag, &a.hd->err, ag);
-#pragma unroll
-                for (int u = 0; u < NB; ++u)
-                    if (u < cnt) {
-                        float np[K];
-                        Rw::mm(ag[u], Win, np);
-#pragma unroll
-                        for (int s = 0; s < K; ++s) Win[s] = np[s] + ag[u][K + s];
-                    }
-            }
-        }
-        if (owner && tl.j > 0) {
-            float Wo[K];
-            Rw::mm(X, Win, Wo);
-#pragma unroll
-            for (int s = 0; s < K; ++s) Wo[s] += X[K + s];
-            publish<K>(a.incl, ftile, tl.slot, tag, Wo);
-        }
-        if (owner) {
-#pragma unroll
-            for (int s = 0; s < K; ++s) sCarry[tl.slot][s] = Win[s];
-        }
-    } else {
+    tree_build<kMatMat, K, NCH, -1>(nodes, tl, X);
+    // P_{t-1}^T = P_{t-2}^T A_{t-1}^T for the chunk's later steps
+    auto recompute = [&] {
 #pragma unroll
         for (int i = 1; i < C; ++i) Rw::mm(PT[i - 1], ATr[i - 1], PT[i]);
-    }
-    __syncthreads();
-    if (lb_wave) {
+    };
+    float Wc[K], zero[K];
 #pragma unroll
-        for (int i = 1; i < C; ++i) Rw::mm(PT[i - 1], ATr[i - 1], PT[i]);
-    }
-    // carry entering the chunk from its end: (composite of chunks q+1..) x (tile carry-in)
-    float Wc[K];
-    if constexpr (MULTI) {
-#pragma unroll
-        for (int s = 0; s < K; ++s) Wc[s] = sCarry[tl.slot][s];
-        if (tl.q < NCH - 1) {
-            float np[K];
-            Rw::mm(sKS[FIN][tl.q + 1][tl.slot], Wc, np);
-#pragma unroll
-            for (int s = 0; s < K; ++s) Wc[s] = np[s] + sKS[FIN][tl.q + 1][tl.slot][K + s];
-        }
+    for (int s = 0; s < K; ++s) zero[s] = Wc[s] = 0.0f;
+    if (MULTI && tl.j < a.nT - 1) {
+        const uint32_t tag = sTicket[0];
+        if (tl.wv == 0 && tl.sub == 0 && tl.j > 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
+        block_lookback<kMatMat, K, W, -1>(a, tl, ftile, tag, nodes[tree_node<NCH>(tree_levels<NCH>(), 0)][tl.slot],
+                                          zero, tl.j > 0, Wc, recompute);
     } else {
-#pragma unroll
-        for (int s = 0; s < K; ++s) Wc[s] = tl.q < NCH - 1 ? sKS[FIN][tl.q + 1][tl.slot][K + s] : 0.0f;
+        if (MULTI) {   // the last tile along T (nT > 1): nothing after it
+            const uint32_t tag = sTicket[0];
+            if (tl.wv == 0 && tl.sub == 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
+            publish_first<kMatMat, K>(a, tl, ftile, tag, X, zero);
+        }
+        recompute();
     }
+    tree_apply<kMatMat, K, NCH, -1>(nodes, tl, Wc);   // carry entering the chunk from its end
 
 #pragma unroll
     for (int i = C - 1; i >= 0; --i) {
