@@ -913,9 +913,11 @@ __device__ __forceinline__ void ks_store(float (*buf)[32][(AggShape<KIND, K>::st
 // minGRU home page; the Clements / EUNN mesh it cites): layer l rotates the
 // pairs (i, i+1), i = l mod 2, l mod 2 + 2, ..., R = L_7 .. L_0, angles in
 // (layer, pair) order, each rotation mapping (x_i, x_j) to
-// (c x_i - s x_j, s x_i + c x_j).  Lane p of a chain's 8 lanes loads angles
-// 4p..4p+3 (lane 7 none), and the chain shares their cosines and sines through
-// LDS, so every angle is loaded once and turned into sin / cos once.
+// (c x_i - s x_j, s x_i + c x_j).  The forward builds each lane's row of R in
+// the lane: lane p of a chain's 8 lanes loads angles 4p..4p+3 (lane 7 none),
+// and the chain shares their cosines and sines through LDS, so every angle is
+// loaded once and turned into sin / cos once.  The backward applies the mesh
+// layer by layer across the chain's lanes (further below).
 
 constexpr int kAngles = 28;
 // row stride (floats) of the per-lane cos / sin exchange buffer: 8 values, padded
@@ -993,41 +995,7 @@ __device__ __forceinline__ void mesh_row(const float (&cc)[kAngles], const float
         }
 }
 
-// column v of R in natural row order: L_7 .. L_0 e_v
-__device__ __forceinline__ void mesh_col(const float (&cc)[kAngles], const float (&ss)[kAngles], int v, float (&y)[8])
-{
-#pragma unroll
-    for (int r = 0; r < 8; ++r) y[r] = (r == v) ? 1.0f : 0.0f;
-#pragma unroll
-    for (int l = 0; l < 8; ++l)
-#pragma unroll
-        for (int i = l & 1, a = mesh_first(l); i + 1 < 8; i += 2, ++a) {
-            const float yi = y[i], yj = y[i + 1];
-            y[i] = cc[a] * yi - ss[a] * yj;
-            y[i + 1] = ss[a] * yi + cc[a] * yj;
-        }
-}
-
-// Reverse pass through mesh_col: y is the built column, dy the gradient on it;
-// writes d(column)/d(angle) contracted with dy into part.  Each layer is undone
-// by its inverse rotation, so no intermediate column is stored.
-__device__ __forceinline__ void mesh_col_adjoint(const float (&cc)[kAngles], const float (&ss)[kAngles],
-                                                 float (&y)[8], float (&dy)[8], float (&part)[kAngles])
-{
-#pragma unroll
-    for (int l = 7; l >= 0; --l)
-#pragma unroll
-        for (int i = l & 1, a = mesh_first(l); i + 1 < 8; i += 2, ++a) {
-            const float yi = y[i], yj = y[i + 1], gi = dy[i], gj = dy[i + 1];
-            part[a] = gj * yi - gi * yj;
-            y[i] = cc[a] * yi + ss[a] * yj;
-            y[i + 1] = cc[a] * yj - ss[a] * yi;
-            dy[i] = cc[a] * gi + ss[a] * gj;
-            dy[i + 1] = cc[a] * gj - ss[a] * gi;
-        }
-}
-
-// natural order <-> this lane's rotated slots (slot s holds entry s ^ (v & 4)).
+// natural order -> this lane's rotated slots (slot s holds entry s ^ (v & 4)).
 // Written as a bitwise blend of two fixed-index registers: a select between
 // x[s] and x[s ^ 4] would be folded into a lane-dependent index, which sends
 // the array to scratch memory.
@@ -1037,13 +1005,6 @@ __device__ __forceinline__ float blend(float a, float b, int mask)
 }
 
 __device__ __forceinline__ void to_slots(const float (&x)[8], int v, float scale, float *y)
-{
-    const int m = -((v >> 2) & 1);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) y[s] = scale * blend(x[s], x[s ^ 4], m);
-}
-
-__device__ __forceinline__ void from_slots(const float *x, int v, float scale, float (&y)[8])
 {
     const int m = -((v >> 2) & 1);
 #pragma unroll
@@ -1067,6 +1028,181 @@ __device__ __forceinline__ float4 load_angles(const BlkArgs &a, const Tile &tl, 
 {
     const int64_t blk = tl.blk0 + static_cast<int64_t>(t) * a.nb;
     return *reinterpret_cast<const float4 *>(a.theta + blk * kAngles + 4 * min(tl.v, 6));
+}
+
+// ------------------------------------------- Givens mesh, layer by layer across the lanes
+// Element v of a chain's vectors, and row v of its 8 x 8 matrices (rotated
+// slots), sit in lane v of the chain's 8 lanes, and the mesh is applied one
+// layer at a time, each lane mixing its value with its pair partner's:
+//     x' = c x + s' x_partner,  s' = -s in the pair's first lane, +s in its second.
+// Partners: even layers v ^ 1 (quad permutation [1,0,3,2]); odd layers 1-2
+// and 5-6 (quad permutation [0,2,1,3], which leaves lanes 0, 3, 4, 7 in place)
+// and 3-4 (half-row mirror); lanes 0 and 7 sit odd layers out (c = 1, s = 0).
+// Every partner is in the chain's own 8 lanes.  A lane needs only the angles
+// of its own pairs, 8 per step: the two lanes of a pair each evaluate the
+// sine and cosine of two of the pair's four angles (one split for the even
+// layers, one for the odd) and swap them, so each of a chain's 28 angles is
+// evaluated once per pass and nothing goes through LDS.
+
+__device__ __forceinline__ float qpe(float x)   // lane v ^ 1
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float qpo(float x)   // lanes 1 <-> 2 and 5 <-> 6; 0, 3, 4, 7 in place
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xD8, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float qx2(float x)   // lane v ^ 2
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+
+// Per-lane constants of the layered mesh.
+struct MeshLane {
+    int ie, io;      // first angle this lane evaluates for its even / odd pair (the second is 7 further)
+    bool re, ro;     // second lane of its even / odd pair
+    bool mir;        // lanes 3 and 4: odd-layer partner through the half-row mirror
+    bool oddp;       // lanes 1 .. 6: in an odd-layer pair
+};
+
+__device__ __forceinline__ MeshLane mesh_lane(int v)
+{
+    MeshLane m;
+    m.re = (v & 1) != 0;
+    m.oddp = v >= 1 && v <= 6;
+    const int qo = m.oddp ? (v - 1) >> 1 : 0;
+    m.ro = m.oddp && ((v - 1) & 1) != 0;
+    m.mir = v == 3 || v == 4;
+    // even pair v/2: layers 0, 2 (first lane) or 4, 6 (second); odd pair
+    // (v-1)/2: layers 1, 3 (first lane) or 5, 7 (second)
+    m.ie = 14 * (m.re ? 1 : 0) + (v >> 1);
+    m.io = 4 + 14 * (m.ro ? 1 : 0) + qo;
+    return m;
+}
+
+__device__ __forceinline__ float mesh_partner(float x, int l, bool mir)
+{
+    if (l & 1) {
+        const float q = qpo(x), h = hm(x);
+        return mir ? h : q;
+    }
+    return qpe(x);
+}
+
+// The four angles this lane evaluates at step t (lanes 0 and 7: zero for the
+// odd pair they do not have).
+__device__ __forceinline__ float4 load_mesh_angles(const BlkArgs &a, const Tile &tl, const MeshLane &ml, int t)
+{
+    const float *p = a.theta + (tl.blk0 + static_cast<int64_t>(t) * a.nb) * kAngles;
+    return make_float4(p[ml.ie], p[ml.ie + 7], ml.oddp ? p[ml.io] : 0.0f, ml.oddp ? p[ml.io + 7] : 0.0f);
+}
+
+// cosines and sines (signed for this lane's place in the pair) of its four angles
+__device__ __forceinline__ void mesh_eval(float4 th, const MeshLane &ml, float (&e)[8])
+{
+    float s;
+    sincos_cw(th.x, s, e[0]); e[1] = ml.re ? s : -s;
+    sincos_cw(th.y, s, e[2]); e[3] = ml.re ? s : -s;
+    sincos_cw(th.z, s, e[4]); e[5] = ml.ro ? s : -s;
+    sincos_cw(th.w, s, e[6]); e[7] = ml.ro ? s : -s;
+}
+
+// Layer coefficients of one step: c[l] and s[l] = s' of layer l in this lane.
+// The partner's values arrive with the opposite sign (it holds the other end
+// of the pair).
+__device__ __forceinline__ void mesh_coef(const float (&e)[8], const MeshLane &ml, float (&c)[8], float (&s)[8])
+{
+    const float pc0 = qpe(e[0]), ps0 = -qpe(e[1]), pc1 = qpe(e[2]), ps1 = -qpe(e[3]);
+    c[0] = ml.re ? pc0 : e[0]; s[0] = ml.re ? ps0 : e[1];
+    c[2] = ml.re ? pc1 : e[2]; s[2] = ml.re ? ps1 : e[3];
+    c[4] = ml.re ? e[0] : pc0; s[4] = ml.re ? e[1] : ps0;
+    c[6] = ml.re ? e[2] : pc1; s[6] = ml.re ? e[3] : ps1;
+    const float qc0 = mesh_partner(e[4], 1, ml.mir), qs0 = -mesh_partner(e[5], 1, ml.mir);
+    const float qc1 = mesh_partner(e[6], 1, ml.mir), qs1 = -mesh_partner(e[7], 1, ml.mir);
+    c[1] = ml.ro ? qc0 : e[4]; s[1] = ml.ro ? qs0 : e[5];
+    c[3] = ml.ro ? qc1 : e[6]; s[3] = ml.ro ? qs1 : e[7];
+    c[5] = ml.ro ? e[4] : qc0; s[5] = ml.ro ? e[5] : qs0;
+    c[7] = ml.ro ? e[6] : qc1; s[7] = ml.ro ? e[7] : qs1;
+}
+
+// One layer on a vector (one value per lane).
+__device__ __forceinline__ float mesh_vec(float x, float c, float s, int l, bool mir)
+{
+    return __builtin_fmaf(s, mesh_partner(x, l, mir), c * x);
+}
+
+// X <- L_even L_odd X: an odd layer, then an even one (the transposed mesh's
+// order; the caller passes negated sines), on eight matrix row entries
+// (rotated slots) and a vector entry X[8], which share the coefficients.  Odd
+// layer: c1; q1 = s' for the quad-permutation partner (0 in lanes 3, 4), m1
+// for the mirror partner (nonzero in lanes 3 and 4 only, whose slot rotations
+// are opposite, so row slot k takes the partner's slot k ^ 4).  Even layer:
+// c0, s0 (partner v ^ 1, same slot order).  Every DPP source inside the block
+// was written at least nine instructions before it is read.
+__device__ __forceinline__ void mesh_rows2r(float (&X)[9], float c1, float q1, float m1, float c0, float s0)
+{
+    float Y[9];
+    asm("s_nop 4\n\t"
+        "v_mul_f32 %9, %18, %0\n\t"
+        "v_mul_f32 %10, %18, %1\n\t"
+        "v_mul_f32 %11, %18, %2\n\t"
+        "v_mul_f32 %12, %18, %3\n\t"
+        "v_mul_f32 %13, %18, %4\n\t"
+        "v_mul_f32 %14, %18, %5\n\t"
+        "v_mul_f32 %15, %18, %6\n\t"
+        "v_mul_f32 %16, %18, %7\n\t"
+        "v_mul_f32 %17, %18, %8\n\t"
+        "v_fmac_f32_dpp %9, %0, %19 quad_perm:[0,2,1,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %1, %19 quad_perm:[0,2,1,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %2, %19 quad_perm:[0,2,1,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %3, %19 quad_perm:[0,2,1,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %4, %19 quad_perm:[0,2,1,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %5, %19 quad_perm:[0,2,1,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %6, %19 quad_perm:[0,2,1,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %16, %7, %19 quad_perm:[0,2,1,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %17, %8, %19 quad_perm:[0,2,1,3] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %9, %4, %20 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %10, %5, %20 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %11, %6, %20 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %12, %7, %20 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %13, %0, %20 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %14, %1, %20 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %15, %2, %20 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %16, %3, %20 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %17, %8, %20 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32 %0, %21, %9\n\t"
+        "v_mul_f32 %1, %21, %10\n\t"
+        "v_mul_f32 %2, %21, %11\n\t"
+        "v_mul_f32 %3, %21, %12\n\t"
+        "v_mul_f32 %4, %21, %13\n\t"
+        "v_mul_f32 %5, %21, %14\n\t"
+        "v_mul_f32 %6, %21, %15\n\t"
+        "v_mul_f32 %7, %21, %16\n\t"
+        "v_mul_f32 %8, %21, %17\n\t"
+        "v_fmac_f32_dpp %0, %9, %22 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %10, %22 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %11, %22 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %12, %22 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %13, %22 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %14, %22 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %15, %22 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %16, %22 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %8, %17, %22 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3]), "+v"(X[4]), "+v"(X[5]), "+v"(X[6]), "+v"(X[7]),
+          "+v"(X[8]), "=&v"(Y[0]), "=&v"(Y[1]), "=&v"(Y[2]), "=&v"(Y[3]), "=&v"(Y[4]), "=&v"(Y[5]), "=&v"(Y[6]),
+          "=&v"(Y[7]), "=&v"(Y[8])
+        : "v"(c1), "v"(q1), "v"(m1), "v"(c0), "v"(s0));
+}
+
+// sum over the chain's 8 lanes, in every lane
+__device__ __forceinline__ float chain_sum8(float x)
+{
+    x += qpe(x);
+    x += qx2(x);
+    return x + hm(x);
 }
 
 // ====================================================== carry phases
@@ -1575,126 +1711,112 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
 }
 
 // =============================================== Givens angle-fused bwd
-// Same reverse scan with A_t = sigmoid(s_t) R(theta_t) formed in registers
-// (unscaled columns of R, the gate applied as a scalar).  dA_t = g_t h_{t-1}^T
-// is never formed as a tensor: lane v holds column v of it, contracts it with
-// the derivative of column v of A (the reverse pass through the mesh) and with
-// column v of R (for the gate), and the chain's 8 lanes add their shares in LDS:
-//     dtheta_t = sigmoid(s_t) <dA_t, dR/dtheta>,  ds_t = sigmoid'(s_t) <dA_t, R>.
+// Same reverse scan with A_t = sigmoid(s_t) R(theta_t), the mesh applied
+// layer by layer across the chain's lanes (A^T = sigmoid L_0^T .. L_7^T).
+// dA_t = g_t h_{t-1}^T is never formed: with y_l the state entering layer l
+// (y_0 = h_{t-1}) and z_l the gradient on layer l's output (z_7 = sigmoid g_t,
+// z_{l-1} = L_l^T z_l), the angle of the pair (i, j) in layer l has gradient
+//     z_j y_{l+1,i} - z_i y_{l+1,j},
+// which the pair's two lanes form from each other's values, and
+//     ds_t = sigmoid'(s_t) <g_t, R h_{t-1}> = sigmoid'(s_t) <g_t, y_8>.
+// z_{-1} = A_t^T g_t is the carry to the step before.  Each lane writes the
+// gradients of the four angles it evaluated.
 
 template <int C, int W, bool MULTI>
 __global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
 {
-    constexpr int NCH = 2 * W;
-    // words per lane in the reduction buffer: 28 angles, the gate, padding to a
-    // stride of 36 (a multiple of 4 for 16-byte accesses; 36 l mod 64 differs for 16
-    // consecutive lanes, so a 16-byte access by 16 lanes touches every bank once)
-    constexpr int PW = 36;
-    __shared__ float sKS[2][NCH][32][(AggShape<kMatVec, 8>::stride)];
+    __shared__ float sKS[2][2 * W][32][(AggShape<kMatVec, 8>::stride)];
     __shared__ float sCarry[32];
     __shared__ uint32_t sTicket[2];
-    __shared__ float sCS[W][64][kCSLd];
-    __shared__ float sPart[W][64][PW];
 
     const int tile = blockIdx.x;
     unsigned long long ep = 0;
     if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<8, C, W>(a, tile, true);
     const int ftile = tl.j * a.nCG + tl.cg;
+    const MeshLane ml = mesh_lane(tl.v);
 
     float4 th[C];
-    float RTr[C][8], sig[C], gv[C], hp[C];   // rows of R^T (unscaled), gate, dh_t, h_{t-1}
+    float sig[C], sgd[C], gv[C], hp[C];   // gate sigmoid(s), its derivative, dh_t, h_{t-1}
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int t = clampT(tl.t0 + i, a.T);
-        th[i] = load_angles(a, tl, t);
+        th[i] = load_mesh_angles(a, tl, ml, t);
         sig[i] = a.sg[tl.blk0 + static_cast<int64_t>(t) * a.nb];
         gv[i] = load_once(&a.y[tl.vec0 + t * tl.vstep]);
         hp[i] = load_once(&a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep]);
     }
     const float xh0 = load_h0<8>(a, tl);
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        float cc[kAngles], ss[kAngles], y[8];
-        mesh_share(th[i], sCS[tl.wv], tl.lane, cc, ss);
-        mesh_col(cc, ss, tl.v, y);
-        to_slots(y, tl.v, 1.0f, RTr[i]);
-        sig[i] = sigmoidf_(sig[i]);
-        settle8(RTr[i]);
-    }
+    float ev[C][8];   // this lane's four cosines and signed sines per step
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int t = tl.t0 + i;
         if (t == 0) hp[i] = xh0;
-        if (!(tl.cv && t < a.T)) {
-            eye_row8(tl.v, RTr[i]);
-            sig[i] = 1.0f;
+        const bool valid = tl.cv && t < a.T;
+        if (!valid) {   // identity step: zero angles, gate 1
+            th[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             gv[i] = 0.0f;
             hp[i] = 0.0f;
         }
+        // with e = exp(-|s|): sigmoid(|s|) = 1 / (1 + e) and sigmoid'(s) =
+        // e / (1 + e)^2, exact in relative terms (1 - sigmoid(s) would cancel
+        // once sigmoid(s) nears 1)
+        const float e = __expf(-fabsf(sig[i])), r = 1.0f / (1.0f + e);
+        sgd[i] = valid ? e * r * r : 0.0f;
+        sig[i] = valid ? (sig[i] >= 0.0f ? r : e * r) : 1.0f;
+        mesh_eval(th[i], ml, ev[i]);
     }
 
-    // chunk aggregate from a zero carry, walking t downwards: X = (Psi, Wl)
+    // chunk aggregate from a zero carry, walking t downwards: X = (Psi, Wl),
+    // Psi <- A_t^T Psi, Wl <- A_t^T (dh_t + Wl)
     float X[9];
+    eye_row8(tl.v, X);
+    X[8] = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) X[s] = sig[C - 1] * RTr[C - 1][s];
-    X[8] = sig[C - 1] * mv8(RTr[C - 1], gv[C - 1], 0.0f);
+    for (int i = C - 1; i >= 0; --i) {
+        float c[8], s[8];
+        mesh_coef(ev[i], ml, c, s);
+        c[0] *= sig[i];
+        s[0] *= sig[i];
+        X[8] += gv[i];
 #pragma unroll
-    for (int i = C - 2; i >= 0; --i) {
-        float np[8];
-        mm8(RTr[i], X, np);
-        X[8] = sig[i] * mv8(RTr[i], gv[i] + X[8], 0.0f);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) X[s] = sig[i] * np[s];
+        for (int l = 7; l >= 0; l -= 2) {   // transposed layers: sines negated
+            const float q = ml.mir ? 0.0f : -s[l], m = ml.mir ? -s[l] : 0.0f;
+            mesh_rows2r(X, c[l], q, m, c[l - 1], -s[l - 1]);
+        }
     }
     float w = affine_bwd_carry<8, C, W, MULTI>(a, tl, ftile, ep, X, sKS, sCarry, sTicket);
 
-    float (*part)[PW] = sPart[tl.wv];
-    const int base = tl.lane & ~7;
-    // with up to 4 steps per lane group the angles loaded for the build stay in
-    // registers; with 8 they are read again here (an L2 hit), one step ahead
-    constexpr bool kKeep = C <= 4;
-    float4 thn = kKeep ? th[C - 1] : load_angles(a, tl, clampT(tl.t0 + C - 1, a.T));
 #pragma unroll
     for (int i = C - 1; i >= 0; --i) {
-        const float4 thc = thn;
-        if (i > 0) thn = kKeep ? th[i - 1] : load_angles(a, tl, clampT(tl.t0 + i - 1, a.T));
         const float g = gv[i] + w;
-        float dAc[8];
-        outer8(hp[i], g, dAc);              // column v of dA_t = g_t h_{t-1}^T (rotated slots)
-        w = sig[i] * mv8(RTr[i], g, 0.0f);  // A_t^T g_t
-        // lane v's share of dtheta_t and ds_t, through column v of A_t
-        float cc[kAngles], ss[kAngles], y[8], dy[8], pt[kAngles];
-        mesh_share(thc, sCS[tl.wv], tl.lane, cc, ss);
-        from_slots(RTr[i], tl.v, 1.0f, y);
-        from_slots(dAc, tl.v, sig[i], dy);
-        float gate = 0.0f;
+        float c[8], s[8], y[8], d[8];
+        mesh_coef(ev[i], ml, c, s);
+        float x = hp[i];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) gate += dy[r] * y[r];
-        mesh_col_adjoint(cc, ss, y, dy, pt);
+        for (int l = 0; l < 8; ++l) y[l] = x = mesh_vec(x, c[l], s[l], l, ml.mir);
+        const float ds = chain_sum8(g * y[7]) * sgd[i];
+        float z = sig[i] * g;
 #pragma unroll
-        for (int q = 0; q < 7; ++q)
-            *reinterpret_cast<float4 *>(&part[tl.lane][4 * q]) =
-                make_float4(pt[4 * q], pt[4 * q + 1], pt[4 * q + 2], pt[4 * q + 3]);
-        *reinterpret_cast<float4 *>(&part[tl.lane][28]) = make_float4((1.0f - sig[i]) * gate, 0.0f, 0.0f, 0.0f);
-        // lane v (< 7) adds up angles 4v..4v+3 over the chain; lane 7 the gate
-        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const float4 u = *reinterpret_cast<const float4 *>(&part[base + p][4 * tl.v]);
-            acc.x += u.x; acc.y += u.y; acc.z += u.z; acc.w += u.w;
+        for (int l = 7; l >= 0; --l) {
+            const float zp = mesh_partner(z, l, ml.mir), yp = mesh_partner(y[l], l, ml.mir);
+            d[l] = zp * y[l] - z * yp;   // the first lane's angle gradient; the second lane's negated
+            z = __builtin_fmaf(-s[l], zp, c[l] * z);
         }
+        w = z;
         const int t = tl.t0 + i;
         if (tl.cv && t < a.T) {
-            const int64_t blk = tl.blk0 + static_cast<int64_t>(t) * a.nb;
+            float *dth = a.dtheta + (tl.blk0 + static_cast<int64_t>(t) * a.nb) * kAngles;
             store_out(&a.out2[tl.vec0 + t * tl.vstep], g);
-            if (tl.v < 7)
-                store_out4(a.dtheta + blk * kAngles + 4 * tl.v, acc.x, acc.y, acc.z, acc.w);
-            else
-                store_out(&a.dsg[blk], acc.x);
+            dth[ml.ie] = ml.re ? -d[4] : d[0];
+            dth[ml.ie + 7] = ml.re ? -d[6] : d[2];
+            if (ml.oddp) {
+                dth[ml.io] = ml.ro ? -d[5] : d[1];
+                dth[ml.io + 7] = ml.ro ? -d[7] : d[3];
+            } else if (tl.v == 7) {
+                a.dsg[tl.blk0 + static_cast<int64_t>(t) * a.nb] = ds;
+            }
         }
-        asm volatile("" : "+v"(w));
-        __builtin_amdgcn_sched_barrier(0);
     }
     if (tl.cv && tl.t0 == 0) store_out(&a.out3[tl.bb * a.d + tl.jb * 8 + tl.v], w);   // A_1^T g_1
 }

@@ -84,6 +84,71 @@ def test_givens_long_T_without_decay(gpu):
         assert np.max(np.abs(x - r)) / np.max(np.abs(r)) <= 2e-5, key
 
 
+def test_givens_long_T_slow_decay_with_gate_gradient(gpu):
+    """Gates at s = 8 (sigmoid = 0.99966: over T = 2000 steps, 16 tiles along T, a
+    state keeps about half its size, so the far tiles' carries still show) with
+    every output compared, ds included: sigmoid'(8) = 3.4e-4 is well inside fp32
+    range here, and the kernel forms it as sigmoid(s) sigmoid(-s), without the
+    cancellation of 1 - sigmoid(s).  Normwise bar of the no-decay cases."""
+    say("givens slow-decay T=2000")
+    theta, s, b, h0, dh = _inp(2, 2000, 16, 10, h0="normal")
+    s = np.full_like(s, 8.0)
+    out, ref = run_givens(theta, s, b, h0, dh, gpu)
+    for key in out:
+        x, r = out[key].astype(np.float64), ref[key]
+        assert np.all(np.isfinite(x)), key
+        assert np.max(np.abs(x - r)) / np.max(np.abs(r)) <= 2e-5, key
+
+
+def test_givens_backward_footprint(gpu):
+    """Device memory the backward holds at its peak on the pages' memory workload
+    (B = 128, T = 64, d = 64, k = 8; "Run the benchmarks", Step 3): the
+    angle-fused backward (theta, s, h, dh in; dtheta, ds, db, dh0 out; its
+    workspace) against the block-affine backward on the materialised
+    A = sigmoid(s) R(theta) (A, h, dh in; dA, db, dh0 out; its workspace), which
+    would still need a further pass from dA to dtheta and ds.  Each figure counts
+    the tensors the call needs, allocated from a common starting point."""
+    import torch
+    import scan_linear_rnns_amd as mgs
+    theta, s, b, h0, dh = _inp(128, 64, 64, 0)
+    A = oracle.givens_matrix(theta, s, 8).astype(np.float32)
+
+    def measure(run):
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        bwd = run()
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        outs = bwd()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        del outs
+        return peak
+
+    def fused():
+        tht, st, bt, dht = (to_dev(x, gpu) for x in (theta, s, b, dh))
+        h, ws = mgs.mgs_givens_scan_fwd(tht, st, bt, None)
+        del bt
+        return lambda: mgs.mgs_givens_scan_bwd(tht, st, None, h, dht, ws=ws)
+
+    def materialised():
+        At, bt, dht = (to_dev(x, gpu) for x in (A, b, dh))
+        h, ws = mgs.mgs_block_affine_scan_fwd(At, bt, None)
+        del bt
+        return lambda: mgs.mgs_block_affine_scan_bwd(At, None, None, h, dht, ws=ws)
+
+    measure(fused)   # first use of the allocator's size classes
+    pf = measure(fused)
+    pm = measure(materialised)
+    say(f"givens backward footprint: fused {pf / 1e6:.2f} MB, materialised block-affine {pm / 1e6:.2f} MB")
+    N = 128 * 64 * 64
+    # fused: theta, dtheta (3.5 N floats each), s, ds (N / 8 each), h, dh, db (N each),
+    # dh0 and the workspace (B d floats each, and a header)
+    need = 4 * (3.5 * 2 + 0.25 + 3) * N + 2 * 4 * 128 * 64 + 256
+    assert pf <= 1.06 * need
+    assert pf < 0.6 * pm
+
+
 def test_givens_matches_block_affine_on_formed_matrices(gpu):
     """The fused op and the block-affine op on A = sigmoid(s) R(theta) (formed on the host)
     agree on h, db, dh0 -- two GPU paths, one input."""
