@@ -61,7 +61,8 @@ struct BlkArgs {
     int T, d, nb, nCG, nT, nTiles;
     WsHeader *hd;
     uint64_t *agg, *incl;
-    float *pstate;       // cumulative product: state entering each chunk, [tile][chunk][slot][k]
+    float *pstate;       // cumulative product: the state entering every 2^pcs-th step, [t >> pcs][chain group][slot][k]
+    int pcs;             // cumulative product: log2 of the steps between saved states (the backward's chunk length)
     const float *theta;  // Givens angle-fused: angles (B,T,nb,28)
     const float *sg;     // Givens angle-fused: gate pre-activations (B,T,nb)
     float *dtheta;       // Givens angle-fused backward: d angles
@@ -90,11 +91,24 @@ constexpr BlkShape affine_shape(int k)
 {
     return k == 8 ? BlkShape{MGS_AFF_W, MGS_AFF_MAXC} : k == 16 ? BlkShape{8, 4} : BlkShape{8, 8};
 }
-constexpr BlkShape matrix_shape(int k)
+// The cumulative product's forward and backward may tile T differently: the
+// forward saves the state entering every step the backward starts a chunk at.
+// k = 16: the backward keeps three 16-float rows per step and its reverse
+// aggregate is two 16 x 16 rows per lane, so it runs four waves of two-step
+// chunks (LDS buffers at 68 KB); the forward keeps one row per step and runs
+// eight waves of eight-step chunks, whose 128-step tiles fit the long-T
+// workload into one workgroup per compute unit.
+#ifndef MGS_MAT16_FWD_W
+#define MGS_MAT16_FWD_W 8
+#endif
+#ifndef MGS_MAT16_FWD_MAXC
+#define MGS_MAT16_FWD_MAXC 8
+#endif
+constexpr BlkShape matrix_shape(int k, bool forward)
 {
-    // k = 16: the backward's reverse aggregate is two 16 x 16 rows per lane;
-    // four waves keep its LDS buffers at 68 KB
-    return k == 8 ? BlkShape{MGS_MAT_W, MGS_MAT_MAXC} : k == 16 ? BlkShape{4, 2} : BlkShape{8, 8};
+    return k == 8    ? BlkShape{MGS_MAT_W, MGS_MAT_MAXC}
+           : k == 16 ? (forward ? BlkShape{MGS_MAT16_FWD_W, MGS_MAT16_FWD_MAXC} : BlkShape{4, 2})
+                     : BlkShape{8, 8};
 }
 
 enum class BlkOp : int { AffineFwd, AffineBwd, MatrixFwd, MatrixBwd };
@@ -1218,10 +1232,24 @@ __device__ __forceinline__ float chain_sum8(float x)
 // the tile is known, each chunk reaches its own entering state by applying at
 // most log2(NCH) tree nodes to it, so no prefix of every chunk is ever formed.
 
-template <int NCH>
-__device__ __forceinline__ constexpr int tree_node(int l, int i)   // level l starts after 2 NCH - 2 NCH / 2^l nodes
+// Node (l, i) of the tree of a tile's NCH chunks (NCH / 2^l nodes at level l,
+// the root at level log2 NCH).  Once the tree is built, the chunks' entering
+// states need only the nodes of a prefix decomposition (forward: even i) or a
+// suffix one (reverse: odd i), and the look-back the root.  Those sit after
+// the others, so the NCH - 1 nodes dead by then form one block at the start
+// of the node array, where the look-back may stage the words it polls.
+template <int NCH, int DIR>
+__device__ __forceinline__ constexpr int tree_node(int l, int i)
 {
-    return 2 * NCH - ((2 * NCH) >> l) + i;
+    const bool live = (NCH >> l) == 1 || (i & 1) == (DIR > 0 ? 0 : 1);
+    return (live ? NCH - 1 : 0) + NCH - (NCH >> l) + (i >> 1);
+}
+
+// floats of the block of dead nodes at the start of a node array
+template <int KIND, int K, int NCH>
+constexpr int dead_nodes_floats()
+{
+    return (NCH - 1) * 32 * AggShape<KIND, K>::stride;
 }
 
 template <int NCH>
@@ -1274,7 +1302,7 @@ __device__ __forceinline__ void tree_build(float (*nodes)[32][(AggShape<KIND, K>
     constexpr int AW = AggShape<KIND, K>::words;
     constexpr int L = tree_levels<NCH>();
 #pragma unroll
-    for (int e = 0; e < AW; ++e) nodes[tree_node<NCH>(0, tl.q)][tl.slot][e] = X[e];
+    for (int e = 0; e < AW; ++e) nodes[tree_node<NCH, DIR>(0, tl.q)][tl.slot][e] = X[e];
     // level 1 inside each wave: its halves hold chunks 2w and 2w + 1 (lanes l
     // and l ^ 32 serve the same row of the same chain)
     {
@@ -1291,14 +1319,14 @@ __device__ __forceinline__ void tree_build(float (*nodes)[32][(AggShape<KIND, K>
         for (int e = 0; e < AW; ++e) X[e] = Y[e];
         if (L > 1 && tl.sub == 0)
 #pragma unroll
-            for (int e = 0; e < AW; ++e) nodes[tree_node<NCH>(1, tl.wv)][tl.slot][e] = X[e];
+            for (int e = 0; e < AW; ++e) nodes[tree_node<NCH, DIR>(1, tl.wv)][tl.slot][e] = X[e];
     }
     lds_barrier();
 #pragma unroll
     for (int l = 2; l <= L; ++l) {
         if (tl.wv < (NCH >> l)) {
-            const float *lo = nodes[tree_node<NCH>(l - 1, 2 * tl.wv)][tl.slot];
-            const float *hi = nodes[tree_node<NCH>(l - 1, 2 * tl.wv + 1)][tl.slot];
+            const float *lo = nodes[tree_node<NCH, DIR>(l - 1, 2 * tl.wv)][tl.slot];
+            const float *hi = nodes[tree_node<NCH, DIR>(l - 1, 2 * tl.wv + 1)][tl.slot];
             float R[AW];
 #pragma unroll
             for (int e = 0; e < AW; ++e) {
@@ -1308,7 +1336,7 @@ __device__ __forceinline__ void tree_build(float (*nodes)[32][(AggShape<KIND, K>
             compose_into<KIND, K>(X, R);
             if (l < L && tl.sub == 0)
 #pragma unroll
-                for (int e = 0; e < AW; ++e) nodes[tree_node<NCH>(l, tl.wv)][tl.slot][e] = X[e];
+                for (int e = 0; e < AW; ++e) nodes[tree_node<NCH, DIR>(l, tl.wv)][tl.slot][e] = X[e];
         }
         if (l < L) lds_barrier();
     }
@@ -1316,7 +1344,7 @@ __device__ __forceinline__ void tree_build(float (*nodes)[32][(AggShape<KIND, K>
     // so that no wave keeps it in registers across the look-back
     if (tl.wv == 0 && tl.sub == 0)
 #pragma unroll
-        for (int e = 0; e < AW; ++e) nodes[tree_node<NCH>(L, 0)][tl.slot][e] = X[e];
+        for (int e = 0; e < AW; ++e) nodes[tree_node<NCH, DIR>(L, 0)][tl.slot][e] = X[e];
 }
 
 // State entering chunk tl.q from the state c entering the tile: the nodes
@@ -1333,7 +1361,7 @@ __device__ __forceinline__ void tree_apply(float (*nodes)[32][(AggShape<KIND, K>
     for (int l = L - 1; l >= 0; --l) {
         if ((r >> l) & 1) {
             const int i = DIR > 0 ? (at >> l) : ((at >> l) - 1);
-            Carry<KIND, K>::apply(nodes[tree_node<NCH>(l, i)][tl.slot], c);
+            Carry<KIND, K>::apply(nodes[tree_node<NCH, DIR>(l, i)][tl.slot], c);
             at += DIR * (1 << l);
         }
     }
@@ -1367,7 +1395,7 @@ __device__ __forceinline__ void publish_wm(uint64_t *dst, int tile, int slot, ui
 template <int KIND, int K, int W, int DIR, typename F>
 __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl, int ftile, uint32_t tag,
                                                const float *X, const float *base0, bool publish_incl,
-                                               float *c, F &&overlap)
+                                               float *c, float *dead, F &&overlap)
 {
     using Cr = Carry<KIND, K>;
     constexpr int CW = Cr::CW, AW = Cr::AW, NWD = CW + AW;
@@ -1376,7 +1404,17 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
     constexpr int PER = HALF ? NWD : (NWD + 1) / 2;   // words one lane loads
     constexpr int SW = NWD | 1;
     static_assert(NU > 0, "the look-back needs more than one wave");
-    __shared__ float sLB[NU][32][SW];
+    // staging: the tree's dead nodes when they hold it (first written only
+    // after a barrier that follows the tree's last reads), else an array of
+    // its own
+    constexpr bool ALIAS = dead_nodes_floats<KIND, K, 2 * W>() >= NU * 32 * SW;
+    float (*sLB)[32][SW];
+    if constexpr (ALIAS) {
+        sLB = reinterpret_cast<float (*)[32][SW]>(dead);
+    } else {
+        __shared__ float sOwn[NU][32][SW];
+        sLB = sOwn;
+    }
     __shared__ int sStat[NU];
     __shared__ float sCar[32][CW];
     __shared__ int sDone;
@@ -1407,10 +1445,13 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
             const uint64_t bI = __ballot(okI), bA = __ballot(okA);
             const bool rI = HALF ? static_cast<uint32_t>(bI >> (32 * tl.sub)) == 0xFFFFFFFFu : bI == ~0ull;
             const bool rA = HALF ? static_cast<uint32_t>(bA >> (32 * tl.sub)) == 0xFFFFFFFFu : bA == ~0ull;
+            if (ALIAS && spin == 0) lds_barrier();   // the tree's last level has read the dead nodes
 #pragma unroll
             for (int i = 0; i < PER; ++i)
                 if (e0 + i < NWD) sLB[u][tl.slot][e0 + i] = tag_value(wd[i]);
             if (HALF ? tl.slot == 0 : tl.lane == 0) sStat[u] = in ? ((rA ? 1 : 0) | (rI ? 2 : 0)) : 4;
+        } else if (ALIAS && spin == 0) {
+            lds_barrier();
         }
         lds_barrier();
         if (tl.wv == 0) {
@@ -1495,10 +1536,11 @@ __device__ __forceinline__ float affine_fwd_carry(const BlkArgs &a, const Tile &
         tree_build<kMatVec, K, NCH, +1>(nodes, tl, X);   // its first barrier also shares the tag
         const uint32_t tag = sTicket[0];
         if (tl.wv == 0 && tl.sub == 0 && tl.j < a.nT - 1) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
-        const float *root = nodes[tree_node<NCH>(tree_levels<NCH>(), 0)][tl.slot];
+        const float *root = nodes[tree_node<NCH, +1>(tree_levels<NCH>(), 0)][tl.slot];
         float c = xh0;
         if (tl.j > 0)
-            block_lookback<kMatVec, K, W, +1>(a, tl, ftile, tag, root, &xh0, tl.j < a.nT - 1, &c, [] {});
+            block_lookback<kMatVec, K, W, +1>(a, tl, ftile, tag, root, &xh0, tl.j < a.nT - 1, &c, &nodes[0][0][0],
+                                              [] {});
         else if (a.nT > 1)
             publish_first<kMatVec, K>(a, tl, ftile, tag, root, &xh0);
         tree_apply<kMatVec, K, NCH, +1>(nodes, tl, &c);
@@ -1529,11 +1571,12 @@ __device__ __forceinline__ float affine_bwd_carry(const BlkArgs &a, const Tile &
         tree_build<kMatVec, K, NCH, -1>(nodes, tl, X);
         const uint32_t tag = sTicket[0];
         if (tl.wv == 0 && tl.sub == 0 && tl.j > 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
-        const float *root = nodes[tree_node<NCH>(tree_levels<NCH>(), 0)][tl.slot];
+        const float *root = nodes[tree_node<NCH, -1>(tree_levels<NCH>(), 0)][tl.slot];
         const float zero = 0.0f;
         float w = 0.0f;
         if (tl.j < a.nT - 1)
-            block_lookback<kMatVec, K, W, -1>(a, tl, ftile, tag, root, &zero, tl.j > 0, &w, [] {});
+            block_lookback<kMatVec, K, W, -1>(a, tl, ftile, tag, root, &zero, tl.j > 0, &w, &nodes[0][0][0],
+                                              [] {});
         else if (a.nT > 1)
             publish_first<kMatVec, K>(a, tl, ftile, tag, root, &zero);
         tree_apply<kMatVec, K, NCH, -1>(nodes, tl, &w);
@@ -1867,16 +1910,25 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
     if constexpr (MULTI) {
         const uint32_t tag = sTicket[0];
         if (tl.wv == 0 && tl.sub == 0 && tl.j < a.nT - 1) publish_wm<K>(a.agg, ftile, tl.slot, tag, X);
-        const float *root = nodes[tree_node<NCH>(tree_levels<NCH>(), 0)][tl.slot];
+        const float *root = nodes[tree_node<NCH, +1>(tree_levels<NCH>(), 0)][tl.slot];
         if (tl.j > 0)
-            block_lookback<kMat, K, W, +1>(a, tl, ftile, tag, root, eye, tl.j < a.nT - 1, P, [] {});
+            block_lookback<kMat, K, W, +1>(a, tl, ftile, tag, root, eye, tl.j < a.nT - 1, P, &nodes[0][0][0],
+                                           [] {});
         else
             publish_first<kMat, K>(a, tl, ftile, tag, root, eye);
     }
     tree_apply<kMat, K, NCH, +1>(nodes, tl, P);
-    // the state entering this chunk, for the backward's recompute (slot order kept)
-    store_vec<K>(a.pstate + ((static_cast<size_t>(ftile) * NCH + tl.q) * 32 + tl.slot) * K, P);
-    if (a.out == nullptr) return;   // states only (requested by a backward)
+    // the states entering the steps t = 0 mod 2^pcs of this chunk, for the
+    // backward's recompute (slot order kept).  When both directions share one
+    // shape, that is the chunk's first step alone.
+    constexpr bool kSame = matrix_shape(K, true).W == matrix_shape(K, false).W &&
+                           matrix_shape(K, true).max_c == matrix_shape(K, false).max_c;
+    auto save = [&](int t) {
+        if ((t & ((1 << a.pcs) - 1)) == 0)
+            store_vec<K>(a.pstate + ((static_cast<size_t>(t >> a.pcs) * a.nCG + tl.cg) * 32 + tl.slot) * K, P);
+    };
+    save(tl.t0);
+    if (a.out == nullptr && (kSame || (1 << a.pcs) >= C)) return;   // states only (requested by a backward)
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         float np[K];
@@ -1884,7 +1936,8 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
 #pragma unroll
         for (int s = 0; s < K; ++s) P[s] = np[s];
         const int t = tl.t0 + i;
-        if (tl.cv && t < a.T) Rw::store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, P);
+        if (a.out && tl.cv && t < a.T) Rw::store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, P);
+        if (!kSame && i + 1 < C) save(t + 1);
     }
 }
 
@@ -1919,7 +1972,7 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
     // c of it at slot col(m, c)
     float PT[C][K];
     {
-        const float *ps = a.pstate + ((static_cast<size_t>(ftile) * NCH + tl.q) * 32 + (tl.slot & ~(K - 1))) * K;
+        const float *ps = a.pstate + ((static_cast<size_t>(tl.t0 >> a.pcs) * a.nCG + tl.cg) * 32 + (tl.slot & ~(K - 1))) * K;
 #pragma unroll
         for (int s = 0; s < K; ++s) {
             const int m = Rw::col(tl.v, s);
@@ -1964,8 +2017,8 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
     if (MULTI && tl.j < a.nT - 1) {
         const uint32_t tag = sTicket[0];
         if (tl.wv == 0 && tl.sub == 0 && tl.j > 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
-        block_lookback<kMatMat, K, W, -1>(a, tl, ftile, tag, nodes[tree_node<NCH>(tree_levels<NCH>(), 0)][tl.slot],
-                                          zero, tl.j > 0, Wc, recompute);
+        block_lookback<kMatMat, K, W, -1>(a, tl, ftile, tag, nodes[tree_node<NCH, -1>(tree_levels<NCH>(), 0)][tl.slot],
+                                          zero, tl.j > 0, Wc, &nodes[0][0][0], recompute);
     } else {
         if (MULTI) {   // the last tile along T (nT > 1): nothing after it
             const uint32_t tag = sTicket[0];
@@ -2025,12 +2078,12 @@ template <int K>
 void launch_blk_impl(BlkOp op, const BlockGeom &g, const BlkArgs &a, hipStream_t s)
 {
     constexpr BlkShape af = affine_shape(K);
-    constexpr BlkShape mt = matrix_shape(K);
+    constexpr BlkShape mf = matrix_shape(K, true), mb = matrix_shape(K, false);
     switch (op) {
     case BlkOp::AffineFwd: launch_baffine_fwd<K, af.W, af.max_c>(g, a, s); break;
     case BlkOp::AffineBwd: launch_baffine_bwd<K, af.W, af.max_c>(g, a, s); break;
-    case BlkOp::MatrixFwd: launch_bmatrix_fwd<K, mt.W, mt.max_c>(g, a, s); break;
-    case BlkOp::MatrixBwd: launch_bmatrix_bwd<K, mt.W, mt.max_c>(g, a, s); break;
+    case BlkOp::MatrixFwd: launch_bmatrix_fwd<K, mf.W, mf.max_c>(g, a, s); break;
+    case BlkOp::MatrixBwd: launch_bmatrix_bwd<K, mb.W, mb.max_c>(g, a, s); break;
     }
 }
 

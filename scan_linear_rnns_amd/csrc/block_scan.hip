@@ -5,6 +5,8 @@
 // one object file per k.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "block_core.hpp"
 
 namespace mgs {
@@ -19,8 +21,10 @@ __global__ void fill_zero_kernel(float *p, int64_t n)
 // zeros_bytes: size of the zero region that stands in for an absent h0 (at
 // least B*d floats; a caller that shares one workspace between shapes passes a
 // fixed capacity, so the region never moves onto words another shape wrote).
+// pstate_chunks: saved states along T the state region holds (0: none);
+// lb_tiles: tiles the look-back regions hold (at least this shape's).
 BlockGeom make_geom(int64_t B, int64_t T, int64_t d, int64_t k, int agg_words, int incl_words,
-                    BlkShape shape, bool pstate, size_t zeros_bytes = 0)
+                    BlkShape shape, int64_t pstate_chunks, int64_t lb_tiles, size_t zeros_bytes = 0)
 {
     BlockGeom g{};
     g.T = static_cast<int>(T);
@@ -45,9 +49,9 @@ BlockGeom make_geom(int64_t B, int64_t T, int64_t d, int64_t k, int agg_words, i
     const size_t zb = static_cast<size_t>(B) * d * 4;
     off = align256(off + (zeros_bytes > zb ? zeros_bytes : zb));
     g.off_pstate = off;  // cumulative product: one k x k state per chain per chunk
-    if (pstate) off = align256(off + static_cast<size_t>(g.nTiles) * nch * 32 * k * 4);
-    if (g.nT > 1) {
-        const size_t slots = static_cast<size_t>(g.nTiles) * 32;
+    if (pstate_chunks > 0) off = align256(off + static_cast<size_t>(pstate_chunks) * g.nCG * 32 * k * 4);
+    if (g.nT > 1 || lb_tiles > 0) {
+        const size_t slots = static_cast<size_t>(lb_tiles > g.nTiles ? lb_tiles : g.nTiles) * 32;
         g.off_agg = off;  off = align256(off + slots * agg_words * 8);
         g.off_incl = off; off = align256(off + slots * incl_words * 8);
     }
@@ -68,6 +72,7 @@ BlkArgs base_args(const BlockGeom &g, void *ws)
         a.incl = reinterpret_cast<uint64_t *>(w + g.off_incl);
     }
     a.pstate = reinterpret_cast<float *>(w + g.off_pstate);
+    a.pcs = g.pcs;
     return a;
 }
 
@@ -128,19 +133,31 @@ bool block_k_supported(int64_t k)
 
 BlockGeom block_affine_geometry(int64_t B, int64_t T, int64_t d, int64_t k)
 {
-    return make_geom(B, T, d, k, static_cast<int>(k) + 1, 1, affine_shape(static_cast<int>(k)), false);
+    return make_geom(B, T, d, k, static_cast<int>(k) + 1, 1, affine_shape(static_cast<int>(k)), 0, 0);
 }
 
 BlockGeom block_affine_geometry_fixed_zeros(int64_t B, int64_t T, int64_t d, int64_t k, size_t zeros_bytes)
 {
-    return make_geom(B, T, d, k, static_cast<int>(k) + 1, 1, affine_shape(static_cast<int>(k)), false,
+    return make_geom(B, T, d, k, static_cast<int>(k) + 1, 1, affine_shape(static_cast<int>(k)), 0, 0,
                      zeros_bytes);
 }
 
-BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k)
+// One workspace layout serves both directions of the cumulative product: the
+// saved states (one per backward chunk: the forward writes the state entering
+// every step the backward starts a chunk at) and the look-back regions are
+// sized for the larger of the two tilings, so the forward's and the
+// backward's geometry place every region at the same offset.
+BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k, bool forward)
 {
-    return make_geom(B, T, d, k, 2 * static_cast<int>(k), static_cast<int>(k), matrix_shape(static_cast<int>(k)),
-                     true);
+    const int ki = static_cast<int>(k);
+    const BlockGeom gf = make_geom(B, T, d, k, 2 * ki, ki, matrix_shape(ki, true), 0, 0);
+    const BlockGeom gb = make_geom(B, T, d, k, 2 * ki, ki, matrix_shape(ki, false), 0, 0);
+    const int64_t steps = std::max(static_cast<int64_t>(gf.nT) * gf.TT, static_cast<int64_t>(gb.nT) * gb.TT);
+    const int64_t tiles = (gf.nT > 1 || gb.nT > 1) ? std::max(gf.nTiles, gb.nTiles) : 0;
+    BlockGeom g = make_geom(B, T, d, k, 2 * ki, ki, matrix_shape(ki, forward), (steps + gb.C - 1) / gb.C, tiles);
+    g.pcs = 0;
+    while ((1 << g.pcs) < gb.C) ++g.pcs;   // C is a power of two
+    return g;
 }
 
 hipError_t launch_block_affine_fwd(const BlockGeom &g, const float *A, const float *b,
@@ -197,13 +214,13 @@ hipError_t launch_block_matrix_fwd(const BlockGeom &g, const float *A, float *P,
     return hipGetLastError();
 }
 
-hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const float *dP, float *dA,
-                                   void *ws, bool fwd_state_valid, hipStream_t s)
+hipError_t launch_block_matrix_bwd(const BlockGeom &gf, const BlockGeom &g, const float *A, const float *dP,
+                                   float *dA, void *ws, bool fwd_state_valid, hipStream_t s)
 {
     if (!fwd_state_valid) {
-        BlkArgs f = base_args(g, ws);
+        BlkArgs f = base_args(gf, ws);
         f.A = A; f.out = nullptr;    // chunk states only
-        launch_blk_any(BlkOp::MatrixFwd, g, f, s);
+        launch_blk_any(BlkOp::MatrixFwd, gf, f, s);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -62,13 +62,16 @@ struct BlockGeom {
     size_t off_agg, off_incl, bytes;  // look-back payload (tagged words)
     int agg_words;  // tagged words per chain per tile in the aggregate
     int incl_words; // tagged words per chain per tile in the inclusive prefix
+    int pcs;        // cumulative product: log2 of the steps between the saved states
 };
 
 // block sizes the block ops are built for: k in {1, 2, 4, 8, 16}
 bool block_k_supported(int64_t k);
 
 BlockGeom block_affine_geometry(int64_t B, int64_t T, int64_t d, int64_t k);
-BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k);
+// the cumulative product's geometry for one direction; both directions share
+// one workspace layout (and size)
+BlockGeom block_matrix_geometry(int64_t B, int64_t T, int64_t d, int64_t k, bool forward);
 // the block-affine layout with a zero region of at least zeros_bytes at a fixed
 // offset (for a workspace shared by calls of different shapes)
 BlockGeom block_affine_geometry_fixed_zeros(int64_t B, int64_t T, int64_t d, int64_t k, size_t zeros_bytes);
@@ -85,8 +88,9 @@ hipError_t launch_givens_bwd(const BlockGeom &g, const float *theta, const float
                              float *dh0, void *ws, hipStream_t s);
 hipError_t launch_block_matrix_fwd(const BlockGeom &g, const float *A, float *P, void *ws,
                                    hipStream_t s);
-hipError_t launch_block_matrix_bwd(const BlockGeom &g, const float *A, const float *dP, float *dA,
-                                   void *ws, bool fwd_state_valid, hipStream_t s);
+// gf: the forward's geometry, for the chunk states when they are not valid
+hipError_t launch_block_matrix_bwd(const BlockGeom &gf, const BlockGeom &g, const float *A, const float *dP,
+                                   float *dA, void *ws, bool fwd_state_valid, hipStream_t s);
 
 // ------------------------------------------------------------- delta rule
 struct DeltaGeom {

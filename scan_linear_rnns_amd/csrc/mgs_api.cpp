@@ -462,7 +462,7 @@ mgs_status mgs_block_matrix_scan_workspace_size(int64_t B, int64_t T, int64_t d,
     BlockSizes z;
     if (mgs_status st = check_block_sizes(B, T, d, k, &z)) return st;
     if (z.n == 0) { *bytes = sizeof(mgs::WsHeader); return MGS_OK; }
-    *bytes = mgs::block_matrix_geometry(B, T, d, k).bytes;
+    *bytes = mgs::block_matrix_geometry(B, T, d, k, true).bytes;
     return MGS_OK;
 }
 
@@ -479,7 +479,7 @@ mgs_status mgs_block_matrix_scan_fwd(const float *A, float *P, int64_t B, int64_
     if (!all_aligned(in, 1) || !all_aligned(out, 1)) return MGS_ERR_INVALID_VALUE;
     if (any_alias(in, 1, out, 1)) return MGS_ERR_INVALID_VALUE;
     if (na == 0) return MGS_OK;
-    const mgs::BlockGeom g = mgs::block_matrix_geometry(B, T, d, k);
+    const mgs::BlockGeom g = mgs::block_matrix_geometry(B, T, d, k, true);
     if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
     return hip_status(mgs::launch_block_matrix_fwd(g, A, P, workspace, as_stream(stream)));
 }
@@ -497,9 +497,10 @@ mgs_status mgs_block_matrix_scan_bwd(const float *A, const float *dP, float *dA,
     if (!all_aligned(in, 2) || !all_aligned(out, 1)) return MGS_ERR_INVALID_VALUE;
     if (any_alias(in, 2, out, 1)) return MGS_ERR_INVALID_VALUE;
     if (na == 0) return MGS_OK;
-    const mgs::BlockGeom g = mgs::block_matrix_geometry(B, T, d, k);
+    const mgs::BlockGeom gf = mgs::block_matrix_geometry(B, T, d, k, true);
+    const mgs::BlockGeom g = mgs::block_matrix_geometry(B, T, d, k, false);
     if (mgs_status st = check_workspace(workspace, workspace_bytes, g.bytes)) return st;
-    return hip_status(mgs::launch_block_matrix_bwd(g, A, dP, dA, workspace, fwd_state_valid != 0,
+    return hip_status(mgs::launch_block_matrix_bwd(gf, g, A, dP, dA, workspace, fwd_state_valid != 0,
                                                    as_stream(stream)));
 }
 
