@@ -87,9 +87,15 @@ struct BlkArgs {
 struct BlkShape {
     int W, max_c;
 };
+// k = 16 block-affine: eight-step chunks (up to 234 VGPRs) make the long-T
+// workload one generation of 256 tiles (two of 512 with four-step chunks:
+// 94.9 -> 83.8 us for the pair)
+#ifndef MGS_AFF16_MAXC
+#define MGS_AFF16_MAXC 8
+#endif
 constexpr BlkShape affine_shape(int k)
 {
-    return k == 8 ? BlkShape{MGS_AFF_W, MGS_AFF_MAXC} : k == 16 ? BlkShape{8, 4} : BlkShape{8, 8};
+    return k == 8 ? BlkShape{MGS_AFF_W, MGS_AFF_MAXC} : k == 16 ? BlkShape{8, MGS_AFF16_MAXC} : BlkShape{8, 8};
 }
 // The cumulative product's forward and backward may tile T differently: the
 // forward saves the state entering every step the backward starts a chunk at.
