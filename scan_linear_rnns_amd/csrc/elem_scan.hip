@@ -43,6 +43,12 @@
 namespace mgs {
 namespace {
 
+// tiles a look-back batch polls at once (measured at the long-T shape, 8
+// tiles along T: 4 beats 8 by ~0.2 us per kernel, 16 is ~0.6 us slower)
+#ifndef MGS_ELEM_LB
+#define MGS_ELEM_LB 4
+#endif
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kInf = __builtin_inff();
 
@@ -250,6 +256,8 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
     constexpr int TT = NCH * C;
     __shared__ float sLA[NCH][CHW];
     __shared__ float sLH[NCH][CHW];
+    __shared__ float sPA[MULTI ? NCH : 1][CHW];   // multi-tile: the tile's chunks [0, q) composed
+    __shared__ float sPH[MULTI ? NCH : 1][CHW];
     __shared__ float sCarry[CHW];
     __shared__ uint32_t sTicket[2];
 
@@ -303,9 +311,13 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
     float carry;
     if constexpr (MULTI) {
         if (threadIdx.x < CHW) {
-            float TA = Alg::idA(), TH = Alg::idH();   // tile aggregate
+            float TA = Alg::idA(), TH = Alg::idH();   // tile aggregate, and each chunk's prefix
 #pragma unroll
-            for (int p = 0; p < NCH; ++p) Alg::combine(TA, TH, sLA[p][ch], sLH[p][ch], TA, TH);
+            for (int p = 0; p < NCH; ++p) {
+                sPA[p][ch] = TA;
+                sPH[p][ch] = TH;
+                Alg::combine(TA, TH, sLA[p][ch], sLH[p][ch], TA, TH);
+            }
             const size_t slot = static_cast<size_t>(tile) * CHW + ch;
             if (j < a.nT - 1) {
                 tagged_store(&a.agg_a[slot], tag, TA);
@@ -321,7 +333,7 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
                 // tile publishes its aggregate, so a walk that reaches the start
                 // of the sequence ends there with the known h0: no tile ever
                 // waits for another tile's look-back to finish.
-                constexpr int LB = 8;
+                constexpr int LB = MGS_ELEM_LB;
                 float accA = Alg::idA(), accH = Alg::idH(), basev = lh0;
                 int p0 = j - 1;
                 for (uint32_t spin = 0;;) {
@@ -378,10 +390,14 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
 
     if (a.h == nullptr) return;
 
-    // carry into this lane's chunk, then the fix-up (log space: written as
+    // carry into this lane's chunk (multi-tile: one composed prefix; else the
+    // chunks before it one by one), then the fix-up (log space: written as
     // h_t = 2^(LA_t + carry) + 2^(LH_t))
     float cq = carry;
-    for (int p = 0; p < q; ++p) cq = Alg::apply(sLA[p][ch], sLH[p][ch], cq);
+    if constexpr (MULTI)
+        cq = Alg::apply(sPA[q][ch], sPH[q][ch], carry);
+    else
+        for (int p = 0; p < q; ++p) cq = Alg::apply(sLA[p][ch], sLH[p][ch], cq);
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int t = t0 + i;
@@ -487,7 +503,7 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
                 // look-back over the later tiles, nearest first (acc composes
                 // tiles j+1 .. p-1), LB tiles per batch of loads; a walk that
                 // passes the last tile ends there (w = 0 beyond the end)
-                constexpr int LB = 8;
+                constexpr int LB = MGS_ELEM_LB;
                 float accP = 1.0f, accW = 0.0f, basev = 0.0f;
                 int p0 = j + 1;
                 for (uint32_t spin = 0;;) {
@@ -540,7 +556,10 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
         wcarry = 0.0f;
     }
 
-    // state entering this chunk (forward) and w entering it from the right
+    // state entering this chunk (forward) and w entering it from the right.
+    // These stay per-lane folds of linear maps: storing composed prefixes in
+    // wave 0's fold, ahead of its look-back, cost the backward more (log
+    // space, long T: +0.15-0.3 us) than the folds take.
     float hc = hin;
     for (int p = 0; p < q; ++p) hc = sA[p][ch] * hc + sH[p][ch];
     float wc = wcarry;
