@@ -99,21 +99,29 @@ constexpr BlkShape affine_shape(int k)
 }
 // The cumulative product's forward and backward may tile T differently: the
 // forward saves the state entering every step the backward starts a chunk at.
-// k = 16: the backward keeps three 16-float rows per step and its reverse
-// aggregate is two 16 x 16 rows per lane, so it runs four waves of two-step
-// chunks (LDS buffers at 68 KB); the forward keeps one row per step and runs
-// eight waves of eight-step chunks, whose 128-step tiles fit the long-T
-// workload into one workgroup per compute unit.
+// k = 16: the backward's reverse aggregate is two 16 x 16 rows per lane, so it
+// runs four waves (LDS buffers at 68 KB, two workgroups per compute unit) of
+// four-step chunks, reading its dP rows a second time in the fix-up to stay
+// within 256 registers; the forward keeps one row per step and runs eight
+// waves of eight-step chunks, whose 128-step tiles fit the long-T workload
+// into one workgroup per compute unit.
 #ifndef MGS_MAT16_FWD_W
 #define MGS_MAT16_FWD_W 8
 #endif
 #ifndef MGS_MAT16_FWD_MAXC
 #define MGS_MAT16_FWD_MAXC 8
 #endif
+#ifndef MGS_MAT16_BWD_W
+#define MGS_MAT16_BWD_W 4
+#endif
+#ifndef MGS_MAT16_BWD_MAXC
+#define MGS_MAT16_BWD_MAXC 4
+#endif
 constexpr BlkShape matrix_shape(int k, bool forward)
 {
     return k == 8    ? BlkShape{MGS_MAT_W, MGS_MAT_MAXC}
-           : k == 16 ? (forward ? BlkShape{MGS_MAT16_FWD_W, MGS_MAT16_FWD_MAXC} : BlkShape{4, 2})
+           : k == 16 ? (forward ? BlkShape{MGS_MAT16_FWD_W, MGS_MAT16_FWD_MAXC}
+                                : BlkShape{MGS_MAT16_BWD_W, MGS_MAT16_BWD_MAXC})
                      : BlkShape{8, 8};
 }
 
@@ -2033,6 +2041,21 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
         }
         recompute();
     }
+    // k = 16 with four or more steps per lane: the dP rows are read again
+    // here (from L2 or the Infinity Cache) rather than held across the tree
+    // and the look-back, which keeps the kernel within 256 registers; the
+    // reads overlap tree_apply
+    constexpr bool kReload = K == 16 && C >= 4;
+    float Gd[kReload ? C : 1][K];
+    if constexpr (kReload) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            Rw::load_row(a.y + tl.ablk0 + clampT(tl.t0 + i, a.T) * tl.astep, tl.v, Gd[i]);
+            if (!(tl.cv && tl.t0 + i < a.T))
+#pragma unroll
+                for (int s = 0; s < K; ++s) Gd[i][s] = 0.0f;
+        }
+    }
     tree_apply<kMatMat, K, NCH, -1>(nodes, tl, Wc);   // carry entering the chunk from its end
 
 #pragma unroll
@@ -2041,7 +2064,7 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
         const bool valid = tl.cv && t < a.T;
         float G[K], dAr[K], nw[K];
 #pragma unroll
-        for (int s = 0; s < K; ++s) G[s] = Gr[i][s] + Wc[s];
+        for (int s = 0; s < K; ++s) G[s] = (kReload ? Gd[i][s] : Gr[i][s]) + Wc[s];
         Rw::mm(G, PT[i], dAr);           // dA_t = G_t P_{t-1}^T
         Rw::mm(ATr[i], G, nw);
 #pragma unroll
