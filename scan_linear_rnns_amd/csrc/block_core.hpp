@@ -2041,11 +2041,12 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
         }
         recompute();
     }
-    // k = 16 with four or more steps per lane: the dP rows are read again
-    // here (from L2 or the Infinity Cache) rather than held across the tree
-    // and the look-back, which keeps the kernel within 256 registers; the
-    // reads overlap tree_apply
-    constexpr bool kReload = K == 16 && C >= 4;
+    // With 8 x 8 rows and eight steps per lane, or 16 x 16 rows and four, the
+    // dP rows are read again here (from L2 or the Infinity Cache) rather than
+    // held across the tree and the look-back: k = 16 fits 256 registers (308
+    // otherwise), k = 8 no longer spills (7 registers otherwise; backward 37.4
+    // -> 35.6 us at the long-T shape).  The reads overlap tree_apply.
+    constexpr bool kReload = (K == 16 && C >= 4) || (K == 8 && C >= 8);
     float Gd[kReload ? C : 1][K];
     if constexpr (kReload) {
 #pragma unroll
