@@ -61,7 +61,8 @@ def test_blocksize_configs(gpu, name, B, T, d, k):
 EDGES = [(1, 1, 1, 1), (3, 7, 3, 1), (2, 300, 37, 1), (1, 2048, 5, 1),
          (1, 1, 2, 2), (3, 65, 6, 2), (2, 129, 34, 2),
          (1, 2, 4, 4), (3, 63, 12, 4), (2, 300, 20, 4), (1, 1000, 4, 4),
-         (1, 1, 16, 16), (3, 7, 16, 16), (2, 65, 48, 16), (1, 300, 32, 16), (1, 1000, 16, 16)]
+         (1, 1, 16, 16), (3, 7, 16, 16), (2, 12, 32, 16), (2, 65, 48, 16), (1, 200, 16, 16), (1, 300, 32, 16),
+         (1, 1000, 16, 16)]
 
 
 @pytest.mark.parametrize("B,T,d,k", EDGES)
@@ -71,7 +72,11 @@ def test_blocksize_edges(gpu, B, T, d, k):
     check(out, ref)
 
 
-@pytest.mark.parametrize("k,B,T,d", [(1, 2, 7, 3), (2, 4, 1024, 64), (4, 3, 300, 12), (16, 2, 1024, 32)])
+# k = 16: the forward and the backward tile T differently (forward chunks of up
+# to 8 steps, backward chunks of up to 4; T = 12 gives a backward chunk longer
+# than the forward's, T = 200 a two-tile forward saving states inside its chunks)
+@pytest.mark.parametrize("k,B,T,d", [(1, 2, 7, 3), (2, 4, 1024, 64), (4, 3, 300, 12), (16, 2, 1024, 32),
+                                     (16, 2, 12, 32), (16, 1, 200, 16)])
 def test_blocksize_matrix_bwd_without_forward_state(gpu, k, B, T, d):
     """A fresh workspace: the backward recomputes the chunk states itself and
     gives the oracle's dA, bit for bit the same as with the forward's states."""
