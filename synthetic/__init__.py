@@ -31,6 +31,14 @@ once to float32 at the end):
   ... < k-1; layers are applied in order (R = L_{k-1} ... L_0) and angles are
   consumed in (layer, pair) order.  Each rotation maps (x_i, x_j) to
   (cos t x_i - sin t x_j, sin t x_i + cos t x_j).  h0 = 0.
+
+Tensors at the boundary's size limit (2^31 - 1 elements) are too large to draw
+on the host, so device_log_inputs / device_block_inputs draw them on a GPU with
+torch's seeded generator (Philox), one batch slice at a time, with the same
+distributions: the log-space recipe above evaluated in float32; for the block
+scans A_t = sigmoid(s_t) Q where Q is picked uniformly from a bank of 4096
+Givens meshes R(theta) (theta ~ U(-pi, pi), numpy seed) and s, b, dh, dP are
+N(0,1).
 """
 from __future__ import annotations
 
@@ -230,3 +238,83 @@ CONFIGS = {
     "delta_lab":   dict(op="delta", B=128, T=64, d=64),
     "delta_longT": dict(op="delta", B=16, T=1024, d=64),
 }
+
+
+# ------------------------------------------------ inputs drawn on a device
+
+def _device_gen(device, seed):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _slices(B, per_item, limit=1 << 27):
+    """Batch ranges of at most `limit` elements (at least one item each)."""
+    n = max(1, limit // max(1, per_item))
+    return [(i, min(B, i + n)) for i in range(0, B, n)]
+
+
+def _log_g_t(x):
+    import torch
+    import torch.nn.functional as F
+    return torch.where(x >= 0, torch.log(x.clamp_min(0) + 0.5), -F.softplus(-x))
+
+
+def device_log_inputs(B: int, T: int, d: int, device, seed: int = 0):
+    """(log_a, log_b, log_h0, dh) as float32 tensors on `device` (the log-space
+    recipe in float32, drawn a batch slice at a time to bound temporaries)."""
+    import torch
+    import torch.nn.functional as F
+    g = _device_gen(device, seed)
+    f32 = dict(dtype=torch.float32, device=device)
+    la = torch.empty((B, T, d), **f32)
+    lb = torch.empty((B, T, d), **f32)
+    dh = torch.empty((B, T, d), **f32)
+    for i, j in _slices(B, T * d):
+        k = torch.randn((j - i, T, d), generator=g, **f32)
+        la[i:j] = -F.softplus(k)
+        lb[i:j] = -F.softplus(k.neg_())
+        del k
+        x = torch.randn((j - i, T, d), generator=g, **f32)
+        lb[i:j] += _log_g_t(x)
+        del x
+    lh0 = _log_g_t(torch.randn((B, d), generator=g, **f32))
+    for i, j in _slices(B, T * d):
+        dh[i:j] = torch.randn((j - i, T, d), generator=g, **f32)
+    return la, lb, lh0, dh
+
+
+def mesh_bank(n: int, k: int, seed: int = 0) -> np.ndarray:
+    """n Givens meshes R(theta), theta ~ U(-pi, pi): (n, k, k) float32."""
+    rng = np.random.default_rng(seed)
+    theta = rng.uniform(-math.pi, math.pi, (n, n_angles(k)))
+    return givens_mesh(theta, k).astype(np.float32)
+
+
+def device_block_inputs(B: int, T: int, d: int, k: int, device, seed: int = 0, *, with_b: bool = True,
+                        with_dh: bool = True, with_dP: bool = False):
+    """dict of float32 tensors on `device`: A (B,T,d/k,k,k) = sigmoid(s) Q_idx
+    (Q from mesh_bank(4096, k, seed)) and, as asked, b and dh (B,T,d) and dP
+    (like A), all N(0,1); drawn a batch slice at a time."""
+    import torch
+    assert d % k == 0
+    nb = d // k
+    g = _device_gen(device, seed)
+    f32 = dict(dtype=torch.float32, device=device)
+    bank = torch.from_numpy(mesh_bank(4096, k, seed)).to(device)
+    A = torch.empty((B, T, nb, k, k), **f32)
+    for i, j in _slices(B, T * d * k):
+        idx = torch.randint(0, bank.shape[0], (j - i, T, nb), generator=g, device=device)
+        s = torch.sigmoid(torch.randn((j - i, T, nb), generator=g, **f32))
+        torch.mul(bank[idx], s[..., None, None], out=A[i:j])
+        del idx, s
+    out = dict(A=A)
+    for name, want, shape in (("b", with_b, (T, d)), ("dh", with_dh, (T, d)), ("dP", with_dP, (T, nb, k, k))):
+        if not want:
+            continue
+        x = torch.empty((B,) + shape, **f32)
+        for i, j in _slices(B, math.prod(shape)):
+            x[i:j] = torch.randn((j - i,) + shape, generator=g, **f32)
+        out[name] = x
+    return out
