@@ -1397,15 +1397,21 @@ __device__ __forceinline__ void publish_wm(uint64_t *dst, int tile, int slot, ui
 // are few, else whole waves whose halves split the words -- each poll one
 // predecessor (the nearest units in the scan direction: earlier tiles for
 // DIR = +1, later ones for DIR = -1) for its inclusive state and its
-// aggregate in one batch of loads, and stage what they find in LDS.  Wave 0
-// then walks from the nearest predecessor: it stops at the first published
-// inclusive state (or past the end of the sequence, whose state base0 is
-// known) and applies the aggregates of the tiles passed on the way.  A tile
-// that shows neither, or a window without an inclusive state that does not
-// reach the end of the sequence, means another round.  `overlap` runs once on
-// every wave while the first round's loads are in flight (wave 0: after the
-// walk).  Leaves the state entering the tile in c (every lane, its slot) and
-// publishes the tile's inclusive state when publish_incl.
+// aggregate in one batch of loads, and stage what they find in LDS.  In the
+// first round a half-wave unit polls again, back to back, until its
+// predecessor shows its aggregate or its inclusive state: every tile
+// publishes its aggregate right after its own tree, waiting on no other tile,
+// so this wait ends, and the round then needs one barrier instead of a
+// barrier round trip per poll.
+// Wave 0 then reads every unit's status at once and walks from the nearest
+// predecessor: it stops at the first published inclusive state (or past the
+// end of the sequence, whose state base0 is known) and applies the
+// aggregates of the tiles passed on the way.  A window without an inclusive
+// state that does not reach the end of the sequence means another round
+// (one poll per unit).  `overlap` runs once on every wave while the first
+// poll's loads are in flight (wave 0: after the walk).  Leaves the state
+// entering the tile in c (every lane, its slot) and publishes the tile's
+// inclusive state when publish_incl.
 template <int KIND, int K, int W, int DIR, typename F>
 __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl, int ftile, uint32_t tag,
                                                const float *X, const float *base0, bool publish_incl,
@@ -1417,7 +1423,7 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
     constexpr int NU = HALF ? 2 * (W - 1) : W - 1;
     constexpr int PER = HALF ? NWD : (NWD + 1) / 2;   // words one lane loads
     constexpr int SW = NWD | 1;
-    static_assert(NU > 0, "the look-back needs more than one wave");
+    static_assert(NU > 0 && NU < 64, "the look-back needs more than one wave");
     // staging: the tree's dead nodes when they hold it (first written only
     // after a barrier that follows the tree's last reads), else an array of
     // its own
@@ -1442,23 +1448,31 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
             const size_t ti = static_cast<size_t>(in ? p : tl.j) * a.nCG + tl.cg;
             const int e0 = HALF ? 0 : tl.sub * PER;
             uint64_t wd[PER];
+            bool rI, rA;
+            for (uint32_t n = 0;; ++n) {
 #pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const int e = e0 + i < NWD ? e0 + i : NWD - 1;
-                wd[i] = e < CW ? tagged_load(a.incl + (ti * CW + e) * 32 + tl.slot)
-                               : tagged_load(a.agg + (ti * AW + (e - CW)) * 32 + tl.slot);
-            }
-            if (spin == 0) overlap();
-            bool okI = true, okA = true;
+                for (int i = 0; i < PER; ++i) {
+                    const int e = e0 + i < NWD ? e0 + i : NWD - 1;
+                    wd[i] = e < CW ? tagged_load(a.incl + (ti * CW + e) * 32 + tl.slot)
+                                   : tagged_load(a.agg + (ti * AW + (e - CW)) * 32 + tl.slot);
+                }
+                if (spin == 0 && n == 0) overlap();
+                bool okI = true, okA = true;
 #pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const int e = e0 + i;
-                if (e < CW) okI = okI && tag_is(wd[i], tag);
-                else if (e < NWD) okA = okA && tag_is(wd[i], tag);
+                for (int i = 0; i < PER; ++i) {
+                    const int e = e0 + i;
+                    if (e < CW) okI = okI && tag_is(wd[i], tag);
+                    else if (e < NWD) okA = okA && tag_is(wd[i], tag);
+                }
+                const uint64_t bI = __ballot(okI), bA = __ballot(okA);
+                rI = HALF ? static_cast<uint32_t>(bI >> (32 * tl.sub)) == 0xFFFFFFFFu : bI == ~0ull;
+                rA = HALF ? static_cast<uint32_t>(bA >> (32 * tl.sub)) == 0xFFFFFFFFu : bA == ~0ull;
+                // first round: again while a unit of this wave sees neither
+                // (half-wave units; a whole-wave unit's loop would hold its
+                // word addresses in registers the larger tiles do not have)
+                const bool again = HALF && spin == 0 && in && !rI && !rA && n < kSpinLimit;
+                if (__ballot(again) == 0) break;
             }
-            const uint64_t bI = __ballot(okI), bA = __ballot(okA);
-            const bool rI = HALF ? static_cast<uint32_t>(bI >> (32 * tl.sub)) == 0xFFFFFFFFu : bI == ~0ull;
-            const bool rA = HALF ? static_cast<uint32_t>(bA >> (32 * tl.sub)) == 0xFFFFFFFFu : bA == ~0ull;
             if (ALIAS && spin == 0) lds_barrier();   // the tree's last level has read the dead nodes
 #pragma unroll
             for (int i = 0; i < PER; ++i)
@@ -1469,20 +1483,38 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
         }
         lds_barrier();
         if (tl.wv == 0) {
-            // nearest first: 4 = past the end of the sequence, 2 = inclusive, 1 = aggregate
-            int stop = -1;
-            bool ok = true;
-            for (int u = 0; u < NU; ++u) {
-                const int st = sStat[u];
-                if (st & 6) { stop = u; break; }
-                if (!(st & 1)) { ok = false; break; }
-            }
-            ok = ok && stop >= 0;
+            // every unit's status at once (4 = past the end of the sequence,
+            // 2 = inclusive, 1 = aggregate); stop at the nearest unit showing
+            // an inclusive state or the end, every nearer one an aggregate
+            const int st = tl.lane < NU ? sStat[tl.lane] : 0;
+            const uint64_t mStop = __ballot((st & 6) != 0), mAgg = __ballot((st & 1) != 0);
+            const uint64_t mEnd = __ballot((st & 4) != 0);
+            const int stop = mStop ? static_cast<int>(__builtin_ctzll(mStop)) : -1;
+            const bool ok = stop >= 0 && ((~mAgg) & ((1ull << stop) - 1)) == 0;
             if (ok) {
-                if (!(sStat[stop] & 4))
+                if (!((mEnd >> stop) & 1))
 #pragma unroll
                     for (int e = 0; e < CW; ++e) c[e] = sLB[stop][tl.slot][e];
-                for (int u = stop - 1; u >= 0; --u) Cr::apply(&sLB[u][tl.slot][CW], c);
+                // the aggregates from the farthest to the nearest; a
+                // matrix-vector aggregate is read from LDS one step ahead of
+                // its use (the larger ones would not fit the registers)
+                if constexpr (KIND == kMatVec) {
+                    float g[AW];
+                    if (stop > 0)
+#pragma unroll
+                        for (int e = 0; e < AW; ++e) g[e] = sLB[stop - 1][tl.slot][CW + e];
+                    for (int u = stop - 1; u >= 0; --u) {
+                        float gn[AW];
+                        if (u > 0)
+#pragma unroll
+                            for (int e = 0; e < AW; ++e) gn[e] = sLB[u - 1][tl.slot][CW + e];
+                        Cr::apply(g, c);
+#pragma unroll
+                        for (int e = 0; e < AW; ++e) g[e] = gn[e];
+                    }
+                } else {
+                    for (int u = stop - 1; u >= 0; --u) Cr::apply(&sLB[u][tl.slot][CW], c);
+                }
                 if (tl.sub == 0)
 #pragma unroll
                     for (int e = 0; e < CW; ++e) sCar[tl.slot][e] = c[e];
