@@ -1424,6 +1424,7 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
     constexpr int PER = HALF ? NWD : (NWD + 1) / 2;   // words one lane loads
     constexpr int SW = NWD | 1;
     static_assert(NU > 0 && NU < 64, "the look-back needs more than one wave");
+    static_assert(HALF || (NWD % 2 == 0 && PER >= CW), "whole-wave units split the words evenly");
     // staging: the tree's dead nodes when they hold it (first written only
     // after a barrier that follows the tree's last reads), else an array of
     // its own
@@ -1446,30 +1447,35 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
             const int p = tl.j - DIR * (1 + u);
             const bool in = p >= 0 && p < a.nT;
             const size_t ti = static_cast<size_t>(in ? p : tl.j) * a.nCG + tl.cg;
-            const int e0 = HALF ? 0 : tl.sub * PER;
+            // this lane's words e0 .. e0 + PER - 1 of the predecessor's CW
+            // inclusive then AW aggregate words (HALF: all of them): two base
+            // pointers and constant offsets, so the polling loop holds no
+            // per-word addresses
+            const bool lower = HALF || tl.sub == 0;
+            const int e0 = lower ? 0 : PER;
+            const uint64_t *wI = a.incl + ti * CW * 32 + tl.slot;
+            const uint64_t *wA = a.agg + ti * AW * 32 + tl.slot;
+            const uint64_t *p0 = lower ? wI : wA + (PER - CW) * 32;   // the lane's words i < CW
+            const uint64_t *p1 = lower ? wA : wA + PER * 32;          // and i >= CW
             uint64_t wd[PER];
             bool rI, rA;
             for (uint32_t n = 0;; ++n) {
 #pragma unroll
-                for (int i = 0; i < PER; ++i) {
-                    const int e = e0 + i < NWD ? e0 + i : NWD - 1;
-                    wd[i] = e < CW ? tagged_load(a.incl + (ti * CW + e) * 32 + tl.slot)
-                                   : tagged_load(a.agg + (ti * AW + (e - CW)) * 32 + tl.slot);
-                }
+                for (int i = 0; i < PER; ++i) wd[i] = tagged_load(i < CW ? p0 + i * 32 : p1 + (i - CW) * 32);
                 if (spin == 0 && n == 0) overlap();
                 bool okI = true, okA = true;
 #pragma unroll
                 for (int i = 0; i < PER; ++i) {
-                    const int e = e0 + i;
-                    if (e < CW) okI = okI && tag_is(wd[i], tag);
-                    else if (e < NWD) okA = okA && tag_is(wd[i], tag);
+                    if (lower && i < CW) okI = okI && tag_is(wd[i], tag);
+                    else if (e0 + i < NWD) okA = okA && tag_is(wd[i], tag);
                 }
                 const uint64_t bI = __ballot(okI), bA = __ballot(okA);
                 rI = HALF ? static_cast<uint32_t>(bI >> (32 * tl.sub)) == 0xFFFFFFFFu : bI == ~0ull;
                 rA = HALF ? static_cast<uint32_t>(bA >> (32 * tl.sub)) == 0xFFFFFFFFu : bA == ~0ull;
                 // first round: again while a unit of this wave sees neither
-                // (half-wave units; a whole-wave unit's loop would hold its
-                // word addresses in registers the larger tiles do not have)
+                // (half-wave units: whole-wave ones, with twice the words per
+                // poll, measured slower when they spun -- k = 16 block-affine
+                // pair 79.2 -> 83.0 us)
                 const bool again = HALF && spin == 0 && in && !rI && !rA && n < kSpinLimit;
                 if (__ballot(again) == 0) break;
             }
