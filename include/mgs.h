@@ -101,6 +101,17 @@ int mgs_last_hip_error(void);
  * library. */
 mgs_status mgs_workspace_check(void *workspace, void *stream, int *flags);
 
+/* For tests of the failure path, not for production use: sets two fields of
+ * the workspace's header (synchronously, on `stream`).  spin_limit is the
+ * number of polls after which a cross-workgroup wait gives up (0 restores the
+ * built-in 2^20).  fail_waits != 0 makes every such wait expect a launch tag
+ * that no launch publishes, so each wait runs to the limit, the kernels still
+ * exit, and mgs_workspace_check then reports bit 0; results of calls made
+ * meanwhile are invalid.  mgs_workspace_set_waits(ws, 0, 0, s) restores
+ * normal operation (a zero-filled workspace starts there).  No effect on the
+ * allocation-free entry point, which has no workspace argument. */
+mgs_status mgs_workspace_set_waits(void *workspace, unsigned spin_limit, int fail_waits, void *stream);
+
 /* ------------------------------------------------------ log-space scan --- */
 /*
  * Forward (minGRU home page, introduction: the log-space MinGRU with Heinsen's

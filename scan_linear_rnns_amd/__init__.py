@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import MgsError, check, declared_functions, load, status_string  # noqa: F401
 
 __all__ = [
-    "MgsError", "load", "workspace", "mgs_workspace_check",
+    "MgsError", "load", "workspace", "mgs_workspace_check", "mgs_workspace_set_waits",
     "mgs_scan_log_workspace_size", "mgs_scan_log_fwd", "mgs_scan_log_bwd",
     "mgs_scan_mingru_workspace_size", "mgs_scan_mingru_fwd", "mgs_scan_mingru_bwd",
     "mgs_scan_linear_workspace_size", "mgs_scan_linear_fwd", "mgs_scan_linear_bwd",
@@ -99,6 +99,13 @@ def mgs_workspace_check(ws, stream=None):
     flags = ctypes.c_int(0)
     check(load().mgs_workspace_check(_ptr(ws), _stream(stream), ctypes.byref(flags)), "mgs_workspace_check")
     return int(flags.value)
+
+
+def mgs_workspace_set_waits(ws, spin_limit=0, fail_waits=False, stream=None):
+    """Failure-path test hook: the look-back waits' poll limit (0 = built-in) and,
+    with fail_waits, waits that can never succeed (results then invalid)."""
+    check(load().mgs_workspace_set_waits(_ptr(ws), int(spin_limit), int(bool(fail_waits)), _stream(stream)),
+          "mgs_workspace_set_waits")
 
 
 # --------------------------------------------------------------- log scan

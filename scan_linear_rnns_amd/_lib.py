@@ -24,6 +24,7 @@ SIGNATURES = {
     "mgs_status_string": ([_INT], ctypes.c_char_p),
     "mgs_last_hip_error": ([], _INT),
     "mgs_workspace_check": ([_P, _P, ctypes.POINTER(_INT)], _INT),
+    "mgs_workspace_set_waits": ([_P, ctypes.c_uint, _INT, _P], _INT),
     "mgs_scan_log_workspace_size": ([_I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),
     "mgs_scan_log_fwd": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P], _INT),
     "mgs_scan_log_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _INT, _P], _INT),

@@ -1441,6 +1441,7 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
     __shared__ int sDone;
 #pragma unroll
     for (int e = 0; e < CW; ++e) c[e] = base0[e];
+    const uint32_t want = wait_tag(a.hd, tag), limit = wait_limit(a.hd);
     for (uint32_t spin = 0;; ++spin) {
         if (tl.wv > 0) {
             const int u = HALF ? 2 * (tl.wv - 1) + tl.sub : tl.wv - 1;
@@ -1466,8 +1467,8 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
                 bool okI = true, okA = true;
 #pragma unroll
                 for (int i = 0; i < PER; ++i) {
-                    if (lower && i < CW) okI = okI && tag_is(wd[i], tag);
-                    else if (e0 + i < NWD) okA = okA && tag_is(wd[i], tag);
+                    if (lower && i < CW) okI = okI && tag_is(wd[i], want);
+                    else if (e0 + i < NWD) okA = okA && tag_is(wd[i], want);
                 }
                 const uint64_t bI = __ballot(okI), bA = __ballot(okA);
                 rI = HALF ? static_cast<uint32_t>(bI >> (32 * tl.sub)) == 0xFFFFFFFFu : bI == ~0ull;
@@ -1476,7 +1477,7 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
                 // (half-wave units: whole-wave ones, with twice the words per
                 // poll, measured slower when they spun -- k = 16 block-affine
                 // pair 79.2 -> 83.0 us)
-                const bool again = HALF && spin == 0 && in && !rI && !rA && n < kSpinLimit;
+                const bool again = HALF && spin == 0 && in && !rI && !rA && n < limit;
                 if (__ballot(again) == 0) break;
             }
             if (ALIAS && spin == 0) lds_barrier();   // the tree's last level has read the dead nodes
@@ -1529,7 +1530,7 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
         }
         lds_barrier();
         if (sDone) break;
-        if (spin >= kSpinLimit) {
+        if (spin >= limit) {
             if (threadIdx.x == 0) raise_error(&a.hd->err, kErrSpin);
             if (tl.wv == 0 && tl.sub == 0)
 #pragma unroll

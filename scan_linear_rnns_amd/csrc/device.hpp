@@ -27,12 +27,31 @@ constexpr uint32_t kSpinLimit = 1u << 20; // polls (each a memory round trip plu
 // tile indices from `count` and its tag from `epoch`, so tags differ between
 // any two launches on one workspace -- also between replays of a captured
 // graph -- and never equal 0 (the value of a zero-filled workspace).
+// `spin_limit` and `fail_waits` are set by the host (0 in normal use) for
+// tests of the failure path: a wait gives up after spin_limit polls (0: the
+// built-in kSpinLimit), and with fail_waits every wait expects kNeverTag,
+// which no launch publishes, so each one runs to its limit.
 struct WsHeader {
     unsigned long long ticket;
     uint32_t err;
-    uint32_t pad[61];
+    uint32_t spin_limit;
+    uint32_t fail_waits;
+    uint32_t pad[59];
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
+constexpr uint32_t kNeverTag = 0xFFFFFFFFu;   // launch tags are 1 .. 2^32 - 2
+
+// The polls' limit and the tag they wait for, from the header's host-set fields.
+__device__ __forceinline__ uint32_t wait_limit(const WsHeader *hd)
+{
+    const uint32_t l = hd->spin_limit;
+    return l ? l : kSpinLimit;
+}
+
+__device__ __forceinline__ uint32_t wait_tag(const WsHeader *hd, uint32_t tag)
+{
+    return hd->fail_waits ? kNeverTag : tag;
+}
 
 // Output stores.  Every output element (and every chunk state a forward saves
 // for its backward) is written exactly once and never read back by the kernel

@@ -336,6 +336,7 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
                 constexpr int LB = MGS_ELEM_LB;
                 float accA = Alg::idA(), accH = Alg::idH(), basev = lh0;
                 int p0 = j - 1;
+                const uint32_t want = wait_tag(a.hd, tag), limit = wait_limit(a.hd);
                 for (uint32_t spin = 0;;) {
                     uint64_t wi[LB], wa[LB], wh[LB];
 #pragma unroll
@@ -354,10 +355,10 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
                         if (stop) continue;
                         if (p < 0) {
                             done = stop = true;          // reached the start: base is h0
-                        } else if (tag_is(wi[u], tag)) {
+                        } else if (tag_is(wi[u], want)) {
                             basev = tag_value(wi[u]);
                             done = stop = true;
-                        } else if (tag_is(wa[u], tag) && tag_is(wh[u], tag)) {
+                        } else if (tag_is(wa[u], want) && tag_is(wh[u], want)) {
                             // tile p's aggregate, then the tiles after it
                             Alg::combine(tag_value(wa[u]), tag_value(wh[u]), accA, accH, accA, accH);
                             adv = u + 1;
@@ -368,7 +369,7 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
                     if (done) break;
                     p0 -= adv;
                     if (adv == 0) {
-                        if (++spin >= kSpinLimit) {
+                        if (++spin >= limit) {
                             raise_error(&a.hd->err, kErrSpin);
                             break;
                         }
@@ -506,6 +507,7 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
                 constexpr int LB = MGS_ELEM_LB;
                 float accP = 1.0f, accW = 0.0f, basev = 0.0f;
                 int p0 = j + 1;
+                const uint32_t want = wait_tag(a.hd, tag), limit = wait_limit(a.hd);
                 for (uint32_t spin = 0;;) {
                     uint64_t wi[LB], wp[LB], ww[LB];
 #pragma unroll
@@ -524,10 +526,10 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
                         if (stop) continue;
                         if (p >= a.nT) {
                             done = stop = true;          // past the last tile: base is 0
-                        } else if (tag_is(wi[u], tag)) {
+                        } else if (tag_is(wi[u], want)) {
                             basev = tag_value(wi[u]);
                             done = stop = true;
-                        } else if (tag_is(wp[u], tag) && tag_is(ww[u], tag)) {
+                        } else if (tag_is(wp[u], want) && tag_is(ww[u], want)) {
                             accW = accW + accP * tag_value(ww[u]);
                             accP = accP * tag_value(wp[u]);
                             adv = u + 1;
@@ -538,7 +540,7 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
                     if (done) break;
                     p0 += adv;
                     if (adv == 0) {
-                        if (++spin >= kSpinLimit) {
+                        if (++spin >= limit) {
                             raise_error(&a.hd->err, kErrSpin);
                             break;
                         }

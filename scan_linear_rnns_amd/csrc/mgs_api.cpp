@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdint>
 #include <cstring>
 #include <initializer_list>
@@ -173,6 +174,18 @@ mgs_status mgs_workspace_check(void *workspace, void *stream, int *flags)
         if (e != hipSuccess) return hip_status(e);
     }
     return MGS_OK;
+}
+
+mgs_status mgs_workspace_set_waits(void *workspace, unsigned spin_limit, int fail_waits, void *stream)
+{
+    if (!workspace) return MGS_ERR_INVALID_VALUE;
+    hipStream_t s = as_stream(stream);
+    mgs::WsHeader *hd = static_cast<mgs::WsHeader *>(workspace);
+    const uint32_t v[2] = {static_cast<uint32_t>(spin_limit), fail_waits ? 1u : 0u};
+    static_assert(offsetof(mgs::WsHeader, fail_waits) == offsetof(mgs::WsHeader, spin_limit) + 4, "header layout");
+    hipError_t e = hipMemcpyAsync(&hd->spin_limit, v, sizeof(v), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e == hipSuccess ? MGS_OK : hip_status(e);
 }
 
 // --------------------------- elementwise scans (log, minGRU cell + log, linear)

@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.declared_functions()
-    assert len(declared) == 25, declared
+    assert len(declared) == 26, declared
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -166,6 +166,7 @@ def test_givens_validation(lib):
 
 def test_workspace_check_validation(lib):
     assert lib.mgs_workspace_check(None, None, None) == INVALID
+    assert lib.mgs_workspace_set_waits(None, 0, 0, None) == INVALID
 
 
 def test_delta_validation(lib):
