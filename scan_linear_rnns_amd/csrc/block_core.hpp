@@ -1413,7 +1413,7 @@ __device__ __forceinline__ void publish_wm(uint64_t *dst, int tile, int slot, ui
 // entering the tile in c (every lane, its slot) and publishes the tile's
 // inclusive state when publish_incl.
 template <int KIND, int K, int W, int DIR, typename F>
-__device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl, int ftile, uint32_t tag,
+__device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl, int ftile, const uint32_t *launch,
                                                const float *X, const float *base0, bool publish_incl,
                                                float *c, float *dead, F &&overlap)
 {
@@ -1441,7 +1441,8 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
     __shared__ int sDone;
 #pragma unroll
     for (int e = 0; e < CW; ++e) c[e] = base0[e];
-    const uint32_t want = wait_tag(a.hd, tag), limit = wait_limit(a.hd);
+    // launch[0]: the tag this launch publishes; [1]: the tag its waits expect; [2]: their poll limit
+    const uint32_t tag = launch[0], want = launch[1], limit = launch[2];
     for (uint32_t spin = 0;; ++spin) {
         if (tl.wv > 0) {
             const int u = HALF ? 2 * (tl.wv - 1) + tl.sub : tl.wv - 1;
@@ -1575,24 +1576,24 @@ __device__ __forceinline__ void publish_first(const BlkArgs &a, const Tile &tl, 
 // tile's tree, runs the look-back (multi-tile launches) and returns the state
 // entering this lane's chunk.
 template <int K, int C, int W, bool MULTI>
-__device__ __forceinline__ float affine_fwd_carry(const BlkArgs &a, const Tile &tl, int ftile, unsigned long long ep,
+__device__ __forceinline__ float affine_fwd_carry(const BlkArgs &a, const Tile &tl, int ftile, const Launch &ep,
                                                   float (&X)[K + 1], float xh0,
                                                   float (&sKS)[2][2 * W][32][(AggShape<kMatVec, K>::stride)],
-                                                  float (&sCarry)[32], uint32_t (&sTicket)[2])
+                                                  float (&sCarry)[32], uint32_t (&sTicket)[3])
 {
     constexpr int NCH = 2 * W;
     using S = AggShape<kMatVec, K>;
     using Rw = Rows<K>;
     if constexpr (MULTI) {
         float (*nodes)[32][S::stride] = reinterpret_cast<float (*)[32][S::stride]>(&sKS[0][0][0][0]);
-        if (threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
+        if (threadIdx.x == 0) epoch_end(a.hd, ep, a.nTiles, sTicket);
         tree_build<kMatVec, K, NCH, +1>(nodes, tl, X);   // its first barrier also shares the tag
         const uint32_t tag = sTicket[0];
         if (tl.wv == 0 && tl.sub == 0 && tl.j < a.nT - 1) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
         const float *root = nodes[tree_node<NCH, +1>(tree_levels<NCH>(), 0)][tl.slot];
         float c = xh0;
         if (tl.j > 0)
-            block_lookback<kMatVec, K, W, +1>(a, tl, ftile, tag, root, &xh0, tl.j < a.nT - 1, &c, &nodes[0][0][0],
+            block_lookback<kMatVec, K, W, +1>(a, tl, ftile, sTicket, root, &xh0, tl.j < a.nT - 1, &c, &nodes[0][0][0],
                                               [] {});
         else if (a.nT > 1)
             publish_first<kMatVec, K>(a, tl, ftile, tag, root, &xh0);
@@ -1610,17 +1611,17 @@ __device__ __forceinline__ float affine_fwd_carry(const BlkArgs &a, const Tile &
 // Backward: X = (row of Psi, entry of Wl) is the chunk's reverse aggregate.
 // Returns w entering this lane's chunk from its end.
 template <int K, int C, int W, bool MULTI>
-__device__ __forceinline__ float affine_bwd_carry(const BlkArgs &a, const Tile &tl, int ftile, unsigned long long ep,
+__device__ __forceinline__ float affine_bwd_carry(const BlkArgs &a, const Tile &tl, int ftile, const Launch &ep,
                                                   float (&X)[K + 1],
                                                   float (&sKS)[2][2 * W][32][(AggShape<kMatVec, K>::stride)],
-                                                  float (&sCarry)[32], uint32_t (&sTicket)[2])
+                                                  float (&sCarry)[32], uint32_t (&sTicket)[3])
 {
     constexpr int NCH = 2 * W;
     using S = AggShape<kMatVec, K>;
     using Rw = Rows<K>;
     if constexpr (MULTI) {
         float (*nodes)[32][S::stride] = reinterpret_cast<float (*)[32][S::stride]>(&sKS[0][0][0][0]);
-        if (threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
+        if (threadIdx.x == 0) epoch_end(a.hd, ep, a.nTiles, sTicket);
         tree_build<kMatVec, K, NCH, -1>(nodes, tl, X);
         const uint32_t tag = sTicket[0];
         if (tl.wv == 0 && tl.sub == 0 && tl.j > 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
@@ -1628,7 +1629,7 @@ __device__ __forceinline__ float affine_bwd_carry(const BlkArgs &a, const Tile &
         const float zero = 0.0f;
         float w = 0.0f;
         if (tl.j < a.nT - 1)
-            block_lookback<kMatVec, K, W, -1>(a, tl, ftile, tag, root, &zero, tl.j > 0, &w, &nodes[0][0][0],
+            block_lookback<kMatVec, K, W, -1>(a, tl, ftile, sTicket, root, &zero, tl.j > 0, &w, &nodes[0][0][0],
                                               [] {});
         else if (a.nT > 1)
             publish_first<kMatVec, K>(a, tl, ftile, tag, root, &zero);
@@ -1655,11 +1656,11 @@ __device__ __forceinline__ void affine_fwd_body(const BlkArgs &a)
     using Rw = Rows<K>;
     __shared__ float sKS[2][NCH][32][(AggShape<kMatVec, K>::stride)];
     __shared__ float sCarry[32];
-    __shared__ uint32_t sTicket[2];
+    __shared__ uint32_t sTicket[3];
     __shared__ float sCS[GIV ? W : 1][64][kCSLd];
 
     const int tile = blockIdx.x;
-    unsigned long long ep = 0;
+    Launch ep{0, 0};
     if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<K, C, W>(a, tile, false);
     const int ftile = tl.j * a.nCG + tl.cg;
@@ -1747,10 +1748,10 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
     using Rw = Rows<K>;
     __shared__ float sKS[2][NCH][32][(AggShape<kMatVec, K>::stride)];
     __shared__ float sCarry[32];
-    __shared__ uint32_t sTicket[2];
+    __shared__ uint32_t sTicket[3];
 
     const int tile = blockIdx.x;
-    unsigned long long ep = 0;
+    Launch ep{0, 0};
     if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<K, C, W>(a, tile, true);
     const int ftile = tl.j * a.nCG + tl.cg;
@@ -1823,10 +1824,10 @@ __global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
 {
     __shared__ float sKS[2][2 * W][32][(AggShape<kMatVec, 8>::stride)];
     __shared__ float sCarry[32];
-    __shared__ uint32_t sTicket[2];
+    __shared__ uint32_t sTicket[3];
 
     const int tile = blockIdx.x;
-    unsigned long long ep = 0;
+    Launch ep{0, 0};
     if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<8, C, W>(a, tile, true);
     const int ftile = tl.j * a.nCG + tl.cg;
@@ -1926,10 +1927,10 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
     using S = AggShape<kMat, K>;
     using Rw = Rows<K>;
     __shared__ float sKS[2][NCH][32][S::stride];
-    __shared__ uint32_t sTicket[2];
+    __shared__ uint32_t sTicket[3];
 
     const int tile = blockIdx.x;
-    unsigned long long ep = 0;
+    Launch ep{0, 0};
     if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<K, C, W>(a, tile, false);
     const int ftile = tl.j * a.nCG + tl.cg;
@@ -1953,7 +1954,7 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
         for (int s = 0; s < K; ++s) X[s] = np[s];
     }
     float (*nodes)[32][S::stride] = reinterpret_cast<float (*)[32][S::stride]>(&sKS[0][0][0][0]);
-    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
+    if (MULTI && threadIdx.x == 0) epoch_end(a.hd, ep, a.nTiles, sTicket);
     tree_build<kMat, K, NCH, +1>(nodes, tl, X);   // its first barrier also shares the tag
     // state entering the tile (P_0 = I before the first), then entering the chunk
     float P[K], eye[K];
@@ -1965,7 +1966,7 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
         if (tl.wv == 0 && tl.sub == 0 && tl.j < a.nT - 1) publish_wm<K>(a.agg, ftile, tl.slot, tag, X);
         const float *root = nodes[tree_node<NCH, +1>(tree_levels<NCH>(), 0)][tl.slot];
         if (tl.j > 0)
-            block_lookback<kMat, K, W, +1>(a, tl, ftile, tag, root, eye, tl.j < a.nT - 1, P, &nodes[0][0][0],
+            block_lookback<kMat, K, W, +1>(a, tl, ftile, sTicket, root, eye, tl.j < a.nT - 1, P, &nodes[0][0][0],
                                            [] {});
         else
             publish_first<kMat, K>(a, tl, ftile, tag, root, eye);
@@ -2005,10 +2006,10 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
     using S = AggShape<kMatMat, K>;
     using Rw = Rows<K>;
     __shared__ float sKS[2][NCH][32][S::stride];
-    __shared__ uint32_t sTicket[2];
+    __shared__ uint32_t sTicket[3];
 
     const int tile = blockIdx.x;
-    unsigned long long ep = 0;
+    Launch ep{0, 0};
     if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<K, C, W>(a, tile, true);
     const int ftile = tl.j * a.nCG + tl.cg;
@@ -2057,7 +2058,7 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
         for (int s = 0; s < K; ++s) { X[s] = np[s]; X[K + s] = nw[s]; }
     }
     float (*nodes)[32][S::stride] = reinterpret_cast<float (*)[32][S::stride]>(&sKS[0][0][0][0]);
-    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
+    if (MULTI && threadIdx.x == 0) epoch_end(a.hd, ep, a.nTiles, sTicket);
     tree_build<kMatMat, K, NCH, -1>(nodes, tl, X);
     // P_{t-1}^T = P_{t-2}^T A_{t-1}^T for the chunk's later steps
     auto recompute = [&] {
@@ -2070,7 +2071,7 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
     if (MULTI && tl.j < a.nT - 1) {
         const uint32_t tag = sTicket[0];
         if (tl.wv == 0 && tl.sub == 0 && tl.j > 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
-        block_lookback<kMatMat, K, W, -1>(a, tl, ftile, tag, nodes[tree_node<NCH, -1>(tree_levels<NCH>(), 0)][tl.slot],
+        block_lookback<kMatMat, K, W, -1>(a, tl, ftile, sTicket, nodes[tree_node<NCH, -1>(tree_levels<NCH>(), 0)][tl.slot],
                                           zero, tl.j > 0, Wc, &nodes[0][0][0], recompute);
     } else {
         if (MULTI) {   // the last tile along T (nT > 1): nothing after it

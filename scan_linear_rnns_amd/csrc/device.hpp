@@ -30,28 +30,19 @@ constexpr uint32_t kSpinLimit = 1u << 20; // polls (each a memory round trip plu
 // `spin_limit` and `fail_waits` are set by the host (0 in normal use) for
 // tests of the failure path: a wait gives up after spin_limit polls (0: the
 // built-in kSpinLimit), and with fail_waits every wait expects kNeverTag,
-// which no launch publishes, so each one runs to its limit.
+// which no launch publishes, so each one runs to its limit.  They sit in a
+// cache line of their own, away from the ticket that every workgroup adds to
+// at kernel start.
 struct WsHeader {
     unsigned long long ticket;
     uint32_t err;
-    uint32_t spin_limit;
+    uint32_t pad0[29];
+    uint32_t spin_limit;   // byte 128
     uint32_t fail_waits;
-    uint32_t pad[59];
+    uint32_t pad1[30];
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
 constexpr uint32_t kNeverTag = 0xFFFFFFFFu;   // launch tags are 1 .. 2^32 - 2
-
-// The polls' limit and the tag they wait for, from the header's host-set fields.
-__device__ __forceinline__ uint32_t wait_limit(const WsHeader *hd)
-{
-    const uint32_t l = hd->spin_limit;
-    return l ? l : kSpinLimit;
-}
-
-__device__ __forceinline__ uint32_t wait_tag(const WsHeader *hd, uint32_t tag)
-{
-    return hd->fail_waits ? kNeverTag : tag;
-}
 
 // Output stores.  Every output element (and every chunk state a forward saves
 // for its backward) is written exactly once and never read back by the kernel
@@ -128,25 +119,39 @@ __device__ __forceinline__ void raise_error(uint32_t *err, uint32_t bits)
 // so every tile a resident workgroup waits on has already been dispatched, and
 // the lowest-numbered unfinished tile can always proceed: no deadlock, with no
 // need to take tile indices from a counter.
-__device__ __forceinline__ unsigned long long epoch_begin(WsHeader *hd)
+// Taken at kernel start: the ticket word before thread 0's add, and the
+// waits' settings (spin_limit, fail_waits; one load of a workgroup-uniform
+// address, so a scalar load that vector loads do not queue behind), both
+// consumed only after the tile's loads.
+struct Launch {
+    unsigned long long old, cfg;
+};
+
+__device__ __forceinline__ Launch epoch_begin(WsHeader *hd)
 {
-    unsigned long long old = 0;
+    Launch l{0, *reinterpret_cast<const unsigned long long *>(&hd->spin_limit)};
     if (threadIdx.x == 0)
-        old = __hip_atomic_fetch_add(&hd->ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return old;
+        l.old = __hip_atomic_fetch_add(&hd->ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return l;
 }
 
-// Thread 0 only: turns epoch_begin's value into the launch tag, starting the
-// next epoch if this workgroup was the last of the launch to arrive.
-__device__ __forceinline__ uint32_t epoch_end(WsHeader *hd, unsigned long long old, uint32_t n_tiles)
+// Thread 0 only: turns epoch_begin's values into the words the workgroup
+// shares through LDS -- w[0] the launch tag (starting the next epoch if this
+// workgroup was the last of the launch to arrive), w[1] the tag the waits
+// expect, w[2] their poll limit.
+__device__ __forceinline__ void epoch_end(WsHeader *hd, const Launch &l, uint32_t n_tiles, uint32_t *w)
 {
-    const uint32_t cnt = static_cast<uint32_t>(old);
-    const uint32_t epoch = static_cast<uint32_t>(old >> 32);
+    const uint32_t cnt = static_cast<uint32_t>(l.old);
+    const uint32_t epoch = static_cast<uint32_t>(l.old >> 32);
     if (cnt == n_tiles - 1)
         __hip_atomic_store(&hd->ticket, static_cast<unsigned long long>(epoch + 1u) << 32, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     if (cnt >= n_tiles) raise_error(&hd->err, kErrTicket);
-    return epoch % 0xFFFFFFFEu + 1u;
+    const uint32_t tag = epoch % 0xFFFFFFFEu + 1u;
+    const uint32_t limit = static_cast<uint32_t>(l.cfg), fail = static_cast<uint32_t>(l.cfg >> 32);
+    w[0] = tag;
+    w[1] = fail ? kNeverTag : tag;
+    w[2] = limit ? limit : kSpinLimit;
 }
 
 // Polls a tagged word until it carries `tag` or the spin limit is reached.

@@ -259,7 +259,7 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
     __shared__ float sPA[MULTI ? NCH : 1][CHW];   // multi-tile: the tile's chunks [0, q) composed
     __shared__ float sPH[MULTI ? NCH : 1][CHW];
     __shared__ float sCarry[CHW];
-    __shared__ uint32_t sTicket[2];
+    __shared__ uint32_t sTicket[3];
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
@@ -267,7 +267,7 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
     const int q = wv * SUB + lane / CHW;
 
     const int tile = blockIdx.x;
-    unsigned long long ep = 0;
+    Launch ep{0, 0};
     if constexpr (MULTI) ep = epoch_begin(a.hd);
     const int j = tile / a.nCG;              // T-tile (tiles are numbered T-major)
     const int cg = tile - j * a.nCG;
@@ -304,7 +304,7 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
     }
     sLA[q][ch] = LA;
     sLH[q][ch] = LH;
-    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
+    if (MULTI && threadIdx.x == 0) epoch_end(a.hd, ep, a.nTiles, sTicket);
     __syncthreads();
     const uint32_t tag = sTicket[0];
 
@@ -336,7 +336,7 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
                 constexpr int LB = MGS_ELEM_LB;
                 float accA = Alg::idA(), accH = Alg::idH(), basev = lh0;
                 int p0 = j - 1;
-                const uint32_t want = wait_tag(a.hd, tag), limit = wait_limit(a.hd);
+                const uint32_t want = sTicket[1], limit = sTicket[2];
                 for (uint32_t spin = 0;;) {
                     uint64_t wi[LB], wa[LB], wh[LB];
 #pragma unroll
@@ -417,7 +417,7 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
     __shared__ float sP[NCH][CHW];   // reverse: prod a over the chunk
     __shared__ float sW[NCH][CHW];   // reverse: w at the chunk start from a zero carry
     __shared__ float sCarry[CHW];
-    __shared__ uint32_t sTicket[2];
+    __shared__ uint32_t sTicket[3];
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
@@ -425,7 +425,7 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
     const int q = wv * SUB + lane / CHW;
 
     const int tile = blockIdx.x;
-    unsigned long long ep = 0;
+    Launch ep{0, 0};
     if constexpr (MULTI) ep = epoch_begin(a.hd);
     const int jr = tile / a.nCG;             // tiles are numbered from the last T-tile back
     const int cg = tile - jr * a.nCG;
@@ -478,7 +478,7 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
     sH[q][ch] = H;
     sP[q][ch] = A;
     sW[q][ch] = wl;
-    if (MULTI && threadIdx.x == 0) sTicket[0] = epoch_end(a.hd, ep, a.nTiles);
+    if (MULTI && threadIdx.x == 0) epoch_end(a.hd, ep, a.nTiles, sTicket);
 
     // state entering the tile: h0 for the first tile, else the forward's carry
     const float hin = (j == 0) ? (cv ? Alg::lin_h0(lh0v) : 0.0f) : Alg::to_linear(cin_f);
@@ -507,7 +507,7 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
                 constexpr int LB = MGS_ELEM_LB;
                 float accP = 1.0f, accW = 0.0f, basev = 0.0f;
                 int p0 = j + 1;
-                const uint32_t want = wait_tag(a.hd, tag), limit = wait_limit(a.hd);
+                const uint32_t want = sTicket[1], limit = sTicket[2];
                 for (uint32_t spin = 0;;) {
                     uint64_t wi[LB], wp[LB], ww[LB];
 #pragma unroll
