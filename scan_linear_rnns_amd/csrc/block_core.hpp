@@ -1660,8 +1660,6 @@ __device__ __forceinline__ void affine_fwd_body(const BlkArgs &a)
     __shared__ float sCS[GIV ? W : 1][64][kCSLd];
 
     const int tile = blockIdx.x;
-    Launch ep{0, 0};
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<K, C, W>(a, tile, false);
     const int ftile = tl.j * a.nCG + tl.cg;
 
@@ -1694,6 +1692,10 @@ __device__ __forceinline__ void affine_fwd_body(const BlkArgs &a)
         }
     }
     const float xh0 = load_h0<K>(a, tl);
+    // the launch ticket after the inputs: its atomic returns behind them
+    // rather than ahead of them in wave 0's in-order load queue
+    Launch ep{0, 0};
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
 #pragma unroll
     for (int i = 0; i < C; ++i)
         if (!(tl.cv && tl.t0 + i < a.T)) {
@@ -1751,8 +1753,6 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
     __shared__ uint32_t sTicket[3];
 
     const int tile = blockIdx.x;
-    Launch ep{0, 0};
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<K, C, W>(a, tile, true);
     const int ftile = tl.j * a.nCG + tl.cg;
 
@@ -1765,6 +1765,9 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
         hp[i] = load_once(&a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep]);
     }
     const float xh0 = load_h0<K>(a, tl);
+    // the launch ticket after the inputs (see the forward)
+    Launch ep{0, 0};
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int t = tl.t0 + i;
@@ -1827,8 +1830,6 @@ __global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
     __shared__ uint32_t sTicket[3];
 
     const int tile = blockIdx.x;
-    Launch ep{0, 0};
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<8, C, W>(a, tile, true);
     const int ftile = tl.j * a.nCG + tl.cg;
     const MeshLane ml = mesh_lane(tl.v);
@@ -1844,6 +1845,8 @@ __global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
         hp[i] = load_once(&a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep]);
     }
     const float xh0 = load_h0<8>(a, tl);
+    Launch ep{0, 0};   // the launch ticket after the inputs (see the block-affine forward)
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
     float ev[C][8];   // this lane's four cosines and signed sines per step
 #pragma unroll
     for (int i = 0; i < C; ++i) {
@@ -1930,8 +1933,6 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
     __shared__ uint32_t sTicket[3];
 
     const int tile = blockIdx.x;
-    Launch ep{0, 0};
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<K, C, W>(a, tile, false);
     const int ftile = tl.j * a.nCG + tl.cg;
 
@@ -1939,6 +1940,8 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
 #pragma unroll
     for (int i = 0; i < C; ++i)
         Rw::load_row(a.A + tl.ablk0 + clampT(tl.t0 + i, a.T) * tl.astep, tl.v, Ar[i]);
+    Launch ep{0, 0};   // the launch ticket after the inputs (see the block-affine forward)
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
 #pragma unroll
     for (int i = 0; i < C; ++i)
         if (!(tl.cv && tl.t0 + i < a.T)) Rw::eye(tl.v, Ar[i]);
@@ -2009,8 +2012,6 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
     __shared__ uint32_t sTicket[3];
 
     const int tile = blockIdx.x;
-    Launch ep{0, 0};
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
     const Tile tl = make_tile<K, C, W>(a, tile, true);
     const int ftile = tl.j * a.nCG + tl.cg;
 
@@ -2033,6 +2034,8 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
             PT[0][s] = ps[m * K + Rw::col(m, tl.v)];
         }
     }
+    Launch ep{0, 0};   // the launch ticket after the inputs (see the block-affine forward)
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         if (!(tl.cv && tl.t0 + i < a.T)) {

@@ -109,9 +109,14 @@ __device__ __forceinline__ void raise_error(uint32_t *err, uint32_t bits)
 // workgroup that brings the count to n_tiles starts the next epoch.  All
 // workgroups of one launch therefore read the same epoch, and any two
 // launches on one workspace (also replays of a captured graph) read different
-// ones.  The atomic is issued at kernel start (epoch_begin) and its result is
-// consumed only when the workgroup first publishes (epoch_end), so its round
-// trip overlaps the tile's loads.
+// ones.  The atomic is issued right after the tile's input loads
+// (epoch_begin) and its result is consumed only when the workgroup first
+// publishes (epoch_end).  Loads complete in issue order within a wave, so an
+// atomic issued ahead of the inputs -- every workgroup's thread 0 adding to
+// the same word -- holds wave 0's inputs back until it returns (block-affine
+// pair 37.1 -> 34.8 us when moved behind them).  The elementwise backward,
+// whose work between its loads and its first publish is too short to hide
+// the round trip, still issues it at kernel start.
 //
 // Tiles are indexed by blockIdx and wait only on tiles with a smaller index
 // (forward) or a larger one whose blockIdx is smaller (backward, which numbers
@@ -119,10 +124,10 @@ __device__ __forceinline__ void raise_error(uint32_t *err, uint32_t bits)
 // so every tile a resident workgroup waits on has already been dispatched, and
 // the lowest-numbered unfinished tile can always proceed: no deadlock, with no
 // need to take tile indices from a counter.
-// Taken at kernel start: the ticket word before thread 0's add, and the
-// waits' settings (spin_limit, fail_waits; one load of a workgroup-uniform
-// address, so a scalar load that vector loads do not queue behind), both
-// consumed only after the tile's loads.
+// Taken after the tile's input loads (or at kernel start): the ticket word
+// before thread 0's add, and the waits' settings (spin_limit, fail_waits; one load of a
+// workgroup-uniform address, so a scalar load that vector loads do not queue
+// behind), both consumed only at the tile's first publish.
 struct Launch {
     unsigned long long old, cfg;
 };

@@ -267,8 +267,6 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
     const int q = wv * SUB + lane / CHW;
 
     const int tile = blockIdx.x;
-    Launch ep{0, 0};
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
     const int j = tile / a.nCG;              // T-tile (tiles are numbered T-major)
     const int cg = tile - j * a.nCG;
 
@@ -289,9 +287,13 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
         x[i] = a.la[off];
         y[i] = a.lb[off];
     }
+    const float lh0v = a.lh0[cc];
+    // the launch ticket after the inputs: its atomic returns behind them
+    // rather than ahead of them in wave 0's in-order load queue
+    Launch ep{0, 0};
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
 #pragma unroll
     for (int i = 0; i < C; ++i) Alg::input(x[i], y[i], cv && t0 + i < a.T, x[i], y[i]);
-    const float lh0v = a.lh0[cc];
 
     // chunk-local pair scan from the identity
     float pA[C], pH[C];
@@ -425,6 +427,9 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
     const int q = wv * SUB + lane / CHW;
 
     const int tile = blockIdx.x;
+    // the launch ticket at kernel start here: the backward's chunk scans are
+    // too short to hide the atomic's round trip behind them (log-space long-T
+    // backward 8.3 -> 8.6 us, minGRU cell 9.1 -> 10.4 us with it after the loads)
     Launch ep{0, 0};
     if constexpr (MULTI) ep = epoch_begin(a.hd);
     const int jr = tile / a.nCG;             // tiles are numbered from the last T-tile back
