@@ -1756,52 +1756,92 @@ __global__ void __launch_bounds__(64 * W) baffine_bwd_kernel(BlkArgs a)
     const Tile tl = make_tile<K, C, W>(a, tile, true);
     const int ftile = tl.j * a.nCG + tl.cg;
 
+    // Multi-tile launches load in the order the chunk aggregate consumes the
+    // inputs (the last step first; h_{t-1}, needed only in the fix-up, after
+    // all of them): a wave's loads complete in issue order, so the aggregate
+    // starts on the last step while the earlier steps' loads are in flight
+    // (long-T backward 21.5 -> 20.9 us, k = 16 49.9 -> 48.4 us).  A single
+    // tile waits for all its loads at its first barrier anyway, and keeps the
+    // plain order (10.2 us against 10.4 us reversed at the lab shape).
     float ATr[C][K], gv[C], hp[C];   // rows of A_t^T, upstream dh_t, h_{t-1}
+    if constexpr (MULTI) {
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int t = clampT(tl.t0 + i, a.T);
-        Rw::load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
-        gv[i] = load_once(&a.y[tl.vec0 + t * tl.vstep]);
-        hp[i] = load_once(&a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep]);
+        for (int i = C - 1; i >= 0; --i) {
+            const int t = clampT(tl.t0 + i, a.T);
+            Rw::load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
+            gv[i] = load_once(&a.y[tl.vec0 + t * tl.vstep]);
+        }
+#pragma unroll
+        for (int i = C - 1; i >= 0; --i) {
+            const int t = clampT(tl.t0 + i, a.T);
+            hp[i] = load_once(&a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int t = clampT(tl.t0 + i, a.T);
+            Rw::load_col(a.A + tl.ablk0 + t * tl.astep, tl.v, ATr[i]);
+            gv[i] = load_once(&a.y[tl.vec0 + t * tl.vstep]);
+            hp[i] = load_once(&a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep]);
+        }
     }
     const float xh0 = load_h0<K>(a, tl);
     // the launch ticket after the inputs (see the forward)
     Launch ep{0, 0};
     if constexpr (MULTI) ep = epoch_begin(a.hd);
+
+    // A step past T (or of a chain past the last) is the identity.  A single
+    // tile makes its inputs so up front; a multi-tile launch leaves the loaded
+    // registers alone and selects the step's results instead, so that nothing
+    // touches a step's registers before the aggregate reaches the step (the
+    // compiler would otherwise wait on all the loads at the first select).
+    if constexpr (!MULTI) {
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int t = tl.t0 + i;
-        if (t == 0) hp[i] = xh0;
-        if (!(tl.cv && t < a.T)) {
-            Rw::eye(tl.v, ATr[i]);
-            gv[i] = 0.0f;
-            hp[i] = 0.0f;
+        for (int i = 0; i < C; ++i) {
+            const int t = tl.t0 + i;
+            if (t == 0) hp[i] = xh0;
+            if (!(tl.cv && t < a.T)) {
+                Rw::eye(tl.v, ATr[i]);
+                gv[i] = 0.0f;
+                hp[i] = 0.0f;
+            }
         }
     }
+    auto live = [&](int i) { return !MULTI || (tl.cv && tl.t0 + i < a.T); };
 
     // chunk aggregate from a zero carry, walking t downwards: X = (Psi, Wl)
     float X[K + 1];
+    {
+        float E[K];
+        Rw::eye(tl.v, E);
+        const bool v = live(C - 1);
 #pragma unroll
-    for (int s = 0; s < K; ++s) X[s] = ATr[C - 1][s];
-    X[K] = Rw::mv(ATr[C - 1], gv[C - 1], 0.0f);
+        for (int s = 0; s < K; ++s) X[s] = v ? ATr[C - 1][s] : E[s];
+        X[K] = v ? Rw::mv(ATr[C - 1], gv[C - 1], 0.0f) : 0.0f;
+    }
 #pragma unroll
     for (int i = C - 2; i >= 0; --i) {
         float np[K];
         Rw::mm(ATr[i], X, np);
-        X[K] = Rw::mv(ATr[i], gv[i] + X[K], 0.0f);
+        const float nw = Rw::mv(ATr[i], gv[i] + X[K], 0.0f);
+        const bool v = live(i);
 #pragma unroll
-        for (int s = 0; s < K; ++s) X[s] = np[s];
+        for (int s = 0; s < K; ++s) X[s] = v ? np[s] : X[s];
+        X[K] = v ? nw : X[K];
     }
     float w = affine_bwd_carry<K, C, W, MULTI>(a, tl, ftile, ep, X, sKS, sCarry, sTicket);
 
     // re-run the reverse recurrence from the true carry; emit dA, db, dh0
 #pragma unroll
     for (int i = C - 1; i >= 0; --i) {
-        const float g = gv[i] + w;
-        float dAr[K];
-        Rw::outer(g, hp[i], dAr);
-        w = Rw::mv(ATr[i], g, 0.0f);
         const int t = tl.t0 + i;
+        const bool v = live(i);
+        const float g = (v ? gv[i] : 0.0f) + w;
+        const float hprev = !MULTI ? hp[i] : (!v ? 0.0f : (t == 0 ? xh0 : hp[i]));
+        float dAr[K];
+        Rw::outer(g, hprev, dAr);
+        const float wn = Rw::mv(ATr[i], g, 0.0f);
+        w = v ? wn : g;
         if (tl.cv && t < a.T) {
             store_out(&a.out2[tl.vec0 + t * tl.vstep], g);
             Rw::store_row(a.out + tl.ablk0 + t * tl.astep, tl.v, dAr);
