@@ -1121,15 +1121,20 @@ __device__ __forceinline__ float mesh_partner(float x, int l, bool mir)
 
 // The four angles this lane evaluates at step t (lanes 0 and 7: zero for the
 // odd pair they do not have).
-__device__ __forceinline__ float4 load_mesh_angles(const BlkArgs &a, const Tile &tl, const MeshLane &ml, int t)
+// This lane's four angles of one step at p (the step's 28 angles).  Lanes
+// without an odd-layer pair load their even pair's angles twice; mesh_eval
+// replaces those by 0 where the values are used, so no select waits on the
+// loads while later ones are still to be issued.
+__device__ __forceinline__ float4 mesh_angles_at(const float *p, const MeshLane &ml)
 {
-    const float *p = a.theta + (tl.blk0 + static_cast<int64_t>(t) * a.nb) * kAngles;
-    return make_float4(p[ml.ie], p[ml.ie + 7], ml.oddp ? p[ml.io] : 0.0f, ml.oddp ? p[ml.io + 7] : 0.0f);
+    const int io = ml.oddp ? ml.io : ml.ie;
+    return make_float4(p[ml.ie], p[ml.ie + 7], p[io], p[io + 7]);
 }
 
 // cosines and sines (signed for this lane's place in the pair) of its four angles
 __device__ __forceinline__ void mesh_eval(float4 th, const MeshLane &ml, float (&e)[8])
 {
+    if (!ml.oddp) th.z = th.w = 0.0f;
     float s;
     sincos_cw(th.x, s, e[0]); e[1] = ml.re ? s : -s;
     sincos_cw(th.y, s, e[2]); e[3] = ml.re ? s : -s;
@@ -1874,37 +1879,69 @@ __global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
     const int ftile = tl.j * a.nCG + tl.cg;
     const MeshLane ml = mesh_lane(tl.v);
 
+    // Multi-tile launches load in the order the first pass consumes the
+    // inputs (the last step first; h_{t-1} after every step's angles, gate and
+    // dh_t), and each step is evaluated (sin / cos, gate) inside the pass, so
+    // the pass starts on the last step while the others' loads are in flight
+    // (long-T backward 30.3 -> 28.8 us).  Their addresses are a base plus a
+    // multiple of a launch-wide stride (a step past T reads the tile's first
+    // step inside the sequence; the identity step replaces it where it is
+    // used): no per-lane 64-bit products between the loads, whose temporaries
+    // the compiler would place in registers of loads still in flight.  A
+    // single tile keeps the plain order and evaluates up front (14.3 us
+    // against 15.6 us the other way at the lab shape).
     float4 th[C];
     float sig[C], sgd[C], gv[C], hp[C];   // gate sigmoid(s), its derivative, dh_t, h_{t-1}
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int t = clampT(tl.t0 + i, a.T);
-        th[i] = load_mesh_angles(a, tl, ml, t);
-        sig[i] = a.sg[tl.blk0 + static_cast<int64_t>(t) * a.nb];
-        gv[i] = load_once(&a.y[tl.vec0 + t * tl.vstep]);
-        hp[i] = load_once(&a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep]);
-    }
-    const float xh0 = load_h0<8>(a, tl);
-    Launch ep{0, 0};   // the launch ticket after the inputs (see the block-affine forward)
-    if constexpr (MULTI) ep = epoch_begin(a.hd);
     float ev[C][8];   // this lane's four cosines and signed sines per step
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int t = tl.t0 + i;
-        if (t == 0) hp[i] = xh0;
-        const bool valid = tl.cv && t < a.T;
-        if (!valid) {   // identity step: zero angles, gate 1
+    // with e = exp(-|s|): sigmoid(|s|) = 1 / (1 + e) and sigmoid'(s) =
+    // e / (1 + e)^2, exact in relative terms (1 - sigmoid(s) would cancel once
+    // sigmoid(s) nears 1); an invalid step is the identity (zero angles, gate 1)
+    auto evaluate = [&](int i) {
+        const bool valid = tl.cv && tl.t0 + i < a.T;
+        if (!valid) {
             th[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             gv[i] = 0.0f;
-            hp[i] = 0.0f;
         }
-        // with e = exp(-|s|): sigmoid(|s|) = 1 / (1 + e) and sigmoid'(s) =
-        // e / (1 + e)^2, exact in relative terms (1 - sigmoid(s) would cancel
-        // once sigmoid(s) nears 1)
         const float e = __expf(-fabsf(sig[i])), r = 1.0f / (1.0f + e);
         sgd[i] = valid ? e * r * r : 0.0f;
         sig[i] = valid ? (sig[i] >= 0.0f ? r : e * r) : 1.0f;
         mesh_eval(th[i], ml, ev[i]);
+    };
+    if constexpr (MULTI) {
+        const int64_t nbs = a.nb, vs = tl.vstep;
+        const int tin = max(min(tl.t0, a.T - 1), 0);
+        const int64_t sb = tl.blk0 + static_cast<int64_t>(tl.t0) * nbs, sbi = tl.blk0 + static_cast<int64_t>(tin) * nbs;
+        const int64_t vb = tl.vec0 + static_cast<int64_t>(tl.t0) * vs, vbi = tl.vec0 + static_cast<int64_t>(tin) * vs;
+#pragma unroll
+        for (int i = C - 1; i >= 0; --i) {
+            const bool in = tl.t0 + i < a.T;
+            const int64_t si = in ? sb + i * nbs : sbi;
+            th[i] = mesh_angles_at(a.theta + si * kAngles, ml);
+            sig[i] = a.sg[si];
+            gv[i] = load_once(&a.y[in ? vb + i * vs : vbi]);
+        }
+#pragma unroll
+        for (int i = C - 1; i >= 0; --i) {
+            const bool in = tl.t0 + i < a.T && tl.t0 + i > 0;
+            hp[i] = load_once(&a.x[in ? vb + (i - 1) * vs : vbi]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int t = clampT(tl.t0 + i, a.T);
+            const float *p = a.theta + (tl.blk0 + static_cast<int64_t>(t) * a.nb) * kAngles;
+            th[i] = make_float4(p[ml.ie], p[ml.ie + 7], ml.oddp ? p[ml.io] : 0.0f, ml.oddp ? p[ml.io + 7] : 0.0f);
+            sig[i] = a.sg[tl.blk0 + static_cast<int64_t>(t) * a.nb];
+            gv[i] = load_once(&a.y[tl.vec0 + t * tl.vstep]);
+            hp[i] = load_once(&a.x[tl.vec0 + (t > 0 ? t - 1 : 0) * tl.vstep]);
+        }
+    }
+    const float xh0 = load_h0<8>(a, tl);
+    Launch ep{0, 0};   // the launch ticket after the inputs (see the block-affine forward)
+    if constexpr (MULTI) ep = epoch_begin(a.hd);
+    if constexpr (!MULTI) {   // a single tile evaluates every step up front
+#pragma unroll
+        for (int i = 0; i < C; ++i) evaluate(i);
     }
 
     // chunk aggregate from a zero carry, walking t downwards: X = (Psi, Wl),
@@ -1914,6 +1951,7 @@ __global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
     X[8] = 0.0f;
 #pragma unroll
     for (int i = C - 1; i >= 0; --i) {
+        if constexpr (MULTI) evaluate(i);   // a multi-tile launch evaluates each step as it reaches it
         float c[8], s[8];
         mesh_coef(ev[i], ml, c, s);
         c[0] *= sig[i];
@@ -1932,7 +1970,8 @@ __global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
         const float g = gv[i] + w;
         float c[8], s[8], y[8], d[8];
         mesh_coef(ev[i], ml, c, s);
-        float x = hp[i];
+        const int t = tl.t0 + i;
+        float x = tl.cv && t < a.T ? (t == 0 ? xh0 : hp[i]) : 0.0f;
 #pragma unroll
         for (int l = 0; l < 8; ++l) y[l] = x = mesh_vec(x, c[l], s[l], l, ml.mir);
         const float ds = chain_sum8(g * y[7]) * sgd[i];
@@ -1944,7 +1983,6 @@ __global__ void __launch_bounds__(64 * W) bgivens_bwd_kernel(BlkArgs a)
             z = __builtin_fmaf(-s[l], zp, c[l] * z);
         }
         w = z;
-        const int t = tl.t0 + i;
         if (tl.cv && t < a.T) {
             float *dth = a.dtheta + (tl.blk0 + static_cast<int64_t>(t) * a.nb) * kAngles;
             store_out(&a.out2[tl.vec0 + t * tl.vstep], g);
