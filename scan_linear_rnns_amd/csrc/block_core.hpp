@@ -67,6 +67,7 @@ struct BlkArgs {
     const float *sg;     // Givens angle-fused: gate pre-activations (B,T,nb)
     float *dtheta;       // Givens angle-fused backward: d angles
     float *dsg;          // Givens angle-fused backward: d gate
+    int lb_local;        // every tile's look-back partners run on its XCD (tagged_store)
 };
 
 // Tile shape per op and block size: waves per workgroup and the cap on steps
@@ -1389,11 +1390,11 @@ __device__ __forceinline__ void tree_apply(float (*nodes)[32][(AggShape<KIND, K>
 // Look-back words in the workspace are word-major per tile ([tile][word][slot]),
 // so a word of all 32 slots is 256 contiguous bytes for a tile's loads and stores.
 template <int NW>
-__device__ __forceinline__ void publish_wm(uint64_t *dst, int tile, int slot, uint32_t tag, const float *x)
+__device__ __forceinline__ void publish_wm(uint64_t *dst, int tile, int slot, uint32_t tag, const float *x, bool local)
 {
     uint64_t *p = dst + static_cast<size_t>(tile) * NW * 32 + slot;
 #pragma unroll
-    for (int e = 0; e < NW; ++e) tagged_store(p + e * 32, tag, x[e]);
+    for (int e = 0; e < NW; ++e) tagged_store(p + e * 32, tag, x[e], local);
 }
 
 // Look-back of a tile whose tree is built (X: the tile aggregate, read by
@@ -1552,7 +1553,7 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
 #pragma unroll
             for (int e = 0; e < CW; ++e) xo[e] = c[e];
             Cr::apply(X, xo);
-            publish_wm<CW>(a.incl, ftile, tl.slot, tag, xo);
+            publish_wm<CW>(a.incl, ftile, tl.slot, tag, xo, a.lb_local);
         }
         overlap();
     } else {
@@ -1573,7 +1574,7 @@ __device__ __forceinline__ void publish_first(const BlkArgs &a, const Tile &tl, 
 #pragma unroll
         for (int e = 0; e < Cr::CW; ++e) xo[e] = base0[e];
         Cr::apply(X, xo);
-        publish_wm<Cr::CW>(a.incl, ftile, tl.slot, tag, xo);
+        publish_wm<Cr::CW>(a.incl, ftile, tl.slot, tag, xo, a.lb_local);
     }
 }
 
@@ -1594,7 +1595,7 @@ __device__ __forceinline__ float affine_fwd_carry(const BlkArgs &a, const Tile &
         if (threadIdx.x == 0) epoch_end(a.hd, ep, a.nTiles, sTicket);
         tree_build<kMatVec, K, NCH, +1>(nodes, tl, X);   // its first barrier also shares the tag
         const uint32_t tag = sTicket[0];
-        if (tl.wv == 0 && tl.sub == 0 && tl.j < a.nT - 1) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
+        if (tl.wv == 0 && tl.sub == 0 && tl.j < a.nT - 1) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X, a.lb_local);
         const float *root = nodes[tree_node<NCH, +1>(tree_levels<NCH>(), 0)][tl.slot];
         float c = xh0;
         if (tl.j > 0)
@@ -1629,7 +1630,7 @@ __device__ __forceinline__ float affine_bwd_carry(const BlkArgs &a, const Tile &
         if (threadIdx.x == 0) epoch_end(a.hd, ep, a.nTiles, sTicket);
         tree_build<kMatVec, K, NCH, -1>(nodes, tl, X);
         const uint32_t tag = sTicket[0];
-        if (tl.wv == 0 && tl.sub == 0 && tl.j > 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
+        if (tl.wv == 0 && tl.sub == 0 && tl.j > 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X, a.lb_local);
         const float *root = nodes[tree_node<NCH, -1>(tree_levels<NCH>(), 0)][tl.slot];
         const float zero = 0.0f;
         float w = 0.0f;
@@ -2044,7 +2045,7 @@ __global__ void __launch_bounds__(64 * W) bmatrix_fwd_kernel(BlkArgs a)
     for (int s = 0; s < K; ++s) P[s] = eye[s];
     if constexpr (MULTI) {
         const uint32_t tag = sTicket[0];
-        if (tl.wv == 0 && tl.sub == 0 && tl.j < a.nT - 1) publish_wm<K>(a.agg, ftile, tl.slot, tag, X);
+        if (tl.wv == 0 && tl.sub == 0 && tl.j < a.nT - 1) publish_wm<K>(a.agg, ftile, tl.slot, tag, X, a.lb_local);
         const float *root = nodes[tree_node<NCH, +1>(tree_levels<NCH>(), 0)][tl.slot];
         if (tl.j > 0)
             block_lookback<kMat, K, W, +1>(a, tl, ftile, sTicket, root, eye, tl.j < a.nT - 1, P, &nodes[0][0][0],
@@ -2151,13 +2152,13 @@ __global__ void __launch_bounds__(64 * W) bmatrix_bwd_kernel(BlkArgs a)
     for (int s = 0; s < K; ++s) zero[s] = Wc[s] = 0.0f;
     if (MULTI && tl.j < a.nT - 1) {
         const uint32_t tag = sTicket[0];
-        if (tl.wv == 0 && tl.sub == 0 && tl.j > 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
+        if (tl.wv == 0 && tl.sub == 0 && tl.j > 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X, a.lb_local);
         block_lookback<kMatMat, K, W, -1>(a, tl, ftile, sTicket, nodes[tree_node<NCH, -1>(tree_levels<NCH>(), 0)][tl.slot],
                                           zero, tl.j > 0, Wc, &nodes[0][0][0], recompute);
     } else {
         if (MULTI) {   // the last tile along T (nT > 1): nothing after it
             const uint32_t tag = sTicket[0];
-            if (tl.wv == 0 && tl.sub == 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X);
+            if (tl.wv == 0 && tl.sub == 0) publish_wm<S::words>(a.agg, ftile, tl.slot, tag, X, a.lb_local);
             publish_first<kMatMat, K>(a, tl, ftile, tag, X, zero);
         }
         recompute();

@@ -236,6 +236,7 @@ struct LogFwdArgs {
     WsHeader *hd;
     uint64_t *agg_a, *agg_h, *incl; // tagged look-back words, [tile][CHW]
     float *carry;                   // state at each tile start (log2 h or h), [tile][CHW]
+    int lb_local;                   // every tile's look-back partners run on its XCD (tagged_store)
 };
 
 struct LogBwdArgs {
@@ -246,6 +247,7 @@ struct LogBwdArgs {
     WsHeader *hd;
     uint64_t *agg_p, *agg_w, *incl;
     const float *carry;
+    int lb_local;
 };
 
 template <class Alg, int CHW, int C, int W, bool MULTI>
@@ -322,8 +324,8 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
             }
             const size_t slot = static_cast<size_t>(tile) * CHW + ch;
             if (j < a.nT - 1) {
-                tagged_store(&a.agg_a[slot], tag, TA);
-                tagged_store(&a.agg_h[slot], tag, TH);
+                tagged_store(&a.agg_a[slot], tag, TA, a.lb_local);
+                tagged_store(&a.agg_h[slot], tag, TH, a.lb_local);
             }
             const float lh0 = Alg::carry0(lh0v, cv);
             float cin = lh0;
@@ -381,7 +383,7 @@ __global__ void __launch_bounds__(64 * W) elem_fwd_kernel(LogFwdArgs a)
                 cin = Alg::apply(accA, accH, basev);
             }
             if (j < a.nT - 1)
-                tagged_store(&a.incl[slot], tag, Alg::apply(TA, TH, cin));
+                tagged_store(&a.incl[slot], tag, Alg::apply(TA, TH, cin), a.lb_local);
             a.carry[slot] = cin;
             sCarry[ch] = cin;
         }
@@ -501,8 +503,8 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
             }
             const size_t slot = static_cast<size_t>(ftile) * CHW + ch;
             if (j > 0) {
-                tagged_store(&a.agg_p[slot], tag, TP);
-                tagged_store(&a.agg_w[slot], tag, TW);
+                tagged_store(&a.agg_p[slot], tag, TP, a.lb_local);
+                tagged_store(&a.agg_w[slot], tag, TW, a.lb_local);
             }
             float cin = 0.0f;
             if (j < a.nT - 1) {
@@ -554,7 +556,7 @@ __global__ void __launch_bounds__(64 * W) elem_bwd_kernel(LogBwdArgs a)
                 }
                 cin = accW + accP * basev;
             }
-            if (j > 0) tagged_store(&a.incl[slot], tag, TW + TP * cin);
+            if (j > 0) tagged_store(&a.incl[slot], tag, TW + TP * cin, a.lb_local);
             sCarry[ch] = cin;
         }
         __syncthreads();
@@ -672,6 +674,7 @@ LogFwdArgs fwd_args(const LogGeom &g, const float *x1, const float *x2, const fl
     a.la = x1; a.lb = x2; a.lh0 = x0; a.h = h;
     a.S = g.S; a.T = g.T; a.d = g.d; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
     a.hd = reinterpret_cast<WsHeader *>(w);
+    a.lb_local = g.nCG % kXcds == 0;   // a chain group's tiles are nCG apart in blockIdx
     if (g.nT > 1) {
         a.agg_a = reinterpret_cast<uint64_t *>(w + g.off_fagg_a);
         a.agg_h = reinterpret_cast<uint64_t *>(w + g.off_fagg_h);
@@ -690,6 +693,7 @@ LogBwdArgs bwd_args(const LogGeom &g, const float *x1, const float *x2, const fl
     a.dla = d1; a.dlb = d2; a.dlh0 = d0;
     a.S = g.S; a.T = g.T; a.d = g.d; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
     a.hd = reinterpret_cast<WsHeader *>(w);
+    a.lb_local = g.nCG % kXcds == 0;
     if (g.nT > 1) {
         a.agg_p = reinterpret_cast<uint64_t *>(w + g.off_bagg_p);
         a.agg_w = reinterpret_cast<uint64_t *>(w + g.off_bagg_w);
