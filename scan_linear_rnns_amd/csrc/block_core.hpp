@@ -1324,15 +1324,19 @@ __device__ __forceinline__ void tree_build(float (*nodes)[32][(AggShape<KIND, K>
 #pragma unroll
     for (int e = 0; e < AW; ++e) nodes[tree_node<NCH, DIR>(0, tl.q)][tl.slot][e] = X[e];
     // level 1 inside each wave: its halves hold chunks 2w and 2w + 1 (lanes l
-    // and l ^ 32 serve the same row of the same chain)
+    // and l ^ 32 serve the same row of the same chain).  One permlane32 swap
+    // of a value with itself leaves the lower half's value in every lane of
+    // the first result and the upper half's in every lane of the second (a
+    // VALU exchange, no LDS round trip); both halves then compose the same pair.
     {
-        const bool own_outer = DIR > 0 ? tl.sub == 1 : tl.sub == 0;   // the factor applied last
         float Y[AW], R[AW];
 #pragma unroll
         for (int e = 0; e < AW; ++e) {
-            const float p = __shfl_xor(X[e], 32);
-            Y[e] = own_outer ? X[e] : p;
-            R[e] = own_outer ? p : X[e];
+            const unsigned u = __float_as_uint(X[e]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+            const float lo = __uint_as_float(sw[0]), hi = __uint_as_float(sw[1]);
+            Y[e] = DIR > 0 ? hi : lo;   // the factor applied last: the later chunk
+            R[e] = DIR > 0 ? lo : hi;
         }
         compose_into<KIND, K>(Y, R);
 #pragma unroll
