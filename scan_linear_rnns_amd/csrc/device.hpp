@@ -2,10 +2,12 @@
 //
 //  * tagged words: a 64-bit word holding (32-bit call tag, 32-bit payload).
 //    Tiles publish their chunk aggregates and inclusive prefixes as tagged
-//    words written and read with relaxed agent-scope atomics; a reader
-//    accepts a word only when its tag equals the current call's tag, so no
-//    flag/payload ordering (and no L2 writeback or invalidate fence) is
-//    needed, and the workspace never has to be cleared between calls.
+//    words with relaxed atomic stores (workgroup scope when every reader runs
+//    on the writer's XCD, else agent scope; see tagged_store) and read them
+//    with relaxed agent-scope atomic loads; a reader accepts a word only when
+//    its tag equals the current call's tag, so no flag/payload ordering (and
+//    no L2 writeback or invalidate fence) is needed, and the workspace never
+//    has to be cleared between calls.
 //  * launch epochs: every multi-tile launch draws its tag from a per-workspace
 //    epoch counter on the device (see epoch_begin), so tags never repeat
 //    between launches on one workspace, replays of a captured graph included.
