@@ -67,7 +67,7 @@ BlkArgs base_args(const BlockGeom &g, void *ws)
     a.nchain = g.nchain;
     a.T = g.T; a.d = g.d; a.nb = g.nb; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
     a.hd = hd;
-    a.lb_local = g.nCG % kXcds == 0;   // a chain group's tiles are nCG apart in blockIdx
+    a.lb_local = lookback_on_one_xcd(g.nCG);
     if (g.nT > 1) {
         a.agg = reinterpret_cast<uint64_t *>(w + g.off_agg);
         a.incl = reinterpret_cast<uint64_t *>(w + g.off_incl);

@@ -86,20 +86,20 @@ __device__ __forceinline__ uint64_t tagged_load(const uint64_t *p)
 }
 
 // Where a tagged word's readers run.  gfx950 deals the workgroups of a launch
-// to its 8 XCDs round robin by blockIdx (the XCC_ID hardware register of every
-// workgroup equals blockIdx % 8, checked on the device at 128 to 2048
-// workgroups), and the XCDs' L2 caches are not coherent with one another.  An
-// agent-scope load returns a line that is dirty in its own XCD's L2 and
+// to its XCDs round robin by blockIdx (the XCC_ID hardware register of every
+// workgroup equals blockIdx % 8 on an MI355X, checked on the device at 128 to
+// 2048 workgroups), and the XCDs' L2 caches are not coherent with one another.
+// An agent-scope load returns a line that is dirty in its own XCD's L2 and
 // fetches any other line from memory; an agent-scope store writes through to
 // memory.  When every reader of a word runs on its writer's XCD (`local`: the
-// launch's tiles of one chain group lie a multiple of kXcds apart in blockIdx),
-// a workgroup-scope store, which leaves the line dirty in that L2, reaches the
-// readers' agent-scope polls without the trip to memory: one hop between two
-// workgroups of one XCD takes ~0.27 us so against ~0.47 us with an
-// agent-scope store (~0.62 us between XCDs; ping-pong of a tagged word).  In
-// every other launch the store is agent-scope.  Either way the tag, not the
-// store's scope, tells a reader whether the word is current.
-constexpr int kXcds = 8;
+// launch's tiles of one chain group lie a multiple of the device's XCD count
+// apart in blockIdx; decided on the host), a workgroup-scope store, which
+// leaves the line dirty in that L2, reaches the readers' agent-scope polls
+// without the trip to memory: one hop between two workgroups of one XCD takes
+// ~0.27 us so against ~0.47 us with an agent-scope store (~0.62 us between
+// XCDs; ping-pong of a tagged word).  In every other launch the store is
+// agent-scope.  Either way the tag, not the store's scope, tells a reader
+// whether the word is current.
 
 __device__ __forceinline__ void tagged_store(uint64_t *p, uint32_t tag, float v, bool local)
 {

@@ -674,7 +674,7 @@ LogFwdArgs fwd_args(const LogGeom &g, const float *x1, const float *x2, const fl
     a.la = x1; a.lb = x2; a.lh0 = x0; a.h = h;
     a.S = g.S; a.T = g.T; a.d = g.d; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
     a.hd = reinterpret_cast<WsHeader *>(w);
-    a.lb_local = g.nCG % kXcds == 0;   // a chain group's tiles are nCG apart in blockIdx
+    a.lb_local = lookback_on_one_xcd(g.nCG);
     if (g.nT > 1) {
         a.agg_a = reinterpret_cast<uint64_t *>(w + g.off_fagg_a);
         a.agg_h = reinterpret_cast<uint64_t *>(w + g.off_fagg_h);
@@ -693,7 +693,7 @@ LogBwdArgs bwd_args(const LogGeom &g, const float *x1, const float *x2, const fl
     a.dla = d1; a.dlb = d2; a.dlh0 = d0;
     a.S = g.S; a.T = g.T; a.d = g.d; a.nCG = g.nCG; a.nT = g.nT; a.nTiles = g.nTiles;
     a.hd = reinterpret_cast<WsHeader *>(w);
-    a.lb_local = g.nCG % kXcds == 0;
+    a.lb_local = lookback_on_one_xcd(g.nCG);
     if (g.nT > 1) {
         a.agg_p = reinterpret_cast<uint64_t *>(w + g.off_bagg_p);
         a.agg_w = reinterpret_cast<uint64_t *>(w + g.off_bagg_w);

@@ -8,9 +8,39 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace mgs {
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// XCDs (compute dies, each with an L2 of its own) of the current device, to
+// which the dispatcher deals a launch's workgroups round robin by blockIdx
+// (8 on an MI355X in its single-partition mode, fewer per partition
+// otherwise); 0 if the runtime cannot say.  Queried once per device.
+inline int xcd_count()
+{
+    constexpr int kDevs = 64;
+    static std::atomic<int> cache[kDevs];   // count + 1; 0 = not queried yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || n < 0) n = 0;
+        v = n + 1;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v - 1;
+}
+
+// Whether every reader of a tile's look-back words runs on the writer's XCD:
+// the tiles of one chain group lie nCG apart in blockIdx.
+inline bool lookback_on_one_xcd(int nCG)
+{
+    const int n = xcd_count();
+    return n > 0 && nCG % n == 0;
+}
 
 // ----------------------------- elementwise scans (log, minGRU cell + log, linear)
 // One geometry and workspace layout serves every arithmetic.

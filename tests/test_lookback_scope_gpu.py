@@ -2,8 +2,9 @@
 
 Tiles publish their look-back words with workgroup-scope stores when every
 reader runs on the writer's XCD -- the launch's tiles of one chain group lie
-nCG apart in blockIdx and nCG is a multiple of 8 -- and with agent-scope
-stores otherwise.  Each case below runs several tiles along T at a chain-group
+nCG apart in blockIdx and nCG is a multiple of the device's XCD count (8 on an
+MI355X in its single-partition mode) -- and with agent-scope stores
+otherwise.  Each case below runs several tiles along T at a chain-group
 count of each kind:
   log-space scan (64 chains per group, 128 steps per tile): S = B*d = 512
   (nCG = 8) and 448 (nCG = 7), T = 600 (5 tiles);
