@@ -43,6 +43,11 @@
 namespace mgs {
 namespace {
 
+// chunks of operands the state pass keeps in flight ahead of the one it computes
+#ifndef MGS_DELTA_PD
+#define MGS_DELTA_PD 3
+#endif
+
 constexpr int kDD = 64;   // dk = dv
 constexpr int kCh = 64;   // steps per chunk
 constexpr int kLd = 68;   // LDS row stride (floats) of 64-wide tiles (16-byte aligned rows)
@@ -427,15 +432,23 @@ struct StateOps {
 __device__ __forceinline__ void load_state_ops(const DeltaArgs &a, int b, int sl, int wv, int li, int lq, int ch,
                                                StateOps &op)
 {
+    // a workgroup-uniform chunk base plus an unsigned 32-bit lane offset: no
+    // per-lane 64-bit address is formed per chunk (such temporaries can land in
+    // registers of loads still in flight, which the compiler then waits for)
     const float *wum = a.wum + (static_cast<int64_t>(b) * a.nC + ch) * kWsTiles * kCh * kDD;
     const float *gAT = wum + 2 * kCh * kDD, *gBT = wum + 3 * kCh * kDD;
-    const int ra = 16 * wv + li;
+    const uint32_t ra = 16 * wv + li;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-        op.at[kb] = *reinterpret_cast<const float4 *>(gAT + ra * kDD + 16 * kb + 4 * lq);
-    op.bt = *reinterpret_cast<const float4 *>(gBT + ra * kDD + 16 * sl + 4 * lq);
+        op.at[kb] = *reinterpret_cast<const float4 *>(gAT + (ra * kDD + 16u * kb + 4u * lq));
+    op.bt = *reinterpret_cast<const float4 *>(gBT + (ra * kDD + 16u * sl + 4u * lq));
 }
 
+// NC > 0: a sequence of exactly NC chunks, unrolled, with the operands of the
+// PD chunks after the one computing in flight (a rotated loop makes the
+// compiler wait, at its top, for loads issued one chunk earlier); NC = 0: any
+// count, in a loop with one chunk of operands ahead.
+template <int NC>
 __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
 {
     __shared__ float sS[2][16][kLd];   // rows 16 sl .. 16 sl + 15 of the state, two buffers in turn
@@ -481,7 +494,17 @@ __global__ void __launch_bounds__(256) delta_state_kernel(DeltaArgs a)
     // conditional load makes the compiler wait for it at the first use of
     // the other set
     const int last = a.nC - 1;
-    if (a.nC == 1) {
+    if constexpr (NC > 0) {
+        constexpr int PD = MGS_DELTA_PD < NC ? MGS_DELTA_PD : NC;
+        StateOps ops[NC];
+#pragma unroll
+        for (int c = 0; c < PD; ++c) load_state_ops(a, b, sl, wv, li, lq, c, ops[c]);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (c + PD < NC) load_state_ops(a, b, sl, wv, li, lq, c + PD, ops[c + PD]);
+            chunk(c, ops[c]);
+        }
+    } else if (a.nC == 1) {
         StateOps A;
         load_state_ops(a, b, sl, wv, li, lq, 0, A);
         chunk(0, A);
@@ -572,7 +595,14 @@ hipError_t launch_delta_fwd(const DeltaGeom &g, const float *q, const float *k, 
     }
     a.B = static_cast<int>(g.B);
     const unsigned groups = static_cast<unsigned>((g.B + 7) / 8) * 32;   // 4 slices x padded sequences
-    hipLaunchKernelGGL(delta_state_kernel, dim3(groups), dim3(256), 0, s, a);
+    switch (g.nC) {
+#define MGS_STATE_NC(n) case n: hipLaunchKernelGGL(delta_state_kernel<n>, dim3(groups), dim3(256), 0, s, a); break;
+    MGS_STATE_NC(1) MGS_STATE_NC(2) MGS_STATE_NC(3) MGS_STATE_NC(4) MGS_STATE_NC(5) MGS_STATE_NC(6)
+    MGS_STATE_NC(7) MGS_STATE_NC(8) MGS_STATE_NC(9) MGS_STATE_NC(10) MGS_STATE_NC(11) MGS_STATE_NC(12)
+    MGS_STATE_NC(13) MGS_STATE_NC(14) MGS_STATE_NC(15) MGS_STATE_NC(16)
+#undef MGS_STATE_NC
+    default: hipLaunchKernelGGL(delta_state_kernel<0>, dim3(groups), dim3(256), 0, s, a); break;
+    }
     if (g.nC > 0) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
