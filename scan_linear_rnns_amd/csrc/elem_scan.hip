@@ -44,9 +44,10 @@ namespace mgs {
 namespace {
 
 // tiles a look-back batch polls at once (measured at the long-T shape, 8
-// tiles along T: 4 beats 8 by ~0.2 us per kernel, 16 is ~0.6 us slower)
+// tiles along T: 4 beats 8 by ~0.2 us per kernel, 16 is ~0.6 us slower; with
+// the workgroup-scope publish, 3 beats 4 by ~0.1 us per kernel)
 #ifndef MGS_ELEM_LB
-#define MGS_ELEM_LB 4
+#define MGS_ELEM_LB 3
 #endif
 
 constexpr float kLog2e = 1.4426950408889634f;
