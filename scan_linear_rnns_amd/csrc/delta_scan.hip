@@ -48,6 +48,12 @@ namespace {
 #define MGS_DELTA_PD 3
 #endif
 
+// waves per workgroup of the multi-chunk prep kernel
+#ifndef MGS_DELTA_PREP_W
+#define MGS_DELTA_PREP_W 8
+#endif
+constexpr int kPrepW = MGS_DELTA_PREP_W;
+
 constexpr int kDD = 64;   // dk = dv
 constexpr int kCh = 64;   // steps per chunk
 constexpr int kLd = 68;   // LDS row stride (floats) of 64-wide tiles (16-byte aligned rows)
@@ -106,9 +112,13 @@ constexpr uint64_t kPrepTiles = 0xFEDCA98540ull;
 // DIRECT: a sequence of one chunk entered with S = 0 (no S0): the state pass
 // reduces to O = M U and S_T = U^T K, written here; only U is solved, one
 // 16-column tile per wave, and nothing goes through the workspace.
-template <bool DIRECT>
-__global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
+// PW: waves per workgroup, 4 or 8 (DIRECT: 4).  With 8, each wave owns one
+// 16-column tile of [W U] and two waves share each SIMD, so one wave's MFMA
+// chains and LDS reads overlap the other's.
+template <bool DIRECT, int PW>
+__global__ void __launch_bounds__(64 * PW) delta_prep_kernel(DeltaArgs a)
 {
+    static_assert(PW == 4 || (PW == 8 && !DIRECT), "prep workgroups of 4 waves, or 8 without DIRECT");
     __shared__ float sK[kCh][kLd], sV[kCh][kLd], sQ[kCh][kLd], sA[kCh][kLd], sM[kCh][kLd];
     __shared__ float sX[4][16][20];   // the inverses of the diagonal blocks of L
     __shared__ __align__(16) float sB[kCh];
@@ -123,12 +133,13 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
     // the chunk's rows of k, v, q (zero past the end of the sequence).  Loads
     // are unconditional from a clamped row, so all twelve are in flight at
     // once; rows past the end are zeroed after the load.
+    constexpr int NIT = 16 / PW;   // rows of 16 float4 per thread and array
     {
-        float4 kk[4], vv[4], qq[4];
+        float4 kk[NIT], vv[NIT], qq[NIT];
         const int c4 = (tid & 15) * 4;
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int r = (tid >> 4) + 16 * it;
+        for (int it = 0; it < NIT; ++it) {
+            const int r = (tid >> 4) + 4 * PW * it;
             const int64_t off = (row0 + min(r, nrow - 1)) * kDD + c4;
             kk[it] = *reinterpret_cast<const float4 *>(a.k + off);
             vv[it] = *reinterpret_cast<const float4 *>(a.v + off);
@@ -136,8 +147,8 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
         }
         const float bt = a.beta[row0 + min(tid & 63, nrow - 1)];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int r = (tid >> 4) + 16 * it;
+        for (int it = 0; it < NIT; ++it) {
+            const int r = (tid >> 4) + 4 * PW * it;
             const bool in = r < nrow;
             *reinterpret_cast<float4 *>(&sK[r][c4]) = in ? kk[it] : f4zero();
             *reinterpret_cast<float4 *>(&sV[r][c4]) = in ? vv[it] : f4zero();
@@ -148,16 +159,19 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
     __syncthreads();
 
     // A = strict_lower(diag(beta) K K^T) and M = causal(Q K^T), lower tiles
-    // only, five tiles per wave: each step of the reduction issues one MFMA
-    // of every tile in turn, so consecutive MFMAs do not depend on each other
+    // only, NT tiles per wave: each step of the reduction issues one MFMA of
+    // every tile in turn, so consecutive MFMAs do not depend on each other.
+    // With 8 waves the 20 tiles fill 24 slots; slots 20-23 repeat tiles 0-3,
+    // whose two writers store the same values.
+    constexpr int NT = (20 + PW - 1) / PW;
     {
-        f4v acc[5];
+        f4v acc[NT];
         const int wvu = __builtin_amdgcn_readfirstlane(wv);
-        int rowL[5], rowK[5];
-        bool isM[5];
+        int rowL[NT], rowK[NT];
+        bool isM[NT];
 #pragma unroll
-        for (int n = 0; n < 5; ++n) {
-            const int slot = wvu + 4 * n;
+        for (int n = 0; n < NT; ++n) {
+            const int slot = (wvu + PW * n) % 20;
             const int tile = static_cast<int>((kPrepTiles >> (4 * (slot % 10))) & 15);
             rowL[n] = 16 * (tile >> 2) + li;
             rowK[n] = 16 * (tile & 3) + li;
@@ -165,35 +179,35 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
             acc[n] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
         }
         // beta of the tiles' rows, read up front
-        float4 bq[5];
+        float4 bq[NT];
 #pragma unroll
-        for (int n = 0; n < 5; ++n) bq[n] = *reinterpret_cast<const float4 *>(&sB[rowL[n] - li + 4 * lq]);
+        for (int n = 0; n < NT; ++n) bq[n] = *reinterpret_cast<const float4 *>(&sB[rowL[n] - li + 4 * lq]);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            float4 x[5], y[5];
+            float4 x[NT], y[NT];
 #pragma unroll
-            for (int n = 0; n < 5; ++n) {
+            for (int n = 0; n < NT; ++n) {
                 const float(*L)[kLd] = isM[n] ? sQ : sK;
                 x[n] = *reinterpret_cast<const float4 *>(&L[rowL[n]][16 * kb + 4 * lq]);
                 y[n] = *reinterpret_cast<const float4 *>(&sK[rowK[n]][16 * kb + 4 * lq]);
             }
 #pragma unroll
-            for (int n = 0; n < 5; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[n].x, y[n].x, acc[n], 0, 0, 0);
+            for (int n = 0; n < NT; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[n].x, y[n].x, acc[n], 0, 0, 0);
 #pragma unroll
-            for (int n = 0; n < 5; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[n].y, y[n].y, acc[n], 0, 0, 0);
+            for (int n = 0; n < NT; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[n].y, y[n].y, acc[n], 0, 0, 0);
 #pragma unroll
-            for (int n = 0; n < 5; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[n].z, y[n].z, acc[n], 0, 0, 0);
+            for (int n = 0; n < NT; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[n].z, y[n].z, acc[n], 0, 0, 0);
 #pragma unroll
-            for (int n = 0; n < 5; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[n].w, y[n].w, acc[n], 0, 0, 0);
+            for (int n = 0; n < NT; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[n].w, y[n].w, acc[n], 0, 0, 0);
         }
         // lower parts of the tiles (rows scaled by beta for A), stored without
         // branches: the destination and the row scale are chosen per tile (the
         // row scales are pinned in registers first, so that their reads are not
         // sunk into the stores as conditional reads with a wait apiece)
 #pragma unroll
-        for (int n = 0; n < 5; ++n) asm volatile("" : "+v"(bq[n].x), "+v"(bq[n].y), "+v"(bq[n].z), "+v"(bq[n].w));
+        for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(bq[n].x), "+v"(bq[n].y), "+v"(bq[n].z), "+v"(bq[n].w));
 #pragma unroll
-        for (int n = 0; n < 5; ++n) {
+        for (int n = 0; n < NT; ++n) {
             const int i0 = rowL[n] - li + 4 * lq, j = rowK[n];
             const float sc[4] = {isM[n] ? 1.0f : bq[n].x, isM[n] ? 1.0f : bq[n].y, isM[n] ? 1.0f : bq[n].z,
                                  isM[n] ? 1.0f : bq[n].w};
@@ -208,7 +222,7 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
     // X_ww = (I + A_ww)^{-1}: lane c < 16 solves column c, row by row, from
     // the block's rows read up front (16-byte reads, the same address in every
     // lane)
-    if (lane < 16) {
+    if (lane < 16 && wv < 4) {
         const int o = 16 * wv;
         float4 rw[16][4];
 #pragma unroll
@@ -233,10 +247,11 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
     }
     __syncthreads();
 
-    // block solve of this wave's column tiles of [W U] (two; DIRECT: one tile of U)
-    constexpr int NH = DIRECT ? 1 : 2;
-    const bool isU = DIRECT || wv >= 2;            // wave-uniform: columns of V give U
-    const int cbase = DIRECT ? 16 * wv : 32 * (wv & 1);   // first column within K or V
+    // block solve of this wave's column tiles of [W U] (two with 4 waves; one
+    // with 8; DIRECT: one tile of U)
+    constexpr int NH = (DIRECT || PW == 8) ? 1 : 2;
+    const bool isU = DIRECT || wv >= PW / 2;       // wave-uniform: columns of V give U
+    const int cbase = DIRECT ? 16 * wv : (PW == 8 ? 16 * (wv & 3) : 32 * (wv & 1));   // first column within K or V
     float(*R)[kLd] = isU ? sV : sK;
     f4v Y[4][NH];
 #pragma unroll
@@ -335,11 +350,11 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
     // the eight (row block, column tile) products advance together, one MFMA
     // of each in turn
     {
-        f4v z[4][2];
+        f4v z[4][NH];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < NH; ++h)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) z[i][h][r] = isU ? 0.0f : sQ[16 * i + 4 * lq + r][cbase + 16 * h + li];
 #pragma unroll
@@ -355,7 +370,7 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
 #pragma unroll
                 for (int i = k2; i < 4; ++i)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
+                    for (int h = 0; h < NH; ++h) {
                         const float mj = j == 0 ? m[i].x : j == 1 ? m[i].y : j == 2 ? m[i].z : m[i].w;
                         z[i][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(mj, Y[k2][h][j], z[i][h], 0, 0, 0);
                     }
@@ -363,7 +378,7 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < NH; ++h) {
                 const int col = cbase + 16 * h + li;
                 const int row = 16 * i + 4 * lq;
                 if (isU) {
@@ -379,11 +394,11 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
     // the key index, columns this wave's W or U columns; A operand K^T[16 cb +
     // li][t] = K[t][16 cb + li], B operand the solved block registers
     {
-        f4v z[4][2];
+        f4v z[4][NH];
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < NH; ++h)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     z[cb][h][r] = (!isU && 16 * cb + 4 * lq + r == cbase + 16 * h + li) ? 1.0f : 0.0f;
@@ -403,14 +418,14 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaArgs a)
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
+                    for (int h = 0; h < NH; ++h)
                         z[cb][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[cb][j], Y[kb][h][j], z[cb][h], 0, 0, 0);
         }
         float *g = isU ? gBT : gAT;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < NH; ++h)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) g[(16 * cb + 4 * lq + r) * kDD + cbase + 16 * h + li] = z[cb][h][r];
     }
@@ -585,11 +600,12 @@ hipError_t launch_delta_fwd(const DeltaGeom &g, const float *q, const float *k, 
     a.T = g.T;
     a.nC = g.nC;
     if (g.nC == 1 && S0 == nullptr) {   // one chunk from a zero state: no state pass
-        hipLaunchKernelGGL(delta_prep_kernel<true>, dim3(static_cast<unsigned>(g.B)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((delta_prep_kernel<true, 4>), dim3(static_cast<unsigned>(g.B)), dim3(256), 0, s, a);
         return hipGetLastError();
     }
     if (g.nC > 0) {
-        hipLaunchKernelGGL(delta_prep_kernel<false>, dim3(static_cast<unsigned>(g.B * g.nC)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((delta_prep_kernel<false, kPrepW>), dim3(static_cast<unsigned>(g.B * g.nC)), dim3(64 * kPrepW), 0,
+                           s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
