@@ -97,16 +97,17 @@ __device__ __forceinline__ void lds_barrier()
 //     [W U]_i = X_ii (R_i - sum_{j<i} A_ij [W U]_j),   X_ii = L_ii^{-1},
 // then the state-free parts of the outputs, M = causal(Q K^T):
 //     Qt = Q - M W,   P = M U,
-// so that the state kernel's output is O = Qt S^T + P.  Wave w owns columns
-// 32w .. 32w+31 of [W U] (two 16-wide tiles) through all four row blocks, so
-// the block solve and the products with M keep every block in registers: an
+// so that the state kernel's output is O = Qt S^T + P.  Each wave owns 16-wide
+// column tiles of [W U] (two with 4 waves, one with 8) through all four row
+// blocks, so the block solve and the products with M keep every block in
+// registers: an
 // MFMA result (accumulator layout, rows 4 (l/16) + r) is directly the B
 // operand of the next MFMA under the permuted reduction index.
 
 // The ten 16 x 16 tiles on or below the diagonal, tile = 4 i + j, one per
 // nibble (slot s in bits 4s .. 4s+3): slots 0-9 are tiles of G, 10-19 the same
-// tiles of M, dealt to the four waves five apiece and decoded with scalar
-// shifts of a wave-uniform slot.
+// tiles of M, dealt to the waves (five apiece with 4 waves, two or three with
+// 8) and decoded with scalar shifts of a wave-uniform slot.
 constexpr uint64_t kPrepTiles = 0xFEDCA98540ull;
 
 // DIRECT: a sequence of one chunk entered with S = 0 (no S0): the state pass
