@@ -100,9 +100,8 @@ __device__ __forceinline__ void lds_barrier()
 // so that the state kernel's output is O = Qt S^T + P.  Each wave owns 16-wide
 // column tiles of [W U] (two with 4 waves, one with 8) through all four row
 // blocks, so the block solve and the products with M keep every block in
-// registers: an
-// MFMA result (accumulator layout, rows 4 (l/16) + r) is directly the B
-// operand of the next MFMA under the permuted reduction index.
+// registers: an MFMA result (accumulator layout, rows 4 (l/16) + r) is
+// directly the B operand of the next MFMA under the permuted reduction index.
 
 // The ten 16 x 16 tiles on or below the diagonal, tile = 4 i + j, one per
 // nibble (slot s in bits 4s .. 4s+3): slots 0-9 are tiles of G, 10-19 the same
