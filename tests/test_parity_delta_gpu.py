@@ -54,6 +54,16 @@ def test_delta_configs(gpu, name, B, T, d, seed):
     check(out, ref)
 
 
+@pytest.mark.parametrize("T", [256, 512, 960, 1024, 1025, 1088])
+def test_delta_state_pass_chunk_counts(gpu, T):
+    """Sequences of 4, 8, 15 and 16 chunks take the state pass unrolled for
+    their chunk count; 17 chunks (T = 1025, a one-step last chunk, and 1088)
+    take the looped pass."""
+    say(f"delta state pass B=2 T={T} ({(T + 63) // 64} chunks)")
+    out, ref = run_delta(delta_inputs(2, T, 64, 9, s0="normal"), gpu)
+    check(out, ref)
+
+
 @pytest.mark.parametrize("B,T", [(1, 1), (3, 7), (2, 63), (2, 64), (2, 65), (1, 129), (3, 300), (1, 2048)])
 def test_delta_edges(gpu, B, T):
     say(f"delta edge B={B} T={T} (S0 drawn)")
