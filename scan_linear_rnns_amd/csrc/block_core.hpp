@@ -1419,7 +1419,7 @@ __device__ __forceinline__ void publish_wm(uint64_t *dst, int tile, int slot, ui
 // aggregates of the tiles passed on the way.  A window without an inclusive
 // state that does not reach the end of the sequence means another round
 // (one poll per unit).  `overlap` runs once on every wave while the first
-// poll's loads are in flight (wave 0: after the walk).  Leaves the state
+// poll's loads are in flight (wave 0: before its first wait for the units).  Leaves the state
 // entering the tile in c (every lane, its slot) and publishes the tile's
 // inclusive state when publish_incl.
 template <int KIND, int K, int W, int DIR, typename F>
@@ -1496,8 +1496,9 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
             for (int i = 0; i < PER; ++i)
                 if (e0 + i < NWD) sLB[u][tl.slot][e0 + i] = tag_value(wd[i]);
             if (HALF ? tl.slot == 0 : tl.lane == 0) sStat[u] = in ? ((rA ? 1 : 0) | (rI ? 2 : 0)) : 4;
-        } else if (ALIAS && spin == 0) {
-            lds_barrier();
+        } else if (spin == 0) {
+            overlap();   // wave 0's own work while the units poll
+            if (ALIAS) lds_barrier();
         }
         lds_barrier();
         if (tl.wv == 0) {
@@ -1559,7 +1560,6 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
             Cr::apply(X, xo);
             publish_wm<CW>(a.incl, ftile, tl.slot, tag, xo, a.lb_local);
         }
-        overlap();
     } else {
 #pragma unroll
         for (int e = 0; e < CW; ++e) c[e] = sCar[tl.slot][e];
