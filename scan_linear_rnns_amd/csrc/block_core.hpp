@@ -1401,6 +1401,60 @@ __device__ __forceinline__ void publish_wm(uint64_t *dst, int tile, int slot, ui
     for (int e = 0; e < NW; ++e) tagged_store(p + e * 32, tag, x[e], local);
 }
 
+// The look-back walk over matrix carries for k = 8 on v_mfma_f32_4x4x1f32.
+// The instruction's 16 blocks are 4 x 4 outer products: block b adds the A
+// operand of lane 4b + i times the B operand of lane 4b + j to register i of
+// lane 4b + j, and a block never leaves a chain's 8 lanes.  While the staged
+// aggregates are applied (c <- G c, plus W for the reverse scan's carries), the
+// carry is held by columns, lane v of a chain holding column v: the B operand
+// is the lane's own column, the A operand row 4q + i of G read straight from
+// the staged words, and register i of instruction q gathers entry 4q + i of
+// the new column.  One transpose through LDS each way (sT: this chain's rows,
+// written and read by wave 0 alone) frames the walk.
+template <int KIND, int SW>
+__device__ __forceinline__ void walk_mfma8(float (*sLB)[32][SW], float (*sT)[8], int slot, int v, int stop, float *c)
+{
+    constexpr int CW = 8;
+    const int cb = slot & ~7, i = v & 3;
+    auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    // rows (slot s of row v holds column s ^ (v & 4)) -> columns
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sT[cb + (s ^ (v & 4))][v] = c[s];
+    wave_sync();
+    float cc[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) cc[m] = sT[cb + v][m];
+    for (int u = stop - 1; u >= 0; --u) {
+        const float *g = &sLB[u][cb][CW];   // row r of G at g + r SW, its column m at word m ^ (r & 4)
+        f32x4 d[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[q][e] = KIND == kMatMat ? g[(4 * q + e) * SW + 8 + (v ^ (4 * q))] : 0.0f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                d[q] = __builtin_amdgcn_mfma_f32_4x4x1f32(g[(4 * q + i) * SW + (m ^ (4 * q))], cc[m], d[q], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cc[4 * q + e] = d[q][e];
+    }
+    // columns -> rows
+    wave_sync();
+#pragma unroll
+    for (int m = 0; m < 8; ++m) sT[cb + m][v] = cc[m];
+    wave_sync();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) c[s] = sT[cb + v][s ^ (v & 4)];
+    wave_sync();
+}
+
 // Look-back of a tile whose tree is built (X: the tile aggregate, read by
 // wave 0's lower half alone, from LDS).
 // Polling units -- half-waves of waves 1 .. W-1 when a tile's CW + AW words
@@ -1531,6 +1585,8 @@ __device__ __forceinline__ void block_lookback(const BlkArgs &a, const Tile &tl,
 #pragma unroll
                         for (int e = 0; e < AW; ++e) g[e] = gn[e];
                     }
+                } else if constexpr (K == 8) {
+                    if (stop > 0) walk_mfma8<KIND, SW>(sLB, sCar, tl.slot, tl.v, stop, c);
                 } else {
                     for (int u = stop - 1; u >= 0; --u) Cr::apply(&sLB[u][tl.slot][CW], c);
                 }
