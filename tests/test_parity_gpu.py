@@ -255,11 +255,12 @@ def test_matrix_bwd_without_forward_state(gpu, B, T, d):
 @pytest.mark.parametrize("B,T", [(4, 1024), (2, 2000)])
 def test_rotation_only_long_T(gpu, B, T):
     """Pure rotations keep P orthogonal, so the long-T product does not decay.
-    T = 2000 gives 16 tiles along T, more than the eight waves of a
-    workgroup: the look-back then composes tiles farther back than the
-    aggregates the idle waves fetch, in batches of which the last is partial
-    (seven far tiles, batches of four).  Without decay a skipped or repeated
-    tile would show in every later output."""
+    T = 2000 gives 16 tiles along T, more than one round of polls reaches
+    (14 half-wave units for the block-affine scan's vector carries, 7 whole-
+    wave units for the cumulative product's matrix carries): later tiles
+    walk back over several rounds or stop at an inclusive state published
+    meanwhile.  Without decay a skipped or repeated tile would show in every
+    later output."""
     say(f"block rotation-only B={B} T={T}")
     out, ref = run_block(B, T, 64, 9, gpu, gate=False, h0="normal")
     # Without the gate nothing contracts: h is a random walk (|h| ~ 50 at
